@@ -1,0 +1,308 @@
+/*
+ * Seeded synthetic inputs for one sparse MoE FFN layer.
+ *
+ * This file produces the bytes that both the HIP path and the CPU oracle
+ * consume: activations, router weights and expert weights.  It holds none of
+ * the layer's arithmetic (no router, no dequantisation, no SwiGLU, no combine).
+ *
+ *   - Every element is a pure function of (seed, tensor id, flat index):
+ *     a SplitMix64 finaliser over a Weyl counter gives 64 random bits, two
+ *     such draws give two uniforms and the Box-Muller transform turns the pair
+ *     into two normals (even index -> cosine branch, odd index -> sine branch).
+ *     Any element can therefore be regenerated on any core in any order.
+ *   - Weight groups are quantised with a min-max affine quantiser: scale =
+ *     fp16((max-min)/(2^bits-1)), bias = fp16(min), q = clamp(rint((w-bias)/scale)).
+ *     4-bit codes are packed two per byte, the even column in the low nibble.
+ *   - Zipf-skewed routing is planted into activations by adding a multiple of
+ *     the chosen experts' router rows (see gen_planted_x).
+ *
+ * fp16 and bf16 values are produced with round-to-nearest-even from fp32.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- RNG --- */
+
+static inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+static inline uint64_t stream_key(uint64_t seed, uint32_t tid) {
+  return mix64(seed * 0x9E3779B97F4A7C15ULL + ((uint64_t)tid << 32) + 0x632BE59BD9B4E019ULL);
+}
+
+static inline uint64_t draw_bits(uint64_t key, uint64_t ctr) {
+  return mix64(key + (ctr + 1) * 0x9E3779B97F4A7C15ULL);
+}
+
+/* uniform on the open interval (0, 1) */
+static inline double u01(uint64_t b) { return ((double)(b >> 11) + 0.5) * (1.0 / 9007199254740992.0); }
+
+static inline double normal_at(uint64_t key, uint64_t i) {
+  uint64_t j = i >> 1;
+  double u1 = u01(draw_bits(key, 2 * j));
+  double u2 = u01(draw_bits(key, 2 * j + 1));
+  double r = sqrt(-2.0 * log(u1));
+  double th = 6.283185307179586476925 * u2;
+  return (i & 1) ? r * sin(th) : r * cos(th);
+}
+
+/* ------------------------------------------------------ fp16 / bf16 ---- */
+
+static uint16_t f32_to_f16_bits(float f) {
+  uint32_t x;
+  memcpy(&x, &f, 4);
+  uint32_t sign = (x >> 16) & 0x8000u;
+  uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax >= 0x7F800000u) return (uint16_t)(sign | (ax > 0x7F800000u ? 0x7E00u : 0x7C00u));
+  if (ax >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u); /* >= 65520 rounds to inf */
+  if (ax < 0x38800000u) {                                    /* below 2^-14: subnormal */
+    float v;
+    memcpy(&v, &ax, 4);
+    float r = nearbyintf(v * 16777216.0f); /* exact scaling by 2^24, then RNE */
+    return (uint16_t)(sign | (uint32_t)r);
+  }
+  uint32_t e = (ax >> 23) - 127 + 15;
+  uint32_t m = ax & 0x7FFFFFu;
+  uint32_t h = (e << 10) | (m >> 13);
+  uint32_t rem = m & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h++;
+  return (uint16_t)(sign | h);
+}
+
+static uint16_t f32_to_bf16_bits(float f) {
+  uint32_t x;
+  memcpy(&x, &f, 4);
+  if ((x & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((x >> 16) | 0x40u);
+  x += 0x7FFFu + ((x >> 16) & 1u);
+  return (uint16_t)(x >> 16);
+}
+
+static double f16_bits_to_double(uint16_t h) {
+  int e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(m | 0x400), e - 25);
+  return (h & 0x8000) ? -v : v;
+}
+
+static double bf16_bits_to_double(uint16_t h) {
+  uint32_t x = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &x, 4);
+  return (double)f;
+}
+
+/* dtype codes: 1 = fp16, 2 = bf16 */
+static inline uint16_t round_to(double v, int dtype) {
+  return dtype == 2 ? f32_to_bf16_bits((float)v) : f32_to_f16_bits((float)v);
+}
+
+static inline double decode(uint16_t b, int dtype) {
+  return dtype == 2 ? bf16_bits_to_double(b) : f16_bits_to_double(b);
+}
+
+/* -------------------------------------------------------- exported ---- */
+
+void gen_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* n normals with standard deviation sigma, elements [start, start+n) of the stream */
+void gen_normal_f64(uint64_t seed, uint32_t tid, int64_t start, int64_t n, double sigma, double* out) {
+  uint64_t key = stream_key(seed, tid);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = sigma * normal_at(key, (uint64_t)(start + i));
+}
+
+/* the same draws, rounded to fp16 (dtype 1) or bf16 (dtype 2) */
+void gen_normal_half(uint64_t seed, uint32_t tid, int64_t start, int64_t n, double sigma, int dtype,
+                     uint16_t* out) {
+  uint64_t key = stream_key(seed, tid);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = round_to(sigma * normal_at(key, (uint64_t)(start + i)), dtype);
+}
+
+/* n uniforms on (0,1) */
+void gen_uniform(uint64_t seed, uint32_t tid, int64_t start, int64_t n, double* out) {
+  uint64_t key = stream_key(seed, tid);
+  for (int64_t i = 0; i < n; ++i) out[i] = u01(draw_bits(key, (uint64_t)(start + i)));
+}
+
+/* round an fp64 array to fp16/bf16 bits (RNE through fp32) */
+void gen_round_half(const double* v, int64_t n, int dtype, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = round_to(v[i], dtype);
+}
+
+/* decode fp16/bf16 bits to fp64 */
+void gen_decode_half(const uint16_t* b, int64_t n, int dtype, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = decode(b[i], dtype);
+}
+
+/*
+ * Quantise one group of `gs` values to `bits` with the min-max affine rule.
+ * Writes codes (unpacked, one per byte) and the fp16 scale/bias bits.
+ */
+static void quant_group(const double* w, int gs, int bits, uint8_t* codes, uint16_t* s_bits, uint16_t* b_bits) {
+  double lo = w[0], hi = w[0];
+  for (int i = 1; i < gs; ++i) {
+    if (w[i] < lo) lo = w[i];
+    if (w[i] > hi) hi = w[i];
+  }
+  int qmax = (1 << bits) - 1;
+  uint16_t sb = f32_to_f16_bits((float)((hi - lo) / qmax));
+  uint16_t bb = f32_to_f16_bits((float)lo);
+  double s = f16_bits_to_double(sb), b = f16_bits_to_double(bb);
+  for (int i = 0; i < gs; ++i) {
+    int q = 0;
+    if (s > 0) {
+      double r = nearbyint((w[i] - b) / s);
+      q = r < 0 ? 0 : (r > qmax ? qmax : (int)r);
+    }
+    codes[i] = (uint8_t)q;
+  }
+  *s_bits = sb;
+  *b_bits = bb;
+}
+
+/* quantise an explicit fp64 matrix [rows, K] (test helper, same rule as below) */
+void gen_quantize_rows(const double* w, int64_t rows, int K, int bits, int gs, uint8_t* q, uint16_t* scales,
+                       uint16_t* biases) {
+  int64_t row_bytes = bits == 4 ? K / 2 : K;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    uint8_t codes[256];
+    for (int g = 0; g < K / gs; ++g) {
+      quant_group(w + r * K + (int64_t)g * gs, gs, bits, codes, &scales[r * (K / gs) + g], &biases[r * (K / gs) + g]);
+      uint8_t* dst = q + r * row_bytes;
+      if (bits == 4) {
+        for (int i = 0; i < gs; i += 2)
+          dst[(g * gs + i) / 2] = (uint8_t)(codes[i] | (codes[i + 1] << 4));
+      } else {
+        memcpy(dst + (int64_t)g * gs, codes, (size_t)gs);
+      }
+    }
+  }
+}
+
+/*
+ * Draw an expert weight tensor [E, N, K] of N(0, sigma) values (flat index
+ * (e*N + n)*K + k of stream `tid`) and quantise it by groups of `gs` columns.
+ *   q:      bits == 4: [E, N, K/2] bytes, low nibble = even column;
+ *           bits == 8: [E, N, K] bytes
+ *   scales, biases: [E, N, K/gs] fp16 bits
+ */
+void gen_quant_weights(uint64_t seed, uint32_t tid, int E, int N, int K, int bits, int gs, double sigma, uint8_t* q,
+                       uint16_t* scales, uint16_t* biases) {
+  uint64_t key = stream_key(seed, tid);
+  int64_t rows = (int64_t)E * N;
+  int64_t row_bytes = bits == 4 ? K / 2 : K;
+  int ng = K / gs;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t r = 0; r < rows; ++r) {
+    double w[256];
+    uint8_t codes[256];
+    for (int g = 0; g < ng; ++g) {
+      uint64_t base = (uint64_t)(r * K + (int64_t)g * gs);
+      for (int i = 0; i < gs; ++i) w[i] = sigma * normal_at(key, base + (uint64_t)i);
+      quant_group(w, gs, bits, codes, &scales[r * ng + g], &biases[r * ng + g]);
+      uint8_t* dst = q + r * row_bytes;
+      if (bits == 4) {
+        for (int i = 0; i < gs; i += 2)
+          dst[(g * gs + i) / 2] = (uint8_t)(codes[i] | (codes[i + 1] << 4));
+      } else {
+        memcpy(dst + (int64_t)g * gs, codes, (size_t)gs);
+      }
+    }
+  }
+}
+
+/*
+ * Zipf-skewed expert sets for tokens [t0, t0+T): k distinct experts drawn without
+ * replacement with P(rank r) proportional to r^-s over a seeded permutation of
+ * the E experts (Fisher-Yates, stream 7); draws use stream 5.
+ */
+void gen_zipf_sets(uint64_t seed, int64_t t0, int T, int E, int k, double s, int32_t* sets) {
+  uint64_t kperm = stream_key(seed, 7), kdraw = stream_key(seed, 5);
+  int* perm = (int*)malloc(sizeof(int) * (size_t)E);
+  double* pw = (double*)malloc(sizeof(double) * (size_t)E);
+  for (int i = 0; i < E; ++i) perm[i] = i;
+  for (int i = E - 1; i > 0; --i) {
+    int j = (int)(u01(draw_bits(kperm, (uint64_t)i)) * (i + 1));
+    if (j > i) j = i;
+    int t = perm[i];
+    perm[i] = perm[j];
+    perm[j] = t;
+  }
+  for (int r = 0; r < E; ++r) pw[r] = pow((double)(r + 1), -s);
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    uint8_t taken[256];
+    memset(taken, 0, sizeof(taken));
+    for (int j = 0; j < k; ++j) {
+      double tot = 0;
+      for (int r = 0; r < E; ++r)
+        if (!taken[r]) tot += pw[r];
+      double u = u01(draw_bits(kdraw, (uint64_t)(t0 + t) * 16 + (uint64_t)j)) * tot;
+      int pick = -1;
+      double c = 0;
+      for (int r = 0; r < E; ++r) {
+        if (taken[r]) continue;
+        pick = r;
+        c += pw[r];
+        if (u < c) break;
+      }
+      taken[pick] = 1;
+      sets[(int64_t)t * k + j] = perm[pick];
+    }
+  }
+  free(perm);
+  free(pw);
+}
+
+/*
+ * Activations of tokens [t0, t0+T) with a planted routing preference:
+ *   x_t = z_t + gamma * sum_{e in S_t} Wr[e] / |Wr[e]|^2,  z_t ~ N(0,1) (stream 0)
+ * computed in fp64 from the already-rounded router rows, then rounded to dtype.
+ * This raises token t's logits for its planted experts by about gamma.
+ */
+void gen_planted_x(uint64_t seed, int64_t t0, int T, int H, int E, int k, const uint16_t* wr, int dtype,
+                   const int32_t* sets, double gamma, uint16_t* x) {
+  uint64_t key = stream_key(seed, 0);
+  double* inv = (double*)malloc(sizeof(double) * (size_t)E);
+  for (int e = 0; e < E; ++e) {
+    double n2 = 0;
+    for (int h = 0; h < H; ++h) {
+      double v = decode(wr[(int64_t)e * H + h], dtype);
+      n2 += v * v;
+    }
+    inv[e] = n2 > 0 ? 1.0 / n2 : 0.0;
+  }
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    for (int h = 0; h < H; ++h) {
+      double v = normal_at(key, (uint64_t)(t0 + t) * (uint64_t)H + (uint64_t)h);
+      for (int j = 0; j < k; ++j) {
+        int e = sets[(int64_t)t * k + j];
+        v += gamma * decode(wr[(int64_t)e * H + h], dtype) * inv[e];
+      }
+      x[(int64_t)t * H + h] = round_to(v, dtype);
+    }
+  }
+  free(inv);
+}

@@ -1,0 +1,457 @@
+/*
+ * CPU oracle for one sparse Mixture-of-Experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  It shares no code with the HIP
+ * path and is deliberately plain: every step is the textbook definition,
+ * written out with sequential fp32 sums (compiled with -ffp-contract=off, so
+ * each product and each sum is rounded separately), no blocking, no fusion.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *   router      logits = x . Wr^T, then softmax and top-k (page "Qwen3.5 Block
+ *               在llama.cpp中的映射与优化原理", section 4.1, the PyTorch router:
+ *               F.linear -> softmax -> topk).  Selection is made on the logits
+ *               in the order (larger logit first, then lower expert index);
+ *               softmax is monotone, so this is the same set as topk over the
+ *               probabilities, without ties created by rounding.  The selected
+ *               probabilities are renormalised to sum to one.
+ *   adaptive k  Shannon entropy of the routing distribution, averaged over the
+ *               tokens of the call; k = 1 if H < 1.2, 2 if 1.2 <= H < 2.5,
+ *               3 otherwise (page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析",
+ *               section 2.2, Entropy-Aware Routing).  Natural logarithm.
+ *   pair sort   stable counting sort of (token, slot) pairs by expert, the
+ *               grouping a gathered expert matmul needs (oMLX page, the sorted
+ *               "_gather_sort" branch under "如何验证正确性").
+ *   dequant     affine group quantisation, w = scale * q + bias with one
+ *               scale/bias per row and 64-column group (oMLX page, "融合原理":
+ *               scales are packed per output row).
+ *   gate_up     the gate and up projections concatenated along the output
+ *               axis, [gate, up] order, then split (oMLX page, steps 3 and 4).
+ *   SwiGLU      h = silu(g) * u, silu(g) = g / (1 + e^-g).
+ *   down        o = W_down . h
+ *   combine     y = sum over the token's slots of weight * o, in slot order,
+ *               with the weight applied after the down projection (llama.cpp
+ *               page, section 4.2, the weighted-sum loop), rounded to the
+ *               activation dtype with round-to-nearest-even.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+
+/* ------------------------------------------------ fp16 / bf16 (own) ---- */
+
+float oracle_half_to_float(uint16_t b, int dtype) {
+  if (dtype == ORACLE_BF16) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+  }
+  int sign = b >> 15, e = (b >> 10) & 31, m = b & 1023;
+  float v;
+  if (e == 0) v = ldexpf((float)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexpf((float)(1024 + m), e - 25);
+  return sign ? -v : v;
+}
+
+/* round-to-nearest-even from fp32, written with frexp/ldexp rather than bits */
+uint16_t oracle_float_to_half(float f, int dtype) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint32_t sign = u >> 31;
+  if (isnan(f)) return (uint16_t)(dtype == ORACLE_BF16 ? ((u >> 16) | 0x40) : ((sign << 15) | 0x7E00));
+  if (dtype == ORACLE_BF16) {
+    /* keep 8 significant bits: value = round_half_even(f / 2^(e-8)) * 2^(e-8) */
+    if (isinf(f) || f == 0.0f) return (uint16_t)(u >> 16);
+    if (fabs((double)f) < ldexp(1.0, -126)) { /* below the normal range: fixed grid 2^-133 */
+      double r = nearbyint(ldexp(fabs((double)f), 133));
+      return (uint16_t)((sign << 15) | (uint32_t)r);
+    }
+    int e;
+    double m = frexp(fabs((double)f), &e); /* |f| = m * 2^e, m in [0.5, 1) */
+    double r = nearbyint(ldexp(m, 8));     /* 8 significant bits, RNE */
+    double v = ldexp(r, e - 8);
+    float fv = (float)v;
+    uint32_t uv;
+    memcpy(&uv, &fv, 4);
+    return (uint16_t)((sign << 15) | ((uv >> 16) & 0x7FFF));
+  }
+  double a = fabs((double)f);
+  uint32_t mag;
+  if (isinf(f) || a >= 65520.0) {
+    mag = 0x7C00;
+  } else if (a < ldexp(1.0, -14)) {
+    mag = (uint32_t)nearbyint(ldexp(a, 24)); /* subnormal grid 2^-24 */
+  } else {
+    int e;
+    double m = frexp(a, &e);               /* a = m * 2^e, m in [0.5,1) */
+    double r = nearbyint(ldexp(m, 11));    /* 11 significant bits */
+    if (r >= 2048.0) { r /= 2.0; e += 1; } /* rounding carried into the next binade */
+    mag = (uint32_t)((e - 1 + 15) << 10) | ((uint32_t)r - 1024u);
+    if (mag >= 0x7C00) mag = 0x7C00;
+  }
+  return (uint16_t)((sign << 15) | mag);
+}
+
+/* -------------------------------------------------------- dequant (A5) -- */
+
+/*
+ * One row of K weights.  bits 4: two codes per byte, even column in the low
+ * nibble; bits 8: one code per byte; code q is unsigned.  w = s*q + b in fp32
+ * (two roundings), s and b fp16, one pair per 64-column group.
+ * bits 16: the row is fp16 values, copied.
+ */
+void oracle_dequant_row(const void* q_row, const uint16_t* s_row, const uint16_t* b_row, int K, int bits, int gs,
+                        float* out) {
+  if (bits == 16) {
+    const uint16_t* w = (const uint16_t*)q_row;
+    for (int k = 0; k < K; ++k) out[k] = oracle_half_to_float(w[k], ORACLE_F16);
+    return;
+  }
+  const uint8_t* q = (const uint8_t*)q_row;
+  for (int k = 0; k < K; ++k) {
+    int code = bits == 4 ? (q[k / 2] >> (4 * (k & 1))) & 15 : q[k];
+    float s = oracle_half_to_float(s_row[k / gs], ORACLE_F16);
+    float b = oracle_half_to_float(b_row[k / gs], ORACLE_F16);
+    float sq = s * (float)code;
+    out[k] = sq + b;
+  }
+}
+
+static int64_t row_bytes_of(int K, int bits) { return bits == 4 ? K / 2 : (bits == 8 ? K : 2 * (int64_t)K); }
+
+/* ---------------------------------------------------------- router (A1) -- */
+
+void oracle_router_logits(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, float* logits) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      float acc = 0.0f;
+      for (int h = 0; h < H; ++h) {
+        float p = oracle_half_to_float(x[(int64_t)t * H + h], dtype) * oracle_half_to_float(wr[(int64_t)e * H + h], dtype);
+        acc = acc + p;
+      }
+      logits[(int64_t)t * E + e] = acc;
+    }
+  }
+}
+
+/* -------------------------------------------- selection + weights (A2) -- */
+
+/* experts ordered by larger logit first, lower index first among equals */
+static void order_experts(const float* l, int E, int* order) {
+  for (int i = 0; i < E; ++i) {
+    int j = i;
+    while (j > 0 && (l[order[j - 1]] < l[i] || (l[order[j - 1]] == l[i] && order[j - 1] > i))) {
+      order[j] = order[j - 1];
+      --j;
+    }
+    order[j] = i;
+  }
+}
+
+/* softmax over all E experts (fp32, max-subtracted), then the chosen k renormalised */
+static void select_one(const float* l, int E, int k, int kcap, int32_t* idx, float* w) {
+  int order[256];
+  float p[256];
+  order_experts(l, E, order);
+  float lmax = l[order[0]];
+  float z = 0.0f;
+  for (int e = 0; e < E; ++e) {
+    p[e] = expf(l[e] - lmax);
+    z = z + p[e];
+  }
+  for (int e = 0; e < E; ++e) p[e] = p[e] / z;
+  float tot = 0.0f;
+  for (int s = 0; s < k; ++s) tot = tot + p[order[s]];
+  for (int s = 0; s < kcap; ++s) {
+    if (s < k) {
+      idx[s] = order[s];
+      w[s] = p[order[s]] / tot;
+    } else {
+      idx[s] = -1;
+      w[s] = 0.0f;
+    }
+  }
+}
+
+void oracle_select_topk(const float* logits, int T, int E, int k, int kcap, int32_t* idx, float* w) {
+  for (int t = 0; t < T; ++t) select_one(logits + (int64_t)t * E, E, k, kcap, idx + (int64_t)t * kcap, w + (int64_t)t * kcap);
+}
+
+/* -------------------------------------------------- adaptive k (A2') --- */
+
+/* Shannon entropy (nats) of softmax(logits) for one token */
+float oracle_token_entropy(const float* l, int E) {
+  float lmax = l[0];
+  for (int e = 1; e < E; ++e)
+    if (l[e] > lmax) lmax = l[e];
+  float p[256], z = 0.0f;
+  for (int e = 0; e < E; ++e) {
+    p[e] = expf(l[e] - lmax);
+    z = z + p[e];
+  }
+  float h = 0.0f;
+  for (int e = 0; e < E; ++e) {
+    float pe = p[e] / z;
+    if (pe > 0.0f) h = h - pe * logf(pe);
+  }
+  return h;
+}
+
+int oracle_entropy_k(float H) {
+  if (H < 1.2f) return 1;
+  if (H < 2.5f) return 2;
+  return 3;
+}
+
+/* batch entropy: the mean over the call's tokens of the per-token entropy */
+float oracle_batch_entropy(const float* logits, int T, int E) {
+  float s = 0.0f;
+  for (int t = 0; t < T; ++t) s = s + oracle_token_entropy(logits + (int64_t)t * E, E);
+  return s / (float)T;
+}
+
+/*
+ * Full routing.  k > 0: static top-k, kcap = k.  k == -1: entropy-adaptive,
+ * kcap = 3, k_used chosen from the batch entropy; slots >= k_used get
+ * index -1 and weight 0.  logits_out may be NULL.
+ */
+void oracle_route(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k, int32_t* idx,
+                  float* w, int32_t* k_used, float* h_mean, float* logits_out) {
+  float* logits = logits_out ? logits_out : (float*)malloc(sizeof(float) * (size_t)T * E);
+  oracle_router_logits(x, dtype, T, H, wr, E, logits);
+  int kcap = k > 0 ? k : 3, ku = k;
+  float hm = 0.0f;
+  if (k < 0) {
+    hm = oracle_batch_entropy(logits, T, E);
+    ku = oracle_entropy_k(hm);
+  }
+  oracle_select_topk(logits, T, E, ku, kcap, idx, w);
+  if (k_used) *k_used = ku;
+  if (h_mean) *h_mean = hm;
+  if (!logits_out) free(logits);
+}
+
+/* ------------------------------------------------------ pair sort (A3) -- */
+
+/*
+ * Pairs p = t*kcap + s for s < k_used.  counts[e] = pairs routed to e,
+ * offsets = exclusive prefix sum (E+1 entries), perm = pair ids grouped by
+ * expert and ascending within an expert, pos = inverse of perm (-1 for the
+ * unused slots).  perm entries past the last valid pair are -1.
+ */
+void oracle_sort_pairs(const int32_t* idx, int T, int kcap, int k_used, int E, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, int32_t* pos) {
+  int64_t P = (int64_t)T * kcap;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < P; ++p)
+    if (p % kcap < k_used) counts[idx[p]]++;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int64_t p = 0; p < P; ++p) perm[p] = -1;
+  for (int64_t p = 0; p < P; ++p) {
+    if (p % kcap >= k_used) {
+      pos[p] = -1;
+      continue;
+    }
+    int e = idx[p];
+    int32_t at = offsets[e] + fill[e]++;
+    perm[at] = (int32_t)p;
+    pos[p] = at;
+  }
+  free(fill);
+}
+
+/* ------------------------------------------------ gate/up packing ------ */
+
+/*
+ * Concatenate gate [E, I, K] and up [E, I, K] along the output axis into
+ * gate_up [E, 2I, K], gate rows first; weights, scales and biases alike.
+ */
+void oracle_fuse_gate_up(const void* gq, const uint16_t* gs_, const uint16_t* gb, const void* uq, const uint16_t* us,
+                         const uint16_t* ub, int E, int I, int K, int bits, int gsz, void* oq, uint16_t* os,
+                         uint16_t* ob) {
+  int64_t rb = row_bytes_of(K, bits);
+  int64_t ng = K / gsz;
+  for (int e = 0; e < E; ++e) {
+    uint8_t* dq = (uint8_t*)oq + (int64_t)e * 2 * I * rb;
+    memcpy(dq, (const uint8_t*)gq + (int64_t)e * I * rb, (size_t)(I * rb));
+    memcpy(dq + I * rb, (const uint8_t*)uq + (int64_t)e * I * rb, (size_t)(I * rb));
+    if (bits != 16) {
+      memcpy(os + (int64_t)e * 2 * I * ng, gs_ + (int64_t)e * I * ng, sizeof(uint16_t) * (size_t)(I * ng));
+      memcpy(os + ((int64_t)e * 2 * I + I) * ng, us + (int64_t)e * I * ng, sizeof(uint16_t) * (size_t)(I * ng));
+      memcpy(ob + (int64_t)e * 2 * I * ng, gb + (int64_t)e * I * ng, sizeof(uint16_t) * (size_t)(I * ng));
+      memcpy(ob + ((int64_t)e * 2 * I + I) * ng, ub + (int64_t)e * I * ng, sizeof(uint16_t) * (size_t)(I * ng));
+    }
+  }
+}
+
+/* ------------------------------------------- expert FFN (A5-A8) -------- */
+
+typedef struct {
+  const void* q;
+  const uint16_t* s;
+  const uint16_t* b;
+  int K, bits, gs;
+} row_src;
+
+static const void* rq(const row_src* r, int64_t row) { return (const uint8_t*)r->q + row * row_bytes_of(r->K, r->bits); }
+static const uint16_t* rs(const row_src* r, int64_t row) { return r->s ? r->s + row * (r->K / r->gs) : NULL; }
+static const uint16_t* rbias(const row_src* r, int64_t row) { return r->b ? r->b + row * (r->K / r->gs) : NULL; }
+
+/* out[n] = sum_k v[k] * W[row0 + n, k] for n in [0, N), sequential fp32 sums */
+static void matvec(const row_src* W, int64_t row0, int N, const float* v, float* out) {
+  int K = W->K;
+#pragma omp parallel
+  {
+    float* wrow = (float*)malloc(sizeof(float) * (size_t)K);
+#pragma omp for schedule(static)
+    for (int n = 0; n < N; ++n) {
+      oracle_dequant_row(rq(W, row0 + n), rs(W, row0 + n), rbias(W, row0 + n), K, W->bits, W->gs, wrow);
+      float acc = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        float p = v[k] * wrow[k];
+        acc = acc + p;
+      }
+      out[n] = acc;
+    }
+    free(wrow);
+  }
+}
+
+static float silu(float g) { return g / (1.0f + expf(-g)); }
+
+/*
+ * One (token, expert): x [H] fp32 values; gate_up rows [2I, H] of this expert
+ * (gate first), down rows [H, I].  h_out [I] (may be NULL), o [H].
+ */
+void oracle_expert_ffn(const float* x, const void* guq, const uint16_t* gus, const uint16_t* gub, const void* dq,
+                       const uint16_t* ds, const uint16_t* db, int H, int I, int bits, int gsz, float* h_out,
+                       float* o) {
+  row_src gu = {guq, gus, gub, H, bits, gsz}, dn = {dq, ds, db, I, bits, gsz};
+  float* gu_v = (float*)malloc(sizeof(float) * 2 * (size_t)I);
+  float* h = (float*)malloc(sizeof(float) * (size_t)I);
+  matvec(&gu, 0, 2 * I, x, gu_v);
+  for (int j = 0; j < I; ++j) {
+    float g = gu_v[j], u = gu_v[I + j];
+    h[j] = silu(g) * u;
+  }
+  matvec(&dn, 0, H, h, o);
+  if (h_out) memcpy(h_out, h, sizeof(float) * (size_t)I);
+  free(gu_v);
+  free(h);
+}
+
+/* the same with separate gate [I, H] and up [I, H] rows */
+void oracle_expert_ffn_unfused(const float* x, const void* gq, const uint16_t* gs_, const uint16_t* gb, const void* uq,
+                               const uint16_t* us, const uint16_t* ub, const void* dq, const uint16_t* ds,
+                               const uint16_t* db, int H, int I, int bits, int gsz, float* h_out, float* o) {
+  row_src ga = {gq, gs_, gb, H, bits, gsz}, ua = {uq, us, ub, H, bits, gsz}, dn = {dq, ds, db, I, bits, gsz};
+  float* g = (float*)malloc(sizeof(float) * (size_t)I);
+  float* u = (float*)malloc(sizeof(float) * (size_t)I);
+  float* h = (float*)malloc(sizeof(float) * (size_t)I);
+  matvec(&ga, 0, I, x, g);
+  matvec(&ua, 0, I, x, u);
+  for (int j = 0; j < I; ++j) h[j] = silu(g[j]) * u[j];
+  matvec(&dn, 0, H, h, o);
+  if (h_out) memcpy(h_out, h, sizeof(float) * (size_t)I);
+  free(g);
+  free(u);
+  free(h);
+}
+
+/* ------------------------------------------------------ layer (A1-A9) -- */
+
+/*
+ * Expert part of the layer for selected tokens, given the routing:
+ *   y_f32[i, :] = sum_{s < k_used} w[t, s] * o_{t,s}  (slot order, fp32)
+ * for t = tokens[i].  gate_up: [E, 2I, H] tensor; down: [E, H, I].
+ * h_out (may be NULL): [n, kcap, I] SwiGLU outputs, rows of unused slots untouched.
+ */
+void oracle_tokens_forward(const uint16_t* x, int dtype, int H, const int32_t* tokens, int n, const int32_t* idx,
+                           const float* w, int kcap, int k_used, const void* guq, const uint16_t* gus,
+                           const uint16_t* gub, const void* dq, const uint16_t* ds, const uint16_t* db, int I,
+                           int bits, int gsz, float* y_f32, float* h_out) {
+  int64_t gu_rows = 2 * (int64_t)I, rbh = row_bytes_of(H, bits), rbi = row_bytes_of(I, bits);
+  int64_t ngh = H / gsz, ngi = I / gsz;
+  float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+  float* o = (float*)malloc(sizeof(float) * (size_t)H);
+  for (int i = 0; i < n; ++i) {
+    int t = tokens[i];
+    for (int h = 0; h < H; ++h) xf[h] = oracle_half_to_float(x[(int64_t)t * H + h], dtype);
+    float* y = y_f32 + (int64_t)i * H;
+    for (int h = 0; h < H; ++h) y[h] = 0.0f;
+    for (int s = 0; s < k_used; ++s) {
+      int e = idx[(int64_t)t * kcap + s];
+      float ws = w[(int64_t)t * kcap + s];
+      const uint8_t* eq = (const uint8_t*)guq + (int64_t)e * gu_rows * rbh;
+      const uint16_t* es = gus ? gus + (int64_t)e * gu_rows * ngh : NULL;
+      const uint16_t* eb = gub ? gub + (int64_t)e * gu_rows * ngh : NULL;
+      const uint8_t* edq = (const uint8_t*)dq + (int64_t)e * H * rbi;
+      const uint16_t* eds = ds ? ds + (int64_t)e * H * ngi : NULL;
+      const uint16_t* edb = db ? db + (int64_t)e * H * ngi : NULL;
+      float* hrow = h_out ? h_out + ((int64_t)i * kcap + s) * I : NULL;
+      oracle_expert_ffn(xf, eq, es, eb, edq, eds, edb, H, I, bits, gsz, hrow, o);
+      for (int h = 0; h < H; ++h) {
+        float c = ws * o[h];
+        y[h] = y[h] + c;
+      }
+    }
+  }
+  free(xf);
+  free(o);
+}
+
+/* round fp32 outputs to the activation dtype */
+void oracle_round_output(const float* y_f32, int64_t n, int dtype, uint16_t* y) {
+  for (int64_t i = 0; i < n; ++i) y[i] = oracle_float_to_half(y_f32[i], dtype);
+}
+
+/*
+ * The whole layer: route, then every token through its selected experts,
+ * combine and round.  idx/w: [T, kcap]; y: [T, H] activation dtype;
+ * y_f32 (may be NULL) the unrounded fp32 result.
+ */
+void oracle_layer_forward(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k,
+                          const void* guq, const uint16_t* gus, const uint16_t* gub, const void* dq,
+                          const uint16_t* ds, const uint16_t* db, int I, int bits, int gsz, uint16_t* y,
+                          float* y_f32, int32_t* idx, float* w, int32_t* k_used, float* h_mean) {
+  int ku = 0;
+  oracle_route(x, dtype, T, H, wr, E, k, idx, w, &ku, h_mean, NULL);
+  if (k_used) *k_used = ku;
+  int kcap = k > 0 ? k : 3;
+  int32_t* tokens = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  for (int t = 0; t < T; ++t) tokens[t] = t;
+  float* yf = y_f32 ? y_f32 : (float*)malloc(sizeof(float) * (size_t)T * H);
+  oracle_tokens_forward(x, dtype, H, tokens, T, idx, w, kcap, ku, guq, gus, gub, dq, ds, db, I, bits, gsz, yf, NULL);
+  oracle_round_output(yf, (int64_t)T * H, dtype, y);
+  if (!y_f32) free(yf);
+  free(tokens);
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test ties one oracle function to something other than itself: hand-worked
+values (tests/golden), closed forms, fp64 brute force, library routines on
+special cases, or invariants.  Together they are chosen so that a plausible
+slip (a dropped term, a wrong sign, a swapped operand, the wrong nibble, the
+wrong tie-break, the wrong logarithm) fails at least one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from conftest import golden_path
+from ref64 import dense_layer64, dequant64, entropy64, half64, rel_l2, select64, silu64
+
+U = 2.0 ** -24  # unit roundoff of fp32
+
+
+# ------------------------------------------------------------ rounding --
+
+def test_half_encode_matches_numpy_and_torch():
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * 3,
+        (rng.standard_normal(5000) * 1e-6).astype(np.float32),  # fp16 subnormals
+        np.float32([0.0, -0.0, 65504, 65519.99, 65520, 1e6, -1e6, 2 ** -24, 2 ** -25, 3 * 2 ** -26,
+                    1 + 2 ** -11, 1 + 3 * 2 ** -11, 1 + 2 ** -8, 1 + 3 * 2 ** -8]),
+    ]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        want16 = vals.astype(np.float16).view(np.uint16)
+    want_bf = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got16 = np.array([oracle.float_to_half(v, "f16") for v in vals], np.uint16)
+    gotbf = np.array([oracle.float_to_half(v, "bf16") for v in vals], np.uint16)
+    assert np.array_equal(got16, want16)
+    assert np.array_equal(gotbf, want_bf)
+
+
+def test_half_decode_matches_numpy():
+    allbits = np.arange(0, 65536, 7, dtype=np.uint16)
+    finite = np.isfinite(allbits.view(np.float16))
+    got = np.array([oracle.half_to_float(b, "f16") for b in allbits[finite]], np.float64)
+    assert np.array_equal(got, allbits[finite].view(np.float16).astype(np.float64))
+    got_bf = np.array([oracle.half_to_float(b, "bf16") for b in allbits[:2000]], np.float64)
+    assert np.array_equal(got_bf, half64(allbits[:2000], "bf16"))
+
+
+def test_round_output_matches_numpy():
+    y = (np.random.default_rng(1).standard_normal(4096) * 5).astype(np.float32)
+    assert np.array_equal(oracle.round_output(y, "f16"), y.astype(np.float16).view(np.uint16))
+    bf = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.round_output(y, "bf16"), bf)
+
+
+# ------------------------------------------------------------- dequant --
+
+def _read_dequant_cases():
+    cases, cur = [], None
+    for line in open(golden_path("dequant_groups.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        tag, *rest = line.split()
+        if tag == "case":
+            cur = dict(name=rest[0], bits=int(rest[1]), s=int(rest[2], 16), b=int(rest[3], 16))
+            cases.append(cur)
+        elif tag == "codes":
+            cur["codes"] = [int(v) for v in rest]
+        elif tag == "expect":
+            cur["expect"] = [float(v) for v in rest]
+    return cases
+
+
+@pytest.mark.parametrize("case", _read_dequant_cases(), ids=lambda c: c["name"])
+def test_dequant_golden(case):
+    codes = np.array(case["codes"], np.uint8)
+    if case["bits"] == 4:
+        q = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)  # even column -> low nibble
+    else:
+        q = codes
+    got = oracle.dequant_row(q, np.array([case["s"]], np.uint16), np.array([case["b"]], np.uint16), 64,
+                             case["bits"])
+    assert np.array_equal(got, np.array(case["expect"], np.float32))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_dequant_requantize_returns_same_codes(bits):
+    w = mi.quant_weights(77, 2, 2, 8, 256, bits)
+    deq = oracle.dequant(w)  # fp32
+    q2, s2, b2 = mi.quantize_rows(deq.reshape(-1, 256).astype(np.float64), bits)
+    assert np.array_equal(q2.reshape(w.q.shape), w.q)
+    assert np.array_equal(s2.reshape(w.scales.shape), w.scales)
+    assert np.array_equal(b2.reshape(w.biases.shape), w.biases)
+
+
+@pytest.mark.parametrize("bits", [4, 8, 16])
+def test_dequant_matches_fp64_statement(bits):
+    w = mi.quant_weights(5, 3, 2, 16, 192, bits)
+    got = oracle.dequant(w).astype(np.float64)
+    want = dequant64(w)
+    # two fp32 roundings of s*q + b
+    assert np.all(np.abs(got - want) <= 2 * U * (np.abs(want) + 1e-3))
+
+
+# -------------------------------------------------------------- router --
+
+def test_router_logits_within_higham_bound():
+    x = mi.normal_half(9, 0, 16 * 1024, 1.0, "f16").reshape(16, 1024)
+    wr = mi.normal_half(9, 1, 24 * 1024, 0.02, "f16").reshape(24, 1024)
+    got = oracle.router_logits(x, wr, "f16").astype(np.float64)
+    x64, w64 = half64(x, "f16"), half64(wr, "f16")
+    want = x64 @ w64.T
+    n = 1024
+    gamma = n * U / (1 - n * U)
+    bound = gamma * (np.abs(x64) @ np.abs(w64).T)
+    assert np.all(np.abs(got - want) <= bound)
+    assert np.max(np.abs(got - want)) > 0  # the bound is not vacuous
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_router_logits_exact_on_exact_inputs(dtype):
+    x, wr = mi.exact_router_inputs(3, 8, 2048, 16, dtype)
+    got = oracle.router_logits(x, wr, dtype)
+    want = half64(x, dtype) @ half64(wr, dtype).T
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def _read_router_worked():
+    d = {"wr": []}
+    for line in open(golden_path("router_worked.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        tag, *rest = line.split()
+        vals = [float(v) for v in rest]
+        if tag == "wr":
+            d["wr"].append(vals)
+        else:
+            d[tag] = vals
+    return d
+
+
+def test_router_worked_example():
+    d = _read_router_worked()
+    x = mi.round_half(np.array([d["x"]]), "f16")
+    wr = mi.round_half(np.array(d["wr"]), "f16")
+    idx, w, ku, _, logits = oracle.route(x, wr, "f16", 2, want_logits=True)
+    assert np.array_equal(logits[0], np.float32(d["logits"]))
+    assert idx[0].tolist() == [int(v) for v in d["idx"]]
+    assert np.allclose(w[0], d["w"], rtol=0, atol=2e-7)
+    assert ku == 2
+
+
+# ------------------------------------------------------------ selection --
+
+@pytest.mark.parametrize("E,k", [(8, 1), (8, 2), (32, 2), (32, 3), (64, 4), (64, 8), (256, 8)])
+def test_selection_brute_force(E, k):
+    rng = np.random.default_rng(E * 10 + k)
+    logits = (rng.standard_normal((64, E)) * 1.3).astype(np.float32)
+    # planted ties: duplicate some logits inside rows
+    logits[:16, 1] = logits[:16, 0]
+    logits[16:32, E - 1] = logits[16:32, 2]
+    idx, w = oracle.select_topk(logits, k)
+    for t in range(64):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))
+        assert idx[t].tolist() == order[:k]
+
+
+def test_selection_matches_torch_topk_without_ties():
+    rng = np.random.default_rng(5)
+    logits = rng.permutation(np.arange(64 * 64, dtype=np.float32)).reshape(64, 64) / 97.0
+    idx, _ = oracle.select_topk(logits, 4)
+    tv, ti = torch.topk(torch.softmax(torch.from_numpy(logits).double(), -1), 4, dim=-1)
+    assert np.array_equal(idx, ti.numpy().astype(np.int32))
+
+
+def test_ties_go_to_lower_index():
+    logits = np.zeros((3, 8), np.float32)
+    logits[1, [5, 2, 7]] = 1.0
+    logits[2, :] = [0, 3, 3, 1, 3, 0, 0, 3]
+    idx, w = oracle.select_topk(logits, 3)
+    assert idx.tolist() == [[0, 1, 2], [2, 5, 7], [1, 2, 4]]
+    assert np.all(w[0] == np.float32(1 / 3)) or np.allclose(w[0], 1 / 3, atol=1e-7)
+
+
+# -------------------------------------------------------------- weights --
+
+def test_weights_sum_to_one_and_closed_forms():
+    rng = np.random.default_rng(11)
+    for k in (1, 2, 3, 4, 8):
+        logits = (rng.standard_normal((256, 64)) * 2).astype(np.float32)
+        _, w = oracle.select_topk(logits, k)
+        s = w.astype(np.float64).sum(axis=1)
+        assert np.all(np.abs(s - 1) <= (k + 2) * 2 ** -23)
+        if k == 1:
+            assert np.all(w == 1.0)
+    # equal logits -> 1/k
+    _, w = oracle.select_topk(np.full((1, 16), 0.75, np.float32), 4)
+    assert np.allclose(w, 0.25, atol=1e-7)
+    # two experts: w1 = 1/(1 + e^(l2 - l1))
+    l = np.array([[0.3, 1.7, -2.0, -5.0]], np.float32)
+    idx, w = oracle.select_topk(l, 2)
+    assert idx[0].tolist() == [1, 0]
+    want = 1.0 / (1.0 + math.exp(float(l[0, 0]) - float(l[0, 1])))
+    assert abs(float(w[0, 0]) - want) < 3e-7
+    assert abs(float(w[0, 1]) - (1 - want)) < 3e-7
+
+
+def test_weights_match_fp64_renormalised_softmax():
+    rng = np.random.default_rng(12)
+    logits = (rng.standard_normal((128, 32)) * 1.5).astype(np.float32)
+    idx, w = oracle.select_topk(logits, 3)
+    i64, w64 = select64(logits.astype(np.float64), 3)
+    assert np.array_equal(idx, i64)
+    assert np.max(np.abs(w - w64)) < 1e-6
+
+
+# -------------------------------------------------------------- entropy --
+
+def _read_entropy_bands():
+    rows = []
+    for line in open(golden_path("entropy_bands.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        E, m, h, k = line.split()
+        rows.append((int(E), int(m), float(h), int(k)))
+    return rows
+
+
+@pytest.mark.parametrize("E,m,h,k", _read_entropy_bands())
+def test_entropy_closed_form_bands(E, m, h, k):
+    l = np.full((4, E), -40.0, np.float32)
+    l[:, :m] = 0.0
+    l[1] = np.roll(l[1], 3)
+    l += np.float32(1.25)  # a common shift changes nothing
+    tol = 4 * E * U * max(1.0, h) + 1e-6  # fp32 sums over E terms
+    assert abs(oracle.token_entropy(l[0]) - h) < tol
+    hm = oracle.batch_entropy(l)
+    assert abs(hm - h) < tol
+    assert oracle.entropy_k(hm) == k
+
+
+def test_entropy_thresholds_inclusive_as_printed():
+    assert oracle.entropy_k(np.nextafter(np.float32(1.2), np.float32(0))) == 1
+    assert oracle.entropy_k(1.2) == 2
+    assert oracle.entropy_k(np.nextafter(np.float32(2.5), np.float32(0))) == 2
+    assert oracle.entropy_k(2.5) == 3
+
+
+def test_entropy_matches_fp64_and_is_natural_log():
+    rng = np.random.default_rng(13)
+    l = (rng.standard_normal((64, 32)) * 1.7).astype(np.float32)
+    want = entropy64(l.astype(np.float64))
+    got = np.array([oracle.token_entropy(r) for r in l])
+    assert np.max(np.abs(got - want)) < 1e-5
+    # uniform distribution: ln E, not log2 E
+    assert abs(oracle.token_entropy(np.zeros(32, np.float32)) - math.log(32)) < 2e-6
+
+
+def test_entropy_route_truncates_to_k_used():
+    # logits with 3 dominant experts per token -> H = ln 3 < 1.2 -> k = 1
+    E, H = 8, 64
+    x = mi.round_half(np.eye(4, H) * 4.0, "f16")
+    wr64 = np.zeros((E, H))
+    for t in range(4):
+        for e in range(3):
+            wr64[(t + e) % E, t] = 10.0
+    wr = mi.round_half(wr64, "f16")
+    idx, w, ku, hm = oracle.route(x, wr, "f16", -1)
+    assert ku == 1 and abs(hm - math.log(3)) < 1e-5
+    assert np.all(idx[:, 1:] == -1) and np.all(w[:, 1:] == 0) and np.all(w[:, 0] == 1)
+
+
+# ----------------------------------------------------------------- sort --
+
+@pytest.mark.parametrize("T,kcap,ku,E", [(1, 4, 4, 64), (37, 2, 2, 8), (128, 3, 2, 32), (513, 4, 4, 64),
+                                         (64, 3, 1, 32), (16, 8, 8, 256)])
+def test_sort_pairs_is_stable_counting_sort(T, kcap, ku, E):
+    rng = np.random.default_rng(T + E)
+    idx = rng.integers(0, E, size=(T, kcap)).astype(np.int32)
+    idx[:, ku:] = -1
+    counts, offsets, perm, pos = oracle.sort_pairs(idx, ku, E)
+    pairs = [p for p in range(T * kcap) if p % kcap < ku]
+    want = sorted(pairs, key=lambda p: (idx.flat[p], p))  # Python's sort is stable
+    assert perm[:len(want)].tolist() == want
+    assert np.all(perm[len(want):] == -1)
+    assert counts.sum() == len(pairs)
+    assert np.array_equal(np.bincount(idx[:, :ku].ravel(), minlength=E), counts)
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
+    for i, p in enumerate(want):
+        assert pos[p] == i
+    assert all(pos[p] == -1 for p in range(T * kcap) if p % kcap >= ku)
+
+
+# ------------------------------------------------------------------ FFN --
+
+@pytest.mark.parametrize("bits", [4, 8, 16])
+def test_fused_gate_up_bit_identical_to_separate(bits):
+    inp = mi.make_inputs("tiny", bits=bits)
+    gu = oracle.fuse_gate_up(inp.gate, inp.up)
+    assert gu.q.shape[1] == 2 * inp.I
+    assert np.array_equal(gu.q[:, :inp.I], inp.gate.q) and np.array_equal(gu.q[:, inp.I:], inp.up.q)
+    x = half64(inp.x, "f16").astype(np.float32)
+    for e in range(inp.E):
+        for t in range(inp.T):
+            h1, o1 = oracle.expert_ffn(x[t], gu, inp.down, e)
+            h2, o2 = oracle.expert_ffn_unfused(x[t], inp.gate, inp.up, inp.down, e)
+            assert np.array_equal(h1.view(np.uint32), h2.view(np.uint32))
+            assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+def _read_layer_worked():
+    d = {}
+    for line in open(golden_path("layer_worked.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split()
+            d[k] = float(v)
+    return d
+
+
+def test_layer_worked_example():
+    d = _read_layer_worked()
+    H = I = 64
+
+    def w_const(N, K, bias):
+        q = np.zeros((1, N, K // 2), np.uint8)
+        s = np.full((1, N, K // 64), 0x3800, np.uint16)
+        b = np.full((1, N, K // 64), mi.round_half(np.array([bias]), "f16")[0], np.uint16)
+        return mi.Weights(q, s, b, 1, N, K, 4)
+
+    gate, up, down = w_const(I, H, 1 / 64), w_const(I, H, 2 / 64), w_const(H, I, 1 / 64)
+    gu = oracle.fuse_gate_up(gate, up)
+    x = mi.round_half(np.ones((1, H)), "f16")
+    wr = mi.round_half(np.ones((1, H)) * 0.01, "f16")
+    res = oracle.layer_forward(x, wr, "f16", 1, gu, down)
+    y, hvec = oracle.tokens_forward(x, "f16", [0], res["idx"], res["w"], 1, gu, down, want_h=True)
+    assert np.allclose(hvec[0, 0], d["h"], rtol=2e-7, atol=0)
+    assert np.all(res["y"].view(np.float16).astype(np.float64) == d["y"])
+    assert float(res["w"][0, 0]) == 1.0
+
+
+def test_single_expert_is_the_textbook_swiglu_mlp():
+    inp = mi.make_inputs("tiny", E=1, k=1, T=6)
+    gu = oracle.fuse_gate_up(inp.gate, inp.up)
+    res = oracle.layer_forward(inp.x, inp.wr, "f16", 1, gu, inp.down)
+    x = half64(inp.x, "f16")
+    Wg, Wu, Wd = dequant64(inp.gate)[0], dequant64(inp.up)[0], dequant64(inp.down)[0]
+    want = (silu64(x @ Wg.T) * (x @ Wu.T)) @ Wd.T
+    assert rel_l2(res["y_f32"], want) < 2e-6
+    assert np.all(res["w"] == 1.0)
+
+
+def test_all_experts_selected_is_the_dense_softmax_mixture():
+    inp = mi.make_inputs("tiny", k=8)
+    gu = oracle.fuse_gate_up(inp.gate, inp.up)
+    res = oracle.layer_forward(inp.x, inp.wr, "f16", 8, gu, inp.down)
+    x = half64(inp.x, "f16")
+    logits = x @ half64(inp.wr, "f16").T
+    p = np.exp(logits - logits.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    Wg, Wu, Wd = dequant64(inp.gate), dequant64(inp.up), dequant64(inp.down)
+    want = sum(p[:, e:e + 1] * ((silu64(x @ Wg[e].T) * (x @ Wu[e].T)) @ Wd[e].T) for e in range(inp.E))
+    assert rel_l2(res["y_f32"], want) < 2e-6
+
+
+# ---------------------------------------------------------------- layer --
+
+@pytest.mark.parametrize("kw", [
+    dict(name="tiny"),
+    dict(name="tiny", bits=8, dtype="bf16"),
+    dict(name="tiny", bits=16, T=9),
+    dict(name="tiny", k=3, E=16, T=7, H=192, I=320),
+    dict(name="batched_decode", T=16, H=256, E=8, I=192),
+    dict(name="prefill", T=24, H=128, E=16, I=128),
+    dict(name="entropy", T=8, H=256, E=8, I=128, bits=4),
+], ids=lambda kw: "-".join("%s%s" % (k, v) for k, v in kw.items()))
+def test_layer_matches_dense_fp64_brute_force(kw):
+    kw = dict(kw)
+    inp = mi.make_inputs(kw.pop("name"), **kw)
+    gu = oracle.fuse_gate_up(inp.gate, inp.up)
+    res = oracle.layer_forward(inp.x, inp.wr, inp.dtype, inp.k, gu, inp.down)
+    y64, idx64, w64 = dense_layer64(inp.x, inp.wr, inp.dtype, inp.k, inp.gate, inp.up, inp.down)
+    ku = res["k_used"]
+    assert np.array_equal(res["idx"][:, :ku], idx64)
+    assert np.max(np.abs(res["w"][:, :ku] - w64)) < 1e-6
+    assert rel_l2(res["y_f32"], y64) < 1e-5
+    # the rounded output is the fp32 result rounded once
+    assert np.array_equal(res["y"], oracle.round_output(res["y_f32"], inp.dtype))
+
+
+def test_token_permutation_equivariance_is_bitwise():
+    inp = mi.make_inputs("tiny", T=12, k=2)
+    gu = oracle.fuse_gate_up(inp.gate, inp.up)
+    res = oracle.layer_forward(inp.x, inp.wr, "f16", 2, gu, inp.down)
+    perm = np.random.default_rng(3).permutation(12)
+    res2 = oracle.layer_forward(np.ascontiguousarray(inp.x[perm]), inp.wr, "f16", 2, gu, inp.down)
+    assert np.array_equal(res2["y"], res["y"][perm])
+    assert np.array_equal(res2["idx"], res["idx"][perm])
+
+
+def test_tokens_forward_matches_layer_forward_rows():
+    inp = mi.make_inputs("tiny", T=10)
+    gu = oracle.fuse_gate_up(inp.gate, inp.up)
+    res = oracle.layer_forward(inp.x, inp.wr, "f16", 2, gu, inp.down)
+    sub = oracle.tokens_forward(inp.x, "f16", [7, 2, 9], res["idx"], res["w"], 2, gu, inp.down)
+    assert np.array_equal(sub, res["y_f32"][[7, 2, 9]])
