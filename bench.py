@@ -1,0 +1,306 @@
+"""Benchmark of one sparse MoE FFN layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one moe_layer_forward call (router, top-k, expert FFN over the
+selected experts, combine) on one batch of synthetic inputs already resident
+in HBM.  The default workload is single-token decode: hidden 4096, 64 experts,
+top-4, intermediate 11008, 4-bit group-64 weights, fp16 activations; each
+step takes the next token of a 256-token pool, so consecutive steps select
+different experts.  Prints one JSON line.
+
+Per-kernel durations come from HIP events recorded on the launch stream
+between the library's kernels inside the timed loop.  The dominant kernel's
+algorithmic bytes (or flops) per launch over its mean duration give the
+roofline fraction.  The CPU baseline times the oracle (plain C, all host
+cores) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; decode HBM TB/s % peak; prefill MFMA util %"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    "decode_b1": dict(recipe="decode_b1", pool=256, T=1,
+                      label="decode b1: 1 token/step, H=4096, E=64, top-4, I=11008, 4-bit g64 weights, fp16"),
+    "batched_decode": dict(recipe="batched_decode", pool=None, T=64,
+                           label="batched decode: 64 tokens, H=4096, E=32, top-2, I=2816, 8-bit g64, bf16, Zipf 1.1"),
+    "prefill": dict(recipe="prefill", pool=None, T=4096,
+                    label="prefill: 4096 tokens, H=4096, E=64, top-4, I=1408, 4-bit g64, bf16, Zipf 1.2"),
+    "entropy_q4": dict(recipe="entropy", pool=None, T=512, bits=4,
+                       label="entropy-adaptive: 512 tokens (segment k=3), H=4096, E=32, I=2816, 4-bit g64, fp16"),
+    "entropy_fp16": dict(recipe="entropy", pool=None, T=512, bits=16,
+                         label="entropy-adaptive: 512 tokens (segment k=3), H=4096, E=32, I=2816, fp16 weights"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes_per_row(K: int, bits: int) -> int:
+    return K * bits // 8 + (0 if bits == 16 else 2 * 2 * (K // 64))
+
+
+def algorithmic(name: str, kernel: str, *, T, H, E, I, bits, idx, k_used, kcap):
+    """Algorithmic HBM bytes and flops of one launch of `kernel`.
+
+    Bytes: every touched expert's weight rows (codes plus fp16 scale/bias)
+    read once, plus the activations read and the outputs written once.
+    """
+    sel = idx[:, :k_used]
+    touched = np.unique(sel)
+    pairs = sel.size
+    if kernel in ("gemv_gate_up_swiglu", "gemm_gate_up_swiglu"):
+        # decode GEMV reads each selected (token, expert) row block; MFMA reads each touched expert once
+        n_exp = pairs if kernel.startswith("gemv") else touched.size
+        b = n_exp * 2 * I * weight_bytes_per_row(H, bits) + T * H * 2 + pairs * I * 2
+        f = 2.0 * pairs * 2 * I * H
+    elif kernel in ("gemv_down_combine",):
+        b = pairs * H * weight_bytes_per_row(I, bits) + pairs * I * 2 + T * H * 2
+        f = 2.0 * pairs * H * I
+    elif kernel == "gemm_down":
+        b = touched.size * H * weight_bytes_per_row(I, bits) + pairs * I * 2 + pairs * H * 2
+        f = 2.0 * pairs * H * I
+    elif kernel == "router_logits":
+        b = E * H * 2 + T * H * 2 + T * E * 4
+        f = 2.0 * T * E * H
+    else:
+        b, f = 0, 0.0
+    return float(b), f
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if the summary in
+    profiles/ was taken on the current kernel source (matching hash)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data.get(workload, {}).get(kernel)
+        if not ent:
+            return None
+        from mixture_experts_router_amd import source_hash
+        if ent.get("source_hash") != source_hash():
+            return None
+        return float(ent["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode_b1", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the layer is benchmarked on one device's share "
+              "(multi-GPU sharding is a design note, not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_router_amd as moe
+    import moe_inputs as mi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    moe.lib()  # fails loudly if the HIP library is missing
+    wl = WORKLOADS[args.workload]
+    recipe = wl["recipe"]
+    mi.set_threads(min(os.cpu_count() or 1, 16))
+
+    t0 = time.time()
+    kw = {}
+    if "bits" in wl:
+        kw["bits"] = wl["bits"]
+    if recipe == "entropy":
+        kw["segment"] = 2
+    T_pool = wl["pool"] or wl["T"]
+    inp = mi.make_inputs(recipe, T=T_pool, **kw)
+    log("generated %s inputs in %.1fs" % (args.workload, time.time() - t0))
+    H, E, I, k, bits = inp.H, inp.E, inp.I, inp.k, inp.bits
+    dt = torch.float16 if inp.dtype == "f16" else torch.bfloat16
+
+    def dev_bits(a, dtype):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(dtype).cuda()
+
+    def dev_w(w):
+        if w.bits == 16:
+            return moe.Weights(dev_bits(w.q, torch.float16), None, None, w.E, w.N, w.K, 16)
+        return moe.Weights(torch.from_numpy(w.q).cuda(), dev_bits(w.scales, torch.float16),
+                           dev_bits(w.biases, torch.float16), w.E, w.N, w.K, w.bits)
+
+    x_pool = dev_bits(inp.x, dt)
+    wr = dev_bits(inp.wr, dt)
+    gate, up = dev_w(inp.gate), dev_w(inp.up)
+    gate_up = moe.fuse_gate_up(gate, up)  # the caller then frees the separate tensors
+    del gate, up
+    down = dev_w(inp.down)
+    torch.cuda.synchronize()
+
+    T = wl["T"]
+    kcap = inp.kcap
+    ws = torch.empty(moe.layer_workspace_size(T, H, E, k, I, 0), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, H), dtype=dt, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def x_of(step):
+        if wl["pool"]:
+            i = step % wl["pool"]
+            return x_pool[i:i + 1]
+        return x_pool
+
+    # discover the kernel plan
+    moe.layer_forward(x_of(0), wr, k, down, gate_up=gate_up, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    plan = moe.last_plan()
+    nk = len(plan)
+
+    for i in range(args.warmup):
+        moe.layer_forward(x_of(i), wr, k, down, gate_up=gate_up, out=y, workspace=ws)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
+    for evs in events:  # create the underlying HIP events
+        for e in evs:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    # ---- timed region
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        moe.debug_set_events(events[i])
+        moe.layer_forward(x_of(args.warmup + i), wr, k, down, gate_up=gate_up, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    moe.debug_set_events(None)
+
+    elapsed = t_end - t_start
+    ms_per_step = elapsed * 1e3 / K
+    value = K * T / elapsed
+    per_kernel = np.zeros(nk)
+    for evs in events:
+        for j in range(nk):
+            per_kernel[j] += evs[j].elapsed_time(evs[j + 1])
+    per_kernel_us = per_kernel / K * 1e3
+    gpu_step_us = float(sum(per_kernel_us))
+    log("plan:", ", ".join("%s %.2fus" % (n, t) for n, t in zip(plan, per_kernel_us)))
+    log("step %.2f us wall, %.2f us between first and last event" % (ms_per_step * 1e3, gpu_step_us))
+
+    # ---- roofline of the dominant kernel
+    j = int(np.argmax(per_kernel_us))
+    kern = plan[j]
+    # routing of a representative step (decode: over the pool; averaged bytes)
+    r = moe.route(x_pool, wr, k)
+    torch.cuda.synchronize()
+    idx_all = r["idx"].cpu().numpy()
+    ku = int(r["k_used"].item())
+    if wl["pool"]:
+        bs, fs = [], []
+        for s in range(min(wl["pool"], K)):
+            b_, f_ = algorithmic(args.workload, kern, T=1, H=H, E=E, I=I, bits=bits, idx=idx_all[s:s + 1],
+                                 k_used=ku, kcap=kcap)
+            bs.append(b_)
+            fs.append(f_)
+        alg_b, alg_f = float(np.mean(bs)), float(np.mean(fs))
+    else:
+        alg_b, alg_f = algorithmic(args.workload, kern, T=T, H=H, E=E, I=I, bits=bits, idx=idx_all, k_used=ku,
+                                   kcap=kcap)
+    dur_s = per_kernel_us[j] * 1e-6
+    gbs = alg_b / dur_s / 1e9
+    tflops = alg_f / dur_s / 1e12
+    if gbs / HBM_PEAK_GBS >= tflops / MFMA_F16_PEAK_TFLOPS:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = kern
+    roof["mean_launch_us"] = round(float(per_kernel_us[j]), 3)
+    roof["algorithmic_bytes"] = int(alg_b)
+    roof["algorithmic_flops"] = int(alg_f)
+    roof["traffic"] = traffic_from_profiles(kern, args.workload)
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        gu_np = oracle.fuse_gate_up(inp.gate, inp.up)
+        cores = oracle.num_threads()
+        if wl["pool"]:
+            def run(n):
+                t = time.perf_counter()
+                oracle.layer_forward(np.ascontiguousarray(inp.x[:n]), inp.wr, inp.dtype, k, gu_np, inp.down)
+                return time.perf_counter() - t
+            n0 = 4
+            t_probe = run(n0)
+            n = int(max(n0, min(wl["pool"], args.cpu_seconds / max(t_probe / n0, 1e-6))))
+            t_run = run(n)
+            cpu = {"value": round(n / t_run, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                   "sample": "%d single tokens of the decode pool (each: route + 4 experts), %.1fs" % (n, t_run)}
+        else:
+            idx_o, w_o, ku_o, _ = oracle.route(inp.x, inp.wr, inp.dtype, k)
+            rng = np.random.default_rng(0)
+            t = time.perf_counter()
+            oracle.tokens_forward(inp.x, inp.dtype, [0], idx_o, w_o, ku_o, gu_np, inp.down)
+            per_tok = time.perf_counter() - t
+            n = int(max(2, min(T, args.cpu_seconds / max(per_tok, 1e-6))))
+            toks = np.sort(rng.choice(T, n, replace=False))
+            t = time.perf_counter()
+            oracle.route(inp.x, inp.wr, inp.dtype, k)
+            t_route = time.perf_counter() - t
+            t = time.perf_counter()
+            oracle.tokens_forward(inp.x, inp.dtype, toks, idx_o, w_o, ku_o, gu_np, inp.down)
+            t_tok = time.perf_counter() - t
+            # whole-batch rate: routing of all T tokens plus T token FFNs at the sampled per-token cost
+            total = t_route + t_tok / n * T
+            cpu = {"value": round(T / total, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                   "sample": "routing of all %d tokens (%.1fs) + expert FFN of %d sampled tokens (%.1fs), "
+                             "scaled to the batch" % (T, t_route, n, t_tok)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl["label"], "tokens_per_step": T, "hidden": H, "experts": E, "top_k": k,
+                   "intermediate": I, "weight_bits": bits, "activations": inp.dtype,
+                   "kernels_per_step": nk, "plan": plan,
+                   "per_kernel_us": [round(float(v), 3) for v in per_kernel_us]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

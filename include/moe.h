@@ -1,0 +1,218 @@
+/*
+ * moe.h — C ABI of one sparse Mixture-of-Experts FFN layer on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer, in the order it runs:
+ *   1. router projection  logits[t, e] = sum_h x[t, h] * Wr[e, h]   (fp32 accumulation)
+ *   2. selection          the k largest logits per token, larger logit first and
+ *                         the lower expert index first among equal logits; the
+ *                         weights are the softmax probabilities of the selected
+ *                         experts renormalised to sum to one
+ *                         (page "Qwen3.5 Block在llama.cpp中的映射与优化原理",
+ *                         section 4.1: linear -> softmax -> top-k)
+ *      or the entropy-adaptive variant: k = 1, 2 or 3 from the mean Shannon
+ *                         entropy H (nats) of the call's routing distributions,
+ *                         k = 1 if H < 1.2, 2 if 1.2 <= H < 2.5, else 3
+ *                         (page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析",
+ *                         section 2.2, Entropy-Aware Routing)
+ *   3. token->expert sort  (token, slot) pairs grouped by expert, stable
+ *   4. gate+up projection  over affine group-quantised weights, w = scale*q + bias,
+ *                         gate and up concatenated along the output axis
+ *                         [E, 2*inter, hidden], gate rows first
+ *                         (oMLX gate/up fusion page, "融合原理" and steps 3-4)
+ *   5. SwiGLU              h = silu(g) * u,  silu(g) = g / (1 + exp(-g))
+ *   6. down projection     o = W_down . h
+ *   7. combine             y[t] = sum over slots s of w[t, s] * o[t, s], in slot
+ *                         order, rounded to the activation dtype (page
+ *                         "Qwen3.5 Block…", section 4.2, the weighted sum after
+ *                         the expert FFN)
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer unless stated otherwise.  The caller
+ *     owns and allocates every buffer, including the workspace.  The library
+ *     never allocates or frees device memory and never synchronises: work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
+ *     asynchronously.  Faults during execution surface at the caller's next
+ *     synchronisation, as with any asynchronous library.
+ *   - Arguments are validated completely on the host before anything is
+ *     enqueued; an error return means nothing was enqueued.  Validation makes
+ *     no HIP call, so it can be exercised without a GPU.
+ *   - Layouts are row-major.  Activations and router weights share one dtype.
+ *   - Calls on different streams are independent; the library keeps no
+ *     mutable state besides a once-per-device cache of device properties and
+ *     the optional per-thread profiling hooks at the end of this header.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,         /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,        /* a size is out of range or inconsistent */
+  MOE_ERR_DTYPE = -3,        /* unknown activation dtype */
+  MOE_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned */
+  MOE_ERR_K = -5,            /* k out of range */
+  MOE_ERR_QUANT = -6,        /* unsupported bits / group size / scale presence */
+  MOE_ERR_INCOMPATIBLE = -7, /* gate and up cannot be fused (different bits, group
+                                size, shape or scale presence); keep them separate */
+  MOE_ERR_WORKSPACE = -8,    /* workspace NULL or smaller than required */
+  MOE_ERR_DEVICE = -9,       /* no usable gfx950 device is current */
+  MOE_ERR_HIP = -10,         /* a HIP launch or query failed */
+  MOE_ERR_INTERNAL = -11     /* unexpected internal error */
+} moe_status;
+
+typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
+
+/* k argument value selecting the entropy-adaptive top-1/2/3 routing */
+#define MOE_K_ENTROPY (-1)
+/* slots kept per token in entropy-adaptive mode */
+#define MOE_K_ENTROPY_CAP 3
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_K 8
+
+/*
+ * One expert weight tensor, logically [E, N, K]: N output rows per expert,
+ * K input columns.  Row n of expert e starts at row index e*expert_stride_rows + n
+ * (expert_stride_rows == N for a dense tensor; 2*inter for the gate or up half
+ * of a fused gate_up tensor, with `q`/`scales`/`biases` pointing at its first row).
+ *
+ *   bits == 4:  q      uint8 [rows, K/2], two codes per byte, the even column
+ *                      in the low nibble; codes are unsigned 0..15
+ *   bits == 8:  q      uint8 [rows, K], codes 0..255
+ *   bits 4, 8:  scales fp16 [rows, K/group_size], biases fp16 [rows, K/group_size];
+ *               w[n, k] = scales[n, k/gs] * q[n, k] + biases[n, k/gs]
+ *               (affine group quantisation, one scale/bias per row and group)
+ *   bits == 16: q      fp16 [rows, K] weights; scales and biases must be NULL
+ *
+ * group_size must be 64.  K must be a multiple of 64.  q, scales and biases
+ * must be 16-byte aligned.
+ */
+typedef struct {
+  const void* q;
+  const void* scales;
+  const void* biases;
+  int32_t E;
+  int32_t N;
+  int32_t K;
+  int32_t bits;
+  int32_t group_size;
+  int64_t expert_stride_rows;
+} moe_weights;
+
+/*
+ * Optional copies of intermediates (each pointer may be NULL).  They only copy;
+ * they never change results.  kcap = k, or MOE_K_ENTROPY_CAP in entropy mode.
+ *   logits     fp32  [T, E]         router logits
+ *   topk_idx   int32 [T, kcap]      selected experts (slots >= k_used hold -1)
+ *   topk_w     fp32  [T, kcap]      routing weights (slots >= k_used hold 0)
+ *   k_used     int32 [1]            k actually used
+ *   entropy    fp32  [1]            batch entropy (entropy mode; 0 otherwise)
+ *   counts     int32 [E]            pairs routed to each expert
+ *   offsets    int32 [E+1]          exclusive prefix sum of counts
+ *   perm       int32 [T*kcap]       pair ids t*kcap+s grouped by expert, ascending
+ *                                   within an expert; entries past the last pair -1
+ *   h          fp16  [T*kcap, inter] SwiGLU output of pair t*kcap+s (unused slots
+ *                                   untouched)
+ */
+typedef struct {
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* k_used;
+  float* entropy;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  void* h;
+} moe_taps;
+
+/* flags of moe_layer_forward */
+#define MOE_FLAG_UNFUSED 0x1u    /* separate gate and up projections, then SwiGLU
+                                    (a fused tensor is split into two views);
+                                    results are bit-identical to the fused path */
+#define MOE_FLAG_FORCE_GEMV 0x2u /* decode path (grouped GEMV) where it applies */
+#define MOE_FLAG_FORCE_MFMA 0x4u /* batched path (sorted MFMA grouped GEMM) */
+
+/*
+ * Router: logits, then top-k selection and renormalised softmax weights.
+ *   x         [T, H] activations (dt); router_w [E, H] (dt)
+ *   k         1..min(E, 8), or MOE_K_ENTROPY (needs E >= 3; kcap = 3)
+ *   topk_idx  int32 [T, kcap] out; topk_w fp32 [T, kcap] out
+ *   k_used    int32 [1] out (may be NULL); entropy fp32 [1] out (may be NULL)
+ *   logits_out fp32 [T, E] out (may be NULL)
+ *   ws        workspace of at least moe_route_workspace_size(T, E, k) bytes
+ * H % 64 == 0, 1 <= E <= 256.  T == 0 is a no-op returning MOE_OK.
+ */
+size_t moe_route_workspace_size(int32_t T, int32_t E, int32_t k);
+moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E, int32_t k,
+                     int32_t* topk_idx, float* topk_w, int32_t* k_used, float* entropy, float* logits_out, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * Selection only, from caller-provided fp32 logits [T, E] (same rules and
+ * outputs as moe_route).  Lets two callers that hold identical logits check
+ * that they select identical experts.
+ */
+moe_status moe_topk_from_logits(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                                float* topk_w, int32_t* k_used, float* entropy, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
+ * The whole layer.
+ *   x         [T, H] activations (dt); router_w [E, H] (dt); y [T, H] out (dt)
+ *   gate_up   fused tensor, N = 2*inter, K = H (gate rows first), or NULL to use
+ *             `gate` and `up` (each N = inter, K = H).  With gate_up given,
+ *             gate/up are ignored.
+ *   down      N = H, K = inter
+ *   flags     MOE_FLAG_*; taps may be NULL
+ *   ws        workspace of at least moe_layer_workspace_size(...) bytes, 256-byte
+ *             aligned
+ * Limits: H % 64 == 0, inter % 64 == 0, 1 <= E <= 256, k as for moe_route, all
+ * weight tensors with the same bits and E.  T == 0 is a no-op.
+ * Returns MOE_ERR_INCOMPATIBLE when separate gate/up tensors differ in bits,
+ * shape or scale presence.
+ */
+size_t moe_layer_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, int32_t inter, uint32_t flags);
+moe_status moe_layer_forward(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E,
+                             int32_t k, const moe_weights* gate_up, const moe_weights* gate, const moe_weights* up,
+                             const moe_weights* down, void* y, uint32_t flags, const moe_taps* taps, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * Pack separate gate [E, inter, K] and up [E, inter, K] into a fused tensor
+ * [E, 2*inter, K], gate rows first, for weights, scales and biases alike
+ * (oMLX page, step 3).  q_out/s_out/b_out are caller-owned with the fused
+ * sizes (s_out/b_out NULL when bits == 16).  The caller may free the sources
+ * afterwards, so resident bytes never double.  Returns MOE_ERR_INCOMPATIBLE
+ * (and enqueues nothing) when the two tensors cannot be fused: different
+ * bits, group size, shape or scale presence (oMLX page, step 2).
+ */
+moe_status moe_fuse_gate_up(const moe_weights* gate, const moe_weights* up, void* q_out, void* s_out, void* b_out,
+                            void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/*
+ * Profiling hooks (per calling thread).  When `events` is non-NULL, every
+ * later entry point on this thread records events[0] on its stream before its
+ * first kernel and events[i+1] after its i-th kernel, for i + 1 < n.
+ * `events` are caller-created hipEvent_t handles.  Pass NULL to stop.
+ * moe_debug_last_plan writes the names of the kernels the last call on this
+ * thread launched, comma-separated, into buf (host memory).
+ */
+void moe_debug_set_events(void* const* events, int32_t n);
+int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

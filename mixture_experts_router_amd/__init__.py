@@ -1,0 +1,297 @@
+"""Python binding of the MI355X MoE-layer library (libmoe_amd.so).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  The names
+mirror the C ABI in include/moe.h:
+
+    route, topk_from_logits, layer_forward, fuse_gate_up,
+    layer_workspace_size, route_workspace_size
+
+If the library is not built this module raises on first use; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_amd.so")
+
+MOE_F16, MOE_BF16 = 1, 2
+MOE_K_ENTROPY = -1
+MOE_K_ENTROPY_CAP = 3
+FLAG_UNFUSED, FLAG_FORCE_GEMV, FLAG_FORCE_MFMA = 0x1, 0x2, 0x4
+
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE", -4: "MOE_ERR_ALIGN",
+          -5: "MOE_ERR_K", -6: "MOE_ERR_QUANT", -7: "MOE_ERR_INCOMPATIBLE", -8: "MOE_ERR_WORKSPACE",
+          -9: "MOE_ERR_DEVICE", -10: "MOE_ERR_HIP", -11: "MOE_ERR_INTERNAL"}
+
+EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_topk_from_logits", "moe_layer_workspace_size",
+           "moe_layer_forward", "moe_fuse_gate_up", "moe_status_string", "moe_debug_set_events",
+           "moe_debug_last_plan")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__("%s failed: %s (%s)" % (what, self.name, _status_text(status)))
+
+
+class CWeights(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("expert_stride_rows", ctypes.c_int64)]
+
+
+class CTaps(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("logits", "topk_idx", "topk_w", "k_used", "entropy", "counts", "offsets", "perm", "h")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_amd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libmoe_amd.so is not built; run `python -m mixture_experts_router_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    u32 = ctypes.c_uint32
+    L.moe_route_workspace_size.argtypes = [i32, i32, i32]
+    L.moe_route_workspace_size.restype = sz
+    L.moe_route.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route.restype = i32
+    L.moe_topk_from_logits.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_topk_from_logits.restype = i32
+    L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, u32]
+    L.moe_layer_workspace_size.restype = sz
+    L.moe_layer_forward.argtypes = [vp, i32, i32, i32, vp, i32, i32, ctypes.POINTER(CWeights),
+                                    ctypes.POINTER(CWeights), ctypes.POINTER(CWeights), ctypes.POINTER(CWeights),
+                                    vp, u32, ctypes.POINTER(CTaps), vp, sz, vp]
+    L.moe_layer_forward.restype = i32
+    L.moe_fuse_gate_up.argtypes = [ctypes.POINTER(CWeights), ctypes.POINTER(CWeights), vp, vp, vp, vp]
+    L.moe_fuse_gate_up.restype = i32
+    L.moe_status_string.argtypes = [i32]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_debug_set_events.argtypes = [vp, i32]
+    L.moe_debug_set_events.restype = None
+    L.moe_debug_last_plan.argtypes = [ctypes.c_char_p, sz]
+    L.moe_debug_last_plan.restype = i32
+    _lib = L
+    return L
+
+
+def _status_text(s: int) -> str:
+    try:
+        return lib().moe_status_string(s).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise MoeError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return MOE_F16
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError("activations must be float16 or bfloat16, got %s" % t.dtype)
+
+
+@dataclasses.dataclass
+class Weights:
+    """Device weight tensor [E, N, K] in the library's layout (see include/moe.h).
+
+    bits 4: q uint8 [E, N, K/2]; bits 8: q uint8 [E, N, K]; bits 16: q float16
+    [E, N, K].  scales/biases float16 [E, N, K/64] (None for bits 16).
+    ``row_offset``/``stride`` describe a view (the gate or up half of a fused
+    tensor): rows start ``row_offset`` rows in, experts are ``stride`` rows apart.
+    """
+
+    q: torch.Tensor
+    scales: Optional[torch.Tensor]
+    biases: Optional[torch.Tensor]
+    E: int
+    N: int
+    K: int
+    bits: int
+    group_size: int = 64
+    stride: Optional[int] = None
+    row_offset: int = 0
+
+    def c(self) -> CWeights:
+        stride = self.N if self.stride is None else self.stride
+        rb = self.K * self.bits // 8
+        ng = self.K // self.group_size
+        q = self.q.data_ptr() + self.row_offset * rb
+        s = None if self.scales is None else self.scales.data_ptr() + self.row_offset * ng * 2
+        b = None if self.biases is None else self.biases.data_ptr() + self.row_offset * ng * 2
+        return CWeights(q, s, b, self.E, self.N, self.K, self.bits, self.group_size, stride)
+
+    def split_gate_up(self):
+        """(gate, up) views of a fused [E, 2I, K] tensor, gate rows first."""
+        I = self.N // 2
+        g = dataclasses.replace(self, N=I, stride=self.N, row_offset=0)
+        u = dataclasses.replace(self, N=I, stride=self.N, row_offset=I)
+        return g, u
+
+
+def route_workspace_size(T: int, E: int, k: int) -> int:
+    return int(lib().moe_route_workspace_size(T, E, k))
+
+
+def layer_workspace_size(T: int, H: int, E: int, k: int, inter: int, flags: int = 0) -> int:
+    return int(lib().moe_layer_workspace_size(T, H, E, k, inter, flags))
+
+
+def _kcap(k: int) -> int:
+    return k if k > 0 else MOE_K_ENTROPY_CAP
+
+
+def route(x: torch.Tensor, router_w: torch.Tensor, k: int, want_logits: bool = False, stream=None):
+    """Router + selection.  Returns dict(idx [T,kcap] int32, w [T,kcap] fp32,
+    k_used [1] int32, entropy [1] fp32[, logits [T,E] fp32])."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    dev = x.device
+    kc = _kcap(k)
+    idx = torch.empty((T, kc), dtype=torch.int32, device=dev)
+    w = torch.empty((T, kc), dtype=torch.float32, device=dev)
+    ku = torch.zeros(1, dtype=torch.int32, device=dev)
+    ent = torch.zeros(1, dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    ws = None
+    if logits is None:
+        ws = torch.empty(max(route_workspace_size(T, E, k), 256), dtype=torch.uint8, device=dev)
+    st = lib().moe_route(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k, _ptr(idx), _ptr(w), _ptr(ku),
+                         _ptr(ent), _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "moe_route")
+    out = dict(idx=idx, w=w, k_used=ku, entropy=ent)
+    if logits is not None:
+        out["logits"] = logits
+    return out
+
+
+def topk_from_logits(logits: torch.Tensor, k: int, stream=None):
+    T, E = logits.shape
+    dev = logits.device
+    kc = _kcap(k)
+    idx = torch.empty((T, kc), dtype=torch.int32, device=dev)
+    w = torch.empty((T, kc), dtype=torch.float32, device=dev)
+    ku = torch.zeros(1, dtype=torch.int32, device=dev)
+    ent = torch.zeros(1, dtype=torch.float32, device=dev)
+    st = lib().moe_topk_from_logits(_ptr(logits.contiguous()), T, E, k, _ptr(idx), _ptr(w), _ptr(ku), _ptr(ent),
+                                    None, 0, _stream(stream))
+    _check(st, "moe_topk_from_logits")
+    return dict(idx=idx, w=w, k_used=ku, entropy=ent)
+
+
+TAP_NAMES = ("logits", "topk_idx", "topk_w", "k_used", "entropy", "counts", "offsets", "perm", "h")
+
+
+def make_taps(T: int, E: int, k: int, inter: int, device, names: Sequence[str] = TAP_NAMES):
+    """Allocate tap buffers (logits, routing, sort results, SwiGLU rows)."""
+    kc = _kcap(k)
+    P = T * kc
+    spec = dict(logits=((T, E), torch.float32), topk_idx=((T, kc), torch.int32), topk_w=((T, kc), torch.float32),
+                k_used=((1,), torch.int32), entropy=((1,), torch.float32), counts=((E,), torch.int32),
+                offsets=((E + 1,), torch.int32), perm=((P,), torch.int32), h=((P, inter), torch.float16))
+    return {n: torch.zeros(spec[n][0], dtype=spec[n][1], device=device) for n in names}
+
+
+def layer_forward(x: torch.Tensor, router_w: torch.Tensor, k: int, down: Weights, gate_up: Optional[Weights] = None,
+                  gate: Optional[Weights] = None, up: Optional[Weights] = None, flags: int = 0,
+                  taps: Optional[dict] = None, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The whole layer: y [T, H] in the activation dtype."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    inter = down.K
+    y = torch.empty_like(x) if out is None else out
+    need = layer_workspace_size(T, H, E, k, inter, flags)
+    ws = workspace
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    ctaps = None
+    if taps:
+        ctaps = CTaps(*[(taps[n].data_ptr() if n in taps and taps[n] is not None else None) for n in
+                        ("logits", "topk_idx", "topk_w", "k_used", "entropy", "counts", "offsets", "perm", "h")])
+    cgu = gate_up.c() if gate_up is not None else None
+    cg = gate.c() if gate is not None else None
+    cu = up.c() if up is not None else None
+    cd = down.c()
+    st = lib().moe_layer_forward(
+        _ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k,
+        ctypes.byref(cgu) if cgu is not None else None, ctypes.byref(cg) if cg is not None else None,
+        ctypes.byref(cu) if cu is not None else None, ctypes.byref(cd), _ptr(y), flags,
+        ctypes.byref(ctaps) if ctaps is not None else None, _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "moe_layer_forward")
+    return y
+
+
+def fuse_gate_up(gate: Weights, up: Weights, stream=None) -> Weights:
+    """Pack gate [E, I, K] and up [E, I, K] into a new fused [E, 2I, K] tensor."""
+    E, I, K, bits = gate.E, gate.N, gate.K, gate.bits
+    dev = gate.q.device
+    qshape = (E, 2 * I) + tuple(gate.q.shape[2:])
+    q = torch.empty(qshape, dtype=gate.q.dtype, device=dev)
+    s = b = None
+    if gate.scales is not None:
+        s = torch.empty((E, 2 * I, K // gate.group_size), dtype=torch.float16, device=dev)
+        b = torch.empty_like(s)
+    cg, cu = gate.c(), up.c()
+    st = lib().moe_fuse_gate_up(ctypes.byref(cg), ctypes.byref(cu), _ptr(q), _ptr(s), _ptr(b), _stream(stream))
+    _check(st, "moe_fuse_gate_up")
+    return Weights(q, s, b, E, 2 * I, K, bits, gate.group_size)
+
+
+def debug_set_events(events: Optional[Sequence]) -> None:
+    """Record the given torch.cuda.Events around each kernel of later calls on this thread."""
+    if not events:
+        lib().moe_debug_set_events(None, 0)
+        debug_set_events._keep = None
+        return
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    debug_set_events._keep = arr  # keep the array alive while the library holds it
+    lib().moe_debug_set_events(ctypes.cast(arr, ctypes.c_void_p), len(events))
+
+
+def source_hash() -> str:
+    """sha256 over the library's sources (identifies which kernels a profile measured)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(_HERE, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def last_plan() -> list:
+    buf = ctypes.create_string_buffer(1024)
+    lib().moe_debug_last_plan(buf, 1024)
+    s = buf.value.decode()
+    return s.split(",") if s else []

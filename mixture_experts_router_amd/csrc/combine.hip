@@ -1,0 +1,101 @@
+// Small element-wise kernels: the routing-weighted combine, the standalone
+// SwiGLU of the unfused path, and copies for the optional taps.
+//
+// Combine: y[t, :] = sum_{s < k} w[t, s] * o[t, s, :], summed in slot order in
+// fp32 and rounded once to the activation dtype (page "Qwen3.5 Block在llama.cpp
+// 中的映射与优化原理", section 4.2: the routing weight multiplies each selected
+// expert's output after its FFN).  One thread owns 8 consecutive output
+// elements, so no atomics are needed and the result is deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ wts,
+                                                      const int32_t* __restrict__ k_used, int k_static, int kcap,
+                                                      int H, void* __restrict__ y, int act) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c >= H) return;
+  const int ku = k_used ? *k_used : k_static;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int s = 0; s < ku; ++s) {
+    const size_t p = (size_t)t * kcap + s;
+    const float ws = wts[p];
+    const u32x4 v = load16(o + (size_t)pos[p] * H + c);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = ws * f16_bits_to_f32(w4[i] & 0xFFFFu);
+      const float hi = ws * f16_bits_to_f32(w4[i] >> 16);
+      acc[2 * i] = acc[2 * i] + lo;
+      acc[2 * i + 1] = acc[2 * i + 1] + hi;
+    }
+  }
+  u32x4 out;
+  uint32_t* ow = (uint32_t*)&out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    ow[i] = (uint32_t)f32_to_act_bits(acc[2 * i], act) | ((uint32_t)f32_to_act_bits(acc[2 * i + 1], act) << 16);
+  *(u32x4*)((uint16_t*)y + (size_t)t * H + c) = out;
+}
+
+hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wts, const int32_t* k_used_dev,
+                          int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st) {
+  dim3 grid((H / 8 + 255) / 256, T);
+  combine_kernel<<<grid, 256, 0, st>>>(o, pos, wts, k_used_dev, k_static, kcap, H, y, act);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g, const float* __restrict__ u,
+                                                     uint16_t* __restrict__ h, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) h[i] = f32_to_f16_bits(swiglu(g[i], u[i]));
+}
+
+hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, hipStream_t st) {
+  const int64_t n = rows * I;
+  swiglu_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, u, h, n);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ src,
+                                                          const int32_t* __restrict__ pos, int I,
+                                                          uint16_t* __restrict__ out, int kcap,
+                                                          const int32_t* __restrict__ k_used, int k_static) {
+  const int64_t p = blockIdx.y;
+  int64_t r;
+  if (pos) {
+    r = pos[p];
+  } else {
+    const int ku = k_used ? *k_used : k_static;
+    r = (int)(p % kcap) < ku ? p : -1;
+  }
+  if (r < 0) return;
+  for (int c = (blockIdx.x * 256 + threadIdx.x) * 8; c < I; c += gridDim.x * 256 * 8)
+    *(u32x4*)(out + p * I + c) = load16(src + (size_t)r * I + c);
+}
+
+hipError_t launch_gather_rows(const uint16_t* src, const int32_t* pos, int64_t P, int I, uint16_t* out, int kcap,
+                              const int32_t* k_used_dev, int k_static, hipStream_t st) {
+  dim3 grid((I / 8 + 255) / 256, (unsigned)P);
+  gather_rows_kernel<<<grid, 256, 0, st>>>(src, pos, I, out, kcap, k_used_dev, k_static);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void copy_words_kernel(const uint32_t* __restrict__ s, uint32_t* __restrict__ d,
+                                                         int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) d[i] = s[i];
+}
+
+hipError_t launch_copy_words(const void* src, void* dst, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  copy_words_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((const uint32_t*)src, (uint32_t*)dst, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

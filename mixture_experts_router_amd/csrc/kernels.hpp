@@ -1,0 +1,73 @@
+// Launch functions of the layer's HIP kernels (internal; called by moe_abi.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_MAX_K_DEV 8
+#define MOE_K_ENTROPY_CAP_DEV 3
+
+namespace moe {
+
+// One expert weight view: row n of expert e starts at q + (e*stride + n)*row_bytes.
+struct WView {
+  const uint8_t* q;
+  const uint16_t* s;  // fp16 scales [rows, K/64] (NULL for bits 16)
+  const uint16_t* b;  // fp16 biases
+  int64_t stride;     // rows between experts
+};
+
+// ---------------------------------------------------------------- router
+hipError_t launch_router_logits(const void* x, const void* wr, float* logits, int T, int H, int E, int act,
+                                hipStream_t st);
+// k > 0: static; k < 0: entropy-adaptive (kcap = 3)
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* k_used,
+                       float* entropy, hipStream_t st);
+
+// ------------------------------------------------------------------ sort
+// k_used_dev may be NULL (then k_static is used)
+hipError_t launch_sort_pairs(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st);
+
+// ------------------------------------------------- decode (grouped GEMV)
+// chunks of 16 bytes per lane needed for a row of K weights
+int gemv_lanes_chunks(int K, int bits);
+// fused=true: h[p, j] = fp16(swiglu(gate_j . x, up_j . x)) for j < I
+// fused=false: out32[p, n] = w0_n . x for n < N
+hipError_t launch_gemv_up(const void* x, int act, const int32_t* idx, const int32_t* k_used_dev, int k_static,
+                          int kcap, int T, int H, int N, int bits, bool fused, WView w0, WView w1, uint16_t* h,
+                          float* out32, hipStream_t st);
+// y[t, m] = act(sum_s w[t,s] * (Wd[e_s, m, :] . h[t*kcap+s, :]))
+size_t gemv_down_lds_bytes(int kcap, int I, int bits);
+// allow the down kernels up to `bytes` of dynamic LDS (once per device)
+hipError_t gemv_down_set_max_lds(int bytes);
+hipError_t launch_gemv_down(const uint16_t* h, const int32_t* idx, const float* wts, const int32_t* k_used_dev,
+                            int k_static, int kcap, int T, int H, int I, int bits, WView wd, void* y, int act,
+                            hipStream_t st);
+
+// -------------------------------------------------- batched (MFMA GEMM)
+enum GemmMode { GEMM_FUSED_SWIGLU = 0, GEMM_GATHER_F32 = 1, GEMM_ROWS_F16 = 2 };
+// rows of one M tile for a dispatch (32, 64 or 128)
+int gemm_block_m(int P, int E);
+// upper bound on M tiles for P pairs over E experts
+int gemm_max_mtiles(int P, int E, int bm);
+// a: GATHER modes read x[perm[row]/kcap], ROWS mode reads a[row]; K = reduction dim
+// FUSED: out = h fp16 [rows, N=I]; GATHER_F32: out fp32 [rows, N]; ROWS_F16: out fp16 [rows, N]
+hipError_t launch_gemm(GemmMode mode, const void* a, int act, const int32_t* perm, const int32_t* counts,
+                       const int32_t* offsets, int kcap, int E, int K, int N, int bits, WView w0, WView w1,
+                       void* out, int bm, int max_mtiles, hipStream_t st);
+
+// --------------------------------------------------------- small kernels
+// h[i, j] = fp16(swiglu(g[i, j], u[i, j])) for i < rows
+hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, hipStream_t st);
+// y[t] = act(sum_{s<k} w[t,s] * o[pos[t*kcap+s]])
+hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wts, const int32_t* k_used_dev,
+                          int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st);
+// out[p, :] = src[r, :] (fp16 rows of width I) with r = pos[p] for pos[p] >= 0,
+// or, when pos is NULL, r = p for the pairs whose slot p % kcap < k_used
+hipError_t launch_gather_rows(const uint16_t* src, const int32_t* pos, int64_t P, int I, uint16_t* out, int kcap,
+                              const int32_t* k_used_dev, int k_static, hipStream_t st);
+// copy n int32/fp32 words
+hipError_t launch_copy_words(const void* src, void* dst, int64_t n, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,470 @@
+// C ABI of the MoE layer: argument validation, workspace layout, path
+// dispatch and launches on the caller's stream.  No device allocation, no
+// synchronisation.  Every validation happens before the first HIP call, so
+// invalid arguments return an error with nothing enqueued (and can be tested
+// without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <exception>
+#include <mutex>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+using moe::WView;
+
+constexpr size_t kAlign = 256;
+constexpr int kGemvMaxPairs = 16;  // decode path when T*kcap <= this
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int kcap_of(int k) { return k > 0 ? k : MOE_K_ENTROPY_CAP; }
+
+// ------------------------------------------------------------ profiling --
+
+struct Prof {
+  hipEvent_t const* ev = nullptr;
+  int n = 0;
+  int next = 0;
+  std::string plan;
+};
+thread_local Prof g_prof;
+
+void plan_begin(hipStream_t st) {
+  g_prof.plan.clear();
+  g_prof.next = 0;
+  if (g_prof.ev && g_prof.n > 0) {
+    hipEventRecord(g_prof.ev[0], st);
+    g_prof.next = 1;
+  }
+}
+
+void plan_step(const char* name, hipStream_t st) {
+  if (!g_prof.plan.empty()) g_prof.plan += ",";
+  g_prof.plan += name;
+  if (g_prof.ev && g_prof.next < g_prof.n) hipEventRecord(g_prof.ev[g_prof.next++], st);
+}
+
+// ------------------------------------------------------- device properties
+
+struct DevProps {
+  bool ok = false;
+  bool gfx950 = false;
+  size_t lds_max = 0;
+};
+
+std::mutex g_props_mu;
+DevProps g_props[64];
+
+moe_status device_props(DevProps* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_props_mu);
+  DevProps& p = g_props[dev];
+  if (!p.ok) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+    p.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    p.lds_max = prop.sharedMemPerBlock;
+    if (p.lds_max > 65536 && moe::gemv_down_set_max_lds((int)p.lds_max) != hipSuccess) {
+      (void)hipGetLastError();  // keep the portable 64 KB limit for the decode path
+      p.lds_max = 65536;
+    }
+    p.ok = true;
+  }
+  *out = p;
+  return p.gfx950 ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+// ----------------------------------------------------------- validation --
+
+moe_status check_weights(const moe_weights* w, int E, int N, int K) {
+  if (!w || !w->q) return MOE_ERR_NULL;
+  if (w->bits != 4 && w->bits != 8 && w->bits != 16) return MOE_ERR_QUANT;
+  if (w->bits == 16) {
+    if (w->scales || w->biases) return MOE_ERR_QUANT;
+  } else {
+    if (!w->scales || !w->biases) return MOE_ERR_NULL;
+    if (w->group_size != 64) return MOE_ERR_QUANT;
+  }
+  if (w->E != E || w->N != N || w->K != K) return MOE_ERR_SHAPE;
+  if (w->K % 64 != 0 || w->expert_stride_rows < w->N) return MOE_ERR_SHAPE;
+  if (!aligned16(w->q)) return MOE_ERR_ALIGN;
+  if (w->bits != 16 && (!aligned16(w->scales) || !aligned16(w->biases))) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+moe_status check_router(const void* x, moe_dtype dt, int T, int H, const void* wr, int E, int k) {
+  if (!x || !wr) return MOE_ERR_NULL;
+  if (dt != MOE_F16 && dt != MOE_BF16) return MOE_ERR_DTYPE;
+  if (T < 0 || H <= 0 || H % 64 != 0) return MOE_ERR_SHAPE;
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (k == MOE_K_ENTROPY) {
+    if (E < MOE_K_ENTROPY_CAP) return MOE_ERR_K;
+  } else if (k < 1 || k > MOE_MAX_K || k > E) {
+    return MOE_ERR_K;
+  }
+  if (!aligned16(x) || !aligned16(wr)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+bool compatible(const moe_weights* a, const moe_weights* b) {
+  return a->bits == b->bits && a->group_size == b->group_size && a->E == b->E && a->N == b->N && a->K == b->K &&
+         (a->scales == nullptr) == (b->scales == nullptr) && (a->biases == nullptr) == (b->biases == nullptr);
+}
+
+// ------------------------------------------------------------ workspace --
+
+struct Layout {
+  size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, g32, u32, total;
+};
+
+Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t flags) {
+  Layout L{};
+  const int64_t P = T * kcap;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = at;
+    at += align_up(bytes);
+    return r;
+  };
+  L.logits = take((size_t)(T * E * 4));
+  L.idx = take((size_t)(P * 4));
+  L.w = take((size_t)(P * 4));
+  L.scal = take(8);
+  L.counts = take((size_t)(E * 4));
+  L.offsets = take((size_t)((E + 1) * 4));
+  L.perm = take((size_t)(P * 4));
+  L.pos = take((size_t)(P * 4));
+  L.h = take((size_t)(P * I * 2));
+  L.o = take((size_t)(P * H * 2));
+  if (flags & MOE_FLAG_UNFUSED) {
+    L.g32 = take((size_t)(P * I * 4));
+    L.u32 = take((size_t)(P * I * 4));
+  }
+  L.total = at;
+  return L;
+}
+
+WView view_of(const moe_weights* w, int64_t row_offset) {
+  WView v;
+  const int64_t rb = (int64_t)w->K * w->bits / 8;
+  const int64_t ng = w->K / 64;
+  v.q = (const uint8_t*)w->q + row_offset * rb;
+  v.s = w->scales ? (const uint16_t*)w->scales + row_offset * ng : nullptr;
+  v.b = w->biases ? (const uint16_t*)w->biases + row_offset * ng : nullptr;
+  v.stride = w->expert_stride_rows;
+  return v;
+}
+
+#define HIP_TRY(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+moe_status route_impl(const void* x, moe_dtype dt, int T, int H, const void* wr, int E, int k, int32_t* idx,
+                      float* w, int32_t* k_used, float* entropy, float* logits, hipStream_t st) {
+  HIP_TRY(moe::launch_router_logits(x, wr, logits, T, H, E, (int)dt, st));
+  plan_step("router_logits", st);
+  HIP_TRY(moe::launch_topk(logits, T, E, k, idx, w, k_used, entropy, st));
+  plan_step(k > 0 ? "topk" : "topk_entropy", st);
+  return MOE_OK;
+}
+
+moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* router_w, int E, int k,
+                        const moe_weights* gate_up, const moe_weights* gate, const moe_weights* up,
+                        const moe_weights* down, void* y, uint32_t flags, const moe_taps* taps, void* ws,
+                        size_t ws_bytes, hipStream_t st) {
+  // ---- validation (host only)
+  moe_status s = check_router(x, dt, T, H, router_w, E, k);
+  if (s != MOE_OK) return s;
+  if (!y || !down) return MOE_ERR_NULL;
+  if (!aligned16(y)) return MOE_ERR_ALIGN;
+  const int I = down->K;
+  if (I <= 0 || I % 64 != 0) return MOE_ERR_SHAPE;
+  if ((s = check_weights(down, E, H, I)) != MOE_OK) return s;
+  WView wg, wu;
+  if (gate_up) {
+    if ((s = check_weights(gate_up, E, 2 * I, H)) != MOE_OK) return s;
+    if (gate_up->bits != down->bits) return MOE_ERR_QUANT;
+    wg = view_of(gate_up, 0);
+    wu = view_of(gate_up, I);
+  } else {
+    if (!gate || !up) return MOE_ERR_NULL;
+    if (!compatible(gate, up)) return MOE_ERR_INCOMPATIBLE;
+    if ((s = check_weights(gate, E, I, H)) != MOE_OK) return s;
+    if ((s = check_weights(up, E, I, H)) != MOE_OK) return s;
+    if (gate->bits != down->bits) return MOE_ERR_QUANT;
+    wg = view_of(gate, 0);
+    wu = view_of(up, 0);
+  }
+  const int bits = down->bits;
+  const int kcap = kcap_of(k);
+  const Layout L = layout(T, H, E, kcap, I, flags);
+  if (T == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_ERR_ALIGN;
+
+  // ---- device
+  DevProps props;
+  if ((s = device_props(&props)) != MOE_OK) return s;
+
+  uint8_t* W = (uint8_t*)ws;
+  const int64_t P = (int64_t)T * kcap;
+  float* logits = (taps && taps->logits) ? taps->logits : (float*)(W + L.logits);
+  int32_t* idx = (int32_t*)(W + L.idx);
+  float* wts = (float*)(W + L.w);
+  int32_t* k_used = (int32_t*)(W + L.scal);
+  float* entropy = (float*)(W + L.scal + 4);
+  int32_t* counts = (int32_t*)(W + L.counts);
+  int32_t* offsets = (int32_t*)(W + L.offsets);
+  int32_t* perm = (int32_t*)(W + L.perm);
+  int32_t* pos = (int32_t*)(W + L.pos);
+  uint16_t* h = (uint16_t*)(W + L.h);
+  uint16_t* o = (uint16_t*)(W + L.o);
+  float* g32 = (float*)(W + L.g32);
+  float* u32 = (float*)(W + L.u32);
+  const bool unfused = (flags & MOE_FLAG_UNFUSED) != 0;
+  const int act = (int)dt;
+
+  const bool gemv_fits = moe::gemv_lanes_chunks(H, bits) <= 8 &&
+                         moe::gemv_down_lds_bytes(kcap, I, bits) <= props.lds_max;
+  bool gemv = false;
+  if (!(flags & MOE_FLAG_FORCE_MFMA)) gemv = gemv_fits && ((flags & MOE_FLAG_FORCE_GEMV) || P <= kGemvMaxPairs);
+  const bool need_sort = !gemv || (taps && (taps->counts || taps->offsets || taps->perm));
+
+  plan_begin(st);
+  if ((s = route_impl(x, dt, T, H, router_w, E, k, idx, wts, k_used, entropy, logits, st)) != MOE_OK) return s;
+  if (need_sort) {
+    HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k > 0 ? k : 0, E, counts, offsets, perm, pos, st));
+    plan_step("sort_pairs", st);
+  }
+  const int k_static = k > 0 ? k : 0;
+  if (gemv) {
+    if (!unfused) {
+      HIP_TRY(moe::launch_gemv_up(x, act, idx, k_used, k_static, kcap, T, H, I, bits, true, wg, wu, h, nullptr, st));
+      plan_step("gemv_gate_up_swiglu", st);
+    } else {
+      HIP_TRY(moe::launch_gemv_up(x, act, idx, k_used, k_static, kcap, T, H, I, bits, false, wg, wg, nullptr, g32, st));
+      plan_step("gemv_gate", st);
+      HIP_TRY(moe::launch_gemv_up(x, act, idx, k_used, k_static, kcap, T, H, I, bits, false, wu, wu, nullptr, u32, st));
+      plan_step("gemv_up", st);
+      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, st));
+      plan_step("swiglu", st);
+    }
+    HIP_TRY(moe::launch_gemv_down(h, idx, wts, k_used, k_static, kcap, T, H, I, bits, view_of(down, 0), y, act, st));
+    plan_step("gemv_down_combine", st);
+  } else {
+    const int bm = moe::gemm_block_m((int)P, E);
+    const int mt = moe::gemm_max_mtiles((int)P, E, bm);
+    if (!unfused) {
+      HIP_TRY(moe::launch_gemm(moe::GEMM_FUSED_SWIGLU, x, act, perm, counts, offsets, kcap, E, H, I, bits, wg, wu, h,
+                               bm, mt, st));
+      plan_step("gemm_gate_up_swiglu", st);
+    } else {
+      HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, x, act, perm, counts, offsets, kcap, E, H, I, bits, wg, wg, g32,
+                               bm, mt, st));
+      plan_step("gemm_gate", st);
+      HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, x, act, perm, counts, offsets, kcap, E, H, I, bits, wu, wu, u32,
+                               bm, mt, st));
+      plan_step("gemm_up", st);
+      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, st));
+      plan_step("swiglu", st);
+    }
+    const WView wd = view_of(down, 0);
+    HIP_TRY(moe::launch_gemm(moe::GEMM_ROWS_F16, h, act, perm, counts, offsets, kcap, E, I, H, bits, wd, wd, o, bm, mt,
+                             st));
+    plan_step("gemm_down", st);
+    HIP_TRY(moe::launch_combine(o, pos, wts, k_used, k_static, kcap, T, H, y, act, st));
+    plan_step("combine", st);
+  }
+
+  // ---- taps (copies only)
+  if (taps) {
+    if (taps->topk_idx) HIP_TRY(moe::launch_copy_words(idx, taps->topk_idx, P, st));
+    if (taps->topk_w) HIP_TRY(moe::launch_copy_words(wts, taps->topk_w, P, st));
+    if (taps->k_used) HIP_TRY(moe::launch_copy_words(k_used, taps->k_used, 1, st));
+    if (taps->entropy) HIP_TRY(moe::launch_copy_words(entropy, taps->entropy, 1, st));
+    if (taps->counts) HIP_TRY(moe::launch_copy_words(counts, taps->counts, E, st));
+    if (taps->offsets) HIP_TRY(moe::launch_copy_words(offsets, taps->offsets, E + 1, st));
+    if (taps->perm) HIP_TRY(moe::launch_copy_words(perm, taps->perm, P, st));
+    if (taps->h) {
+      if (gemv) HIP_TRY(moe::launch_gather_rows(h, nullptr, P, I, (uint16_t*)taps->h, kcap, k_used, k_static, st));
+      else HIP_TRY(moe::launch_gather_rows(h, pos, P, I, (uint16_t*)taps->h, kcap, k_used, k_static, st));
+    }
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_DTYPE: return "unknown activation dtype";
+    case MOE_ERR_ALIGN: return "a pointer is not suitably aligned";
+    case MOE_ERR_K: return "k out of range";
+    case MOE_ERR_QUANT: return "unsupported quantisation (bits, group size or scale presence)";
+    case MOE_ERR_INCOMPATIBLE: return "gate and up cannot be fused";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_DEVICE: return "no usable gfx950 device is current";
+    case MOE_ERR_HIP: return "a HIP call failed";
+    case MOE_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+size_t moe_route_workspace_size(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1) return 0;
+  (void)k;
+  return align_up((size_t)T * (size_t)E * 4);
+}
+
+moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E, int32_t k,
+                     int32_t* topk_idx, float* topk_w, int32_t* k_used, float* entropy, float* logits_out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  try {
+    moe_status s = check_router(x, dt, T, H, router_w, E, k);
+    if (s != MOE_OK) return s;
+    if (!topk_idx || !topk_w) return MOE_ERR_NULL;
+    if (T == 0) return MOE_OK;
+    float* logits = logits_out;
+    if (!logits) {
+      if (!ws) return MOE_ERR_WORKSPACE;
+      if (ws_bytes < moe_route_workspace_size(T, E, k)) return MOE_ERR_WORKSPACE;
+      if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return MOE_ERR_ALIGN;
+      logits = (float*)ws;
+    }
+    DevProps props;
+    if ((s = device_props(&props)) != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    plan_begin(st);
+    return route_impl(x, dt, T, H, router_w, E, k, topk_idx, topk_w, k_used, entropy, logits, st);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_topk_from_logits(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                                float* topk_w, int32_t* k_used, float* entropy, void* ws, size_t ws_bytes,
+                                void* stream) {
+  try {
+    (void)ws;
+    (void)ws_bytes;
+    if (!logits || !topk_idx || !topk_w) return MOE_ERR_NULL;
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+    if (k == MOE_K_ENTROPY) {
+      if (E < MOE_K_ENTROPY_CAP) return MOE_ERR_K;
+    } else if (k < 1 || k > MOE_MAX_K || k > E) {
+      return MOE_ERR_K;
+    }
+    if (T == 0) return MOE_OK;
+    DevProps props;
+    moe_status s = device_props(&props);
+    if (s != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    plan_begin(st);
+    if (moe::launch_topk(logits, T, E, k, topk_idx, topk_w, k_used, entropy, st) != hipSuccess) return MOE_ERR_HIP;
+    plan_step(k > 0 ? "topk" : "topk_entropy", st);
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+size_t moe_layer_workspace_size(int32_t T, int32_t H, int32_t E, int32_t k, int32_t inter, uint32_t flags) {
+  if (T < 0 || H < 0 || E < 1 || inter < 0) return 0;
+  return layout(T, H, E, kcap_of(k), inter, flags).total;
+}
+
+moe_status moe_layer_forward(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E,
+                             int32_t k, const moe_weights* gate_up, const moe_weights* gate, const moe_weights* up,
+                             const moe_weights* down, void* y, uint32_t flags, const moe_taps* taps, void* ws,
+                             size_t ws_bytes, void* stream) {
+  try {
+    return forward_impl(x, dt, T, H, router_w, E, k, gate_up, gate, up, down, y, flags, taps, ws, ws_bytes,
+                        (hipStream_t)stream);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_fuse_gate_up(const moe_weights* gate, const moe_weights* up, void* q_out, void* s_out, void* b_out,
+                            void* stream) {
+  try {
+    if (!gate || !up || !gate->q || !up->q || !q_out) return MOE_ERR_NULL;
+    if (!compatible(gate, up)) return MOE_ERR_INCOMPATIBLE;
+    moe_status s = check_weights(gate, gate->E, gate->N, gate->K);
+    if (s != MOE_OK) return s;
+    if ((s = check_weights(up, gate->E, gate->N, gate->K)) != MOE_OK) return s;
+    const bool quant = gate->bits != 16;
+    if (quant && (!s_out || !b_out)) return MOE_ERR_NULL;
+    if (!quant && (s_out || b_out)) return MOE_ERR_QUANT;
+    if (!aligned16(q_out) || (quant && (!aligned16(s_out) || !aligned16(b_out)))) return MOE_ERR_ALIGN;
+    DevProps props;
+    if ((s = device_props(&props)) != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    plan_begin(st);
+    const size_t E = (size_t)gate->E, I = (size_t)gate->N;
+    const size_t rb = (size_t)gate->K * gate->bits / 8, sb = (size_t)(gate->K / 64) * 2;
+    struct Part {
+      void* dst;
+      const void* src;
+      size_t row, sstride;
+    };
+    Part parts[6] = {{q_out, gate->q, rb, (size_t)gate->expert_stride_rows},
+                     {(uint8_t*)q_out + I * rb, up->q, rb, (size_t)up->expert_stride_rows},
+                     {s_out, gate->scales, sb, (size_t)gate->expert_stride_rows},
+                     {(uint8_t*)s_out + I * sb, up->scales, sb, (size_t)up->expert_stride_rows},
+                     {b_out, gate->biases, sb, (size_t)gate->expert_stride_rows},
+                     {(uint8_t*)b_out + I * sb, up->biases, sb, (size_t)up->expert_stride_rows}};
+    const int nparts = quant ? 6 : 2;
+    for (int i = 0; i < nparts; ++i) {
+      const Part& p = parts[i];
+      // E blocks of I rows; destination experts are 2*I rows apart
+      if (hipMemcpy2DAsync(p.dst, 2 * I * p.row, p.src, p.sstride * p.row, I * p.row, E, hipMemcpyDeviceToDevice,
+                           st) != hipSuccess) {
+        (void)hipGetLastError();
+        for (size_t e = 0; e < E; ++e)
+          if (hipMemcpyAsync((uint8_t*)p.dst + e * 2 * I * p.row, (const uint8_t*)p.src + e * p.sstride * p.row,
+                             I * p.row, hipMemcpyDeviceToDevice, st) != hipSuccess)
+            return MOE_ERR_HIP;
+      }
+    }
+    plan_step("fuse_gate_up_copy", st);
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+void moe_debug_set_events(void* const* events, int32_t n) {
+  g_prof.ev = (hipEvent_t const*)events;
+  g_prof.n = events ? n : 0;
+  g_prof.next = 0;
+}
+
+int32_t moe_debug_last_plan(char* buf, size_t buf_bytes) {
+  const std::string& p = g_prof.plan;
+  if (buf && buf_bytes > 0) {
+    size_t n = std::min(buf_bytes - 1, p.size());
+    std::memcpy(buf, p.data(), n);
+    buf[n] = 0;
+  }
+  return (int32_t)p.size();
+}
+
+}  // extern "C"

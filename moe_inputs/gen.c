@@ -46,13 +46,20 @@ static inline uint64_t draw_bits(uint64_t key, uint64_t ctr) {
 /* uniform on the open interval (0, 1) */
 static inline double u01(uint64_t b) { return ((double)(b >> 11) + 0.5) * (1.0 / 9007199254740992.0); }
 
-static inline double normal_at(uint64_t key, uint64_t i) {
-  uint64_t j = i >> 1;
+/* both normals of Box-Muller pair j: elements 2j (cosine) and 2j+1 (sine) */
+static inline void normal_pair(uint64_t key, uint64_t j, double* c, double* s) {
   double u1 = u01(draw_bits(key, 2 * j));
   double u2 = u01(draw_bits(key, 2 * j + 1));
   double r = sqrt(-2.0 * log(u1));
   double th = 6.283185307179586476925 * u2;
-  return (i & 1) ? r * sin(th) : r * cos(th);
+  *c = r * cos(th);
+  *s = r * sin(th);
+}
+
+static inline double normal_at(uint64_t key, uint64_t i) {
+  double c, s;
+  normal_pair(key, i >> 1, &c, &s);
+  return (i & 1) ? s : c;
 }
 
 /* ------------------------------------------------------ fp16 / bf16 ---- */
@@ -132,6 +139,16 @@ void gen_normal_f64(uint64_t seed, uint32_t tid, int64_t start, int64_t n, doubl
 void gen_normal_half(uint64_t seed, uint32_t tid, int64_t start, int64_t n, double sigma, int dtype,
                      uint16_t* out) {
   uint64_t key = stream_key(seed, tid);
+  if ((start & 1) == 0 && (n & 1) == 0) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i += 2) {
+      double c, s;
+      normal_pair(key, (uint64_t)(start + i) >> 1, &c, &s);
+      out[i] = round_to(sigma * c, dtype);
+      out[i + 1] = round_to(sigma * s, dtype);
+    }
+    return;
+  }
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = round_to(sigma * normal_at(key, (uint64_t)(start + i)), dtype);
 }
@@ -218,8 +235,13 @@ void gen_quant_weights(uint64_t seed, uint32_t tid, int E, int N, int K, int bit
     double w[256];
     uint8_t codes[256];
     for (int g = 0; g < ng; ++g) {
-      uint64_t base = (uint64_t)(r * K + (int64_t)g * gs);
-      for (int i = 0; i < gs; ++i) w[i] = sigma * normal_at(key, base + (uint64_t)i);
+      uint64_t base = (uint64_t)(r * K + (int64_t)g * gs); /* even, since gs and K are even */
+      for (int i = 0; i < gs; i += 2) {
+        double c, sn;
+        normal_pair(key, (base + (uint64_t)i) >> 1, &c, &sn);
+        w[i] = sigma * c;
+        w[i + 1] = sigma * sn;
+      }
       quant_group(w, gs, bits, codes, &scales[r * ng + g], &biases[r * ng + g]);
       uint8_t* dst = q + r * row_bytes;
       if (bits == 4) {

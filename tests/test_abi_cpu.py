@@ -1,0 +1,171 @@
+"""The C ABI on the CPU: the library loads, exports what include/moe.h
+declares, and validates arguments on the host before touching a device.
+
+Pointers here are fake aligned addresses: validation never dereferences them,
+and every call below returns before the first HIP call (or, for the valid
+call without a GPU, at the device check).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_router_amd as moe
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moe.h")
+P = 0x100000  # a 16-byte aligned fake address
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert "moe_route" in names and "moe_layer_forward" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(moe.EXPORTS) == set(names)
+
+
+def test_status_strings():
+    L = moe.lib()
+    for code, name in moe.STATUS.items():
+        s = L.moe_status_string(code).decode()
+        assert s and s != "unknown status", name
+    assert L.moe_status_string(12345).decode() == "unknown status"
+
+
+def W(E, N, K, bits=4, q=P, s=P, b=P, gs=64, stride=None):
+    return moe.CWeights(q, None if bits == 16 else s, None if bits == 16 else b, E, N, K, bits, gs,
+                        N if stride is None else stride)
+
+
+def fwd(T=4, H=256, E=8, k=2, I=128, dt=moe.MOE_F16, x=P, wr=P, y=P, gu="fused", gate=None, up=None, down=None,
+        flags=0, ws=P, ws_bytes=None, bits=4):
+    L = moe.lib()
+    if gu == "fused":
+        gu = W(E, 2 * I, H, bits)
+    down = W(E, H, I, bits) if down is None else down
+    if ws_bytes is None:
+        ws_bytes = L.moe_layer_workspace_size(T, H, E, k, I, flags)
+    ref = lambda w: ctypes.byref(w) if w is not None else None
+    return L.moe_layer_forward(x, dt, T, H, wr, E, k, ref(gu), ref(gate), ref(up), ref(down), y, flags, None, ws,
+                               ws_bytes, None)
+
+
+def test_zero_tokens_is_a_noop():
+    assert fwd(T=0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), "MOE_ERR_NULL"),
+    (dict(wr=None), "MOE_ERR_NULL"),
+    (dict(y=None), "MOE_ERR_NULL"),
+    (dict(gu=None), "MOE_ERR_NULL"),
+    (dict(dt=3), "MOE_ERR_DTYPE"),
+    (dict(H=200), "MOE_ERR_SHAPE"),
+    (dict(E=0), "MOE_ERR_SHAPE"),
+    (dict(E=257, k=2), "MOE_ERR_SHAPE"),
+    (dict(k=0), "MOE_ERR_K"),
+    (dict(k=9, E=16), "MOE_ERR_K"),
+    (dict(k=5, E=4), "MOE_ERR_K"),
+    (dict(k=-1, E=2), "MOE_ERR_K"),
+    (dict(k=-2), "MOE_ERR_K"),
+    (dict(I=100, down=W(8, 256, 100)), "MOE_ERR_SHAPE"),
+    (dict(x=P + 8), "MOE_ERR_ALIGN"),
+    (dict(y=P + 2), "MOE_ERR_ALIGN"),
+    (dict(ws=None), "MOE_ERR_WORKSPACE"),
+    (dict(ws_bytes=1024), "MOE_ERR_WORKSPACE"),
+    (dict(ws=P + 16), "MOE_ERR_ALIGN"),
+    (dict(gu=W(8, 2 * 128, 256, bits=5)), "MOE_ERR_QUANT"),
+    (dict(gu=W(8, 2 * 128, 256, gs=32)), "MOE_ERR_QUANT"),
+    (dict(gu=W(8, 2 * 128, 256, s=None)), "MOE_ERR_NULL"),
+    (dict(gu=W(8, 2 * 128, 256, q=P + 4)), "MOE_ERR_ALIGN"),
+    (dict(gu=W(8, 2 * 100, 256)), "MOE_ERR_SHAPE"),
+    (dict(gu=W(7, 2 * 128, 256)), "MOE_ERR_SHAPE"),
+    (dict(gu=W(8, 2 * 128, 256, stride=100)), "MOE_ERR_SHAPE"),
+    (dict(gu=W(8, 2 * 128, 256, bits=8)), "MOE_ERR_QUANT"),
+    (dict(down=W(8, 256, 128, bits=16)), "MOE_ERR_QUANT"),
+])
+def test_validation_errors(kw, status):
+    assert moe.STATUS[fwd(**kw)] == status
+
+
+def test_bits16_rejects_scales():
+    bad = moe.CWeights(P, P, P, 8, 256, 256, 16, 64, 256)
+    assert moe.STATUS[fwd(gu=bad, down=W(8, 256, 128, bits=16), bits=16)] == "MOE_ERR_QUANT"
+
+
+def test_separate_gate_up_must_be_compatible():
+    # the _can_fuse rule of the oMLX page: same bits, group size, shape, scale presence
+    ok = W(8, 128, 256)
+    assert moe.STATUS[fwd(gu=None, gate=ok, up=W(8, 128, 256, bits=8))] == "MOE_ERR_INCOMPATIBLE"
+    assert moe.STATUS[fwd(gu=None, gate=ok, up=W(8, 128, 256, gs=32))] == "MOE_ERR_INCOMPATIBLE"
+    assert moe.STATUS[fwd(gu=None, gate=ok, up=W(8, 64, 256))] == "MOE_ERR_INCOMPATIBLE"
+    assert moe.STATUS[fwd(gu=None, gate=ok, up=None)] == "MOE_ERR_NULL"
+
+
+def test_fuse_gate_up_validation():
+    L = moe.lib()
+    g, u = W(8, 128, 256), W(8, 128, 256, bits=8)
+    assert moe.STATUS[L.moe_fuse_gate_up(ctypes.byref(g), ctypes.byref(u), P, P, P, None)] == "MOE_ERR_INCOMPATIBLE"
+    u = W(8, 128, 512)
+    assert moe.STATUS[L.moe_fuse_gate_up(ctypes.byref(g), ctypes.byref(u), P, P, P, None)] == "MOE_ERR_INCOMPATIBLE"
+    u = W(8, 128, 256)
+    assert moe.STATUS[L.moe_fuse_gate_up(ctypes.byref(g), ctypes.byref(u), None, P, P, None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[L.moe_fuse_gate_up(ctypes.byref(g), ctypes.byref(u), P, None, P, None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[L.moe_fuse_gate_up(ctypes.byref(g), ctypes.byref(u), P + 8, P, P, None)] == "MOE_ERR_ALIGN"
+
+
+def test_route_validation():
+    L = moe.lib()
+    ws = 1 << 20
+    call = lambda **kw: L.moe_route(kw.get("x", P), kw.get("dt", 1), kw.get("T", 4), kw.get("H", 256),
+                                    kw.get("wr", P), kw.get("E", 8), kw.get("k", 2), kw.get("idx", P),
+                                    kw.get("w", P), None, None, kw.get("logits", None), kw.get("ws", P),
+                                    kw.get("ws_bytes", ws), None)
+    assert call(T=0) == 0
+    assert moe.STATUS[call(x=None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[call(idx=None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[call(k=3, E=2)] == "MOE_ERR_K"
+    assert moe.STATUS[call(H=100)] == "MOE_ERR_SHAPE"
+    assert moe.STATUS[call(ws=None)] == "MOE_ERR_WORKSPACE"
+    assert moe.STATUS[call(ws_bytes=16)] == "MOE_ERR_WORKSPACE"
+    assert moe.STATUS[L.moe_topk_from_logits(None, 4, 8, 2, P, P, None, None, None, 0, None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[L.moe_topk_from_logits(P, 4, 8, 9, P, P, None, None, None, 0, None)] == "MOE_ERR_K"
+
+
+def test_workspace_size_is_host_arithmetic():
+    L = moe.lib()
+    a = L.moe_layer_workspace_size(4096, 4096, 64, 4, 1408, 0)
+    b = L.moe_layer_workspace_size(4096, 4096, 64, 4, 1408, moe.FLAG_UNFUSED)
+    P_ = 4096 * 4
+    # h (fp16 [P, I]) and o (fp16 [P, H]) dominate; unfused adds g and u in fp32
+    assert a >= P_ * 1408 * 2 + P_ * 4096 * 2
+    assert b - a >= 2 * P_ * 1408 * 4
+    assert L.moe_layer_workspace_size(1, 4096, 64, -1, 11008, 0) > L.moe_layer_workspace_size(1, 4096, 64, 1, 11008, 0)
+    assert L.moe_layer_workspace_size(0, 4096, 64, 4, 11008, 0) > 0
+    assert L.moe_route_workspace_size(512, 32, -1) >= 512 * 32 * 4
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert moe.STATUS[fwd()] == "MOE_ERR_DEVICE"
+
+
+def test_debug_plan_hooks_are_callable_without_gpu():
+    L = moe.lib()
+    L.moe_debug_set_events(None, 0)
+    buf = ctypes.create_string_buffer(64)
+    assert L.moe_debug_last_plan(buf, 64) >= 0

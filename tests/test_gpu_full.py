@@ -1,0 +1,119 @@
+"""Full-size workloads on the GPU, in the launch configuration the benchmark
+times, checked against the oracle on sampled tokens (the oracle computes each
+token's output independently), plus the properties that hold at any size:
+bit-exact routing on identical logits, exact sort, fused == unfused.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_router_amd as moe
+import moe_inputs as mi
+import oracle
+from gpu_util import Dev, assert_within_tolerance, check_routing_identical_logits, host_bits, reference_outputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _gen(recipe, **kw):
+    t = time.time()
+    inp = mi.make_inputs(recipe, **kw)
+    gu_np = oracle.fuse_gate_up(inp.gate, inp.up)
+    dev = Dev(inp)
+    torch.cuda.synchronize()
+    _say("generated %s %s in %.1fs" % (recipe, kw, time.time() - t))
+    return inp, gu_np, dev
+
+
+def _forward(dev, flags=0):
+    inp = dev.inp
+    taps = moe.make_taps(inp.T, inp.E, inp.k, inp.I, "cuda", names=("logits", "topk_idx", "topk_w", "k_used",
+                                                                      "counts", "offsets", "perm"))
+    y = dev.forward(flags=flags, taps=taps)
+    return host_bits(y), {k: v.cpu().numpy() for k, v in taps.items()}, moe.last_plan()
+
+
+def _check(inp, gu_np, y, taps, tokens, label):
+    ku = int(taps["k_used"][0])
+    check_routing_identical_logits(taps["logits"], taps["topk_idx"], taps["topk_w"], ku)
+    ref, flips = reference_outputs(inp, gu_np, tokens, taps["topk_idx"], taps["topk_w"], ku)
+    assert_within_tolerance(y[tokens], ref, inp.dtype, "%s (tokens %d, near-tie flips %d)" % (label, len(tokens),
+                                                                                             flips))
+    if "perm" in taps:
+        counts, offsets, perm, _ = oracle.sort_pairs(taps["topk_idx"], ku, inp.E)
+        assert np.array_equal(taps["counts"], counts) and np.array_equal(taps["perm"], perm)
+
+
+def test_decode_b1_full_size():
+    inp, gu_np, dev = _gen("decode_b1", T=6)
+    for t in range(inp.T):
+        # one token per call, as the benchmark runs it
+        x1 = dev.x[t:t + 1]
+        taps = moe.make_taps(1, inp.E, inp.k, inp.I, "cuda", names=("logits", "topk_idx", "topk_w", "k_used"))
+        y = host_bits(moe.layer_forward(x1, dev.wr, inp.k, dev.down, gate_up=dev.gate_up, taps=taps))
+        plan = moe.last_plan()
+        y_u = host_bits(moe.layer_forward(x1, dev.wr, inp.k, dev.down, gate_up=dev.gate_up, flags=moe.FLAG_UNFUSED))
+        assert np.array_equal(y, y_u), "decode fused vs unfused"
+        assert "gemv_gate_up_swiglu" in plan, plan
+        tp = {k: v.cpu().numpy() for k, v in taps.items()}
+        import dataclasses
+        sub = dataclasses.replace(inp, T=1, x=np.ascontiguousarray(inp.x[t:t + 1]))
+        _check(sub, gu_np, y, tp, np.array([0]), "decode_b1 token %d" % t)
+
+
+def test_decode_b1_full_size_mfma_path():
+    inp, gu_np, dev = _gen("decode_b1", T=2)
+    y, taps, plan = _forward(dev, moe.FLAG_FORCE_MFMA)
+    assert "gemm_gate_up_swiglu" in plan
+    _check(inp, gu_np, y, taps, np.arange(inp.T), "decode_b1/mfma")
+
+
+def test_batched_decode_full_size():
+    inp, gu_np, dev = _gen("batched_decode")
+    y, taps, plan = _forward(dev)
+    _say("plan", plan, "counts", taps["counts"].tolist())
+    _check(inp, gu_np, y, taps, np.arange(inp.T), "batched_decode")
+    y_u, _, _ = _forward(dev, moe.FLAG_UNFUSED)
+    assert np.array_equal(y, y_u)
+
+
+def test_prefill_full_size():
+    inp, gu_np, dev = _gen("prefill")
+    y, taps, plan = _forward(dev)
+    counts = taps["counts"]
+    _say("plan", plan, "hot expert %d tokens, mean %.1f" % (counts.max(), counts.mean()))
+    assert counts.max() >= 10 * counts.mean()
+    # sampled tokens: the first few, some of the hot expert's, and a spread
+    hot = int(np.argmax(counts))
+    hot_tokens = np.where((taps["topk_idx"] == hot).any(axis=1))[0]
+    rng = np.random.default_rng(0)
+    tokens = np.unique(np.concatenate([np.arange(4), hot_tokens[:6], hot_tokens[-4:],
+                                       rng.choice(inp.T, 14, replace=False), [inp.T - 1]]))
+    _check(inp, gu_np, y, taps, tokens, "prefill")
+    y_u, _, _ = _forward(dev, moe.FLAG_UNFUSED)
+    assert np.array_equal(y, y_u)
+
+
+@pytest.mark.parametrize("bits", [16, 4])
+def test_entropy_full_size(bits):
+    import dataclasses
+    from gpu_util import dev_half
+    inp0, gu_np, dev = _gen("entropy", bits=bits, segment=0)
+    for seg, k_expect in enumerate((1, 2, 3, 3)):
+        # same expert weights; each segment has its own tokens and router temperature
+        x, wr, _ = mi.make_router_inputs("entropy", segment=seg)
+        inp = dataclasses.replace(inp0, x=x, wr=wr, segment=seg)
+        dev.inp, dev.x, dev.wr = inp, dev_half(x, "f16"), dev_half(wr, "f16")
+        y, taps, plan = _forward(dev)
+        assert int(taps["k_used"][0]) == k_expect
+        rng = np.random.default_rng(seg)
+        tokens = np.unique(np.concatenate([[0, inp.T - 1], rng.choice(inp.T, 10, replace=False)]))
+        _check(inp, gu_np, y, taps, tokens, "entropy bits=%d segment %d (k=%d)" % (bits, seg, k_expect))
+        y_u, _, _ = _forward(dev, moe.FLAG_UNFUSED)
+        assert np.array_equal(y, y_u)
