@@ -169,34 +169,71 @@ def main():
             return x_pool[i:i + 1]
         return x_pool
 
+    def step(i):
+        moe.layer_forward(x_of(i), wr, k, down, gate_up=gate_up, out=y, workspace=ws)
+
     # discover the kernel plan
-    moe.layer_forward(x_of(0), wr, k, down, gate_up=gate_up, out=y, workspace=ws)
+    step(0)
     torch.cuda.synchronize()
     plan = moe.last_plan()
     nk = len(plan)
 
     for i in range(args.warmup):
-        moe.layer_forward(x_of(i), wr, k, down, gate_up=gate_up, out=y, workspace=ws)
+        step(i)
     torch.cuda.synchronize()
-
     K = args.steps
+
+    # ---- timed region 1: stream launches, no instrumentation
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - t0
+
+    # ---- timed region 2: hipGraph replay of G consecutive layer calls
+    graph_s = None
+    G = min(64, K)
+    reps = max(1, K // G)
+    try:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            for i in range(G):
+                step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(G):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_s = (time.perf_counter() - t0) * K / (reps * G)
+    except Exception as ex:  # graph capture unavailable: report stream launches only
+        log("graph capture failed:", ex)
+
+    # ---- timed region 3: HIP events between the kernels, on the launch stream
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
     for evs in events:  # create the underlying HIP events
         for e in evs:
             e.record(stream)
     torch.cuda.synchronize()
-
-    # ---- timed region
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
+    t0 = time.perf_counter()
     for i in range(K):
         moe.debug_set_events(events[i])
-        moe.layer_forward(x_of(args.warmup + i), wr, k, down, gate_up=gate_up, out=y, workspace=ws)
+        step(args.warmup + i)
     torch.cuda.synchronize()
-    t_end = time.perf_counter()
+    events_s = time.perf_counter() - t0
     moe.debug_set_events(None)
 
-    elapsed = t_end - t_start
+    best_s = min(v for v in (eager_s, graph_s) if v is not None)
+    mode = "graph" if graph_s is not None and graph_s <= eager_s else "eager"
+    elapsed = best_s
     ms_per_step = elapsed * 1e3 / K
     value = K * T / elapsed
     per_kernel = np.zeros(nk)
@@ -206,7 +243,8 @@ def main():
     per_kernel_us = per_kernel / K * 1e3
     gpu_step_us = float(sum(per_kernel_us))
     log("plan:", ", ".join("%s %.2fus" % (n, t) for n, t in zip(plan, per_kernel_us)))
-    log("step %.2f us wall, %.2f us between first and last event" % (ms_per_step * 1e3, gpu_step_us))
+    log("per step: eager %.2f us, graph %s us, with events %.2f us (sum of kernel spans %.2f us)" % (
+        eager_s * 1e6 / K, "%.2f" % (graph_s * 1e6 / K) if graph_s else "n/a", events_s * 1e6 / K, gpu_step_us))
 
     # ---- roofline of the dominant kernel
     j = int(np.argmax(per_kernel_us))
@@ -294,6 +332,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl["label"], "tokens_per_step": T, "hidden": H, "experts": E, "top_k": k,
                    "intermediate": I, "weight_bits": bits, "activations": inp.dtype,
+                   "launch": mode, "eager_tokens_per_s": round(K * T / eager_s, 2),
+                   "graph_tokens_per_s": round(K * T / graph_s, 2) if graph_s else None,
                    "kernels_per_step": nk, "plan": plan,
                    "per_kernel_us": [round(float(v), 3) for v in per_kernel_us]},
         "roofline": roof,

@@ -38,6 +38,8 @@
  *     enqueued; an error return means nothing was enqueued.  Validation makes
  *     no HIP call, so it can be exercised without a GPU.
  *   - Layouts are row-major.  Activations and router weights share one dtype.
+ *   - T == 0 is a no-op returning MOE_OK; buffers whose size is proportional
+ *     to T (activations, outputs, routing results) may then be NULL.
  *   - Calls on different streams are independent; the library keeps no
  *     mutable state besides a once-per-device cache of device properties and
  *     the optional per-thread profiling hooks at the end of this header.
@@ -210,6 +212,12 @@ const char* moe_status_string(moe_status s);
  */
 void moe_debug_set_events(void* const* events, int32_t n);
 int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
+/*
+ * Launch-shape knobs for measurement sweeps (process-wide): key 0 = resident
+ * waves per CU targeted by the decode gate+up kernel, key 1 = by the decode
+ * down kernel.  Values <= 0 are ignored.  Results do not depend on them.
+ */
+void moe_debug_set_tuning(int32_t key, int32_t value);
 
 #ifdef __cplusplus
 }

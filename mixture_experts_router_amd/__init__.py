@@ -33,7 +33,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
 
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_topk_from_logits", "moe_layer_workspace_size",
            "moe_layer_forward", "moe_fuse_gate_up", "moe_status_string", "moe_debug_set_events",
-           "moe_debug_last_plan")
+           "moe_debug_last_plan", "moe_debug_set_tuning")
 
 
 class MoeError(RuntimeError):
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.moe_debug_set_events.restype = None
     L.moe_debug_last_plan.argtypes = [ctypes.c_char_p, sz]
     L.moe_debug_last_plan.restype = i32
+    L.moe_debug_set_tuning.argtypes = [i32, i32]
+    L.moe_debug_set_tuning.restype = None
     _lib = L
     return L
 
@@ -142,20 +144,25 @@ class Weights:
     stride: Optional[int] = None
     row_offset: int = 0
 
+    _cstruct: Optional[CWeights] = dataclasses.field(default=None, repr=False, compare=False)
+
     def c(self) -> CWeights:
+        if self._cstruct is not None:
+            return self._cstruct
         stride = self.N if self.stride is None else self.stride
         rb = self.K * self.bits // 8
         ng = self.K // self.group_size
         q = self.q.data_ptr() + self.row_offset * rb
         s = None if self.scales is None else self.scales.data_ptr() + self.row_offset * ng * 2
         b = None if self.biases is None else self.biases.data_ptr() + self.row_offset * ng * 2
-        return CWeights(q, s, b, self.E, self.N, self.K, self.bits, self.group_size, stride)
+        self._cstruct = CWeights(q, s, b, self.E, self.N, self.K, self.bits, self.group_size, stride)
+        return self._cstruct
 
     def split_gate_up(self):
         """(gate, up) views of a fused [E, 2I, K] tensor, gate rows first."""
         I = self.N // 2
-        g = dataclasses.replace(self, N=I, stride=self.N, row_offset=0)
-        u = dataclasses.replace(self, N=I, stride=self.N, row_offset=I)
+        g = dataclasses.replace(self, N=I, stride=self.N, row_offset=0, _cstruct=None)
+        u = dataclasses.replace(self, N=I, stride=self.N, row_offset=I, _cstruct=None)
         return g, u
 
 
@@ -277,6 +284,11 @@ def debug_set_events(events: Optional[Sequence]) -> None:
     arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
     debug_set_events._keep = arr  # keep the array alive while the library holds it
     lib().moe_debug_set_events(ctypes.cast(arr, ctypes.c_void_p), len(events))
+
+
+def debug_set_tuning(key: int, value: int) -> None:
+    """Launch-shape knob (0: decode gate+up waves/CU, 1: decode down waves/CU)."""
+    lib().moe_debug_set_tuning(int(key), int(value))
 
 
 def source_hash() -> str:

@@ -83,9 +83,47 @@ __device__ __forceinline__ u32x4 perm8_nibble_order(u32x4 v) {
 }
 
 // ----------------------------------------------------- unpacking codes ---
+//
+// gfx9 VOP3 instructions cannot encode 32-bit literals, so (v & mask) | magic
+// would compile to two instructions; with mask and magic held in registers it
+// is one v_and_or_b32.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(mask), "v"(magic));
+  return r;
+}
 
-// 8 packed 4-bit codes (one u32) -> four fp16 pairs holding 1024 + q, in the
-// order (q0,q4) (q1,q5) (q2,q6) (q3,q7)
+// Loop-invariant constants for unpacking 4-bit codes into fp16 numbers:
+// exponent bits 0x6400 turn a code q in mantissa bits 0-3 into 1024 + q and a
+// code in mantissa bits 4-7 into 1024 + 16 q.
+struct Q4Consts {
+  uint32_t lo, hi, magic;
+};
+
+__device__ __forceinline__ Q4Consts q4_consts() {
+  Q4Consts c;
+  c.lo = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  c.hi = __builtin_amdgcn_readfirstlane(0x00F000F0u);
+  c.magic = __builtin_amdgcn_readfirstlane(0x64006400u);
+  // keep them in VGPRs (one v_and_or_b32 may read at most one SGPR on gfx9)
+  asm volatile("" : "+v"(c.lo), "+v"(c.hi), "+v"(c.magic));
+  return c;
+}
+
+// 8 packed 4-bit codes (one u32: codes k0..k7, even k in the low nibble of
+// each byte) -> four fp16 pairs: (k0,k4) and (k2,k6) holding 1024 + q, and
+// (k1,k5) and (k3,k7) holding 1024 + 16 q.
+__device__ __forceinline__ void q4_word_unpack(uint32_t v, const Q4Consts& c, uint32_t& p04, uint32_t& p15,
+                                               uint32_t& p26, uint32_t& p37) {
+  const uint32_t v8 = v >> 8;
+  p04 = and_or(v, c.lo, c.magic);
+  p15 = and_or(v, c.hi, c.magic);
+  p26 = and_or(v8, c.lo, c.magic);
+  p37 = and_or(v8, c.hi, c.magic);
+}
+
+// 8 packed 4-bit codes -> four fp16 pairs holding 1024 + q, in the order
+// (q0,q4) (q1,q5) (q2,q6) (q3,q7)
 __device__ __forceinline__ void q4_word_to_biased_pairs(uint32_t v, uint32_t out[4]) {
   out[0] = (v & 0x000F000Fu) | 0x64006400u;
   out[1] = ((v >> 4) & 0x000F000Fu) | 0x64006400u;
@@ -114,18 +152,51 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 }
 
 // ---------------------------------------------------------- reductions ---
+//
+// Cross-lane sums use DPP (data-parallel primitives: lane permutations fused
+// into the VALU operand, no LDS round trip).  Pairs, quads, 8-lane halves and
+// 16-lane rows are combined with the symmetric permutations quad_perm[1,0,3,2],
+// quad_perm[2,3,0,1], row_half_mirror and row_mirror, so every lane of a row
+// ends with the identical row total (a+b == b+a); the four row totals are then
+// read from lanes 0/16/32/48 and added in row order.  The result is the same
+// in every lane and independent of timing.
 
-// butterfly sum over the 64 lanes; every lane ends with the same value
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int DPP_QUAD_1032 = 0xB1;
+constexpr int DPP_QUAD_2301 = 0x4E;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// sum over the 64 lanes; every lane ends with the same value
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+  v += dpp_f<DPP_QUAD_1032>(v);
+  v += dpp_f<DPP_QUAD_2301>(v);
+  v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_f<DPP_ROW_MIRROR>(v);
+  const float r0 = readlane_f(v, 0), r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
+  return ((r0 + r1) + r2) + r3;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
+  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+  const float r0 = readlane_f(v, 0), r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }

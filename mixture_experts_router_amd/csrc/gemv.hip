@@ -9,21 +9,48 @@
 // the routing-weighted combine y = sum_s w_s * o_s in slot order.
 //
 // Dequantisation happens in registers and is factored out of the dot
-// product: for a 16-byte chunk of codes q with scale s and bias b,
-//     sum_k x_k (s q_k + b) = s * (sum_k x_k (1024 + q_k) - 1024 * X) + b * X,
-// X = sum_k x_k.  The codes become the fp16 numbers 1024 + q with one
-// AND-OR per pair (exponent bits 0x6400), and v_dot2_f32_f16 multiplies two
-// code/activation pairs with fp32 accumulation, so the inner loop costs
-// about 1.4 VALU operations per 4-bit weight.
+// product.  For a 16-byte chunk of codes q with scale s and bias b,
+//     sum_k x_k (s q_k + b) = s * sum_k x_k q_k + b * X,     X = sum_k x_k.
+// A 32-bit word of eight 4-bit codes becomes four fp16 pairs with one shift
+// and four v_and_or_b32: exponent bits 0x6400 make a code in mantissa bits 0-3
+// the number 1024 + q and a code in bits 4-7 the number 1024 + 16 q.  So
+//     sum_k x_k q_k = (A - 1024 Xa) + (B - 1024 Xb) / 16,
+// where A and B are v_dot2_f32_f16 sums (fp32 accumulation) over the two
+// kinds of pairs and Xa, Xb the matching activation sums, computed once per
+// wave.  8-bit codes use v_perm_b32 to build 1024 + q pairs the same way.
+// About 1.4 VALU operations per 4-bit weight.
 //
 // Lane l of a wave owns the 16-byte chunks c = l + 64*i of every row, so one
-// load instruction covers 1 KB of contiguous weights.  Each row's 64 lane
-// partials are summed with a butterfly; the same row code serves the fused
-// (gate+up+SwiGLU) and the single-projection kernels, so both round the same.
+// load instruction covers 1 KB of contiguous weights.  The chunk loops have no
+// per-lane branches (a lane past the end of a row re-reads the last chunk and
+// masks its contribution), so every load is issued ahead of its use.  Each
+// row's 64 lane partials are summed with a DPP butterfly; the same row code
+// serves the fused (gate+up+SwiGLU) and the single-projection kernels, so both
+// round identically.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace moe {
+
+// Route token t inside a decode kernel: with logits given (static k), every
+// wave recomputes the token's selection (topk.hpp, identical in all kernels)
+// instead of waiting for a separate selection launch.
+struct RouteSrc {
+  const float* logits;  // [T, E] or NULL: read idx/wts
+  int E;
+  int32_t* idx;         // [T, kcap]: output when logits is given, else input
+  float* wts;
+  int32_t* k_used;      // device scalar: output when logits is given, else input (may be NULL)
+  float* entropy;
+};
+
+template <typename F>
+__device__ __forceinline__ void for_slot(int s, F f) {
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_K_DEV; ++j)
+    if (j == s) f(j);
+}
 
 template <int BITS>
 struct Chunk {
@@ -38,45 +65,79 @@ int gemv_lanes_chunks(int K, int bits) {
   return (K / vals + 63) / 64;
 }
 
-// dot of one 16-byte weight chunk with its activation pairs (fp32 accumulate)
+// Per-chunk activation terms: 1024 * (sum over the 1024+q pairs),
+// 1024 * (sum over the 1024+16q pairs), and the plain sum.
+struct XSums {
+  float ca, cb, x;
+};
+
+// Activation sums of one chunk held as fp16 pairs in unpack order.
 template <int BITS>
-__device__ __forceinline__ float chunk_dot(u32x4 w, const uint32_t* xp) {
-  float acc = 0.0f;
-  uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+__device__ __forceinline__ XSums chunk_xsums(const uint32_t* xp) {
+  XSums r = {0.0f, 0.0f, 0.0f};
   if constexpr (BITS == 4) {
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int j = 0; j < Chunk<4>::PAIRS; ++j) {
+      const f16x2 hp = __builtin_bit_cast(f16x2, xp[j]);
+      const float s2 = (float)hp.x + (float)hp.y;
+      if ((j & 1) == 0) a += s2;  // pairs (k0,k4), (k2,k6)
+      else b += s2;               // pairs (k1,k5), (k3,k7)
+    }
+    r.ca = 1024.0f * a;
+    r.cb = 1024.0f * b;
+    r.x = a + b;
+  } else if constexpr (BITS == 8) {
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < Chunk<8>::PAIRS; ++j) {
+      const f16x2 hp = __builtin_bit_cast(f16x2, xp[j]);
+      a += (float)hp.x + (float)hp.y;
+    }
+    r.ca = 1024.0f * a;
+    r.x = a;
+  }
+  return r;
+}
+
+// Contribution of one 16-byte chunk of weights to its row (affine terms applied).
+template <int BITS>
+__device__ __forceinline__ float chunk_value(u32x4 w, const uint32_t* xp, const XSums& xs, uint32_t s_bits,
+                                             uint32_t b_bits, const Q4Consts& qc) {
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (BITS == 4) {
+    float A = 0.0f, B = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t p[4];
-      q4_word_to_biased_pairs(wv[j], p);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc = dot2(p[i], xp[4 * j + i], acc);
+      uint32_t p04, p15, p26, p37;
+      q4_word_unpack(wv[j], qc, p04, p15, p26, p37);
+      A = dot2(p04, xp[4 * j + 0], A);
+      B = dot2(p15, xp[4 * j + 1], B);
+      A = dot2(p26, xp[4 * j + 2], A);
+      B = dot2(p37, xp[4 * j + 3], B);
     }
+    const float qa = A - xs.ca;
+    const float qb = B - xs.cb;
+    const float dq = qa + 0.0625f * qb;
+    const float s = f16_bits_to_f32(s_bits), b = f16_bits_to_f32(b_bits);
+    return s * dq + b * xs.x;
   } else if constexpr (BITS == 8) {
+    float A = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t p[2];
       q8_word_to_biased_pairs(wv[j], p);
-      acc = dot2(p[0], xp[2 * j], acc);
-      acc = dot2(p[1], xp[2 * j + 1], acc);
+      A = dot2(p[0], xp[2 * j], A);
+      A = dot2(p[1], xp[2 * j + 1], A);
     }
+    const float dq = A - xs.ca;
+    const float s = f16_bits_to_f32(s_bits), b = f16_bits_to_f32(b_bits);
+    return s * dq + b * xs.x;
   } else {
+    float A = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = dot2(wv[j], xp[j], acc);
-  }
-  return acc;
-}
-
-// chunk dot -> contribution of the chunk to the row (affine terms applied)
-template <int BITS>
-__device__ __forceinline__ float chunk_value(float d, float xsum, uint32_t s_bits, uint32_t b_bits) {
-  if constexpr (BITS == 16) {
-    return d;
-  } else {
-    float s = f16_bits_to_f32(s_bits), b = f16_bits_to_f32(b_bits);
-    float c = 1024.0f * xsum;
-    float a = s * (d - c);
-    float bb = b * xsum;
-    return a + bb;
+    for (int j = 0; j < 4; ++j) A = dot2(wv[j], xp[j], A);
+    return A;
   }
 }
 
@@ -85,18 +146,98 @@ __device__ __forceinline__ float chunk_value(float d, float xsum, uint32_t s_bit
 struct GemvUpParams {
   const uint16_t* x;
   int act;
-  const int32_t* idx;
-  const int32_t* k_used;
+  RouteSrc rt;
   int k_static, kcap;
   int H, N;  // N: output columns (fused: inter) or rows (single)
   WView w0, w1;
   uint16_t* h;
   float* out32;
-  int iters;            // row-iterations per pair
+  int iters;  // row-iterations per pair
   int iters_per_wave;
 };
 
-constexpr int GEMV_ROWS = 4;  // rows per iteration
+// rows per iteration: 4 for short rows, 2 when a lane holds more chunks
+// (keeps two iterations of loads in registers without spilling)
+template <int CPL>
+struct Rows {
+  static constexpr int N = CPL <= 2 ? 4 : 2;
+};
+
+// raw bytes of one iteration's rows, as seen by one lane
+template <int BITS, int CPL>
+struct RowBuf {
+  static constexpr int R = Rows<CPL>::N;
+  u32x4 q[R][CPL];
+  uint32_t s[R][CPL], b[R][CPL];
+};
+
+// Row r of iteration `it`.  Fused: the first half of the rows are gate rows
+// j, the second half the up rows j of the same output columns.  Single: R
+// consecutive rows of one projection.
+template <int CPL, bool FUSED>
+__device__ __forceinline__ int row_of(int it, int r) {
+  constexpr int R = Rows<CPL>::N;
+  return FUSED ? (R / 2) * it + (r % (R / 2)) : R * it + r;
+}
+
+template <int BITS, int CPL, bool FUSED>
+__device__ __forceinline__ void load_rows(RowBuf<BITS, CPL>& buf, const GemvUpParams& prm, int e, int it,
+                                          const int* cc, int ng, int64_t row_bytes) {
+  using C = Chunk<BITS>;
+  constexpr int R = Rows<CPL>::N;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const WView& wv = (FUSED && r >= R / 2) ? prm.w1 : prm.w0;
+    const int64_t row = (int64_t)e * wv.stride + row_of<CPL, FUSED>(it, r);
+    const uint8_t* rq = wv.q + row * row_bytes;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      buf.q[r][i] = load_stream16(rq + (size_t)cc[i] * 16);
+      if constexpr (BITS != 16) {
+        buf.s[r][i] = wv.s[row * ng + cc[i] / C::PER_GROUP];
+        buf.b[r][i] = wv.b[row * ng + cc[i] / C::PER_GROUP];
+      }
+    }
+  }
+}
+
+template <int BITS, int CPL, bool FUSED>
+__device__ __forceinline__ void finish_iter(const RowBuf<BITS, CPL>& buf, const GemvUpParams& prm, int p, int it,
+                                            const uint32_t (*xr)[Chunk<BITS>::PAIRS], const XSums* xs,
+                                            const bool* valid, const Q4Consts& qc) {
+  constexpr int R = Rows<CPL>::N;
+  float part[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const float v = chunk_value<BITS>(buf.q[r][i], xr[i], xs[i], buf.s[r][i], buf.b[r][i], qc);
+      acc += valid[i] ? v : 0.0f;
+    }
+    part[r] = wave_sum(acc);
+  }
+  if (lane_id() == 0) {
+    if constexpr (FUSED) {
+      if constexpr (R == 4) {
+        const int j = 2 * it;
+        const uint32_t h0 = f32_to_f16_bits(swiglu(part[0], part[2]));
+        const uint32_t h1 = f32_to_f16_bits(swiglu(part[1], part[3]));
+        *(uint32_t*)(prm.h + (size_t)p * prm.N + j) = h0 | (h1 << 16);
+      } else {
+        prm.h[(size_t)p * prm.N + it] = f32_to_f16_bits(swiglu(part[0], part[1]));
+      }
+    } else {
+      if constexpr (R == 4) {
+        const f32x4 o = {part[0], part[1], part[2], part[3]};
+        *(f32x4*)(prm.out32 + (size_t)p * prm.N + R * it) = o;
+      } else {
+        prm.out32[(size_t)p * prm.N + R * it] = part[0];
+        prm.out32[(size_t)p * prm.N + R * it + 1] = part[1];
+      }
+    }
+  }
+}
 
 template <int BITS, int CPL, bool FUSED>
 __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
@@ -104,102 +245,101 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   const int lane = lane_id();
   const int p = blockIdx.y;
   const int t = p / prm.kcap, slot = p % prm.kcap;
-  const int ku = prm.k_used ? *prm.k_used : prm.k_static;
+  const int ku = prm.rt.logits ? prm.k_static : *prm.rt.k_used;
   if (slot >= ku) return;
-  const int e = prm.idx[p];
+  // iterations it = gw, gw + W, gw + 2W, ...: at any moment the waves of a
+  // pair read one contiguous stretch of rows, so each expert is swept linearly
   const int gw = blockIdx.x * 4 + threadIdx.x / WAVE;
-  const int it0 = gw * prm.iters_per_wave;
-  if (it0 >= prm.iters) return;
-  const int it1 = min(it0 + prm.iters_per_wave, prm.iters);
+  const int W = gridDim.x * 4;
+  if (gw >= prm.iters) return;
+  int e;
+  if (prm.rt.logits) {
+    int si[MOE_MAX_K_DEV];
+    float sw[MOE_MAX_K_DEV];
+    route_token(prm.rt.logits + (size_t)t * prm.rt.E, prm.rt.E, ku, si, sw);
+    float wsel = 0.0f;
+    e = 0;
+    for_slot(slot, [&](int j) {
+      e = si[j];
+      wsel = sw[j];
+    });
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      prm.rt.idx[p] = e;
+      prm.rt.wts[p] = wsel;
+      if (p == 0) {
+        *prm.rt.k_used = ku;
+        *prm.rt.entropy = 0.0f;
+      }
+    }
+  } else {
+    e = prm.rt.idx[p];
+  }
+  e = __builtin_amdgcn_readfirstlane(e);  // uniform: row addressing stays scalar
   const int H = prm.H;
   const int nch = H / C::VALS;
   const int ng = H / 64;
   const int64_t row_bytes = (int64_t)H * BITS / 8;
+  const Q4Consts qc = q4_consts();
 
-  // activations of this lane's chunks, as fp16 pairs in the unpack order
-  uint32_t xr[CPL][C::PAIRS];
-  float xs[CPL];
-  const uint16_t* xrow = prm.x + (size_t)t * H;
+  int cc[CPL];
+  bool valid[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
-    xs[i] = 0.0f;
+    valid[i] = c < nch;
+    cc[i] = valid[i] ? c : nch - 1;
+  }
+
+  // first rows in flight before the activations are prepared
+  // rows in flight before the activations are prepared; short rows keep two
+  // iterations ahead of the one being reduced, long rows one
+  constexpr bool DEEP = CPL <= 2;
+  RowBuf<BITS, CPL> bufA, bufB, bufC;
+  const int it1 = prm.iters;
+  load_rows<BITS, CPL, FUSED>(bufA, prm, e, gw, cc, ng, row_bytes);
+  if (DEEP && gw + W < it1) load_rows<BITS, CPL, FUSED>(bufB, prm, e, gw + W, cc, ng, row_bytes);
+
+  // activations of this lane's chunks, as fp16 pairs in the unpack order
+  uint32_t xr[CPL][C::PAIRS];
+  XSums xs[CPL];
+  const uint16_t* xrow = prm.x + (size_t)t * H;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
 #pragma unroll
     for (int j = 0; j < C::PIECES; ++j) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (c < nch) v = act8_to_f16(load16(xrow + (size_t)c * C::VALS + 8 * j), prm.act);
+      u32x4 v = act8_to_f16(load16(xrow + (size_t)cc[i] * C::VALS + 8 * j), prm.act);
       if constexpr (BITS == 4) v = perm8_nibble_order(v);
       xr[i][4 * j + 0] = v.x;
       xr[i][4 * j + 1] = v.y;
       xr[i][4 * j + 2] = v.z;
       xr[i][4 * j + 3] = v.w;
     }
-    if constexpr (BITS != 16) {
-#pragma unroll
-      for (int j = 0; j < C::PAIRS; ++j) {
-        f16x2 hp = __builtin_bit_cast(f16x2, xr[i][j]);
-        xs[i] += (float)hp.x;
-        xs[i] += (float)hp.y;
-      }
-    }
+    xs[i] = chunk_xsums<BITS>(xr[i]);
   }
 
-  for (int it = it0; it < it1; ++it) {
-    // the 4 rows of this iteration
-    const uint8_t* rq[GEMV_ROWS];
-    const uint16_t* rs[GEMV_ROWS];
-    const uint16_t* rb[GEMV_ROWS];
-#pragma unroll
-    for (int r = 0; r < GEMV_ROWS; ++r) {
-      const WView& wv = (FUSED && r >= 2) ? prm.w1 : prm.w0;
-      const int n = FUSED ? 2 * it + (r & 1) : GEMV_ROWS * it + r;
-      const int64_t row = (int64_t)e * wv.stride + n;
-      rq[r] = wv.q + row * row_bytes;
-      rs[r] = BITS == 16 ? nullptr : wv.s + row * ng;
-      rb[r] = BITS == 16 ? nullptr : wv.b + row * ng;
+  // two row buffers: the next iteration's loads are in flight while the
+  // current one is reduced
+  if constexpr (DEEP) {
+    for (int it = gw; it < it1; it += 3 * W) {
+      if (it + 2 * W < it1) load_rows<BITS, CPL, FUSED>(bufC, prm, e, it + 2 * W, cc, ng, row_bytes);
+      finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it, xr, xs, valid, qc);
+      if (it + W < it1) {
+        if (it + 3 * W < it1) load_rows<BITS, CPL, FUSED>(bufA, prm, e, it + 3 * W, cc, ng, row_bytes);
+        finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it + W, xr, xs, valid, qc);
+      }
+      if (it + 2 * W < it1) {
+        if (it + 4 * W < it1) load_rows<BITS, CPL, FUSED>(bufB, prm, e, it + 4 * W, cc, ng, row_bytes);
+        finish_iter<BITS, CPL, FUSED>(bufC, prm, p, it + 2 * W, xr, xs, valid, qc);
+      }
     }
-    u32x4 wq[GEMV_ROWS][CPL];
-    uint32_t sb[GEMV_ROWS][CPL], bb[GEMV_ROWS][CPL];
-#pragma unroll
-    for (int r = 0; r < GEMV_ROWS; ++r)
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nch) {
-          wq[r][i] = load_stream16(rq[r] + (size_t)c * 16);
-          if constexpr (BITS != 16) {
-            sb[r][i] = rs[r][c / C::PER_GROUP];
-            bb[r][i] = rb[r][c / C::PER_GROUP];
-          }
-        }
-      }
-    float part[GEMV_ROWS];
-#pragma unroll
-    for (int r = 0; r < GEMV_ROWS; ++r) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nch) {
-          float d = chunk_dot<BITS>(wq[r][i], xr[i]);
-          float v;
-          if constexpr (BITS == 16) v = chunk_value<BITS>(d, 0.0f, 0u, 0u);
-          else v = chunk_value<BITS>(d, xs[i], sb[r][i], bb[r][i]);
-          acc += v;
-        }
-      }
-      part[r] = wave_sum(acc);
-    }
-    if (lane == 0) {
-      if constexpr (FUSED) {
-        const int j = 2 * it;
-        uint32_t h0 = f32_to_f16_bits(swiglu(part[0], part[2]));
-        uint32_t h1 = f32_to_f16_bits(swiglu(part[1], part[3]));
-        *(uint32_t*)(prm.h + (size_t)p * prm.N + j) = h0 | (h1 << 16);
-      } else {
-        f32x4 o = {part[0], part[1], part[2], part[3]};
-        *(f32x4*)(prm.out32 + (size_t)p * prm.N + GEMV_ROWS * it) = o;
-      }
+    return;
+  }
+  for (int it = gw; it < it1; it += 2 * W) {
+    if (it + W < it1) load_rows<BITS, CPL, FUSED>(bufB, prm, e, it + W, cc, ng, row_bytes);
+    finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it, xr, xs, valid, qc);
+    if (it + W < it1) {
+      if (it + 2 * W < it1) load_rows<BITS, CPL, FUSED>(bufA, prm, e, it + 2 * W, cc, ng, row_bytes);
+      finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it + W, xr, xs, valid, qc);
     }
   }
 }
@@ -217,14 +357,13 @@ static hipError_t launch_up_cpl(int cpl, const GemvUpParams& prm, dim3 grid, hip
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_up(const void* x, int act, const int32_t* idx, const int32_t* k_used_dev, int k_static,
-                          int kcap, int T, int H, int N, int bits, bool fused, WView w0, WView w1, uint16_t* h,
-                          float* out32, hipStream_t st) {
+hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_static, int kcap, int T, int H,
+                          int N, int bits, bool fused, WView w0, WView w1, uint16_t* h, float* out32, int num_cu,
+                          hipStream_t st) {
   GemvUpParams prm;
   prm.x = (const uint16_t*)x;
   prm.act = act;
-  prm.idx = idx;
-  prm.k_used = k_used_dev;
+  prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy};
   prm.k_static = k_static;
   prm.kcap = kcap;
   prm.H = H;
@@ -233,136 +372,194 @@ hipError_t launch_gemv_up(const void* x, int act, const int32_t* idx, const int3
   prm.w1 = w1;
   prm.h = h;
   prm.out32 = out32;
-  prm.iters = fused ? N / 2 : N / GEMV_ROWS;
-  prm.iters_per_wave = 4;
   int cpl = gemv_lanes_chunks(H, bits);
   if (cpl > 4 && cpl <= 8) cpl = 8;
-  const int waves = (prm.iters + prm.iters_per_wave - 1) / prm.iters_per_wave;
-  dim3 grid((waves + 3) / 4, T * kcap);
+  const int rows = cpl <= 2 ? 4 : 2;
+  prm.iters = fused ? N / (rows / 2) : N / rows;
+  // about `waves_per_cu` resident waves per CU, shared by the pairs
+  const int64_t want = (int64_t)(num_cu > 0 ? num_cu : 256) * tuning(TUNE_UP_WAVES_PER_CU);
+  int64_t per_pair = want / ((int64_t)T * kcap);
+  if (per_pair < 4) per_pair = 4;
+  if (per_pair > prm.iters) per_pair = prm.iters;
+  prm.iters_per_wave = (int)((prm.iters + per_pair - 1) / per_pair);
+  dim3 grid((unsigned)((per_pair + 3) / 4), T * kcap);
   if (bits == 4) return fused ? launch_up_cpl<4, true>(cpl, prm, grid, st) : launch_up_cpl<4, false>(cpl, prm, grid, st);
   if (bits == 8) return fused ? launch_up_cpl<8, true>(cpl, prm, grid, st) : launch_up_cpl<8, false>(cpl, prm, grid, st);
   return fused ? launch_up_cpl<16, true>(cpl, prm, grid, st) : launch_up_cpl<16, false>(cpl, prm, grid, st);
 }
 
 // ---------------------------------------------------- down + combine ------
+//
+// Workgroup = kcap waves, wave s handles slot s of token t: it keeps the
+// slot's SwiGLU row h in registers (in unpack order, with per-chunk sums) and
+// streams R rows m = blockIdx.x + j * gridDim.x of that slot's expert (so all
+// workgroups sweep the down weights linearly).  The row values o_s[m] meet in
+// LDS and wave 0 combines them in slot order: y = sum_s w_s * o_s.
 
-constexpr int DOWN_WAVES = 16;
+constexpr int DOWN_MAX_ROWS = 64;
 
 size_t gemv_down_lds_bytes(int kcap, int I, int bits) {
-  int vals = bits == 4 ? 32 : (bits == 8 ? 16 : 8);
-  size_t nch = (size_t)I / vals;
-  return (size_t)kcap * I * 2 + (bits == 16 ? 0 : (size_t)kcap * nch * 4);
+  (void)I;
+  (void)bits;
+  return (size_t)kcap * DOWN_MAX_ROWS * 4;
 }
 
 struct GemvDownParams {
   const uint16_t* h;  // fp16 [T*kcap, I], pair order
-  const int32_t* idx;
-  const float* wts;
-  const int32_t* k_used;
+  RouteSrc rt;
   int k_static, kcap;
   int H, I;
+  int rows;           // rows per workgroup
   WView wd;
   void* y;
   int act;
 };
 
-// Workgroup = 16 waves = 16 output rows of one token.  The token's SwiGLU
-// rows are staged in LDS once (piece-major so lanes read consecutive 16-byte
-// words), with per-chunk sums for the affine terms.
-template <int BITS>
+template <int BITS, int DCPL>
+struct DownBuf {
+  u32x4 q[DCPL];
+  uint32_t s[DCPL], b[DCPL];
+};
+
+template <int BITS, int DCPL>
+__device__ __forceinline__ void load_down_row(DownBuf<BITS, DCPL>& buf, const GemvDownParams& prm, int e, int m,
+                                              const int* cc, int ng, int64_t row_bytes) {
+  using C = Chunk<BITS>;
+  const int64_t row = (int64_t)e * prm.wd.stride + m;
+  const uint8_t* rq = prm.wd.q + row * row_bytes;
+#pragma unroll
+  for (int i = 0; i < DCPL; ++i) {
+    buf.q[i] = load_stream16(rq + (size_t)cc[i] * 16);
+    if constexpr (BITS != 16) {
+      buf.s[i] = prm.wd.s[row * ng + cc[i] / C::PER_GROUP];
+      buf.b[i] = prm.wd.b[row * ng + cc[i] / C::PER_GROUP];
+    }
+  }
+}
+
+// KS waves share a slot: wave ks owns lane chunks i in [ks*DC, (ks+1)*DC)
+// of every row (DC chunks per lane), halving the registers a long row needs.
+template <int BITS, int DC, int KS>
 __global__ __launch_bounds__(1024) void gemv_down_kernel(GemvDownParams prm) {
   using C = Chunk<BITS>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ float part[MOE_MAX_K_DEV][KS][DOWN_MAX_ROWS];
   const int t = blockIdx.y;
-  const int ku = prm.k_used ? *prm.k_used : prm.k_static;
+  const int wv = threadIdx.x / WAVE;
+  const int s = wv / KS, ks = wv % KS;
+  const int lane = lane_id();
+  const int ku = prm.rt.logits ? prm.k_static : *prm.rt.k_used;
   const int I = prm.I;
   const int nch = I / C::VALS;
   const int ng = I / 64;
-  u32x4* hl = (u32x4*)lds;                                   // [kcap][PIECES][nch]
-  float* hsum = (float*)(lds + (size_t)prm.kcap * I * 2);   // [kcap][nch]
+  const int G = gridDim.x;
+  const int R = prm.rows;
+  const int64_t row_bytes = (int64_t)I * BITS / 8;
+  const Q4Consts qc = q4_consts();
 
-  for (int s = 0; s < ku; ++s) {
+  // the token's experts and routing weights, uniform across the wave
+  int si[MOE_MAX_K_DEV];
+  float sw[MOE_MAX_K_DEV];
+  if (prm.rt.logits) {
+    route_token(prm.rt.logits + (size_t)t * prm.rt.E, prm.rt.E, ku, si, sw);
+  } else {
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_K_DEV; ++j) {
+      si[j] = j < ku ? prm.rt.idx[(size_t)t * prm.kcap + j] : 0;
+      sw[j] = j < ku ? prm.rt.wts[(size_t)t * prm.kcap + j] : 0.0f;
+    }
+  }
+
+  if (s < ku) {
+    int e = 0;
+    for_slot(s, [&](int j) { e = si[j]; });
+    e = __builtin_amdgcn_readfirstlane(e);
+    int cc[DC];
+    bool valid[DC];
+#pragma unroll
+    for (int i = 0; i < DC; ++i) {
+      const int c = lane + 64 * (ks * DC + i);
+      valid[i] = c < nch;
+      cc[i] = valid[i] ? c : nch - 1;
+    }
+    DownBuf<BITS, DC> bufA, bufB;
+    const int m0 = blockIdx.x;
+    load_down_row<BITS, DC>(bufA, prm, e, m0, cc, ng, row_bytes);
+
+    // this slot's SwiGLU row (the wave's chunks), as fp16 pairs in unpack order
+    uint32_t hr[DC][C::PAIRS];
+    XSums hs[DC];
     const uint16_t* hrow = prm.h + ((size_t)t * prm.kcap + s) * I;
-    for (int q = threadIdx.x; q < nch * C::PIECES; q += blockDim.x) {
-      const int c = q / C::PIECES, j = q % C::PIECES;
-      u32x4 v = load16(hrow + (size_t)q * 8);
-      if constexpr (BITS == 4) v = perm8_nibble_order(v);
-      hl[((size_t)s * C::PIECES + j) * nch + c] = v;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) {
+#pragma unroll
+      for (int j = 0; j < C::PIECES; ++j) {
+        u32x4 v = load16(hrow + (size_t)cc[i] * C::VALS + 8 * j);
+        if constexpr (BITS == 4) v = perm8_nibble_order(v);
+        hr[i][4 * j + 0] = v.x;
+        hr[i][4 * j + 1] = v.y;
+        hr[i][4 * j + 2] = v.z;
+        hr[i][4 * j + 3] = v.w;
+      }
+      hs[i] = chunk_xsums<BITS>(hr[i]);
+    }
+
+    auto row_value = [&](const DownBuf<BITS, DC>& buf) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < DC; ++i) {
+        const float v = chunk_value<BITS>(buf.q[i], hr[i], hs[i], buf.s[i], buf.b[i], qc);
+        acc += valid[i] ? v : 0.0f;
+      }
+      return wave_sum(acc);
+    };
+
+    for (int j = 0; j < R; j += 2) {
+      const int ma = m0 + j * G, mb = m0 + (j + 1) * G;
+      const bool hb = j + 1 < R && mb < prm.H;
+      if (hb) load_down_row<BITS, DC>(bufB, prm, e, mb, cc, ng, row_bytes);
+      if (ma < prm.H) {
+        const float o = row_value(bufA);
+        if (lane == 0) part[s][ks][j] = o;
+      }
+      if (hb) {
+        const int mc = m0 + (j + 2) * G;
+        if (j + 2 < R && mc < prm.H) load_down_row<BITS, DC>(bufA, prm, e, mc, cc, ng, row_bytes);
+        const float o = row_value(bufB);
+        if (lane == 0) part[s][ks][j + 1] = o;
+      }
     }
   }
   __syncthreads();
-  if constexpr (BITS != 16) {
-    for (int q = threadIdx.x; q < ku * nch; q += blockDim.x) {
-      const int s = q / nch, c = q % nch;
-      float a = 0.0f;
-      for (int j = 0; j < C::PIECES; ++j) {
-        u32x4 v = hl[((size_t)s * C::PIECES + j) * nch + c];
-        uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        for (int i = 0; i < 4; ++i) {
-          f16x2 hp = __builtin_bit_cast(f16x2, w4[i]);
-          a += (float)hp.x;
-          a += (float)hp.y;
-        }
-      }
-      hsum[q] = a;
-    }
-    __syncthreads();
-  }
-
-  const int lane = lane_id();
-  const int m = blockIdx.x * DOWN_WAVES + threadIdx.x / WAVE;
-  if (m >= prm.H) return;
-  const int64_t row_bytes = (int64_t)I * BITS / 8;
-  float y = 0.0f;
-  for (int s = 0; s < ku; ++s) {
-    const int e = prm.idx[(size_t)t * prm.kcap + s];
-    const int64_t row = (int64_t)e * prm.wd.stride + m;
-    const uint8_t* rq = prm.wd.q + row * row_bytes;
-    const uint16_t* rs = BITS == 16 ? nullptr : prm.wd.s + row * ng;
-    const uint16_t* rb = BITS == 16 ? nullptr : prm.wd.b + row * ng;
-    float acc = 0.0f;
-    for (int c = lane; c < nch; c += 64) {
-      u32x4 w = load_stream16(rq + (size_t)c * 16);
-      uint32_t xp[C::PAIRS];
+  if (wv == 0 && lane < R) {
+    const int m = blockIdx.x + lane * G;
+    if (m < prm.H) {
+      float y = 0.0f;
+      for (int q = 0; q < ku; ++q) {
+        float w = 0.0f;
+        for_slot(q, [&](int j) { w = sw[j]; });
+        float o = part[q][0][lane];
 #pragma unroll
-      for (int j = 0; j < C::PIECES; ++j) {
-        u32x4 v = hl[((size_t)s * C::PIECES + j) * nch + c];
-        xp[4 * j + 0] = v.x;
-        xp[4 * j + 1] = v.y;
-        xp[4 * j + 2] = v.z;
-        xp[4 * j + 3] = v.w;
+        for (int k2 = 1; k2 < KS; ++k2) o = o + part[q][k2][lane];
+        const float c = w * o;
+        y = y + c;
       }
-      float d = chunk_dot<BITS>(w, xp);
-      float v;
-      if constexpr (BITS == 16) v = chunk_value<BITS>(d, 0.0f, 0u, 0u);
-      else v = chunk_value<BITS>(d, hsum[s * nch + c], rs[c / C::PER_GROUP], rb[c / C::PER_GROUP]);
-      acc += v;
+      ((uint16_t*)prm.y)[(size_t)t * prm.H + m] = f32_to_act_bits(y, prm.act);
     }
-    const float o = wave_sum(acc);
-    const float ws = prm.wts[(size_t)t * prm.kcap + s];
-    const float contrib = ws * o;
-    y = y + contrib;
   }
-  if (lane == 0) ((uint16_t*)prm.y)[(size_t)t * prm.H + m] = f32_to_act_bits(y, prm.act);
 }
 
 hipError_t gemv_down_set_max_lds(int bytes) {
-  hipError_t e = hipFuncSetAttribute((const void*)gemv_down_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void*)gemv_down_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void*)gemv_down_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  return e;
+  (void)bytes;
+  return hipSuccess;
 }
 
-hipError_t launch_gemv_down(const uint16_t* h, const int32_t* idx, const float* wts, const int32_t* k_used_dev,
-                            int k_static, int kcap, int T, int H, int I, int bits, WView wd, void* y, int act,
-                            hipStream_t st) {
+int gemv_down_max_chunks_per_lane() { return 6; }
+
+hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_static, int kcap, int T, int H, int I,
+                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st) {
   GemvDownParams prm;
   prm.h = h;
-  prm.idx = idx;
-  prm.wts = wts;
-  prm.k_used = k_used_dev;
+  prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy};
   prm.k_static = k_static;
   prm.kcap = kcap;
   prm.H = H;
@@ -370,11 +567,26 @@ hipError_t launch_gemv_down(const uint16_t* h, const int32_t* idx, const float* 
   prm.wd = wd;
   prm.y = y;
   prm.act = act;
-  const size_t lds = gemv_down_lds_bytes(kcap, I, bits);
-  dim3 grid((H + DOWN_WAVES - 1) / DOWN_WAVES, T);
-  if (bits == 4) gemv_down_kernel<4><<<grid, 1024, lds, st>>>(prm);
-  else if (bits == 8) gemv_down_kernel<8><<<grid, 1024, lds, st>>>(prm);
-  else gemv_down_kernel<16><<<grid, 1024, lds, st>>>(prm);
+  const int dcpl = gemv_lanes_chunks(I, bits);
+  const int ks = dcpl >= 4 ? 2 : 1;            // waves per slot
+  const int dc = (dcpl + ks - 1) / ks;          // chunks per lane per wave
+  // rows per workgroup so that about `waves_per_cu` waves per CU are resident
+  const int64_t want = (int64_t)(num_cu > 0 ? num_cu : 256) * tuning(TUNE_DOWN_WAVES_PER_CU);
+  int64_t groups = want / ((int64_t)T * kcap * ks);
+  if (groups < 1) groups = 1;
+  int rows = (int)((H + groups - 1) / groups);
+  if (rows < 2) rows = 2;
+  if (rows > DOWN_MAX_ROWS) rows = DOWN_MAX_ROWS;
+  prm.rows = rows;
+  const int G = (H + rows - 1) / rows;
+  dim3 grid(G, T);
+  dim3 block(64 * kcap * ks);
+#define X(B, D, K) \
+  if (bits == B && dc == D && ks == K) gemv_down_kernel<B, D, K><<<grid, block, 0, st>>>(prm); else
+#define CASES(B) X(B, 1, 1) X(B, 2, 1) X(B, 3, 1) X(B, 2, 2) X(B, 3, 2)
+  CASES(4) CASES(8) CASES(16) return hipErrorInvalidValue;
+#undef CASES
+#undef X
   return hipGetLastError();
 }
 

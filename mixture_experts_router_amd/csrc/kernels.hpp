@@ -9,6 +9,11 @@
 
 namespace moe {
 
+// Launch-shape knobs (resident waves per CU the decode kernels aim for).
+// Defaults are the measured best; moe_debug_set_tuning overrides them.
+enum TuneKey { TUNE_UP_WAVES_PER_CU = 0, TUNE_DOWN_WAVES_PER_CU = 1, TUNE_KEYS = 2 };
+int tuning(TuneKey key);
+
 // One expert weight view: row n of expert e starts at q + (e*stride + n)*row_bytes.
 struct WView {
   const uint8_t* q;
@@ -32,18 +37,32 @@ hipError_t launch_sort_pairs(const int32_t* idx, int T, int kcap, const int32_t*
 // ------------------------------------------------- decode (grouped GEMV)
 // chunks of 16 bytes per lane needed for a row of K weights
 int gemv_lanes_chunks(int K, int bits);
+// Where a decode kernel gets its routing: with `logits` set (static k) it
+// selects the experts itself and writes idx/wts/k_used/entropy (from the
+// gate+up kernel); with `logits` NULL it reads idx, wts and *k_used.
+struct GemvRoute {
+  const float* logits;
+  int E;
+  int32_t* idx;
+  float* wts;
+  int32_t* k_used;
+  float* entropy;
+};
 // fused=true: h[p, j] = fp16(swiglu(gate_j . x, up_j . x)) for j < I
 // fused=false: out32[p, n] = w0_n . x for n < N
-hipError_t launch_gemv_up(const void* x, int act, const int32_t* idx, const int32_t* k_used_dev, int k_static,
-                          int kcap, int T, int H, int N, int bits, bool fused, WView w0, WView w1, uint16_t* h,
-                          float* out32, hipStream_t st);
+hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_static, int kcap, int T, int H,
+                          int N, int bits, bool fused, WView w0, WView w1, uint16_t* h, float* out32, int num_cu,
+                          hipStream_t st);
 // y[t, m] = act(sum_s w[t,s] * (Wd[e_s, m, :] . h[t*kcap+s, :]))
 size_t gemv_down_lds_bytes(int kcap, int I, int bits);
 // allow the down kernels up to `bytes` of dynamic LDS (once per device)
 hipError_t gemv_down_set_max_lds(int bytes);
-hipError_t launch_gemv_down(const uint16_t* h, const int32_t* idx, const float* wts, const int32_t* k_used_dev,
-                            int k_static, int kcap, int T, int H, int I, int bits, WView wd, void* y, int act,
-                            hipStream_t st);
+// largest 16-byte chunks per lane of a down row the decode kernels handle
+int gemv_down_max_chunks_per_lane();
+hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_static, int kcap, int T, int H, int I,
+                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st);
+// tokens up to which the router uses one workgroup per (expert, token)
+int router_small_max_tokens();
 
 // -------------------------------------------------- batched (MFMA GEMM)
 enum GemmMode { GEMM_FUSED_SWIGLU = 0, GEMM_GATHER_F32 = 1, GEMM_ROWS_F16 = 2 };

@@ -59,6 +59,7 @@ struct DevProps {
   bool ok = false;
   bool gfx950 = false;
   size_t lds_max = 0;
+  int num_cu = 0;
 };
 
 std::mutex g_props_mu;
@@ -74,6 +75,7 @@ moe_status device_props(DevProps* out) {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
     p.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     p.lds_max = prop.sharedMemPerBlock;
+    p.num_cu = prop.multiProcessorCount;
     if (p.lds_max > 65536 && moe::gemv_down_set_max_lds((int)p.lds_max) != hipSuccess) {
       (void)hipGetLastError();  // keep the portable 64 KB limit for the decode path
       p.lds_max = 65536;
@@ -102,8 +104,9 @@ moe_status check_weights(const moe_weights* w, int E, int N, int K) {
   return MOE_OK;
 }
 
+// Buffers sized by T (x, y, routing outputs) may be NULL when T == 0.
 moe_status check_router(const void* x, moe_dtype dt, int T, int H, const void* wr, int E, int k) {
-  if (!x || !wr) return MOE_ERR_NULL;
+  if ((!x && T != 0) || !wr) return MOE_ERR_NULL;
   if (dt != MOE_F16 && dt != MOE_BF16) return MOE_ERR_DTYPE;
   if (T < 0 || H <= 0 || H % 64 != 0) return MOE_ERR_SHAPE;
   if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
@@ -112,7 +115,7 @@ moe_status check_router(const void* x, moe_dtype dt, int T, int H, const void* w
   } else if (k < 1 || k > MOE_MAX_K || k > E) {
     return MOE_ERR_K;
   }
-  if (!aligned16(x) || !aligned16(wr)) return MOE_ERR_ALIGN;
+  if ((T != 0 && !aligned16(x)) || !aligned16(wr)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -186,8 +189,8 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   // ---- validation (host only)
   moe_status s = check_router(x, dt, T, H, router_w, E, k);
   if (s != MOE_OK) return s;
-  if (!y || !down) return MOE_ERR_NULL;
-  if (!aligned16(y)) return MOE_ERR_ALIGN;
+  if ((!y && T != 0) || !down) return MOE_ERR_NULL;
+  if (T != 0 && !aligned16(y)) return MOE_ERR_ALIGN;
   const int I = down->K;
   if (I <= 0 || I % 64 != 0) return MOE_ERR_SHAPE;
   if ((s = check_weights(down, E, H, I)) != MOE_OK) return s;
@@ -235,35 +238,52 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   float* u32 = (float*)(W + L.u32);
   const bool unfused = (flags & MOE_FLAG_UNFUSED) != 0;
   const int act = (int)dt;
+  (void)pos;
 
-  const bool gemv_fits = moe::gemv_lanes_chunks(H, bits) <= 8 &&
+  const bool gemv_fits = moe::gemv_lanes_chunks(H, bits) <= 4 &&
+                         moe::gemv_lanes_chunks(I, bits) <= moe::gemv_down_max_chunks_per_lane() &&
                          moe::gemv_down_lds_bytes(kcap, I, bits) <= props.lds_max;
   bool gemv = false;
   if (!(flags & MOE_FLAG_FORCE_MFMA)) gemv = gemv_fits && ((flags & MOE_FLAG_FORCE_GEMV) || P <= kGemvMaxPairs);
-  const bool need_sort = !gemv || (taps && (taps->counts || taps->offsets || taps->perm));
+  const bool want_sort_taps = taps && (taps->counts || taps->offsets || taps->perm);
+  const int k_static = k > 0 ? k : 0;
 
   plan_begin(st);
-  if ((s = route_impl(x, dt, T, H, router_w, E, k, idx, wts, k_used, entropy, logits, st)) != MOE_OK) return s;
-  if (need_sort) {
-    HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k > 0 ? k : 0, E, counts, offsets, perm, pos, st));
-    plan_step("sort_pairs", st);
-  }
-  const int k_static = k > 0 ? k : 0;
   if (gemv) {
+    // decode path: with static k the GEMV kernels select the experts from the
+    // logits themselves (no separate selection launch)
+    HIP_TRY(moe::launch_router_logits(x, router_w, logits, T, H, E, act, st));
+    plan_step("router_logits", st);
+    moe::GemvRoute rt{logits, E, idx, wts, k_used, entropy};
+    if (k <= 0) {
+      HIP_TRY(moe::launch_topk(logits, T, E, k, idx, wts, k_used, entropy, st));
+      plan_step("topk_entropy", st);
+      rt.logits = nullptr;
+    }
     if (!unfused) {
-      HIP_TRY(moe::launch_gemv_up(x, act, idx, k_used, k_static, kcap, T, H, I, bits, true, wg, wu, h, nullptr, st));
+      HIP_TRY(moe::launch_gemv_up(x, act, rt, k_static, kcap, T, H, I, bits, true, wg, wu, h, nullptr, props.num_cu,
+                                  st));
       plan_step("gemv_gate_up_swiglu", st);
     } else {
-      HIP_TRY(moe::launch_gemv_up(x, act, idx, k_used, k_static, kcap, T, H, I, bits, false, wg, wg, nullptr, g32, st));
+      HIP_TRY(moe::launch_gemv_up(x, act, rt, k_static, kcap, T, H, I, bits, false, wg, wg, nullptr, g32,
+                                  props.num_cu, st));
       plan_step("gemv_gate", st);
-      HIP_TRY(moe::launch_gemv_up(x, act, idx, k_used, k_static, kcap, T, H, I, bits, false, wu, wu, nullptr, u32, st));
+      HIP_TRY(moe::launch_gemv_up(x, act, rt, k_static, kcap, T, H, I, bits, false, wu, wu, nullptr, u32,
+                                  props.num_cu, st));
       plan_step("gemv_up", st);
       HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, st));
       plan_step("swiglu", st);
     }
-    HIP_TRY(moe::launch_gemv_down(h, idx, wts, k_used, k_static, kcap, T, H, I, bits, view_of(down, 0), y, act, st));
+    HIP_TRY(moe::launch_gemv_down(h, rt, k_static, kcap, T, H, I, bits, view_of(down, 0), y, act, props.num_cu, st));
     plan_step("gemv_down_combine", st);
+    if (want_sort_taps) {
+      HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st));
+      plan_step("sort_pairs", st);
+    }
   } else {
+    if ((s = route_impl(x, dt, T, H, router_w, E, k, idx, wts, k_used, entropy, logits, st)) != MOE_OK) return s;
+    HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st));
+    plan_step("sort_pairs", st);
     const int bm = moe::gemm_block_m((int)P, E);
     const int mt = moe::gemm_max_mtiles((int)P, E, bm);
     if (!unfused) {
@@ -307,6 +327,16 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
 
 }  // namespace
 
+namespace moe {
+namespace {
+int g_tuning[TUNE_KEYS] = {8, 8};
+}
+int tuning(TuneKey key) { return g_tuning[key]; }
+void set_tuning(int key, int value) {
+  if (key >= 0 && key < TUNE_KEYS && value > 0) g_tuning[key] = value;
+}
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_status_string(moe_status s) {
@@ -339,8 +369,8 @@ moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const vo
   try {
     moe_status s = check_router(x, dt, T, H, router_w, E, k);
     if (s != MOE_OK) return s;
-    if (!topk_idx || !topk_w) return MOE_ERR_NULL;
     if (T == 0) return MOE_OK;
+    if (!topk_idx || !topk_w) return MOE_ERR_NULL;
     float* logits = logits_out;
     if (!logits) {
       if (!ws) return MOE_ERR_WORKSPACE;
@@ -364,8 +394,8 @@ moe_status moe_topk_from_logits(const float* logits, int32_t T, int32_t E, int32
   try {
     (void)ws;
     (void)ws_bytes;
-    if (!logits || !topk_idx || !topk_w) return MOE_ERR_NULL;
     if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+    if (T != 0 && (!logits || !topk_idx || !topk_w)) return MOE_ERR_NULL;
     if (k == MOE_K_ENTROPY) {
       if (E < MOE_K_ENTROPY_CAP) return MOE_ERR_K;
     } else if (k < 1 || k > MOE_MAX_K || k > E) {
@@ -456,6 +486,8 @@ void moe_debug_set_events(void* const* events, int32_t n) {
   g_prof.n = events ? n : 0;
   g_prof.next = 0;
 }
+
+void moe_debug_set_tuning(int32_t key, int32_t value) { moe::set_tuning(key, value); }
 
 int32_t moe_debug_last_plan(char* buf, size_t buf_bytes) {
   const std::string& p = g_prof.plan;

@@ -4,26 +4,68 @@
 // logits[t, e] = sum_h x[t, h] * Wr[e, h], fp32 accumulation (page "Qwen3.5
 // Block在llama.cpp中的映射与优化原理", section 4.1: the router is one linear
 // layer followed by softmax and top-k).  Selection is made on logits with the
-// key (larger logit, lower index); weights are exp(l_s - l_1) / sum over the
-// selected slots, the softmax renormalised over the selected experts.
-// Entropy-adaptive k (page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析", section
-// 2.2): mean over the call's tokens of the Shannon entropy (nats) of the
-// routing distribution; k = 1 if H < 1.2, 2 if H < 2.5, else 3.
+// key (larger logit, lower index); see topk.hpp.  Entropy-adaptive k (page
+// "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析", section 2.2): mean over the call's
+// tokens of the Shannon entropy (nats) of the routing distribution; k = 1 if
+// H < 1.2, 2 if H < 2.5, else 3.
+//
+// Products of two fp16 (or two bf16) values are exact in fp32, so fmaf here
+// rounds exactly like a separate multiply and add.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace moe {
 
-// --------------------------------------------------------------- logits --
+__device__ __forceinline__ void unpack8(u32x4 r, int act, float* v) {
+  const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = act_to_f32(w4[i] & 0xFFFFu, act);
+    v[2 * i + 1] = act_to_f32(w4[i] >> 16, act);
+  }
+}
+
+// --------------------------------------------------------- small batches --
 //
-// A wave computes a TT-token x 4-expert tile; lane l owns the 8-element
-// column slices h = 8*l + 512*i.  Products of two fp16 (or two bf16) values
-// are exact in fp32; each lane sums its slice in order, then the wave sums the
-// 64 lane partials with a butterfly.
-template <int TT>
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ wr, float* __restrict__ logits,
-                                                            int T, int H, int E, int act) {
+// One workgroup per (expert, token); its four waves take consecutive quarters
+// of H, each lane sums its 8-element slices in order, the wave sums its lanes,
+// and the four wave partials are added in wave order.  Spreads a decode
+// step's router over E workgroups (E x 8 KB of router rows at H = 4096).
+__global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ wr,
+                                                                  float* __restrict__ logits, int H, int E,
+                                                                  int act) {
+  __shared__ float part[4];
+  const int e = blockIdx.x, t = blockIdx.y;
+  const int lane = lane_id(), wave = threadIdx.x / WAVE;
+  const int q = H / 4;
+  const uint16_t* xr = x + (size_t)t * H + wave * q;
+  const uint16_t* wrow = wr + (size_t)e * H + wave * q;
+  float acc = 0.0f;
+#pragma unroll 4
+  for (int h = lane * 8; h < q; h += 512) {
+    float xv[8], wv[8];
+    unpack8(load16(xr + h), act, xv);
+    unpack8(load16(wrow + h), act, wv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(xv[i], wv[i], acc);
+  }
+  const float s = wave_sum(acc);
+  if (lane == 0) part[wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) logits[(size_t)t * E + e] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+// ---------------------------------------------------------- large batches --
+//
+// A wave computes a 4-token x 4-expert tile; lane l owns the 8-element column
+// slices h = 8*l + 512*i.
+__global__ __launch_bounds__(256) void router_logits_tile_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wr,
+                                                                 float* __restrict__ logits, int T, int H, int E,
+                                                                 int act) {
+  constexpr int TT = 4;
   const int lane = lane_id();
   const int wave = threadIdx.x / WAVE;
   const int t0 = blockIdx.x * TT;
@@ -39,124 +81,32 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     float xv[TT][8], wv[4][8];
 #pragma unroll
     for (int a = 0; a < TT; ++a) {
-      int t = t0 + a;
-      u32x4 r = {0u, 0u, 0u, 0u};
-      if (t < T) r = load16(x + (size_t)t * H + h);
-      uint32_t w4[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xv[a][2 * i] = act_to_f32(w4[i] & 0xFFFFu, act);
-        xv[a][2 * i + 1] = act_to_f32(w4[i] >> 16, act);
-      }
+      const int t = min(t0 + a, T - 1);
+      unpack8(load16(x + (size_t)t * H + h), act, xv[a]);
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      int e = e0 + b;
-      u32x4 r = {0u, 0u, 0u, 0u};
-      if (e < E) r = load16(wr + (size_t)e * H + h);
-      uint32_t w4[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wv[b][2 * i] = act_to_f32(w4[i] & 0xFFFFu, act);
-        wv[b][2 * i + 1] = act_to_f32(w4[i] >> 16, act);
-      }
+      const int e = min(e0 + b, E - 1);
+      unpack8(load16(wr + (size_t)e * H + h), act, wv[b]);
     }
 #pragma unroll
     for (int a = 0; a < TT; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[a][b] = fmaf(xv[a][i], wv[b][i], acc[a][b]);  // exact product
+        for (int i = 0; i < 8; ++i) acc[a][b] = fmaf(xv[a][i], wv[b][i], acc[a][b]);
   }
 #pragma unroll
   for (int a = 0; a < TT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      float s = wave_sum(acc[a][b]);
-      int t = t0 + a, e = e0 + b;
+      const float s = wave_sum(acc[a][b]);
+      const int t = t0 + a, e = e0 + b;
       if (lane == 0 && t < T && e < E) logits[(size_t)t * E + e] = s;
     }
 }
 
-// ------------------------------------------------------------ selection --
-
-struct Cand {
-  float v;
-  int i;
-};
-
-// larger value first, lower index first among equal values; index -1 = none
-__device__ __forceinline__ Cand better(Cand a, Cand b) {
-  if (a.i < 0) return b;
-  if (b.i < 0) return a;
-  if (a.v > b.v) return a;
-  if (b.v > a.v) return b;
-  return a.i < b.i ? a : b;
-}
-
-__device__ __forceinline__ Cand wave_best(Cand c) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    Cand d;
-    d.v = __shfl_xor(c.v, o, WAVE);
-    d.i = __shfl_xor(c.i, o, WAVE);
-    c = better(c, d);
-  }
-  return c;
-}
-
-// One wave selects k of token t's E <= 256 logits (4 per lane, expert
-// e = lane + 64*j).  Returns the selected logits/indices in slot order in
-// every lane (arrays of MOE_MAX_K).
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, float* sv, int* si) {
-  const int lane = lane_id();
-  float v[4];
-  bool live[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int e = lane + 64 * j;
-    live[j] = e < E;
-    v[j] = live[j] ? row[e] : 0.0f;
-  }
-#pragma unroll
-  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
-    if (s < k) {
-      Cand c = {0.0f, -1};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Cand d = {v[j], live[j] ? lane + 64 * j : -1};
-        c = better(c, d);
-      }
-      c = wave_best(c);
-      sv[s] = c.v;
-      si[s] = c.i;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (lane + 64 * j == c.i) live[j] = false;
-    }
-  }
-}
-
-// weights of the first k selected slots; slots [k, kcap) get index -1, weight 0
-__device__ __forceinline__ void write_selection(int32_t* idx, float* w, const float* sv, const int* si, int k,
-                                                int kcap) {
-  float ex[MOE_MAX_K_DEV];
-  float z = 0.0f;
-#pragma unroll
-  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
-    if (s < k) {
-      ex[s] = expf(sv[s] - sv[0]);
-      z += ex[s];
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
-    if (s < kcap) {
-      idx[s] = s < k ? si[s] : -1;
-      w[s] = s < k ? ex[s] / z : 0.0f;
-    }
-  }
-}
+// ------------------------------------------------------------- selection --
 
 __global__ __launch_bounds__(256) void topk_static_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                           int32_t* __restrict__ idx, float* __restrict__ w,
@@ -167,10 +117,17 @@ __global__ __launch_bounds__(256) void topk_static_kernel(const float* __restric
     if (entropy) *entropy = 0.0f;
   }
   if (t >= T) return;
-  float sv[MOE_MAX_K_DEV];
   int si[MOE_MAX_K_DEV];
-  wave_topk(logits + (size_t)t * E, E, k, sv, si);
-  if (lane_id() == 0) write_selection(idx + (size_t)t * k, w + (size_t)t * k, sv, si, k, k);
+  float sw[MOE_MAX_K_DEV];
+  route_token(logits + (size_t)t * E, E, k, si, sw);
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int s = 0; s < MOE_MAX_K_DEV; ++s)
+      if (s < k) {
+        idx[(size_t)t * k + s] = si[s];
+        w[(size_t)t * k + s] = sw[s];
+      }
+  }
 }
 
 // Shannon entropy (nats) of softmax(row): H = ln Z - sum_e p_e (l_e - l_max)
@@ -180,7 +137,7 @@ __device__ __forceinline__ float wave_entropy(const float* __restrict__ row, int
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int e = lane + 64 * j;
+    const int e = lane + 64 * j;
     v[j] = e < E ? row[e] : -INFINITY;
     m = fmaxf(m, v[j]);
   }
@@ -189,8 +146,8 @@ __device__ __forceinline__ float wave_entropy(const float* __restrict__ row, int
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (lane + 64 * j < E) {
-      float d = v[j] - m;
-      float p = expf(d);
+      const float d = v[j] - m;
+      const float p = expf(d);
       z += p;
       s1 += p * d;
     }
@@ -217,35 +174,41 @@ __global__ __launch_bounds__(1024) void topk_entropy_kernel(const float* __restr
   if (threadIdx.x == 0) {
     float tot = 0.0f;
     for (int i = 0; i < 16; ++i) tot += part[i];
-    float h = tot / (float)T;
-    int k = h < 1.2f ? 1 : (h < 2.5f ? 2 : 3);
+    const float h = tot / (float)T;
+    const int k = h < 1.2f ? 1 : (h < 2.5f ? 2 : 3);
     k_sh = k;
     if (k_used) *k_used = k;
     if (entropy) *entropy = h;
   }
   __syncthreads();
   const int k = k_sh;
+  constexpr int KC = MOE_K_ENTROPY_CAP_DEV;
   for (int t = wave; t < T; t += 16) {
-    float sv[MOE_MAX_K_DEV];
     int si[MOE_MAX_K_DEV];
-    wave_topk(logits + (size_t)t * E, E, k, sv, si);
-    if (lane_id() == 0)
-      write_selection(idx + (size_t)t * MOE_K_ENTROPY_CAP_DEV, w + (size_t)t * MOE_K_ENTROPY_CAP_DEV, sv, si, k,
-                      MOE_K_ENTROPY_CAP_DEV);
+    float sw[MOE_MAX_K_DEV];
+    route_token(logits + (size_t)t * E, E, k, si, sw);
+    if (lane_id() == 0) {
+#pragma unroll
+      for (int s = 0; s < KC; ++s) {
+        idx[(size_t)t * KC + s] = si[s];
+        w[(size_t)t * KC + s] = sw[s];
+      }
+    }
   }
 }
 
 // ------------------------------------------------------------- launchers --
 
+int router_small_max_tokens() { return 16; }
+
 hipError_t launch_router_logits(const void* x, const void* wr, float* logits, int T, int H, int E, int act,
                                 hipStream_t st) {
-  dim3 block(256);
-  if (T < 4) {
-    dim3 grid(T, (E + 15) / 16);
-    router_logits_kernel<1><<<grid, block, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr, logits, T, H, E, act);
+  if (T <= router_small_max_tokens()) {
+    router_logits_small_kernel<<<dim3(E, T), 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr, logits, H, E,
+                                                            act);
   } else {
     dim3 grid((T + 3) / 4, (E + 15) / 16);
-    router_logits_kernel<4><<<grid, block, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr, logits, T, H, E, act);
+    router_logits_tile_kernel<<<grid, 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr, logits, T, H, E, act);
   }
   return hipGetLastError();
 }

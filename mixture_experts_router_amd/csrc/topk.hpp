@@ -1,0 +1,128 @@
+// Top-k selection of one token's logits by one wave (shared by the router
+// kernels and the decode GEMV kernels, which recompute it from the logits so
+// that every kernel sees the same experts and weights).
+//
+// Key: larger logit first, lower expert index first among equal logits.
+// Weights: exp(l_s - l_1) / sum over the selected slots of exp(l_s' - l_1),
+// i.e. the softmax renormalised over the selected experts (page "Qwen3.5
+// Block在llama.cpp中的映射与优化原理", section 4.1: linear -> softmax -> top-k).
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+struct Cand {
+  float v;
+  int i;
+};
+
+// larger value first, lower index first among equal values; index -1 = none
+__device__ __forceinline__ Cand better(Cand a, Cand b) {
+  if (a.i < 0) return b;
+  if (b.i < 0) return a;
+  if (a.v > b.v) return a;
+  if (b.v > a.v) return b;
+  return a.i < b.i ? a : b;
+}
+
+template <int CTRL>
+__device__ __forceinline__ Cand dpp_cand(Cand c) {
+  Cand d;
+  d.v = dpp_f<CTRL>(c.v);
+  d.i = dpp_i<CTRL>(c.i);
+  return d;
+}
+
+// best candidate over the wave (the order is total, so every lane agrees)
+__device__ __forceinline__ Cand wave_best(Cand c) {
+  c = better(c, dpp_cand<DPP_QUAD_1032>(c));
+  c = better(c, dpp_cand<DPP_QUAD_2301>(c));
+  c = better(c, dpp_cand<DPP_ROW_HALF_MIRROR>(c));
+  c = better(c, dpp_cand<DPP_ROW_MIRROR>(c));
+  Cand r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r[j].v = readlane_f(c.v, 16 * j);
+    r[j].i = __builtin_amdgcn_readlane(c.i, 16 * j);
+  }
+  return better(better(r[0], r[1]), better(r[2], r[3]));
+}
+
+// One wave selects k of token t's E <= 256 logits (4 per lane, expert
+// e = lane + 64*j).  Returns the selected logits/indices in slot order in
+// every lane (arrays of MOE_MAX_K).
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, float* sv, int* si) {
+  const int lane = lane_id();
+  float v[4];
+  bool live[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int e = lane + 64 * j;
+    live[j] = e < E;
+    v[j] = live[j] ? row[e] : 0.0f;
+  }
+#pragma unroll
+  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
+    if (s < k) {
+      Cand c = {0.0f, -1};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Cand d = {v[j], live[j] ? lane + 64 * j : -1};
+        c = better(c, d);
+      }
+      c = wave_best(c);
+      sv[s] = c.v;
+      si[s] = c.i;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (lane + 64 * j == c.i) live[j] = false;
+    }
+  }
+}
+
+// weights of the first k selected slots; slots [k, kcap) get index -1, weight 0
+__device__ __forceinline__ void write_selection(int32_t* idx, float* w, const float* sv, const int* si, int k,
+                                                int kcap) {
+  float ex[MOE_MAX_K_DEV];
+  float z = 0.0f;
+#pragma unroll
+  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
+    if (s < k) {
+      ex[s] = expf(sv[s] - sv[0]);
+      z += ex[s];
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
+    if (s < kcap) {
+      idx[s] = s < k ? si[s] : -1;
+      w[s] = s < k ? ex[s] / z : 0.0f;
+    }
+  }
+}
+
+
+// Select k experts of one token; every lane receives the same idx/w arrays.
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int* idx, float* w) {
+  float sv[MOE_MAX_K_DEV];
+  int si[MOE_MAX_K_DEV];
+  wave_topk(row, E, k, sv, si);
+  float ex[MOE_MAX_K_DEV];
+  float z = 0.0f;
+#pragma unroll
+  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
+    if (s < k) {
+      ex[s] = expf(sv[s] - sv[0]);
+      z += ex[s];
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
+    idx[s] = s < k ? si[s] : -1;
+    w[s] = s < k ? ex[s] / z : 0.0f;
+  }
+}
+
+}  // namespace moe

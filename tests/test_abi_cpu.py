@@ -64,6 +64,7 @@ def fwd(T=4, H=256, E=8, k=2, I=128, dt=moe.MOE_F16, x=P, wr=P, y=P, gu="fused",
 
 def test_zero_tokens_is_a_noop():
     assert fwd(T=0) == 0
+    assert fwd(T=0, x=None, y=None, ws=None) == 0  # empty tensors have NULL data pointers
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -134,6 +135,7 @@ def test_route_validation():
                                     kw.get("w", P), None, None, kw.get("logits", None), kw.get("ws", P),
                                     kw.get("ws_bytes", ws), None)
     assert call(T=0) == 0
+    assert call(T=0, x=None, idx=None, w=None, ws=None) == 0
     assert moe.STATUS[call(x=None)] == "MOE_ERR_NULL"
     assert moe.STATUS[call(idx=None)] == "MOE_ERR_NULL"
     assert moe.STATUS[call(k=3, E=2)] == "MOE_ERR_K"
