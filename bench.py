@@ -10,7 +10,8 @@ step takes the next token of a 256-token pool, so consecutive steps select
 different experts.  Prints one JSON line.
 
 Per-kernel durations come from HIP events recorded on the launch stream
-between the library's kernels inside the timed loop.  The dominant kernel's
+between the library's kernels, in a separate loop whose launches are queued
+behind a spin kernel so the GPU runs them back to back.  The dominant kernel's
 algorithmic bytes (or flops) per launch over its mean duration give the
 roofline fraction.  The CPU baseline times the oracle (plain C, all host
 cores) on a bounded sample of the same workload.
@@ -109,6 +110,10 @@ def main():
     ap.add_argument("--workload", default="decode_b1", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the oracle sample")
+    ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph timed region (counter runs)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain elementwise copy (torch.neg) of this many MiB, 5 launches: the known-size "
+                         "kernel that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -196,6 +201,8 @@ def main():
     G = min(64, K)
     reps = max(1, K // G)
     try:
+        if args.no_graph:
+            raise RuntimeError("skipped (--no-graph)")
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
@@ -217,19 +224,33 @@ def main():
     except Exception as ex:  # graph capture unavailable: report stream launches only
         log("graph capture failed:", ex)
 
-    # ---- timed region 3: HIP events between the kernels, on the launch stream
+    # ---- timed region 3: HIP events between the kernels, on the launch stream.
+    # Each chunk of steps is queued behind a spin kernel, so the GPU runs the
+    # chunk back to back instead of waiting on the host's launches and the
+    # event spans hold kernel time only.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
     for evs in events:  # create the underlying HIP events
         for e in evs:
             e.record(stream)
     torch.cuda.synchronize()
+    CH = 32
     t0 = time.perf_counter()
-    for i in range(K):
-        moe.debug_set_events(events[i])
-        step(args.warmup + i)
+    for c0 in range(0, K, CH):
+        torch.cuda._sleep(20_000_000)
+        for i in range(c0, min(K, c0 + CH)):
+            moe.debug_set_events(events[i])
+            step(args.warmup + i)
     torch.cuda.synchronize()
-    events_s = time.perf_counter() - t0
     moe.debug_set_events(None)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 19  # fp16 elements
+        src = torch.empty(n, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     best_s = min(v for v in (eager_s, graph_s) if v is not None)
     mode = "graph" if graph_s is not None and graph_s <= eager_s else "eager"
@@ -243,8 +264,8 @@ def main():
     per_kernel_us = per_kernel / K * 1e3
     gpu_step_us = float(sum(per_kernel_us))
     log("plan:", ", ".join("%s %.2fus" % (n, t) for n, t in zip(plan, per_kernel_us)))
-    log("per step: eager %.2f us, graph %s us, with events %.2f us (sum of kernel spans %.2f us)" % (
-        eager_s * 1e6 / K, "%.2f" % (graph_s * 1e6 / K) if graph_s else "n/a", events_s * 1e6 / K, gpu_step_us))
+    log("per step: eager %.2f us, graph %s us, sum of kernel spans %.2f us" % (
+        eager_s * 1e6 / K, "%.2f" % (graph_s * 1e6 / K) if graph_s else "n/a", gpu_step_us))
 
     # ---- roofline of the dominant kernel
     j = int(np.argmax(per_kernel_us))

@@ -173,6 +173,10 @@ __device__ __forceinline__ int dpp_i(int v) {
 
 constexpr int DPP_QUAD_1032 = 0xB1;
 constexpr int DPP_QUAD_2301 = 0x4E;
+constexpr int DPP_QUAD_2323 = 0xEE;  // lanes 0,1 of a quad read lanes 2,3
+constexpr int DPP_QUAD_1111 = 0x55;  // every lane of a quad reads lane 1
+constexpr int DPP_ROW_ROR4 = 0x124;  // rotate a 16-lane row by 4 lanes
+constexpr int DPP_ROW_ROR8 = 0x128;
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
 constexpr int DPP_ROW_MIRROR = 0x140;
 
@@ -201,9 +205,80 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
+// value of `v` in lane `src` (ds_bpermute: the LDS crossbar, no LDS memory)
+__device__ __forceinline__ float lane_read_f(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
+// Sums of R per-lane partials (R = 1, 2 or 4 rows) over the 64 lanes.  On
+// return, lane l (l < R) holds the total of row l; every lane holds the total
+// of row l % R.  The partials are first transposed between neighbouring lanes
+// (each exchange sends the half the partner keeps), so one butterfly reduces
+// all R rows at once.  Every row total is formed by the same expression
+// (pairs, then quads, then 16-lane rows, then halves; additions commute
+// exactly), whatever the row's position among the R, so a row sums to the
+// same bits in any kernel that reduces it with this function.
+template <int R>
+__device__ __forceinline__ float reduce_rows(const float (&p)[R]) {
+  static_assert(R == 1 || R == 2 || R == 4, "1, 2 or 4 rows");
+  const int lane = lane_id();
+  float v;
+  if constexpr (R == 4) {
+    const bool o1 = lane & 1, o2 = lane & 2;
+    const float k01 = o1 ? p[1] : p[0], s01 = o1 ? p[0] : p[1];
+    const float k23 = o1 ? p[3] : p[2], s23 = o1 ? p[2] : p[3];
+    const float r01 = k01 + dpp_f<DPP_QUAD_1032>(s01);  // rows 0|1 over the lane pair
+    const float r23 = k23 + dpp_f<DPP_QUAD_1032>(s23);  // rows 2|3
+    const float k = o2 ? r23 : r01, s = o2 ? r01 : r23;
+    v = k + dpp_f<DPP_QUAD_2301>(s);  // row lane%4 over the quad
+  } else if constexpr (R == 2) {
+    const bool o1 = lane & 1;
+    const float k = o1 ? p[1] : p[0], s = o1 ? p[0] : p[1];
+    v = k + dpp_f<DPP_QUAD_1032>(s);
+    v = v + dpp_f<DPP_QUAD_2301>(v);
+  } else {
+    v = p[0] + dpp_f<DPP_QUAD_1032>(p[0]);
+    v = v + dpp_f<DPP_QUAD_2301>(v);
+  }
+  v = v + dpp_f<DPP_ROW_ROR4>(v);
+  v = v + dpp_f<DPP_ROW_ROR8>(v);
+  v = v + lane_read_f(v, lane ^ 16);
+  v = v + lane_read_f(v, lane ^ 32);
+  return v;
+}
+
+// Index of the calling wave in its workgroup, marked wave-uniform (so values
+// derived from it live in scalar registers and branches on it stay scalar).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE)); }
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   int l = lane_id();
   return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// ------------------------------------------------------ buffer loads ----
+//
+// Streamed weights are read with buffer instructions: the row's base address
+// lives in scalar registers (its arithmetic runs on the scalar unit) and
+// every lane adds a fixed byte offset.  A resource of size 0 makes a load
+// return zeros without touching memory (the hardware range check), which is
+// how loads issued past the end of a wave's work stay harmless.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 buffer format word: raw 32-bit data
+constexpr int AUX_NT = 2;               // cache policy: non-temporal (read once)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_WORD3);
+}
+
+__device__ __forceinline__ u32x4 buf_load16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX_NT);
+}
+
+__device__ __forceinline__ uint32_t buf_load_u16_nt(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, AUX_NT);
 }
 
 // non-temporal 16-byte load for streamed weights

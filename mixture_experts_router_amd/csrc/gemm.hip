@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
   __shared__ int s_tile[4];
 
   const int lane = lane_id();
-  const int wave = threadIdx.x / WAVE;
+  const int wave = wave_id();
   const int tid = threadIdx.x;
 
   // ---- which (expert, M tile) this workgroup owns: tiles are numbered

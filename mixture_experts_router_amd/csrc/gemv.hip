@@ -65,16 +65,17 @@ int gemv_lanes_chunks(int K, int bits) {
   return (K / vals + 63) / 64;
 }
 
-// Per-chunk activation terms: 1024 * (sum over the 1024+q pairs),
-// 1024 * (sum over the 1024+16q pairs), and the plain sum.
+// Per-chunk activation terms: k, the amount the biased codes add to the
+// chunk's dot sum (1024 Xa + 64 Xb for 4-bit codes, where the 1024+16q pairs
+// are scaled by 1/16; 1024 X for 8-bit codes), and the plain sum X.
 struct XSums {
-  float ca, cb, x;
+  float k, x;
 };
 
 // Activation sums of one chunk held as fp16 pairs in unpack order.
 template <int BITS>
 __device__ __forceinline__ XSums chunk_xsums(const uint32_t* xp) {
-  XSums r = {0.0f, 0.0f, 0.0f};
+  XSums r = {0.0f, 0.0f};
   if constexpr (BITS == 4) {
     float a = 0.0f, b = 0.0f;
 #pragma unroll
@@ -84,8 +85,7 @@ __device__ __forceinline__ XSums chunk_xsums(const uint32_t* xp) {
       if ((j & 1) == 0) a += s2;  // pairs (k0,k4), (k2,k6)
       else b += s2;               // pairs (k1,k5), (k3,k7)
     }
-    r.ca = 1024.0f * a;
-    r.cb = 1024.0f * b;
+    r.k = 1024.0f * a + 64.0f * b;
     r.x = a + b;
   } else if constexpr (BITS == 8) {
     float a = 0.0f;
@@ -94,16 +94,23 @@ __device__ __forceinline__ XSums chunk_xsums(const uint32_t* xp) {
       const f16x2 hp = __builtin_bit_cast(f16x2, xp[j]);
       a += (float)hp.x + (float)hp.y;
     }
-    r.ca = 1024.0f * a;
+    r.k = 1024.0f * a;
     r.x = a;
   }
   return r;
 }
 
-// Contribution of one 16-byte chunk of weights to its row (affine terms applied).
+__device__ __forceinline__ float half_bits_f(uint32_t b) {
+  return (float)__builtin_bit_cast(f16, (uint16_t)b);
+}
+
+// acc + (contribution of one 16-byte chunk of weights to its row):
+//     s * (sum_k x_k q_k) + b * X,  sum_k x_k q_k = A + B/16 - k
+// (A, B: dot sums over the two kinds of biased pairs).  The fp16 scale and
+// bias enter the fused multiply-adds directly (v_fma_mix_f32).
 template <int BITS>
-__device__ __forceinline__ float chunk_value(u32x4 w, const uint32_t* xp, const XSums& xs, uint32_t s_bits,
-                                             uint32_t b_bits, const Q4Consts& qc) {
+__device__ __forceinline__ float chunk_acc(u32x4 w, const uint32_t* xp, const XSums& xs, uint32_t s_bits,
+                                           uint32_t b_bits, const Q4Consts& qc, float acc) {
   const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
   if constexpr (BITS == 4) {
     float A = 0.0f, B = 0.0f;
@@ -116,11 +123,8 @@ __device__ __forceinline__ float chunk_value(u32x4 w, const uint32_t* xp, const 
       A = dot2(p26, xp[4 * j + 2], A);
       B = dot2(p37, xp[4 * j + 3], B);
     }
-    const float qa = A - xs.ca;
-    const float qb = B - xs.cb;
-    const float dq = qa + 0.0625f * qb;
-    const float s = f16_bits_to_f32(s_bits), b = f16_bits_to_f32(b_bits);
-    return s * dq + b * xs.x;
+    const float dq = __builtin_fmaf(B, 0.0625f, A) - xs.k;
+    return __builtin_fmaf(half_bits_f(s_bits), dq, __builtin_fmaf(half_bits_f(b_bits), xs.x, acc));
   } else if constexpr (BITS == 8) {
     float A = 0.0f;
 #pragma unroll
@@ -130,14 +134,12 @@ __device__ __forceinline__ float chunk_value(u32x4 w, const uint32_t* xp, const 
       A = dot2(p[0], xp[2 * j], A);
       A = dot2(p[1], xp[2 * j + 1], A);
     }
-    const float dq = A - xs.ca;
-    const float s = f16_bits_to_f32(s_bits), b = f16_bits_to_f32(b_bits);
-    return s * dq + b * xs.x;
+    const float dq = A - xs.k;
+    return __builtin_fmaf(half_bits_f(s_bits), dq, __builtin_fmaf(half_bits_f(b_bits), xs.x, acc));
   } else {
-    float A = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) A = dot2(wv[j], xp[j], A);
-    return A;
+    for (int j = 0; j < 4; ++j) acc = dot2(wv[j], xp[j], acc);
+    return acc;
   }
 }
 
@@ -180,62 +182,59 @@ __device__ __forceinline__ int row_of(int it, int r) {
   return FUSED ? (R / 2) * it + (r % (R / 2)) : R * it + r;
 }
 
+// Loads of iteration `it`.  When `live` is false (an iteration past the
+// wave's end, issued only to keep the wait counts exact) the loads go through
+// empty resources: they return zeros and read no memory.
 template <int BITS, int CPL, bool FUSED>
-__device__ __forceinline__ void load_rows(RowBuf<BITS, CPL>& buf, const GemvUpParams& prm, int e, int it,
-                                          const int* cc, int ng, int64_t row_bytes) {
-  using C = Chunk<BITS>;
+__device__ __forceinline__ void load_rows(RowBuf<BITS, CPL>& buf, const GemvUpParams& prm, int e, int it, bool live,
+                                          const uint32_t* qoff, const uint32_t* goff, int ng, int64_t row_bytes) {
   constexpr int R = Rows<CPL>::N;
+  const uint32_t nq = live ? (uint32_t)row_bytes : 0u;
+  const uint32_t ns = live ? (uint32_t)ng * 2u : 0u;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const WView& wv = (FUSED && r >= R / 2) ? prm.w1 : prm.w0;
     const int64_t row = (int64_t)e * wv.stride + row_of<CPL, FUSED>(it, r);
-    const uint8_t* rq = wv.q + row * row_bytes;
+    const rsrc_t rq = make_rsrc(wv.q + row * row_bytes, nq);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      buf.q[r][i] = load_stream16(rq + (size_t)cc[i] * 16);
-      if constexpr (BITS != 16) {
-        buf.s[r][i] = wv.s[row * ng + cc[i] / C::PER_GROUP];
-        buf.b[r][i] = wv.b[row * ng + cc[i] / C::PER_GROUP];
+    for (int i = 0; i < CPL; ++i) buf.q[r][i] = buf_load16_nt(rq, qoff[i]);
+    if constexpr (BITS != 16) {
+      const rsrc_t rs = make_rsrc(wv.s + row * ng, ns);
+      const rsrc_t rb = make_rsrc(wv.b + row * ng, ns);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        buf.s[r][i] = buf_load_u16_nt(rs, goff[i]);
+        buf.b[r][i] = buf_load_u16_nt(rb, goff[i]);
       }
     }
   }
 }
 
+// Row sums of one iteration and their store.  After reduce_rows, lane r holds
+// row r: fused R = 4 rows are (gate j, gate j+1, up j, up j+1), so lanes 0
+// and 1 form h[j] and h[j+1]; fused R = 2 rows are (gate j, up j).
 template <int BITS, int CPL, bool FUSED>
 __device__ __forceinline__ void finish_iter(const RowBuf<BITS, CPL>& buf, const GemvUpParams& prm, int p, int it,
-                                            const uint32_t (*xr)[Chunk<BITS>::PAIRS], const XSums* xs,
-                                            const bool* valid, const Q4Consts& qc) {
+                                            bool store, const uint32_t (*xr)[Chunk<BITS>::PAIRS], const XSums* xs,
+                                            const Q4Consts& qc) {
   constexpr int R = Rows<CPL>::N;
   float part[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const float v = chunk_value<BITS>(buf.q[r][i], xr[i], xs[i], buf.s[r][i], buf.b[r][i], qc);
-      acc += valid[i] ? v : 0.0f;
-    }
-    part[r] = wave_sum(acc);
+    for (int i = 0; i < CPL; ++i) acc = chunk_acc<BITS>(buf.q[r][i], xr[i], xs[i], buf.s[r][i], buf.b[r][i], qc, acc);
+    part[r] = acc;
   }
-  if (lane_id() == 0) {
-    if constexpr (FUSED) {
-      if constexpr (R == 4) {
-        const int j = 2 * it;
-        const uint32_t h0 = f32_to_f16_bits(swiglu(part[0], part[2]));
-        const uint32_t h1 = f32_to_f16_bits(swiglu(part[1], part[3]));
-        *(uint32_t*)(prm.h + (size_t)p * prm.N + j) = h0 | (h1 << 16);
-      } else {
-        prm.h[(size_t)p * prm.N + it] = f32_to_f16_bits(swiglu(part[0], part[1]));
-      }
-    } else {
-      if constexpr (R == 4) {
-        const f32x4 o = {part[0], part[1], part[2], part[3]};
-        *(f32x4*)(prm.out32 + (size_t)p * prm.N + R * it) = o;
-      } else {
-        prm.out32[(size_t)p * prm.N + R * it] = part[0];
-        prm.out32[(size_t)p * prm.N + R * it + 1] = part[1];
-      }
-    }
+  const float v = reduce_rows<R>(part);
+  const int lane = lane_id();
+  if constexpr (FUSED) {
+    // the up value of lane 0 (and 1) sits in lane R/2 (and R/2 + 1)
+    const float u = R == 4 ? dpp_f<DPP_QUAD_2323>(v) : dpp_f<DPP_QUAD_1111>(v);
+    const float hv = swiglu(v, u);
+    if (store && lane < R / 2) prm.h[(size_t)p * prm.N + (R / 2) * it + lane] = f32_to_f16_bits(hv);
+  } else {
+    if (store && lane < R) prm.out32[(size_t)p * prm.N + R * it + lane] = v;
   }
 }
 
@@ -249,7 +248,7 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   if (slot >= ku) return;
   // iterations it = gw, gw + W, gw + 2W, ...: at any moment the waves of a
   // pair read one contiguous stretch of rows, so each expert is swept linearly
-  const int gw = blockIdx.x * 4 + threadIdx.x / WAVE;
+  const int gw = blockIdx.x * 4 + wave_id();
   const int W = gridDim.x * 4;
   if (gw >= prm.iters) return;
   int e;
@@ -281,33 +280,52 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   const int64_t row_bytes = (int64_t)H * BITS / 8;
   const Q4Consts qc = q4_consts();
 
+  // lane chunks c = lane + 64 i; a lane past the end of the row re-reads the
+  // last chunk against zero activations, which adds exactly 0
   int cc[CPL];
   bool valid[CPL];
+  uint32_t qoff[CPL], goff[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
     valid[i] = c < nch;
     cc[i] = valid[i] ? c : nch - 1;
+    qoff[i] = (uint32_t)cc[i] * 16u;
+    goff[i] = (uint32_t)(cc[i] / C::PER_GROUP) * 2u;
   }
 
-  // first rows in flight before the activations are prepared
-  // rows in flight before the activations are prepared; short rows keep two
-  // iterations ahead of the one being reduced, long rows one
-  constexpr bool DEEP = CPL <= 2;
+  // The wave's iterations are it(k) = gw + k*W, k < n.  Loads are issued
+  // unconditionally (past the end through empty resources, results not
+  // stored): with loads on every path the wait counts stay exact, so a
+  // buffer's loads remain in flight while an older one is reduced.
+  const int n = (prm.iters - gw + W - 1) / W;
+  auto it_of = [&](int k) { return gw + (k < n ? k : n - 1) * W; };
+  constexpr bool DEEP = CPL <= 2;  // short rows: two iterations ahead, else one
+
+  // activation loads first: vmcnt retires in issue order, so waiting for
+  // them later does not wait for the weight loads issued after them
+  u32x4 xraw[CPL][C::PIECES];
+  const uint16_t* xrow = prm.x + (size_t)t * H;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i)
+#pragma unroll
+    for (int j = 0; j < C::PIECES; ++j) {
+      const u32x4 v = load16(xrow + (size_t)cc[i] * C::VALS + 8 * j);
+      xraw[i][j] = valid[i] ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+
   RowBuf<BITS, CPL> bufA, bufB, bufC;
-  const int it1 = prm.iters;
-  load_rows<BITS, CPL, FUSED>(bufA, prm, e, gw, cc, ng, row_bytes);
-  if (DEEP && gw + W < it1) load_rows<BITS, CPL, FUSED>(bufB, prm, e, gw + W, cc, ng, row_bytes);
+  load_rows<BITS, CPL, FUSED>(bufA, prm, e, it_of(0), 0 < n, qoff, goff, ng, row_bytes);
+  if constexpr (DEEP) load_rows<BITS, CPL, FUSED>(bufB, prm, e, it_of(1), 1 < n, qoff, goff, ng, row_bytes);
 
   // activations of this lane's chunks, as fp16 pairs in the unpack order
   uint32_t xr[CPL][C::PAIRS];
   XSums xs[CPL];
-  const uint16_t* xrow = prm.x + (size_t)t * H;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
 #pragma unroll
     for (int j = 0; j < C::PIECES; ++j) {
-      u32x4 v = act8_to_f16(load16(xrow + (size_t)cc[i] * C::VALS + 8 * j), prm.act);
+      u32x4 v = act8_to_f16(xraw[i][j], prm.act);
       if constexpr (BITS == 4) v = perm8_nibble_order(v);
       xr[i][4 * j + 0] = v.x;
       xr[i][4 * j + 1] = v.y;
@@ -317,29 +335,21 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
     xs[i] = chunk_xsums<BITS>(xr[i]);
   }
 
-  // two row buffers: the next iteration's loads are in flight while the
-  // current one is reduced
   if constexpr (DEEP) {
-    for (int it = gw; it < it1; it += 3 * W) {
-      if (it + 2 * W < it1) load_rows<BITS, CPL, FUSED>(bufC, prm, e, it + 2 * W, cc, ng, row_bytes);
-      finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it, xr, xs, valid, qc);
-      if (it + W < it1) {
-        if (it + 3 * W < it1) load_rows<BITS, CPL, FUSED>(bufA, prm, e, it + 3 * W, cc, ng, row_bytes);
-        finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it + W, xr, xs, valid, qc);
-      }
-      if (it + 2 * W < it1) {
-        if (it + 4 * W < it1) load_rows<BITS, CPL, FUSED>(bufB, prm, e, it + 4 * W, cc, ng, row_bytes);
-        finish_iter<BITS, CPL, FUSED>(bufC, prm, p, it + 2 * W, xr, xs, valid, qc);
-      }
+    for (int k = 0; k < n; k += 3) {
+      load_rows<BITS, CPL, FUSED>(bufC, prm, e, it_of(k + 2), k + 2 < n, qoff, goff, ng, row_bytes);
+      finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it_of(k), k < n, xr, xs, qc);
+      load_rows<BITS, CPL, FUSED>(bufA, prm, e, it_of(k + 3), k + 3 < n, qoff, goff, ng, row_bytes);
+      finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it_of(k + 1), k + 1 < n, xr, xs, qc);
+      load_rows<BITS, CPL, FUSED>(bufB, prm, e, it_of(k + 4), k + 4 < n, qoff, goff, ng, row_bytes);
+      finish_iter<BITS, CPL, FUSED>(bufC, prm, p, it_of(k + 2), k + 2 < n, xr, xs, qc);
     }
-    return;
-  }
-  for (int it = gw; it < it1; it += 2 * W) {
-    if (it + W < it1) load_rows<BITS, CPL, FUSED>(bufB, prm, e, it + W, cc, ng, row_bytes);
-    finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it, xr, xs, valid, qc);
-    if (it + W < it1) {
-      if (it + 2 * W < it1) load_rows<BITS, CPL, FUSED>(bufA, prm, e, it + 2 * W, cc, ng, row_bytes);
-      finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it + W, xr, xs, valid, qc);
+  } else {
+    for (int k = 0; k < n; k += 2) {
+      load_rows<BITS, CPL, FUSED>(bufB, prm, e, it_of(k + 1), k + 1 < n, qoff, goff, ng, row_bytes);
+      finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it_of(k), k < n, xr, xs, qc);
+      load_rows<BITS, CPL, FUSED>(bufA, prm, e, it_of(k + 2), k + 2 < n, qoff, goff, ng, row_bytes);
+      finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it_of(k + 1), k + 1 < n, xr, xs, qc);
     }
   }
 }
@@ -421,18 +431,24 @@ struct DownBuf {
   uint32_t s[DCPL], b[DCPL];
 };
 
+// Row m of expert e; a row past the workgroup's end (`live` false) loads
+// through empty resources (zeros, no memory access).
 template <int BITS, int DCPL>
 __device__ __forceinline__ void load_down_row(DownBuf<BITS, DCPL>& buf, const GemvDownParams& prm, int e, int m,
-                                              const int* cc, int ng, int64_t row_bytes) {
-  using C = Chunk<BITS>;
+                                              bool live, const uint32_t* qoff, const uint32_t* goff, int ng,
+                                              int64_t row_bytes) {
   const int64_t row = (int64_t)e * prm.wd.stride + m;
-  const uint8_t* rq = prm.wd.q + row * row_bytes;
+  const rsrc_t rq = make_rsrc(prm.wd.q + row * row_bytes, live ? (uint32_t)row_bytes : 0u);
 #pragma unroll
-  for (int i = 0; i < DCPL; ++i) {
-    buf.q[i] = load_stream16(rq + (size_t)cc[i] * 16);
-    if constexpr (BITS != 16) {
-      buf.s[i] = prm.wd.s[row * ng + cc[i] / C::PER_GROUP];
-      buf.b[i] = prm.wd.b[row * ng + cc[i] / C::PER_GROUP];
+  for (int i = 0; i < DCPL; ++i) buf.q[i] = buf_load16_nt(rq, qoff[i]);
+  if constexpr (BITS != 16) {
+    const uint32_t ns = live ? (uint32_t)ng * 2u : 0u;
+    const rsrc_t rs = make_rsrc(prm.wd.s + row * ng, ns);
+    const rsrc_t rb = make_rsrc(prm.wd.b + row * ng, ns);
+#pragma unroll
+    for (int i = 0; i < DCPL; ++i) {
+      buf.s[i] = buf_load_u16_nt(rs, goff[i]);
+      buf.b[i] = buf_load_u16_nt(rb, goff[i]);
     }
   }
 }
@@ -440,11 +456,11 @@ __device__ __forceinline__ void load_down_row(DownBuf<BITS, DCPL>& buf, const Ge
 // KS waves share a slot: wave ks owns lane chunks i in [ks*DC, (ks+1)*DC)
 // of every row (DC chunks per lane), halving the registers a long row needs.
 template <int BITS, int DC, int KS>
-__global__ __launch_bounds__(1024) void gemv_down_kernel(GemvDownParams prm) {
+__global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
   using C = Chunk<BITS>;
   __shared__ float part[MOE_MAX_K_DEV][KS][DOWN_MAX_ROWS];
   const int t = blockIdx.y;
-  const int wv = threadIdx.x / WAVE;
+  const int wv = wave_id();
   const int s = wv / KS, ks = wv % KS;
   const int lane = lane_id();
   const int ku = prm.rt.logits ? prm.k_static : *prm.rt.k_used;
@@ -475,25 +491,44 @@ __global__ __launch_bounds__(1024) void gemv_down_kernel(GemvDownParams prm) {
     e = __builtin_amdgcn_readfirstlane(e);
     int cc[DC];
     bool valid[DC];
+    uint32_t qoff[DC], goff[DC];
 #pragma unroll
     for (int i = 0; i < DC; ++i) {
       const int c = lane + 64 * (ks * DC + i);
       valid[i] = c < nch;
       cc[i] = valid[i] ? c : nch - 1;
+      qoff[i] = (uint32_t)cc[i] * 16u;
+      goff[i] = (uint32_t)(cc[i] / C::PER_GROUP) * 2u;
     }
-    DownBuf<BITS, DC> bufA, bufB;
+    // rows m(j) = blockIdx.x + j*G, j < nr; loads past the end go through
+    // empty resources (unconditional loads keep the wait counts exact)
     const int m0 = blockIdx.x;
-    load_down_row<BITS, DC>(bufA, prm, e, m0, cc, ng, row_bytes);
+    const int nr = min(R, (prm.H - m0 + G - 1) / G);
+    auto m_of = [&](int j) { return m0 + (j < nr ? j : nr - 1) * G; };
+    // SwiGLU-row loads first (see the gate+up kernel), then three weight rows;
+    // a lane past the end of the row gets zero activations (adds exactly 0)
+    u32x4 hraw[DC][C::PIECES];
+    const uint16_t* hrow = prm.h + ((size_t)t * prm.kcap + s) * I;
+#pragma unroll
+    for (int i = 0; i < DC; ++i)
+#pragma unroll
+      for (int j = 0; j < C::PIECES; ++j) {
+        const u32x4 v = load16(hrow + (size_t)cc[i] * C::VALS + 8 * j);
+        hraw[i][j] = valid[i] ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    DownBuf<BITS, DC> b0, b1, b2, b3;
+    load_down_row<BITS, DC>(b0, prm, e, m_of(0), 0 < nr, qoff, goff, ng, row_bytes);
+    load_down_row<BITS, DC>(b1, prm, e, m_of(1), 1 < nr, qoff, goff, ng, row_bytes);
+    load_down_row<BITS, DC>(b2, prm, e, m_of(2), 2 < nr, qoff, goff, ng, row_bytes);
 
     // this slot's SwiGLU row (the wave's chunks), as fp16 pairs in unpack order
     uint32_t hr[DC][C::PAIRS];
     XSums hs[DC];
-    const uint16_t* hrow = prm.h + ((size_t)t * prm.kcap + s) * I;
 #pragma unroll
     for (int i = 0; i < DC; ++i) {
 #pragma unroll
       for (int j = 0; j < C::PIECES; ++j) {
-        u32x4 v = load16(hrow + (size_t)cc[i] * C::VALS + 8 * j);
+        u32x4 v = hraw[i][j];
         if constexpr (BITS == 4) v = perm8_nibble_order(v);
         hr[i][4 * j + 0] = v.x;
         hr[i][4 * j + 1] = v.y;
@@ -503,35 +538,42 @@ __global__ __launch_bounds__(1024) void gemv_down_kernel(GemvDownParams prm) {
       hs[i] = chunk_xsums<BITS>(hr[i]);
     }
 
-    auto row_value = [&](const DownBuf<BITS, DC>& buf) {
+    auto row_part = [&](const DownBuf<BITS, DC>& buf) {
       float acc = 0.0f;
 #pragma unroll
-      for (int i = 0; i < DC; ++i) {
-        const float v = chunk_value<BITS>(buf.q[i], hr[i], hs[i], buf.s[i], buf.b[i], qc);
-        acc += valid[i] ? v : 0.0f;
-      }
-      return wave_sum(acc);
+      for (int i = 0; i < DC; ++i) acc = chunk_acc<BITS>(buf.q[i], hr[i], hs[i], buf.s[i], buf.b[i], qc, acc);
+      return acc;
     };
 
-    for (int j = 0; j < R; j += 2) {
-      const int ma = m0 + j * G, mb = m0 + (j + 1) * G;
-      const bool hb = j + 1 < R && mb < prm.H;
-      if (hb) load_down_row<BITS, DC>(bufB, prm, e, mb, cc, ng, row_bytes);
-      if (ma < prm.H) {
-        const float o = row_value(bufA);
-        if (lane == 0) part[s][ks][j] = o;
-      }
-      if (hb) {
-        const int mc = m0 + (j + 2) * G;
-        if (j + 2 < R && mc < prm.H) load_down_row<BITS, DC>(bufA, prm, e, mc, cc, ng, row_bytes);
-        const float o = row_value(bufB);
-        if (lane == 0) part[s][ks][j + 1] = o;
-      }
+    // ring of four row buffers, three rows ahead: b3 is loaded and consumed
+    // in the same trip, the other three are refilled right after their use
+    // and consumed in the next trip.  (A loop in which no load is consumed
+    // in its own trip makes the compiler drain every load at the loop head.)
+    // Scheduling barriers keep each load next to the use it follows.
+    for (int j = 0; j < nr; j += 4) {
+      float pr[4];
+      load_down_row<BITS, DC>(b3, prm, e, m_of(j + 3), j + 3 < nr, qoff, goff, ng, row_bytes);
+      __builtin_amdgcn_sched_barrier(0);
+      pr[0] = row_part(b0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_down_row<BITS, DC>(b0, prm, e, m_of(j + 4), j + 4 < nr, qoff, goff, ng, row_bytes);
+      __builtin_amdgcn_sched_barrier(0);
+      pr[1] = row_part(b1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_down_row<BITS, DC>(b1, prm, e, m_of(j + 5), j + 5 < nr, qoff, goff, ng, row_bytes);
+      __builtin_amdgcn_sched_barrier(0);
+      pr[2] = row_part(b2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_down_row<BITS, DC>(b2, prm, e, m_of(j + 6), j + 6 < nr, qoff, goff, ng, row_bytes);
+      __builtin_amdgcn_sched_barrier(0);
+      pr[3] = row_part(b3);
+      const float o = reduce_rows<4>(pr);
+      if (lane < 4 && j + lane < nr) part[s][ks][j + lane] = o;
     }
   }
   __syncthreads();
   if (wv == 0 && lane < R) {
-    const int m = blockIdx.x + lane * G;
+    const int m = blockIdx.x + lane * G;  // lanes past this workgroup's rows store nothing
     if (m < prm.H) {
       float y = 0.0f;
       for (int q = 0; q < ku; ++q) {
@@ -568,7 +610,7 @@ hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_sta
   prm.y = y;
   prm.act = act;
   const int dcpl = gemv_lanes_chunks(I, bits);
-  const int ks = dcpl >= 4 ? 2 : 1;            // waves per slot
+  const int ks = dcpl >= 4 && kcap <= 4 ? 2 : 1;  // waves per slot (block of at most 512 threads)
   const int dc = (dcpl + ks - 1) / ks;          // chunks per lane per wave
   // rows per workgroup so that about `waves_per_cu` waves per CU are resident
   const int64_t want = (int64_t)(num_cu > 0 ? num_cu : 256) * tuning(TUNE_DOWN_WAVES_PER_CU);
@@ -583,7 +625,7 @@ hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_sta
   dim3 block(64 * kcap * ks);
 #define X(B, D, K) \
   if (bits == B && dc == D && ks == K) gemv_down_kernel<B, D, K><<<grid, block, 0, st>>>(prm); else
-#define CASES(B) X(B, 1, 1) X(B, 2, 1) X(B, 3, 1) X(B, 2, 2) X(B, 3, 2)
+#define CASES(B) X(B, 1, 1) X(B, 2, 1) X(B, 3, 1) X(B, 4, 1) X(B, 5, 1) X(B, 6, 1) X(B, 2, 2) X(B, 3, 2)
   CASES(4) CASES(8) CASES(16) return hipErrorInvalidValue;
 #undef CASES
 #undef X

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t
                                                                   int act) {
   __shared__ float part[4];
   const int e = blockIdx.x, t = blockIdx.y;
-  const int lane = lane_id(), wave = threadIdx.x / WAVE;
+  const int lane = lane_id(), wave = wave_id();
   const int q = H / 4;
   const uint16_t* xr = x + (size_t)t * H + wave * q;
   const uint16_t* wrow = wr + (size_t)e * H + wave * q;
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void router_logits_tile_kernel(const uint16_t*
                                                                  int act) {
   constexpr int TT = 4;
   const int lane = lane_id();
-  const int wave = threadIdx.x / WAVE;
+  const int wave = wave_id();
   const int t0 = blockIdx.x * TT;
   const int e0 = blockIdx.y * 16 + wave * 4;
   if (e0 >= E) return;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void router_logits_tile_kernel(const uint16_t*
 __global__ __launch_bounds__(256) void topk_static_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                           int32_t* __restrict__ idx, float* __restrict__ w,
                                                           int32_t* __restrict__ k_used, float* __restrict__ entropy) {
-  const int t = blockIdx.x * 4 + threadIdx.x / WAVE;
+  const int t = blockIdx.x * 4 + wave_id();
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (k_used) *k_used = k;
     if (entropy) *entropy = 0.0f;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(1024) void topk_entropy_kernel(const float* __restr
                                                             float* __restrict__ entropy) {
   __shared__ float part[16];
   __shared__ int k_sh;
-  const int wave = threadIdx.x / WAVE;
+  const int wave = wave_id();
   float hs = 0.0f;
   for (int t = wave; t < T; t += 16) hs += wave_entropy(logits + (size_t)t * E, E);
   if (lane_id() == 0) part[wave] = hs;

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
   __shared__ int s_lt[16], s_eq[16];
   const int e = blockIdx.x;
   const int lane = lane_id();
-  const int wave = threadIdx.x / WAVE;
+  const int wave = wave_id();
   const int ku = k_used_dev ? *k_used_dev : k_static;
   const int64_t P = (int64_t)T * kcap;
   const int64_t seg = ((P + 16 * 64 - 1) / (16 * 64)) * 64;

@@ -18,13 +18,17 @@ struct Cand {
   int i;
 };
 
-// larger value first, lower index first among equal values; index -1 = none
+// larger value first, lower index first among equal values; index -1 = none.
+// Written with selects (no short-circuit branches): symmetric, so every lane
+// of a reduction picks the same candidate.
 __device__ __forceinline__ Cand better(Cand a, Cand b) {
-  if (a.i < 0) return b;
-  if (b.i < 0) return a;
-  if (a.v > b.v) return a;
-  if (b.v > a.v) return b;
-  return a.i < b.i ? a : b;
+  const bool a_none = a.i < 0, b_none = b.i < 0;
+  const bool b_higher = (b.v > a.v) | ((b.v == a.v) & (b.i < a.i));
+  const bool take_b = a_none | (!b_none & b_higher);
+  Cand r;
+  r.v = take_b ? b.v : a.v;
+  r.i = take_b ? b.i : a.i;
+  return r;
 }
 
 template <int CTRL>
