@@ -9,8 +9,9 @@ top-4, intermediate 11008, 4-bit group-64 weights, fp16 activations; each
 step takes the next token of a 256-token pool, so consecutive steps select
 different experts.  Prints one JSON line.
 
-Per-kernel durations come from HIP events recorded on the launch stream
-between the library's kernels, in a separate loop whose launches are queued
+Per-kernel durations come from HIP event pairs that the library attaches to
+each kernel launch (hipExtLaunchKernelGGL: the events take the kernel's own
+start and end timestamps), in a separate loop whose launches are queued
 behind a spin kernel so the GPU runs them back to back.  The dominant kernel's
 algorithmic bytes (or flops) per launch over its mean duration give the
 roofline fraction.  The CPU baseline times the oracle (plain C, all host
@@ -224,11 +225,12 @@ def main():
     except Exception as ex:  # graph capture unavailable: report stream launches only
         log("graph capture failed:", ex)
 
-    # ---- timed region 3: HIP events between the kernels, on the launch stream.
+    # ---- timed region 3: per-kernel durations.  The library launches each
+    # kernel with hipExtLaunchKernelGGL and a start/stop HIP event pair, which
+    # take the kernel's own start and end timestamps on the launch stream.
     # Each chunk of steps is queued behind a spin kernel, so the GPU runs the
-    # chunk back to back instead of waiting on the host's launches and the
-    # event spans hold kernel time only.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
+    # chunk back to back as in the untimed loop.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(K)]
     for evs in events:  # create the underlying HIP events
         for e in evs:
             e.record(stream)
@@ -260,11 +262,11 @@ def main():
     per_kernel = np.zeros(nk)
     for evs in events:
         for j in range(nk):
-            per_kernel[j] += evs[j].elapsed_time(evs[j + 1])
+            per_kernel[j] += evs[2 * j].elapsed_time(evs[2 * j + 1])
     per_kernel_us = per_kernel / K * 1e3
     gpu_step_us = float(sum(per_kernel_us))
     log("plan:", ", ".join("%s %.2fus" % (n, t) for n, t in zip(plan, per_kernel_us)))
-    log("per step: eager %.2f us, graph %s us, sum of kernel spans %.2f us" % (
+    log("per step: eager %.2f us, graph %s us, sum of kernel durations %.2f us" % (
         eager_s * 1e6 / K, "%.2f" % (graph_s * 1e6 / K) if graph_s else "n/a", gpu_step_us))
 
     # ---- roofline of the dominant kernel

@@ -203,10 +203,12 @@ moe_status moe_fuse_gate_up(const moe_weights* gate, const moe_weights* up, void
 const char* moe_status_string(moe_status s);
 
 /*
- * Profiling hooks (per calling thread).  When `events` is non-NULL, every
- * later entry point on this thread records events[0] on its stream before its
- * first kernel and events[i+1] after its i-th kernel, for i + 1 < n.
- * `events` are caller-created hipEvent_t handles.  Pass NULL to stop.
+ * Profiling hooks (per calling thread).  When `events` is non-NULL, the i-th
+ * kernel of every later entry point on this thread is launched with
+ * hipExtLaunchKernelGGL, which stamps events[2i] when the kernel starts and
+ * events[2i+1] when it ends (the kernel's own dispatch timestamps, no extra
+ * packets in the stream), for 2i + 1 < n.  `events` are caller-created
+ * hipEvent_t handles, owned by the caller.  Pass NULL to stop.
  * moe_debug_last_plan writes the names of the kernels the last call on this
  * thread launched, comma-separated, into buf (host memory).
  */

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wts, const int32_t* k_used_dev,
                           int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st) {
   dim3 grid((H / 8 + 255) / 256, T);
-  combine_kernel<<<grid, 256, 0, st>>>(o, pos, wts, k_used_dev, k_static, kcap, H, y, act);
+  launch_kernel(combine_kernel, grid, 256, 0, st, o, pos, wts, k_used_dev, k_static, kcap, H, y, act);
   return hipGetLastError();
 }
 
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g
 
 hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, hipStream_t st) {
   const int64_t n = rows * I;
-  swiglu_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, u, h, n);
+  launch_kernel(swiglu_kernel, (unsigned)((n + 255) / 256), 256, 0, st, g, u, h, n);
   return hipGetLastError();
 }
 
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
 hipError_t launch_gather_rows(const uint16_t* src, const int32_t* pos, int64_t P, int I, uint16_t* out, int kcap,
                               const int32_t* k_used_dev, int k_static, hipStream_t st) {
   dim3 grid((I / 8 + 255) / 256, (unsigned)P);
-  gather_rows_kernel<<<grid, 256, 0, st>>>(src, pos, I, out, kcap, k_used_dev, k_static);
+  launch_kernel(gather_rows_kernel, grid, 256, 0, st, src, pos, I, out, kcap, k_used_dev, k_static);
   return hipGetLastError();
 }
 
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void copy_words_kernel(const uint32_t* __restr
 
 hipError_t launch_copy_words(const void* src, void* dst, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  copy_words_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>((const uint32_t*)src, (uint32_t*)dst, n);
+  launch_kernel(copy_words_kernel, (unsigned)((n + 255) / 256), 256, 0, st, (const uint32_t*)src, (uint32_t*)dst, n);
   return hipGetLastError();
 }
 

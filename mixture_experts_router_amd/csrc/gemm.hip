@@ -320,9 +320,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
 template <int BITS, int MODE>
 static hipError_t launch_ms(int bm, const GemmParams& prm, dim3 grid, hipStream_t st) {
   switch (bm) {
-    case 32: gemm_kernel<BITS, MODE, 1><<<grid, 256, 0, st>>>(prm); break;
-    case 64: gemm_kernel<BITS, MODE, 2><<<grid, 256, 0, st>>>(prm); break;
-    case 128: gemm_kernel<BITS, MODE, 4><<<grid, 256, 0, st>>>(prm); break;
+    case 32: launch_kernel(gemm_kernel<BITS, MODE, 1>, grid, 256, 0, st, prm); break;
+    case 64: launch_kernel(gemm_kernel<BITS, MODE, 2>, grid, 256, 0, st, prm); break;
+    case 128: launch_kernel(gemm_kernel<BITS, MODE, 4>, grid, 256, 0, st, prm); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -357,11 +357,11 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
 template <int BITS, bool FUSED>
 static hipError_t launch_up_cpl(int cpl, const GemvUpParams& prm, dim3 grid, hipStream_t st) {
   switch (cpl) {
-    case 1: gemv_up_kernel<BITS, 1, FUSED><<<grid, 256, 0, st>>>(prm); break;
-    case 2: gemv_up_kernel<BITS, 2, FUSED><<<grid, 256, 0, st>>>(prm); break;
-    case 3: gemv_up_kernel<BITS, 3, FUSED><<<grid, 256, 0, st>>>(prm); break;
-    case 4: gemv_up_kernel<BITS, 4, FUSED><<<grid, 256, 0, st>>>(prm); break;
-    case 8: gemv_up_kernel<BITS, 8, FUSED><<<grid, 256, 0, st>>>(prm); break;
+    case 1: launch_kernel(gemv_up_kernel<BITS, 1, FUSED>, grid, 256, 0, st, prm); break;
+    case 2: launch_kernel(gemv_up_kernel<BITS, 2, FUSED>, grid, 256, 0, st, prm); break;
+    case 3: launch_kernel(gemv_up_kernel<BITS, 3, FUSED>, grid, 256, 0, st, prm); break;
+    case 4: launch_kernel(gemv_up_kernel<BITS, 4, FUSED>, grid, 256, 0, st, prm); break;
+    case 8: launch_kernel(gemv_up_kernel<BITS, 8, FUSED>, grid, 256, 0, st, prm); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -624,7 +624,7 @@ hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_sta
   dim3 grid(G, T);
   dim3 block(64 * kcap * ks);
 #define X(B, D, K) \
-  if (bits == B && dc == D && ks == K) gemv_down_kernel<B, D, K><<<grid, block, 0, st>>>(prm); else
+  if (bits == B && dc == D && ks == K) launch_kernel(gemv_down_kernel<B, D, K>, grid, block, 0, st, prm); else
 #define CASES(B) X(B, 1, 1) X(B, 2, 1) X(B, 3, 1) X(B, 4, 1) X(B, 5, 1) X(B, 6, 1) X(B, 2, 2) X(B, 3, 2)
   CASES(4) CASES(8) CASES(16) return hipErrorInvalidValue;
 #undef CASES

@@ -1,6 +1,7 @@
 // Launch functions of the layer's HIP kernels (internal; called by moe_abi.cpp).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -8,6 +9,25 @@
 #define MOE_K_ENTROPY_CAP_DEV 3
 
 namespace moe {
+
+// Debug timing hook (moe_debug_set_events): the start/stop event pair for the
+// next kernel launch on this thread, if one is pending.
+bool next_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is launched through here.  With a pending
+// event pair the launch carries it (hipExtLaunchKernelGGL: the events take the
+// kernel's own start/end timestamps); otherwise a plain launch.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t st,
+                                Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (next_launch_events(&a, &b))
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, a, b, 0, static_cast<KArgs>(args)...);
+  else
+    kernel<<<grid, block, lds, st>>>(static_cast<KArgs>(args)...);
+  return hipGetLastError();
+}
+
 
 // Launch-shape knobs (resident waves per CU the decode kernels aim for).
 // Defaults are the measured best; moe_debug_set_tuning overrides them.

@@ -38,19 +38,30 @@ struct Prof {
 };
 thread_local Prof g_prof;
 
+}  // namespace
+
+namespace moe {
+bool next_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_prof.ev || g_prof.next + 1 >= g_prof.n) return false;
+  *start = g_prof.ev[g_prof.next];
+  *stop = g_prof.ev[g_prof.next + 1];
+  g_prof.next += 2;
+  return true;
+}
+}  // namespace moe
+
+namespace {
+
 void plan_begin(hipStream_t st) {
+  (void)st;
   g_prof.plan.clear();
   g_prof.next = 0;
-  if (g_prof.ev && g_prof.n > 0) {
-    hipEventRecord(g_prof.ev[0], st);
-    g_prof.next = 1;
-  }
 }
 
 void plan_step(const char* name, hipStream_t st) {
+  (void)st;
   if (!g_prof.plan.empty()) g_prof.plan += ",";
   g_prof.plan += name;
-  if (g_prof.ev && g_prof.next < g_prof.n) hipEventRecord(g_prof.ev[g_prof.next++], st);
 }
 
 // ------------------------------------------------------- device properties

@@ -204,11 +204,11 @@ int router_small_max_tokens() { return 16; }
 hipError_t launch_router_logits(const void* x, const void* wr, float* logits, int T, int H, int E, int act,
                                 hipStream_t st) {
   if (T <= router_small_max_tokens()) {
-    router_logits_small_kernel<<<dim3(E, T), 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr, logits, H, E,
+    launch_kernel(router_logits_small_kernel, dim3(E, T), 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr, logits, H, E,
                                                             act);
   } else {
     dim3 grid((T + 3) / 4, (E + 15) / 16);
-    router_logits_tile_kernel<<<grid, 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)wr, logits, T, H, E, act);
+    launch_kernel(router_logits_tile_kernel, grid, 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr, logits, T, H, E, act);
   }
   return hipGetLastError();
 }
@@ -216,9 +216,9 @@ hipError_t launch_router_logits(const void* x, const void* wr, float* logits, in
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* k_used,
                        float* entropy, hipStream_t st) {
   if (k > 0) {
-    topk_static_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, T, E, k, idx, w, k_used, entropy);
+    launch_kernel(topk_static_kernel, (T + 3) / 4, 256, 0, st, logits, T, E, k, idx, w, k_used, entropy);
   } else {
-    topk_entropy_kernel<<<1, 1024, 0, st>>>(logits, T, E, idx, w, k_used, entropy);
+    launch_kernel(topk_entropy_kernel, 1, 1024, 0, st, logits, T, E, idx, w, k_used, entropy);
   }
   return hipGetLastError();
 }

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
 
 hipError_t launch_sort_pairs(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st) {
-  sort_pairs_kernel<<<E, 1024, 0, st>>>(idx, T, kcap, k_used_dev, k_static, E, counts, offsets, perm, pos);
+  launch_kernel(sort_pairs_kernel, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets, perm, pos);
   return hipGetLastError();
 }
 
