@@ -217,7 +217,10 @@ int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
 /*
  * Launch-shape knobs for measurement sweeps (process-wide): key 0 = resident
  * waves per CU targeted by the decode gate+up kernel, key 1 = by the decode
- * down kernel.  Values <= 0 are ignored.  Results do not depend on them.
+ * down kernel, key 2 = row tiles per group in the batched GEMM's tile order,
+ * key 3 = the batched GEMM's row tile (32, 64 or 128; other values: chosen
+ * from the batch).
+ * Values <= 0 are ignored.  Results do not depend on them.
  */
 void moe_debug_set_tuning(int32_t key, int32_t value);
 

@@ -287,7 +287,7 @@ def debug_set_events(events: Optional[Sequence]) -> None:
 
 
 def debug_set_tuning(key: int, value: int) -> None:
-    """Launch-shape knob (0: decode gate+up waves/CU, 1: decode down waves/CU)."""
+    """Launch-shape knob (0: decode gate+up waves/CU, 1: decode down waves/CU, 2: GEMM row tiles per group, 3: GEMM row tile)."""
     lib().moe_debug_set_tuning(int(key), int(value))
 
 

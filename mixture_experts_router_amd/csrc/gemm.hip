@@ -39,11 +39,38 @@ struct GemmParams {
   int kcap, E, K, N;
   WView w0, w1;
   void* out;
+  // tile order (see tile_of): n_tiles column tiles x m_tiles row tiles, in
+  // groups of group_m row tiles; per_xcd consecutive tiles per XCD
+  int n_tiles, m_tiles, group_m, per_xcd;
 };
+
+constexpr int NUM_XCD = 8;  // MI355X: workgroups go round-robin over 8 XCDs, each with its own L2
+
+// Logical tile of workgroup `bid`.  The dispatcher places workgroup b on XCD
+// b % 8, so XCD x is given the contiguous logical range [x*per_xcd,
+// (x+1)*per_xcd).  Logical tiles run over groups of group_m row tiles, then
+// column tiles, then the row tiles of the group: the workgroups of one XCD
+// share a column tile's weights across the row tiles of a group and the
+// group's activation rows across column tiles, in the same L2.  Returns false
+// for indices past the last tile.
+__device__ __forceinline__ bool tile_of(const GemmParams& prm, int bid, int& n, int& mt) {
+  const int logical = (bid % NUM_XCD) * prm.per_xcd + bid / NUM_XCD;
+  const int per_group = prm.n_tiles * prm.group_m;
+  const int mg = logical / per_group;
+  const int rem = logical - mg * per_group;
+  const int gsz = min(prm.group_m, prm.m_tiles - mg * prm.group_m);
+  if (gsz <= 0) return false;
+  n = rem / gsz;
+  if (n >= prm.n_tiles) return false;
+  mt = mg * prm.group_m + rem % gsz;
+  return true;
+}
 
 constexpr int A_STRIDE = 144;  // bytes per staged A row (64 fp16 + 16 bytes padding)
 
 int gemm_block_m(int P, int E) {
+  const int forced = tuning(TUNE_GEMM_BM);
+  if (forced == 32 || forced == 64 || forced == 128) return forced;
   const int avg = E > 0 ? P / E : P;
   if (avg <= 32) return 32;
   if (avg <= 96) return 64;
@@ -65,55 +92,70 @@ __device__ __forceinline__ void load_b(BRaw<BITS>& r, const uint8_t* qrow, const
   constexpr int GROUP_BYTES = 64 * BITS / 8;
   const uint8_t* p = qrow + (size_t)g * GROUP_BYTES + hh * (GROUP_BYTES / 2);
 #pragma unroll
-  for (int i = 0; i < BRaw<BITS>::WORDS / 4; ++i) r.q[i] = load_stream16(p + 16 * i);
+  // cached loads: a lane reads part of a 128-byte line per group and the next
+  // groups read the rest of it from L2
+  for (int i = 0; i < BRaw<BITS>::WORDS / 4; ++i) r.q[i] = load16(p + 16 * i);
   if constexpr (BITS != 16) {
     r.s = srow[g];
     r.b = brow[g];
   }
 }
 
-// one fp16 pair of codes (biased by 1024) -> dequantised fp16 pair
-__device__ __forceinline__ uint32_t deq_pair(uint32_t biased, f16x2 s2, f16x2 b2) {
-  f16x2 q = __builtin_bit_cast(f16x2, biased) - (f16x2){(f16)1024.0f, (f16)1024.0f};
-  f16x2 w = __builtin_elementwise_fma(q, s2, b2);
-  return __builtin_bit_cast(uint32_t, w);
-}
-
-// dequantised B operands of the 4 MFMA k-steps of one group
+// Dequantised B operand of MFMA k-step j (8 weights of this lane's column)
+// of one group.  Every weight is w = fp16(fma(q, s, b)) (one rounding):
+// codes become 1024 + q (or 1024 + 16q for the high nibble of a 4-bit byte)
+// with v_and_or_b32 / v_perm_b32, an exact packed fp16 operation recovers q,
+// and a packed fma applies the group's scale and bias.
 template <int BITS>
-__device__ __forceinline__ void dequant_b(const BRaw<BITS>& r, f16x8 bf[4]) {
+__device__ __forceinline__ f16x8 dequant_b(const BRaw<BITS>& r, int j, const Q4Consts& qc) {
   if constexpr (BITS == 16) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = __builtin_bit_cast(f16x8, r.q[j]);
+    return __builtin_bit_cast(f16x8, r.q[j]);
   } else {
     const f16 s = __builtin_bit_cast(f16, (uint16_t)r.s), b = __builtin_bit_cast(f16, (uint16_t)r.b);
     const f16x2 s2 = {s, s}, b2 = {b, b};
+    const f16x2 m1024 = {(f16)-1024.0f, (f16)-1024.0f};
+    auto lo = [&](uint32_t p) {  // 1024 + q  ->  s q + b
+      const f16x2 q = __builtin_bit_cast(f16x2, p) + m1024;
+      return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
+    };
     if constexpr (BITS == 4) {
-      const uint32_t w[4] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t p[4];
-        q4_word_to_biased_pairs(w[j], p);
-        u32x4 o = {deq_pair(p[0], s2, b2), deq_pair(p[1], s2, b2), deq_pair(p[2], s2, b2), deq_pair(p[3], s2, b2)};
-        bf[j] = __builtin_bit_cast(f16x8, o);
-      }
+      const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f}, m64 = {(f16)-64.0f, (f16)-64.0f};
+      auto hi = [&](uint32_t p) {  // 1024 + 16q  ->  q (exact)  ->  s q + b
+        const f16x2 q = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p), sixteenth, m64);
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
+      };
+      const uint32_t w = j == 0 ? r.q[0].x : j == 1 ? r.q[0].y : j == 2 ? r.q[0].z : r.q[0].w;
+      uint32_t p04, p15, p26, p37;
+      q4_word_unpack(w, qc, p04, p15, p26, p37);
+      const u32x4 o = {lo(p04), hi(p15), lo(p26), hi(p37)};
+      return __builtin_bit_cast(f16x8, o);
     } else {
-      const uint32_t w[8] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w, r.q[1].x, r.q[1].y, r.q[1].z, r.q[1].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t p0[2], p1[2];
-        q8_word_to_biased_pairs(w[2 * j], p0);
-        q8_word_to_biased_pairs(w[2 * j + 1], p1);
-        u32x4 o = {deq_pair(p0[0], s2, b2), deq_pair(p0[1], s2, b2), deq_pair(p1[0], s2, b2),
-                   deq_pair(p1[1], s2, b2)};
-        bf[j] = __builtin_bit_cast(f16x8, o);
-      }
+      const u32x4 q = r.q[j / 2];
+      const uint32_t w0 = (j & 1) ? q.z : q.x, w1 = (j & 1) ? q.w : q.y;
+      uint32_t p0[2], p1[2];
+      q8_word_to_biased_pairs(w0, p0);
+      q8_word_to_biased_pairs(w1, p1);
+      const u32x4 o = {lo(p0[0]), lo(p0[1]), lo(p1[0]), lo(p1[1])};
+      return __builtin_bit_cast(f16x8, o);
     }
   }
 }
 
-template <int BITS, int MODE, int MS>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
+// One workgroup = one (expert, row tile, column tile).  4 waves side by side
+// along N, each 32*MS rows x 64 columns (two 32-column subtiles; fused: 32
+// gate and the matching 32 up columns).  K advances one 64-column group per
+// step.  Software pipeline, one barrier per group:
+//   A (activation rows): global loads two groups ahead into a 2-deep register
+//     ring, converted to fp16 and written to a double-buffered LDS tile one
+//     group ahead;
+//   B (weights): loads two groups ahead into a 2-deep register ring,
+//     dequantised right before use.
+// Every load is issued on every path (rows past the tile re-read the tile's
+// first row, groups past the end re-read the last group, columns past N
+// re-read column 0; none of those results is stored), so the compiler's wait
+// counts stay exact and loads stay in flight across the MFMAs.
+template <int BITS, int MODE, int MS, int ACT>
+__global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams prm) {
   constexpr int BM = 32 * MS;
   constexpr int APT = BM * 8 / 256;  // 16-byte A pieces per thread per group
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][BM * A_STRIDE];
@@ -125,8 +167,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
 
   // ---- which (expert, M tile) this workgroup owns: tiles are numbered
   // expert by expert, ceil(count/BM) tiles per expert
+  int n_tile = 0, y = 0;
+  if (!tile_of(prm, blockIdx.x, n_tile, y)) return;
   if (tid < WAVE) {
-    const int y = blockIdx.y;
     int base_tiles = 0, fe = -1, fmt = 0;
     for (int base = 0; base < prm.E; base += WAVE) {
       const int e = base + lane;
@@ -167,6 +210,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
   const int row0 = s_tile[2];
   const int K = prm.K;
   const int ng = K / 64;
+  const Q4Consts qc = q4_consts();
 
   // ---- A sources: APT pieces per thread, fixed across groups
   const uint16_t* a_src[APT];
@@ -175,18 +219,15 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
   for (int i = 0; i < APT; ++i) {
     const int pc = tid + 256 * i;
     const int r = pc / 8, j = pc % 8;
+    const int rr = r < rows ? r : 0;  // past the tile: the tile's first row (never stored)
     a_off[i] = r * A_STRIDE + j * 16;
-    a_src[i] = nullptr;
-    if (r < rows) {
-      if constexpr (MODE == GEMM_ROWS_F16) {
-        a_src[i] = prm.a + (size_t)(row0 + r) * K + 8 * j;
-      } else {
-        const int pair = prm.perm[row0 + r];
-        a_src[i] = prm.a + (size_t)(pair / prm.kcap) * K + 8 * j;
-      }
+    if constexpr (MODE == GEMM_ROWS_F16) {
+      a_src[i] = prm.a + (size_t)(row0 + rr) * K + 8 * j;
+    } else {
+      const int pair = prm.perm[row0 + rr];
+      a_src[i] = prm.a + (size_t)(pair / prm.kcap) * K + 8 * j;
     }
   }
-  const int act = MODE == GEMM_ROWS_F16 ? ACT_F16 : prm.act;
 
   // ---- B rows of this wave (2 subtiles of 32 columns)
   const int hh = lane / 32;
@@ -198,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
   const uint16_t* bb[2];
   const int64_t row_bytes = (int64_t)K * BITS / 8;
   if constexpr (MODE == GEMM_FUSED_SWIGLU) {
-    col0 = blockIdx.x * 128 + wave * 32;
+    col0 = n_tile * 128 + wave * 32;
     valid[0] = valid[1] = col0 < prm.N;
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
@@ -209,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
       bb[ni] = BITS == 16 ? nullptr : wv.b + row * ng;
     }
   } else {
-    col0 = blockIdx.x * 256 + wave * 64;
+    col0 = n_tile * 256 + wave * 64;
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
       valid[ni] = col0 + 32 * ni < prm.N;
@@ -219,7 +260,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
       bb[ni] = BITS == 16 ? nullptr : prm.w0.b + row * ng;
     }
   }
-  const bool wave_live = valid[0];
 
   f32x16 acc[MS][2];
 #pragma unroll
@@ -229,68 +269,64 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  u32x4 areg[APT];
-  auto load_a = [&](int g) {
+  u32x4 areg[2][APT];
+  BRaw<BITS> braw[2][2];
+  auto load_a = [&](u32x4 (&dst)[APT], int g) {
+#pragma unroll
+    for (int i = 0; i < APT; ++i) dst[i] = load16(a_src[i] + (size_t)g * 64);
+  };
+  auto store_a = [&](const u32x4 (&src)[APT], int buf) {
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (a_src[i]) v = act8_to_f16(load16(a_src[i] + (size_t)g * 64), act);
+      u32x4 v = src[i];
+      if constexpr (ACT == ACT_BF16) v = act8_to_f16(v, ACT_BF16);
       if constexpr (BITS == 4) v = perm8_nibble_order(v);
-      areg[i] = v;
+      *(u32x4*)(&a_lds[buf][a_off[i]]) = v;
     }
   };
-  auto store_a = [&](int buf) {
+  auto load_bg = [&](BRaw<BITS> (&dst)[2], int g) {
 #pragma unroll
-    for (int i = 0; i < APT; ++i) *(u32x4*)(&a_lds[buf][a_off[i]]) = areg[i];
+    for (int ni = 0; ni < 2; ++ni) load_b<BITS>(dst[ni], bq[ni], bs[ni], bb[ni], g, hh);
   };
-
-  BRaw<BITS> braw[2];
-  if (wave_live) {
+  auto mma = [&](const BRaw<BITS> (&src)[2], int buf) {
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-      if (valid[ni]) load_b<BITS>(braw[ni], bq[ni], bs[ni], bb[ni], 0, hh);
-  }
-  load_a(0);
-  store_a(0);
+    for (int j = 0; j < 4; ++j) {
+      const f16x8 b0 = dequant_b<BITS>(src[0], j, qc), b1 = dequant_b<BITS>(src[1], j, qc);
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi) {
+        const f16x8 af = *(const f16x8*)(&a_lds[buf][(mi * 32 + col_in) * A_STRIDE + (32 * hh + 8 * j) * 2]);
+        acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b0, acc[mi][0], 0, 0, 0);
+        acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b1, acc[mi][1], 0, 0, 0);
+      }
+    }
+  };
+  const int last = ng - 1;
+  auto gi = [&](int g) { return g < last ? g : last; };
+
+  // prologue: A(0) in LDS, A(1) and B(0), B(1) in flight
+  load_a(areg[0], 0);
+  load_a(areg[1], gi(1));
+  load_bg(braw[0], 0);
+  load_bg(braw[1], gi(1));
+  store_a(areg[0], 0);
   __syncthreads();
 
-  for (int g = 0; g < ng; ++g) {
-    const int cur = g & 1;
-    const bool more = g + 1 < ng;
-    if (more) load_a(g + 1);
-    if (wave_live) {
-      f16x8 bf[2][4];
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        if (valid[ni]) dequant_b<BITS>(braw[ni], bf[ni]);
-        else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bf[ni][j] = (f16x8){};
-        }
-      }
-      if (more) {
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          if (valid[ni]) load_b<BITS>(braw[ni], bq[ni], bs[ni], bb[ni], g + 1, hh);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int mi = 0; mi < MS; ++mi) {
-          if (mi * 32 < rows) {
-            const f16x8 af = *(const f16x8*)(&a_lds[cur][(mi * 32 + col_in) * A_STRIDE + (32 * hh + 8 * j) * 2]);
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[ni][j], acc[mi][ni], 0, 0, 0);
-          }
-        }
-      }
-    }
-    if (more) store_a(cur ^ 1);
+  // group g: A(g) in LDS buffer g%2, A(g+1) in areg[(g+1)%2], B(g) in braw[g%2]
+  for (int g = 0; g < ng; g += 2) {
+    load_a(areg[0], gi(g + 2));
+    mma(braw[0], 0);
+    load_bg(braw[0], gi(g + 2));
+    store_a(areg[1], 1);
+    __syncthreads();
+    if (g + 1 >= ng) break;
+    load_a(areg[1], gi(g + 3));
+    mma(braw[1], 1);
+    load_bg(braw[1], gi(g + 3));
+    store_a(areg[0], 0);
     __syncthreads();
   }
 
-  if (!wave_live) return;
+  if (!valid[0]) return;
   // ---- epilogue.  32x32 accumulator layout: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
@@ -317,15 +353,21 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams prm) {
   }
 }
 
-template <int BITS, int MODE>
-static hipError_t launch_ms(int bm, const GemmParams& prm, dim3 grid, hipStream_t st) {
+template <int BITS, int MODE, int ACT>
+static hipError_t launch_act(int bm, const GemmParams& prm, dim3 grid, hipStream_t st) {
   switch (bm) {
-    case 32: launch_kernel(gemm_kernel<BITS, MODE, 1>, grid, 256, 0, st, prm); break;
-    case 64: launch_kernel(gemm_kernel<BITS, MODE, 2>, grid, 256, 0, st, prm); break;
-    case 128: launch_kernel(gemm_kernel<BITS, MODE, 4>, grid, 256, 0, st, prm); break;
+    case 32: return launch_kernel(gemm_kernel<BITS, MODE, 1, ACT>, grid, 256, 0, st, prm);
+    case 64: return launch_kernel(gemm_kernel<BITS, MODE, 2, ACT>, grid, 256, 0, st, prm);
+    case 128: return launch_kernel(gemm_kernel<BITS, MODE, 4, ACT>, grid, 256, 0, st, prm);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+}
+
+// the down projection reads fp16 SwiGLU rows whatever the activation dtype
+template <int BITS, int MODE>
+static hipError_t launch_ms(int bm, const GemmParams& prm, dim3 grid, hipStream_t st) {
+  if (MODE != GEMM_ROWS_F16 && prm.act == ACT_BF16) return launch_act<BITS, MODE, ACT_BF16>(bm, prm, grid, st);
+  return launch_act<BITS, MODE, ACT_F16>(bm, prm, grid, st);
 }
 
 template <int BITS>
@@ -355,7 +397,12 @@ hipError_t launch_gemm(GemmMode mode, const void* a, int act, const int32_t* per
   prm.w1 = w1;
   prm.out = out;
   const int ncols = mode == GEMM_FUSED_SWIGLU ? 128 : 256;
-  dim3 grid((N + ncols - 1) / ncols, max_mtiles);
+  prm.n_tiles = (N + ncols - 1) / ncols;
+  prm.m_tiles = max_mtiles;
+  prm.group_m = tuning(TUNE_GEMM_GROUP_M);
+  const int64_t total = (int64_t)prm.n_tiles * prm.m_tiles;
+  prm.per_xcd = (int)((total + NUM_XCD - 1) / NUM_XCD);
+  dim3 grid((unsigned)(prm.per_xcd * NUM_XCD));
   if (bits == 4) return launch_bits<4>(mode, bm, prm, grid, st);
   if (bits == 8) return launch_bits<8>(mode, bm, prm, grid, st);
   return launch_bits<16>(mode, bm, prm, grid, st);

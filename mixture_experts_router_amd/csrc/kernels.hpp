@@ -31,7 +31,13 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 
 // Launch-shape knobs (resident waves per CU the decode kernels aim for).
 // Defaults are the measured best; moe_debug_set_tuning overrides them.
-enum TuneKey { TUNE_UP_WAVES_PER_CU = 0, TUNE_DOWN_WAVES_PER_CU = 1, TUNE_KEYS = 2 };
+enum TuneKey {
+  TUNE_UP_WAVES_PER_CU = 0,
+  TUNE_DOWN_WAVES_PER_CU = 1,
+  TUNE_GEMM_GROUP_M = 2,
+  TUNE_GEMM_BM = 3,  // 32, 64 or 128 forces the GEMM row tile; anything else: chosen from the batch
+  TUNE_KEYS = 4
+};
 int tuning(TuneKey key);
 
 // One expert weight view: row n of expert e starts at q + (e*stride + n)*row_bytes.
