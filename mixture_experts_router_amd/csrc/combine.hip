@@ -50,22 +50,50 @@ hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wt
   return hipGetLastError();
 }
 
+// h = silu(g) * u; with perm8 set, each 8-element block of h is stored in
+// 4-bit unpack order (the operand order of the batched 4-bit down GEMM).
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g, const float* __restrict__ u,
-                                                     uint16_t* __restrict__ h, int64_t n) {
+                                                     uint16_t* __restrict__ h, int64_t n, int perm8) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) h[i] = f32_to_f16_bits(swiglu(g[i], u[i]));
+  if (i >= n) return;
+  const int64_t at = perm8 ? (i & ~(int64_t)7) + perm8_slot((int)(i & 7)) : i;
+  h[at] = f32_to_f16_bits(swiglu(g[i], u[i]));
 }
 
-hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, hipStream_t st) {
+hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, bool perm8,
+                         hipStream_t st) {
   const int64_t n = rows * I;
-  launch_kernel(swiglu_kernel, (unsigned)((n + 255) / 256), 256, 0, st, g, u, h, n);
+  launch_kernel(swiglu_kernel, (unsigned)((n + 255) / 256), 256, 0, st, g, u, h, n, perm8 ? 1 : 0);
   return hipGetLastError();
 }
 
+// Activation operand of the batched GEMM: x (fp16 or bf16) -> fp16, each
+// 8-element block optionally in 4-bit unpack order.  bf16 -> fp16 is exact
+// for values in fp16's normal range.
+__global__ __launch_bounds__(256) void prep_a_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ a,
+                                                     int64_t n8, int act, int perm8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  u32x4 v = act8_to_f16(load16(x + 8 * i), act);
+  if (perm8) v = perm8_nibble_order(v);
+  *(u32x4*)(a + 8 * i) = v;
+}
+
+hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, bool perm8, hipStream_t st) {
+  const int64_t n8 = T * H / 8;
+  if (n8 <= 0) return hipSuccess;
+  launch_kernel(prep_a_kernel, (unsigned)((n8 + 255) / 256), 256, 0, st, (const uint16_t*)x, a, n8, act,
+                perm8 ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Rows of h in pair order (taps); perm8 restores the natural element order
+// of rows stored in 4-bit unpack order.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ src,
                                                           const int32_t* __restrict__ pos, int I,
                                                           uint16_t* __restrict__ out, int kcap,
-                                                          const int32_t* __restrict__ k_used, int k_static) {
+                                                          const int32_t* __restrict__ k_used, int k_static,
+                                                          int perm8) {
   const int64_t p = blockIdx.y;
   int64_t r;
   if (pos) {
@@ -75,14 +103,17 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
     r = (int)(p % kcap) < ku ? p : -1;
   }
   if (r < 0) return;
-  for (int c = (blockIdx.x * 256 + threadIdx.x) * 8; c < I; c += gridDim.x * 256 * 8)
-    *(u32x4*)(out + p * I + c) = load16(src + (size_t)r * I + c);
+  for (int c = (blockIdx.x * 256 + threadIdx.x) * 8; c < I; c += gridDim.x * 256 * 8) {
+    u32x4 v = load16(src + (size_t)r * I + c);
+    if (perm8) v = perm8_natural_order(v);
+    *(u32x4*)(out + p * I + c) = v;
+  }
 }
 
 hipError_t launch_gather_rows(const uint16_t* src, const int32_t* pos, int64_t P, int I, uint16_t* out, int kcap,
-                              const int32_t* k_used_dev, int k_static, hipStream_t st) {
+                              const int32_t* k_used_dev, int k_static, bool perm8, hipStream_t st) {
   dim3 grid((I / 8 + 255) / 256, (unsigned)P);
-  launch_kernel(gather_rows_kernel, grid, 256, 0, st, src, pos, I, out, kcap, k_used_dev, k_static);
+  launch_kernel(gather_rows_kernel, grid, 256, 0, st, src, pos, I, out, kcap, k_used_dev, k_static, perm8 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -82,6 +82,19 @@ __device__ __forceinline__ u32x4 perm8_nibble_order(u32x4 v) {
   return r;
 }
 
+// Inverse of perm8_nibble_order: (k0,k4) (k1,k5) (k2,k6) (k3,k7) -> k0..k7.
+__device__ __forceinline__ u32x4 perm8_natural_order(u32x4 v) {
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (k0, k1)
+  r.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (k2, k3)
+  r.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (k4, k5)
+  r.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (k6, k7)
+  return r;
+}
+
+// Position of element i (0..7) of an 8-element block in unpack order.
+__device__ __forceinline__ int perm8_slot(int i) { return (i & 3) * 2 + (i >> 2); }
+
 // ----------------------------------------------------- unpacking codes ---
 //
 // gfx9 VOP3 instructions cannot encode 32-bit literals, so (v & mask) | magic

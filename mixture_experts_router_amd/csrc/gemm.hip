@@ -3,24 +3,32 @@
 // Rows of one M tile are consecutive sorted pairs of one expert (the sorted
 // gather branch of the oMLX gate/up fusion page), so every tile multiplies one
 // expert's weights.  Three instantiations:
-//   GEMM_FUSED_SWIGLU  A = x rows gathered through perm, B = the fused gate_up
-//                      tensor; each wave owns 32 gate and the matching 32 up
-//                      columns, so the SwiGLU epilogue h = silu(g) * u is local
-//                      to a lane (oMLX page, steps 3-4: one matmul over the
-//                      [gate, up] concatenation, split, then activation)
+//   GEMM_FUSED_SWIGLU  A = activation rows gathered through perm, B = the
+//                      fused gate_up tensor; each wave owns 32 gate and the
+//                      matching 32 up columns, so the SwiGLU epilogue
+//                      h = silu(g) * u is local to a lane (oMLX page, steps 3-4:
+//                      one matmul over the [gate, up] concatenation, split,
+//                      then activation)
 //   GEMM_GATHER_F32    the same A, one projection, fp32 output (unfused path)
 //   GEMM_ROWS_F16      A = h rows in sorted order, B = down, fp16 output
 //
-// Tile: BM = 32*MS rows x 256 columns (fused: 128 gate/up column pairs), 4
-// waves side by side along N, each 32*MS x 64, K stepped one 64-column
-// quantisation group at a time.  A (fp16; bf16 activations are converted,
-// exact in range) is staged through LDS, double-buffered, rows padded to
-// 144 bytes so 8 lanes of a 16-byte read hit 8 different bank groups.
-// B never touches LDS: each lane loads the 16 bytes of codes it needs,
-// dequantises them in registers (w = fma(q, s, b) in fp16, one rounding) and
-// feeds v_mfma_f32_32x32x16_f16 with fp32 accumulation.  For 4-bit weights the
-// k order inside each 8-column block is (0,4,1,5,2,6,3,7) on both operands,
-// the order in which a 32-bit word of nibbles unpacks.
+// The A operand is fp16 in HBM, each 8-element block in the order in which
+// the weights unpack (4-bit: 0,4,1,5,2,6,3,7; otherwise natural): the
+// activations are converted once by prep_a_kernel and the fused epilogue
+// writes h that way.  Tile: BM = 32*MS rows x 256 columns (fused: 128
+// gate/up column pairs), 4 waves side by side along N, each 32*MS x 64; K
+// advances one 64-column quantisation group per step.
+//
+// Both operands stream HBM -> LDS with global_load_lds_dwordx4 (no register
+// staging) through NS stages sized to the LDS: A rows with a 16-byte-chunk XOR
+// swizzle (chunk ^ (row/2 % 8)) so the MFMA operand reads are conflict free;
+// each wave's 64 weight rows into its own LDS region.  Scales and biases ride
+// a register ring of the same depth.  One wait (this wave's loads of the
+// stage) and one barrier (every wave's loads; the oldest stage free) per
+// group, then the next group's loads are issued and the stage is consumed:
+// B codes read once per group, dequantised per MFMA k-step in registers
+// (w = fma(q, s, b) in fp16, one rounding), v_mfma_f32_32x32x16_f16 with fp32
+// accumulation.
 //
 // Each output element's reduction runs over the same k order whichever
 // instantiation, tile or column position computes it, so the fused and
@@ -31,14 +39,14 @@
 namespace moe {
 
 struct GemmParams {
-  const uint16_t* a;
-  int act;
+  const uint16_t* a;  // fp16 operand rows, 8-element blocks in the weights' unpack order
   const int32_t* perm;
   const int32_t* counts;
   const int32_t* offsets;
   int kcap, E, K, N;
   WView w0, w1;
   void* out;
+  int perm8_out;  // fused: store h blocks in 4-bit unpack order
   // tile order (see tile_of): n_tiles column tiles x m_tiles row tiles, in
   // groups of group_m row tiles; per_xcd consecutive tiles per XCD
   int n_tiles, m_tiles, group_m, per_xcd;
@@ -66,8 +74,6 @@ __device__ __forceinline__ bool tile_of(const GemmParams& prm, int bid, int& n, 
   return true;
 }
 
-constexpr int A_STRIDE = 144;  // bytes per staged A row (64 fp16 + 16 bytes padding)
-
 int gemm_block_m(int P, int E) {
   const int forced = tuning(TUNE_GEMM_BM);
   if (forced == 32 || forced == 64 || forced == 128) return forced;
@@ -79,39 +85,79 @@ int gemm_block_m(int P, int E) {
 
 int gemm_max_mtiles(int P, int E, int bm) { return (P + bm - 1) / bm + E; }
 
-template <int BITS>
-struct BRaw {
-  static constexpr int WORDS = BITS == 4 ? 4 : (BITS == 8 ? 8 : 16);  // u32 of codes per lane per group
-  u32x4 q[WORDS / 4];
-  uint32_t s, b;
+// Geometry of one pipeline stage (KG quantisation groups of 64 k columns) of
+// a wave's 64 weight rows, stored row-major [64 rows][SEG bytes] in LDS: a
+// load instruction reads SEG contiguous bytes of each of RPI rows (DRAM
+// streams rows in segments of at least 64 bytes far better than in 32).
+template <int BITS, int KG>
+struct BGeo {
+  static constexpr int ROW = 64 * BITS / 8;  // code bytes of one row per group: 32 / 64 / 128
+  static constexpr int SEG = KG * ROW;       // bytes of one row per stage
+  static constexpr int LPR = SEG / 16;       // 16-byte pieces per row
+  static constexpr int RPI = 64 / LPR;       // rows per 64-lane load instruction
+  static constexpr int NI = 64 / RPI;        // load instructions per wave
+  static constexpr int HALF = ROW / 2;       // bytes a lane feeds per group (its half of the group's k)
+  static constexpr int READS = HALF / 16;    // 16-byte LDS reads per lane, subtile and group
 };
 
-template <int BITS>
-__device__ __forceinline__ void load_b(BRaw<BITS>& r, const uint8_t* qrow, const uint16_t* srow, const uint16_t* brow,
-                                       int g, int hh) {
-  constexpr int GROUP_BYTES = 64 * BITS / 8;
-  const uint8_t* p = qrow + (size_t)g * GROUP_BYTES + hh * (GROUP_BYTES / 2);
-#pragma unroll
-  // cached loads: a lane reads part of a 128-byte line per group and the next
-  // groups read the rest of it from L2
-  for (int i = 0; i < BRaw<BITS>::WORDS / 4; ++i) r.q[i] = load16(p + 16 * i);
-  if constexpr (BITS != 16) {
-    r.s = srow[g];
-    r.b = brow[g];
+template <int BITS, int MS, int KG>
+struct GemmCfg {
+  static constexpr int BM = 32 * MS;
+  static constexpr int A_SUB = BM * 128;  // A of one group: BM rows x 64 fp16
+  static constexpr int A_BYTES = KG * A_SUB;
+  static constexpr int B_BYTES = 4 * 64 * BGeo<BITS, KG>::SEG;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  // 128-row tiles: one workgroup per CU (160 KB LDS); smaller: two
+  static constexpr int BUDGET = MS == 4 ? 156 * 1024 : 78 * 1024;
+  static constexpr int NS_FIT = BUDGET / STAGE;
+  static constexpr int NS = NS_FIT < 2 ? 2 : (NS_FIT > 6 ? 6 : NS_FIT);
+  // vector memory instructions per wave per stage: A, B, scales and biases
+  static constexpr int LOADS = KG * MS + BGeo<BITS, KG>::NI + (BITS != 16 ? 4 * KG : 0);
+  static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
+  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from buffer r at voff + soff into LDS (lane i at dst + 16 i)
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+}
+
+// wait until at most N vector memory instructions of this wave are pending
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+
+// f(IC<0>), f(IC<1>), ... while f returns true
+template <int S, int N, typename F>
+__device__ __forceinline__ void for_stages(F&& f) {
+  if constexpr (S < N) {
+    if (f(IC<S>{})) for_stages<S + 1, N>(f);
   }
 }
 
 // Dequantised B operand of MFMA k-step j (8 weights of this lane's column)
-// of one group.  Every weight is w = fp16(fma(q, s, b)) (one rounding):
+// of one group, from the lane's code bytes c (4-bit: c[0]; 8-bit: c[0..1];
+// fp16: c[0..3]).  Every weight is w = fp16(fma(q, s, b)) (one rounding):
 // codes become 1024 + q (or 1024 + 16q for the high nibble of a 4-bit byte)
 // with v_and_or_b32 / v_perm_b32, an exact packed fp16 operation recovers q,
 // and a packed fma applies the group's scale and bias.
 template <int BITS>
-__device__ __forceinline__ f16x8 dequant_b(const BRaw<BITS>& r, int j, const Q4Consts& qc) {
+__device__ __forceinline__ f16x8 dequant_b(const u32x4* c, int j, uint32_t s_bits, uint32_t b_bits,
+                                           const Q4Consts& qc) {
   if constexpr (BITS == 16) {
-    return __builtin_bit_cast(f16x8, r.q[j]);
+    return __builtin_bit_cast(f16x8, c[j]);
   } else {
-    const f16 s = __builtin_bit_cast(f16, (uint16_t)r.s), b = __builtin_bit_cast(f16, (uint16_t)r.b);
+    const f16 s = __builtin_bit_cast(f16, (uint16_t)s_bits), b = __builtin_bit_cast(f16, (uint16_t)b_bits);
     const f16x2 s2 = {s, s}, b2 = {b, b};
     const f16x2 m1024 = {(f16)-1024.0f, (f16)-1024.0f};
     auto lo = [&](uint32_t p) {  // 1024 + q  ->  s q + b
@@ -124,13 +170,13 @@ __device__ __forceinline__ f16x8 dequant_b(const BRaw<BITS>& r, int j, const Q4C
         const f16x2 q = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p), sixteenth, m64);
         return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
       };
-      const uint32_t w = j == 0 ? r.q[0].x : j == 1 ? r.q[0].y : j == 2 ? r.q[0].z : r.q[0].w;
+      const uint32_t w = j == 0 ? c[0].x : j == 1 ? c[0].y : j == 2 ? c[0].z : c[0].w;
       uint32_t p04, p15, p26, p37;
       q4_word_unpack(w, qc, p04, p15, p26, p37);
       const u32x4 o = {lo(p04), hi(p15), lo(p26), hi(p37)};
       return __builtin_bit_cast(f16x8, o);
     } else {
-      const u32x4 q = r.q[j / 2];
+      const u32x4 q = c[j / 2];
       const uint32_t w0 = (j & 1) ? q.z : q.x, w1 = (j & 1) ? q.w : q.y;
       uint32_t p0[2], p1[2];
       q8_word_to_biased_pairs(w0, p0);
@@ -141,25 +187,25 @@ __device__ __forceinline__ f16x8 dequant_b(const BRaw<BITS>& r, int j, const Q4C
   }
 }
 
-// One workgroup = one (expert, row tile, column tile).  4 waves side by side
-// along N, each 32*MS rows x 64 columns (two 32-column subtiles; fused: 32
-// gate and the matching 32 up columns).  K advances one 64-column group per
-// step.  Software pipeline, one barrier per group:
-//   A (activation rows): global loads two groups ahead into a 2-deep register
-//     ring, converted to fp16 and written to a double-buffered LDS tile one
-//     group ahead;
-//   B (weights): loads two groups ahead into a 2-deep register ring,
-//     dequantised right before use.
-// Every load is issued on every path (rows past the tile re-read the tile's
-// first row, groups past the end re-read the last group, columns past N
-// re-read column 0; none of those results is stored), so the compiler's wait
-// counts stay exact and loads stay in flight across the MFMAs.
-template <int BITS, int MODE, int MS, int ACT>
+template <int BITS, int MODE, int MS, int KG>
 __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams prm) {
-  constexpr int BM = 32 * MS;
-  constexpr int APT = BM * 8 / 256;  // 16-byte A pieces per thread per group
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][BM * A_STRIDE];
+  using G = BGeo<BITS, KG>;
+  using C = GemmCfg<BITS, MS, KG>;
+  constexpr int BM = C::BM, NS = C::NS;
+  // one array per stage: distinct objects let the compiler see that reading
+  // a stage does not wait on loads still landing in the others
+  __shared__ __attribute__((aligned(16))) uint8_t st0[C::STAGE], st1[C::STAGE], st2[NS > 2 ? C::STAGE : 16],
+      st3[NS > 3 ? C::STAGE : 16], st4[NS > 4 ? C::STAGE : 16], st5[NS > 5 ? C::STAGE : 16];
   __shared__ int s_tile[4];
+  auto stage = [&](auto S_) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int S = decltype(S_)::value;
+    if constexpr (S == 0) return st0;
+    else if constexpr (S == 1) return st1;
+    else if constexpr (S == 2) return st2;
+    else if constexpr (S == 3) return st3;
+    else if constexpr (S == 4) return st4;
+    else return st5;
+  };
 
   const int lane = lane_id();
   const int wave = wave_id();
@@ -211,55 +257,71 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
   const int K = prm.K;
   const int ng = K / 64;
   const Q4Consts qc = q4_consts();
-
-  // ---- A sources: APT pieces per thread, fixed across groups
-  const uint16_t* a_src[APT];
-  int a_off[APT];
-#pragma unroll
-  for (int i = 0; i < APT; ++i) {
-    const int pc = tid + 256 * i;
-    const int r = pc / 8, j = pc % 8;
-    const int rr = r < rows ? r : 0;  // past the tile: the tile's first row (never stored)
-    a_off[i] = r * A_STRIDE + j * 16;
-    if constexpr (MODE == GEMM_ROWS_F16) {
-      a_src[i] = prm.a + (size_t)(row0 + rr) * K + 8 * j;
-    } else {
-      const int pair = prm.perm[row0 + rr];
-      a_src[i] = prm.a + (size_t)(pair / prm.kcap) * K + 8 * j;
-    }
-  }
-
-  // ---- B rows of this wave (2 subtiles of 32 columns)
   const int hh = lane / 32;
   const int col_in = lane % 32;
+
+  // All loads are buffer loads: base addresses in scalar registers, a fixed
+  // 32-bit byte offset per lane, the group's offset as the scalar offset.
+  //
+  // ---- A: load instruction q of this wave covers tile rows r0 = 8*(wave*MS+q)
+  // .. r0+7; lane i writes LDS chunk i%8 of row r0 + i/8, which holds the
+  // row's logical 16-byte chunk (i%8) ^ (row/2 % 8).  Rows past the tile
+  // re-read the tile's first row (never stored).
+  const rsrc_t ra = make_rsrc(prm.a, 0xFFFFFFFFu);
+  uint32_t a_off[MS];
+#pragma unroll
+  for (int q = 0; q < MS; ++q) {
+    const int r = 8 * (wave * MS + q) + lane / 8;
+    const int rr = r < rows ? r : 0;
+    uint32_t arow;
+    if constexpr (MODE == GEMM_ROWS_F16) arow = (uint32_t)(row0 + rr);
+    else arow = (uint32_t)(prm.perm[row0 + rr] / prm.kcap);
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    a_off[q] = arow * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
+  }
+
+  // ---- B: this wave's 64 weight rows; rows [32 ni, 32 ni + 32) are subtile
+  // ni (fused: 32 gate columns, then the matching 32 up columns).  Columns
+  // past N re-read column 0 (never stored).
   int col0;
   bool valid[2];
-  const uint8_t* bq[2];
-  const uint16_t* bs[2];
-  const uint16_t* bb[2];
-  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  const WView* view[2];
   if constexpr (MODE == GEMM_FUSED_SWIGLU) {
     col0 = n_tile * 128 + wave * 32;
     valid[0] = valid[1] = col0 < prm.N;
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const WView& wv = ni == 0 ? prm.w0 : prm.w1;
-      const int64_t row = (int64_t)e * wv.stride + (valid[ni] ? col0 + col_in : 0);
-      bq[ni] = wv.q + row * row_bytes;
-      bs[ni] = BITS == 16 ? nullptr : wv.s + row * ng;
-      bb[ni] = BITS == 16 ? nullptr : wv.b + row * ng;
-    }
+    view[0] = &prm.w0;
+    view[1] = &prm.w1;
   } else {
     col0 = n_tile * 256 + wave * 64;
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      valid[ni] = col0 + 32 * ni < prm.N;
-      const int64_t row = (int64_t)e * prm.w0.stride + (valid[ni] ? col0 + 32 * ni + col_in : 0);
-      bq[ni] = prm.w0.q + row * row_bytes;
-      bs[ni] = BITS == 16 ? nullptr : prm.w0.s + row * ng;
-      bb[ni] = BITS == 16 ? nullptr : prm.w0.b + row * ng;
-    }
+    valid[0] = col0 < prm.N;
+    valid[1] = col0 + 32 < prm.N;
+    view[0] = view[1] = &prm.w0;
   }
+  auto column = [&](int ni, int rin) __attribute__((always_inline)) {
+    const int c = MODE == GEMM_FUSED_SWIGLU ? col0 + rin : col0 + 32 * ni + rin;
+    return valid[ni] ? c : 0;
+  };
+  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  rsrc_t rq[2], rs[2], rbias[2];
+  uint32_t s_off[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const WView& v = *view[ni];
+    const int64_t erow = (int64_t)e * v.stride;  // the expert's first row
+    rq[ni] = make_rsrc(v.q + erow * row_bytes, 0xFFFFFFFFu);
+    if constexpr (BITS != 16) {
+      rs[ni] = make_rsrc(v.s + erow * ng, 0xFFFFFFFFu);
+      rbias[ni] = make_rsrc(v.b + erow * ng, 0xFFFFFFFFu);
+    }
+    s_off[ni] = (uint32_t)column(ni, col_in) * (uint32_t)ng * 2u;
+  }
+  uint32_t b_off[G::NI];
+#pragma unroll
+  for (int q = 0; q < G::NI; ++q) {
+    const int rl = q * G::RPI + lane / G::LPR;  // subtile (q * RPI) / 32 for the whole instruction
+    b_off[q] = (uint32_t)(column(rl / 32, rl % 32) * row_bytes) + (uint32_t)(lane % G::LPR) * 16u;
+  }
+  const int nst = ng / KG;  // pipeline steps (the launcher makes KG divide ng)
 
   f32x16 acc[MS][2];
 #pragma unroll
@@ -269,62 +331,101 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  u32x4 areg[2][APT];
-  BRaw<BITS> braw[2][2];
-  auto load_a = [&](u32x4 (&dst)[APT], int g) {
+  uint32_t sreg[NS][KG][2], breg[NS][KG][2];
+  const int b_lane = C::A_BYTES + wave * 64 * G::SEG + col_in * G::SEG + hh * G::HALF;  // this lane's B codes
+  const int last = nst - 1;
+  // step k (groups KG k .. KG k + KG - 1; clamped to the last step) into stage S
+  auto issue = [&](auto S_, int k) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    k = k < last ? k : last;
+    uint8_t* st = stage(S_);
 #pragma unroll
-    for (int i = 0; i < APT; ++i) dst[i] = load16(a_src[i] + (size_t)g * 64);
-  };
-  auto store_a = [&](const u32x4 (&src)[APT], int buf) {
+    for (int gi = 0; gi < KG; ++gi)
 #pragma unroll
-    for (int i = 0; i < APT; ++i) {
-      u32x4 v = src[i];
-      if constexpr (ACT == ACT_BF16) v = act8_to_f16(v, ACT_BF16);
-      if constexpr (BITS == 4) v = perm8_nibble_order(v);
-      *(u32x4*)(&a_lds[buf][a_off[i]]) = v;
+      for (int q = 0; q < MS; ++q) {
+        const int lds_off = gi * C::A_SUB + 8 * (wave * MS + q) * 128;
+        dma16(ra, a_off[q], (uint32_t)(k * KG + gi) * 128u, st + lds_off);
+      }
+#pragma unroll
+    for (int q = 0; q < G::NI; ++q) {
+      const int lds_off = C::A_BYTES + wave * 64 * G::SEG + q * 1024;
+      dma16(rq[(q * G::RPI) / 32], b_off[q], (uint32_t)k * G::SEG, st + lds_off);
+    }
+    if constexpr (BITS != 16) {
+#pragma unroll
+      for (int gi = 0; gi < KG; ++gi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          sreg[S][gi][ni] = __builtin_amdgcn_raw_buffer_load_b16(rs[ni], (int)s_off[ni], (k * KG + gi) * 2, 0);
+          breg[S][gi][ni] = __builtin_amdgcn_raw_buffer_load_b16(rbias[ni], (int)s_off[ni], (k * KG + gi) * 2, 0);
+        }
     }
   };
-  auto load_bg = [&](BRaw<BITS> (&dst)[2], int g) {
+  auto compute = [&](auto S_) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    // LDS addresses are formed as one integer offset from the stage array:
+    // the compiler attributes an access to its array (and so knows it does
+    // not wait on loads landing in other stages) only through a short chain
+    // of address arithmetic on the array itself
+    const uint8_t* st = stage(S_);
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) load_b<BITS>(dst[ni], bq[ni], bs[ni], bb[ni], g, hh);
-  };
-  auto mma = [&](const BRaw<BITS> (&src)[2], int buf) {
+    for (int gi = 0; gi < KG; ++gi) {
+      u32x4 bc[2][G::READS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f16x8 b0 = dequant_b<BITS>(src[0], j, qc), b1 = dequant_b<BITS>(src[1], j, qc);
+      for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int mi = 0; mi < MS; ++mi) {
-        const f16x8 af = *(const f16x8*)(&a_lds[buf][(mi * 32 + col_in) * A_STRIDE + (32 * hh + 8 * j) * 2]);
-        acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b0, acc[mi][0], 0, 0, 0);
-        acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b1, acc[mi][1], 0, 0, 0);
+        for (int t = 0; t < G::READS; ++t) {
+          const int off = b_lane + ni * 32 * G::SEG + gi * G::ROW + t * 16;
+          bc[ni][t] = *(const u32x4*)(st + off);
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 b0 = dequant_b<BITS>(bc[0], j, sreg[S][gi][0], breg[S][gi][0], qc);
+        const f16x8 b1 = dequant_b<BITS>(bc[1], j, sreg[S][gi][1], breg[S][gi][1], qc);
+#pragma unroll
+        for (int mi = 0; mi < MS; ++mi) {
+          const int row = mi * 32 + col_in;
+          const int off = gi * C::A_SUB + row * 128 + (((4 * hh + j) ^ ((row >> 1) & 7)) << 4);
+          const f16x8 af = *(const f16x8*)(st + off);
+          acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b0, acc[mi][0], 0, 0, 0);
+          acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b1, acc[mi][1], 0, 0, 0);
+        }
       }
     }
   };
-  const int last = ng - 1;
-  auto gi = [&](int g) { return g < last ? g : last; };
 
-  // prologue: A(0) in LDS, A(1) and B(0), B(1) in flight
-  load_a(areg[0], 0);
-  load_a(areg[1], gi(1));
-  load_bg(braw[0], 0);
-  load_bg(braw[1], gi(1));
-  store_a(areg[0], 0);
-  __syncthreads();
-
-  // group g: A(g) in LDS buffer g%2, A(g+1) in areg[(g+1)%2], B(g) in braw[g%2]
-  for (int g = 0; g < ng; g += 2) {
-    load_a(areg[0], gi(g + 2));
-    mma(braw[0], 0);
-    load_bg(braw[0], gi(g + 2));
-    store_a(areg[1], 1);
-    __syncthreads();
-    if (g + 1 >= ng) break;
-    load_a(areg[1], gi(g + 3));
-    mma(braw[1], 1);
-    load_bg(braw[1], gi(g + 3));
-    store_a(areg[0], 0);
-    __syncthreads();
+  // prologue: steps 0 .. NS-2 in flight
+  for_stages<0, NS - 1>([&](auto S_) __attribute__((always_inline)) {
+    issue(S_, decltype(S_)::value);
+    __builtin_amdgcn_sched_barrier(0);  // keep each step's loads together, in step order
+    return true;
+  });
+  // step k = NS*trip + S uses stage S
+  auto step = [&](auto S_, int k) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    wait_vmcnt<(NS - 2) * C::LOADS>();  // this wave's loads of step k have landed
+    __builtin_amdgcn_s_barrier();       // every wave's have; stage (S-1) is free
+    issue(IC<(S + NS - 1) % NS>{}, k + NS - 1);
+    __builtin_amdgcn_sched_barrier(0);  // the next step's loads go out before this step's MFMAs
+    compute(S_);
+  };
+  // whole trips with no branch inside (one basic block, so no load is moved
+  // away from where it is issued), then the remaining steps
+  const int trips = nst / NS;
+  for (int t = 0; t < trips; ++t) {
+    for_stages<0, NS>([&](auto S_) __attribute__((always_inline)) {
+      step(S_, t * NS + decltype(S_)::value);
+      return true;
+    });
   }
+  const int rem = nst - trips * NS;
+  for_stages<0, NS - 1>([&](auto S_) __attribute__((always_inline)) {
+    constexpr int S = decltype(S_)::value;
+    if (S >= rem) return false;
+    step(S_, trips * NS + S);
+    return true;
+  });
+  wait_vmcnt<0>();  // no load into LDS may land after the workgroup ends
 
   if (!valid[0]) return;
   // ---- epilogue.  32x32 accumulator layout: register r of lane l holds
@@ -339,7 +440,9 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
       const size_t orow = (size_t)(row0 + row) * prm.N;
       if constexpr (MODE == GEMM_FUSED_SWIGLU) {
         const float hv = swiglu(acc[mi][0][r], acc[mi][1][r]);
-        ((uint16_t*)prm.out)[orow + col0 + col_in] = f32_to_f16_bits(hv);
+        const int col = col0 + col_in;
+        const int at = prm.perm8_out ? (col & ~7) + perm8_slot(col & 7) : col;
+        ((uint16_t*)prm.out)[orow + at] = f32_to_f16_bits(hv);
       } else {
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
@@ -353,21 +456,24 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
   }
 }
 
-template <int BITS, int MODE, int ACT>
-static hipError_t launch_act(int bm, const GemmParams& prm, dim3 grid, hipStream_t st) {
-  switch (bm) {
-    case 32: return launch_kernel(gemm_kernel<BITS, MODE, 1, ACT>, grid, 256, 0, st, prm);
-    case 64: return launch_kernel(gemm_kernel<BITS, MODE, 2, ACT>, grid, 256, 0, st, prm);
-    case 128: return launch_kernel(gemm_kernel<BITS, MODE, 4, ACT>, grid, 256, 0, st, prm);
-    default: return hipErrorInvalidValue;
+// 4-bit weights stage two groups per step (64-byte row segments) when K
+// allows; 8-bit and fp16 rows already give 64 / 128 bytes per group
+template <int BITS, int MODE, int MS>
+static hipError_t launch_one(const GemmParams& prm, dim3 grid, hipStream_t st) {
+  if constexpr (BITS == 4) {
+    if ((prm.K / 64) % 2 == 0) return launch_kernel(gemm_kernel<BITS, MODE, MS, 2>, grid, 256, 0, st, prm);
   }
+  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1>, grid, 256, 0, st, prm);
 }
 
-// the down projection reads fp16 SwiGLU rows whatever the activation dtype
 template <int BITS, int MODE>
 static hipError_t launch_ms(int bm, const GemmParams& prm, dim3 grid, hipStream_t st) {
-  if (MODE != GEMM_ROWS_F16 && prm.act == ACT_BF16) return launch_act<BITS, MODE, ACT_BF16>(bm, prm, grid, st);
-  return launch_act<BITS, MODE, ACT_F16>(bm, prm, grid, st);
+  switch (bm) {
+    case 32: return launch_one<BITS, MODE, 1>(prm, grid, st);
+    case 64: return launch_one<BITS, MODE, 2>(prm, grid, st);
+    case 128: return launch_one<BITS, MODE, 4>(prm, grid, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int BITS>
@@ -380,12 +486,11 @@ static hipError_t launch_bits(GemmMode mode, int bm, const GemmParams& prm, dim3
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(GemmMode mode, const void* a, int act, const int32_t* perm, const int32_t* counts,
+hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const int32_t* perm, const int32_t* counts,
                        const int32_t* offsets, int kcap, int E, int K, int N, int bits, WView w0, WView w1,
-                       void* out, int bm, int max_mtiles, hipStream_t st) {
+                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st) {
   GemmParams prm;
-  prm.a = (const uint16_t*)a;
-  prm.act = act;
+  prm.a = a;
   prm.perm = perm;
   prm.counts = counts;
   prm.offsets = offsets;
@@ -396,10 +501,14 @@ hipError_t launch_gemm(GemmMode mode, const void* a, int act, const int32_t* per
   prm.w0 = w0;
   prm.w1 = w1;
   prm.out = out;
+  prm.perm8_out = perm8_out ? 1 : 0;
+  // per-lane buffer offsets are 32-bit: the operand rows and one expert's weight rows
+  if (a_rows * K * 2 > 0xFFFFFFFFll || w0.stride * (int64_t)K * bits / 8 > 0xFFFFFFFFll) return hipErrorInvalidValue;
   const int ncols = mode == GEMM_FUSED_SWIGLU ? 128 : 256;
   prm.n_tiles = (N + ncols - 1) / ncols;
   prm.m_tiles = max_mtiles;
-  prm.group_m = tuning(TUNE_GEMM_GROUP_M);
+  const int gm = tuning(TUNE_GEMM_GROUP_M);
+  prm.group_m = gm >= 1 && gm < max_mtiles ? gm : max_mtiles;
   const int64_t total = (int64_t)prm.n_tiles * prm.m_tiles;
   prm.per_xcd = (int)((total + NUM_XCD - 1) / NUM_XCD);
   dim3 grid((unsigned)(prm.per_xcd * NUM_XCD));

@@ -96,22 +96,28 @@ enum GemmMode { GEMM_FUSED_SWIGLU = 0, GEMM_GATHER_F32 = 1, GEMM_ROWS_F16 = 2 };
 int gemm_block_m(int P, int E);
 // upper bound on M tiles for P pairs over E experts
 int gemm_max_mtiles(int P, int E, int bm);
-// a: GATHER modes read x[perm[row]/kcap], ROWS mode reads a[row]; K = reduction dim
-// FUSED: out = h fp16 [rows, N=I]; GATHER_F32: out fp32 [rows, N]; ROWS_F16: out fp16 [rows, N]
-hipError_t launch_gemm(GemmMode mode, const void* a, int act, const int32_t* perm, const int32_t* counts,
+// a: fp16 rows, 8-element blocks in the weights' unpack order (prep_a / the
+// fused epilogue); GATHER modes read a[perm[row]/kcap], ROWS mode a[row];
+// K = reduction dim.  FUSED: out = h fp16 [rows, N=I] (blocks in 4-bit unpack
+// order if perm8_out); GATHER_F32: out fp32 [rows, N]; ROWS_F16: out fp16
+// a_rows: rows of a (T or P); a and one expert's weight rows must each stay
+// below 4 GB (32-bit buffer offsets), else hipErrorInvalidValue
+hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const int32_t* perm, const int32_t* counts,
                        const int32_t* offsets, int kcap, int E, int K, int N, int bits, WView w0, WView w1,
-                       void* out, int bm, int max_mtiles, hipStream_t st);
+                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st);
 
 // --------------------------------------------------------- small kernels
 // h[i, j] = fp16(swiglu(g[i, j], u[i, j])) for i < rows
-hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, hipStream_t st);
+hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, bool perm8,
+                         hipStream_t st);
+hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, bool perm8, hipStream_t st);
 // y[t] = act(sum_{s<k} w[t,s] * o[pos[t*kcap+s]])
 hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wts, const int32_t* k_used_dev,
                           int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st);
 // out[p, :] = src[r, :] (fp16 rows of width I) with r = pos[p] for pos[p] >= 0,
 // or, when pos is NULL, r = p for the pairs whose slot p % kcap < k_used
 hipError_t launch_gather_rows(const uint16_t* src, const int32_t* pos, int64_t P, int I, uint16_t* out, int kcap,
-                              const int32_t* k_used_dev, int k_static, hipStream_t st);
+                              const int32_t* k_used_dev, int k_static, bool perm8, hipStream_t st);
 // copy n int32/fp32 words
 hipError_t launch_copy_words(const void* src, void* dst, int64_t n, hipStream_t st);
 

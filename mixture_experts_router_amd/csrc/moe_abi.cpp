@@ -138,7 +138,7 @@ bool compatible(const moe_weights* a, const moe_weights* b) {
 // ------------------------------------------------------------ workspace --
 
 struct Layout {
-  size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, g32, u32, total;
+  size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, a16, g32, u32, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t flags) {
@@ -160,6 +160,7 @@ Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t
   L.pos = take((size_t)(P * 4));
   L.h = take((size_t)(P * I * 2));
   L.o = take((size_t)(P * H * 2));
+  L.a16 = take((size_t)(T * H * 2));  // batched path: the activations as the GEMM's fp16 operand
   if (flags & MOE_FLAG_UNFUSED) {
     L.g32 = take((size_t)(P * I * 4));
     L.u32 = take((size_t)(P * I * 4));
@@ -245,6 +246,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   int32_t* pos = (int32_t*)(W + L.pos);
   uint16_t* h = (uint16_t*)(W + L.h);
   uint16_t* o = (uint16_t*)(W + L.o);
+  uint16_t* a16w = (uint16_t*)(W + L.a16);
   float* g32 = (float*)(W + L.g32);
   float* u32 = (float*)(W + L.u32);
   const bool unfused = (flags & MOE_FLAG_UNFUSED) != 0;
@@ -282,7 +284,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       HIP_TRY(moe::launch_gemv_up(x, act, rt, k_static, kcap, T, H, I, bits, false, wu, wu, nullptr, u32,
                                   props.num_cu, st));
       plan_step("gemv_up", st);
-      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, st));
+      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, false, st));
       plan_step("swiglu", st);
     }
     HIP_TRY(moe::launch_gemv_down(h, rt, k_static, kcap, T, H, I, bits, view_of(down, 0), y, act, props.num_cu, st));
@@ -297,23 +299,31 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     plan_step("sort_pairs", st);
     const int bm = moe::gemm_block_m((int)P, E);
     const int mt = moe::gemm_max_mtiles((int)P, E, bm);
+    // the GEMM operand: fp16 activations, 8-element blocks in 4-bit unpack order
+    const bool perm8 = bits == 4;
+    const uint16_t* a16 = (const uint16_t*)x;
+    if (perm8 || dt != MOE_F16) {
+      HIP_TRY(moe::launch_prep_a(x, act, a16w, T, H, perm8, st));
+      plan_step("prep_a", st);
+      a16 = a16w;
+    }
     if (!unfused) {
-      HIP_TRY(moe::launch_gemm(moe::GEMM_FUSED_SWIGLU, x, act, perm, counts, offsets, kcap, E, H, I, bits, wg, wu, h,
-                               bm, mt, st));
+      HIP_TRY(moe::launch_gemm(moe::GEMM_FUSED_SWIGLU, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wg, wu, h,
+                               perm8, bm, mt, st));
       plan_step("gemm_gate_up_swiglu", st);
     } else {
-      HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, x, act, perm, counts, offsets, kcap, E, H, I, bits, wg, wg, g32,
-                               bm, mt, st));
+      HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wg, wg, g32,
+                               false, bm, mt, st));
       plan_step("gemm_gate", st);
-      HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, x, act, perm, counts, offsets, kcap, E, H, I, bits, wu, wu, u32,
-                               bm, mt, st));
+      HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wu, wu, u32,
+                               false, bm, mt, st));
       plan_step("gemm_up", st);
-      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, st));
+      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, perm8, st));
       plan_step("swiglu", st);
     }
     const WView wd = view_of(down, 0);
-    HIP_TRY(moe::launch_gemm(moe::GEMM_ROWS_F16, h, act, perm, counts, offsets, kcap, E, I, H, bits, wd, wd, o, bm, mt,
-                             st));
+    HIP_TRY(moe::launch_gemm(moe::GEMM_ROWS_F16, h, P, perm, counts, offsets, kcap, E, I, H, bits, wd, wd, o, false, bm,
+                             mt, st));
     plan_step("gemm_down", st);
     HIP_TRY(moe::launch_combine(o, pos, wts, k_used, k_static, kcap, T, H, y, act, st));
     plan_step("combine", st);
@@ -329,8 +339,10 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     if (taps->offsets) HIP_TRY(moe::launch_copy_words(offsets, taps->offsets, E + 1, st));
     if (taps->perm) HIP_TRY(moe::launch_copy_words(perm, taps->perm, P, st));
     if (taps->h) {
-      if (gemv) HIP_TRY(moe::launch_gather_rows(h, nullptr, P, I, (uint16_t*)taps->h, kcap, k_used, k_static, st));
-      else HIP_TRY(moe::launch_gather_rows(h, pos, P, I, (uint16_t*)taps->h, kcap, k_used, k_static, st));
+      if (gemv)
+        HIP_TRY(moe::launch_gather_rows(h, nullptr, P, I, (uint16_t*)taps->h, kcap, k_used, k_static, false, st));
+      else
+        HIP_TRY(moe::launch_gather_rows(h, pos, P, I, (uint16_t*)taps->h, kcap, k_used, k_static, bits == 4, st));
     }
   }
   return MOE_OK;
@@ -340,7 +352,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
 
 namespace moe {
 namespace {
-int g_tuning[TUNE_KEYS] = {8, 8, 4, 1};
+int g_tuning[TUNE_KEYS] = {8, 8, 1 << 30, 1};
 }
 int tuning(TuneKey key) { return g_tuning[key]; }
 void set_tuning(int key, int value) {
