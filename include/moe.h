@@ -150,6 +150,8 @@ typedef struct {
  *   k_used    int32 [1] out (may be NULL); entropy fp32 [1] out (may be NULL)
  *   logits_out fp32 [T, E] out (may be NULL)
  *   ws        workspace of at least moe_route_workspace_size(T, E, k) bytes
+ *             (may be NULL when logits_out is given; with MOE_K_ENTROPY the
+ *             per-token entropies then go through a single-workgroup pass)
  * H % 64 == 0, 1 <= E <= 256.  T == 0 is a no-op returning MOE_OK.
  */
 size_t moe_route_workspace_size(int32_t T, int32_t E, int32_t k);

@@ -190,11 +190,9 @@ def route(x: torch.Tensor, router_w: torch.Tensor, k: int, want_logits: bool = F
     ku = torch.zeros(1, dtype=torch.int32, device=dev)
     ent = torch.zeros(1, dtype=torch.float32, device=dev)
     logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
-    ws = None
-    if logits is None:
-        ws = torch.empty(max(route_workspace_size(T, E, k), 256), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(route_workspace_size(T, E, k), 256), dtype=torch.uint8, device=dev)
     st = lib().moe_route(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k, _ptr(idx), _ptr(w), _ptr(ku),
-                         _ptr(ent), _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+                         _ptr(ent), _ptr(logits), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_route")
     out = dict(idx=idx, w=w, k_used=ku, entropy=ent)
     if logits is not None:

@@ -89,32 +89,33 @@ int gemm_max_mtiles(int P, int E, int bm) { return (P + bm - 1) / bm + E; }
 // a wave's 64 weight rows, stored row-major [64 rows][SEG bytes] in LDS: a
 // load instruction reads SEG contiguous bytes of each of RPI rows (DRAM
 // streams rows in segments of at least 64 bytes far better than in 32).
-template <int BITS, int KG>
+template <int BITS, int KG, int NSUB>
 struct BGeo {
   static constexpr int ROW = 64 * BITS / 8;  // code bytes of one row per group: 32 / 64 / 128
   static constexpr int SEG = KG * ROW;       // bytes of one row per stage
   static constexpr int LPR = SEG / 16;       // 16-byte pieces per row
   static constexpr int RPI = 64 / LPR;       // rows per 64-lane load instruction
-  static constexpr int NI = 64 / RPI;        // load instructions per wave
+  static constexpr int ROWS = 32 * NSUB;     // weight rows (output columns) per wave
+  static constexpr int NI = ROWS / RPI;      // load instructions per wave
   static constexpr int HALF = ROW / 2;       // bytes a lane feeds per group (its half of the group's k)
   static constexpr int READS = HALF / 16;    // 16-byte LDS reads per lane, subtile and group
 };
 
-template <int BITS, int MS, int KG>
+template <int BITS, int MS, int KG, int NSUB>
 struct GemmCfg {
   static constexpr int BM = 32 * MS;
   static constexpr int A_SUB = BM * 128;  // A of one group: BM rows x 64 fp16
   static constexpr int A_BYTES = KG * A_SUB;
-  static constexpr int B_BYTES = 4 * 64 * BGeo<BITS, KG>::SEG;
+  static constexpr int B_BYTES = 4 * BGeo<BITS, KG, NSUB>::ROWS * BGeo<BITS, KG, NSUB>::SEG;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   // 128-row tiles: one workgroup per CU (160 KB LDS); smaller: two
   static constexpr int BUDGET = MS == 4 ? 156 * 1024 : 78 * 1024;
   static constexpr int NS_FIT = BUDGET / STAGE;
   static constexpr int NS = NS_FIT < 2 ? 2 : (NS_FIT > 6 ? 6 : NS_FIT);
   // vector memory instructions per wave per stage: A, B, scales and biases
-  static constexpr int LOADS = KG * MS + BGeo<BITS, KG>::NI + (BITS != 16 ? 4 * KG : 0);
+  static constexpr int LOADS = KG * MS + BGeo<BITS, KG, NSUB>::NI + (BITS != 16 ? 2 * NSUB * KG : 0);
   static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
-  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+  static_assert(NS * STAGE <= 159 * 1024, "LDS (160 KB less the tile lookup)");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -187,10 +188,11 @@ __device__ __forceinline__ f16x8 dequant_b(const u32x4* c, int j, uint32_t s_bit
   }
 }
 
-template <int BITS, int MODE, int MS, int KG>
+template <int BITS, int MODE, int MS, int KG, int NSUB>
 __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams prm) {
-  using G = BGeo<BITS, KG>;
-  using C = GemmCfg<BITS, MS, KG>;
+  using G = BGeo<BITS, KG, NSUB>;
+  using C = GemmCfg<BITS, MS, KG, NSUB>;
+  constexpr int HALFSUB = NSUB / 2;  // fused: subtiles [0, HALFSUB) gate, the rest the matching up
   constexpr int BM = C::BM, NS = C::NS;
   // one array per stage: distinct objects let the compiler see that reading
   // a stage does not wait on loads still landing in the others
@@ -280,32 +282,33 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
     a_off[q] = arow * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
   }
 
-  // ---- B: this wave's 64 weight rows; rows [32 ni, 32 ni + 32) are subtile
-  // ni (fused: 32 gate columns, then the matching 32 up columns).  Columns
-  // past N re-read column 0 (never stored).
-  int col0;
-  bool valid[2];
-  const WView* view[2];
-  if constexpr (MODE == GEMM_FUSED_SWIGLU) {
-    col0 = n_tile * 128 + wave * 32;
-    valid[0] = valid[1] = col0 < prm.N;
-    view[0] = &prm.w0;
-    view[1] = &prm.w1;
-  } else {
-    col0 = n_tile * 256 + wave * 64;
-    valid[0] = col0 < prm.N;
-    valid[1] = col0 + 32 < prm.N;
-    view[0] = view[1] = &prm.w0;
+  // ---- B: this wave's 32*NSUB weight rows; rows [32 ni, 32 ni + 32) are
+  // subtile ni (fused: NSUB/2 subtiles of gate columns, then the matching up
+  // columns).  Columns past N re-read column 0 (never stored).
+  int col0;  // first output column of this wave (fused: first gate / h column)
+  bool valid[NSUB];
+  const WView* view[NSUB];
+#pragma unroll
+  for (int ni = 0; ni < NSUB; ++ni) {
+    if constexpr (MODE == GEMM_FUSED_SWIGLU) {
+      col0 = n_tile * (4 * 32 * HALFSUB) + wave * 32 * HALFSUB;
+      valid[ni] = col0 + 32 * (ni % HALFSUB) < prm.N;
+      view[ni] = ni < HALFSUB ? &prm.w0 : &prm.w1;
+    } else {
+      col0 = n_tile * (4 * 32 * NSUB) + wave * 32 * NSUB;
+      valid[ni] = col0 + 32 * ni < prm.N;
+      view[ni] = &prm.w0;
+    }
   }
   auto column = [&](int ni, int rin) __attribute__((always_inline)) {
-    const int c = MODE == GEMM_FUSED_SWIGLU ? col0 + rin : col0 + 32 * ni + rin;
+    const int c = col0 + 32 * (MODE == GEMM_FUSED_SWIGLU ? ni % HALFSUB : ni) + rin;
     return valid[ni] ? c : 0;
   };
   const int64_t row_bytes = (int64_t)K * BITS / 8;
-  rsrc_t rq[2], rs[2], rbias[2];
-  uint32_t s_off[2];
+  rsrc_t rq[NSUB], rs[NSUB], rbias[NSUB];
+  uint32_t s_off[NSUB];
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni) {
+  for (int ni = 0; ni < NSUB; ++ni) {
     const WView& v = *view[ni];
     const int64_t erow = (int64_t)e * v.stride;  // the expert's first row
     rq[ni] = make_rsrc(v.q + erow * row_bytes, 0xFFFFFFFFu);
@@ -323,16 +326,16 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
   }
   const int nst = ng / KG;  // pipeline steps (the launcher makes KG divide ng)
 
-  f32x16 acc[MS][2];
+  f32x16 acc[MS][NSUB];
 #pragma unroll
   for (int mi = 0; mi < MS; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < NSUB; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  uint32_t sreg[NS][KG][2], breg[NS][KG][2];
-  const int b_lane = C::A_BYTES + wave * 64 * G::SEG + col_in * G::SEG + hh * G::HALF;  // this lane's B codes
+  uint32_t sreg[NS][KG][NSUB], breg[NS][KG][NSUB];
+  const int b_lane = C::A_BYTES + wave * G::ROWS * G::SEG + col_in * G::SEG + hh * G::HALF;  // this lane's B codes
   const int last = nst - 1;
   // step k (groups KG k .. KG k + KG - 1; clamped to the last step) into stage S
   auto issue = [&](auto S_, int k) __attribute__((always_inline)) {
@@ -348,14 +351,14 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
       }
 #pragma unroll
     for (int q = 0; q < G::NI; ++q) {
-      const int lds_off = C::A_BYTES + wave * 64 * G::SEG + q * 1024;
+      const int lds_off = C::A_BYTES + wave * G::ROWS * G::SEG + q * 1024;
       dma16(rq[(q * G::RPI) / 32], b_off[q], (uint32_t)k * G::SEG, st + lds_off);
     }
     if constexpr (BITS != 16) {
 #pragma unroll
       for (int gi = 0; gi < KG; ++gi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
+        for (int ni = 0; ni < NSUB; ++ni) {
           sreg[S][gi][ni] = __builtin_amdgcn_raw_buffer_load_b16(rs[ni], (int)s_off[ni], (k * KG + gi) * 2, 0);
           breg[S][gi][ni] = __builtin_amdgcn_raw_buffer_load_b16(rbias[ni], (int)s_off[ni], (k * KG + gi) * 2, 0);
         }
@@ -370,9 +373,9 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
     const uint8_t* st = stage(S_);
 #pragma unroll
     for (int gi = 0; gi < KG; ++gi) {
-      u32x4 bc[2][G::READS];
+      u32x4 bc[NSUB][G::READS];
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < NSUB; ++ni)
 #pragma unroll
         for (int t = 0; t < G::READS; ++t) {
           const int off = b_lane + ni * 32 * G::SEG + gi * G::ROW + t * 16;
@@ -380,15 +383,17 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
         }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f16x8 b0 = dequant_b<BITS>(bc[0], j, sreg[S][gi][0], breg[S][gi][0], qc);
-        const f16x8 b1 = dequant_b<BITS>(bc[1], j, sreg[S][gi][1], breg[S][gi][1], qc);
+        f16x8 bf[NSUB];
+#pragma unroll
+        for (int ni = 0; ni < NSUB; ++ni) bf[ni] = dequant_b<BITS>(bc[ni], j, sreg[S][gi][ni], breg[S][gi][ni], qc);
 #pragma unroll
         for (int mi = 0; mi < MS; ++mi) {
           const int row = mi * 32 + col_in;
           const int off = gi * C::A_SUB + row * 128 + (((4 * hh + j) ^ ((row >> 1) & 7)) << 4);
           const f16x8 af = *(const f16x8*)(st + off);
-          acc[mi][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b0, acc[mi][0], 0, 0, 0);
-          acc[mi][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b1, acc[mi][1], 0, 0, 0);
+#pragma unroll
+          for (int ni = 0; ni < NSUB; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[ni], acc[mi][ni], 0, 0, 0);
         }
       }
     }
@@ -427,7 +432,6 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
   });
   wait_vmcnt<0>();  // no load into LDS may land after the workgroup ends
 
-  if (!valid[0]) return;
   // ---- epilogue.  32x32 accumulator layout: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
@@ -439,13 +443,17 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
       if (row >= rows) continue;
       const size_t orow = (size_t)(row0 + row) * prm.N;
       if constexpr (MODE == GEMM_FUSED_SWIGLU) {
-        const float hv = swiglu(acc[mi][0][r], acc[mi][1][r]);
-        const int col = col0 + col_in;
-        const int at = prm.perm8_out ? (col & ~7) + perm8_slot(col & 7) : col;
-        ((uint16_t*)prm.out)[orow + at] = f32_to_f16_bits(hv);
+#pragma unroll
+        for (int ni = 0; ni < HALFSUB; ++ni) {
+          if (!valid[ni]) continue;
+          const float hv = swiglu(acc[mi][ni][r], acc[mi][ni + HALFSUB][r]);
+          const int col = col0 + 32 * ni + col_in;
+          const int at = prm.perm8_out ? (col & ~7) + perm8_slot(col & 7) : col;
+          ((uint16_t*)prm.out)[orow + at] = f32_to_f16_bits(hv);
+        }
       } else {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
+        for (int ni = 0; ni < NSUB; ++ni) {
           if (!valid[ni]) continue;
           const int col = col0 + 32 * ni + col_in;
           if constexpr (MODE == GEMM_GATHER_F32) ((float*)prm.out)[orow + col] = acc[mi][ni][r];
@@ -456,32 +464,50 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
   }
 }
 
-// 4-bit weights stage two groups per step (64-byte row segments) when K
-// allows; 8-bit and fp16 rows already give 64 / 128 bytes per group
-template <int BITS, int MODE, int MS>
-static hipError_t launch_one(const GemmParams& prm, dim3 grid, hipStream_t st) {
+// One instantiation: each wave owns NSUB subtiles of 32 columns.  4-bit
+// weights stage two groups per step (64-byte row segments) when K allows,
+// unless the tuning knob asks for one.
+template <int BITS, int MODE, int MS, int NSUB>
+static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
+  const int ncols = 4 * 32 * (MODE == GEMM_FUSED_SWIGLU ? NSUB / 2 : NSUB);
+  prm.n_tiles = (prm.N + ncols - 1) / ncols;
+  const int gm = tuning(TUNE_GEMM_GROUP_M);
+  prm.group_m = gm >= 1 && gm < prm.m_tiles ? gm : prm.m_tiles;
+  const int64_t total = (int64_t)prm.n_tiles * prm.m_tiles;
+  prm.per_xcd = (int)((total + NUM_XCD - 1) / NUM_XCD);
+  dim3 grid((unsigned)(prm.per_xcd * NUM_XCD));
   if constexpr (BITS == 4) {
-    if ((prm.K / 64) % 2 == 0) return launch_kernel(gemm_kernel<BITS, MODE, MS, 2>, grid, 256, 0, st, prm);
+    if ((prm.K / 64) % 2 == 0 && tuning(TUNE_GEMM_KG) != 1)
+      return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB>, grid, 256, 0, st, prm);
   }
-  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1>, grid, 256, 0, st, prm);
+  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB>, grid, 256, 0, st, prm);
+}
+
+template <int BITS, int MODE, int MS>
+static hipError_t launch_one(const GemmParams& prm, hipStream_t st) {
+  // fp16 rows: two stages of four subtiles would not fit in LDS
+  if constexpr (MS == 4 && BITS != 16) {
+    if (tuning(TUNE_GEMM_NSUB) == 4) return launch_sub<BITS, MODE, MS, 4>(prm, st);
+  }
+  return launch_sub<BITS, MODE, MS, 2>(prm, st);
 }
 
 template <int BITS, int MODE>
-static hipError_t launch_ms(int bm, const GemmParams& prm, dim3 grid, hipStream_t st) {
+static hipError_t launch_ms(int bm, const GemmParams& prm, hipStream_t st) {
   switch (bm) {
-    case 32: return launch_one<BITS, MODE, 1>(prm, grid, st);
-    case 64: return launch_one<BITS, MODE, 2>(prm, grid, st);
-    case 128: return launch_one<BITS, MODE, 4>(prm, grid, st);
+    case 32: return launch_one<BITS, MODE, 1>(prm, st);
+    case 64: return launch_one<BITS, MODE, 2>(prm, st);
+    case 128: return launch_one<BITS, MODE, 4>(prm, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int BITS>
-static hipError_t launch_bits(GemmMode mode, int bm, const GemmParams& prm, dim3 grid, hipStream_t st) {
+static hipError_t launch_bits(GemmMode mode, int bm, const GemmParams& prm, hipStream_t st) {
   switch (mode) {
-    case GEMM_FUSED_SWIGLU: return launch_ms<BITS, GEMM_FUSED_SWIGLU>(bm, prm, grid, st);
-    case GEMM_GATHER_F32: return launch_ms<BITS, GEMM_GATHER_F32>(bm, prm, grid, st);
-    case GEMM_ROWS_F16: return launch_ms<BITS, GEMM_ROWS_F16>(bm, prm, grid, st);
+    case GEMM_FUSED_SWIGLU: return launch_ms<BITS, GEMM_FUSED_SWIGLU>(bm, prm, st);
+    case GEMM_GATHER_F32: return launch_ms<BITS, GEMM_GATHER_F32>(bm, prm, st);
+    case GEMM_ROWS_F16: return launch_ms<BITS, GEMM_ROWS_F16>(bm, prm, st);
   }
   return hipErrorInvalidValue;
 }
@@ -504,17 +530,10 @@ hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const i
   prm.perm8_out = perm8_out ? 1 : 0;
   // per-lane buffer offsets are 32-bit: the operand rows and one expert's weight rows
   if (a_rows * K * 2 > 0xFFFFFFFFll || w0.stride * (int64_t)K * bits / 8 > 0xFFFFFFFFll) return hipErrorInvalidValue;
-  const int ncols = mode == GEMM_FUSED_SWIGLU ? 128 : 256;
-  prm.n_tiles = (N + ncols - 1) / ncols;
   prm.m_tiles = max_mtiles;
-  const int gm = tuning(TUNE_GEMM_GROUP_M);
-  prm.group_m = gm >= 1 && gm < max_mtiles ? gm : max_mtiles;
-  const int64_t total = (int64_t)prm.n_tiles * prm.m_tiles;
-  prm.per_xcd = (int)((total + NUM_XCD - 1) / NUM_XCD);
-  dim3 grid((unsigned)(prm.per_xcd * NUM_XCD));
-  if (bits == 4) return launch_bits<4>(mode, bm, prm, grid, st);
-  if (bits == 8) return launch_bits<8>(mode, bm, prm, grid, st);
-  return launch_bits<16>(mode, bm, prm, grid, st);
+  if (bits == 4) return launch_bits<4>(mode, bm, prm, st);
+  if (bits == 8) return launch_bits<8>(mode, bm, prm, st);
+  return launch_bits<16>(mode, bm, prm, st);
 }
 
 }  // namespace moe

@@ -36,7 +36,9 @@ enum TuneKey {
   TUNE_DOWN_WAVES_PER_CU = 1,
   TUNE_GEMM_GROUP_M = 2,
   TUNE_GEMM_BM = 3,  // 32, 64 or 128 forces the GEMM row tile; anything else: chosen from the batch
-  TUNE_KEYS = 4
+  TUNE_GEMM_KG = 4,  // 1: 4-bit GEMM stages one quantisation group per step (default: two when K allows)
+  TUNE_GEMM_NSUB = 5,  // 4: 128-row GEMM tiles give each wave 128 columns (default 64)
+  TUNE_KEYS = 6
 };
 int tuning(TuneKey key);
 
@@ -52,8 +54,10 @@ struct WView {
 hipError_t launch_router_logits(const void* x, const void* wr, float* logits, int T, int H, int E, int act,
                                 hipStream_t st);
 // k > 0: static; k < 0: entropy-adaptive (kcap = 3)
+// k > 0: static top-k; k <= 0: entropy-adaptive (scratch: T floats, or NULL
+// for the single-workgroup pass)
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* k_used,
-                       float* entropy, hipStream_t st);
+                       float* entropy, float* scratch, hipStream_t st);
 
 // ------------------------------------------------------------------ sort
 // k_used_dev may be NULL (then k_static is used)

@@ -138,7 +138,7 @@ bool compatible(const moe_weights* a, const moe_weights* b) {
 // ------------------------------------------------------------ workspace --
 
 struct Layout {
-  size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, a16, g32, u32, total;
+  size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, a16, hent, g32, u32, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t flags) {
@@ -161,6 +161,7 @@ Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t
   L.h = take((size_t)(P * I * 2));
   L.o = take((size_t)(P * H * 2));
   L.a16 = take((size_t)(T * H * 2));  // batched path: the activations as the GEMM's fp16 operand
+  L.hent = take((size_t)(T * 4));     // adaptive k: per-token entropies
   if (flags & MOE_FLAG_UNFUSED) {
     L.g32 = take((size_t)(P * I * 4));
     L.u32 = take((size_t)(P * I * 4));
@@ -185,13 +186,21 @@ WView view_of(const moe_weights* w, int64_t row_offset) {
     if ((expr) != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
 
-moe_status route_impl(const void* x, moe_dtype dt, int T, int H, const void* wr, int E, int k, int32_t* idx,
-                      float* w, int32_t* k_used, float* entropy, float* logits, hipStream_t st) {
-  HIP_TRY(moe::launch_router_logits(x, wr, logits, T, H, E, (int)dt, st));
-  plan_step("router_logits", st);
-  HIP_TRY(moe::launch_topk(logits, T, E, k, idx, w, k_used, entropy, st));
+// the selection launches: static top-k, or the adaptive pass (two launches
+// with scratch for the per-token entropies, one without)
+moe_status select_impl(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* k_used,
+                       float* entropy, float* scratch, hipStream_t st) {
+  HIP_TRY(moe::launch_topk(logits, T, E, k, idx, w, k_used, entropy, scratch, st));
+  if (k <= 0 && scratch) plan_step("entropy_tokens", st);
   plan_step(k > 0 ? "topk" : "topk_entropy", st);
   return MOE_OK;
+}
+
+moe_status route_impl(const void* x, moe_dtype dt, int T, int H, const void* wr, int E, int k, int32_t* idx,
+                      float* w, int32_t* k_used, float* entropy, float* logits, float* scratch, hipStream_t st) {
+  HIP_TRY(moe::launch_router_logits(x, wr, logits, T, H, E, (int)dt, st));
+  plan_step("router_logits", st);
+  return select_impl(logits, T, E, k, idx, w, k_used, entropy, scratch, st);
 }
 
 moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* router_w, int E, int k,
@@ -269,8 +278,8 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     plan_step("router_logits", st);
     moe::GemvRoute rt{logits, E, idx, wts, k_used, entropy};
     if (k <= 0) {
-      HIP_TRY(moe::launch_topk(logits, T, E, k, idx, wts, k_used, entropy, st));
-      plan_step("topk_entropy", st);
+      moe_status s2 = select_impl(logits, T, E, k, idx, wts, k_used, entropy, (float*)(W + L.hent), st);
+      if (s2 != MOE_OK) return s2;
       rt.logits = nullptr;
     }
     if (!unfused) {
@@ -294,7 +303,9 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       plan_step("sort_pairs", st);
     }
   } else {
-    if ((s = route_impl(x, dt, T, H, router_w, E, k, idx, wts, k_used, entropy, logits, st)) != MOE_OK) return s;
+    if ((s = route_impl(x, dt, T, H, router_w, E, k, idx, wts, k_used, entropy, logits, (float*)(W + L.hent), st)) !=
+        MOE_OK)
+      return s;
     HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st));
     plan_step("sort_pairs", st);
     const int bm = moe::gemm_block_m((int)P, E);
@@ -352,7 +363,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
 
 namespace moe {
 namespace {
-int g_tuning[TUNE_KEYS] = {8, 8, 1 << 30, 1};
+int g_tuning[TUNE_KEYS] = {8, 8, 1 << 30, 1, 2, 2};
 }
 int tuning(TuneKey key) { return g_tuning[key]; }
 void set_tuning(int key, int value) {
@@ -382,8 +393,8 @@ const char* moe_status_string(moe_status s) {
 
 size_t moe_route_workspace_size(int32_t T, int32_t E, int32_t k) {
   if (T < 0 || E < 1) return 0;
-  (void)k;
-  return align_up((size_t)T * (size_t)E * 4);
+  // logits, then (adaptive k) the per-token entropies
+  return align_up((size_t)T * (size_t)E * 4) + (k == MOE_K_ENTROPY ? align_up((size_t)T * 4) : 0);
 }
 
 moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E, int32_t k,
@@ -395,17 +406,19 @@ moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const vo
     if (T == 0) return MOE_OK;
     if (!topk_idx || !topk_w) return MOE_ERR_NULL;
     float* logits = logits_out;
-    if (!logits) {
+    float* scratch = nullptr;
+    if (!logits || ws) {
       if (!ws) return MOE_ERR_WORKSPACE;
       if (ws_bytes < moe_route_workspace_size(T, E, k)) return MOE_ERR_WORKSPACE;
       if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return MOE_ERR_ALIGN;
-      logits = (float*)ws;
+      if (!logits) logits = (float*)ws;
+      if (k == MOE_K_ENTROPY) scratch = (float*)((char*)ws + align_up((size_t)T * (size_t)E * 4));
     }
     DevProps props;
     if ((s = device_props(&props)) != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     plan_begin(st);
-    return route_impl(x, dt, T, H, router_w, E, k, topk_idx, topk_w, k_used, entropy, logits, st);
+    return route_impl(x, dt, T, H, router_w, E, k, topk_idx, topk_w, k_used, entropy, logits, scratch, st);
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -430,7 +443,8 @@ moe_status moe_topk_from_logits(const float* logits, int32_t T, int32_t E, int32
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     plan_begin(st);
-    if (moe::launch_topk(logits, T, E, k, topk_idx, topk_w, k_used, entropy, st) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_topk(logits, T, E, k, topk_idx, topk_w, k_used, entropy, nullptr, st) != hipSuccess)
+      return MOE_ERR_HIP;
     plan_step(k > 0 ? "topk" : "topk_entropy", st);
     return MOE_OK;
   } catch (...) {

@@ -59,51 +59,53 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t
 
 // ---------------------------------------------------------- large batches --
 //
-// A wave computes a 4-token x 4-expert tile; lane l owns the 8-element column
-// slices h = 8*l + 512*i.
-__global__ __launch_bounds__(256) void router_logits_tile_kernel(const uint16_t* __restrict__ x,
-                                                                 const uint16_t* __restrict__ wr,
-                                                                 float* __restrict__ logits, int T, int H, int E,
-                                                                 int act) {
-  constexpr int TT = 4;
-  const int lane = lane_id();
-  const int wave = wave_id();
-  const int t0 = blockIdx.x * TT;
-  const int e0 = blockIdx.y * 16 + wave * 4;
-  if (e0 >= E) return;
-  float acc[TT][4];
-#pragma unroll
-  for (int a = 0; a < TT; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+// One workgroup per 32-token x 32-expert tile on the matrix cores: the four
+// waves take consecutive quarters of H (split K), each accumulating a 32x32
+// fp32 tile with v_mfma_f32_32x32x16_{f16,bf16} fed straight from memory
+// (lane l supplies row l%32 and 8 consecutive k), and the partial tiles are
+// added in wave order through LDS.  Products of two fp16 (bf16) values are
+// exact in fp32; only the summation order differs from a sequential sum.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-  for (int h = lane * 8; h < H; h += 512) {
-    float xv[TT][8], wv[4][8];
+template <int ACT>
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wr,
+                                                                 float* __restrict__ logits, int T, int H, int E) {
+  __shared__ float part[3][16][WAVE];
+  const int lane = lane_id(), wave = wave_id();
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int r32 = lane % 32, half = lane / 32;
+  const int t = min(t0 + r32, T - 1), e = min(e0 + r32, E - 1);  // past the end: re-read (not stored)
+  const int q = H / 4;
+  const uint16_t* xa = x + (size_t)t * H + wave * q + half * 8;
+  const uint16_t* wb = wr + (size_t)e * H + wave * q + half * 8;
+  f32x16 acc;
 #pragma unroll
-    for (int a = 0; a < TT; ++a) {
-      const int t = min(t0 + a, T - 1);
-      unpack8(load16(x + (size_t)t * H + h), act, xv[a]);
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int e = min(e0 + b, E - 1);
-      unpack8(load16(wr + (size_t)e * H + h), act, wv[b]);
-    }
-#pragma unroll
-    for (int a = 0; a < TT; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[a][b] = fmaf(xv[a][i], wv[b][i], acc[a][b]);
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll 8
+  for (int k = 0; k < q; k += 16) {
+    const u32x4 a = load16(xa + k), b = load16(wb + k);
+    if constexpr (ACT == ACT_BF16)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                    0, 0, 0);
+    else
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0,
+                                                   0, 0);
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int a = 0; a < TT; ++a)
+    for (int i = 0; i < 16; ++i) part[wave - 1][i][lane] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // register i of lane l: token row 8*(i/4) + 4*(l/32) + i%4, expert column l%32
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float s = wave_sum(acc[a][b]);
-      const int t = t0 + a, e = e0 + b;
-      if (lane == 0 && t < T && e < E) logits[(size_t)t * E + e] = s;
+    for (int i = 0; i < 16; ++i) {
+      const float v = ((acc[i] + part[0][i][lane]) + part[1][i][lane]) + part[2][i][lane];
+      const int tt = t0 + 8 * (i / 4) + 4 * half + (i % 4), ee = e0 + r32;
+      if (tt < T && ee < E) logits[(size_t)tt * E + ee] = v;
     }
+  }
 }
 
 // ------------------------------------------------------------- selection --
@@ -197,24 +199,84 @@ __global__ __launch_bounds__(1024) void topk_entropy_kernel(const float* __restr
   }
 }
 
+// Parallel form of the adaptive selection, in two launches.  First one wave
+// per token writes the token's entropy to scratch.  Then every workgroup sums
+// the T entropies in the same fixed order (lane l takes tokens l, l+64, ...
+// in order; the lanes are combined by the DPP butterfly), so all of them
+// reach the same batch entropy and k, and selects its own tokens.
+__global__ __launch_bounds__(256) void entropy_tokens_kernel(const float* __restrict__ logits, int T, int E,
+                                                             float* __restrict__ hent) {
+  const int t = blockIdx.x * 4 + wave_id();
+  if (t >= T) return;
+  const float h = wave_entropy(logits + (size_t)t * E, E);
+  if (lane_id() == 0) hent[t] = h;
+}
+
+__global__ __launch_bounds__(256) void entropy_select_kernel(const float* __restrict__ logits, int T, int E,
+                                                             const float* __restrict__ hent,
+                                                             int32_t* __restrict__ idx, float* __restrict__ w,
+                                                             int32_t* __restrict__ k_used,
+                                                             float* __restrict__ entropy) {
+  __shared__ int k_sh;
+  const int wave = wave_id(), lane = lane_id();
+  if (wave == 0) {
+    float s = 0.0f;
+    for (int i = lane; i < T; i += WAVE) s += hent[i];
+    const float h = wave_sum(s) / (float)T;
+    const int k = h < 1.2f ? 1 : (h < 2.5f ? 2 : 3);
+    if (lane == 0) {
+      k_sh = k;
+      if (blockIdx.x == 0) {
+        if (k_used) *k_used = k;
+        if (entropy) *entropy = h;
+      }
+    }
+  }
+  __syncthreads();
+  const int k = k_sh;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  constexpr int KC = MOE_K_ENTROPY_CAP_DEV;
+  int si[MOE_MAX_K_DEV];
+  float sw[MOE_MAX_K_DEV];
+  route_token(logits + (size_t)t * E, E, k, si, sw);
+  if (lane == 0) {
+#pragma unroll
+    for (int s = 0; s < KC; ++s) {
+      idx[(size_t)t * KC + s] = si[s];
+      w[(size_t)t * KC + s] = sw[s];
+    }
+  }
+}
+
 // ------------------------------------------------------------- launchers --
 
-int router_small_max_tokens() { return 16; }
+int router_small_max_tokens() { return 128; }
 
 hipError_t launch_router_logits(const void* x, const void* wr, float* logits, int T, int H, int E, int act,
                                 hipStream_t st) {
-  if (T <= router_small_max_tokens()) {
-    launch_kernel(router_logits_small_kernel, dim3(E, T), 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr, logits, H, E,
-                                                            act);
-  } else {
-    dim3 grid((T + 3) / 4, (E + 15) / 16);
-    launch_kernel(router_logits_tile_kernel, grid, 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr, logits, T, H, E, act);
+  if (T > router_small_max_tokens()) {
+    dim3 grid((T + 31) / 32, (E + 31) / 32);
+    if (act == ACT_BF16)
+      return launch_kernel(router_logits_mfma_kernel<ACT_BF16>, grid, 256, 0, st, (const uint16_t*)x,
+                           (const uint16_t*)wr, logits, T, H, E);
+    return launch_kernel(router_logits_mfma_kernel<ACT_F16>, grid, 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr,
+                         logits, T, H, E);
   }
+  launch_kernel(router_logits_small_kernel, dim3(E, T), 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr, logits, H,
+                E, act);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* k_used,
-                       float* entropy, hipStream_t st) {
+                       float* entropy, float* scratch, hipStream_t st) {
+  if (k <= 0 && scratch) {
+    const unsigned g = (unsigned)((T + 3) / 4);
+    hipError_t e = launch_kernel(entropy_tokens_kernel, g, 256, 0, st, logits, T, E, scratch);
+    if (e != hipSuccess) return e;
+    return launch_kernel(entropy_select_kernel, g, 256, 0, st, logits, T, E, (const float*)scratch, idx, w, k_used,
+                         entropy);
+  }
   if (k > 0) {
     launch_kernel(topk_static_kernel, (T + 3) / 4, 256, 0, st, logits, T, E, k, idx, w, k_used, entropy);
   } else {

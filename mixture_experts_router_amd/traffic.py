@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # kernel symbol -> the plan name the library reports for that launch
 KERNEL_PLAN = [
-    (re.compile(r"router_logits_(small|tile)_kernel"), "router_logits"),
+    (re.compile(r"router_logits_(small|mfma)_kernel"), "router_logits"),
     (re.compile(r"gemv_up_kernel<\d+, \d+, true>"), "gemv_gate_up_swiglu"),
     (re.compile(r"gemv_down_kernel"), "gemv_down_combine"),
     (re.compile(r"gemm_kernel<\d+, 0, \d+, \d+>"), "gemm_gate_up_swiglu"),

@@ -137,7 +137,8 @@ def test_fuse_gate_up_matches_oracle_concatenation(built):
 # ------------------------------------------------------------------ router --
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("T,E,k", [(1, 64, 4), (7, 8, 2), (300, 64, 4), (64, 256, 8), (33, 32, -1)])
+@pytest.mark.parametrize("T,E,k", [(1, 64, 4), (7, 8, 2), (300, 64, 4), (64, 256, 8), (33, 32, -1),
+                                   (300, 32, -1), (200, 8, 2), (129, 256, 8)])
 def test_router_exact_inputs_with_planted_ties(dtype, T, E, k):
     H = 1024
     x, wr = mi.exact_router_inputs(7, T, H, E, dtype)
