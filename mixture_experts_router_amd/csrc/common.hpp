@@ -157,10 +157,13 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // -------------------------------------------------------------- SwiGLU ---
 
 // The one SwiGLU used by every path (fused epilogues and the standalone
-// kernel), so fused and unfused results are bit-identical.
+// kernel), so fused and unfused results are bit-identical.  silu(g) =
+// g / (1 + e^-g) with the hardware exponential and reciprocal (v_exp_f32,
+// v_rcp_f32; about 1 ulp each), far inside the fp16 rounding of h.  For
+// very negative g, e^-g overflows to inf and the reciprocal gives 0.
 __device__ __forceinline__ float swiglu(float g, float u) {
-  float e = expf(-g);
-  float s = g / (1.0f + e);
+  const float e = __expf(-g);
+  const float s = g * __builtin_amdgcn_rcpf(1.0f + e);
   return s * u;
 }
 

@@ -21,7 +21,7 @@
 //
 // Both operands stream HBM -> LDS with global_load_lds_dwordx4 (no register
 // staging) through NS stages sized to the LDS: A rows with a 16-byte-chunk XOR
-// swizzle (chunk ^ (row/2 % 8)) so the MFMA operand reads are conflict free;
+// swizzle (see piece_swizzle) so the MFMA operand reads are conflict free;
 // each wave's 64 weight rows into its own LDS region.  Scales and biases ride
 // a register ring of the same depth.  One wait (this wave's loads of the
 // stage) and one barrier (every wave's loads; the oldest stage free) per
@@ -76,7 +76,7 @@ __device__ __forceinline__ bool tile_of(const GemmParams& prm, int bid, int& n, 
 
 int gemm_block_m(int P, int E) {
   const int forced = tuning(TUNE_GEMM_BM);
-  if (forced == 32 || forced == 64 || forced == 128) return forced;
+  if (forced == 32 || forced == 64 || forced == 128 || forced == 256) return forced;
   const int avg = E > 0 ? P / E : P;
   if (avg <= 32) return 32;
   if (avg <= 96) return 64;
@@ -101,24 +101,41 @@ struct BGeo {
   static constexpr int READS = HALF / 16;    // 16-byte LDS reads per lane, subtile and group
 };
 
-template <int BITS, int MS, int KG, int NSUB>
+template <int BITS, int MS, int KG, int NSUB, int WM>
 struct GemmCfg {
-  static constexpr int BM = 32 * MS;
+  static constexpr int BM = 32 * MS * WM;  // WM waves along M, each 32*MS rows
   static constexpr int A_SUB = BM * 128;  // A of one group: BM rows x 64 fp16
   static constexpr int A_BYTES = KG * A_SUB;
   static constexpr int B_BYTES = 4 * BGeo<BITS, KG, NSUB>::ROWS * BGeo<BITS, KG, NSUB>::SEG;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   // 128-row tiles: one workgroup per CU (160 KB LDS); smaller: two
-  static constexpr int BUDGET = MS == 4 ? 156 * 1024 : 78 * 1024;
+  static constexpr int BUDGET = MS == 4 || WM == 2 ? 156 * 1024 : 78 * 1024;
   static constexpr int NS_FIT = BUDGET / STAGE;
   static constexpr int NS = NS_FIT < 2 ? 2 : (NS_FIT > 6 ? 6 : NS_FIT);
   // vector memory instructions per wave per stage: A, B, scales and biases
-  static constexpr int LOADS = KG * MS + BGeo<BITS, KG, NSUB>::NI + (BITS != 16 ? 2 * NSUB * KG : 0);
+  // (the WM waves of a column block share its weight loads)
+  static constexpr int LOADS = KG * MS + BGeo<BITS, KG, NSUB>::NI / WM + (BITS != 16 ? 2 * NSUB * KG : 0);
   static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
   static_assert(NS * STAGE <= 159 * 1024, "LDS (160 KB less the tile lookup)");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS layout swizzles.  A 16-byte read by a wave is served in phases over
+// bank rows of LDS_BANK_ROW bytes; rows of a tile that start in the same
+// bank row would collide on the same banks.  Each tile row's 16-byte pieces
+// are XOR-permuted by the row's index in units of the rows that share a bank
+// row, so the lanes of a phase (consecutive rows, same logical piece) hit
+// distinct banks.
+#ifndef MOE_LDS_BANK_ROW
+#define MOE_LDS_BANK_ROW 256
+#endif
+template <int ROW_BYTES>
+__device__ __forceinline__ int piece_swizzle(int row) {
+  constexpr int PIECES = ROW_BYTES / 16;
+  constexpr int SHARE = MOE_LDS_BANK_ROW / ROW_BYTES > 1 ? MOE_LDS_BANK_ROW / ROW_BYTES : 1;
+  return (row / SHARE) % PIECES;
+}
 
 // 16 bytes per lane from buffer r at voff + soff into LDS (lane i at dst + 16 i)
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_dst) {
@@ -188,10 +205,11 @@ __device__ __forceinline__ f16x8 dequant_b(const u32x4* c, int j, uint32_t s_bit
   }
 }
 
-template <int BITS, int MODE, int MS, int KG, int NSUB>
-__global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams prm) {
+template <int BITS, int MODE, int MS, int KG, int NSUB, int WM>
+__global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2)) void gemm_kernel(GemmParams prm) {
   using G = BGeo<BITS, KG, NSUB>;
-  using C = GemmCfg<BITS, MS, KG, NSUB>;
+  using C = GemmCfg<BITS, MS, KG, NSUB, WM>;
+  static_assert(G::NI % WM == 0, "weight loads split over the M waves");
   constexpr int HALFSUB = NSUB / 2;  // fused: subtiles [0, HALFSUB) gate, the rest the matching up
   constexpr int BM = C::BM, NS = C::NS;
   // one array per stage: distinct objects let the compiler see that reading
@@ -210,7 +228,9 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
   };
 
   const int lane = lane_id();
-  const int wave = wave_id();
+  const int wave = wave_id();     // 0 .. 4*WM-1
+  const int wn = wave % 4;        // column block of this wave
+  const int wm = WM == 1 ? 0 : wave / 4;  // row block of this wave
   const int tid = threadIdx.x;
 
   // ---- which (expert, M tile) this workgroup owns: tiles are numbered
@@ -267,7 +287,7 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
   //
   // ---- A: load instruction q of this wave covers tile rows r0 = 8*(wave*MS+q)
   // .. r0+7; lane i writes LDS chunk i%8 of row r0 + i/8, which holds the
-  // row's logical 16-byte chunk (i%8) ^ (row/2 % 8).  Rows past the tile
+  // row's logical 16-byte chunk (i%8) ^ piece_swizzle(row).  Rows past the tile
   // re-read the tile's first row (never stored).
   const rsrc_t ra = make_rsrc(prm.a, 0xFFFFFFFFu);
   uint32_t a_off[MS];
@@ -278,7 +298,7 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
     uint32_t arow;
     if constexpr (MODE == GEMM_ROWS_F16) arow = (uint32_t)(row0 + rr);
     else arow = (uint32_t)(prm.perm[row0 + rr] / prm.kcap);
-    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    const int chunk = (lane & 7) ^ piece_swizzle<128>(r);
     a_off[q] = arow * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
   }
 
@@ -291,11 +311,11 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
 #pragma unroll
   for (int ni = 0; ni < NSUB; ++ni) {
     if constexpr (MODE == GEMM_FUSED_SWIGLU) {
-      col0 = n_tile * (4 * 32 * HALFSUB) + wave * 32 * HALFSUB;
+      col0 = n_tile * (4 * 32 * HALFSUB) + wn * 32 * HALFSUB;
       valid[ni] = col0 + 32 * (ni % HALFSUB) < prm.N;
       view[ni] = ni < HALFSUB ? &prm.w0 : &prm.w1;
     } else {
-      col0 = n_tile * (4 * 32 * NSUB) + wave * 32 * NSUB;
+      col0 = n_tile * (4 * 32 * NSUB) + wn * 32 * NSUB;
       valid[ni] = col0 + 32 * ni < prm.N;
       view[ni] = &prm.w0;
     }
@@ -305,24 +325,38 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
     return valid[ni] ? c : 0;
   };
   const int64_t row_bytes = (int64_t)K * BITS / 8;
-  rsrc_t rq[NSUB], rs[NSUB], rbias[NSUB];
+  const uint8_t* qbase[NSUB];
+  rsrc_t rs[NSUB], rbias[NSUB];
   uint32_t s_off[NSUB];
 #pragma unroll
   for (int ni = 0; ni < NSUB; ++ni) {
     const WView& v = *view[ni];
     const int64_t erow = (int64_t)e * v.stride;  // the expert's first row
-    rq[ni] = make_rsrc(v.q + erow * row_bytes, 0xFFFFFFFFu);
+    qbase[ni] = v.q + erow * row_bytes;
     if constexpr (BITS != 16) {
       rs[ni] = make_rsrc(v.s + erow * ng, 0xFFFFFFFFu);
       rbias[ni] = make_rsrc(v.b + erow * ng, 0xFFFFFFFFu);
     }
     s_off[ni] = (uint32_t)column(ni, col_in) * (uint32_t)ng * 2u;
   }
-  uint32_t b_off[G::NI];
+  // this wave's weight load instructions: q = q0 + qq, qq < NI / WM (the
+  // row waves of a column block split its loads); q0 and the subtile of an
+  // instruction are wave-uniform, so the descriptors stay in scalar registers
+  constexpr int NQ = G::NI / WM;
+  const int q0 = WM == 1 ? 0 : wm * NQ;
+  rsrc_t rq[NQ];
+  uint32_t b_off[NQ];
 #pragma unroll
-  for (int q = 0; q < G::NI; ++q) {
-    const int rl = q * G::RPI + lane / G::LPR;  // subtile (q * RPI) / 32 for the whole instruction
-    b_off[q] = (uint32_t)(column(rl / 32, rl % 32) * row_bytes) + (uint32_t)(lane % G::LPR) * 16u;
+  for (int qq = 0; qq < NQ; ++qq) {
+    const int q = q0 + qq;
+    const int sub = (q * G::RPI) / 32;  // subtile of the whole instruction
+    const uint8_t* base = qbase[0];
+#pragma unroll
+    for (int ni = 1; ni < NSUB; ++ni) base = sub == ni ? qbase[ni] : base;
+    rq[qq] = make_rsrc(base, 0xFFFFFFFFu);
+    const int rl = q * G::RPI + lane / G::LPR;
+    const int piece = (lane % G::LPR) ^ piece_swizzle<G::SEG>(rl);
+    b_off[qq] = (uint32_t)(column(rl / 32, rl % 32) * row_bytes) + (uint32_t)piece * 16u;
   }
   const int nst = ng / KG;  // pipeline steps (the launcher makes KG divide ng)
 
@@ -335,7 +369,7 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
   uint32_t sreg[NS][KG][NSUB], breg[NS][KG][NSUB];
-  const int b_lane = C::A_BYTES + wave * G::ROWS * G::SEG + col_in * G::SEG + hh * G::HALF;  // this lane's B codes
+  const int b_wave = C::A_BYTES + wn * G::ROWS * G::SEG;  // this wave's B codes
   const int last = nst - 1;
   // step k (groups KG k .. KG k + KG - 1; clamped to the last step) into stage S
   auto issue = [&](auto S_, int k) __attribute__((always_inline)) {
@@ -350,9 +384,9 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
         dma16(ra, a_off[q], (uint32_t)(k * KG + gi) * 128u, st + lds_off);
       }
 #pragma unroll
-    for (int q = 0; q < G::NI; ++q) {
-      const int lds_off = C::A_BYTES + wave * G::ROWS * G::SEG + q * 1024;
-      dma16(rq[(q * G::RPI) / 32], b_off[q], (uint32_t)k * G::SEG, st + lds_off);
+    for (int qq = 0; qq < NQ; ++qq) {
+      const int lds_off = C::A_BYTES + wn * G::ROWS * G::SEG + (q0 + qq) * 1024;
+      dma16(rq[qq], b_off[qq], (uint32_t)k * G::SEG, st + lds_off);
     }
     if constexpr (BITS != 16) {
 #pragma unroll
@@ -378,7 +412,9 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
       for (int ni = 0; ni < NSUB; ++ni)
 #pragma unroll
         for (int t = 0; t < G::READS; ++t) {
-          const int off = b_lane + ni * 32 * G::SEG + gi * G::ROW + t * 16;
+          const int r = ni * 32 + col_in;
+          const int piece = (gi * (G::ROW / 16) + hh * G::READS + t) ^ piece_swizzle<G::SEG>(r);
+          const int off = b_wave + r * G::SEG + piece * 16;
           bc[ni][t] = *(const u32x4*)(st + off);
         }
 #pragma unroll
@@ -388,8 +424,8 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
         for (int ni = 0; ni < NSUB; ++ni) bf[ni] = dequant_b<BITS>(bc[ni], j, sreg[S][gi][ni], breg[S][gi][ni], qc);
 #pragma unroll
         for (int mi = 0; mi < MS; ++mi) {
-          const int row = mi * 32 + col_in;
-          const int off = gi * C::A_SUB + row * 128 + (((4 * hh + j) ^ ((row >> 1) & 7)) << 4);
+          const int row = (wm * MS + mi) * 32 + col_in;
+          const int off = gi * C::A_SUB + row * 128 + (((4 * hh + j) ^ piece_swizzle<128>(row)) << 4);
           const f16x8 af = *(const f16x8*)(st + off);
 #pragma unroll
           for (int ni = 0; ni < NSUB; ++ni)
@@ -436,10 +472,10 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
   for (int mi = 0; mi < MS; ++mi) {
-    if (mi * 32 >= rows) continue;
+    if ((wm * MS + mi) * 32 >= rows) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = mi * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
+      const int row = (wm * MS + mi) * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
       if (row >= rows) continue;
       const size_t orow = (size_t)(row0 + row) * prm.N;
       if constexpr (MODE == GEMM_FUSED_SWIGLU) {
@@ -467,7 +503,7 @@ __global__ __launch_bounds__(256, MS == 4 ? 1 : 2) void gemm_kernel(GemmParams p
 // One instantiation: each wave owns NSUB subtiles of 32 columns.  4-bit
 // weights stage two groups per step (64-byte row segments) when K allows,
 // unless the tuning knob asks for one.
-template <int BITS, int MODE, int MS, int NSUB>
+template <int BITS, int MODE, int MS, int NSUB, int WM>
 static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
   const int ncols = 4 * 32 * (MODE == GEMM_FUSED_SWIGLU ? NSUB / 2 : NSUB);
   prm.n_tiles = (prm.N + ncols - 1) / ncols;
@@ -476,20 +512,20 @@ static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
   const int64_t total = (int64_t)prm.n_tiles * prm.m_tiles;
   prm.per_xcd = (int)((total + NUM_XCD - 1) / NUM_XCD);
   dim3 grid((unsigned)(prm.per_xcd * NUM_XCD));
-  if constexpr (BITS == 4) {
+  if constexpr (BITS == 4 && WM == 1) {  // two M waves: two-group stages would not fit
     if ((prm.K / 64) % 2 == 0 && tuning(TUNE_GEMM_KG) != 1)
-      return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB>, grid, 256, 0, st, prm);
+      return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB, WM>, grid, 256 * WM, 0, st, prm);
   }
-  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB>, grid, 256, 0, st, prm);
+  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB, WM>, grid, 256 * WM, 0, st, prm);
 }
 
 template <int BITS, int MODE, int MS>
 static hipError_t launch_one(const GemmParams& prm, hipStream_t st) {
   // fp16 rows: two stages of four subtiles would not fit in LDS
   if constexpr (MS == 4 && BITS != 16) {
-    if (tuning(TUNE_GEMM_NSUB) == 4) return launch_sub<BITS, MODE, MS, 4>(prm, st);
+    if (tuning(TUNE_GEMM_NSUB) == 4) return launch_sub<BITS, MODE, MS, 4, 1>(prm, st);
   }
-  return launch_sub<BITS, MODE, MS, 2>(prm, st);
+  return launch_sub<BITS, MODE, MS, 2, 1>(prm, st);
 }
 
 template <int BITS, int MODE>
@@ -498,6 +534,7 @@ static hipError_t launch_ms(int bm, const GemmParams& prm, hipStream_t st) {
     case 32: return launch_one<BITS, MODE, 1>(prm, st);
     case 64: return launch_one<BITS, MODE, 2>(prm, st);
     case 128: return launch_one<BITS, MODE, 4>(prm, st);
+    case 256: return launch_sub<BITS, MODE, 4, 2, 2>(prm, st);  // eight waves, two along M
     default: return hipErrorInvalidValue;
   }
 }

@@ -31,8 +31,8 @@ KERNEL_PLAN = [
     (re.compile(r"router_logits_(small|mfma)_kernel"), "router_logits"),
     (re.compile(r"gemv_up_kernel<\d+, \d+, true>"), "gemv_gate_up_swiglu"),
     (re.compile(r"gemv_down_kernel"), "gemv_down_combine"),
-    (re.compile(r"gemm_kernel<\d+, 0, \d+, \d+>"), "gemm_gate_up_swiglu"),
-    (re.compile(r"gemm_kernel<\d+, 2, \d+, \d+>"), "gemm_down"),
+    (re.compile(r"gemm_kernel<\d+, 0,"), "gemm_gate_up_swiglu"),
+    (re.compile(r"gemm_kernel<\d+, 2,"), "gemm_down"),
     (re.compile(r"sort_pairs_kernel"), "sort_pairs"),
     (re.compile(r"combine_kernel"), "combine"),
 ]

@@ -106,6 +106,31 @@ def test_sort_matches_oracle_exactly(name, built):
     assert np.array_equal(taps["perm"], perm)
 
 
+# (row tile, K groups per stage, N subtiles per wave): every launch shape the
+# batched GEMM can take accumulates each output over K in the same order, so
+# all of them must give the same bits as the default choice
+GEMM_SHAPES = [(32, 2, 2), (64, 1, 2), (64, 2, 2), (128, 1, 2), (128, 2, 2), (128, 2, 4), (256, 1, 2)]
+DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2}
+
+
+@pytest.mark.parametrize("name", ["prefill_bm128", "prefill_small", "tiny_q8_bf16", "tiny_fp16w"])
+def test_gemm_launch_shapes_are_bit_identical(name, built):
+    inp, _, dev = built(name)
+    ref, _ = _run(dev, moe.FLAG_FORCE_MFMA)
+    try:
+        for bm, kg, nsub in GEMM_SHAPES:
+            print("case", name, "bm", bm, "kg", kg, "nsub", nsub, flush=True)
+            moe.debug_set_tuning(3, bm)
+            moe.debug_set_tuning(4, kg)
+            moe.debug_set_tuning(5, nsub)
+            moe.debug_set_tuning(2, 2)  # short row groups: exercises the grouped tile order
+            y, _ = _run(dev, moe.FLAG_FORCE_MFMA)
+            assert np.array_equal(y, ref), "%s bm %d kg %d nsub %d" % (name, bm, kg, nsub)
+    finally:
+        for key, v in DEFAULT_TUNING.items():
+            moe.debug_set_tuning(key, v)
+
+
 def test_runs_are_deterministic(built):
     inp, _, dev = built("prefill_small")
     a, _ = _run(dev, 0)
