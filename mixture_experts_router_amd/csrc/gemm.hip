@@ -22,8 +22,8 @@
 // Both operands stream HBM -> LDS with global_load_lds_dwordx4 (no register
 // staging) through NS stages sized to the LDS: A rows with a 16-byte-chunk XOR
 // swizzle (see piece_swizzle) so the MFMA operand reads are conflict free;
-// each wave's 64 weight rows into its own LDS region.  Scales and biases ride
-// a register ring of the same depth.  One wait (this wave's loads of the
+// each wave's 64 weight rows into its own LDS region; the stage's scales and
+// biases (KG fp16 values of a column per lane) beside them.  One wait (this wave's loads of the
 // stage) and one barrier (every wave's loads; the oldest stage free) per
 // group, then the next group's loads are issued and the stage is consumed:
 // B codes read once per group, dequantised per MFMA k-step in registers
@@ -107,14 +107,20 @@ struct GemmCfg {
   static constexpr int A_SUB = BM * 128;  // A of one group: BM rows x 64 fp16
   static constexpr int A_BYTES = KG * A_SUB;
   static constexpr int B_BYTES = 4 * BGeo<BITS, KG, NSUB>::ROWS * BGeo<BITS, KG, NSUB>::SEG;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
+  // scales and biases: per column block, tensor and subtile one 64-lane
+  // region, KG fp16 values per lane (lanes 0-31 hold the subtile's columns).
+  // Loads of at most 4 bytes into LDS place lane i at 4 i.
+  static constexpr int SC_LANE = 2 * KG;  // bytes loaded per lane
+  static constexpr int SC_REGION = 64 * 4;
+  static constexpr int SC_BYTES = BITS != 16 ? 4 * 2 * NSUB * SC_REGION : 0;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   // 128-row tiles: one workgroup per CU (160 KB LDS); smaller: two
   static constexpr int BUDGET = MS == 4 || WM == 2 ? 156 * 1024 : 78 * 1024;
   static constexpr int NS_FIT = BUDGET / STAGE;
   static constexpr int NS = NS_FIT < 2 ? 2 : (NS_FIT > 6 ? 6 : NS_FIT);
   // vector memory instructions per wave per stage: A, B, scales and biases
   // (the WM waves of a column block share its weight loads)
-  static constexpr int LOADS = KG * MS + BGeo<BITS, KG, NSUB>::NI / WM + (BITS != 16 ? 2 * NSUB * KG : 0);
+  static constexpr int LOADS = KG * MS + BGeo<BITS, KG, NSUB>::NI / WM + (BITS != 16 ? 2 * NSUB / WM : 0);
   static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
   static_assert(NS * STAGE <= 159 * 1024, "LDS (160 KB less the tile lookup)");
 };
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
   };
   const int64_t row_bytes = (int64_t)K * BITS / 8;
   const uint8_t* qbase[NSUB];
-  rsrc_t rs[NSUB], rbias[NSUB];
+  rsrc_t rsb[2][NSUB];  // scales, biases of each subtile's view
   uint32_t s_off[NSUB];
 #pragma unroll
   for (int ni = 0; ni < NSUB; ++ni) {
@@ -334,10 +340,11 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
     const int64_t erow = (int64_t)e * v.stride;  // the expert's first row
     qbase[ni] = v.q + erow * row_bytes;
     if constexpr (BITS != 16) {
-      rs[ni] = make_rsrc(v.s + erow * ng, 0xFFFFFFFFu);
-      rbias[ni] = make_rsrc(v.b + erow * ng, 0xFFFFFFFFu);
+      rsb[0][ni] = make_rsrc(v.s + erow * ng, 0x80000000u);
+      rsb[1][ni] = make_rsrc(v.b + erow * ng, 0x80000000u);
     }
-    s_off[ni] = (uint32_t)column(ni, col_in) * (uint32_t)ng * 2u;
+    // lanes 32-63 read past the descriptor's range: no memory access
+    s_off[ni] = lane < 32 ? (uint32_t)column(ni, lane) * (uint32_t)ng * 2u : 0xFFFF0000u;
   }
   // this wave's weight load instructions: q = q0 + qq, qq < NI / WM (the
   // row waves of a column block split its loads); q0 and the subtile of an
@@ -368,7 +375,10 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  uint32_t sreg[NS][KG][NSUB], breg[NS][KG][NSUB];
+  // the scale regions this wave loads: WM == 1 both tensors, else one each
+  constexpr int T_PER_WAVE = 2 / WM;
+  const int t0 = WM == 1 ? 0 : wm;
+  const int sc_wave = C::A_BYTES + C::B_BYTES + wn * 2 * NSUB * C::SC_REGION;
   const int b_wave = C::A_BYTES + wn * G::ROWS * G::SEG;  // this wave's B codes
   const int last = nst - 1;
   // step k (groups KG k .. KG k + KG - 1; clamped to the last step) into stage S
@@ -390,11 +400,14 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
     }
     if constexpr (BITS != 16) {
 #pragma unroll
-      for (int gi = 0; gi < KG; ++gi)
+      for (int tt = 0; tt < T_PER_WAVE; ++tt)
 #pragma unroll
         for (int ni = 0; ni < NSUB; ++ni) {
-          sreg[S][gi][ni] = __builtin_amdgcn_raw_buffer_load_b16(rs[ni], (int)s_off[ni], (k * KG + gi) * 2, 0);
-          breg[S][gi][ni] = __builtin_amdgcn_raw_buffer_load_b16(rbias[ni], (int)s_off[ni], (k * KG + gi) * 2, 0);
+          const int t = t0 + tt;
+          const int lds_off = sc_wave + (t * NSUB + ni) * C::SC_REGION;
+          const rsrc_t r = WM == 1 ? rsb[tt][ni] : (t == 0 ? rsb[0][ni] : rsb[1][ni]);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(st + lds_off), C::SC_LANE, s_off[ni],
+                                                   (uint32_t)k * C::SC_LANE, 0, 0);
         }
     }
   };
@@ -417,11 +430,20 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
           const int off = b_wave + r * G::SEG + piece * 16;
           bc[ni][t] = *(const u32x4*)(st + off);
         }
+      uint32_t sv[NSUB] = {}, bv[NSUB] = {};
+      if constexpr (BITS != 16) {
+#pragma unroll
+        for (int ni = 0; ni < NSUB; ++ni) {
+          const int off = sc_wave + ni * C::SC_REGION + col_in * 4 + gi * 2;
+          sv[ni] = *(const uint16_t*)(st + off);
+          bv[ni] = *(const uint16_t*)(st + off + NSUB * C::SC_REGION);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f16x8 bf[NSUB];
 #pragma unroll
-        for (int ni = 0; ni < NSUB; ++ni) bf[ni] = dequant_b<BITS>(bc[ni], j, sreg[S][gi][ni], breg[S][gi][ni], qc);
+        for (int ni = 0; ni < NSUB; ++ni) bf[ni] = dequant_b<BITS>(bc[ni], j, sv[ni], bv[ni], qc);
 #pragma unroll
         for (int mi = 0; mi < MS; ++mi) {
           const int row = (wm * MS + mi) * 32 + col_in;
