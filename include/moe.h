@@ -220,10 +220,12 @@ int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
  * Launch-shape knobs for measurement sweeps (process-wide): key 0 = resident
  * waves per CU targeted by the decode gate+up kernel, key 1 = by the decode
  * down kernel, key 2 = row tiles per group in the batched GEMM's tile order,
- * key 3 = the batched GEMM's row tile (32, 64, 128 or 256; other values:
- * chosen from the batch), key 4 = K groups of 64 per pipeline stage (1; other
+ * key 3 = the batched GEMM's row tile (32, 64 or 128; other values: chosen
+ * from the batch), key 4 = K groups of 64 per pipeline stage (1; other
  * values: 2 where the stage fits in LDS), key 5 = 32-column subtiles per wave
- * at the 128-row tile (4; other values: 2).
+ * at the 128-row tile (4; other values: 2), key 6 = waves per column block at
+ * the 64- and 128-row tiles (1; other values: 2, splitting each group's
+ * k-steps).
  * Values <= 0 are ignored.  Results do not depend on them.
  */
 void moe_debug_set_tuning(int32_t key, int32_t value);

@@ -76,7 +76,7 @@ __device__ __forceinline__ bool tile_of(const GemmParams& prm, int bid, int& n, 
 
 int gemm_block_m(int P, int E) {
   const int forced = tuning(TUNE_GEMM_BM);
-  if (forced == 32 || forced == 64 || forced == 128 || forced == 256) return forced;
+  if (forced == 32 || forced == 64 || forced == 128) return forced;
   const int avg = E > 0 ? P / E : P;
   if (avg <= 32) return 32;
   if (avg <= 96) return 64;
@@ -101,9 +101,9 @@ struct BGeo {
   static constexpr int READS = HALF / 16;    // 16-byte LDS reads per lane, subtile and group
 };
 
-template <int BITS, int MS, int KG, int NSUB, int WM>
+template <int BITS, int MS, int KG, int NSUB, int KS>
 struct GemmCfg {
-  static constexpr int BM = 32 * MS * WM;  // WM waves along M, each 32*MS rows
+  static constexpr int BM = 32 * MS;
   static constexpr int A_SUB = BM * 128;  // A of one group: BM rows x 64 fp16
   static constexpr int A_BYTES = KG * A_SUB;
   static constexpr int B_BYTES = 4 * BGeo<BITS, KG, NSUB>::ROWS * BGeo<BITS, KG, NSUB>::SEG;
@@ -114,13 +114,15 @@ struct GemmCfg {
   static constexpr int SC_REGION = 64 * 4;
   static constexpr int SC_BYTES = BITS != 16 ? 4 * 2 * NSUB * SC_REGION : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
-  // 128-row tiles: one workgroup per CU (160 KB LDS); smaller: two
-  static constexpr int BUDGET = MS == 4 || WM == 2 ? 156 * 1024 : 78 * 1024;
+  // 128-row tiles and eight-wave workgroups: one workgroup per CU (160 KB
+  // LDS); otherwise two
+  static constexpr int BUDGET = MS == 4 || KS == 2 ? 156 * 1024 : 78 * 1024;
   static constexpr int NS_FIT = BUDGET / STAGE;
   static constexpr int NS = NS_FIT < 2 ? 2 : (NS_FIT > 6 ? 6 : NS_FIT);
   // vector memory instructions per wave per stage: A, B, scales and biases
-  // (the WM waves of a column block share its weight loads)
-  static constexpr int LOADS = KG * MS + BGeo<BITS, KG, NSUB>::NI / WM + (BITS != 16 ? 2 * NSUB / WM : 0);
+  // (the KS waves of a column block split its loads evenly)
+  static_assert(MS % KS == 0 && BGeo<BITS, KG, NSUB>::NI % KS == 0, "loads split over the K waves");
+  static constexpr int LOADS = KG * MS / KS + BGeo<BITS, KG, NSUB>::NI / KS + (BITS != 16 ? 2 * NSUB / KS : 0);
   static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
   static_assert(NS * STAGE <= 159 * 1024, "LDS (160 KB less the tile lookup)");
 };
@@ -211,11 +213,10 @@ __device__ __forceinline__ f16x8 dequant_b(const u32x4* c, int j, uint32_t s_bit
   }
 }
 
-template <int BITS, int MODE, int MS, int KG, int NSUB, int WM>
-__global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2)) void gemm_kernel(GemmParams prm) {
+template <int BITS, int MODE, int MS, int KG, int NSUB, int KS>
+__global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_kernel(GemmParams prm) {
   using G = BGeo<BITS, KG, NSUB>;
-  using C = GemmCfg<BITS, MS, KG, NSUB, WM>;
-  static_assert(G::NI % WM == 0, "weight loads split over the M waves");
+  using C = GemmCfg<BITS, MS, KG, NSUB, KS>;
   constexpr int HALFSUB = NSUB / 2;  // fused: subtiles [0, HALFSUB) gate, the rest the matching up
   constexpr int BM = C::BM, NS = C::NS;
   // one array per stage: distinct objects let the compiler see that reading
@@ -234,9 +235,10 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
   };
 
   const int lane = lane_id();
-  const int wave = wave_id();     // 0 .. 4*WM-1
-  const int wn = wave % 4;        // column block of this wave
-  const int wm = WM == 1 ? 0 : wave / 4;  // row block of this wave
+  const int wave = wave_id();                 // 0 .. 4*KS-1
+  const int wn = wave % 4;                    // column block of this wave
+  const int kh = KS == 1 ? 0 : wave / 4;      // which share of each group's k-steps
+  constexpr int JW = 4 / KS;                  // MFMA k-steps per group and wave
   const int tid = threadIdx.x;
 
   // ---- which (expert, M tile) this workgroup owns: tiles are numbered
@@ -291,15 +293,18 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
   // All loads are buffer loads: base addresses in scalar registers, a fixed
   // 32-bit byte offset per lane, the group's offset as the scalar offset.
   //
-  // ---- A: load instruction q of this wave covers tile rows r0 = 8*(wave*MS+q)
-  // .. r0+7; lane i writes LDS chunk i%8 of row r0 + i/8, which holds the
-  // row's logical 16-byte chunk (i%8) ^ piece_swizzle(row).  Rows past the tile
-  // re-read the tile's first row (never stored).
+  // ---- A: the tile's 4*MS load instructions per group, MS/KS per wave;
+  // instruction q covers tile rows r0 = 8*q .. r0+7; lane i writes LDS chunk
+  // i%8 of row r0 + i/8, which holds the row's logical 16-byte chunk
+  // (i%8) ^ piece_swizzle(row).  Rows past the tile re-read the tile's first
+  // row (never stored).
+  constexpr int NA = MS / KS;
+  const int qa0 = wn * MS + kh * NA;  // this wave's first A instruction
   const rsrc_t ra = make_rsrc(prm.a, 0xFFFFFFFFu);
-  uint32_t a_off[MS];
+  uint32_t a_off[NA];
 #pragma unroll
-  for (int q = 0; q < MS; ++q) {
-    const int r = 8 * (wave * MS + q) + lane / 8;
+  for (int q = 0; q < NA; ++q) {
+    const int r = 8 * (qa0 + q) + lane / 8;
     const int rr = r < rows ? r : 0;
     uint32_t arow;
     if constexpr (MODE == GEMM_ROWS_F16) arow = (uint32_t)(row0 + rr);
@@ -346,11 +351,11 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
     // lanes 32-63 read past the descriptor's range: no memory access
     s_off[ni] = lane < 32 ? (uint32_t)column(ni, lane) * (uint32_t)ng * 2u : 0xFFFF0000u;
   }
-  // this wave's weight load instructions: q = q0 + qq, qq < NI / WM (the
-  // row waves of a column block split its loads); q0 and the subtile of an
+  // this wave's weight load instructions: q = q0 + qq, qq < NI / KS (the K
+  // waves of a column block split its loads); q0 and the subtile of an
   // instruction are wave-uniform, so the descriptors stay in scalar registers
-  constexpr int NQ = G::NI / WM;
-  const int q0 = WM == 1 ? 0 : wm * NQ;
+  constexpr int NQ = G::NI / KS;
+  const int q0 = kh * NQ;
   rsrc_t rq[NQ];
   uint32_t b_off[NQ];
 #pragma unroll
@@ -375,9 +380,9 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  // the scale regions this wave loads: WM == 1 both tensors, else one each
-  constexpr int T_PER_WAVE = 2 / WM;
-  const int t0 = WM == 1 ? 0 : wm;
+  // the scale regions this wave loads: KS == 1 both tensors, else one each
+  constexpr int T_PER_WAVE = 2 / KS;
+  const int t0 = kh;
   const int sc_wave = C::A_BYTES + C::B_BYTES + wn * 2 * NSUB * C::SC_REGION;
   const int b_wave = C::A_BYTES + wn * G::ROWS * G::SEG;  // this wave's B codes
   const int last = nst - 1;
@@ -389,8 +394,8 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
 #pragma unroll
     for (int gi = 0; gi < KG; ++gi)
 #pragma unroll
-      for (int q = 0; q < MS; ++q) {
-        const int lds_off = gi * C::A_SUB + 8 * (wave * MS + q) * 128;
+      for (int q = 0; q < NA; ++q) {
+        const int lds_off = gi * C::A_SUB + 8 * (qa0 + q) * 128;
         dma16(ra, a_off[q], (uint32_t)(k * KG + gi) * 128u, st + lds_off);
       }
 #pragma unroll
@@ -405,56 +410,90 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
         for (int ni = 0; ni < NSUB; ++ni) {
           const int t = t0 + tt;
           const int lds_off = sc_wave + (t * NSUB + ni) * C::SC_REGION;
-          const rsrc_t r = WM == 1 ? rsb[tt][ni] : (t == 0 ? rsb[0][ni] : rsb[1][ni]);
+          const rsrc_t r = KS == 1 ? rsb[tt][ni] : (t == 0 ? rsb[0][ni] : rsb[1][ni]);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(st + lds_off), C::SC_LANE, s_off[ni],
                                                    (uint32_t)k * C::SC_LANE, 0, 0);
         }
     }
   };
+  // One stage: 4 KG MFMA k-steps.  The A fragments and dequantised weights
+  // of k-step s+1 are produced (LDS reads, VALU) ahead of the MFMAs of
+  // k-step s, so LDS latency and the dequantisation overlap the matrix cores;
+  // each group's weight codes and scales are read one group ahead.
   auto compute = [&](auto S_) __attribute__((always_inline)) {
-    constexpr int S = decltype(S_)::value;
     // LDS addresses are formed as one integer offset from the stage array:
     // the compiler attributes an access to its array (and so knows it does
     // not wait on loads landing in other stages) only through a short chain
     // of address arithmetic on the array itself
     const uint8_t* st = stage(S_);
+    constexpr int NJ = JW * KG;
+    // this wave's share of a lane's code bytes of a group: RB bytes (its JW
+    // k-steps) at byte kh*RB of the lane's half of the group
+    constexpr int RB = G::HALF / KS;
+    constexpr int RT = RB >= 16 ? RB / 16 : 1;
+    u32x4 bc[KG][NSUB][RT];
+    uint32_t sv[KG][NSUB], bv[KG][NSUB];
+    auto read_group = [&](auto GI_) __attribute__((always_inline)) {
+      constexpr int gi = decltype(GI_)::value;
 #pragma unroll
-    for (int gi = 0; gi < KG; ++gi) {
-      u32x4 bc[NSUB][G::READS];
+      for (int ni = 0; ni < NSUB; ++ni) {
+        const int r = ni * 32 + col_in;
+        if constexpr (RB >= 16) {
 #pragma unroll
-      for (int ni = 0; ni < NSUB; ++ni)
-#pragma unroll
-        for (int t = 0; t < G::READS; ++t) {
-          const int r = ni * 32 + col_in;
-          const int piece = (gi * (G::ROW / 16) + hh * G::READS + t) ^ piece_swizzle<G::SEG>(r);
-          const int off = b_wave + r * G::SEG + piece * 16;
-          bc[ni][t] = *(const u32x4*)(st + off);
+          for (int t = 0; t < RT; ++t) {
+            const int piece = (gi * (G::ROW / 16) + hh * G::READS + kh * RT + t) ^ piece_swizzle<G::SEG>(r);
+            bc[gi][ni][t] = *(const u32x4*)(st + (b_wave + r * G::SEG + piece * 16));
+          }
+        } else {  // 8 bytes inside one piece
+          const int piece = (gi * (G::ROW / 16) + hh * G::READS) ^ piece_swizzle<G::SEG>(r);
+          const u32x2 v = *(const u32x2*)(st + (b_wave + r * G::SEG + piece * 16 + kh * 8));
+          bc[gi][ni][0] = u32x4{v.x, v.y, 0u, 0u};
         }
-      uint32_t sv[NSUB] = {}, bv[NSUB] = {};
-      if constexpr (BITS != 16) {
-#pragma unroll
-        for (int ni = 0; ni < NSUB; ++ni) {
+        if constexpr (BITS != 16) {
           const int off = sc_wave + ni * C::SC_REGION + col_in * 4 + gi * 2;
-          sv[ni] = *(const uint16_t*)(st + off);
-          bv[ni] = *(const uint16_t*)(st + off + NSUB * C::SC_REGION);
+          sv[gi][ni] = *(const uint16_t*)(st + off);
+          bv[gi][ni] = *(const uint16_t*)(st + (off + NSUB * C::SC_REGION));
+        } else {
+          sv[gi][ni] = bv[gi][ni] = 0;
         }
       }
+    };
+    // k-step s2 of the stage: group s2 / JW, k-step kh*JW + s2 % JW of the group
+    auto read_a = [&](auto S2_, f16x8 (&af)[MS]) __attribute__((always_inline)) {
+      constexpr int gi = decltype(S2_)::value / JW, jj = decltype(S2_)::value % JW;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f16x8 bf[NSUB];
-#pragma unroll
-        for (int ni = 0; ni < NSUB; ++ni) bf[ni] = dequant_b<BITS>(bc[ni], j, sv[ni], bv[ni], qc);
-#pragma unroll
-        for (int mi = 0; mi < MS; ++mi) {
-          const int row = (wm * MS + mi) * 32 + col_in;
-          const int off = gi * C::A_SUB + row * 128 + (((4 * hh + j) ^ piece_swizzle<128>(row)) << 4);
-          const f16x8 af = *(const f16x8*)(st + off);
-#pragma unroll
-          for (int ni = 0; ni < NSUB; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[ni], acc[mi][ni], 0, 0, 0);
-        }
+      for (int mi = 0; mi < MS; ++mi) {
+        const int row = mi * 32 + col_in;
+        const int piece = (4 * hh + kh * JW + jj) ^ piece_swizzle<128>(row);
+        af[mi] = *(const f16x8*)(st + (gi * C::A_SUB + row * 128 + (piece << 4)));
       }
-    }
+    };
+    auto deq = [&](auto S2_, f16x8 (&bf)[NSUB]) __attribute__((always_inline)) {
+      constexpr int gi = decltype(S2_)::value / JW, jj = decltype(S2_)::value % JW;
+#pragma unroll
+      for (int ni = 0; ni < NSUB; ++ni) bf[ni] = dequant_b<BITS>(bc[gi][ni], jj, sv[gi][ni], bv[gi][ni], qc);
+    };
+    f16x8 af[2][MS], bf[2][NSUB];
+    read_group(IC<0>{});
+    read_a(IC<0>{}, af[0]);
+    deq(IC<0>{}, bf[0]);
+    for_stages<0, NJ>([&](auto S2_) __attribute__((always_inline)) {
+      constexpr int s2 = decltype(S2_)::value;
+      constexpr int c = s2 & 1;
+      // the reads for k-step s2+1 go out before this k-step's MFMAs (the
+      // scheduler would otherwise sink each read to just before its use)
+      if constexpr (s2 % JW == 0 && s2 / JW + 1 < KG) read_group(IC<s2 / JW + 1>{});
+      if constexpr (s2 + 1 < NJ) read_a(IC<s2 + 1>{}, af[c ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (s2 + 1 < NJ) deq(IC<s2 + 1>{}, bf[c ^ 1]);
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NSUB; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][mi], bf[c][ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      return true;
+    });
   };
 
   // prologue: steps 0 .. NS-2 in flight
@@ -490,14 +529,62 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
   });
   wait_vmcnt<0>();  // no load into LDS may land after the workgroup ends
 
+  if constexpr (KS == 2) {
+    // the two waves of a column block hold partial sums over disjoint
+    // k-steps: the second passes its accumulators through the stage memory
+    // (4 KB per 32x32 tile and wave) and the first adds them, always in the
+    // same order.  TPS tiles of all four column blocks fit in one stage.
+    constexpr int TPS = C::STAGE / 16384;
+    constexpr int CAP = TPS * NS;
+    static_assert(TPS >= 1, "stage too small for the pair reduction");
+    for_stages<0, (MS * NSUB + CAP - 1) / CAP>([&](auto R_) __attribute__((always_inline)) {
+      constexpr int t_lo = decltype(R_)::value * CAP;
+      __syncthreads();  // every wave is done with the stage memory (or the last round)
+      if (kh == 1) {
+        for_stages<t_lo, (t_lo + CAP < MS * NSUB ? t_lo + CAP : MS * NSUB)>([&](auto T_)
+                                                                            __attribute__((always_inline)) {
+          constexpr int t = decltype(T_)::value, u = t - t_lo;
+          uint8_t* dst = stage(IC<u / TPS>{});
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc[t / NSUB][t % NSUB];
+            const f32x4 v = {a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+            *(f32x4*)(dst + ((u % TPS) * 16384 + wn * 4096 + q * 1024 + lane * 16)) = v;
+          }
+          return true;
+        });
+      }
+      __syncthreads();
+      if (kh == 0) {
+        for_stages<t_lo, (t_lo + CAP < MS * NSUB ? t_lo + CAP : MS * NSUB)>([&](auto T_)
+                                                                            __attribute__((always_inline)) {
+          constexpr int t = decltype(T_)::value, u = t - t_lo;
+          const uint8_t* src = stage(IC<u / TPS>{});
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = *(const f32x4*)(src + ((u % TPS) * 16384 + wn * 4096 + q * 1024 + lane * 16));
+            f32x16& a = acc[t / NSUB][t % NSUB];
+            a[4 * q] += v.x;
+            a[4 * q + 1] += v.y;
+            a[4 * q + 2] += v.z;
+            a[4 * q + 3] += v.w;
+          }
+          return true;
+        });
+      }
+      return true;
+    });
+    if (kh == 1) return;
+  }
+
   // ---- epilogue.  32x32 accumulator layout: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
   for (int mi = 0; mi < MS; ++mi) {
-    if ((wm * MS + mi) * 32 >= rows) continue;
+    if (mi * 32 >= rows) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = (wm * MS + mi) * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
+      const int row = mi * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
       if (row >= rows) continue;
       const size_t orow = (size_t)(row0 + row) * prm.N;
       if constexpr (MODE == GEMM_FUSED_SWIGLU) {
@@ -525,7 +612,7 @@ __global__ __launch_bounds__(256 * WM, MS == 4 && WM == 1 ? 1 : (WM == 2 ? 1 : 2
 // One instantiation: each wave owns NSUB subtiles of 32 columns.  4-bit
 // weights stage two groups per step (64-byte row segments) when K allows,
 // unless the tuning knob asks for one.
-template <int BITS, int MODE, int MS, int NSUB, int WM>
+template <int BITS, int MODE, int MS, int NSUB, int KS>
 static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
   const int ncols = 4 * 32 * (MODE == GEMM_FUSED_SWIGLU ? NSUB / 2 : NSUB);
   prm.n_tiles = (prm.N + ncols - 1) / ncols;
@@ -534,18 +621,23 @@ static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
   const int64_t total = (int64_t)prm.n_tiles * prm.m_tiles;
   prm.per_xcd = (int)((total + NUM_XCD - 1) / NUM_XCD);
   dim3 grid((unsigned)(prm.per_xcd * NUM_XCD));
-  if constexpr (BITS == 4 && WM == 1) {  // two M waves: two-group stages would not fit
+  if constexpr (BITS == 4) {
     if ((prm.K / 64) % 2 == 0 && tuning(TUNE_GEMM_KG) != 1)
-      return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB, WM>, grid, 256 * WM, 0, st, prm);
+      return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB, KS>, grid, 256 * KS, 0, st, prm);
   }
-  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB, WM>, grid, 256 * WM, 0, st, prm);
+  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB, KS>, grid, 256 * KS, 0, st, prm);
 }
 
+// Row tiles of 64 and 128 run eight waves, two per column block splitting
+// each group's k-steps, unless the tuning knob asks for four.
 template <int BITS, int MODE, int MS>
 static hipError_t launch_one(const GemmParams& prm, hipStream_t st) {
   // fp16 rows: two stages of four subtiles would not fit in LDS
   if constexpr (MS == 4 && BITS != 16) {
     if (tuning(TUNE_GEMM_NSUB) == 4) return launch_sub<BITS, MODE, MS, 4, 1>(prm, st);
+  }
+  if constexpr (MS >= 2) {
+    if (tuning(TUNE_GEMM_KSPLIT) != 1) return launch_sub<BITS, MODE, MS, 2, 2>(prm, st);
   }
   return launch_sub<BITS, MODE, MS, 2, 1>(prm, st);
 }
@@ -556,7 +648,6 @@ static hipError_t launch_ms(int bm, const GemmParams& prm, hipStream_t st) {
     case 32: return launch_one<BITS, MODE, 1>(prm, st);
     case 64: return launch_one<BITS, MODE, 2>(prm, st);
     case 128: return launch_one<BITS, MODE, 4>(prm, st);
-    case 256: return launch_sub<BITS, MODE, 4, 2, 2>(prm, st);  // eight waves, two along M
     default: return hipErrorInvalidValue;
   }
 }

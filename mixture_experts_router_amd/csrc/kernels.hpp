@@ -35,10 +35,11 @@ enum TuneKey {
   TUNE_UP_WAVES_PER_CU = 0,
   TUNE_DOWN_WAVES_PER_CU = 1,
   TUNE_GEMM_GROUP_M = 2,
-  TUNE_GEMM_BM = 3,  // 32, 64, 128 or 256 forces the GEMM row tile; anything else: chosen from the batch
+  TUNE_GEMM_BM = 3,  // 32, 64 or 128 forces the GEMM row tile; anything else: chosen from the batch
   TUNE_GEMM_KG = 4,  // 1: 4-bit GEMM stages one quantisation group per step (default: two when K allows)
   TUNE_GEMM_NSUB = 5,  // 4: 128-row GEMM tiles give each wave 128 columns (default 64)
-  TUNE_KEYS = 6
+  TUNE_GEMM_KSPLIT = 6,  // 1: 64- and 128-row GEMM tiles run four waves (default eight, splitting k)
+  TUNE_KEYS = 7
 };
 int tuning(TuneKey key);
 
@@ -96,7 +97,7 @@ int router_small_max_tokens();
 
 // -------------------------------------------------- batched (MFMA GEMM)
 enum GemmMode { GEMM_FUSED_SWIGLU = 0, GEMM_GATHER_F32 = 1, GEMM_ROWS_F16 = 2 };
-// rows of one M tile for a dispatch (32, 64, 128 or 256)
+// rows of one M tile for a dispatch (32, 64 or 128)
 int gemm_block_m(int P, int E);
 // upper bound on M tiles for P pairs over E experts
 int gemm_max_mtiles(int P, int E, int bm);
