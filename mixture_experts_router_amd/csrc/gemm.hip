@@ -46,6 +46,7 @@ struct GemmParams {
   int kcap, E, K, N;
   WView w0, w1;
   void* out;
+  uint32_t a_bytes;  // extent of the A rows (offsets at or past it read nothing)
   int perm8_out;  // fused: store h blocks in 4-bit unpack order
   // tile order (see tile_of): n_tiles column tiles x m_tiles row tiles, in
   // groups of group_m row tiles; per_xcd consecutive tiles per XCD
@@ -296,11 +297,11 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
   // ---- A: the tile's 4*MS load instructions per group, MS/KS per wave;
   // instruction q covers tile rows r0 = 8*q .. r0+7; lane i writes LDS chunk
   // i%8 of row r0 + i/8, which holds the row's logical 16-byte chunk
-  // (i%8) ^ piece_swizzle(row).  Rows past the tile re-read the tile's first
-  // row (never stored).
+  // (i%8) ^ piece_swizzle(row).  Lanes of rows past the tile point past the
+  // descriptor's range: no memory access (their LDS rows are never used).
   constexpr int NA = MS / KS;
   const int qa0 = wn * MS + kh * NA;  // this wave's first A instruction
-  const rsrc_t ra = make_rsrc(prm.a, 0xFFFFFFFFu);
+  const rsrc_t ra = make_rsrc(prm.a, prm.a_bytes);
   uint32_t a_off[NA];
 #pragma unroll
   for (int q = 0; q < NA; ++q) {
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
     if constexpr (MODE == GEMM_ROWS_F16) arow = (uint32_t)(row0 + rr);
     else arow = (uint32_t)(prm.perm[row0 + rr] / prm.kcap);
     const int chunk = (lane & 7) ^ piece_swizzle<128>(r);
-    a_off[q] = arow * (uint32_t)K * 2u + (uint32_t)chunk * 16u;
+    a_off[q] = r < rows ? arow * (uint32_t)K * 2u + (uint32_t)chunk * 16u : 0x80000000u;
   }
 
   // ---- B: this wave's 32*NSUB weight rows; rows [32 ni, 32 ni + 32) are
@@ -416,81 +417,105 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
         }
     }
   };
-  // One stage: 4 KG MFMA k-steps.  The A fragments and dequantised weights
-  // of k-step s+1 are produced (LDS reads, VALU) ahead of the MFMAs of
-  // k-step s, so LDS latency and the dequantisation overlap the matrix cores;
+  // ---- reading a stage.  LDS addresses are formed as one integer offset
+  // from the stage array: the compiler attributes an access to its array (and
+  // so knows it does not wait on loads landing in other stages) only through
+  // a short chain of address arithmetic on the array itself.
+  //
+  // This wave's share of a lane's code bytes of a group: RB bytes (its JW
+  // k-steps) at byte kh*RB of the lane's half of the group.
+  constexpr int RB = G::HALF / KS;
+  constexpr int RT = RB >= 16 ? RB / 16 : 1;
+  typedef u32x4 Codes[NSUB][RT];
+  auto read_codes = [&](const uint8_t* st, auto GI_, Codes& bc, uint32_t (&sv)[NSUB], uint32_t (&bv)[NSUB])
+                        __attribute__((always_inline)) {
+    constexpr int gi = decltype(GI_)::value;
+#pragma unroll
+    for (int ni = 0; ni < NSUB; ++ni) {
+      const int r = ni * 32 + col_in;
+      if constexpr (RB >= 16) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const int piece = (gi * (G::ROW / 16) + hh * G::READS + kh * RT + t) ^ piece_swizzle<G::SEG>(r);
+          bc[ni][t] = *(const u32x4*)(st + (b_wave + r * G::SEG + piece * 16));
+        }
+      } else {  // 8 bytes inside one piece
+        const int piece = (gi * (G::ROW / 16) + hh * G::READS) ^ piece_swizzle<G::SEG>(r);
+        const u32x2 v = *(const u32x2*)(st + (b_wave + r * G::SEG + piece * 16 + kh * 8));
+        bc[ni][0] = u32x4{v.x, v.y, 0u, 0u};
+      }
+      if constexpr (BITS != 16) {
+        const int off = sc_wave + ni * C::SC_REGION + col_in * 4 + gi * 2;
+        sv[ni] = *(const uint16_t*)(st + off);
+        bv[ni] = *(const uint16_t*)(st + (off + NSUB * C::SC_REGION));
+      } else {
+        sv[ni] = bv[ni] = 0;
+      }
+    }
+  };
+  // A fragments of group gi, k-step kh*JW + jj of the group
+  // msv: 32-row subtiles holding rows of the tile (wave-uniform); the
+  // eight-wave loop skips the others' reads and MFMAs
+  const int msv = __builtin_amdgcn_readfirstlane(min(MS, (rows + 31) / 32));
+  auto read_a = [&](const uint8_t* st, auto GI_, auto JJ_, f16x8 (&af)[MS], bool skip = false)
+                    __attribute__((always_inline)) {
+    constexpr int gi = decltype(GI_)::value, jj = decltype(JJ_)::value;
+#pragma unroll
+    for (int mi = 0; mi < MS; ++mi) {
+      if (skip && mi > 0 && mi >= msv) break;
+      const int row = mi * 32 + col_in;
+      const int piece = (4 * hh + kh * JW + jj) ^ piece_swizzle<128>(row);
+      af[mi] = *(const f16x8*)(st + (gi * C::A_SUB + row * 128 + (piece << 4)));
+    }
+  };
+  auto deq = [&](const Codes& bc, const uint32_t (&sv)[NSUB], const uint32_t (&bv)[NSUB], auto JJ_,
+                 f16x8 (&bf)[NSUB]) __attribute__((always_inline)) {
+    constexpr int jj = decltype(JJ_)::value;
+#pragma unroll
+    for (int ni = 0; ni < NSUB; ++ni) bf[ni] = dequant_b<BITS>(bc[ni], jj, sv[ni], bv[ni], qc);
+  };
+  auto mma = [&](const f16x8 (&af)[MS], const f16x8 (&bf)[NSUB], bool skip = false) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < MS; ++mi) {
+      if (skip && mi > 0 && mi >= msv) break;
+#pragma unroll
+      for (int ni = 0; ni < NSUB; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+  // One stage, one wave per column block: 4 KG MFMA k-steps.  A fragments
+  // are read two k-steps ahead and weights dequantised one ahead of the
+  // MFMAs, so LDS latency and the dequantisation overlap the matrix cores;
   // each group's weight codes and scales are read one group ahead.
   auto compute = [&](auto S_) __attribute__((always_inline)) {
-    // LDS addresses are formed as one integer offset from the stage array:
-    // the compiler attributes an access to its array (and so knows it does
-    // not wait on loads landing in other stages) only through a short chain
-    // of address arithmetic on the array itself
     const uint8_t* st = stage(S_);
     constexpr int NJ = JW * KG;
-    // this wave's share of a lane's code bytes of a group: RB bytes (its JW
-    // k-steps) at byte kh*RB of the lane's half of the group
-    constexpr int RB = G::HALF / KS;
-    constexpr int RT = RB >= 16 ? RB / 16 : 1;
-    u32x4 bc[KG][NSUB][RT];
+    constexpr int PD = 2;
+    Codes bc[KG];
     uint32_t sv[KG][NSUB], bv[KG][NSUB];
-    auto read_group = [&](auto GI_) __attribute__((always_inline)) {
-      constexpr int gi = decltype(GI_)::value;
-#pragma unroll
-      for (int ni = 0; ni < NSUB; ++ni) {
-        const int r = ni * 32 + col_in;
-        if constexpr (RB >= 16) {
-#pragma unroll
-          for (int t = 0; t < RT; ++t) {
-            const int piece = (gi * (G::ROW / 16) + hh * G::READS + kh * RT + t) ^ piece_swizzle<G::SEG>(r);
-            bc[gi][ni][t] = *(const u32x4*)(st + (b_wave + r * G::SEG + piece * 16));
-          }
-        } else {  // 8 bytes inside one piece
-          const int piece = (gi * (G::ROW / 16) + hh * G::READS) ^ piece_swizzle<G::SEG>(r);
-          const u32x2 v = *(const u32x2*)(st + (b_wave + r * G::SEG + piece * 16 + kh * 8));
-          bc[gi][ni][0] = u32x4{v.x, v.y, 0u, 0u};
-        }
-        if constexpr (BITS != 16) {
-          const int off = sc_wave + ni * C::SC_REGION + col_in * 4 + gi * 2;
-          sv[gi][ni] = *(const uint16_t*)(st + off);
-          bv[gi][ni] = *(const uint16_t*)(st + (off + NSUB * C::SC_REGION));
-        } else {
-          sv[gi][ni] = bv[gi][ni] = 0;
-        }
-      }
-    };
-    // k-step s2 of the stage: group s2 / JW, k-step kh*JW + s2 % JW of the group
-    auto read_a = [&](auto S2_, f16x8 (&af)[MS]) __attribute__((always_inline)) {
-      constexpr int gi = decltype(S2_)::value / JW, jj = decltype(S2_)::value % JW;
-#pragma unroll
-      for (int mi = 0; mi < MS; ++mi) {
-        const int row = mi * 32 + col_in;
-        const int piece = (4 * hh + kh * JW + jj) ^ piece_swizzle<128>(row);
-        af[mi] = *(const f16x8*)(st + (gi * C::A_SUB + row * 128 + (piece << 4)));
-      }
-    };
-    auto deq = [&](auto S2_, f16x8 (&bf)[NSUB]) __attribute__((always_inline)) {
-      constexpr int gi = decltype(S2_)::value / JW, jj = decltype(S2_)::value % JW;
-#pragma unroll
-      for (int ni = 0; ni < NSUB; ++ni) bf[ni] = dequant_b<BITS>(bc[gi][ni], jj, sv[gi][ni], bv[gi][ni], qc);
-    };
-    f16x8 af[2][MS], bf[2][NSUB];
-    read_group(IC<0>{});
-    read_a(IC<0>{}, af[0]);
-    deq(IC<0>{}, bf[0]);
+    f16x8 af[PD + 1][MS], bf[2][NSUB];
+    read_codes(st, IC<0>{}, bc[0], sv[0], bv[0]);
+    for_stages<0, (PD < NJ ? PD : NJ)>([&](auto P_) __attribute__((always_inline)) {
+      constexpr int p = decltype(P_)::value;
+      read_a(st, IC<p / JW>{}, IC<p % JW>{}, af[p]);
+      return true;
+    });
+    deq(bc[0], sv[0], bv[0], IC<0>{}, bf[0]);
     for_stages<0, NJ>([&](auto S2_) __attribute__((always_inline)) {
       constexpr int s2 = decltype(S2_)::value;
       constexpr int c = s2 & 1;
-      // the reads for k-step s2+1 go out before this k-step's MFMAs (the
-      // scheduler would otherwise sink each read to just before its use)
-      if constexpr (s2 % JW == 0 && s2 / JW + 1 < KG) read_group(IC<s2 / JW + 1>{});
-      if constexpr (s2 + 1 < NJ) read_a(IC<s2 + 1>{}, af[c ^ 1]);
+      // the reads go out before this k-step's MFMAs (the scheduler would
+      // otherwise sink each read to just before its use)
+      if constexpr (s2 % JW == 0 && s2 / JW + 1 < KG)
+        read_codes(st, IC<s2 / JW + 1>{}, bc[s2 / JW + 1], sv[s2 / JW + 1], bv[s2 / JW + 1]);
+      if constexpr (s2 + PD < NJ) read_a(st, IC<(s2 + PD) / JW>{}, IC<(s2 + PD) % JW>{}, af[(s2 + PD) % (PD + 1)]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (s2 + 1 < NJ) deq(IC<s2 + 1>{}, bf[c ^ 1]);
-#pragma unroll
-      for (int mi = 0; mi < MS; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NSUB; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[c][mi], bf[c][ni], acc[mi][ni], 0, 0, 0);
+      if constexpr (s2 + 1 < NJ) {
+        constexpr int n = s2 + 1;
+        deq(bc[n / JW], sv[n / JW], bv[n / JW], IC<n % JW>{}, bf[c ^ 1]);
+      }
+      mma(af[s2 % (PD + 1)], bf[c]);
       __builtin_amdgcn_sched_barrier(0);
       return true;
     });
@@ -502,31 +527,103 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
     __builtin_amdgcn_sched_barrier(0);  // keep each step's loads together, in step order
     return true;
   });
-  // step k = NS*trip + S uses stage S
-  auto step = [&](auto S_, int k) __attribute__((always_inline)) {
-    constexpr int S = decltype(S_)::value;
-    wait_vmcnt<(NS - 2) * C::LOADS>();  // this wave's loads of step k have landed
-    __builtin_amdgcn_s_barrier();       // every wave's have; stage (S-1) is free
-    issue(IC<(S + NS - 1) % NS>{}, k + NS - 1);
-    __builtin_amdgcn_sched_barrier(0);  // the next step's loads go out before this step's MFMAs
-    compute(S_);
-  };
-  // whole trips with no branch inside (one basic block, so no load is moved
-  // away from where it is issued), then the remaining steps
   const int trips = nst / NS;
-  for (int t = 0; t < trips; ++t) {
-    for_stages<0, NS>([&](auto S_) __attribute__((always_inline)) {
-      step(S_, t * NS + decltype(S_)::value);
+  const int rem = nst - trips * NS;
+  if constexpr (KS == 1) {
+    // step k = NS*trip + S uses stage S
+    auto step = [&](auto S_, int k) __attribute__((always_inline)) {
+      constexpr int S = decltype(S_)::value;
+      wait_vmcnt<(NS - 2) * C::LOADS>();  // this wave's loads of step k have landed
+      __builtin_amdgcn_s_barrier();       // every wave's have; stage (S-1) is free
+      issue(IC<(S + NS - 1) % NS>{}, k + NS - 1);
+      __builtin_amdgcn_sched_barrier(0);  // the next step's loads go out before this step's MFMAs
+      compute(S_);
+    };
+    // whole trips with no branch inside (one basic block, so no load is moved
+    // away from where it is issued), then the remaining steps
+    for (int t = 0; t < trips; ++t) {
+      for_stages<0, NS>([&](auto S_) __attribute__((always_inline)) {
+        step(S_, t * NS + decltype(S_)::value);
+        return true;
+      });
+    }
+    for_stages<0, NS - 1>([&](auto S_) __attribute__((always_inline)) {
+      constexpr int S = decltype(S_)::value;
+      if (S >= rem) return false;
+      step(S_, trips * NS + S);
       return true;
     });
+  } else {
+    // Ping-pong: the two waves on a SIMD (same column block, k shares kh = 0
+    // and 1) alternate between preparing a group's fragments (LDS reads,
+    // dequantisation) and multiplying them, and the kh = 1 wave runs one
+    // barrier behind, so while one issues MFMAs the other prepares.  Global
+    // phase 2g is kh = 0 preparing group g, 2g+1 its MFMAs and kh = 1
+    // preparing g, 2g+2 kh = 1's MFMAs.  A stage's loads are waited for one
+    // phase before its first group is prepared, and a stage is refilled only
+    // after the barrier that ends the last preparation reading it.
+    f16x8 paf[JW][MS], pbf[JW][NSUB];
+    auto group = [&](auto S_, auto GI_, int k) __attribute__((always_inline)) {
+      constexpr int S = decltype(S_)::value, gi = decltype(GI_)::value;
+      if constexpr (gi == 0) {
+        issue(IC<(S + NS - 1) % NS>{}, k + NS - 1);  // into the stage of step k-1
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const uint8_t* st = stage(S_);
+      Codes bc;
+      uint32_t sv[NSUB], bv[NSUB];
+      read_codes(st, GI_, bc, sv, bv);
+      for_stages<0, JW>([&](auto J_) __attribute__((always_inline)) {
+        read_a(st, GI_, J_, paf[decltype(J_)::value], true);
+        return true;
+      });
+      for_stages<0, JW>([&](auto J_) __attribute__((always_inline)) {
+        deq(bc, sv, bv, J_, pbf[decltype(J_)::value]);
+        return true;
+      });
+      // the dequantised weights are complete here: the compiler must not sink
+      // their VALU work past the barrier into the MFMA phase
+#pragma unroll
+      for (int jj = 0; jj < JW; ++jj)
+#pragma unroll
+        for (int ni = 0; ni < NSUB; ++ni) asm volatile("" ::"v"(pbf[jj][ni]));
+      if constexpr (gi == KG - 1) wait_vmcnt<(NS - 2) * C::LOADS>();  // step k+1's loads have landed
+      // this wave's reads of the stage are complete before the barrier
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      for_stages<0, JW>([&](auto J_) __attribute__((always_inline)) {
+        mma(paf[decltype(J_)::value], pbf[decltype(J_)::value], true);
+        return true;
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    wait_vmcnt<(NS - 2) * C::LOADS>();  // step 0's loads have landed
+    __builtin_amdgcn_s_barrier();
+    if (kh == 1) __builtin_amdgcn_s_barrier();
+    for (int t = 0; t < trips; ++t) {
+      for_stages<0, NS>([&](auto S_) __attribute__((always_inline)) {
+        for_stages<0, KG>([&](auto GI_) __attribute__((always_inline)) {
+          group(S_, GI_, t * NS + decltype(S_)::value);
+          return true;
+        });
+        return true;
+      });
+    }
+    for_stages<0, NS - 1>([&](auto S_) __attribute__((always_inline)) {
+      constexpr int S = decltype(S_)::value;
+      if (S >= rem) return false;
+      for_stages<0, KG>([&](auto GI_) __attribute__((always_inline)) {
+        group(S_, GI_, trips * NS + S);
+        return true;
+      });
+      return true;
+    });
+    if (kh == 0) __builtin_amdgcn_s_barrier();  // both waves pass the same number of barriers
   }
-  const int rem = nst - trips * NS;
-  for_stages<0, NS - 1>([&](auto S_) __attribute__((always_inline)) {
-    constexpr int S = decltype(S_)::value;
-    if (S >= rem) return false;
-    step(S_, trips * NS + S);
-    return true;
-  });
   wait_vmcnt<0>();  // no load into LDS may land after the workgroup ends
 
   if constexpr (KS == 2) {
@@ -677,9 +774,11 @@ hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const i
   prm.w0 = w0;
   prm.w1 = w1;
   prm.out = out;
+  prm.a_bytes = (uint32_t)(a_rows * K * 2);
   prm.perm8_out = perm8_out ? 1 : 0;
   // per-lane buffer offsets are 32-bit: the operand rows and one expert's weight rows
-  if (a_rows * K * 2 > 0xFFFFFFFFll || w0.stride * (int64_t)K * bits / 8 > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  // (A below 2 GB, so an offset of 2^31 is past its end)
+  if (a_rows * K * 2 > 0x7FFFFFFFll || w0.stride * (int64_t)K * bits / 8 > 0xFFFFFFFFll) return hipErrorInvalidValue;
   prm.m_tiles = max_mtiles;
   if (bits == 4) return launch_bits<4>(mode, bm, prm, st);
   if (bits == 8) return launch_bits<8>(mode, bm, prm, st);
