@@ -161,6 +161,10 @@ def main():
     gate_up = moe.fuse_gate_up(gate, up)  # the caller then frees the separate tensors
     del gate, up
     down = dev_w(inp.down)
+    if bits != 16 and wl["T"] > 1:
+        # one-time repack of scales and biases for the batched path (like the
+        # gate/up fusion, done when the weights are loaded)
+        gate_up, down = moe.pack_sb(gate_up), moe.pack_sb(down)
     torch.cuda.synchronize()
 
     T = wl["T"]

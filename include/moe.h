@@ -95,6 +95,17 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
  *
  * group_size must be 64.  K must be a multiple of 64.  q, scales and biases
  * must be 16-byte aligned.
+ *
+ * packed_sb (optional, bits 4 and 8): the same scales and biases repacked for
+ * the batched path by moe_pack_sb, pointing at the tensor's (or view's) first
+ * row like q.  Layout: for expert e, group pair p (groups 2p and 2p+1; a
+ * missing last group is 0) and row n, 8 bytes {scale[2p], scale[2p+1],
+ * bias[2p], bias[2p+1]} (fp16) at byte ((e*NP + p)*expert_stride_rows + n)*8,
+ * NP = ceil(K/128).  One step of the batched GEMM then reads a column block's
+ * scales and biases as a few contiguous 128-byte lines instead of one line
+ * per column.  NULL: the batched path repacks them into the workspace on every
+ * call.  The gate and up views of a fused tensor share its packed_sb (the up
+ * view's pointer is the gate view's plus inter*8 bytes).
  */
 typedef struct {
   const void* q;
@@ -106,6 +117,7 @@ typedef struct {
   int32_t bits;
   int32_t group_size;
   int64_t expert_stride_rows;
+  const void* packed_sb;
 } moe_weights;
 
 /*
@@ -200,6 +212,19 @@ moe_status moe_layer_forward(const void* x, moe_dtype dt, int32_t T, int32_t H, 
  */
 moe_status moe_fuse_gate_up(const moe_weights* gate, const moe_weights* up, void* q_out, void* s_out, void* b_out,
                             void* stream);
+
+/*
+ * Bytes of packed_sb for a tensor of E experts, expert_stride_rows rows per
+ * expert and K input columns: E * ceil(K/128) * expert_stride_rows * 8.
+ */
+size_t moe_packed_sb_bytes(int32_t E, int64_t expert_stride_rows, int32_t K);
+/*
+ * Write w's scales and biases in the packed_sb layout (see moe_weights) to
+ * out (caller-owned, moe_packed_sb_bytes, 16-byte aligned), rows [0, N) of
+ * every expert at w->expert_stride_rows rows per expert.  Enqueued on
+ * `stream`.  MOE_ERR_QUANT for bits 16 (no scales).
+ */
+moe_status moe_pack_sb(const moe_weights* w, void* out, void* stream);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);

@@ -32,7 +32,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
           -9: "MOE_ERR_DEVICE", -10: "MOE_ERR_HIP", -11: "MOE_ERR_INTERNAL"}
 
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_topk_from_logits", "moe_layer_workspace_size",
-           "moe_layer_forward", "moe_fuse_gate_up", "moe_status_string", "moe_debug_set_events",
+           "moe_layer_forward", "moe_fuse_gate_up", "moe_packed_sb_bytes", "moe_pack_sb", "moe_status_string",
+           "moe_debug_set_events",
            "moe_debug_last_plan", "moe_debug_set_tuning")
 
 
@@ -46,7 +47,7 @@ class MoeError(RuntimeError):
 class CWeights(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bits", ctypes.c_int32),
-                ("group_size", ctypes.c_int32), ("expert_stride_rows", ctypes.c_int64)]
+                ("group_size", ctypes.c_int32), ("expert_stride_rows", ctypes.c_int64), ("packed_sb", ctypes.c_void_p)]
 
 
 class CTaps(ctypes.Structure):
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
     L.moe_layer_forward.restype = i32
     L.moe_fuse_gate_up.argtypes = [ctypes.POINTER(CWeights), ctypes.POINTER(CWeights), vp, vp, vp, vp]
     L.moe_fuse_gate_up.restype = i32
+    L.moe_packed_sb_bytes.argtypes = [i32, ctypes.c_int64, i32]
+    L.moe_packed_sb_bytes.restype = sz
+    L.moe_pack_sb.argtypes = [ctypes.POINTER(CWeights), vp, vp]
+    L.moe_pack_sb.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_debug_set_events.argtypes = [vp, i32]
@@ -131,6 +136,8 @@ class Weights:
     [E, N, K].  scales/biases float16 [E, N, K/64] (None for bits 16).
     ``row_offset``/``stride`` describe a view (the gate or up half of a fused
     tensor): rows start ``row_offset`` rows in, experts are ``stride`` rows apart.
+    ``packed_sb`` (optional, uint8): the scales and biases repacked by pack_sb
+    for the batched path (the whole tensor's; views share it).
     """
 
     q: torch.Tensor
@@ -143,6 +150,7 @@ class Weights:
     group_size: int = 64
     stride: Optional[int] = None
     row_offset: int = 0
+    packed_sb: Optional[torch.Tensor] = None
 
     _cstruct: Optional[CWeights] = dataclasses.field(default=None, repr=False, compare=False)
 
@@ -155,7 +163,8 @@ class Weights:
         q = self.q.data_ptr() + self.row_offset * rb
         s = None if self.scales is None else self.scales.data_ptr() + self.row_offset * ng * 2
         b = None if self.biases is None else self.biases.data_ptr() + self.row_offset * ng * 2
-        self._cstruct = CWeights(q, s, b, self.E, self.N, self.K, self.bits, self.group_size, stride)
+        sb = None if self.packed_sb is None else self.packed_sb.data_ptr() + self.row_offset * 8
+        self._cstruct = CWeights(q, s, b, self.E, self.N, self.K, self.bits, self.group_size, stride, sb)
         return self._cstruct
 
     def split_gate_up(self):
@@ -271,6 +280,18 @@ def fuse_gate_up(gate: Weights, up: Weights, stream=None) -> Weights:
     st = lib().moe_fuse_gate_up(ctypes.byref(cg), ctypes.byref(cu), _ptr(q), _ptr(s), _ptr(b), _stream(stream))
     _check(st, "moe_fuse_gate_up")
     return Weights(q, s, b, E, 2 * I, K, bits, gate.group_size)
+
+
+def pack_sb(w: Weights, stream=None) -> Weights:
+    """The same weights with packed_sb filled (scales and biases in the batched
+    path's layout; a one-time repack, like fusing gate and up)."""
+    if w.bits == 16 or w.row_offset != 0:
+        raise ValueError("pack_sb: needs a whole quantised tensor")
+    stride = w.N if w.stride is None else w.stride
+    nbytes = int(lib().moe_packed_sb_bytes(w.E, stride, w.K))
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w.q.device)
+    _check(lib().moe_pack_sb(ctypes.byref(w.c()), _ptr(out), _stream(stream)), "moe_pack_sb")
+    return dataclasses.replace(w, packed_sb=out, _cstruct=None)
 
 
 def debug_set_events(events: Optional[Sequence]) -> None:

@@ -129,4 +129,36 @@ hipError_t launch_copy_words(const void* src, void* dst, int64_t n, hipStream_t 
   return hipGetLastError();
 }
 
+// Scales and biases [rows, ng] (fp16, rows e*src_stride + n) -> the packed
+// layout of the batched path: 8 bytes {s[2p], s[2p+1], b[2p], b[2p+1]} per
+// (expert e, group pair p, row n) at ((e*NP + p)*dst_stride + dst_row0 + n)*8;
+// a group past ng is 0.  One thread per element, rows fastest (coalesced
+// stores).
+__global__ __launch_bounds__(256) void pack_sb_kernel(const uint16_t* __restrict__ s, const uint16_t* __restrict__ b,
+                                                      int N, int ng, int NP, int64_t src_stride, uint8_t* dst,
+                                                      int64_t dst_stride, int64_t dst_row0, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int n = (int)(i % N);
+  const int64_t ep = i / N;  // e*NP + p
+  const int p = (int)(ep % NP);
+  const int64_t e = ep / NP;
+  const int64_t src = (e * src_stride + n) * ng;
+  const int g0 = 2 * p, g1 = 2 * p + 1;
+  const uint32_t s0 = s[src + g0], b0 = b[src + g0];
+  const uint32_t s1 = g1 < ng ? s[src + g1] : 0u, b1 = g1 < ng ? b[src + g1] : 0u;
+  *(u32x2*)(dst + (ep * dst_stride + dst_row0 + n) * 8) = u32x2{s0 | (s1 << 16), b0 | (b1 << 16)};
+}
+
+hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, int K, int64_t src_stride, uint8_t* dst,
+                          int64_t dst_stride, int64_t dst_row0, hipStream_t st) {
+  const int ng = K / 64, NP = (ng + 1) / 2;
+  const int64_t total = (int64_t)E * NP * N;
+  if (total <= 0) return hipSuccess;
+  if ((total + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
+  launch_kernel(pack_sb_kernel, (unsigned)((total + 255) / 256), 256, 0, st, s, b, N, ng, NP, src_stride, dst,
+                dst_stride, dst_row0, total);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -47,6 +47,7 @@ struct GemmParams {
   WView w0, w1;
   void* out;
   uint32_t a_bytes;  // extent of the A rows (offsets at or past it read nothing)
+  int32_t sb_up_delta;  // fused: bytes from a gate column's packed scales to its up column's
   int perm8_out;  // fused: store h blocks in 4-bit unpack order
   // tile order (see tile_of): n_tiles column tiles x m_tiles row tiles, in
   // groups of group_m row tiles; per_xcd consecutive tiles per XCD
@@ -108,12 +109,9 @@ struct GemmCfg {
   static constexpr int A_SUB = BM * 128;  // A of one group: BM rows x 64 fp16
   static constexpr int A_BYTES = KG * A_SUB;
   static constexpr int B_BYTES = 4 * BGeo<BITS, KG, NSUB>::ROWS * BGeo<BITS, KG, NSUB>::SEG;
-  // scales and biases: per column block, tensor and subtile one 64-lane
-  // region, KG fp16 values per lane (lanes 0-31 hold the subtile's columns).
-  // Loads of at most 4 bytes into LDS place lane i at 4 i.
-  static constexpr int SC_LANE = 2 * KG;  // bytes loaded per lane
-  static constexpr int SC_REGION = 64 * 4;
-  static constexpr int SC_BYTES = BITS != 16 ? 4 * 2 * NSUB * SC_REGION : 0;
+  // scales and biases: per column block one 1 KB region (one 64-lane load of
+  // its 32*NSUB columns' packed group pair, repeated over the spare lanes)
+  static constexpr int SC_BYTES = BITS != 16 ? 4 * 1024 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   // 128-row tiles and eight-wave workgroups: one workgroup per CU (160 KB
   // LDS); otherwise two
@@ -123,7 +121,7 @@ struct GemmCfg {
   // vector memory instructions per wave per stage: A, B, scales and biases
   // (the KS waves of a column block split its loads evenly)
   static_assert(MS % KS == 0 && BGeo<BITS, KG, NSUB>::NI % KS == 0, "loads split over the K waves");
-  static constexpr int LOADS = KG * MS / KS + BGeo<BITS, KG, NSUB>::NI / KS + (BITS != 16 ? 2 * NSUB / KS : 0);
+  static constexpr int LOADS = KG * MS / KS + BGeo<BITS, KG, NSUB>::NI / KS + (BITS != 16 ? 1 : 0);
   static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
   static_assert(NS * STAGE <= 159 * 1024, "LDS (160 KB less the tile lookup)");
 };
@@ -338,19 +336,27 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
   };
   const int64_t row_bytes = (int64_t)K * BITS / 8;
   const uint8_t* qbase[NSUB];
-  rsrc_t rsb[2][NSUB];  // scales, biases of each subtile's view
-  uint32_t s_off[NSUB];
 #pragma unroll
   for (int ni = 0; ni < NSUB; ++ni) {
     const WView& v = *view[ni];
-    const int64_t erow = (int64_t)e * v.stride;  // the expert's first row
-    qbase[ni] = v.q + erow * row_bytes;
-    if constexpr (BITS != 16) {
-      rsb[0][ni] = make_rsrc(v.s + erow * ng, 0x80000000u);
-      rsb[1][ni] = make_rsrc(v.b + erow * ng, 0x80000000u);
-    }
-    // lanes 32-63 read past the descriptor's range: no memory access
-    s_off[ni] = lane < 32 ? (uint32_t)column(ni, lane) * (uint32_t)ng * 2u : 0xFFFF0000u;
+    qbase[ni] = v.q + (int64_t)e * v.stride * row_bytes;  // the expert's first row
+  }
+  // ---- scales and biases (packed_sb layout: 8 bytes per column and group
+  // pair, columns contiguous): one load per step, lane l takes the 16 bytes
+  // of columns 2(c%16), 2(c%16)+1 of subtile c/16, c = l % (16 NSUB); the up
+  // columns of the fused tensor lie sb_up_delta bytes after the gate columns
+  const int np = (ng + 1) / 2;
+  const int64_t sb_expert = (int64_t)np * prm.w0.sb_stride * 8;
+  const rsrc_t rsb = make_rsrc(prm.w0.sb + (BITS != 16 ? e * sb_expert : 0), (uint32_t)sb_expert);
+  uint32_t sb_off;
+  {
+    const int c = lane % (16 * NSUB), ni = c / 16;
+    uint32_t off = 0;
+#pragma unroll
+    for (int n2 = 0; n2 < NSUB; ++n2)
+      if (n2 == ni) off = (uint32_t)column(n2, 2 * (c % 16)) * 8u;
+    if (MODE == GEMM_FUSED_SWIGLU && ni >= HALFSUB) off += (uint32_t)prm.sb_up_delta;
+    sb_off = off;
   }
   // this wave's weight load instructions: q = q0 + qq, qq < NI / KS (the K
   // waves of a column block split its loads); q0 and the subtile of an
@@ -381,10 +387,8 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  // the scale regions this wave loads: KS == 1 both tensors, else one each
-  constexpr int T_PER_WAVE = 2 / KS;
-  const int t0 = kh;
-  const int sc_wave = C::A_BYTES + C::B_BYTES + wn * 2 * NSUB * C::SC_REGION;
+  // this column block's scale region (both waves of a K split load it, alike)
+  const int sc_wave = C::A_BYTES + C::B_BYTES + wn * 1024;
   const int b_wave = C::A_BYTES + wn * G::ROWS * G::SEG;  // this wave's B codes
   const int last = nst - 1;
   // step k (groups KG k .. KG k + KG - 1; clamped to the last step) into stage S
@@ -405,16 +409,8 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
       dma16(rq[qq], b_off[qq], (uint32_t)k * G::SEG, st + lds_off);
     }
     if constexpr (BITS != 16) {
-#pragma unroll
-      for (int tt = 0; tt < T_PER_WAVE; ++tt)
-#pragma unroll
-        for (int ni = 0; ni < NSUB; ++ni) {
-          const int t = t0 + tt;
-          const int lds_off = sc_wave + (t * NSUB + ni) * C::SC_REGION;
-          const rsrc_t r = KS == 1 ? rsb[tt][ni] : (t == 0 ? rsb[0][ni] : rsb[1][ni]);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(st + lds_off), C::SC_LANE, s_off[ni],
-                                                   (uint32_t)k * C::SC_LANE, 0, 0);
-        }
+      const uint32_t pair = KG == 2 ? (uint32_t)k : (uint32_t)k >> 1;  // group pair of the step
+      dma16(rsb, sb_off, pair * (uint32_t)prm.w0.sb_stride * 8u, st + sc_wave);
     }
   };
   // ---- reading a stage.  LDS addresses are formed as one integer offset
@@ -427,8 +423,9 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
   constexpr int RB = G::HALF / KS;
   constexpr int RT = RB >= 16 ? RB / 16 : 1;
   typedef u32x4 Codes[NSUB][RT];
-  auto read_codes = [&](const uint8_t* st, auto GI_, Codes& bc, uint32_t (&sv)[NSUB], uint32_t (&bv)[NSUB])
-                        __attribute__((always_inline)) {
+  // kodd: odd step (one-group stages take the second group of the pair)
+  auto read_codes = [&](const uint8_t* st, auto GI_, Codes& bc, uint32_t (&sv)[NSUB], uint32_t (&bv)[NSUB],
+                        bool kodd) __attribute__((always_inline)) {
     constexpr int gi = decltype(GI_)::value;
 #pragma unroll
     for (int ni = 0; ni < NSUB; ++ni) {
@@ -445,9 +442,10 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
         bc[ni][0] = u32x4{v.x, v.y, 0u, 0u};
       }
       if constexpr (BITS != 16) {
-        const int off = sc_wave + ni * C::SC_REGION + col_in * 4 + gi * 2;
-        sv[ni] = *(const uint16_t*)(st + off);
-        bv[ni] = *(const uint16_t*)(st + (off + NSUB * C::SC_REGION));
+        const u32x2 sb = *(const u32x2*)(st + (sc_wave + (ni * 16 + col_in / 2) * 16 + (col_in & 1) * 8));
+        const bool hi = KG == 2 ? gi == 1 : kodd;
+        sv[ni] = hi ? sb.x >> 16 : sb.x & 0xFFFFu;
+        bv[ni] = hi ? sb.y >> 16 : sb.y & 0xFFFFu;
       } else {
         sv[ni] = bv[ni] = 0;
       }
@@ -488,14 +486,15 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
   // are read two k-steps ahead and weights dequantised one ahead of the
   // MFMAs, so LDS latency and the dequantisation overlap the matrix cores;
   // each group's weight codes and scales are read one group ahead.
-  auto compute = [&](auto S_) __attribute__((always_inline)) {
+  auto compute = [&](auto S_, int k) __attribute__((always_inline)) {
+    const bool kodd = (k & 1) != 0;
     const uint8_t* st = stage(S_);
     constexpr int NJ = JW * KG;
     constexpr int PD = 2;
     Codes bc[KG];
     uint32_t sv[KG][NSUB], bv[KG][NSUB];
     f16x8 af[PD + 1][MS], bf[2][NSUB];
-    read_codes(st, IC<0>{}, bc[0], sv[0], bv[0]);
+    read_codes(st, IC<0>{}, bc[0], sv[0], bv[0], kodd);
     for_stages<0, (PD < NJ ? PD : NJ)>([&](auto P_) __attribute__((always_inline)) {
       constexpr int p = decltype(P_)::value;
       read_a(st, IC<p / JW>{}, IC<p % JW>{}, af[p]);
@@ -508,7 +507,7 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
       // the reads go out before this k-step's MFMAs (the scheduler would
       // otherwise sink each read to just before its use)
       if constexpr (s2 % JW == 0 && s2 / JW + 1 < KG)
-        read_codes(st, IC<s2 / JW + 1>{}, bc[s2 / JW + 1], sv[s2 / JW + 1], bv[s2 / JW + 1]);
+        read_codes(st, IC<s2 / JW + 1>{}, bc[s2 / JW + 1], sv[s2 / JW + 1], bv[s2 / JW + 1], kodd);
       if constexpr (s2 + PD < NJ) read_a(st, IC<(s2 + PD) / JW>{}, IC<(s2 + PD) % JW>{}, af[(s2 + PD) % (PD + 1)]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (s2 + 1 < NJ) {
@@ -537,7 +536,7 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
       __builtin_amdgcn_s_barrier();       // every wave's have; stage (S-1) is free
       issue(IC<(S + NS - 1) % NS>{}, k + NS - 1);
       __builtin_amdgcn_sched_barrier(0);  // the next step's loads go out before this step's MFMAs
-      compute(S_);
+      compute(S_, k);
     };
     // whole trips with no branch inside (one basic block, so no load is moved
     // away from where it is issued), then the remaining steps
@@ -572,7 +571,7 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
       const uint8_t* st = stage(S_);
       Codes bc;
       uint32_t sv[NSUB], bv[NSUB];
-      read_codes(st, GI_, bc, sv, bv);
+      read_codes(st, GI_, bc, sv, bv, (k & 1) != 0);
       for_stages<0, JW>([&](auto J_) __attribute__((always_inline)) {
         read_a(st, GI_, J_, paf[decltype(J_)::value], true);
         return true;
@@ -775,6 +774,17 @@ hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const i
   prm.w1 = w1;
   prm.out = out;
   prm.a_bytes = (uint32_t)(a_rows * K * 2);
+  prm.sb_up_delta = 0;
+  if (bits != 16) {
+    if (!w0.sb || !w1.sb) return hipErrorInvalidValue;
+    const int64_t delta = w1.sb - w0.sb;
+    if (mode == GEMM_FUSED_SWIGLU) {
+      // both halves under one descriptor: the up half after the gate half
+      if (delta < 0 || delta > 0x7FFFFFFFll || w0.sb_stride != w1.sb_stride) return hipErrorInvalidValue;
+      prm.sb_up_delta = (int32_t)delta;
+    }
+    if ((int64_t)((K / 64 + 1) / 2) * w0.sb_stride * 8 > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  }
   prm.perm8_out = perm8_out ? 1 : 0;
   // per-lane buffer offsets are 32-bit: the operand rows and one expert's weight rows
   // (A below 2 GB, so an offset of 2^31 is past its end)

@@ -49,6 +49,8 @@ struct WView {
   const uint16_t* s;  // fp16 scales [rows, K/64] (NULL for bits 16)
   const uint16_t* b;  // fp16 biases
   int64_t stride;     // rows between experts
+  const uint8_t* sb;  // scales and biases in the packed_sb layout (batched path)
+  int64_t sb_stride;  // rows between experts in sb
 };
 
 // ---------------------------------------------------------------- router
@@ -125,5 +127,9 @@ hipError_t launch_gather_rows(const uint16_t* src, const int32_t* pos, int64_t P
                               const int32_t* k_used_dev, int k_static, bool perm8, hipStream_t st);
 // copy n int32/fp32 words
 hipError_t launch_copy_words(const void* src, void* dst, int64_t n, hipStream_t st);
+// scales/biases of rows [0, N) of E experts -> packed_sb layout (see moe.h)
+hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, int K, int64_t src_stride, uint8_t* dst,
+                          int64_t dst_stride, int64_t dst_row0, hipStream_t st);
+inline int64_t packed_sb_bytes(int E, int64_t stride, int K) { return (int64_t)E * ((K / 64 + 1) / 2) * stride * 8; }
 
 }  // namespace moe

@@ -112,6 +112,7 @@ moe_status check_weights(const moe_weights* w, int E, int N, int K) {
   if (w->K % 64 != 0 || w->expert_stride_rows < w->N) return MOE_ERR_SHAPE;
   if (!aligned16(w->q)) return MOE_ERR_ALIGN;
   if (w->bits != 16 && (!aligned16(w->scales) || !aligned16(w->biases))) return MOE_ERR_ALIGN;
+  if (w->packed_sb && (w->bits == 16 || !aligned16(w->packed_sb))) return w->bits == 16 ? MOE_ERR_QUANT : MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -138,7 +139,7 @@ bool compatible(const moe_weights* a, const moe_weights* b) {
 // ------------------------------------------------------------ workspace --
 
 struct Layout {
-  size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, a16, hent, g32, u32, total;
+  size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, a16, hent, sbgu, sbd, g32, u32, total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t flags) {
@@ -162,6 +163,9 @@ Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t
   L.o = take((size_t)(P * H * 2));
   L.a16 = take((size_t)(T * H * 2));  // batched path: the activations as the GEMM's fp16 operand
   L.hent = take((size_t)(T * 4));     // adaptive k: per-token entropies
+  // batched path: scales and biases repacked when the weights carry no packed_sb
+  L.sbgu = take((size_t)moe::packed_sb_bytes((int)E, 2 * I, (int)H));
+  L.sbd = take((size_t)moe::packed_sb_bytes((int)E, H, (int)I));
   if (flags & MOE_FLAG_UNFUSED) {
     L.g32 = take((size_t)(P * I * 4));
     L.u32 = take((size_t)(P * I * 4));
@@ -178,6 +182,8 @@ WView view_of(const moe_weights* w, int64_t row_offset) {
   v.s = w->scales ? (const uint16_t*)w->scales + row_offset * ng : nullptr;
   v.b = w->biases ? (const uint16_t*)w->biases + row_offset * ng : nullptr;
   v.stride = w->expert_stride_rows;
+  v.sb = (const uint8_t*)w->packed_sb;
+  v.sb_stride = w->expert_stride_rows;
   return v;
 }
 
@@ -318,6 +324,19 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       plan_step("prep_a", st);
       a16 = a16w;
     }
+    // the gate and up scales in one packed_sb, up rows inter rows after gate
+    // rows (the GEMM reads both halves with one descriptor)
+    if (bits != 16 && !(gate_up && gate_up->packed_sb)) {
+      uint8_t* sb = W + L.sbgu;
+      HIP_TRY(moe::launch_pack_sb(wg.s, wg.b, E, I, H, wg.stride, sb, 2 * I, 0, st));
+      HIP_TRY(moe::launch_pack_sb(wu.s, wu.b, E, I, H, wu.stride, sb, 2 * I, I, st));
+      plan_step("pack_sb_gate_up", st);
+      wg.sb = sb;
+      wu.sb = sb + (size_t)I * 8;
+      wg.sb_stride = wu.sb_stride = 2 * I;
+    } else if (bits != 16) {
+      wu.sb = wg.sb + (size_t)I * 8;  // the fused tensor's packed_sb, up half
+    }
     if (!unfused) {
       HIP_TRY(moe::launch_gemm(moe::GEMM_FUSED_SWIGLU, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wg, wu, h,
                                perm8, bm, mt, st));
@@ -332,7 +351,14 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, perm8, st));
       plan_step("swiglu", st);
     }
-    const WView wd = view_of(down, 0);
+    WView wd = view_of(down, 0);
+    if (bits != 16 && !wd.sb) {
+      uint8_t* sb = W + L.sbd;
+      HIP_TRY(moe::launch_pack_sb(wd.s, wd.b, E, H, I, wd.stride, sb, H, 0, st));
+      plan_step("pack_sb_down", st);
+      wd.sb = sb;
+      wd.sb_stride = H;
+    }
     HIP_TRY(moe::launch_gemm(moe::GEMM_ROWS_F16, h, P, perm, counts, offsets, kcap, E, I, H, bits, wd, wd, o, false, bm,
                              mt, st));
     plan_step("gemm_down", st);
@@ -467,6 +493,27 @@ moe_status moe_layer_forward(const void* x, moe_dtype dt, int32_t T, int32_t H, 
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
+}
+
+size_t moe_packed_sb_bytes(int32_t E, int64_t expert_stride_rows, int32_t K) {
+  if (E < 1 || expert_stride_rows < 1 || K < 64 || K % 64 != 0) return 0;
+  return (size_t)moe::packed_sb_bytes(E, expert_stride_rows, K);
+}
+
+moe_status moe_pack_sb(const moe_weights* w, void* out, void* stream) {
+  if (!w || !out) return MOE_ERR_NULL;
+  if (w->bits == 16) return MOE_ERR_QUANT;
+  moe_status s = check_weights(w, w->E, w->N, w->K);
+  if (s != MOE_OK) return s;
+  if (!aligned16(out)) return MOE_ERR_ALIGN;
+  DevProps props;
+  if ((s = device_props(&props)) != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  plan_begin(st);
+  HIP_TRY(moe::launch_pack_sb((const uint16_t*)w->scales, (const uint16_t*)w->biases, w->E, w->N, w->K,
+                              w->expert_stride_rows, (uint8_t*)out, w->expert_stride_rows, 0, st));
+  plan_step("pack_sb", st);
+  return MOE_OK;
 }
 
 moe_status moe_fuse_gate_up(const moe_weights* gate, const moe_weights* up, void* q_out, void* s_out, void* b_out,

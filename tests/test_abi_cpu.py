@@ -44,9 +44,9 @@ def test_status_strings():
     assert L.moe_status_string(12345).decode() == "unknown status"
 
 
-def W(E, N, K, bits=4, q=P, s=P, b=P, gs=64, stride=None):
+def W(E, N, K, bits=4, q=P, s=P, b=P, gs=64, stride=None, sb=None):
     return moe.CWeights(q, None if bits == 16 else s, None if bits == 16 else b, E, N, K, bits, gs,
-                        N if stride is None else stride)
+                        N if stride is None else stride, sb)
 
 
 def fwd(T=4, H=256, E=8, k=2, I=128, dt=moe.MOE_F16, x=P, wr=P, y=P, gu="fused", gate=None, up=None, down=None,
@@ -96,6 +96,8 @@ def test_zero_tokens_is_a_noop():
     (dict(gu=W(8, 2 * 128, 256, stride=100)), "MOE_ERR_SHAPE"),
     (dict(gu=W(8, 2 * 128, 256, bits=8)), "MOE_ERR_QUANT"),
     (dict(down=W(8, 256, 128, bits=16)), "MOE_ERR_QUANT"),
+    (dict(gu=W(8, 2 * 128, 256, sb=P + 8)), "MOE_ERR_ALIGN"),
+    (dict(down=W(8, 256, 128, sb=P + 4)), "MOE_ERR_ALIGN"),
 ])
 def test_validation_errors(kw, status):
     assert moe.STATUS[fwd(**kw)] == status
@@ -113,6 +115,23 @@ def test_separate_gate_up_must_be_compatible():
     assert moe.STATUS[fwd(gu=None, gate=ok, up=W(8, 128, 256, gs=32))] == "MOE_ERR_INCOMPATIBLE"
     assert moe.STATUS[fwd(gu=None, gate=ok, up=W(8, 64, 256))] == "MOE_ERR_INCOMPATIBLE"
     assert moe.STATUS[fwd(gu=None, gate=ok, up=None)] == "MOE_ERR_NULL"
+
+
+def test_packed_sb_size_and_validation():
+    L = moe.lib()
+    # E * ceil(K/128) * rows * 8: odd group counts round up to a pair
+    assert L.moe_packed_sb_bytes(8, 256, 256) == 8 * 2 * 256 * 8
+    assert L.moe_packed_sb_bytes(4, 100, 192) == 4 * 2 * 100 * 8
+    assert L.moe_packed_sb_bytes(64, 2816, 4096) == 64 * 32 * 2816 * 8
+    assert L.moe_packed_sb_bytes(0, 256, 256) == 0 and L.moe_packed_sb_bytes(8, 256, 100) == 0
+    w = W(8, 256, 256)
+    assert moe.STATUS[L.moe_pack_sb(ctypes.byref(w), None, None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[L.moe_pack_sb(None, P, None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[L.moe_pack_sb(ctypes.byref(w), P + 8, None)] == "MOE_ERR_ALIGN"
+    w16 = W(8, 256, 256, bits=16)
+    assert moe.STATUS[L.moe_pack_sb(ctypes.byref(w16), P, None)] == "MOE_ERR_QUANT"
+    bad = W(8, 256, 200)
+    assert moe.STATUS[L.moe_pack_sb(ctypes.byref(bad), P, None)] == "MOE_ERR_SHAPE"
 
 
 def test_fuse_gate_up_validation():

@@ -143,6 +143,39 @@ def test_gemm_launch_shapes_are_bit_identical(name, built):
     assert np.linalg.norm(a - b) <= 5e-3 * np.linalg.norm(a)
 
 
+def _packed_reference(w):
+    """packed_sb layout written out with numpy from the host copies."""
+    E, N, ng = w.scales.shape
+    NP = (ng + 1) // 2
+    pad = lambda a: np.concatenate([a, np.zeros((E, N, 1), np.uint16)], axis=2) if ng % 2 else a
+    s, b = pad(w.scales), pad(w.biases)
+    out = np.zeros((E, NP, N, 4), np.uint16)
+    out[..., 0] = s[:, :, 0::2].transpose(0, 2, 1)
+    out[..., 1] = s[:, :, 1::2].transpose(0, 2, 1)
+    out[..., 2] = b[:, :, 0::2].transpose(0, 2, 1)
+    out[..., 3] = b[:, :, 1::2].transpose(0, 2, 1)
+    return out
+
+
+@pytest.mark.parametrize("name", ["prefill_small", "tiny_q8_bf16", "ragged_shapes", "entropy_q4"])
+def test_packed_sb_layout_and_bit_identity(name, built):
+    inp, gu_np, dev = built(name)
+    down = moe.pack_sb(dev.down)
+    gate_up = moe.pack_sb(dev.gate_up)
+    torch.cuda.synchronize()
+    E, N, ng = inp.down.scales.shape
+    got = down.packed_sb.cpu().numpy().view(np.uint16).reshape(E, (ng + 1) // 2, N, 4)
+    assert np.array_equal(got, _packed_reference(inp.down))
+    got = gate_up.packed_sb.cpu().numpy().view(np.uint16).reshape(E, -1, 2 * inp.I, 4)
+    assert np.array_equal(got, _packed_reference(gu_np))
+    # the batched path gives the same bits whether it repacks per call or not
+    for flags in (moe.FLAG_FORCE_MFMA, moe.FLAG_FORCE_MFMA | moe.FLAG_UNFUSED):
+        y0 = host_bits(dev.forward(flags=flags))
+        y1 = moe.layer_forward(dev.x, dev.wr, inp.k, down, gate_up=gate_up, flags=flags)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(y1), y0), flags
+
+
 def test_runs_are_deterministic(built):
     inp, _, dev = built("prefill_small")
     a, _ = _run(dev, 0)
