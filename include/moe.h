@@ -249,8 +249,8 @@ int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
  * from the batch), key 4 = K groups of 64 per pipeline stage (1; other
  * values: 2 where the stage fits in LDS), key 5 = 32-column subtiles per wave
  * at the 128-row tile (4; other values: 2), key 6 = waves per column block at
- * the 64- and 128-row tiles (1; other values: 2, splitting each group's
- * k-steps).
+ * the 64- and 128-row tiles (2, splitting each group's k-steps; other values:
+ * 1).
  * Values <= 0 are ignored.  Results do not depend on them.
  */
 void moe_debug_set_tuning(int32_t key, int32_t value);

@@ -79,9 +79,12 @@ __device__ __forceinline__ bool tile_of(const GemmParams& prm, int bid, int& n, 
 int gemm_block_m(int P, int E) {
   const int forced = tuning(TUNE_GEMM_BM);
   if (forced == 32 || forced == 64 || forced == 128) return forced;
+  // measured on MI355X: 32-row tiles up to ~64 pairs per expert, 64-row
+  // tiles (two workgroups per CU) beyond; 128-row tiles only for very large
+  // batches, where the per-tile weight traffic dominates
   const int avg = E > 0 ? P / E : P;
-  if (avg <= 32) return 32;
-  if (avg <= 96) return 64;
+  if (avg <= 64) return 32;
+  if (avg <= 1024) return 64;
   return 128;
 }
 
@@ -724,8 +727,8 @@ static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
   return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB, KS>, grid, 256 * KS, 0, st, prm);
 }
 
-// Row tiles of 64 and 128 run eight waves, two per column block splitting
-// each group's k-steps, unless the tuning knob asks for four.
+// Row tiles of 64 and 128 run four waves, one per column block, or with the
+// tuning knob eight, two per column block splitting each group's k-steps.
 template <int BITS, int MODE, int MS>
 static hipError_t launch_one(const GemmParams& prm, hipStream_t st) {
   // fp16 rows: two stages of four subtiles would not fit in LDS
@@ -733,7 +736,7 @@ static hipError_t launch_one(const GemmParams& prm, hipStream_t st) {
     if (tuning(TUNE_GEMM_NSUB) == 4) return launch_sub<BITS, MODE, MS, 4, 1>(prm, st);
   }
   if constexpr (MS >= 2) {
-    if (tuning(TUNE_GEMM_KSPLIT) != 1) return launch_sub<BITS, MODE, MS, 2, 2>(prm, st);
+    if (tuning(TUNE_GEMM_KSPLIT) == 2) return launch_sub<BITS, MODE, MS, 2, 2>(prm, st);
   }
   return launch_sub<BITS, MODE, MS, 2, 1>(prm, st);
 }

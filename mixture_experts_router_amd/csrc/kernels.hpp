@@ -38,7 +38,7 @@ enum TuneKey {
   TUNE_GEMM_BM = 3,  // 32, 64 or 128 forces the GEMM row tile; anything else: chosen from the batch
   TUNE_GEMM_KG = 4,  // 1: 4-bit GEMM stages one quantisation group per step (default: two when K allows)
   TUNE_GEMM_NSUB = 5,  // 4: 128-row GEMM tiles give each wave 128 columns (default 64)
-  TUNE_GEMM_KSPLIT = 6,  // 1: 64- and 128-row GEMM tiles run four waves (default eight, splitting k)
+  TUNE_GEMM_KSPLIT = 6,  // 2: 64- and 128-row GEMM tiles run eight waves splitting k (default four)
   TUNE_KEYS = 7
 };
 int tuning(TuneKey key);

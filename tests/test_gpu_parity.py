@@ -26,7 +26,7 @@ CASES = {
     "decode_t3": ("decode_b1", dict(T=3, H=512, E=16, I=320)),
     "batched_small": ("batched_decode", dict(T=40, H=512, E=8, I=320)),
     "prefill_small": ("prefill", dict(T=300, H=512, E=16, I=192)),
-    "prefill_bm128": ("prefill", dict(T=640, H=256, E=8, I=384)),
+    "prefill_bm128": ("prefill", dict(T=2304, H=256, E=8, I=384)),
     "entropy_fp16w": ("entropy", dict(T=96, H=512, E=16, I=192, bits=16)),
     "entropy_q4": ("entropy", dict(T=96, H=512, E=16, I=192, bits=4, segment=2)),
     "one_expert": ("tiny", dict(E=1, k=1, T=5)),
@@ -112,7 +112,7 @@ def test_sort_matches_oracle_exactly(name, built):
 # compared with each other within the layer tolerance and each with the oracle
 GEMM_SHAPES = [(32, 2, 2, 1), (64, 1, 2, 1), (64, 2, 2, 2), (64, 1, 2, 2), (128, 1, 2, 1), (128, 2, 2, 1),
                (128, 2, 4, 1), (128, 1, 2, 2), (128, 2, 2, 2)]
-DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2, 6: 2}
+DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2, 6: 1}
 
 
 @pytest.mark.parametrize("name", ["prefill_bm128", "prefill_small", "tiny_q8_bf16", "tiny_fp16w"])
