@@ -250,7 +250,9 @@ int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
  * values: 2 where the stage fits in LDS), key 5 = 32-column subtiles per wave
  * at the 128-row tile (4; other values: 2), key 6 = waves per column block at
  * the 64- and 128-row tiles (2, splitting each group's k-steps; other values:
- * 1).
+ * 1), key 7 = workgroups per CU at the 32- and 64-row tiles (1: the whole LDS
+ * for one, deeper pipeline and two-group 8-bit stages; 2: two; other values:
+ * one for 8-bit weights at 32-row tiles, else two).
  * Values <= 0 are ignored.  Results do not depend on them.
  */
 void moe_debug_set_tuning(int32_t key, int32_t value);

@@ -308,7 +308,8 @@ def debug_set_events(events: Optional[Sequence]) -> None:
 def debug_set_tuning(key: int, value: int) -> None:
     """Launch-shape knob (0: decode gate+up waves/CU, 1: decode down waves/CU, 2: GEMM row tiles per group,
     3: GEMM row tile 32/64/128 (else automatic), 4: GEMM K groups per stage (1 or 2), 5: GEMM N subtiles
-    per wave (2 or 4), 6: GEMM waves per column block (1 or 2))."""
+    per wave (2 or 4), 6: GEMM waves per column block (1 or 2), 7: GEMM workgroups per CU at 32/64-row
+    tiles (1 or 2))."""
     lib().moe_debug_set_tuning(int(key), int(value))
 
 

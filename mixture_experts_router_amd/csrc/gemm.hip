@@ -106,7 +106,8 @@ struct BGeo {
   static constexpr int READS = HALF / 16;    // 16-byte LDS reads per lane, subtile and group
 };
 
-template <int BITS, int MS, int KG, int NSUB, int KS>
+// WPC: workgroups per CU the LDS budget allows (1: 156 KB, 2: 78 KB each)
+template <int BITS, int MS, int KG, int NSUB, int KS, int WPC>
 struct GemmCfg {
   static constexpr int BM = 32 * MS;
   static constexpr int A_SUB = BM * 128;  // A of one group: BM rows x 64 fp16
@@ -116,9 +117,7 @@ struct GemmCfg {
   // its 32*NSUB columns' packed group pair, repeated over the spare lanes)
   static constexpr int SC_BYTES = BITS != 16 ? 4 * 1024 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
-  // 128-row tiles and eight-wave workgroups: one workgroup per CU (160 KB
-  // LDS); otherwise two
-  static constexpr int BUDGET = MS == 4 || KS == 2 ? 156 * 1024 : 78 * 1024;
+  static constexpr int BUDGET = WPC == 1 ? 156 * 1024 : 78 * 1024;
   static constexpr int NS_FIT = BUDGET / STAGE;
   static constexpr int NS = NS_FIT < 2 ? 2 : (NS_FIT > 6 ? 6 : NS_FIT);
   // vector memory instructions per wave per stage: A, B, scales and biases
@@ -215,10 +214,10 @@ __device__ __forceinline__ f16x8 dequant_b(const u32x4* c, int j, uint32_t s_bit
   }
 }
 
-template <int BITS, int MODE, int MS, int KG, int NSUB, int KS>
-__global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_kernel(GemmParams prm) {
+template <int BITS, int MODE, int MS, int KG, int NSUB, int KS, int WPC>
+__global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
   using G = BGeo<BITS, KG, NSUB>;
-  using C = GemmCfg<BITS, MS, KG, NSUB, KS>;
+  using C = GemmCfg<BITS, MS, KG, NSUB, KS, WPC>;
   constexpr int HALFSUB = NSUB / 2;  // fused: subtiles [0, HALFSUB) gate, the rest the matching up
   constexpr int BM = C::BM, NS = C::NS;
   // one array per stage: distinct objects let the compiler see that reading
@@ -711,7 +710,7 @@ __global__ __launch_bounds__(256 * KS, MS == 4 || KS == 2 ? 1 : 2) void gemm_ker
 // One instantiation: each wave owns NSUB subtiles of 32 columns.  4-bit
 // weights stage two groups per step (64-byte row segments) when K allows,
 // unless the tuning knob asks for one.
-template <int BITS, int MODE, int MS, int NSUB, int KS>
+template <int BITS, int MODE, int MS, int NSUB, int KS, int WPC>
 static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
   const int ncols = 4 * 32 * (MODE == GEMM_FUSED_SWIGLU ? NSUB / 2 : NSUB);
   prm.n_tiles = (prm.N + ncols - 1) / ncols;
@@ -720,11 +719,12 @@ static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
   const int64_t total = (int64_t)prm.n_tiles * prm.m_tiles;
   prm.per_xcd = (int)((total + NUM_XCD - 1) / NUM_XCD);
   dim3 grid((unsigned)(prm.per_xcd * NUM_XCD));
-  if constexpr (BITS == 4) {
+  // two-group stages: 4-bit rows, or 8-bit rows with the whole LDS
+  if constexpr (BITS == 4 || (BITS == 8 && WPC == 1 && NSUB == 2 && MS < 4 && KS == 1)) {
     if ((prm.K / 64) % 2 == 0 && tuning(TUNE_GEMM_KG) != 1)
-      return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB, KS>, grid, 256 * KS, 0, st, prm);
+      return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
   }
-  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB, KS>, grid, 256 * KS, 0, st, prm);
+  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
 }
 
 // Row tiles of 64 and 128 run four waves, one per column block, or with the
@@ -733,12 +733,19 @@ template <int BITS, int MODE, int MS>
 static hipError_t launch_one(const GemmParams& prm, hipStream_t st) {
   // fp16 rows: two stages of four subtiles would not fit in LDS
   if constexpr (MS == 4 && BITS != 16) {
-    if (tuning(TUNE_GEMM_NSUB) == 4) return launch_sub<BITS, MODE, MS, 4, 1>(prm, st);
+    if (tuning(TUNE_GEMM_NSUB) == 4) return launch_sub<BITS, MODE, MS, 4, 1, 1>(prm, st);
   }
   if constexpr (MS >= 2) {
-    if (tuning(TUNE_GEMM_KSPLIT) == 2) return launch_sub<BITS, MODE, MS, 2, 2>(prm, st);
+    if (tuning(TUNE_GEMM_KSPLIT) == 2) return launch_sub<BITS, MODE, MS, 2, 2, 1>(prm, st);
   }
-  return launch_sub<BITS, MODE, MS, 2, 1>(prm, st);
+  if constexpr (MS < 4) {
+    // 8-bit weights at 32-row tiles: one workgroup per CU streaming two-group
+    // (128-byte) row segments measured faster than two with one-group stages
+    const int wpc = tuning(TUNE_GEMM_WPC);
+    if (wpc == 1 || (wpc != 2 && MS == 1 && BITS == 8)) return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
+    return launch_sub<BITS, MODE, MS, 2, 1, 2>(prm, st);
+  }
+  return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
 }
 
 template <int BITS, int MODE>

@@ -39,7 +39,8 @@ enum TuneKey {
   TUNE_GEMM_KG = 4,  // 1: 4-bit GEMM stages one quantisation group per step (default: two when K allows)
   TUNE_GEMM_NSUB = 5,  // 4: 128-row GEMM tiles give each wave 128 columns (default 64)
   TUNE_GEMM_KSPLIT = 6,  // 2: 64- and 128-row GEMM tiles run eight waves splitting k (default four)
-  TUNE_KEYS = 7
+  TUNE_GEMM_WPC = 7,  // 1 / 2: workgroups per CU at 32- and 64-row GEMM tiles (other values: by bits and tile)
+  TUNE_KEYS = 8
 };
 int tuning(TuneKey key);
 

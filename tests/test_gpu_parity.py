@@ -106,13 +106,14 @@ def test_sort_matches_oracle_exactly(name, built):
     assert np.array_equal(taps["perm"], perm)
 
 
-# (row tile, K groups per stage, N subtiles per wave, waves per column block):
-# every launch shape of one k split accumulates each output over K in the same
-# order, so the shapes of a split give identical bits; the two splits are
-# compared with each other within the layer tolerance and each with the oracle
-GEMM_SHAPES = [(32, 2, 2, 1), (64, 1, 2, 1), (64, 2, 2, 2), (64, 1, 2, 2), (128, 1, 2, 1), (128, 2, 2, 1),
-               (128, 2, 4, 1), (128, 1, 2, 2), (128, 2, 2, 2)]
-DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2, 6: 1}
+# (row tile, K groups per stage, N subtiles per wave, waves per column block,
+# workgroups per CU): every launch shape of one k split accumulates each
+# output over K in the same order, so the shapes of a split give identical
+# bits; the two splits are compared with each other within the layer tolerance
+GEMM_SHAPES = [(32, 2, 2, 1, 2), (32, 2, 2, 1, 1), (64, 1, 2, 1, 2), (64, 2, 2, 1, 1), (64, 2, 2, 2, 2),
+               (64, 1, 2, 2, 2), (128, 1, 2, 1, 2), (128, 2, 2, 1, 2), (128, 2, 4, 1, 2), (128, 1, 2, 2, 2),
+               (128, 2, 2, 2, 2)]
+DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2, 6: 1, 7: 3}
 
 
 @pytest.mark.parametrize("name", ["prefill_bm128", "prefill_small", "tiny_q8_bf16", "tiny_fp16w"])
@@ -121,8 +122,9 @@ def test_gemm_launch_shapes_are_bit_identical(name, built):
     inp, _, dev = built(name)
     first = {}
     try:
-        for bm, kg, nsub, ks in GEMM_SHAPES:
-            print("case", name, "bm", bm, "kg", kg, "nsub", nsub, "ksplit", ks, flush=True)
+        for bm, kg, nsub, ks, wpc in GEMM_SHAPES:
+            print("case", name, "bm", bm, "kg", kg, "nsub", nsub, "ksplit", ks, "wpc", wpc, flush=True)
+            moe.debug_set_tuning(7, wpc)
             moe.debug_set_tuning(3, bm)
             moe.debug_set_tuning(4, kg)
             moe.debug_set_tuning(5, nsub)
