@@ -34,8 +34,9 @@
 namespace moe {
 
 // Route token t inside a decode kernel: with logits given (static k), every
-// wave recomputes the token's selection (topk.hpp, identical in all kernels)
-// instead of waiting for a separate selection launch.
+// wave of the gate+up kernel selects its slot's expert from the logits
+// (topk.hpp) instead of waiting for a separate selection launch, and block 0
+// of each pair writes the selection, which the down kernel then reads.
 struct RouteSrc {
   const float* logits;  // [T, E] or NULL: read idx/wts
   int E;
@@ -253,15 +254,8 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   if (gw >= prm.iters) return;
   int e;
   if (prm.rt.logits) {
-    int si[MOE_MAX_K_DEV];
-    float sw[MOE_MAX_K_DEV];
-    route_token(prm.rt.logits + (size_t)t * prm.rt.E, prm.rt.E, ku, si, sw);
     float wsel = 0.0f;
-    e = 0;
-    for_slot(slot, [&](int j) {
-      e = si[j];
-      wsel = sw[j];
-    });
+    route_slot(prm.rt.logits + (size_t)t * prm.rt.E, prm.rt.E, ku, slot, e, wsel);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       prm.rt.idx[p] = e;
       prm.rt.wts[p] = wsel;

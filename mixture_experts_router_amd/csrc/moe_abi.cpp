@@ -302,7 +302,12 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, false, st));
       plan_step("swiglu", st);
     }
-    HIP_TRY(moe::launch_gemv_down(h, rt, k_static, kcap, T, H, I, bits, view_of(down, 0), y, act, props.num_cu, st));
+    // the gate+up kernel wrote the selection: the down kernel reads it
+    // instead of selecting again
+    moe::GemvRoute rt_down = rt;
+    rt_down.logits = nullptr;
+    HIP_TRY(moe::launch_gemv_down(h, rt_down, k_static, kcap, T, H, I, bits, view_of(down, 0), y, act, props.num_cu,
+                                  st));
     plan_step("gemv_down_combine", st);
     if (want_sort_taps) {
       HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st));

@@ -1,6 +1,6 @@
 // Top-k selection of one token's logits by one wave (shared by the router
-// kernels and the decode GEMV kernels, which recompute it from the logits so
-// that every kernel sees the same experts and weights).
+// kernels and the decode gate+up GEMV, which selects from the logits itself
+// with the same operations, so every kernel sees the same experts and weights).
 //
 // Key: larger logit first, lower expert index first among equal logits.
 // Weights: exp(l_s - l_1) / sum over the selected slots of exp(l_s' - l_1),
@@ -127,6 +127,48 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     idx[s] = s < k ? si[s] : -1;
     w[s] = s < k ? ex[s] / z : 0.0f;
   }
+}
+
+// The expert and routing weight of one slot of token t (the same values as
+// route_token: z sums exp(l_s - l_1) in slot order), with one selection
+// round per slot in a loop rather than unrolled over MOE_MAX_K slots: a
+// decode kernel runs this before its first weight load, and a short code path
+// is fetched into the instruction cache faster.
+__device__ __forceinline__ void route_slot(const float* __restrict__ row, int E, int k, int slot, int& e_out,
+                                           float& w_out) {
+  const int lane = lane_id();
+  float v[4];
+  bool live[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    live[j] = e < E;
+    v[j] = live[j] ? row[e] : 0.0f;
+  }
+  float v0 = 0.0f, z = 0.0f, mine = 0.0f;
+  int mye = 0;
+#pragma unroll 1
+  for (int s = 0; s < k; ++s) {
+    Cand c = {0.0f, -1};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const Cand d = {v[j], live[j] ? lane + 64 * j : -1};
+      c = better(c, d);
+    }
+    c = wave_best(c);
+    if (s == 0) v0 = c.v;
+    const float ex = expf(c.v - v0);
+    z += ex;
+    if (s == slot) {
+      mye = c.i;
+      mine = ex;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j == c.i) live[j] = false;
+  }
+  e_out = mye;
+  w_out = mine / z;
 }
 
 }  // namespace moe
