@@ -125,7 +125,7 @@ struct GemmCfg {
   static_assert(MS % KS == 0 && BGeo<BITS, KG, NSUB>::NI % KS == 0, "loads split over the K waves");
   static constexpr int LOADS = KG * MS / KS + BGeo<BITS, KG, NSUB>::NI / KS + (BITS != 16 ? 1 : 0);
   static_assert((NS - 2) * LOADS <= 63, "vmcnt range");
-  static_assert(NS * STAGE <= 159 * 1024, "LDS (160 KB less the tile lookup)");
+  static_assert(NS * STAGE <= 159 * 1024, "LDS");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -224,7 +224,6 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
   // a stage does not wait on loads still landing in the others
   __shared__ __attribute__((aligned(16))) uint8_t st0[C::STAGE], st1[C::STAGE], st2[NS > 2 ? C::STAGE : 16],
       st3[NS > 3 ? C::STAGE : 16], st4[NS > 4 ? C::STAGE : 16], st5[NS > 5 ? C::STAGE : 16];
-  __shared__ int s_tile[4];
   auto stage = [&](auto S_) __attribute__((always_inline)) -> uint8_t* {
     constexpr int S = decltype(S_)::value;
     if constexpr (S == 0) return st0;
@@ -240,51 +239,46 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
   const int wn = wave % 4;                    // column block of this wave
   const int kh = KS == 1 ? 0 : wave / 4;      // which share of each group's k-steps
   constexpr int JW = 4 / KS;                  // MFMA k-steps per group and wave
-  const int tid = threadIdx.x;
 
   // ---- which (expert, M tile) this workgroup owns: tiles are numbered
-  // expert by expert, ceil(count/BM) tiles per expert
+  // expert by expert, ceil(count/BM) tiles per expert.  Every wave finds it
+  // itself from one round of loads (counts and offsets together): no LDS
+  // hand-off, no barrier, one memory latency.
   int n_tile = 0, y = 0;
   if (!tile_of(prm, blockIdx.x, n_tile, y)) return;
-  if (tid < WAVE) {
-    int base_tiles = 0, fe = -1, fmt = 0;
+  int e = -1, rows = 0, row0 = 0;
+  {
+    int base_tiles = 0, fe = -1, fmt = 0, fc = 0, fo = 0;
     for (int base = 0; base < prm.E; base += WAVE) {
-      const int e = base + lane;
-      const int c = e < prm.E ? prm.counts[e] : 0;
+      const int ee = base + lane;
+      const int c = ee < prm.E ? prm.counts[ee] : 0;
+      const int o = ee < prm.E ? prm.offsets[ee] : 0;
       const int nt = (c + BM - 1) / BM;
       int incl = nt;
 #pragma unroll
-      for (int o = 1; o < WAVE; o <<= 1) {
-        int v = __shfl_up(incl, o, WAVE);
-        if (lane >= o) incl += v;
+      for (int d = 1; d < WAVE; d <<= 1) {
+        int v = __shfl_up(incl, d, WAVE);
+        if (lane >= d) incl += v;
       }
       const int excl = incl - nt;
       if (nt > 0 && y >= base_tiles + excl && y < base_tiles + incl) {
-        fe = e;
+        fe = ee;
         fmt = y - base_tiles - excl;
+        fc = c;
+        fo = o;
       }
       base_tiles += __shfl(incl, WAVE - 1, WAVE);
     }
     const uint64_t m = __ballot(fe >= 0);
-    if (m == 0) {
-      if (lane == 0) s_tile[0] = -1;
-    } else {
+    if (m != 0) {
       const int src = __ffsll((unsigned long long)m) - 1;
-      const int e = __shfl(fe, src, WAVE);
-      const int mt = __shfl(fmt, src, WAVE);
-      if (lane == 0) {
-        const int m0 = mt * BM;
-        s_tile[0] = e;
-        s_tile[1] = min(BM, prm.counts[e] - m0);
-        s_tile[2] = prm.offsets[e] + m0;
-      }
+      e = __builtin_amdgcn_readlane(fe, src);
+      const int m0 = __builtin_amdgcn_readlane(fmt, src) * BM;
+      rows = min(BM, __builtin_amdgcn_readlane(fc, src) - m0);
+      row0 = __builtin_amdgcn_readlane(fo, src) + m0;
     }
   }
-  __syncthreads();
-  const int e = s_tile[0];
-  if (e < 0) return;
-  const int rows = s_tile[1];
-  const int row0 = s_tile[2];
+  if (e < 0) return;  // the same in every wave of the workgroup
   const int K = prm.K;
   const int ng = K / 64;
   const Q4Consts qc = q4_consts();

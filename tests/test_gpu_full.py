@@ -50,6 +50,15 @@ def _check(inp, gu_np, y, taps, tokens, label):
         assert np.array_equal(taps["counts"], counts) and np.array_equal(taps["perm"], perm)
 
 
+def _assert_packed_same(dev, y):
+    """The benchmark loads its weights with pack_sb: same bits as the per-call repack."""
+    if dev.inp.bits == 16:
+        return
+    gu, dn = moe.pack_sb(dev.gate_up), moe.pack_sb(dev.down)
+    yp = host_bits(moe.layer_forward(dev.x, dev.wr, dev.inp.k, dn, gate_up=gu))
+    assert np.array_equal(yp, y), "prepacked scales vs per-call repack"
+
+
 def test_decode_b1_full_size():
     inp, gu_np, dev = _gen("decode_b1", T=6)
     for t in range(inp.T):
@@ -81,6 +90,7 @@ def test_batched_decode_full_size():
     _check(inp, gu_np, y, taps, np.arange(inp.T), "batched_decode")
     y_u, _, _ = _forward(dev, moe.FLAG_UNFUSED)
     assert np.array_equal(y, y_u)
+    _assert_packed_same(dev, y)
 
 
 def test_prefill_full_size():
@@ -98,6 +108,7 @@ def test_prefill_full_size():
     _check(inp, gu_np, y, taps, tokens, "prefill")
     y_u, _, _ = _forward(dev, moe.FLAG_UNFUSED)
     assert np.array_equal(y, y_u)
+    _assert_packed_same(dev, y)
 
 
 @pytest.mark.parametrize("bits", [16, 4])
@@ -117,3 +128,4 @@ def test_entropy_full_size(bits):
         _check(inp, gu_np, y, taps, tokens, "entropy bits=%d segment %d (k=%d)" % (bits, seg, k_expect))
         y_u, _, _ = _forward(dev, moe.FLAG_UNFUSED)
         assert np.array_equal(y, y_u)
+        _assert_packed_same(dev, y)
