@@ -49,6 +49,12 @@ def _load():
     lib.oracle_dequant_row.argtypes = [vp, vp, vp, i32, i32, i32, vp]
     lib.oracle_router_logits.argtypes = [vp, i32, i32, i32, vp, i32, vp]
     lib.oracle_select_topk.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+    lib.oracle_select_topk_grouped.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.oracle_correct_logits.argtypes = [vp, i32, i32, vp, f32]
+    lib.oracle_load_stats.argtypes = [vp, i32, vp, vp]
+    lib.oracle_route_ex.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, f32, i32, vp, vp, vp, vp, vp]
+    lib.oracle_layer_forward_ex.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, f32, i32, vp, vp, vp, vp, vp, vp,
+                                            i32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.oracle_token_entropy.argtypes = [vp, i32]
     lib.oracle_token_entropy.restype = f32
     lib.oracle_entropy_k.argtypes = [f32]
@@ -137,14 +143,38 @@ def router_logits(x: np.ndarray, wr: np.ndarray, dtype: str) -> np.ndarray:
     return out
 
 
-def select_topk(logits: np.ndarray, k: int, kcap: Optional[int] = None):
+def select_topk(logits: np.ndarray, k: int, kcap: Optional[int] = None, groups: int = 0):
+    """groups > 1: at most one expert per group of E/groups consecutive experts."""
     logits = _c(logits, np.float32)
     T, E = logits.shape
     kcap = k if kcap is None else kcap
     idx = np.empty((T, kcap), np.int32)
     w = np.empty((T, kcap), np.float32)
-    _load().oracle_select_topk(_p(logits), T, E, k, kcap, _p(idx), _p(w))
+    if groups > 1:
+        assert E % groups == 0 and k <= groups
+        _load().oracle_select_topk_grouped(_p(logits), T, E, groups, k, kcap, _p(idx), _p(w))
+    else:
+        _load().oracle_select_topk(_p(logits), T, E, k, kcap, _p(idx), _p(w))
     return idx, w
+
+
+def correct_logits(logits: np.ndarray, health: np.ndarray, alpha: float) -> np.ndarray:
+    """logits - alpha * health[e] in fp32 (a new array)."""
+    out = np.array(logits, np.float32, order="C", copy=True)
+    h = _c(health, np.float32)
+    T, E = out.shape
+    assert h.shape == (E,)
+    _load().oracle_correct_logits(_p(out), T, E, _p(h), float(alpha))
+    return out
+
+
+def load_stats(counts: np.ndarray):
+    """(least-used expert, population standard deviation) of per-expert counts."""
+    c = _c(counts, np.int32)
+    lu = np.zeros(1, np.int32)
+    sd = np.zeros(1, np.float32)
+    _load().oracle_load_stats(_p(c), c.size, _p(lu), _p(sd))
+    return int(lu[0]), float(sd[0])
 
 
 def token_entropy(logit_row: np.ndarray) -> float:
@@ -161,8 +191,9 @@ def entropy_k(h: float) -> int:
     return int(_load().oracle_entropy_k(float(h)))
 
 
-def route(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, want_logits: bool = False):
-    """Returns (idx [T,kcap], w [T,kcap], k_used, h_mean[, logits])."""
+def route(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, want_logits: bool = False,
+          health: Optional[np.ndarray] = None, alpha: float = 0.0, groups: int = 0):
+    """Returns (idx [T,kcap], w [T,kcap], k_used, h_mean[, logits]); logits are the corrected ones."""
     x = _c(x, np.uint16)
     wr = _c(wr, np.uint16)
     T, H = x.shape
@@ -173,7 +204,9 @@ def route(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, want_logits: bool =
     ku = np.zeros(1, np.int32)
     hm = np.zeros(1, np.float32)
     logits = np.empty((T, E), np.float32) if want_logits else None
-    _load().oracle_route(_p(x), DTYPE_CODE[dtype], T, H, _p(wr), E, k, _p(idx), _p(w), _p(ku), _p(hm), _p(logits))
+    h = _c(health, np.float32)
+    _load().oracle_route_ex(_p(x), DTYPE_CODE[dtype], T, H, _p(wr), E, k, _p(h), float(alpha), int(groups), _p(idx),
+                            _p(w), _p(ku), _p(hm), _p(logits))
     res = (idx, w, int(ku[0]), float(hm[0]))
     return res + (logits,) if want_logits else res
 
@@ -255,7 +288,8 @@ def tokens_forward(x: np.ndarray, dtype: str, tokens: Sequence[int], idx: np.nda
     return (y, h) if want_h else y
 
 
-def layer_forward(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, gate_up, down):
+def layer_forward(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, gate_up, down,
+                  health: Optional[np.ndarray] = None, alpha: float = 0.0, groups: int = 0):
     """The whole layer.  Returns dict(y bits, y_f32, idx, w, k_used, h_mean)."""
     x = _c(x, np.uint16)
     wr = _c(wr, np.uint16)
@@ -268,7 +302,9 @@ def layer_forward(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, gate_up, do
     w = np.empty((T, kcap), np.float32)
     ku = np.zeros(1, np.int32)
     hm = np.zeros(1, np.float32)
-    _load().oracle_layer_forward(_p(x), DTYPE_CODE[dtype], T, H, _p(wr), E, k, _p(gate_up.q), _p(gate_up.scales),
-                                 _p(gate_up.biases), _p(down.q), _p(down.scales), _p(down.biases), down.K,
-                                 down.bits, down.group_size, _p(y), _p(yf), _p(idx), _p(w), _p(ku), _p(hm))
+    h = _c(health, np.float32)
+    _load().oracle_layer_forward_ex(_p(x), DTYPE_CODE[dtype], T, H, _p(wr), E, k, _p(h), float(alpha), int(groups),
+                                    _p(gate_up.q), _p(gate_up.scales), _p(gate_up.biases), _p(down.q),
+                                    _p(down.scales), _p(down.biases), down.K, down.bits, down.group_size, _p(y),
+                                    _p(yf), _p(idx), _p(w), _p(ku), _p(hm))
     return dict(y=y, y_f32=yf, idx=idx, w=w, k_used=int(ku[0]), h_mean=float(hm[0]))

@@ -30,6 +30,18 @@
  *               axis, [gate, up] order, then split (oMLX page, steps 3 and 4).
  *   SwiGLU      h = silu(g) * u, silu(g) = g / (1 + e^-g).
  *   down        o = W_down . h
+ *   load-aware  logits_final = logits - alpha * H_e, the per-expert load index
+ *   correction  H_e weighted by a scale alpha, subtracted before selection
+ *               (page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析", section 3.3,
+ *               auxiliary routing head).  Every later step of the routing
+ *               (entropy, selection, weights) uses the corrected logits.
+ *   groups      the E experts in G groups of E/G consecutive experts and at
+ *               most one expert chosen per group: each group's best expert,
+ *               then the k best of those (llama.cpp page, section 1.1: 64
+ *               experts in 4 groups of 16, the best of each group, 4 chosen).
+ *   load stats  the least-used expert and the standard deviation of the
+ *               per-expert activation counts (page "Qwen3.5-MoE与Qwen3-MoE
+ *               架构差异深度解析", the closing advice on monitoring MoE health).
  *   combine     y = sum over the token's slots of weight * o, in slot order,
  *               with the weight applied after the down projection (llama.cpp
  *               page, section 4.2, the weighted-sum loop), rounded to the
@@ -188,6 +200,83 @@ void oracle_select_topk(const float* logits, int T, int E, int k, int kcap, int3
   for (int t = 0; t < T; ++t) select_one(logits + (int64_t)t * E, E, k, kcap, idx + (int64_t)t * kcap, w + (int64_t)t * kcap);
 }
 
+/*
+ * Group-limited selection for one token: G groups of E/G consecutive experts.
+ * First the best expert of every group (larger logit, then lower index), then
+ * those G winners ordered by the same key; the first k are the slots.  The
+ * weights are the softmax over all E experts renormalised over the chosen k,
+ * as in select_one.
+ */
+static void select_grouped(const float* l, int E, int G, int k, int kcap, int32_t* idx, float* w) {
+  int gs = E / G, win[256], order[256];
+  float wl[256], p[256];
+  for (int g = 0; g < G; ++g) {
+    int b = g * gs;
+    for (int e = g * gs + 1; e < (g + 1) * gs; ++e)
+      if (l[e] > l[b]) b = e; /* strictly larger: the lower index stays on ties */
+    win[g] = b;
+    wl[g] = l[b];
+  }
+  order_experts(wl, G, order); /* order of the winners by (logit, then group = index order) */
+  float lmax = l[win[order[0]]];
+  float z = 0.0f;
+  for (int e = 0; e < E; ++e) {
+    p[e] = expf(l[e] - lmax);
+    z = z + p[e];
+  }
+  for (int e = 0; e < E; ++e) p[e] = p[e] / z;
+  float tot = 0.0f;
+  for (int s = 0; s < k; ++s) tot = tot + p[win[order[s]]];
+  for (int s = 0; s < kcap; ++s) {
+    if (s < k) {
+      idx[s] = win[order[s]];
+      w[s] = p[win[order[s]]] / tot;
+    } else {
+      idx[s] = -1;
+      w[s] = 0.0f;
+    }
+  }
+}
+
+/* groups <= 1: plain top-k; else group-limited (E % groups == 0, k <= groups) */
+void oracle_select_topk_grouped(const float* logits, int T, int E, int groups, int k, int kcap, int32_t* idx,
+                                float* w) {
+  for (int t = 0; t < T; ++t) {
+    if (groups <= 1)
+      select_one(logits + (int64_t)t * E, E, k, kcap, idx + (int64_t)t * kcap, w + (int64_t)t * kcap);
+    else
+      select_grouped(logits + (int64_t)t * E, E, groups, k, kcap, idx + (int64_t)t * kcap, w + (int64_t)t * kcap);
+  }
+}
+
+/* logits[t, e] -= alpha * health[e] (the product and the difference each rounded to fp32) */
+void oracle_correct_logits(float* logits, int T, int E, const float* health, float alpha) {
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      float c = alpha * health[e];
+      logits[(int64_t)t * E + e] = logits[(int64_t)t * E + e] - c;
+    }
+}
+
+/*
+ * Health figures of a vector of per-expert activation counts: the least-used
+ * expert (the lowest index among the smallest counts) and the population
+ * standard deviation of the counts, sqrt(sum_e (c_e - mean)^2 / E), computed
+ * in fp64 and rounded to fp32.
+ */
+void oracle_load_stats(const int32_t* counts, int E, int32_t* least_used, float* stddev) {
+  int m = 0;
+  for (int e = 1; e < E; ++e)
+    if (counts[e] < counts[m]) m = e;
+  double mean = 0.0;
+  for (int e = 0; e < E; ++e) mean += (double)counts[e];
+  mean /= (double)E;
+  double ss = 0.0;
+  for (int e = 0; e < E; ++e) ss += ((double)counts[e] - mean) * ((double)counts[e] - mean);
+  *least_used = m;
+  *stddev = (float)sqrt(ss / (double)E);
+}
+
 /* -------------------------------------------------- adaptive k (A2') --- */
 
 /* Shannon entropy (nats) of softmax(logits) for one token */
@@ -226,20 +315,27 @@ float oracle_batch_entropy(const float* logits, int T, int E) {
  * kcap = 3, k_used chosen from the batch entropy; slots >= k_used get
  * index -1 and weight 0.  logits_out may be NULL.
  */
-void oracle_route(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k, int32_t* idx,
-                  float* w, int32_t* k_used, float* h_mean, float* logits_out) {
+void oracle_route_ex(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k,
+                     const float* health, float alpha, int groups, int32_t* idx, float* w, int32_t* k_used,
+                     float* h_mean, float* logits_out) {
   float* logits = logits_out ? logits_out : (float*)malloc(sizeof(float) * (size_t)T * E);
   oracle_router_logits(x, dtype, T, H, wr, E, logits);
+  if (health) oracle_correct_logits(logits, T, E, health, alpha);
   int kcap = k > 0 ? k : 3, ku = k;
   float hm = 0.0f;
   if (k < 0) {
     hm = oracle_batch_entropy(logits, T, E);
     ku = oracle_entropy_k(hm);
   }
-  oracle_select_topk(logits, T, E, ku, kcap, idx, w);
+  oracle_select_topk_grouped(logits, T, E, groups, ku, kcap, idx, w);
   if (k_used) *k_used = ku;
   if (h_mean) *h_mean = hm;
   if (!logits_out) free(logits);
+}
+
+void oracle_route(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k, int32_t* idx,
+                  float* w, int32_t* k_used, float* h_mean, float* logits_out) {
+  oracle_route_ex(x, dtype, T, H, wr, E, k, NULL, 0.0f, 0, idx, w, k_used, h_mean, logits_out);
 }
 
 /* ------------------------------------------------------ pair sort (A3) -- */
@@ -423,12 +519,13 @@ void oracle_round_output(const float* y_f32, int64_t n, int dtype, uint16_t* y) 
  * combine and round.  idx/w: [T, kcap]; y: [T, H] activation dtype;
  * y_f32 (may be NULL) the unrounded fp32 result.
  */
-void oracle_layer_forward(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k,
-                          const void* guq, const uint16_t* gus, const uint16_t* gub, const void* dq,
-                          const uint16_t* ds, const uint16_t* db, int I, int bits, int gsz, uint16_t* y,
-                          float* y_f32, int32_t* idx, float* w, int32_t* k_used, float* h_mean) {
+void oracle_layer_forward_ex(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k,
+                             const float* health, float alpha, int groups, const void* guq, const uint16_t* gus,
+                             const uint16_t* gub, const void* dq, const uint16_t* ds, const uint16_t* db, int I,
+                             int bits, int gsz, uint16_t* y, float* y_f32, int32_t* idx, float* w, int32_t* k_used,
+                             float* h_mean) {
   int ku = 0;
-  oracle_route(x, dtype, T, H, wr, E, k, idx, w, &ku, h_mean, NULL);
+  oracle_route_ex(x, dtype, T, H, wr, E, k, health, alpha, groups, idx, w, &ku, h_mean, NULL);
   if (k_used) *k_used = ku;
   int kcap = k > 0 ? k : 3;
   int32_t* tokens = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
@@ -438,6 +535,14 @@ void oracle_layer_forward(const uint16_t* x, int dtype, int T, int H, const uint
   oracle_round_output(yf, (int64_t)T * H, dtype, y);
   if (!y_f32) free(yf);
   free(tokens);
+}
+
+void oracle_layer_forward(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k,
+                          const void* guq, const uint16_t* gus, const uint16_t* gub, const void* dq,
+                          const uint16_t* ds, const uint16_t* db, int I, int bits, int gsz, uint16_t* y,
+                          float* y_f32, int32_t* idx, float* w, int32_t* k_used, float* h_mean) {
+  oracle_layer_forward_ex(x, dtype, T, H, wr, E, k, NULL, 0.0f, 0, guq, gus, gub, dq, ds, db, I, bits, gsz, y, y_f32,
+                          idx, w, k_used, h_mean);
 }
 
 int oracle_num_threads(void) {

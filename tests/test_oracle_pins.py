@@ -409,3 +409,149 @@ def test_tokens_forward_matches_layer_forward_rows():
     res = oracle.layer_forward(inp.x, inp.wr, "f16", 2, gu, inp.down)
     sub = oracle.tokens_forward(inp.x, "f16", [7, 2, 9], res["idx"], res["w"], 2, gu, inp.down)
     assert np.array_equal(sub, res["y_f32"][[7, 2, 9]])
+
+
+# ------------------------------------- load-aware correction, groups, stats --
+# Page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析", section 3.3: the final logits
+# are the main logits minus alpha times the per-expert load index H.  Page
+# "Qwen3.5 Block在llama.cpp中的映射与优化原理", section 1.1: 64 experts in 4
+# groups of 16, the best expert of each group.  Closing advice of the first
+# page: watch the least-used expert and the standard deviation of the counts.
+
+def test_correction_worked_example():
+    # one token, logits (2, 1.5, 1, 0), H = (1, 0, 0, 0).  alpha = 1 gives
+    # (1, 1.5, 1, 0): top-2 is expert 1, then the tie at 1.0 goes to expert 0;
+    # weights 1/(1+e^-0.5) and e^-0.5/(1+e^-0.5).  A plus sign would keep
+    # (0, 1); alpha = 2 gives (0, 1.5, 1, 0) and the slots (1, 2).
+    l = np.float32([[2.0, 1.5, 1.0, 0.0]])
+    hv = np.float32([1.0, 0.0, 0.0, 0.0])
+    c1 = oracle.correct_logits(l, hv, 1.0)
+    assert np.array_equal(c1, np.float32([[1.0, 1.5, 1.0, 0.0]]))
+    idx, w = oracle.select_topk(c1, 2)
+    assert idx.tolist() == [[1, 0]]
+    e = math.exp(-0.5)
+    assert np.allclose(w[0], [1 / (1 + e), e / (1 + e)], rtol=4 * U, atol=0)
+    idx2, _ = oracle.select_topk(oracle.correct_logits(l, hv, 2.0), 2)
+    assert idx2.tolist() == [[1, 2]]
+    # the raw logits are left alone
+    assert np.array_equal(l, np.float32([[2.0, 1.5, 1.0, 0.0]]))
+
+
+def test_correction_zero_alpha_and_constant_health_change_nothing():
+    rng = np.random.default_rng(11)
+    T, E, k = 16, 32, 4
+    # logits on a 2^-10 grid in [-4, 4) with no repeats in a row: subtracting
+    # 0.5 is exact, so the shifted softmax sees the same differences
+    l = np.stack([rng.permutation(8192)[:E] for _ in range(T)]).astype(np.float32) / 1024.0 - 4.0
+    i0, w0 = oracle.select_topk(l, k)
+    for hv, a in [(rng.standard_normal(E).astype(np.float32), 0.0), (np.full(E, 0.25, np.float32), 2.0)]:
+        c = oracle.correct_logits(l, hv, a)
+        i1, w1 = oracle.select_topk(c, k)
+        assert np.array_equal(i0, i1)
+        assert np.array_equal(w0, w1)
+
+
+def test_correction_steers_away_from_an_overloaded_expert():
+    rng = np.random.default_rng(12)
+    T, E, k = 64, 32, 2
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    hot = int(np.argmax(np.bincount(oracle.select_topk(l, k)[0].ravel(), minlength=E)))
+    hv = np.zeros(E, np.float32)
+    hv[hot] = 100.0  # far above any logit gap of N(0,1) logits
+    idx, _ = oracle.select_topk(oracle.correct_logits(l, hv, 1.0), k)
+    assert (idx != hot).all()
+    # every other expert keeps its rank order: the selection equals the top-k
+    # of the logits with the hot expert removed
+    l2 = l.copy()
+    l2[:, hot] = -np.inf
+    assert np.array_equal(idx, np.argsort(-l2, axis=1, kind="stable")[:, :k])
+
+
+def _grouped_brute(l, G, k):
+    """All k-sets with at most one expert per group; the chosen set has the
+    lexicographically best key sequence (larger logit, then lower index)."""
+    import itertools
+    E = l.size
+    gs = E // G
+    best = None
+    for S in itertools.combinations(range(E), k):
+        if len({e // gs for e in S}) < k:
+            continue
+        key = sorted((-float(l[e]), e) for e in S)
+        if best is None or key < best:
+            best = key
+    return [e for _, e in best]
+
+
+@pytest.mark.parametrize("E,G", [(8, 4), (12, 3), (16, 4)])
+def test_grouped_selection_brute_force(E, G):
+    rng = np.random.default_rng(E * 10 + G)
+    for trial in range(60):
+        # coarse values so that ties inside and across groups occur
+        l = (rng.integers(-3, 4, size=E) / 2.0).astype(np.float32)
+        for k in range(1, G + 1):
+            idx, w = oracle.select_topk(l[None], k, groups=G)
+            assert idx[0].tolist() == _grouped_brute(l, G, k), (l, k)
+            p = np.exp(l.astype(np.float64) - l.max())
+            want = p[idx[0]] / p[idx[0]].sum()
+            assert np.allclose(w[0], want, rtol=64 * U, atol=0)
+
+
+def test_grouped_with_singleton_groups_is_plain_topk():
+    rng = np.random.default_rng(13)
+    l = rng.standard_normal((32, 16)).astype(np.float32)
+    for k in (1, 3, 8):
+        a = oracle.select_topk(l, k)
+        b = oracle.select_topk(l, k, groups=16)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_grouped_page_shape_one_best_per_group():
+    # 64 experts in 4 groups of 16, one from each group: 4 slots, and each
+    # slot is the first maximum of its group
+    rng = np.random.default_rng(14)
+    l = rng.standard_normal((200, 64)).astype(np.float32)
+    idx, w = oracle.select_topk(l, 4, groups=4)
+    for t in range(l.shape[0]):
+        assert sorted(e // 16 for e in idx[t]) == [0, 1, 2, 3]
+        assert set(idx[t]) == {g * 16 + int(np.argmax(l[t, g * 16:(g + 1) * 16])) for g in range(4)}
+        assert list(l[t, idx[t]]) == sorted(l[t, idx[t]], reverse=True)
+    assert np.allclose(w.sum(axis=1), 1.0, atol=8 * U)
+
+
+def test_load_stats_closed_forms():
+    import statistics
+    E = 32
+    assert oracle.load_stats(np.full(E, 7, np.int32)) == (0, 0.0)
+    for j, c in [(0, 9), (5, 12), (31, 1)]:
+        v = np.zeros(E, np.int32)
+        v[j] = c
+        lu, sd = oracle.load_stats(v)
+        assert lu == (1 if j == 0 else 0)
+        # one count c among E: the deviation is c * sqrt(E - 1) / E
+        assert sd == np.float32(c * math.sqrt(E - 1) / E)
+    assert oracle.load_stats(np.int32([3, 10])) == (0, 3.5)
+    # an activation vector like the trace example on the same page (counts of
+    # 12 and 8 for two experts, the rest silent), against the library routine
+    v = np.zeros(E, np.int32)
+    v[2], v[5] = 12, 8
+    lu, sd = oracle.load_stats(v)
+    assert lu == 0 and sd == np.float32(statistics.pstdev(v.tolist()))
+    rng = np.random.default_rng(15)
+    for _ in range(20):
+        v = rng.integers(0, 5000, size=E).astype(np.int32)
+        lu, sd = oracle.load_stats(v)
+        assert lu == int(np.argmin(v))
+        assert sd == np.float32(statistics.pstdev(v.tolist()))
+
+
+def test_route_with_options_is_correction_then_grouped_selection():
+    inp = mi.make_inputs("tiny")
+    rng = np.random.default_rng(16)
+    hv = rng.random(inp.E).astype(np.float32)
+    idx, w, ku, hm, logits = oracle.route(inp.x, inp.wr, inp.dtype, 2, want_logits=True, health=hv, alpha=0.75,
+                                          groups=4)
+    raw = oracle.router_logits(inp.x, inp.wr, inp.dtype)
+    assert np.array_equal(logits, oracle.correct_logits(raw, hv, 0.75))
+    i2, w2 = oracle.select_topk(logits, 2, groups=4)
+    assert np.array_equal(idx, i2) and np.array_equal(w, w2)
