@@ -67,7 +67,8 @@ typedef enum {
   MOE_ERR_WORKSPACE = -8,    /* workspace NULL or smaller than required */
   MOE_ERR_DEVICE = -9,       /* no usable gfx950 device is current */
   MOE_ERR_HIP = -10,         /* a HIP launch or query failed */
-  MOE_ERR_INTERNAL = -11     /* unexpected internal error */
+  MOE_ERR_INTERNAL = -11,    /* unexpected internal error */
+  MOE_ERR_OPTION = -12       /* a routing option is out of range (moe_route_opts) */
 } moe_status;
 
 typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
@@ -147,6 +148,37 @@ typedef struct {
   void* h;
 } moe_taps;
 
+/*
+ * Routing options of the *_ex entry points (NULL: none of them).
+ *
+ *   health   fp32 [E] on the device, or NULL.  The logits that every later
+ *            routing step uses (entropy, selection, weights, the logits tap)
+ *            are logits[t, e] - alpha * health[e], the product and the
+ *            difference each rounded to fp32: the load-aware correction of
+ *            page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析", section 3.3, where
+ *            an auxiliary head supplies a per-expert load index H and a scale
+ *            alpha.  The library only applies it; health holds whatever load
+ *            index the caller keeps (e.g. activation frequencies).  4-byte
+ *            aligned.
+ *   alpha    the scale of the correction (ignored when health is NULL).
+ *   groups   0 or 1: plain top-k.  G > 1: the E experts form G groups of E/G
+ *            consecutive experts and at most one expert per group is chosen:
+ *            the best expert of each group, and of those the k best, in key
+ *            order (page "Qwen3.5 Block在llama.cpp中的映射与优化原理", section
+ *            1.1: 64 experts in 4 groups of 16, the best of each group, so
+ *            4 chosen).  Needs E % G == 0 and k <= G (with MOE_K_ENTROPY:
+ *            G >= 3).  The weights stay the softmax over all E experts,
+ *            renormalised over the chosen ones.
+ * MOE_ERR_OPTION: groups < 0, E % groups != 0, k too large for the groups,
+ * or (moe_topk_from_logits_ex) health given.  MOE_ERR_ALIGN: health not
+ * 4-byte aligned.
+ */
+typedef struct {
+  const float* health;
+  float alpha;
+  int32_t groups;
+} moe_route_opts;
+
 /* flags of moe_layer_forward */
 #define MOE_FLAG_UNFUSED 0x1u    /* separate gate and up projections, then SwiGLU
                                     (a fused tensor is split into two views);
@@ -170,6 +202,10 @@ size_t moe_route_workspace_size(int32_t T, int32_t E, int32_t k);
 moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E, int32_t k,
                      int32_t* topk_idx, float* topk_w, int32_t* k_used, float* entropy, float* logits_out, void* ws,
                      size_t ws_bytes, void* stream);
+/* moe_route with routing options (opts may be NULL; see moe_route_opts). */
+moe_status moe_route_ex(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E,
+                        int32_t k, const moe_route_opts* opts, int32_t* topk_idx, float* topk_w, int32_t* k_used,
+                        float* entropy, float* logits_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Selection only, from caller-provided fp32 logits [T, E] (same rules and
@@ -179,6 +215,11 @@ moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const vo
 moe_status moe_topk_from_logits(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
                                 float* topk_w, int32_t* k_used, float* entropy, void* ws, size_t ws_bytes,
                                 void* stream);
+/* Selection with routing options; the logits are taken as final, so
+ * opts->health must be NULL (MOE_ERR_OPTION otherwise). */
+moe_status moe_topk_from_logits_ex(const float* logits, int32_t T, int32_t E, int32_t k, const moe_route_opts* opts,
+                                   int32_t* topk_idx, float* topk_w, int32_t* k_used, float* entropy, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /*
  * The whole layer.
@@ -200,6 +241,25 @@ moe_status moe_layer_forward(const void* x, moe_dtype dt, int32_t T, int32_t H, 
                              int32_t k, const moe_weights* gate_up, const moe_weights* gate, const moe_weights* up,
                              const moe_weights* down, void* y, uint32_t flags, const moe_taps* taps, void* ws,
                              size_t ws_bytes, void* stream);
+/* moe_layer_forward with routing options (opts may be NULL; see
+ * moe_route_opts); same workspace size. */
+moe_status moe_layer_forward_ex(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E,
+                                int32_t k, const moe_route_opts* opts, const moe_weights* gate_up,
+                                const moe_weights* gate, const moe_weights* up, const moe_weights* down, void* y,
+                                uint32_t flags, const moe_taps* taps, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Health figures of per-expert activation counts (page "Qwen3.5-MoE与Qwen3-MoE
+ * 架构差异深度解析", closing advice on monitoring: the least-activated expert
+ * and the standard deviation of the activation counts), e.g. of the counts
+ * tap of moe_layer_forward or of counts the caller accumulates over a window.
+ *   counts      int32 [E] on the device, each >= 0
+ *   least_used  int32 [1] out: the lowest expert index among the smallest counts
+ *   stddev      fp32 [1] out: sqrt(sum_e (counts[e] - mean)^2 / E) (population)
+ * 1 <= E <= 256.  Enqueued on `stream`.
+ */
+moe_status moe_expert_load_stats(const int32_t* counts, int32_t E, int32_t* least_used, float* stddev,
+                                 void* stream);
 
 /*
  * Pack separate gate [E, inter, K] and up [E, inter, K] into a fused tensor

@@ -29,10 +29,11 @@ FLAG_UNFUSED, FLAG_FORCE_GEMV, FLAG_FORCE_MFMA = 0x1, 0x2, 0x4
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE", -4: "MOE_ERR_ALIGN",
           -5: "MOE_ERR_K", -6: "MOE_ERR_QUANT", -7: "MOE_ERR_INCOMPATIBLE", -8: "MOE_ERR_WORKSPACE",
-          -9: "MOE_ERR_DEVICE", -10: "MOE_ERR_HIP", -11: "MOE_ERR_INTERNAL"}
+          -9: "MOE_ERR_DEVICE", -10: "MOE_ERR_HIP", -11: "MOE_ERR_INTERNAL", -12: "MOE_ERR_OPTION"}
 
-EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_topk_from_logits", "moe_layer_workspace_size",
-           "moe_layer_forward", "moe_fuse_gate_up", "moe_packed_sb_bytes", "moe_pack_sb", "moe_status_string",
+EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_ex", "moe_topk_from_logits",
+           "moe_topk_from_logits_ex", "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_ex",
+           "moe_expert_load_stats", "moe_fuse_gate_up", "moe_packed_sb_bytes", "moe_pack_sb", "moe_status_string",
            "moe_debug_set_events",
            "moe_debug_last_plan", "moe_debug_set_tuning")
 
@@ -48,6 +49,10 @@ class CWeights(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("expert_stride_rows", ctypes.c_int64), ("packed_sb", ctypes.c_void_p)]
+
+
+class CRouteOpts(ctypes.Structure):
+    _fields_ = [("health", ctypes.c_void_p), ("alpha", ctypes.c_float), ("groups", ctypes.c_int32)]
 
 
 class CTaps(ctypes.Structure):
@@ -75,6 +80,17 @@ def lib() -> ctypes.CDLL:
     L.moe_route.restype = i32
     L.moe_topk_from_logits.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.moe_topk_from_logits.restype = i32
+    ropt = ctypes.POINTER(CRouteOpts)
+    L.moe_route_ex.argtypes = [vp, i32, i32, i32, vp, i32, i32, ropt, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route_ex.restype = i32
+    L.moe_topk_from_logits_ex.argtypes = [vp, i32, i32, i32, ropt, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_topk_from_logits_ex.restype = i32
+    L.moe_layer_forward_ex.argtypes = [vp, i32, i32, i32, vp, i32, i32, ropt, ctypes.POINTER(CWeights),
+                                       ctypes.POINTER(CWeights), ctypes.POINTER(CWeights), ctypes.POINTER(CWeights),
+                                       vp, u32, ctypes.POINTER(CTaps), vp, sz, vp]
+    L.moe_layer_forward_ex.restype = i32
+    L.moe_expert_load_stats.argtypes = [vp, i32, vp, vp, vp]
+    L.moe_expert_load_stats.restype = i32
     L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, u32]
     L.moe_layer_workspace_size.restype = sz
     L.moe_layer_forward.argtypes = [vp, i32, i32, i32, vp, i32, i32, ctypes.POINTER(CWeights),
@@ -187,9 +203,21 @@ def _kcap(k: int) -> int:
     return k if k > 0 else MOE_K_ENTROPY_CAP
 
 
-def route(x: torch.Tensor, router_w: torch.Tensor, k: int, want_logits: bool = False, stream=None):
+def _opts(health: Optional[torch.Tensor], alpha: float, groups: int):
+    """moe_route_opts for the *_ex entry points, or None when no option is set."""
+    if health is None and not groups:
+        return None
+    if health is not None:
+        assert health.dtype == torch.float32 and health.is_contiguous()
+    return CRouteOpts(_ptr(health), float(alpha), int(groups))
+
+
+def route(x: torch.Tensor, router_w: torch.Tensor, k: int, want_logits: bool = False, stream=None,
+          health: Optional[torch.Tensor] = None, alpha: float = 0.0, groups: int = 0):
     """Router + selection.  Returns dict(idx [T,kcap] int32, w [T,kcap] fp32,
-    k_used [1] int32, entropy [1] fp32[, logits [T,E] fp32])."""
+    k_used [1] int32, entropy [1] fp32[, logits [T,E] fp32]).  health/alpha:
+    load-aware correction of the logits; groups: at most one expert per group
+    of E/groups consecutive experts (moe_route_opts)."""
     T, H = x.shape
     E = router_w.shape[0]
     dev = x.device
@@ -200,8 +228,13 @@ def route(x: torch.Tensor, router_w: torch.Tensor, k: int, want_logits: bool = F
     ent = torch.zeros(1, dtype=torch.float32, device=dev)
     logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
     ws = torch.empty(max(route_workspace_size(T, E, k), 256), dtype=torch.uint8, device=dev)
-    st = lib().moe_route(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k, _ptr(idx), _ptr(w), _ptr(ku),
-                         _ptr(ent), _ptr(logits), _ptr(ws), ws.numel(), _stream(stream))
+    o = _opts(health, alpha, groups)
+    if o is None:
+        st = lib().moe_route(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k, _ptr(idx), _ptr(w), _ptr(ku),
+                             _ptr(ent), _ptr(logits), _ptr(ws), ws.numel(), _stream(stream))
+    else:
+        st = lib().moe_route_ex(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k, ctypes.byref(o), _ptr(idx),
+                                _ptr(w), _ptr(ku), _ptr(ent), _ptr(logits), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "moe_route")
     out = dict(idx=idx, w=w, k_used=ku, entropy=ent)
     if logits is not None:
@@ -209,7 +242,7 @@ def route(x: torch.Tensor, router_w: torch.Tensor, k: int, want_logits: bool = F
     return out
 
 
-def topk_from_logits(logits: torch.Tensor, k: int, stream=None):
+def topk_from_logits(logits: torch.Tensor, k: int, stream=None, groups: int = 0):
     T, E = logits.shape
     dev = logits.device
     kc = _kcap(k)
@@ -217,8 +250,14 @@ def topk_from_logits(logits: torch.Tensor, k: int, stream=None):
     w = torch.empty((T, kc), dtype=torch.float32, device=dev)
     ku = torch.zeros(1, dtype=torch.int32, device=dev)
     ent = torch.zeros(1, dtype=torch.float32, device=dev)
-    st = lib().moe_topk_from_logits(_ptr(logits.contiguous()), T, E, k, _ptr(idx), _ptr(w), _ptr(ku), _ptr(ent),
-                                    None, 0, _stream(stream))
+    lg = logits.contiguous()
+    if not groups:
+        st = lib().moe_topk_from_logits(_ptr(lg), T, E, k, _ptr(idx), _ptr(w), _ptr(ku), _ptr(ent), None, 0,
+                                        _stream(stream))
+    else:
+        o = CRouteOpts(None, 0.0, int(groups))
+        st = lib().moe_topk_from_logits_ex(_ptr(lg), T, E, k, ctypes.byref(o), _ptr(idx), _ptr(w), _ptr(ku),
+                                           _ptr(ent), None, 0, _stream(stream))
     _check(st, "moe_topk_from_logits")
     return dict(idx=idx, w=w, k_used=ku, entropy=ent)
 
@@ -239,8 +278,9 @@ def make_taps(T: int, E: int, k: int, inter: int, device, names: Sequence[str] =
 def layer_forward(x: torch.Tensor, router_w: torch.Tensor, k: int, down: Weights, gate_up: Optional[Weights] = None,
                   gate: Optional[Weights] = None, up: Optional[Weights] = None, flags: int = 0,
                   taps: Optional[dict] = None, out: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """The whole layer: y [T, H] in the activation dtype."""
+                  workspace: Optional[torch.Tensor] = None, stream=None, health: Optional[torch.Tensor] = None,
+                  alpha: float = 0.0, groups: int = 0) -> torch.Tensor:
+    """The whole layer: y [T, H] in the activation dtype (routing options as in route())."""
     T, H = x.shape
     E = router_w.shape[0]
     inter = down.K
@@ -257,13 +297,27 @@ def layer_forward(x: torch.Tensor, router_w: torch.Tensor, k: int, down: Weights
     cg = gate.c() if gate is not None else None
     cu = up.c() if up is not None else None
     cd = down.c()
-    st = lib().moe_layer_forward(
-        _ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k,
-        ctypes.byref(cgu) if cgu is not None else None, ctypes.byref(cg) if cg is not None else None,
-        ctypes.byref(cu) if cu is not None else None, ctypes.byref(cd), _ptr(y), flags,
-        ctypes.byref(ctaps) if ctaps is not None else None, _ptr(ws), ws.numel(), _stream(stream))
+    wargs = (ctypes.byref(cgu) if cgu is not None else None, ctypes.byref(cg) if cg is not None else None,
+             ctypes.byref(cu) if cu is not None else None, ctypes.byref(cd), _ptr(y), flags,
+             ctypes.byref(ctaps) if ctaps is not None else None, _ptr(ws), ws.numel(), _stream(stream))
+    o = _opts(health, alpha, groups)
+    if o is None:
+        st = lib().moe_layer_forward(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k, *wargs)
+    else:
+        st = lib().moe_layer_forward_ex(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k, ctypes.byref(o),
+                                        *wargs)
     _check(st, "moe_layer_forward")
     return y
+
+
+def expert_load_stats(counts: torch.Tensor, stream=None):
+    """(least-used expert [1] int32, standard deviation [1] fp32) of int32 counts [E] on the device."""
+    assert counts.dtype == torch.int32 and counts.dim() == 1 and counts.is_contiguous()
+    lu = torch.empty(1, dtype=torch.int32, device=counts.device)
+    sd = torch.empty(1, dtype=torch.float32, device=counts.device)
+    _check(lib().moe_expert_load_stats(_ptr(counts), counts.numel(), _ptr(lu), _ptr(sd), _stream(stream)),
+           "moe_expert_load_stats")
+    return lu, sd
 
 
 def fuse_gate_up(gate: Weights, up: Weights, stream=None) -> Weights:

@@ -44,6 +44,7 @@ struct RouteSrc {
   float* wts;
   int32_t* k_used;      // device scalar: output when logits is given, else input (may be NULL)
   float* entropy;
+  int gs;               // experts per selection group (1: plain top-k)
 };
 
 template <typename F>
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   int e;
   if (prm.rt.logits) {
     float wsel = 0.0f;
-    route_slot(prm.rt.logits + (size_t)t * prm.rt.E, prm.rt.E, ku, slot, e, wsel);
+    route_slot(prm.rt.logits + (size_t)t * prm.rt.E, prm.rt.E, ku, slot, e, wsel, prm.rt.gs);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       prm.rt.idx[p] = e;
       prm.rt.wts[p] = wsel;
@@ -367,7 +368,7 @@ hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_
   GemvUpParams prm;
   prm.x = (const uint16_t*)x;
   prm.act = act;
-  prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy};
+  prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy, route.gs};
   prm.k_static = k_static;
   prm.kcap = kcap;
   prm.H = H;
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
   int si[MOE_MAX_K_DEV];
   float sw[MOE_MAX_K_DEV];
   if (prm.rt.logits) {
-    route_token(prm.rt.logits + (size_t)t * prm.rt.E, prm.rt.E, ku, si, sw);
+    route_token(prm.rt.logits + (size_t)t * prm.rt.E, prm.rt.E, ku, si, sw, prm.rt.gs);
   } else {
 #pragma unroll
     for (int j = 0; j < MOE_MAX_K_DEV; ++j) {
@@ -595,7 +596,7 @@ hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_sta
                             int bits, WView wd, void* y, int act, int num_cu, hipStream_t st) {
   GemvDownParams prm;
   prm.h = h;
-  prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy};
+  prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy, route.gs};
   prm.k_static = k_static;
   prm.kcap = kcap;
   prm.H = H;

@@ -55,12 +55,14 @@ struct WView {
 };
 
 // ---------------------------------------------------------------- router
+// health (fp32 [E], or NULL): logits[t, e] - alpha * health[e] are stored
 hipError_t launch_router_logits(const void* x, const void* wr, float* logits, int T, int H, int E, int act,
-                                hipStream_t st);
-// k > 0: static; k < 0: entropy-adaptive (kcap = 3)
-// k > 0: static top-k; k <= 0: entropy-adaptive (scratch: T floats, or NULL
-// for the single-workgroup pass)
-hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* k_used,
+                                const float* health, float alpha, hipStream_t st);
+// least-used expert and population standard deviation of E counts
+hipError_t launch_load_stats(const int32_t* counts, int E, int32_t* least_used, float* stddev, hipStream_t st);
+// k > 0: static top-k; k <= 0: entropy-adaptive, kcap = 3 (scratch: T
+// floats, or NULL for the single-workgroup pass); gs experts per group
+hipError_t launch_topk(const float* logits, int T, int E, int k, int gs, int32_t* idx, float* w, int32_t* k_used,
                        float* entropy, float* scratch, hipStream_t st);
 
 // ------------------------------------------------------------------ sort
@@ -81,6 +83,7 @@ struct GemvRoute {
   float* wts;
   int32_t* k_used;
   float* entropy;
+  int gs = 1;  // experts per selection group (1: plain top-k)
 };
 // fused=true: h[p, j] = fp16(swiglu(gate_j . x, up_j . x)) for j < I
 // fused=false: out32[p, n] = w0_n . x for n < N

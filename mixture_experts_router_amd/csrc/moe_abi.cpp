@@ -192,30 +192,57 @@ WView view_of(const moe_weights* w, int64_t row_offset) {
     if ((expr) != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
 
+// Routing options, checked: the correction vector and its scale, and the
+// experts per selection group (1: plain top-k).
+struct RouteOpt {
+  const float* health = nullptr;
+  float alpha = 0.0f;
+  int gs = 1;
+};
+
+moe_status check_opts(const moe_route_opts* o, int E, int k, RouteOpt* out) {
+  *out = RouteOpt{};
+  if (!o) return MOE_OK;
+  if (o->health && (reinterpret_cast<uintptr_t>(o->health) & 3u) != 0) return MOE_ERR_ALIGN;
+  if (o->groups < 0) return MOE_ERR_OPTION;
+  if (o->groups > 1) {
+    if (E % o->groups != 0) return MOE_ERR_OPTION;
+    const int need = k == MOE_K_ENTROPY ? MOE_K_ENTROPY_CAP : k;
+    if (need > o->groups) return MOE_ERR_OPTION;
+    out->gs = E / o->groups;
+  }
+  out->health = o->health;
+  out->alpha = o->alpha;
+  return MOE_OK;
+}
+
 // the selection launches: static top-k, or the adaptive pass (two launches
 // with scratch for the per-token entropies, one without)
-moe_status select_impl(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* k_used,
+moe_status select_impl(const float* logits, int T, int E, int k, int gs, int32_t* idx, float* w, int32_t* k_used,
                        float* entropy, float* scratch, hipStream_t st) {
-  HIP_TRY(moe::launch_topk(logits, T, E, k, idx, w, k_used, entropy, scratch, st));
+  HIP_TRY(moe::launch_topk(logits, T, E, k, gs, idx, w, k_used, entropy, scratch, st));
   if (k <= 0 && scratch) plan_step("entropy_tokens", st);
   plan_step(k > 0 ? "topk" : "topk_entropy", st);
   return MOE_OK;
 }
 
-moe_status route_impl(const void* x, moe_dtype dt, int T, int H, const void* wr, int E, int k, int32_t* idx,
-                      float* w, int32_t* k_used, float* entropy, float* logits, float* scratch, hipStream_t st) {
-  HIP_TRY(moe::launch_router_logits(x, wr, logits, T, H, E, (int)dt, st));
+moe_status route_impl(const void* x, moe_dtype dt, int T, int H, const void* wr, int E, int k, const RouteOpt& ro,
+                      int32_t* idx, float* w, int32_t* k_used, float* entropy, float* logits, float* scratch,
+                      hipStream_t st) {
+  HIP_TRY(moe::launch_router_logits(x, wr, logits, T, H, E, (int)dt, ro.health, ro.alpha, st));
   plan_step("router_logits", st);
-  return select_impl(logits, T, E, k, idx, w, k_used, entropy, scratch, st);
+  return select_impl(logits, T, E, k, ro.gs, idx, w, k_used, entropy, scratch, st);
 }
 
 moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* router_w, int E, int k,
-                        const moe_weights* gate_up, const moe_weights* gate, const moe_weights* up,
-                        const moe_weights* down, void* y, uint32_t flags, const moe_taps* taps, void* ws,
-                        size_t ws_bytes, hipStream_t st) {
+                        const moe_route_opts* opts, const moe_weights* gate_up, const moe_weights* gate,
+                        const moe_weights* up, const moe_weights* down, void* y, uint32_t flags,
+                        const moe_taps* taps, void* ws, size_t ws_bytes, hipStream_t st) {
   // ---- validation (host only)
   moe_status s = check_router(x, dt, T, H, router_w, E, k);
   if (s != MOE_OK) return s;
+  RouteOpt ro;
+  if ((s = check_opts(opts, E, k, &ro)) != MOE_OK) return s;
   if ((!y && T != 0) || !down) return MOE_ERR_NULL;
   if (T != 0 && !aligned16(y)) return MOE_ERR_ALIGN;
   const int I = down->K;
@@ -280,11 +307,11 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   if (gemv) {
     // decode path: with static k the GEMV kernels select the experts from the
     // logits themselves (no separate selection launch)
-    HIP_TRY(moe::launch_router_logits(x, router_w, logits, T, H, E, act, st));
+    HIP_TRY(moe::launch_router_logits(x, router_w, logits, T, H, E, act, ro.health, ro.alpha, st));
     plan_step("router_logits", st);
-    moe::GemvRoute rt{logits, E, idx, wts, k_used, entropy};
+    moe::GemvRoute rt{logits, E, idx, wts, k_used, entropy, ro.gs};
     if (k <= 0) {
-      moe_status s2 = select_impl(logits, T, E, k, idx, wts, k_used, entropy, (float*)(W + L.hent), st);
+      moe_status s2 = select_impl(logits, T, E, k, ro.gs, idx, wts, k_used, entropy, (float*)(W + L.hent), st);
       if (s2 != MOE_OK) return s2;
       rt.logits = nullptr;
     }
@@ -314,8 +341,8 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       plan_step("sort_pairs", st);
     }
   } else {
-    if ((s = route_impl(x, dt, T, H, router_w, E, k, idx, wts, k_used, entropy, logits, (float*)(W + L.hent), st)) !=
-        MOE_OK)
+    if ((s = route_impl(x, dt, T, H, router_w, E, k, ro, idx, wts, k_used, entropy, logits, (float*)(W + L.hent),
+                        st)) != MOE_OK)
       return s;
     HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st));
     plan_step("sort_pairs", st);
@@ -418,6 +445,7 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_DEVICE: return "no usable gfx950 device is current";
     case MOE_ERR_HIP: return "a HIP call failed";
     case MOE_ERR_INTERNAL: return "internal error";
+    case MOE_ERR_OPTION: return "a routing option is out of range";
   }
   return "unknown status";
 }
@@ -431,9 +459,18 @@ size_t moe_route_workspace_size(int32_t T, int32_t E, int32_t k) {
 moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E, int32_t k,
                      int32_t* topk_idx, float* topk_w, int32_t* k_used, float* entropy, float* logits_out, void* ws,
                      size_t ws_bytes, void* stream) {
+  return moe_route_ex(x, dt, T, H, router_w, E, k, nullptr, topk_idx, topk_w, k_used, entropy, logits_out, ws,
+                      ws_bytes, stream);
+}
+
+moe_status moe_route_ex(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E,
+                        int32_t k, const moe_route_opts* opts, int32_t* topk_idx, float* topk_w, int32_t* k_used,
+                        float* entropy, float* logits_out, void* ws, size_t ws_bytes, void* stream) {
   try {
     moe_status s = check_router(x, dt, T, H, router_w, E, k);
     if (s != MOE_OK) return s;
+    RouteOpt ro;
+    if ((s = check_opts(opts, E, k, &ro)) != MOE_OK) return s;
     if (T == 0) return MOE_OK;
     if (!topk_idx || !topk_w) return MOE_ERR_NULL;
     float* logits = logits_out;
@@ -449,7 +486,7 @@ moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const vo
     if ((s = device_props(&props)) != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     plan_begin(st);
-    return route_impl(x, dt, T, H, router_w, E, k, topk_idx, topk_w, k_used, entropy, logits, scratch, st);
+    return route_impl(x, dt, T, H, router_w, E, k, ro, topk_idx, topk_w, k_used, entropy, logits, scratch, st);
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }
@@ -458,6 +495,12 @@ moe_status moe_route(const void* x, moe_dtype dt, int32_t T, int32_t H, const vo
 moe_status moe_topk_from_logits(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_idx,
                                 float* topk_w, int32_t* k_used, float* entropy, void* ws, size_t ws_bytes,
                                 void* stream) {
+  return moe_topk_from_logits_ex(logits, T, E, k, nullptr, topk_idx, topk_w, k_used, entropy, ws, ws_bytes, stream);
+}
+
+moe_status moe_topk_from_logits_ex(const float* logits, int32_t T, int32_t E, int32_t k, const moe_route_opts* opts,
+                                   int32_t* topk_idx, float* topk_w, int32_t* k_used, float* entropy, void* ws,
+                                   size_t ws_bytes, void* stream) {
   try {
     (void)ws;
     (void)ws_bytes;
@@ -468,13 +511,17 @@ moe_status moe_topk_from_logits(const float* logits, int32_t T, int32_t E, int32
     } else if (k < 1 || k > MOE_MAX_K || k > E) {
       return MOE_ERR_K;
     }
+    RouteOpt ro;
+    moe_status so = check_opts(opts, E, k, &ro);
+    if (so != MOE_OK) return so;
+    if (ro.health) return MOE_ERR_OPTION;
     if (T == 0) return MOE_OK;
     DevProps props;
     moe_status s = device_props(&props);
     if (s != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     plan_begin(st);
-    if (moe::launch_topk(logits, T, E, k, topk_idx, topk_w, k_used, entropy, nullptr, st) != hipSuccess)
+    if (moe::launch_topk(logits, T, E, k, ro.gs, topk_idx, topk_w, k_used, entropy, nullptr, st) != hipSuccess)
       return MOE_ERR_HIP;
     plan_step(k > 0 ? "topk" : "topk_entropy", st);
     return MOE_OK;
@@ -493,8 +540,41 @@ moe_status moe_layer_forward(const void* x, moe_dtype dt, int32_t T, int32_t H, 
                              const moe_weights* down, void* y, uint32_t flags, const moe_taps* taps, void* ws,
                              size_t ws_bytes, void* stream) {
   try {
-    return forward_impl(x, dt, T, H, router_w, E, k, gate_up, gate, up, down, y, flags, taps, ws, ws_bytes,
+    return forward_impl(x, dt, T, H, router_w, E, k, nullptr, gate_up, gate, up, down, y, flags, taps, ws, ws_bytes,
                         (hipStream_t)stream);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_layer_forward_ex(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w, int32_t E,
+                                int32_t k, const moe_route_opts* opts, const moe_weights* gate_up,
+                                const moe_weights* gate, const moe_weights* up, const moe_weights* down, void* y,
+                                uint32_t flags, const moe_taps* taps, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    return forward_impl(x, dt, T, H, router_w, E, k, opts, gate_up, gate, up, down, y, flags, taps, ws, ws_bytes,
+                        (hipStream_t)stream);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_expert_load_stats(const int32_t* counts, int32_t E, int32_t* least_used, float* stddev,
+                                 void* stream) {
+  try {
+    if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+    if (!counts || !least_used || !stddev) return MOE_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(counts) & 3u) || (reinterpret_cast<uintptr_t>(least_used) & 3u) ||
+        (reinterpret_cast<uintptr_t>(stddev) & 3u))
+      return MOE_ERR_ALIGN;
+    DevProps props;
+    moe_status s = device_props(&props);
+    if (s != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    plan_begin(st);
+    HIP_TRY(moe::launch_load_stats(counts, E, least_used, stddev, st));
+    plan_step("load_stats", st);
+    return MOE_OK;
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }

@@ -35,7 +35,8 @@ __device__ __forceinline__ void unpack8(u32x4 r, int act, float* v) {
 __global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t* __restrict__ x,
                                                                   const uint16_t* __restrict__ wr,
                                                                   float* __restrict__ logits, int H, int E,
-                                                                  int act) {
+                                                                  int act, const float* __restrict__ health,
+                                                                  float alpha) {
   __shared__ float part[4];
   const int e = blockIdx.x, t = blockIdx.y;
   const int lane = lane_id(), wave = wave_id();
@@ -54,7 +55,11 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t
   const float s = wave_sum(acc);
   if (lane == 0) part[wave] = s;
   __syncthreads();
-  if (threadIdx.x == 0) logits[(size_t)t * E + e] = ((part[0] + part[1]) + part[2]) + part[3];
+  if (threadIdx.x == 0) {
+    float l = ((part[0] + part[1]) + part[2]) + part[3];
+    if (health) l = l - alpha * health[e];
+    logits[(size_t)t * E + e] = l;
+  }
 }
 
 // ---------------------------------------------------------- large batches --
@@ -70,7 +75,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 template <int ACT>
 __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t* __restrict__ x,
                                                                  const uint16_t* __restrict__ wr,
-                                                                 float* __restrict__ logits, int T, int H, int E) {
+                                                                 float* __restrict__ logits, int T, int H, int E,
+                                                                 const float* __restrict__ health, float alpha) {
   __shared__ float part[3][16][WAVE];
   const int lane = lane_id(), wave = wave_id();
   const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
@@ -101,8 +107,9 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
     // register i of lane l: token row 8*(i/4) + 4*(l/32) + i%4, expert column l%32
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float v = ((acc[i] + part[0][i][lane]) + part[1][i][lane]) + part[2][i][lane];
+      float v = ((acc[i] + part[0][i][lane]) + part[1][i][lane]) + part[2][i][lane];
       const int tt = t0 + 8 * (i / 4) + 4 * half + (i % 4), ee = e0 + r32;
+      if (health) v = v - alpha * health[e];  // e = min(ee, E - 1): equal to ee where stored
       if (tt < T && ee < E) logits[(size_t)tt * E + ee] = v;
     }
   }
@@ -110,7 +117,7 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
 
 // ------------------------------------------------------------- selection --
 
-__global__ __launch_bounds__(256) void topk_static_kernel(const float* __restrict__ logits, int T, int E, int k,
+__global__ __launch_bounds__(256) void topk_static_kernel(const float* __restrict__ logits, int T, int E, int k, int gs,
                                                           int32_t* __restrict__ idx, float* __restrict__ w,
                                                           int32_t* __restrict__ k_used, float* __restrict__ entropy) {
   const int t = blockIdx.x * 4 + wave_id();
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(256) void topk_static_kernel(const float* __restric
   if (t >= T) return;
   int si[MOE_MAX_K_DEV];
   float sw[MOE_MAX_K_DEV];
-  route_token(logits + (size_t)t * E, E, k, si, sw);
+  route_token(logits + (size_t)t * E, E, k, si, sw, gs);
   if (lane_id() == 0) {
 #pragma unroll
     for (int s = 0; s < MOE_MAX_K_DEV; ++s)
@@ -162,7 +169,7 @@ __device__ __forceinline__ float wave_entropy(const float* __restrict__ row, int
 // One workgroup of 16 waves.  Wave w handles tokens w, w+16, ...; its
 // entropies are summed in token order, the 16 wave partials in wave order,
 // so the batch entropy does not depend on timing.
-__global__ __launch_bounds__(1024) void topk_entropy_kernel(const float* __restrict__ logits, int T, int E,
+__global__ __launch_bounds__(1024) void topk_entropy_kernel(const float* __restrict__ logits, int T, int E, int gs,
                                                             int32_t* __restrict__ idx, float* __restrict__ w,
                                                             int32_t* __restrict__ k_used,
                                                             float* __restrict__ entropy) {
@@ -188,7 +195,7 @@ __global__ __launch_bounds__(1024) void topk_entropy_kernel(const float* __restr
   for (int t = wave; t < T; t += 16) {
     int si[MOE_MAX_K_DEV];
     float sw[MOE_MAX_K_DEV];
-    route_token(logits + (size_t)t * E, E, k, si, sw);
+    route_token(logits + (size_t)t * E, E, k, si, sw, gs);
     if (lane_id() == 0) {
 #pragma unroll
       for (int s = 0; s < KC; ++s) {
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(256) void entropy_tokens_kernel(const float* __rest
   if (lane_id() == 0) hent[t] = h;
 }
 
-__global__ __launch_bounds__(256) void entropy_select_kernel(const float* __restrict__ logits, int T, int E,
+__global__ __launch_bounds__(256) void entropy_select_kernel(const float* __restrict__ logits, int T, int E, int gs,
                                                              const float* __restrict__ hent,
                                                              int32_t* __restrict__ idx, float* __restrict__ w,
                                                              int32_t* __restrict__ k_used,
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(256) void entropy_select_kernel(const float* __rest
   constexpr int KC = MOE_K_ENTROPY_CAP_DEV;
   int si[MOE_MAX_K_DEV];
   float sw[MOE_MAX_K_DEV];
-  route_token(logits + (size_t)t * E, E, k, si, sw);
+  route_token(logits + (size_t)t * E, E, k, si, sw, gs);
   if (lane == 0) {
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
@@ -254,35 +261,85 @@ __global__ __launch_bounds__(256) void entropy_select_kernel(const float* __rest
 int router_small_max_tokens() { return 128; }
 
 hipError_t launch_router_logits(const void* x, const void* wr, float* logits, int T, int H, int E, int act,
-                                hipStream_t st) {
+                                const float* health, float alpha, hipStream_t st) {
   if (T > router_small_max_tokens()) {
     dim3 grid((T + 31) / 32, (E + 31) / 32);
     if (act == ACT_BF16)
       return launch_kernel(router_logits_mfma_kernel<ACT_BF16>, grid, 256, 0, st, (const uint16_t*)x,
-                           (const uint16_t*)wr, logits, T, H, E);
+                           (const uint16_t*)wr, logits, T, H, E, health, alpha);
     return launch_kernel(router_logits_mfma_kernel<ACT_F16>, grid, 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr,
-                         logits, T, H, E);
+                         logits, T, H, E, health, alpha);
   }
   launch_kernel(router_logits_small_kernel, dim3(E, T), 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr, logits, H,
-                E, act);
+                E, act, health, alpha);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, int32_t* k_used,
+hipError_t launch_topk(const float* logits, int T, int E, int k, int gs, int32_t* idx, float* w, int32_t* k_used,
                        float* entropy, float* scratch, hipStream_t st) {
   if (k <= 0 && scratch) {
     const unsigned g = (unsigned)((T + 3) / 4);
     hipError_t e = launch_kernel(entropy_tokens_kernel, g, 256, 0, st, logits, T, E, scratch);
     if (e != hipSuccess) return e;
-    return launch_kernel(entropy_select_kernel, g, 256, 0, st, logits, T, E, (const float*)scratch, idx, w, k_used,
-                         entropy);
+    return launch_kernel(entropy_select_kernel, g, 256, 0, st, logits, T, E, gs, (const float*)scratch, idx, w,
+                         k_used, entropy);
   }
   if (k > 0) {
-    launch_kernel(topk_static_kernel, (T + 3) / 4, 256, 0, st, logits, T, E, k, idx, w, k_used, entropy);
+    launch_kernel(topk_static_kernel, (T + 3) / 4, 256, 0, st, logits, T, E, k, gs, idx, w, k_used, entropy);
   } else {
-    launch_kernel(topk_entropy_kernel, 1, 1024, 0, st, logits, T, E, idx, w, k_used, entropy);
+    launch_kernel(topk_entropy_kernel, 1, 1024, 0, st, logits, T, E, gs, idx, w, k_used, entropy);
   }
   return hipGetLastError();
+}
+
+// ------------------------------------------------------- load statistics --
+//
+// One wave.  Lane l holds the counts of experts l, l+64, l+128, l+192: the
+// least-used expert is the smallest (count, index) over the wave; the
+// standard deviation is sqrt(sum_e (c_e - mean)^2 / E) with the mean from the
+// exact integer total and the squares summed in fp64 (page "Qwen3.5-MoE与
+// Qwen3-MoE架构差异深度解析", closing advice: watch the least-activated expert
+// and the standard deviation of the activation counts).  E <= 256.
+__global__ __launch_bounds__(64) void load_stats_kernel(const int32_t* __restrict__ counts, int E,
+                                                         int32_t* __restrict__ least_used, float* __restrict__ sd) {
+  const int lane = lane_id();
+  int c[4];
+  int64_t s1 = 0;
+  int best_c = 0, best_e = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + WAVE * j;
+    c[j] = e < E ? counts[e] : 0;
+    s1 += c[j];
+    if (e < E && (best_e < 0 || c[j] < best_c)) {  // e grows with j: a lane keeps its lowest index among equals
+      best_c = c[j];
+      best_e = e;
+    }
+  }
+  for (int off = 1; off < WAVE; off <<= 1) {
+    s1 += __shfl_xor(s1, off);
+    const int oc = __shfl_xor(best_c, off), oe = __shfl_xor(best_e, off);
+    const bool take = oe >= 0 && (best_e < 0 || oc < best_c || (oc == best_c && oe < best_e));
+    best_c = take ? oc : best_c;
+    best_e = take ? oe : best_e;
+  }
+  const double mean = (double)s1 / (double)E;
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (lane + WAVE * j < E) {
+      const double d = (double)c[j] - mean;
+      ss += d * d;
+    }
+  for (int off = 1; off < WAVE; off <<= 1) ss += __shfl_xor(ss, off);
+  if (lane == 0) {
+    *least_used = best_e;
+    *sd = (float)sqrt(ss / (double)E);
+  }
+}
+
+hipError_t launch_load_stats(const int32_t* counts, int E, int32_t* least_used, float* stddev, hipStream_t st) {
+  return launch_kernel(load_stats_kernel, 1, 64, 0, st, counts, E, least_used, stddev);
 }
 
 }  // namespace moe

@@ -3,6 +3,11 @@
 // with the same operations, so every kernel sees the same experts and weights).
 //
 // Key: larger logit first, lower expert index first among equal logits.
+// Groups (gs > 1 experts each, consecutive): choosing an expert retires its
+// whole group, so at most one expert per group is chosen, and the slots are
+// the best experts of the best groups in key order (page "Qwen3.5 Block在
+// llama.cpp中的映射与优化原理", section 1.1: 64 experts in 4 groups of 16, the
+// best of each group).  gs = 1 is plain top-k.
 // Weights: exp(l_s - l_1) / sum over the selected slots of exp(l_s' - l_1),
 // i.e. the softmax renormalised over the selected experts (page "Qwen3.5
 // Block在llama.cpp中的映射与优化原理", section 4.1: linear -> softmax -> top-k).
@@ -57,15 +62,17 @@ __device__ __forceinline__ Cand wave_best(Cand c) {
 // One wave selects k of token t's E <= 256 logits (4 per lane, expert
 // e = lane + 64*j).  Returns the selected logits/indices in slot order in
 // every lane (arrays of MOE_MAX_K).
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, float* sv, int* si) {
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, float* sv, int* si, int gs) {
   const int lane = lane_id();
   float v[4];
   bool live[4];
+  int grp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     int e = lane + 64 * j;
     live[j] = e < E;
     v[j] = live[j] ? row[e] : 0.0f;
+    grp[j] = e / gs;
   }
 #pragma unroll
   for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
@@ -79,9 +86,10 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
       c = wave_best(c);
       sv[s] = c.v;
       si[s] = c.i;
+      const int cg = c.i / gs;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (lane + 64 * j == c.i) live[j] = false;
+        if (grp[j] == cg) live[j] = false;
     }
   }
 }
@@ -109,10 +117,11 @@ __device__ __forceinline__ void write_selection(int32_t* idx, float* w, const fl
 
 
 // Select k experts of one token; every lane receives the same idx/w arrays.
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int* idx, float* w) {
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int* idx, float* w,
+                                            int gs) {
   float sv[MOE_MAX_K_DEV];
   int si[MOE_MAX_K_DEV];
-  wave_topk(row, E, k, sv, si);
+  wave_topk(row, E, k, sv, si, gs);
   float ex[MOE_MAX_K_DEV];
   float z = 0.0f;
 #pragma unroll
@@ -135,15 +144,17 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
 // decode kernel runs this before its first weight load, and a short code path
 // is fetched into the instruction cache faster.
 __device__ __forceinline__ void route_slot(const float* __restrict__ row, int E, int k, int slot, int& e_out,
-                                           float& w_out) {
+                                           float& w_out, int gs) {
   const int lane = lane_id();
   float v[4];
   bool live[4];
+  int grp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
     live[j] = e < E;
     v[j] = live[j] ? row[e] : 0.0f;
+    grp[j] = e / gs;
   }
   float v0 = 0.0f, z = 0.0f, mine = 0.0f;
   int mye = 0;
@@ -163,9 +174,10 @@ __device__ __forceinline__ void route_slot(const float* __restrict__ row, int E,
       mye = c.i;
       mine = ex;
     }
+    const int cg = c.i / gs;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j == c.i) live[j] = false;
+      if (grp[j] == cg) live[j] = false;
   }
   e_out = mye;
   w_out = mine / z;

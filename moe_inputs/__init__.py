@@ -173,6 +173,16 @@ def zipf_sets(seed: int, T: int, E: int, k: int, s: float, t0: int = 0) -> np.nd
     return out
 
 
+def load_index(seed: int, E: int, s: float = 1.1, window: int = 100, tokens: int = 64, k: int = 2) -> np.ndarray:
+    """A per-expert load index H [E] fp32 with mean 1: the activation counts of
+    `window` steps of `tokens` tokens routed top-k with Zipf(s) expert
+    popularity, divided by their mean (the activation frequency over a recent
+    window that a load-aware router subtracts, scaled, from its logits)."""
+    sets = zipf_sets(seed, window * tokens, E, min(k, E), s)
+    c = np.bincount(sets.ravel(), minlength=E).astype(np.float64)
+    return (c / c.mean()).astype(np.float32)
+
+
 def planted_x(seed: int, T: int, H: int, wr: np.ndarray, dtype: str, sets: np.ndarray, gamma: float = 8.0,
               t0: int = 0):
     """Activations of tokens [t0, t0+T) with each token's set planted."""

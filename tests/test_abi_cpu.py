@@ -190,3 +190,43 @@ def test_debug_plan_hooks_are_callable_without_gpu():
     L.moe_debug_set_events(None, 0)
     buf = ctypes.create_string_buffer(64)
     assert L.moe_debug_last_plan(buf, 64) >= 0
+
+
+def test_route_options_validation():
+    """moe_route_opts: group count, k against the groups, health alignment,
+    and health refused where the logits are taken as final."""
+    L = moe.lib()
+    ws = 1 << 20
+    O = lambda health=None, alpha=0.0, groups=0: ctypes.byref(moe.CRouteOpts(health, alpha, groups))
+    call = lambda opts, E=8, k=2: L.moe_route_ex(P, 1, 4, 256, P, E, k, opts, P, P, None, None, None, P, ws, None)
+    st = lambda v: moe.STATUS[v]
+    assert st(call(O(groups=-1))) == "MOE_ERR_OPTION"
+    assert st(call(O(groups=3))) == "MOE_ERR_OPTION"          # 8 % 3 != 0
+    assert st(call(O(groups=2), k=4)) == "MOE_ERR_OPTION"     # one per group: k <= groups
+    assert st(call(O(groups=2), k=-1)) == "MOE_ERR_OPTION"    # entropy mode needs 3 groups
+    assert st(call(O(health=P + 2, alpha=1.0))) == "MOE_ERR_ALIGN"
+    # valid options get past validation to the device check (no GPU here)
+    import torch
+    if not torch.cuda.is_available():
+        for o in (None, O(groups=4), O(groups=1), O(health=P, alpha=0.5, groups=2), O(groups=8, health=P)):
+            assert st(call(o)) == "MOE_ERR_DEVICE"
+        assert st(call(O(groups=4), k=-1, E=12)) == "MOE_ERR_DEVICE"
+    tk = lambda opts, k=2: L.moe_topk_from_logits_ex(P, 4, 8, k, opts, P, P, None, None, None, 0, None)
+    assert st(tk(O(health=P))) == "MOE_ERR_OPTION"
+    assert st(tk(O(groups=2), k=3)) == "MOE_ERR_OPTION"
+    # the layer entry point applies the same checks
+    ref = lambda w: ctypes.byref(w)
+    gu, dn = W(8, 256, 256), W(8, 256, 128)
+    lay = lambda opts: L.moe_layer_forward_ex(P, 1, 4, 256, P, 8, 2, opts, ref(gu), None, None, ref(dn), P, 0, None,
+                                              P, L.moe_layer_workspace_size(4, 256, 8, 2, 128, 0), None)
+    assert st(lay(O(groups=5))) == "MOE_ERR_OPTION"
+    assert st(lay(O(health=P + 1))) == "MOE_ERR_ALIGN"
+
+
+def test_load_stats_validation():
+    L = moe.lib()
+    st = lambda v: moe.STATUS[v]
+    assert st(L.moe_expert_load_stats(P, 0, P, P, None)) == "MOE_ERR_SHAPE"
+    assert st(L.moe_expert_load_stats(P, 257, P, P, None)) == "MOE_ERR_SHAPE"
+    assert st(L.moe_expert_load_stats(None, 8, P, P, None)) == "MOE_ERR_NULL"
+    assert st(L.moe_expert_load_stats(P, 8, P + 2, P, None)) == "MOE_ERR_ALIGN"
