@@ -53,8 +53,10 @@ def _load():
     lib.oracle_correct_logits.argtypes = [vp, i32, i32, vp, f32]
     lib.oracle_load_stats.argtypes = [vp, i32, vp, vp]
     lib.oracle_route_ex.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, f32, i32, vp, vp, vp, vp, vp]
-    lib.oracle_layer_forward_ex.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, f32, i32, vp, vp, vp, vp, vp, vp,
-                                            i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.oracle_layer_forward_ex.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, f32, i32, i32, vp, vp, vp, vp, vp,
+                                            vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.oracle_capacity_keep.argtypes = [vp, i32, i32, i32, i32, i32, vp]
+    lib.oracle_sort_pairs_capped.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.oracle_token_entropy.argtypes = [vp, i32]
     lib.oracle_token_entropy.restype = f32
     lib.oracle_entropy_k.argtypes = [f32]
@@ -211,8 +213,9 @@ def route(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, want_logits: bool =
     return res + (logits,) if want_logits else res
 
 
-def sort_pairs(idx: np.ndarray, k_used: int, E: int):
-    """Returns (counts [E], offsets [E+1], perm [P], pos [P])."""
+def sort_pairs(idx: np.ndarray, k_used: int, E: int, capacity: int = 0):
+    """Returns (counts [E], offsets [E+1], perm [P], pos [P]); capacity > 0
+    keeps the first `capacity` pairs of every expert (dropped: pos -1)."""
     idx = _c(idx, np.int32)
     T, kcap = idx.shape
     P = T * kcap
@@ -220,8 +223,21 @@ def sort_pairs(idx: np.ndarray, k_used: int, E: int):
     offsets = np.empty(E + 1, np.int32)
     perm = np.empty(P, np.int32)
     pos = np.empty(P, np.int32)
-    _load().oracle_sort_pairs(_p(idx), T, kcap, k_used, E, _p(counts), _p(offsets), _p(perm), _p(pos))
+    if capacity > 0:
+        _load().oracle_sort_pairs_capped(_p(idx), T, kcap, k_used, E, int(capacity), _p(counts), _p(offsets),
+                                         _p(perm), _p(pos))
+    else:
+        _load().oracle_sort_pairs(_p(idx), T, kcap, k_used, E, _p(counts), _p(offsets), _p(perm), _p(pos))
     return counts, offsets, perm, pos
+
+
+def capacity_keep(idx: np.ndarray, k_used: int, E: int, capacity: int) -> np.ndarray:
+    """bool [T, kcap]: the pairs kept under a per-expert capacity."""
+    idx = _c(idx, np.int32)
+    T, kcap = idx.shape
+    keep = np.empty((T, kcap), np.uint8)
+    _load().oracle_capacity_keep(_p(idx), T, kcap, k_used, E, int(capacity), _p(keep))
+    return keep.astype(bool)
 
 
 def fuse_gate_up(gate, up):
@@ -289,7 +305,7 @@ def tokens_forward(x: np.ndarray, dtype: str, tokens: Sequence[int], idx: np.nda
 
 
 def layer_forward(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, gate_up, down,
-                  health: Optional[np.ndarray] = None, alpha: float = 0.0, groups: int = 0):
+                  health: Optional[np.ndarray] = None, alpha: float = 0.0, groups: int = 0, capacity: int = 0):
     """The whole layer.  Returns dict(y bits, y_f32, idx, w, k_used, h_mean)."""
     x = _c(x, np.uint16)
     wr = _c(wr, np.uint16)
@@ -304,6 +320,7 @@ def layer_forward(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, gate_up, do
     hm = np.zeros(1, np.float32)
     h = _c(health, np.float32)
     _load().oracle_layer_forward_ex(_p(x), DTYPE_CODE[dtype], T, H, _p(wr), E, k, _p(h), float(alpha), int(groups),
+                                    int(capacity),
                                     _p(gate_up.q), _p(gate_up.scales), _p(gate_up.biases), _p(down.q),
                                     _p(down.scales), _p(down.biases), down.K, down.bits, down.group_size, _p(y),
                                     _p(yf), _p(idx), _p(w), _p(ku), _p(hm))

@@ -39,6 +39,11 @@
  *               most one expert chosen per group: each group's best expert,
  *               then the k best of those (llama.cpp page, section 1.1: 64
  *               experts in 4 groups of 16, the best of each group, 4 chosen).
+ *   capacity    at most C (token, slot) pairs per expert: the first C in pair
+ *               order are kept, the rest dropped and contribute nothing to the
+ *               output (page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析", section
+ *               5.2: a per-expert token capacity, expert_capacity=8; which
+ *               pairs overflow is not stated, so the earliest are kept).
  *   load stats  the least-used expert and the standard deviation of the
  *               per-expert activation counts (page "Qwen3.5-MoE与Qwen3-MoE
  *               架构差异深度解析", the closing advice on monitoring MoE health).
@@ -369,6 +374,53 @@ void oracle_sort_pairs(const int32_t* idx, int T, int kcap, int k_used, int E, i
   free(fill);
 }
 
+/*
+ * Capacity: keep[p] = 1 for the first `capacity` valid pairs of every expert
+ * in ascending pair id, 0 for the rest and for the unused slots; capacity
+ * <= 0 keeps every valid pair.
+ */
+void oracle_capacity_keep(const int32_t* idx, int T, int kcap, int k_used, int E, int capacity, uint8_t* keep) {
+  int64_t P = (int64_t)T * kcap;
+  int32_t* seen = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int64_t p = 0; p < P; ++p) {
+    if (p % kcap >= k_used) {
+      keep[p] = 0;
+      continue;
+    }
+    int e = idx[p];
+    keep[p] = (uint8_t)(capacity <= 0 || seen[e] < capacity);
+    seen[e]++;
+  }
+  free(seen);
+}
+
+/* the pair sort over the kept pairs only (dropped pairs get pos -1) */
+void oracle_sort_pairs_capped(const int32_t* idx, int T, int kcap, int k_used, int E, int capacity, int32_t* counts,
+                              int32_t* offsets, int32_t* perm, int32_t* pos) {
+  int64_t P = (int64_t)T * kcap;
+  uint8_t* keep = (uint8_t*)malloc((size_t)(P > 0 ? P : 1));
+  oracle_capacity_keep(idx, T, kcap, k_used, E, capacity, keep);
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < P; ++p)
+    if (keep[p]) counts[idx[p]]++;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (int64_t p = 0; p < P; ++p) perm[p] = -1;
+  for (int64_t p = 0; p < P; ++p) {
+    if (!keep[p]) {
+      pos[p] = -1;
+      continue;
+    }
+    int e = idx[p];
+    int32_t at = offsets[e] + fill[e]++;
+    perm[at] = (int32_t)p;
+    pos[p] = at;
+  }
+  free(fill);
+  free(keep);
+}
+
 /* ------------------------------------------------ gate/up packing ------ */
 
 /*
@@ -490,6 +542,7 @@ void oracle_tokens_forward(const uint16_t* x, int dtype, int H, const int32_t* t
     for (int h = 0; h < H; ++h) y[h] = 0.0f;
     for (int s = 0; s < k_used; ++s) {
       int e = idx[(int64_t)t * kcap + s];
+      if (e < 0) continue; /* a dropped pair (capacity) contributes nothing */
       float ws = w[(int64_t)t * kcap + s];
       const uint8_t* eq = (const uint8_t*)guq + (int64_t)e * gu_rows * rbh;
       const uint16_t* es = gus ? gus + (int64_t)e * gu_rows * ngh : NULL;
@@ -520,29 +573,38 @@ void oracle_round_output(const float* y_f32, int64_t n, int dtype, uint16_t* y) 
  * y_f32 (may be NULL) the unrounded fp32 result.
  */
 void oracle_layer_forward_ex(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k,
-                             const float* health, float alpha, int groups, const void* guq, const uint16_t* gus,
-                             const uint16_t* gub, const void* dq, const uint16_t* ds, const uint16_t* db, int I,
-                             int bits, int gsz, uint16_t* y, float* y_f32, int32_t* idx, float* w, int32_t* k_used,
-                             float* h_mean) {
+                             const float* health, float alpha, int groups, int capacity, const void* guq,
+                             const uint16_t* gus, const uint16_t* gub, const void* dq, const uint16_t* ds,
+                             const uint16_t* db, int I, int bits, int gsz, uint16_t* y, float* y_f32, int32_t* idx,
+                             float* w, int32_t* k_used, float* h_mean) {
   int ku = 0;
   oracle_route_ex(x, dtype, T, H, wr, E, k, health, alpha, groups, idx, w, &ku, h_mean, NULL);
   if (k_used) *k_used = ku;
   int kcap = k > 0 ? k : 3;
+  /* the experts of the dropped pairs become -1 in a copy; idx stays the routing */
+  int64_t P = (int64_t)T * kcap;
+  int32_t* idx_kept = (int32_t*)malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+  uint8_t* keep = (uint8_t*)malloc((size_t)(P > 0 ? P : 1));
+  oracle_capacity_keep(idx, T, kcap, ku, E, capacity, keep);
+  for (int64_t p = 0; p < P; ++p) idx_kept[p] = keep[p] ? idx[p] : -1;
   int32_t* tokens = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
   for (int t = 0; t < T; ++t) tokens[t] = t;
   float* yf = y_f32 ? y_f32 : (float*)malloc(sizeof(float) * (size_t)T * H);
-  oracle_tokens_forward(x, dtype, H, tokens, T, idx, w, kcap, ku, guq, gus, gub, dq, ds, db, I, bits, gsz, yf, NULL);
+  oracle_tokens_forward(x, dtype, H, tokens, T, idx_kept, w, kcap, ku, guq, gus, gub, dq, ds, db, I, bits, gsz, yf,
+                        NULL);
   oracle_round_output(yf, (int64_t)T * H, dtype, y);
   if (!y_f32) free(yf);
   free(tokens);
+  free(idx_kept);
+  free(keep);
 }
 
 void oracle_layer_forward(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k,
                           const void* guq, const uint16_t* gus, const uint16_t* gub, const void* dq,
                           const uint16_t* ds, const uint16_t* db, int I, int bits, int gsz, uint16_t* y,
                           float* y_f32, int32_t* idx, float* w, int32_t* k_used, float* h_mean) {
-  oracle_layer_forward_ex(x, dtype, T, H, wr, E, k, NULL, 0.0f, 0, guq, gus, gub, dq, ds, db, I, bits, gsz, y, y_f32,
-                          idx, w, k_used, h_mean);
+  oracle_layer_forward_ex(x, dtype, T, H, wr, E, k, NULL, 0.0f, 0, 0, guq, gus, gub, dq, ds, db, I, bits, gsz, y,
+                          y_f32, idx, w, k_used, h_mean);
 }
 
 int oracle_num_threads(void) {

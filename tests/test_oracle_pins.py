@@ -555,3 +555,65 @@ def test_route_with_options_is_correction_then_grouped_selection():
     assert np.array_equal(logits, oracle.correct_logits(raw, hv, 0.75))
     i2, w2 = oracle.select_topk(logits, 2, groups=4)
     assert np.array_equal(idx, i2) and np.array_equal(w, w2)
+
+
+# ------------------------------------------------------------- capacity --
+# Page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析", section 5.2: a per-expert token
+# capacity (expert_capacity).  Reading: the first C pairs of an expert in pair
+# order are kept, the rest contribute nothing.
+
+def _keep_brute(idx, ku, C):
+    T, kcap = idx.shape
+    flat = idx.ravel()
+    valid = (np.arange(T * kcap) % kcap) < ku
+    return np.array([bool(valid[p]) and (C <= 0 or sum(1 for q in range(p) if valid[q] and flat[q] == flat[p]) < C)
+                     for p in range(T * kcap)]).reshape(T, kcap)
+
+
+@pytest.mark.parametrize("T,kcap,ku,E,C", [(9, 2, 2, 4, 1), (13, 3, 2, 5, 2), (20, 4, 4, 6, 3), (7, 3, 3, 3, 0),
+                                           (16, 2, 2, 2, 16)])
+def test_capacity_keep_brute_force_and_sort(T, kcap, ku, E, C):
+    rng = np.random.default_rng(T * 100 + C)
+    for _ in range(10):
+        idx = rng.integers(0, E, size=(T, kcap)).astype(np.int32)
+        keep = oracle.capacity_keep(idx, ku, E, C)
+        assert np.array_equal(keep, _keep_brute(idx, ku, C))
+        c0, o0, p0, _ = oracle.sort_pairs(idx, ku, E)
+        c1, o1, p1, pos1 = oracle.sort_pairs(idx, ku, E, capacity=C)
+        want = np.minimum(c0, C) if C > 0 else c0
+        assert np.array_equal(c1, want)
+        assert np.array_equal(o1, np.concatenate([[0], np.cumsum(want)]))
+        for e in range(E):  # an expert's kept list is the prefix of its full list
+            assert np.array_equal(p1[o1[e]:o1[e + 1]], p0[o0[e]:o0[e] + want[e]])
+        assert (p1[o1[-1]:] == -1).all()
+        flat_keep = keep.ravel()
+        assert ((pos1 >= 0) == flat_keep).all()
+        assert (p1[pos1[flat_keep]] == np.flatnonzero(flat_keep)).all()
+
+
+def test_capacity_layer_drops_whole_pairs():
+    inp = mi.make_inputs("tiny", T=12)
+    gu = oracle.fuse_gate_up(inp.gate, inp.up)
+    full = oracle.layer_forward(inp.x, inp.wr, inp.dtype, inp.k, gu, inp.down)
+    counts = np.bincount(full["idx"].ravel(), minlength=inp.E)
+    # a capacity at or above every count changes nothing, bit for bit
+    same = oracle.layer_forward(inp.x, inp.wr, inp.dtype, inp.k, gu, inp.down, capacity=int(counts.max()))
+    assert np.array_equal(same["y"], full["y"]) and np.array_equal(same["y_f32"], full["y_f32"])
+    for C in (1, 2):
+        cap = oracle.layer_forward(inp.x, inp.wr, inp.dtype, inp.k, gu, inp.down, capacity=C)
+        assert np.array_equal(cap["idx"], full["idx"])  # routing itself is unchanged
+        keep = oracle.capacity_keep(full["idx"], inp.k, inp.E, C)
+        assert keep.sum() == np.minimum(counts, C).sum()
+        for t in range(inp.T):
+            # each token's output is the slot-order sum over its kept slots
+            # only: the full layer rebuilt one slot at a time
+            acc = np.zeros(inp.H, np.float32)
+            for s in range(inp.k):
+                if keep[t, s]:
+                    one = np.full((1, inp.k), -1, np.int32)
+                    one[0, s] = full["idx"][t, s]
+                    acc = acc + oracle.tokens_forward(inp.x[t:t + 1], inp.dtype, [0], one, full["w"][t:t + 1],
+                                                      inp.k, gu, inp.down)[0]
+            assert np.array_equal(cap["y_f32"][t], acc)
+            if not keep[t].any():
+                assert not cap["y_f32"][t].any()
