@@ -56,13 +56,34 @@ def weight_bytes_per_row(K: int, bits: int) -> int:
     return K * bits // 8 + (0 if bits == 16 else 2 * 2 * (K // 64))
 
 
-def algorithmic(name: str, kernel: str, *, T, H, E, I, bits, idx, k_used, kcap):
+def capacity_keep(idx: np.ndarray, k_used: int, capacity: int) -> np.ndarray:
+    """bool [T, kcap]: pairs within the first `capacity` of their expert in pair order."""
+    T, kcap = idx.shape
+    keep = np.zeros((T, kcap), bool)
+    keep[:, :k_used] = True
+    if capacity > 0:
+        flat = idx.ravel()
+        valid = keep.ravel()
+        seen = {}
+        for p in np.flatnonzero(valid):
+            e = int(flat[p])
+            seen[e] = seen.get(e, 0) + 1
+            if seen[e] > capacity:
+                valid[p] = False
+        keep = valid.reshape(T, kcap)
+    return keep
+
+
+def algorithmic(name: str, kernel: str, *, T, H, E, I, bits, idx, k_used, kcap, keep=None):
     """Algorithmic HBM bytes and flops of one launch of `kernel`.
 
     Bytes: every touched expert's weight rows (codes plus fp16 scale/bias)
     read once, plus the activations read and the outputs written once.
     """
-    sel = idx[:, :k_used]
+    if keep is not None and kernel != "gemv_gate_up_swiglu":  # the decode gate+up computes dropped pairs too
+        sel = idx[keep]
+    else:
+        sel = idx[:, :k_used]
     touched = np.unique(sel)
     pairs = sel.size
     if kernel in ("gemv_gate_up_swiglu", "gemm_gate_up_swiglu"):
@@ -115,6 +136,11 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain elementwise copy (torch.neg) of this many MiB, 5 launches: the known-size "
                          "kernel that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--load-aware", type=float, default=None, metavar="ALPHA",
+                    help="route with the load-aware correction: logits - ALPHA * H, H a seeded load index "
+                         "(activation counts of a Zipf-1.1 window, mean 1)")
+    ap.add_argument("--groups", type=int, default=0, help="group-limited routing: at most one expert per group")
+    ap.add_argument("--capacity", type=int, default=0, help="expert capacity: at most this many pairs per expert")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -179,8 +205,16 @@ def main():
             return x_pool[i:i + 1]
         return x_pool
 
+    ropt = {}
+    if args.load_aware is not None:
+        ropt["health"] = torch.from_numpy(mi.load_index(5, E)).cuda()
+        ropt["alpha"] = args.load_aware
+    if args.groups:
+        ropt["groups"] = args.groups
+    lopt = dict(ropt, capacity=args.capacity) if args.capacity else ropt
+
     def step(i):
-        moe.layer_forward(x_of(i), wr, k, down, gate_up=gate_up, out=y, workspace=ws)
+        moe.layer_forward(x_of(i), wr, k, down, gate_up=gate_up, out=y, workspace=ws, **lopt)
 
     # discover the kernel plan
     step(0)
@@ -277,7 +311,7 @@ def main():
     j = int(np.argmax(per_kernel_us))
     kern = plan[j]
     # routing of a representative step (decode: over the pool; averaged bytes)
-    r = moe.route(x_pool, wr, k)
+    r = moe.route(x_pool, wr, k, **ropt)
     torch.cuda.synchronize()
     idx_all = r["idx"].cpu().numpy()
     ku = int(r["k_used"].item())
@@ -285,13 +319,14 @@ def main():
         bs, fs = [], []
         for s in range(min(wl["pool"], K)):
             b_, f_ = algorithmic(args.workload, kern, T=1, H=H, E=E, I=I, bits=bits, idx=idx_all[s:s + 1],
-                                 k_used=ku, kcap=kcap)
+                                 k_used=ku, kcap=kcap,
+                                 keep=capacity_keep(idx_all[s:s + 1], ku, args.capacity) if args.capacity else None)
             bs.append(b_)
             fs.append(f_)
         alg_b, alg_f = float(np.mean(bs)), float(np.mean(fs))
     else:
         alg_b, alg_f = algorithmic(args.workload, kern, T=T, H=H, E=E, I=I, bits=bits, idx=idx_all, k_used=ku,
-                                   kcap=kcap)
+                                   kcap=kcap, keep=capacity_keep(idx_all, ku, args.capacity) if args.capacity else None)
     dur_s = per_kernel_us[j] * 1e-6
     gbs = alg_b / dur_s / 1e9
     tflops = alg_f / dur_s / 1e12
@@ -313,10 +348,16 @@ def main():
         import oracle
         gu_np = oracle.fuse_gate_up(inp.gate, inp.up)
         cores = oracle.num_threads()
+        oopt = {}
+        if "health" in ropt:
+            oopt = dict(health=ropt["health"].cpu().numpy(), alpha=ropt["alpha"])
+        if args.groups:
+            oopt["groups"] = args.groups
+        lo = dict(oopt, capacity=args.capacity) if args.capacity else oopt
         if wl["pool"]:
             def run(n):
                 t = time.perf_counter()
-                oracle.layer_forward(np.ascontiguousarray(inp.x[:n]), inp.wr, inp.dtype, k, gu_np, inp.down)
+                oracle.layer_forward(np.ascontiguousarray(inp.x[:n]), inp.wr, inp.dtype, k, gu_np, inp.down, **lo)
                 return time.perf_counter() - t
             n0 = 4
             t_probe = run(n0)
@@ -325,7 +366,7 @@ def main():
             cpu = {"value": round(n / t_run, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
                    "sample": "%d single tokens of the decode pool (each: route + 4 experts), %.1fs" % (n, t_run)}
         else:
-            idx_o, w_o, ku_o, _ = oracle.route(inp.x, inp.wr, inp.dtype, k)
+            idx_o, w_o, ku_o, _ = oracle.route(inp.x, inp.wr, inp.dtype, k, **oopt)
             rng = np.random.default_rng(0)
             t = time.perf_counter()
             oracle.tokens_forward(inp.x, inp.dtype, [0], idx_o, w_o, ku_o, gu_np, inp.down)
@@ -333,7 +374,7 @@ def main():
             n = int(max(2, min(T, args.cpu_seconds / max(per_tok, 1e-6))))
             toks = np.sort(rng.choice(T, n, replace=False))
             t = time.perf_counter()
-            oracle.route(inp.x, inp.wr, inp.dtype, k)
+            oracle.route(inp.x, inp.wr, inp.dtype, k, **oopt)
             t_route = time.perf_counter() - t
             t = time.perf_counter()
             oracle.tokens_forward(inp.x, inp.dtype, toks, idx_o, w_o, ku_o, gu_np, inp.down)
@@ -362,6 +403,8 @@ def main():
                    "launch": mode, "eager_tokens_per_s": round(K * T / eager_s, 2),
                    "graph_tokens_per_s": round(K * T / graph_s, 2) if graph_s else None,
                    "kernels_per_step": nk, "plan": plan,
+                   "routing_options": {"load_aware_alpha": args.load_aware, "groups": args.groups,
+                                       "capacity": args.capacity} if lopt else None,
                    "per_kernel_us": [round(float(v), 3) for v in per_kernel_us]},
         "roofline": roof,
         "cpu_baseline": cpu,

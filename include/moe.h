@@ -169,7 +169,16 @@ typedef struct {
  *            4 chosen).  Needs E % G == 0 and k <= G (with MOE_K_ENTROPY:
  *            G >= 3).  The weights stay the softmax over all E experts,
  *            renormalised over the chosen ones.
+ *   capacity 0: no limit.  C > 0 (moe_layer_forward_ex only): at most C
+ *            (token, slot) pairs per expert, the first C in pair order
+ *            t*kcap+s; the others are dropped and add nothing to y (their
+ *            routing weight is not handed to the other slots).  Page
+ *            "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析", section 5.2: a per-
+ *            expert token capacity (expert_capacity).  The topk taps keep
+ *            the routing; counts/offsets/perm list the kept pairs only; the
+ *            h rows of dropped pairs are unspecified.
  * MOE_ERR_OPTION: groups < 0, E % groups != 0, k too large for the groups,
+ * capacity < 0, capacity given to moe_route_ex / moe_topk_from_logits_ex,
  * or (moe_topk_from_logits_ex) health given.  MOE_ERR_ALIGN: health not
  * 4-byte aligned.
  */
@@ -177,6 +186,7 @@ typedef struct {
   const float* health;
   float alpha;
   int32_t groups;
+  int32_t capacity;
 } moe_route_opts;
 
 /* flags of moe_layer_forward */

@@ -52,7 +52,8 @@ class CWeights(ctypes.Structure):
 
 
 class CRouteOpts(ctypes.Structure):
-    _fields_ = [("health", ctypes.c_void_p), ("alpha", ctypes.c_float), ("groups", ctypes.c_int32)]
+    _fields_ = [("health", ctypes.c_void_p), ("alpha", ctypes.c_float), ("groups", ctypes.c_int32),
+                ("capacity", ctypes.c_int32)]
 
 
 class CTaps(ctypes.Structure):
@@ -203,13 +204,13 @@ def _kcap(k: int) -> int:
     return k if k > 0 else MOE_K_ENTROPY_CAP
 
 
-def _opts(health: Optional[torch.Tensor], alpha: float, groups: int):
+def _opts(health: Optional[torch.Tensor], alpha: float, groups: int, capacity: int = 0):
     """moe_route_opts for the *_ex entry points, or None when no option is set."""
-    if health is None and not groups:
+    if health is None and not groups and not capacity:
         return None
     if health is not None:
         assert health.dtype == torch.float32 and health.is_contiguous()
-    return CRouteOpts(_ptr(health), float(alpha), int(groups))
+    return CRouteOpts(_ptr(health), float(alpha), int(groups), int(capacity))
 
 
 def route(x: torch.Tensor, router_w: torch.Tensor, k: int, want_logits: bool = False, stream=None,
@@ -255,7 +256,7 @@ def topk_from_logits(logits: torch.Tensor, k: int, stream=None, groups: int = 0)
         st = lib().moe_topk_from_logits(_ptr(lg), T, E, k, _ptr(idx), _ptr(w), _ptr(ku), _ptr(ent), None, 0,
                                         _stream(stream))
     else:
-        o = CRouteOpts(None, 0.0, int(groups))
+        o = CRouteOpts(None, 0.0, int(groups), 0)
         st = lib().moe_topk_from_logits_ex(_ptr(lg), T, E, k, ctypes.byref(o), _ptr(idx), _ptr(w), _ptr(ku),
                                            _ptr(ent), None, 0, _stream(stream))
     _check(st, "moe_topk_from_logits")
@@ -279,8 +280,9 @@ def layer_forward(x: torch.Tensor, router_w: torch.Tensor, k: int, down: Weights
                   gate: Optional[Weights] = None, up: Optional[Weights] = None, flags: int = 0,
                   taps: Optional[dict] = None, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, stream=None, health: Optional[torch.Tensor] = None,
-                  alpha: float = 0.0, groups: int = 0) -> torch.Tensor:
-    """The whole layer: y [T, H] in the activation dtype (routing options as in route())."""
+                  alpha: float = 0.0, groups: int = 0, capacity: int = 0) -> torch.Tensor:
+    """The whole layer: y [T, H] in the activation dtype (routing options as in
+    route(); capacity > 0: at most that many pairs per expert, moe_route_opts)."""
     T, H = x.shape
     E = router_w.shape[0]
     inter = down.K
@@ -300,7 +302,7 @@ def layer_forward(x: torch.Tensor, router_w: torch.Tensor, k: int, down: Weights
     wargs = (ctypes.byref(cgu) if cgu is not None else None, ctypes.byref(cg) if cg is not None else None,
              ctypes.byref(cu) if cu is not None else None, ctypes.byref(cd), _ptr(y), flags,
              ctypes.byref(ctaps) if ctaps is not None else None, _ptr(ws), ws.numel(), _stream(stream))
-    o = _opts(health, alpha, groups)
+    o = _opts(health, alpha, groups, capacity)
     if o is None:
         st = lib().moe_layer_forward(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k, *wargs)
     else:

@@ -24,6 +24,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   for (int s = 0; s < ku; ++s) {
     const size_t p = (size_t)t * kcap + s;
+    if (pos[p] < 0) continue;  // dropped by the expert capacity
     const float ws = wts[p];
     const u32x4 v = load16(o + (size_t)pos[p] * H + c);
     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};

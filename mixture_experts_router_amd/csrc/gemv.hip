@@ -418,6 +418,7 @@ struct GemvDownParams {
   WView wd;
   void* y;
   int act;
+  int cap;            // expert capacity (0: none)
 };
 
 template <int BITS, int DCPL>
@@ -480,7 +481,27 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
     }
   }
 
-  if (s < ku) {
+  // expert capacity: slot q is kept when fewer than cap earlier valid pairs
+  // of the call chose its expert (page "Qwen3.5-MoE与Qwen3-MoE架构差异深度
+  // 解析", section 5.2); the selection of every pair is in rt.idx
+  uint32_t keep = 0xFFFFFFFFu;
+  if (prm.cap > 0) {
+    keep = 0u;
+    for (int q = 0; q < ku; ++q) {
+      int eq = 0;
+      for_slot(q, [&](int j) { eq = si[j]; });
+      const int pq = t * prm.kcap + q;
+      int before = 0;
+      for (int c0 = 0; c0 < pq; c0 += WAVE) {
+        const int pp = c0 + lane;
+        const bool hit = pp < pq && (pp % prm.kcap) < ku && prm.rt.idx[pp] == eq;
+        before += (int)__popcll(__ballot(hit));
+      }
+      if (before < prm.cap) keep |= 1u << q;
+    }
+  }
+
+  if (s < ku && ((keep >> s) & 1u)) {
     int e = 0;
     for_slot(s, [&](int j) { e = si[j]; });
     e = __builtin_amdgcn_readfirstlane(e);
@@ -572,6 +593,7 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
     if (m < prm.H) {
       float y = 0.0f;
       for (int q = 0; q < ku; ++q) {
+        if (!((keep >> q) & 1u)) continue;  // dropped by the capacity
         float w = 0.0f;
         for_slot(q, [&](int j) { w = sw[j]; });
         float o = part[q][0][lane];
@@ -593,8 +615,10 @@ hipError_t gemv_down_set_max_lds(int bytes) {
 int gemv_down_max_chunks_per_lane() { return 6; }
 
 hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_static, int kcap, int T, int H, int I,
-                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st) {
+                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st, int capacity) {
+  if (capacity > 0 && route.logits) return hipErrorInvalidValue;
   GemvDownParams prm;
+  prm.cap = capacity;
   prm.h = h;
   prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy, route.gs};
   prm.k_static = k_static;

@@ -7,6 +7,7 @@
 
 #define MOE_MAX_K_DEV 8
 #define MOE_K_ENTROPY_CAP_DEV 3
+#define MOE_MAX_EXPERTS_DEV 256
 
 namespace moe {
 
@@ -66,9 +67,11 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int gs, int32_t
                        float* entropy, float* scratch, hipStream_t st);
 
 // ------------------------------------------------------------------ sort
-// k_used_dev may be NULL (then k_static is used)
+// k_used_dev may be NULL (then k_static is used); capacity > 0 lists only the
+// first `capacity` pairs of every expert (the rest get pos -1)
 hipError_t launch_sort_pairs(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
-                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st);
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st,
+                             int capacity = 0);
 
 // ------------------------------------------------- decode (grouped GEMV)
 // chunks of 16 bytes per lane needed for a row of K weights
@@ -96,8 +99,10 @@ size_t gemv_down_lds_bytes(int kcap, int I, int bits);
 hipError_t gemv_down_set_max_lds(int bytes);
 // largest 16-byte chunks per lane of a down row the decode kernels handle
 int gemv_down_max_chunks_per_lane();
+// capacity > 0: a pair beyond the first `capacity` pairs of its expert (pair
+// order) is left out of y (needs route.logits NULL: the selection is read)
 hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_static, int kcap, int T, int H, int I,
-                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st);
+                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st, int capacity = 0);
 // tokens up to which the router uses one workgroup per (expert, token)
 int router_small_max_tokens();
 

@@ -198,13 +198,15 @@ struct RouteOpt {
   const float* health = nullptr;
   float alpha = 0.0f;
   int gs = 1;
+  int cap = 0;  // expert capacity (0: none)
 };
 
 moe_status check_opts(const moe_route_opts* o, int E, int k, RouteOpt* out) {
   *out = RouteOpt{};
   if (!o) return MOE_OK;
   if (o->health && (reinterpret_cast<uintptr_t>(o->health) & 3u) != 0) return MOE_ERR_ALIGN;
-  if (o->groups < 0) return MOE_ERR_OPTION;
+  if (o->groups < 0 || o->capacity < 0) return MOE_ERR_OPTION;
+  out->cap = o->capacity;
   if (o->groups > 1) {
     if (E % o->groups != 0) return MOE_ERR_OPTION;
     const int need = k == MOE_K_ENTROPY ? MOE_K_ENTROPY_CAP : k;
@@ -334,17 +336,17 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     moe::GemvRoute rt_down = rt;
     rt_down.logits = nullptr;
     HIP_TRY(moe::launch_gemv_down(h, rt_down, k_static, kcap, T, H, I, bits, view_of(down, 0), y, act, props.num_cu,
-                                  st));
+                                  st, ro.cap));
     plan_step("gemv_down_combine", st);
     if (want_sort_taps) {
-      HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st));
+      HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st, ro.cap));
       plan_step("sort_pairs", st);
     }
   } else {
     if ((s = route_impl(x, dt, T, H, router_w, E, k, ro, idx, wts, k_used, entropy, logits, (float*)(W + L.hent),
                         st)) != MOE_OK)
       return s;
-    HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st));
+    HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st, ro.cap));
     plan_step("sort_pairs", st);
     const int bm = moe::gemm_block_m((int)P, E);
     const int mt = moe::gemm_max_mtiles((int)P, E, bm);
@@ -471,6 +473,7 @@ moe_status moe_route_ex(const void* x, moe_dtype dt, int32_t T, int32_t H, const
     if (s != MOE_OK) return s;
     RouteOpt ro;
     if ((s = check_opts(opts, E, k, &ro)) != MOE_OK) return s;
+    if (ro.cap) return MOE_ERR_OPTION;  // capacity is a dispatch option: moe_layer_forward_ex only
     if (T == 0) return MOE_OK;
     if (!topk_idx || !topk_w) return MOE_ERR_NULL;
     float* logits = logits_out;
@@ -514,7 +517,7 @@ moe_status moe_topk_from_logits_ex(const float* logits, int32_t T, int32_t E, in
     RouteOpt ro;
     moe_status so = check_opts(opts, E, k, &ro);
     if (so != MOE_OK) return so;
-    if (ro.health) return MOE_ERR_OPTION;
+    if (ro.health || ro.cap) return MOE_ERR_OPTION;
     if (T == 0) return MOE_OK;
     DevProps props;
     moe_status s = device_props(&props);

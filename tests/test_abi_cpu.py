@@ -197,7 +197,7 @@ def test_route_options_validation():
     and health refused where the logits are taken as final."""
     L = moe.lib()
     ws = 1 << 20
-    O = lambda health=None, alpha=0.0, groups=0: ctypes.byref(moe.CRouteOpts(health, alpha, groups))
+    O = lambda health=None, alpha=0.0, groups=0, capacity=0: ctypes.byref(moe.CRouteOpts(health, alpha, groups, capacity))
     call = lambda opts, E=8, k=2: L.moe_route_ex(P, 1, 4, 256, P, E, k, opts, P, P, None, None, None, P, ws, None)
     st = lambda v: moe.STATUS[v]
     assert st(call(O(groups=-1))) == "MOE_ERR_OPTION"
@@ -220,6 +220,11 @@ def test_route_options_validation():
     lay = lambda opts: L.moe_layer_forward_ex(P, 1, 4, 256, P, 8, 2, opts, ref(gu), None, None, ref(dn), P, 0, None,
                                               P, L.moe_layer_workspace_size(4, 256, 8, 2, 128, 0), None)
     assert st(lay(O(groups=5))) == "MOE_ERR_OPTION"
+    assert st(lay(O(capacity=-1))) == "MOE_ERR_OPTION"
+    assert st(call(O(capacity=4))) == "MOE_ERR_OPTION"  # a dispatch option: layer only
+    assert st(tk(O(capacity=4))) == "MOE_ERR_OPTION"
+    if not torch.cuda.is_available():
+        assert st(lay(O(capacity=3))) == "MOE_ERR_DEVICE"
     assert st(lay(O(health=P + 1))) == "MOE_ERR_ALIGN"
 
 

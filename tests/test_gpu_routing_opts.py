@@ -148,3 +148,57 @@ def test_load_stats_matches_oracle(E):
         olu, osd = oracle.load_stats(c)
         assert int(lu.item()) == olu, (E, c[:8])
         assert abs(float(sd.item()) - osd) <= np.spacing(np.float32(osd)), (E, float(sd.item()), osd)
+
+
+# ----------------------------------------------------------- capacity --
+
+CAP_CASES = {
+    "decode_t3": ("decode_b1", dict(T=3, H=512, E=16, I=320), [1, 2]),
+    "decode_t4_e4": ("decode_b1", dict(T=4, H=512, E=4, k=2, I=320), [1, 3]),
+    "batched_small": ("batched_decode", dict(T=40, H=512, E=8, I=320), [3, 8]),
+    "prefill_small": ("prefill", dict(T=300, H=512, E=16, I=192), [20, 64]),
+    "entropy_q4": ("entropy", dict(T=96, H=512, E=16, I=192, bits=4, segment=2), [5]),
+}
+
+
+@pytest.mark.parametrize("name", list(CAP_CASES))
+def test_layer_with_capacity_matches_oracle(name):
+    recipe, kw, caps = CAP_CASES[name]
+    inp = mi.make_inputs(recipe, **kw)
+    dev = Dev(inp)
+    gu_np = oracle.fuse_gate_up(inp.gate, inp.up)
+    P = inp.T * inp.kcap
+    paths = [("mfma", moe.FLAG_FORCE_MFMA)] + ([("gemv", moe.FLAG_FORCE_GEMV)] if P <= 128 else [])
+    for pname, pflag in paths:
+        base_t = moe.make_taps(inp.T, inp.E, inp.k, inp.I, "cuda")
+        y0 = host_bits(moe.layer_forward(dev.x, dev.wr, inp.k, dev.down, gate_up=dev.gate_up, flags=pflag,
+                                         taps=base_t))
+        torch.cuda.synchronize()
+        idx = base_t["topk_idx"].cpu().numpy()
+        w = base_t["topk_w"].cpu().numpy()
+        ku = int(base_t["k_used"].item())
+        routed = np.bincount(idx[:, :ku].ravel(), minlength=inp.E)
+        for C in caps + [int(routed.max())]:
+            print("case", name, pname, "capacity", C, "max routed", int(routed.max()), flush=True)
+            outs = []
+            for extra in (0, moe.FLAG_UNFUSED):
+                taps = moe.make_taps(inp.T, inp.E, inp.k, inp.I, "cuda")
+                y = moe.layer_forward(dev.x, dev.wr, inp.k, dev.down, gate_up=dev.gate_up, flags=pflag | extra,
+                                      taps=taps, capacity=C)
+                torch.cuda.synchronize()
+                outs.append((host_bits(y), {n: v.cpu().numpy() for n, v in taps.items()}))
+            (y, t), (y_u, _) = outs
+            assert np.array_equal(y, y_u), "fused vs unfused"
+            assert np.array_equal(t["topk_idx"], idx)  # routing unchanged
+            # the dispatch lists exactly the oracle's kept pairs
+            c, o, p_, _ = oracle.sort_pairs(idx, ku, inp.E, capacity=C)
+            assert np.array_equal(t["counts"], c) and np.array_equal(t["offsets"], o)
+            assert np.array_equal(t["perm"], p_)
+            keep = oracle.capacity_keep(idx, ku, inp.E, C)
+            if C >= routed.max():
+                assert keep[:, :ku].all()
+                assert np.array_equal(y, y0), "a capacity above every count changes nothing"
+            idx_kept = np.where(keep, idx, -1).astype(np.int32)
+            ref = oracle.tokens_forward(inp.x, inp.dtype, np.arange(inp.T), idx_kept, w, ku, gu_np, inp.down)
+            assert_within_tolerance(y, ref, inp.dtype, "%s/%s C=%d (dropped %d)" % (name, pname, C,
+                                                                                   int((~keep[:, :ku]).sum())))
