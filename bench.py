@@ -340,7 +340,8 @@ def main():
     roof["mean_launch_us"] = round(float(per_kernel_us[j]), 3)
     roof["algorithmic_bytes"] = int(alg_b)
     roof["algorithmic_flops"] = int(alg_f)
-    roof["traffic"] = traffic_from_profiles(kern, args.workload)
+    # counters are taken without routing options: with options the traffic is unmeasured
+    roof["traffic"] = None if lopt else traffic_from_profiles(kern, args.workload)
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
