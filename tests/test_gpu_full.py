@@ -129,3 +129,70 @@ def test_entropy_full_size(bits):
         y_u, _, _ = _forward(dev, moe.FLAG_UNFUSED)
         assert np.array_equal(y, y_u)
         _assert_packed_same(dev, y)
+
+
+# ------------------------------------------ routing options, full size --
+
+def _opt_check(inp, gu_np, dev, tokens, label, flags=0, **opt):
+    """Layer with routing options vs the oracle on sampled tokens: corrected
+    logits, selection on identical logits, capped sort, outputs under the kept
+    pairs, fused == unfused."""
+    health = opt.pop("health", None)
+    extra = dict(opt)
+    if health is not None:
+        extra["health"] = torch.from_numpy(health).cuda()
+    outs, plans = [], []
+    for f in (flags, flags | moe.FLAG_UNFUSED):
+        taps = moe.make_taps(inp.T, inp.E, inp.k, inp.I, "cuda",
+                             names=("logits", "topk_idx", "topk_w", "k_used", "counts", "offsets", "perm"))
+        y = host_bits(moe.layer_forward(dev.x, dev.wr, inp.k, dev.down, gate_up=dev.gate_up, flags=f, taps=taps,
+                                        **extra))
+        plans.append(moe.last_plan())
+        outs.append((y, {k: v.cpu().numpy() for k, v in taps.items()}))
+    (y, t), (y_u, _) = outs
+    assert np.array_equal(y, y_u), label + " fused vs unfused"
+    ku = int(t["k_used"][0])
+    groups, cap = opt.get("groups", 0), opt.get("capacity", 0)
+    if health is not None:
+        raw = moe.route(dev.x, dev.wr, inp.k, want_logits=True)["logits"].cpu().numpy()
+        assert np.array_equal(t["logits"], oracle.correct_logits(raw, health, opt["alpha"]))
+    oi, ow = oracle.select_topk(t["logits"], ku, inp.kcap, groups=groups)
+    assert np.array_equal(t["topk_idx"], oi), label + " selection"
+    assert np.max(np.abs(t["topk_w"] - ow)) <= 1e-6
+    c, o, p, _ = oracle.sort_pairs(t["topk_idx"], ku, inp.E, capacity=cap)
+    assert np.array_equal(t["counts"], c) and np.array_equal(t["offsets"], o) and np.array_equal(t["perm"], p)
+    keep = oracle.capacity_keep(t["topk_idx"], ku, inp.E, cap)
+    idx_kept = np.where(keep, t["topk_idx"], -1).astype(np.int32)
+    ref = oracle.tokens_forward(inp.x, inp.dtype, tokens, idx_kept, t["topk_w"], ku, gu_np, inp.down)
+    assert_within_tolerance(y[tokens], ref, inp.dtype, "%s (tokens %d, dropped pairs %d)" % (
+        label, len(tokens), int((~keep[:, :ku]).sum())))
+    return t, keep, plans[0]
+
+
+def test_decode_b1_full_size_with_options():
+    inp, gu_np, dev = _gen("decode_b1", T=4)
+    hv = mi.load_index(5, inp.E)
+    # the decode path (four tokens, 16 pairs) with correction and groups, and
+    # a capacity that drops pairs two tokens share
+    _, _, plan = _opt_check(inp, gu_np, dev, np.arange(inp.T), "decode_b1 opts", flags=moe.FLAG_FORCE_GEMV,
+                            health=hv, alpha=0.5, groups=4, capacity=1)
+    assert "gemv_gate_up_swiglu" in plan, plan
+
+
+def test_prefill_full_size_with_options():
+    inp, gu_np, dev = _gen("prefill")
+    hv = mi.load_index(5, inp.E)
+    rng = np.random.default_rng(3)
+    tokens = np.unique(np.concatenate([np.arange(3), rng.choice(inp.T, 12, replace=False), [inp.T - 1]]))
+    _opt_check(inp, gu_np, dev, tokens, "prefill correction+groups", health=hv, alpha=0.5, groups=4)
+    # capacity 512 (twice the mean) caps the hot experts; sample dropped tokens too
+    cap = 512
+    base = moe.make_taps(inp.T, inp.E, inp.k, inp.I, "cuda", names=("topk_idx", "k_used"))
+    dev.forward(taps=base)
+    bidx = base["topk_idx"].cpu().numpy()
+    bkeep = oracle.capacity_keep(bidx, inp.k, inp.E, cap)
+    dropped = np.where(~bkeep.all(axis=1))[0]
+    _say("capacity %d drops %d pairs of %d tokens" % (cap, int((~bkeep).sum()), dropped.size))
+    assert dropped.size > 0
+    tokens = np.unique(np.concatenate([tokens, dropped[:6], dropped[-4:]]))
+    _opt_check(inp, gu_np, dev, tokens, "prefill capacity", capacity=cap)
