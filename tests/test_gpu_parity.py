@@ -33,6 +33,11 @@ CASES = {
     "dense_k_eq_e": ("tiny", dict(k=8, T=6)),
     "k8_e256": ("tiny", dict(E=256, k=8, T=12, H=128, I=64)),
     "ragged_shapes": ("tiny", dict(T=37, H=192, E=12, k=3, I=320)),
+    # decode shapes with long down rows (two waves per slot), one per
+    # weight format
+    "decode_1l_q4": ("decode_b1", dict(T=2, H=1024, E=8, I=8192)),
+    "decode_1l_q8": ("decode_b1", dict(T=1, H=2048, E=8, I=6144, bits=8)),
+    "decode_1l_fp16": ("decode_b1", dict(T=1, H=1024, E=8, I=3072, bits=16)),
 }
 
 
@@ -280,3 +285,4 @@ def test_zero_tokens_and_errors_on_gpu():
     with pytest.raises(moe.MoeError) as e:
         moe.layer_forward(dev.x, dev.wr, 9, dev.down, gate_up=dev.gate_up)
     assert e.value.name == "MOE_ERR_K"
+
