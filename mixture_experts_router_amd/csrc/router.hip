@@ -32,6 +32,7 @@ __device__ __forceinline__ void unpack8(u32x4 r, int act, float* v) {
 // of H, each lane sums its 8-element slices in order, the wave sums its lanes,
 // and the four wave partials are added in wave order.  Spreads a decode
 // step's router over E workgroups (E x 8 KB of router rows at H = 4096).
+template <int ACT>
 __global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t* __restrict__ x,
                                                                   const uint16_t* __restrict__ wr,
                                                                   float* __restrict__ logits, int H, int E,
@@ -43,14 +44,41 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t
   const int q = H / 4;
   const uint16_t* xr = x + (size_t)t * H + wave * q;
   const uint16_t* wrow = wr + (size_t)e * H + wave * q;
+  // up to four slices per lane per round, all loaded before the sums (which
+  // run slice by slice in order, as one slice at a time would)
   float acc = 0.0f;
-#pragma unroll 4
-  for (int h = lane * 8; h < q; h += 512) {
+  auto slice = [&](u32x4 xr8, u32x4 wr8) __attribute__((always_inline)) {
     float xv[8], wv[8];
-    unpack8(load16(xr + h), act, xv);
-    unpack8(load16(wrow + h), act, wv);
+    unpack8(xr8, ACT, xv);
+    unpack8(wr8, ACT, wv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = fmaf(xv[i], wv[i], acc);
+  };
+  int h = lane * 8;
+  for (; h + 3 * 512 < q; h += 4 * 512) {
+    u32x4 xa[4], wa[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      xa[u] = load16(xr + h + 512 * u);
+      wa[u] = load16(wrow + h + 512 * u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) slice(xa[u], wa[u]);
+  }
+  if (h < q) {
+    // the remaining one to three slices of this lane, loaded together
+    u32x4 xa[3], wa[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      if (h + 512 * u < q) {
+        xa[u] = load16(xr + h + 512 * u);
+        wa[u] = load16(wrow + h + 512 * u);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      if (h + 512 * u < q) slice(xa[u], wa[u]);
   }
   const float s = wave_sum(acc);
   if (lane == 0) part[wave] = s;
@@ -64,40 +92,58 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t
 
 // ---------------------------------------------------------- large batches --
 //
-// One workgroup per 32-token x 32-expert tile on the matrix cores: the four
-// waves take consecutive quarters of H (split K), each accumulating a 32x32
+// One workgroup per 32-token x 32-expert tile on the matrix cores: the NW
+// waves take consecutive parts of H (split K), each accumulating a 32x32
 // fp32 tile with v_mfma_f32_32x32x16_{f16,bf16} fed straight from memory
 // (lane l supplies row l%32 and 8 consecutive k), and the partial tiles are
 // added in wave order through LDS.  Products of two fp16 (bf16) values are
 // exact in fp32; only the summation order differs from a sequential sum.
+// Sixteen waves (H % 256 == 0) keep a wave's share of H to a few k-steps
+// whose loads all go out at once: the tile count is small (16 tiles for 512
+// tokens and 32 experts), so the kernel is bound by load latency.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-template <int ACT>
-__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t* __restrict__ x,
-                                                                 const uint16_t* __restrict__ wr,
-                                                                 float* __restrict__ logits, int T, int H, int E,
-                                                                 const float* __restrict__ health, float alpha) {
-  __shared__ float part[3][16][WAVE];
+template <int ACT, int NW>
+__global__ __launch_bounds__(64 * NW) void router_logits_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                     const uint16_t* __restrict__ wr,
+                                                                     float* __restrict__ logits, int T, int H, int E,
+                                                                     const float* __restrict__ health, float alpha) {
+  __shared__ float part[NW - 1][16][WAVE];
   const int lane = lane_id(), wave = wave_id();
   const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
   const int r32 = lane % 32, half = lane / 32;
   const int t = min(t0 + r32, T - 1), e = min(e0 + r32, E - 1);  // past the end: re-read (not stored)
-  const int q = H / 4;
+  const int q = H / NW;
   const uint16_t* xa = x + (size_t)t * H + wave * q + half * 8;
   const uint16_t* wb = wr + (size_t)e * H + wave * q + half * 8;
   f32x16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-#pragma unroll 8
-  for (int k = 0; k < q; k += 16) {
-    const u32x4 a = load16(xa + k), b = load16(wb + k);
+  // eight k-steps per round: all sixteen loads go out before the MFMAs
+  // (the same accumulation order as one step at a time)
+  auto mfma = [&](u32x4 av, u32x4 bv) __attribute__((always_inline)) {
     if constexpr (ACT == ACT_BF16)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
-                                                    0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv),
+                                                    acc, 0, 0, 0);
     else
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc, 0,
-                                                   0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, bv), acc,
+                                                   0, 0, 0);
+  };
+  constexpr int KU = 8;
+  int k = 0;
+  for (; k + 16 * KU <= q; k += 16 * KU) {
+    u32x4 av[KU], bv[KU];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      av[u] = load16(xa + k + 16 * u);
+      bv[u] = load16(wb + k + 16 * u);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+#pragma unroll
+    for (int u = 0; u < KU; ++u) mfma(av[u], bv[u]);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  for (; k < q; k += 16) mfma(load16(xa + k), load16(wb + k));
   if (wave > 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) part[wave - 1][i][lane] = acc[i];
@@ -107,7 +153,9 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
     // register i of lane l: token row 8*(i/4) + 4*(l/32) + i%4, expert column l%32
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float v = ((acc[i] + part[0][i][lane]) + part[1][i][lane]) + part[2][i][lane];
+      float v = acc[i];
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) v = v + part[w][i][lane];
       const int tt = t0 + 8 * (i / 4) + 4 * half + (i % 4), ee = e0 + r32;
       if (health) v = v - alpha * health[e];  // e = min(ee, E - 1): equal to ee where stored
       if (tt < T && ee < E) logits[(size_t)tt * E + ee] = v;
@@ -264,14 +312,27 @@ hipError_t launch_router_logits(const void* x, const void* wr, float* logits, in
                                 const float* health, float alpha, hipStream_t st) {
   if (T > router_small_max_tokens()) {
     dim3 grid((T + 31) / 32, (E + 31) / 32);
+    const uint16_t* xs = (const uint16_t*)x;
+    const uint16_t* ws = (const uint16_t*)wr;
+    if (H % (16 * 16) == 0) {
+      if (act == ACT_BF16)
+        return launch_kernel(router_logits_mfma_kernel<ACT_BF16, 16>, grid, 1024, 0, st, xs, ws, logits, T, H, E, health,
+                             alpha);
+      return launch_kernel(router_logits_mfma_kernel<ACT_F16, 16>, grid, 1024, 0, st, xs, ws, logits, T, H, E, health,
+                           alpha);
+    }
     if (act == ACT_BF16)
-      return launch_kernel(router_logits_mfma_kernel<ACT_BF16>, grid, 256, 0, st, (const uint16_t*)x,
-                           (const uint16_t*)wr, logits, T, H, E, health, alpha);
-    return launch_kernel(router_logits_mfma_kernel<ACT_F16>, grid, 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr,
-                         logits, T, H, E, health, alpha);
+      return launch_kernel(router_logits_mfma_kernel<ACT_BF16, 4>, grid, 256, 0, st, xs, ws, logits, T, H, E, health,
+                           alpha);
+    return launch_kernel(router_logits_mfma_kernel<ACT_F16, 4>, grid, 256, 0, st, xs, ws, logits, T, H, E, health,
+                         alpha);
   }
-  launch_kernel(router_logits_small_kernel, dim3(E, T), 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr, logits, H,
-                E, act, health, alpha);
+  if (act == ACT_BF16)
+    launch_kernel(router_logits_small_kernel<ACT_BF16>, dim3(E, T), 256, 0, st, (const uint16_t*)x,
+                  (const uint16_t*)wr, logits, H, E, act, health, alpha);
+  else
+    launch_kernel(router_logits_small_kernel<ACT_F16>, dim3(E, T), 256, 0, st, (const uint16_t*)x,
+                  (const uint16_t*)wr, logits, H, E, act, health, alpha);
   return hipGetLastError();
 }
 
