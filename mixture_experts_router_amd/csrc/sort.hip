@@ -22,6 +22,7 @@
 
 namespace moe {
 
+template <int CH>
 __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restrict__ idx, int T, int kcap,
                                                           const int32_t* __restrict__ k_used_dev, int k_static, int E,
                                                           int32_t* __restrict__ counts,
@@ -38,13 +39,30 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
   const int64_t beg = wave * seg;
   const int64_t end = beg + seg < P ? beg + seg : P;
 
+  // The segment is read in groups of CH rounds of 64 pairs whose loads all
+  // go out together (addresses clamped, so every load is issued); pairs past
+  // the segment or in unused slots read as "no expert".  CH follows the
+  // segment length (the launcher picks it).
+  // pair ids fit in 32 bits (perm and pos are int32)
+  const uint32_t ukcap = (uint32_t)kcap, uend = (uint32_t)end, uP = (uint32_t)P;
+  auto load_group = [&](int64_t c0, int* v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const uint32_t p = (uint32_t)c0 + 64u * u + (uint32_t)lane;
+      const bool valid = p < uend && (int)(p % ukcap) < ku;
+      const int raw = idx[p < uP ? p : 0u];
+      v[u] = valid ? raw : 0x7FFFFFFF;
+    }
+  };
   int lt = 0, eq = 0;
-  for (int64_t c = beg; c < end; c += 64) {
-    int64_t p = c + lane;
-    bool valid = p < end && (int)(p % kcap) < ku;
-    int v = valid ? idx[p] : 0x7FFFFFFF;
-    lt += __popcll(__ballot(v < e));
-    eq += __popcll(__ballot(v == e));
+  for (int64_t c0 = beg; c0 < end; c0 += 64 * CH) {
+    int v[CH];
+    load_group(c0, v);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      lt += __popcll(__ballot(v[u] < e));
+      eq += __popcll(__ballot(v[u] == e));
+    }
   }
   if (lane == 0) {
     s_lt[wave] = lt;
@@ -69,22 +87,25 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
     cnt = min(cnt, cap);
   }
   int r = before;  // rank within expert e of the segment's first pair of e
-  for (int64_t c = beg; c < end; c += 64) {
-    int64_t p = c + lane;
-    bool valid = p < end && (int)(p % kcap) < ku;
-    int v = valid ? idx[p] : 0x7FFFFFFF;
-    uint64_t m = __ballot(v == e);
-    if (v == e) {
-      const int rank = r + (int)__popcll(m & lanemask_lt());
-      if (cap <= 0 || rank < cap) {
-        const int at = off + rank;
-        perm[at] = (int32_t)p;
-        pos[p] = at;
-      } else {
-        pos[p] = -1;
+  for (int64_t c0 = beg; c0 < end; c0 += 64 * CH) {
+    int v[CH];
+    load_group(c0, v);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int64_t p = c0 + 64 * u + lane;
+      const uint64_t m = __ballot(v[u] == e);
+      if (v[u] == e) {
+        const int rank = r + (int)__popcll(m & lanemask_lt());
+        if (cap <= 0 || rank < cap) {
+          const int at = off + rank;
+          perm[at] = (int32_t)p;
+          pos[p] = at;
+        } else {
+          pos[p] = -1;
+        }
       }
+      r += (int)__popcll(m);
     }
-    r += (int)__popcll(m);
   }
   if (threadIdx.x == 0) {
     counts[e] = cnt;
@@ -104,8 +125,17 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
 hipError_t launch_sort_pairs(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st,
                              int capacity) {
-  (void)launch_kernel(sort_pairs_kernel, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets, perm, pos,
-                capacity);
+  const int64_t P = (int64_t)T * kcap;
+  const int64_t rounds = (P + 16 * 64 - 1) / (16 * 64);  // rounds of 64 pairs per wave
+  if (rounds >= 16)
+    (void)launch_kernel(sort_pairs_kernel<16>, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
+                        perm, pos, capacity);
+  else if (rounds >= 4)
+    (void)launch_kernel(sort_pairs_kernel<4>, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
+                        perm, pos, capacity);
+  else
+    (void)launch_kernel(sort_pairs_kernel<2>, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
+                        perm, pos, capacity);
   return hipGetLastError();
 }
 
