@@ -102,7 +102,8 @@ def test_fused_and_unfused_are_bit_identical(name, built):
         assert np.array_equal(hf, t_s["h"].view(np.uint16)[valid])
 
 
-@pytest.mark.parametrize("name", ["tiny", "prefill_small", "batched_small", "entropy_q4", "ragged_shapes"])
+@pytest.mark.parametrize("name", ["tiny", "prefill_small", "batched_small", "entropy_q4", "ragged_shapes",
+                                  "prefill_bm128"])
 def test_sort_matches_oracle_exactly(name, built):
     inp, _, dev = built(name)
     _, taps = _run(dev, moe.FLAG_FORCE_MFMA)
