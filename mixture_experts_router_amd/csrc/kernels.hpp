@@ -103,8 +103,9 @@ int gemv_down_max_chunks_per_lane();
 // order) is left out of y (needs route.logits NULL: the selection is read)
 hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_static, int kcap, int T, int H, int I,
                             int bits, WView wd, void* y, int act, int num_cu, hipStream_t st, int capacity = 0);
-// tokens up to which the router uses one workgroup per (expert, token)
-int router_small_max_tokens();
+// whether the router uses one workgroup per (expert, token) logit rather
+// than the 32 x 32 tiled matrix-core kernel
+bool router_use_small(int T, int E);
 
 // -------------------------------------------------- batched (MFMA GEMM)
 enum GemmMode { GEMM_FUSED_SWIGLU = 0, GEMM_GATHER_F32 = 1, GEMM_ROWS_F16 = 2 };

@@ -33,8 +33,8 @@ CASES = {
     "dense_k_eq_e": ("tiny", dict(k=8, T=6)),
     "k8_e256": ("tiny", dict(E=256, k=8, T=12, H=128, I=64)),
     "ragged_shapes": ("tiny", dict(T=37, H=192, E=12, k=3, I=320)),
-    # more than 128 tokens with H not a multiple of 256: the four-wave MFMA router
-    "ragged_mfma_router": ("tiny", dict(T=200, H=192, E=12, k=3, I=128)),
+    # more than 16384 logits with H not a multiple of 256: the four-wave MFMA router
+    "ragged_mfma_router": ("tiny", dict(T=200, H=192, E=96, k=3, I=128)),
     # decode shapes with long down rows (two waves per slot), one per
     # weight format
     "decode_1l_q4": ("decode_b1", dict(T=2, H=1024, E=8, I=8192)),
@@ -220,10 +220,10 @@ def test_fuse_gate_up_matches_oracle_concatenation(built):
 @pytest.mark.parametrize("T,E,k", [(1, 64, 4), (7, 8, 2), (300, 64, 4), (64, 256, 8), (33, 32, -1),
                                    (300, 32, -1), (200, 8, 2), (129, 256, 8)])
 def test_router_exact_inputs_with_planted_ties(dtype, T, E, k):
-    # H = 1024 takes the sixteen-wave MFMA router above 128 tokens; H = 320
-    # (not a multiple of 256) the four-wave one; H = 8192 runs the small-batch
-    # router's four-slice rounds (partial sums stay exact: multiples of 2^-14
-    # below 2^9)
+    # H = 1024 takes the sixteen-wave MFMA router above 128 tokens and 16384
+    # logits; H = 320 (not a multiple of 256) the four-wave one; H = 8192 runs
+    # the small-batch router's four-slice rounds (partial sums stay exact:
+    # multiples of 2^-14 below 2^9)
     for H in (1024, 320) + ((8192,) if T <= 128 else ()):
         _router_exact_case(dtype, T, E, k, H)
 
