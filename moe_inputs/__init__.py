@@ -120,8 +120,9 @@ def decode_half(b: np.ndarray, dtype: str) -> np.ndarray:
 class Weights:
     """One expert weight tensor [E, N, K].
 
-    bits 4/8: ``q`` uint8 [E, N, K/2] (4-bit, low nibble = even column) or
-    [E, N, K] (8-bit); ``scales``/``biases`` fp16 bits [E, N, K/group].
+    bits 4/6/8: ``q`` uint8 [E, N, K/2] (4-bit, low nibble = even column),
+    [E, N, 3K/4] (6-bit, code k at bits 6k..6k+5 of the row's little-endian bit
+    stream) or [E, N, K] (8-bit); ``scales``/``biases`` fp16 bits [E, N, K/group].
     bits 16:  ``q`` fp16 bits [E, N, K]; scales/biases None.
     """
 
@@ -147,8 +148,8 @@ def quant_weights(seed: int, tid: int, E: int, N: int, K: int, bits: int, sigma:
     if bits == 16:
         q = normal_half(seed, tid, E * N * K, sigma, "f16").reshape(E, N, K)
         return Weights(q, None, None, E, N, K, 16, gs)
-    assert bits in (4, 8) and K % gs == 0
-    q = np.empty((E, N, K // 2 if bits == 4 else K), np.uint8)
+    assert bits in (4, 6, 8) and K % gs == 0
+    q = np.empty((E, N, K * bits // 8), np.uint8)
     s = np.empty((E, N, K // gs), np.uint16)
     b = np.empty((E, N, K // gs), np.uint16)
     _load().gen_quant_weights(seed, tid, E, N, K, bits, gs, sigma, _p(q), _p(s), _p(b))
@@ -159,7 +160,7 @@ def quantize_rows(w: np.ndarray, bits: int, gs: int = 64):
     """Quantise an explicit fp64 matrix [rows, K] with the same min-max rule."""
     w = np.ascontiguousarray(w, np.float64)
     rows, K = w.shape
-    q = np.empty((rows, K // 2 if bits == 4 else K), np.uint8)
+    q = np.empty((rows, K * bits // 8), np.uint8)
     s = np.empty((rows, K // gs), np.uint16)
     b = np.empty((rows, K // gs), np.uint16)
     _load().gen_quantize_rows(_p(w), rows, K, bits, gs, _p(q), _p(s), _p(b))

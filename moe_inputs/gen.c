@@ -197,22 +197,38 @@ static void quant_group(const double* w, int gs, int bits, uint8_t* codes, uint1
   *b_bits = bb;
 }
 
+/*
+ * Store one group's codes at column offset `col` of a row.  bits 4: two per
+ * byte, low nibble = even column; bits 6: a little-endian bit stream, code i
+ * of the row at bits 6i .. 6i+5 (byte 6i/8, shifted by 6i%8, spilling into the
+ * next byte); bits 8: one per byte.  dst must start zeroed for bits 6.
+ */
+static void store_codes(const uint8_t* codes, int gs, int bits, int64_t col, uint8_t* dst) {
+  if (bits == 4) {
+    for (int i = 0; i < gs; i += 2) dst[(col + i) / 2] = (uint8_t)(codes[i] | (codes[i + 1] << 4));
+  } else if (bits == 6) {
+    for (int i = 0; i < gs; ++i) {
+      int64_t bit = 6 * (col + i);
+      int sh = (int)(bit % 8);
+      dst[bit / 8] |= (uint8_t)(codes[i] << sh);
+      if (sh > 2) dst[bit / 8 + 1] |= (uint8_t)(codes[i] >> (8 - sh));
+    }
+  } else {
+    memcpy(dst + col, codes, (size_t)gs);
+  }
+}
+
 /* quantise an explicit fp64 matrix [rows, K] (test helper, same rule as below) */
 void gen_quantize_rows(const double* w, int64_t rows, int K, int bits, int gs, uint8_t* q, uint16_t* scales,
                        uint16_t* biases) {
-  int64_t row_bytes = bits == 4 ? K / 2 : K;
+  int64_t row_bytes = (int64_t)K * bits / 8;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
     uint8_t codes[256];
+    memset(q + r * row_bytes, 0, (size_t)row_bytes);
     for (int g = 0; g < K / gs; ++g) {
       quant_group(w + r * K + (int64_t)g * gs, gs, bits, codes, &scales[r * (K / gs) + g], &biases[r * (K / gs) + g]);
-      uint8_t* dst = q + r * row_bytes;
-      if (bits == 4) {
-        for (int i = 0; i < gs; i += 2)
-          dst[(g * gs + i) / 2] = (uint8_t)(codes[i] | (codes[i + 1] << 4));
-      } else {
-        memcpy(dst + (int64_t)g * gs, codes, (size_t)gs);
-      }
+      store_codes(codes, gs, bits, (int64_t)g * gs, q + r * row_bytes);
     }
   }
 }
@@ -221,6 +237,7 @@ void gen_quantize_rows(const double* w, int64_t rows, int K, int bits, int gs, u
  * Draw an expert weight tensor [E, N, K] of N(0, sigma) values (flat index
  * (e*N + n)*K + k of stream `tid`) and quantise it by groups of `gs` columns.
  *   q:      bits == 4: [E, N, K/2] bytes, low nibble = even column;
+ *           bits == 6: [E, N, 3K/4] bytes, a little-endian 6-bit stream per row;
  *           bits == 8: [E, N, K] bytes
  *   scales, biases: [E, N, K/gs] fp16 bits
  */
@@ -228,7 +245,7 @@ void gen_quant_weights(uint64_t seed, uint32_t tid, int E, int N, int K, int bit
                        uint16_t* scales, uint16_t* biases) {
   uint64_t key = stream_key(seed, tid);
   int64_t rows = (int64_t)E * N;
-  int64_t row_bytes = bits == 4 ? K / 2 : K;
+  int64_t row_bytes = (int64_t)K * bits / 8;
   int ng = K / gs;
 #pragma omp parallel for schedule(dynamic, 64)
   for (int64_t r = 0; r < rows; ++r) {
@@ -242,14 +259,9 @@ void gen_quant_weights(uint64_t seed, uint32_t tid, int E, int N, int K, int bit
         w[i] = sigma * c;
         w[i + 1] = sigma * sn;
       }
+      if (g == 0) memset(q + r * row_bytes, 0, (size_t)row_bytes);
       quant_group(w, gs, bits, codes, &scales[r * ng + g], &biases[r * ng + g]);
-      uint8_t* dst = q + r * row_bytes;
-      if (bits == 4) {
-        for (int i = 0; i < gs; i += 2)
-          dst[(g * gs + i) / 2] = (uint8_t)(codes[i] | (codes[i + 1] << 4));
-      } else {
-        memcpy(dst + (int64_t)g * gs, codes, (size_t)gs);
-      }
+      store_codes(codes, gs, bits, (int64_t)g * gs, q + r * row_bytes);
     }
   }
 }

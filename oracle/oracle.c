@@ -123,7 +123,8 @@ uint16_t oracle_float_to_half(float f, int dtype) {
 
 /*
  * One row of K weights.  bits 4: two codes per byte, even column in the low
- * nibble; bits 8: one code per byte; code q is unsigned.  w = s*q + b in fp32
+ * nibble; bits 6: code k at bits 6k .. 6k+5 of the row read as a
+ * little-endian bit stream; bits 8: one code per byte; code q is unsigned.  w = s*q + b in fp32
  * (two roundings), s and b fp16, one pair per 64-column group.
  * bits 16: the row is fp16 values, copied.
  */
@@ -136,7 +137,18 @@ void oracle_dequant_row(const void* q_row, const uint16_t* s_row, const uint16_t
   }
   const uint8_t* q = (const uint8_t*)q_row;
   for (int k = 0; k < K; ++k) {
-    int code = bits == 4 ? (q[k / 2] >> (4 * (k & 1))) & 15 : q[k];
+    int code;
+    if (bits == 4) {
+      code = (q[k / 2] >> (4 * (k & 1))) & 15;
+    } else if (bits == 6) {
+      int64_t bit = 6 * (int64_t)k;
+      int sh = (int)(bit % 8);
+      int v = q[bit / 8] >> sh;
+      if (sh > 2) v |= q[bit / 8 + 1] << (8 - sh);
+      code = v & 63;
+    } else {
+      code = q[k];
+    }
     float s = oracle_half_to_float(s_row[k / gs], ORACLE_F16);
     float b = oracle_half_to_float(b_row[k / gs], ORACLE_F16);
     float sq = s * (float)code;
@@ -144,7 +156,7 @@ void oracle_dequant_row(const void* q_row, const uint16_t* s_row, const uint16_t
   }
 }
 
-static int64_t row_bytes_of(int K, int bits) { return bits == 4 ? K / 2 : (bits == 8 ? K : 2 * (int64_t)K); }
+static int64_t row_bytes_of(int K, int bits) { return (int64_t)K * bits / 8; }
 
 /* ---------------------------------------------------------- router (A1) -- */
 
