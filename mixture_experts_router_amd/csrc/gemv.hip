@@ -54,17 +54,32 @@ __device__ __forceinline__ void for_slot(int s, F f) {
     if (j == s) f(j);
 }
 
+// A lane's unit of a weight row: 16 bytes (32 4-bit, 16 8-bit or 8 fp16
+// weights), or 12 bytes of 6-bit codes (16 weights: three whole words)
 template <int BITS>
 struct Chunk {
-  static constexpr int VALS = BITS == 4 ? 32 : (BITS == 8 ? 16 : 8);  // weights per 16 bytes
-  static constexpr int PAIRS = VALS / 2;                               // fp16 pairs of activations
-  static constexpr int PER_GROUP = 64 / VALS;                          // chunks per 64-column group
-  static constexpr int PIECES = VALS / 8;                              // 16-byte activation pieces
+  static constexpr int VALS = BITS == 4 ? 32 : (BITS == 6 || BITS == 8 ? 16 : 8);  // weights per chunk
+  static constexpr int BYTES = BITS == 6 ? 12 : 16;                                 // bytes per chunk
+  static constexpr int PAIRS = VALS / 2;       // fp16 pairs of activations
+  static constexpr int PER_GROUP = 64 / VALS;  // chunks per 64-column group
+  static constexpr int PIECES = VALS / 8;      // 16-byte activation pieces
 };
 
 int gemv_lanes_chunks(int K, int bits) {
-  int vals = bits == 4 ? 32 : (bits == 8 ? 16 : 8);
+  int vals = bits == 4 ? 32 : (bits == 6 || bits == 8 ? 16 : 8);
   return (K / vals + 63) / 64;
+}
+
+// one chunk of codes (a 6-bit chunk is 12 bytes: the fourth word is zero)
+template <int BITS>
+__device__ __forceinline__ u32x4 load_chunk_nt(rsrc_t r, uint32_t off) {
+  if constexpr (BITS == 6) {
+    typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)off, 0, AUX_NT);
+    return u32x4{v.x, v.y, v.z, 0u};
+  } else {
+    return buf_load16_nt(r, off);
+  }
 }
 
 // Per-chunk activation terms: k, the amount the biased codes add to the
@@ -89,10 +104,10 @@ __device__ __forceinline__ XSums chunk_xsums(const uint32_t* xp) {
     }
     r.k = 1024.0f * a + 64.0f * b;
     r.x = a + b;
-  } else if constexpr (BITS == 8) {
+  } else if constexpr (BITS == 6 || BITS == 8) {
     float a = 0.0f;
 #pragma unroll
-    for (int j = 0; j < Chunk<8>::PAIRS; ++j) {
+    for (int j = 0; j < Chunk<BITS>::PAIRS; ++j) {
       const f16x2 hp = __builtin_bit_cast(f16x2, xp[j]);
       a += (float)hp.x + (float)hp.y;
     }
@@ -135,6 +150,25 @@ __device__ __forceinline__ float chunk_acc(u32x4 w, const uint32_t* xp, const XS
       q8_word_to_biased_pairs(wv[j], p);
       A = dot2(p[0], xp[2 * j], A);
       A = dot2(p[1], xp[2 * j + 1], A);
+    }
+    const float dq = A - xs.k;
+    return __builtin_fmaf(half_bits_f(s_bits), dq, __builtin_fmaf(half_bits_f(b_bits), xs.x, acc));
+  } else if constexpr (BITS == 6) {
+    // 16 codes in the 96-bit little-endian value w.x | w.y << 32 | w.z << 64:
+    // code i at bits 6i .. 6i+5.  Each pair of codes becomes the fp16 pair
+    // (1024 + q_2j, 1024 + q_2j+1) (exponent bits 0x6400), as for 8 bits.
+    const uint64_t lo = (uint64_t)wv[0] | ((uint64_t)wv[1] << 32);
+    auto code = [&](int i) __attribute__((always_inline)) -> uint32_t {
+      const int bit = 6 * i;
+      if (bit + 6 <= 64) return (uint32_t)(lo >> bit) & 63u;
+      if (bit >= 64) return (wv[2] >> (bit - 64)) & 63u;
+      return ((uint32_t)(lo >> bit) | (wv[2] << (64 - bit))) & 63u;
+    };
+    float A = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t p = 0x64006400u | code(2 * j) | (code(2 * j + 1) << 16);
+      A = dot2(p, xp[j], A);
     }
     const float dq = A - xs.k;
     return __builtin_fmaf(half_bits_f(s_bits), dq, __builtin_fmaf(half_bits_f(b_bits), xs.x, acc));
@@ -199,7 +233,7 @@ __device__ __forceinline__ void load_rows(RowBuf<BITS, CPL>& buf, const GemvUpPa
     const int64_t row = (int64_t)e * wv.stride + row_of<CPL, FUSED>(it, r);
     const rsrc_t rq = make_rsrc(wv.q + row * row_bytes, nq);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) buf.q[r][i] = buf_load16_nt(rq, qoff[i]);
+    for (int i = 0; i < CPL; ++i) buf.q[r][i] = load_chunk_nt<BITS>(rq, qoff[i]);
     if constexpr (BITS != 16) {
       const rsrc_t rs = make_rsrc(wv.s + row * ng, ns);
       const rsrc_t rb = make_rsrc(wv.b + row * ng, ns);
@@ -285,7 +319,7 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
     const int c = lane + 64 * i;
     valid[i] = c < nch;
     cc[i] = valid[i] ? c : nch - 1;
-    qoff[i] = (uint32_t)cc[i] * 16u;
+    qoff[i] = (uint32_t)cc[i] * (uint32_t)C::BYTES;
     goff[i] = (uint32_t)(cc[i] / C::PER_GROUP) * 2u;
   }
 
@@ -390,6 +424,7 @@ hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_
   dim3 grid((unsigned)((per_pair + 3) / 4), T * kcap);
   if (bits == 4) return fused ? launch_up_cpl<4, true>(cpl, prm, grid, st) : launch_up_cpl<4, false>(cpl, prm, grid, st);
   if (bits == 8) return fused ? launch_up_cpl<8, true>(cpl, prm, grid, st) : launch_up_cpl<8, false>(cpl, prm, grid, st);
+  if (bits == 6) return fused ? launch_up_cpl<6, true>(cpl, prm, grid, st) : launch_up_cpl<6, false>(cpl, prm, grid, st);
   return fused ? launch_up_cpl<16, true>(cpl, prm, grid, st) : launch_up_cpl<16, false>(cpl, prm, grid, st);
 }
 
@@ -436,7 +471,7 @@ __device__ __forceinline__ void load_down_row(DownBuf<BITS, DCPL>& buf, const Ge
   const int64_t row = (int64_t)e * prm.wd.stride + m;
   const rsrc_t rq = make_rsrc(prm.wd.q + row * row_bytes, live ? (uint32_t)row_bytes : 0u);
 #pragma unroll
-  for (int i = 0; i < DCPL; ++i) buf.q[i] = buf_load16_nt(rq, qoff[i]);
+  for (int i = 0; i < DCPL; ++i) buf.q[i] = load_chunk_nt<BITS>(rq, qoff[i]);
   if constexpr (BITS != 16) {
     const uint32_t ns = live ? (uint32_t)ng * 2u : 0u;
     const rsrc_t rs = make_rsrc(prm.wd.s + row * ng, ns);
@@ -513,7 +548,7 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
       const int c = lane + 64 * (ks * DC + i);
       valid[i] = c < nch;
       cc[i] = valid[i] ? c : nch - 1;
-      qoff[i] = (uint32_t)cc[i] * 16u;
+      qoff[i] = (uint32_t)cc[i] * (uint32_t)C::BYTES;
       goff[i] = (uint32_t)(cc[i] / C::PER_GROUP) * 2u;
     }
     // rows m(j) = blockIdx.x + j*G, j < nr; loads past the end go through
@@ -645,7 +680,7 @@ hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_sta
 #define X(B, D, K) \
   if (bits == B && dc == D && ks == K) launch_kernel(gemv_down_kernel<B, D, K>, grid, block, 0, st, prm); else
 #define CASES(B) X(B, 1, 1) X(B, 2, 1) X(B, 3, 1) X(B, 4, 1) X(B, 5, 1) X(B, 6, 1) X(B, 2, 2) X(B, 3, 2)
-  CASES(4) CASES(8) CASES(16) return hipErrorInvalidValue;
+  CASES(4) CASES(6) CASES(8) CASES(16) return hipErrorInvalidValue;
 #undef CASES
 #undef X
   return hipGetLastError();

@@ -40,6 +40,11 @@ CASES = {
     "decode_1l_q4": ("decode_b1", dict(T=2, H=1024, E=8, I=8192)),
     "decode_1l_q8": ("decode_b1", dict(T=1, H=2048, E=8, I=6144, bits=8)),
     "decode_1l_fp16": ("decode_b1", dict(T=1, H=1024, E=8, I=3072, bits=16)),
+    # 6-bit codes (decode path only): a ragged batch, three chunks per lane,
+    # and the longest down row the decode kernels take (six chunks per lane)
+    "decode_q6": ("decode_b1", dict(T=3, H=1024, E=16, I=704, bits=6)),
+    "decode_q6_h4096": ("decode_b1", dict(T=1, H=4096, E=8, I=2816, bits=6)),
+    "decode_q6_long": ("decode_b1", dict(T=2, H=1024, E=8, I=6144, bits=6)),
 }
 
 
@@ -67,6 +72,8 @@ def _run(dev, flags, fused_tensor=True):
 
 def _paths(inp):
     P = inp.T * inp.kcap
+    if inp.bits == 6:  # the batched path takes 4-, 8- and 16-bit weights only
+        return [("gemv", moe.FLAG_FORCE_GEMV)]
     paths = [("mfma", moe.FLAG_FORCE_MFMA)]
     if P <= 128:
         paths.append(("gemv", moe.FLAG_FORCE_GEMV))
@@ -184,6 +191,16 @@ def test_packed_sb_layout_and_bit_identity(name, built):
         y1 = moe.layer_forward(dev.x, dev.wr, inp.k, down, gate_up=gate_up, flags=flags)
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(y1), y0), flags
+
+
+def test_six_bit_weights_refused_on_the_batched_path(built):
+    inp, _, dev = built("decode_q6")
+    with pytest.raises(moe.MoeError) as e:
+        dev.forward(flags=moe.FLAG_FORCE_MFMA)
+    assert e.value.name == "MOE_ERR_QUANT"
+    with pytest.raises(moe.MoeError) as e:
+        moe.pack_sb(dev.down)
+    assert e.value.name == "MOE_ERR_QUANT"
 
 
 def test_runs_are_deterministic(built):
