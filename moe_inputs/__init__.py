@@ -120,9 +120,10 @@ def decode_half(b: np.ndarray, dtype: str) -> np.ndarray:
 class Weights:
     """One expert weight tensor [E, N, K].
 
-    bits 4/6/8: ``q`` uint8 [E, N, K/2] (4-bit, low nibble = even column),
-    [E, N, 3K/4] (6-bit, code k at bits 6k..6k+5 of the row's little-endian bit
-    stream) or [E, N, K] (8-bit); ``scales``/``biases`` fp16 bits [E, N, K/group].
+    bits 4/5/6/8: ``q`` uint8 [E, N, K/2] (4-bit, low nibble = even column),
+    [E, N, 5K/8] or [E, N, 3K/4] (5- or 6-bit, code k at bits b*k..b*k+b-1 of
+    the row's little-endian bit stream, b = bits) or [E, N, K] (8-bit);
+    ``scales``/``biases`` fp16 bits [E, N, K/group].
     bits 16:  ``q`` fp16 bits [E, N, K]; scales/biases None.
     """
 
@@ -148,7 +149,7 @@ def quant_weights(seed: int, tid: int, E: int, N: int, K: int, bits: int, sigma:
     if bits == 16:
         q = normal_half(seed, tid, E * N * K, sigma, "f16").reshape(E, N, K)
         return Weights(q, None, None, E, N, K, 16, gs)
-    assert bits in (4, 6, 8) and K % gs == 0
+    assert bits in (4, 5, 6, 8) and K % gs == 0
     q = np.empty((E, N, K * bits // 8), np.uint8)
     s = np.empty((E, N, K // gs), np.uint16)
     b = np.empty((E, N, K // gs), np.uint16)

@@ -199,19 +199,20 @@ static void quant_group(const double* w, int gs, int bits, uint8_t* codes, uint1
 
 /*
  * Store one group's codes at column offset `col` of a row.  bits 4: two per
- * byte, low nibble = even column; bits 6: a little-endian bit stream, code i
- * of the row at bits 6i .. 6i+5 (byte 6i/8, shifted by 6i%8, spilling into the
- * next byte); bits 8: one per byte.  dst must start zeroed for bits 6.
+ * byte, low nibble = even column; bits 5 and 6: a little-endian bit stream,
+ * code i of the row at bits b*i .. b*i+b-1 (byte b*i/8, shifted by b*i%8,
+ * spilling into the next byte; b = bits); bits 8: one per byte.  dst must
+ * start zeroed for bits 5 and 6.
  */
 static void store_codes(const uint8_t* codes, int gs, int bits, int64_t col, uint8_t* dst) {
   if (bits == 4) {
     for (int i = 0; i < gs; i += 2) dst[(col + i) / 2] = (uint8_t)(codes[i] | (codes[i + 1] << 4));
-  } else if (bits == 6) {
+  } else if (bits == 5 || bits == 6) {
     for (int i = 0; i < gs; ++i) {
-      int64_t bit = 6 * (col + i);
+      int64_t bit = (int64_t)bits * (col + i);
       int sh = (int)(bit % 8);
       dst[bit / 8] |= (uint8_t)(codes[i] << sh);
-      if (sh > 2) dst[bit / 8 + 1] |= (uint8_t)(codes[i] >> (8 - sh));
+      if (sh + bits > 8) dst[bit / 8 + 1] |= (uint8_t)(codes[i] >> (8 - sh));
     }
   } else {
     memcpy(dst + col, codes, (size_t)gs);
@@ -237,6 +238,7 @@ void gen_quantize_rows(const double* w, int64_t rows, int K, int bits, int gs, u
  * Draw an expert weight tensor [E, N, K] of N(0, sigma) values (flat index
  * (e*N + n)*K + k of stream `tid`) and quantise it by groups of `gs` columns.
  *   q:      bits == 4: [E, N, K/2] bytes, low nibble = even column;
+ *           bits == 5: [E, N, 5K/8] bytes, a little-endian 5-bit stream per row;
  *           bits == 6: [E, N, 3K/4] bytes, a little-endian 6-bit stream per row;
  *           bits == 8: [E, N, K] bytes
  *   scales, biases: [E, N, K/gs] fp16 bits

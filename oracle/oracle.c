@@ -123,8 +123,9 @@ uint16_t oracle_float_to_half(float f, int dtype) {
 
 /*
  * One row of K weights.  bits 4: two codes per byte, even column in the low
- * nibble; bits 6: code k at bits 6k .. 6k+5 of the row read as a
- * little-endian bit stream; bits 8: one code per byte; code q is unsigned.  w = s*q + b in fp32
+ * nibble; bits 5 and 6: code k at bits b*k .. b*k+b-1 of the row read as a
+ * little-endian bit stream (b = bits); bits 8: one code per byte; code q is
+ * unsigned.  w = s*q + b in fp32
  * (two roundings), s and b fp16, one pair per 64-column group.
  * bits 16: the row is fp16 values, copied.
  */
@@ -140,12 +141,12 @@ void oracle_dequant_row(const void* q_row, const uint16_t* s_row, const uint16_t
     int code;
     if (bits == 4) {
       code = (q[k / 2] >> (4 * (k & 1))) & 15;
-    } else if (bits == 6) {
-      int64_t bit = 6 * (int64_t)k;
+    } else if (bits == 5 || bits == 6) {
+      int64_t bit = (int64_t)bits * k;
       int sh = (int)(bit % 8);
       int v = q[bit / 8] >> sh;
-      if (sh > 2) v |= q[bit / 8 + 1] << (8 - sh);
-      code = v & 63;
+      if (sh + bits > 8) v |= q[bit / 8 + 1] << (8 - sh);
+      code = v & ((1 << bits) - 1);
     } else {
       code = q[k];
     }

@@ -24,11 +24,11 @@ def codes(w: mi.Weights) -> np.ndarray:
         lo = (w.q & 0x0F).astype(np.int64)
         hi = (w.q >> 4).astype(np.int64)
         return np.stack([lo, hi], axis=-1).reshape(w.E, w.N, w.K)
-    if w.bits == 6:
-        # each row's bytes as a little-endian bit stream, six bits per code
-        bits = np.unpackbits(w.q.reshape(-1, w.q.shape[-1]), axis=-1, bitorder="little")
-        six = bits.reshape(-1, w.K, 6).astype(np.int64)
-        return (six << np.arange(6)).sum(axis=-1).reshape(w.E, w.N, w.K)
+    if w.bits in (5, 6):
+        # each row's bytes as a little-endian bit stream, `bits` bits per code
+        stream = np.unpackbits(w.q.reshape(-1, w.q.shape[-1]), axis=-1, bitorder="little")
+        per_code = stream.reshape(-1, w.K, w.bits).astype(np.int64)
+        return (per_code << np.arange(w.bits)).sum(axis=-1).reshape(w.E, w.N, w.K)
     return w.q.astype(np.int64)
 
 

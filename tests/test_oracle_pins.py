@@ -79,9 +79,10 @@ def test_dequant_golden(case):
     codes = np.array(case["codes"], np.uint8)
     if case["bits"] == 4:
         q = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)  # even column -> low nibble
-    elif case["bits"] == 6:
+    elif case["bits"] in (5, 6):
         # the bits of each code, least significant first, as one little-endian stream
-        stream = ((codes[:, None].astype(np.int64) >> np.arange(6)) & 1).astype(np.uint8).ravel()
+        nb = case["bits"]
+        stream = ((codes[:, None].astype(np.int64) >> np.arange(nb)) & 1).astype(np.uint8).ravel()
         q = np.packbits(stream, bitorder="little")
     else:
         q = codes
@@ -90,7 +91,7 @@ def test_dequant_golden(case):
     assert np.array_equal(got, np.array(case["expect"], np.float32))
 
 
-@pytest.mark.parametrize("bits", [4, 6, 8])
+@pytest.mark.parametrize("bits", [4, 5, 6, 8])
 def test_dequant_requantize_returns_same_codes(bits):
     w = mi.quant_weights(77, 2, 2, 8, 256, bits)
     deq = oracle.dequant(w)  # fp32
@@ -100,7 +101,7 @@ def test_dequant_requantize_returns_same_codes(bits):
     assert np.array_equal(b2.reshape(w.biases.shape), w.biases)
 
 
-@pytest.mark.parametrize("bits", [4, 6, 8, 16])
+@pytest.mark.parametrize("bits", [4, 5, 6, 8, 16])
 def test_dequant_matches_fp64_statement(bits):
     w = mi.quant_weights(5, 3, 2, 16, 192, bits)
     got = oracle.dequant(w).astype(np.float64)
@@ -383,6 +384,7 @@ def test_all_experts_selected_is_the_dense_softmax_mixture():
     dict(name="prefill", T=24, H=128, E=16, I=128),
     dict(name="entropy", T=8, H=256, E=8, I=128, bits=4),
     dict(name="decode_b1", T=3, H=256, E=8, I=192, bits=6),
+    dict(name="decode_b1", T=2, H=192, E=8, I=256, bits=5),
 ], ids=lambda kw: "-".join("%s%s" % (k, v) for k, v in kw.items()))
 def test_layer_matches_dense_fp64_brute_force(kw):
     kw = dict(kw)
