@@ -37,6 +37,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 WORKLOADS = {
     "decode_b1": dict(recipe="decode_b1", pool=256, T=1,
                       label="decode b1: 1 token/step, H=4096, E=64, top-4, I=11008, 4-bit g64 weights, fp16"),
+    "decode_q6": dict(recipe="decode_b1", pool=256, T=1, bits=6, I=2816,
+                      label="decode b1: 1 token/step, H=4096, E=64, top-4, I=2816, 6-bit g64 weights, fp16"),
     "batched_decode": dict(recipe="batched_decode", pool=None, T=64,
                            label="batched decode: 64 tokens, H=4096, E=32, top-2, I=2816, 8-bit g64, bf16, Zipf 1.1"),
     "prefill": dict(recipe="prefill", pool=None, T=4096,
@@ -162,8 +164,9 @@ def main():
 
     t0 = time.time()
     kw = {}
-    if "bits" in wl:
-        kw["bits"] = wl["bits"]
+    for key in ("bits", "I"):
+        if key in wl:
+            kw[key] = wl[key]
     if recipe == "entropy":
         kw["segment"] = 2
     T_pool = wl["pool"] or wl["T"]
