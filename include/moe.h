@@ -88,13 +88,17 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
  *
  *   bits == 4:  q      uint8 [rows, K/2], two codes per byte, the even column
  *                      in the low nibble; codes are unsigned 0..15
+ *   bits == 5:  q      uint8 [rows, 5K/8], code k at bits 5k .. 5k+4 of the row
+ *                      read as a little-endian bit stream (eight codes per five
+ *                      bytes); codes 0..31
  *   bits == 6:  q      uint8 [rows, 3K/4], code k at bits 6k .. 6k+5 of the row
  *                      read as a little-endian bit stream (four codes per three
- *                      bytes); codes 0..63.  Decode path only: a 6-bit layer
- *                      that takes the batched path (or MOE_FLAG_FORCE_MFMA)
- *                      returns MOE_ERR_QUANT, as does moe_pack_sb
+ *                      bytes); codes 0..63
+ *               5 and 6 bits: decode path only.  A layer that would take the
+ *                      batched path (or MOE_FLAG_FORCE_MFMA) returns
+ *                      MOE_ERR_QUANT, as does moe_pack_sb
  *   bits == 8:  q      uint8 [rows, K], codes 0..255
- *   bits 4,6,8: scales fp16 [rows, K/group_size], biases fp16 [rows, K/group_size];
+ *   bits 4-8:   scales fp16 [rows, K/group_size], biases fp16 [rows, K/group_size];
  *               w[n, k] = scales[n, k/gs] * q[n, k] + biases[n, k/gs]
  *               (affine group quantisation, one scale/bias per row and group)
  *   bits == 16: q      fp16 [rows, K] weights; scales and biases must be NULL

@@ -149,8 +149,9 @@ def _dtype_code(t: torch.Tensor) -> int:
 class Weights:
     """Device weight tensor [E, N, K] in the library's layout (see include/moe.h).
 
-    bits 4: q uint8 [E, N, K/2]; bits 6: q uint8 [E, N, 3K/4] (code k at bits
-    6k..6k+5 of the row's little-endian bit stream); bits 8: q uint8 [E, N, K];
+    bits 4: q uint8 [E, N, K/2]; bits 5 / 6: q uint8 [E, N, 5K/8] / [E, N, 3K/4]
+    (code k at bits b*k..b*k+b-1 of the row's little-endian bit stream, b =
+    bits; decode path only); bits 8: q uint8 [E, N, K];
     bits 16: q float16 [E, N, K].  scales/biases float16 [E, N, K/64] (None for bits 16).
     ``row_offset``/``stride`` describe a view (the gate or up half of a fused
     tensor): rows start ``row_offset`` rows in, experts are ``stride`` rows apart.

@@ -55,25 +55,42 @@ __device__ __forceinline__ void for_slot(int s, F f) {
 }
 
 // A lane's unit of a weight row: 16 bytes (32 4-bit, 16 8-bit or 8 fp16
-// weights), or 12 bytes of 6-bit codes (16 weights: three whole words)
+// weights), 12 bytes of 6-bit codes (16 weights: three whole words) or 20
+// bytes of 5-bit codes (32 weights: five whole words)
 template <int BITS>
 struct Chunk {
-  static constexpr int VALS = BITS == 4 ? 32 : (BITS == 6 || BITS == 8 ? 16 : 8);  // weights per chunk
-  static constexpr int BYTES = BITS == 6 ? 12 : 16;                                 // bytes per chunk
+  static constexpr int VALS = BITS == 4 || BITS == 5 ? 32 : (BITS == 6 || BITS == 8 ? 16 : 8);  // weights per chunk
+  static constexpr int BYTES = BITS == 6 ? 12 : (BITS == 5 ? 20 : 16);                          // bytes per chunk
   static constexpr int PAIRS = VALS / 2;       // fp16 pairs of activations
   static constexpr int PER_GROUP = 64 / VALS;  // chunks per 64-column group
   static constexpr int PIECES = VALS / 8;      // 16-byte activation pieces
 };
 
 int gemv_lanes_chunks(int K, int bits) {
-  int vals = bits == 4 ? 32 : (bits == 6 || bits == 8 ? 16 : 8);
+  int vals = bits == 4 || bits == 5 ? 32 : (bits == 6 || bits == 8 ? 16 : 8);
   return (K / vals + 63) / 64;
 }
 
+// a chunk's words in registers: four, or five for 5-bit codes
+struct Raw5 {
+  u32x4 a;
+  uint32_t e;
+};
+template <int BITS>
+struct RawOf {
+  typedef u32x4 T;
+};
+template <>
+struct RawOf<5> {
+  typedef Raw5 T;
+};
+
 // one chunk of codes (a 6-bit chunk is 12 bytes: the fourth word is zero)
 template <int BITS>
-__device__ __forceinline__ u32x4 load_chunk_nt(rsrc_t r, uint32_t off) {
-  if constexpr (BITS == 6) {
+__device__ __forceinline__ typename RawOf<BITS>::T load_chunk_nt(rsrc_t r, uint32_t off) {
+  if constexpr (BITS == 5) {
+    return Raw5{buf_load16_nt(r, off), __builtin_amdgcn_raw_buffer_load_b32(r, (int)off + 16, 0, AUX_NT)};
+  } else if constexpr (BITS == 6) {
     typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
     const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)off, 0, AUX_NT);
     return u32x4{v.x, v.y, v.z, 0u};
@@ -104,7 +121,7 @@ __device__ __forceinline__ XSums chunk_xsums(const uint32_t* xp) {
     }
     r.k = 1024.0f * a + 64.0f * b;
     r.x = a + b;
-  } else if constexpr (BITS == 6 || BITS == 8) {
+  } else if constexpr (BITS == 5 || BITS == 6 || BITS == 8) {
     float a = 0.0f;
 #pragma unroll
     for (int j = 0; j < Chunk<BITS>::PAIRS; ++j) {
@@ -126,8 +143,37 @@ __device__ __forceinline__ float half_bits_f(uint32_t b) {
 // (A, B: dot sums over the two kinds of biased pairs).  The fp16 scale and
 // bias enter the fused multiply-adds directly (v_fma_mix_f32).
 template <int BITS>
-__device__ __forceinline__ float chunk_acc(u32x4 w, const uint32_t* xp, const XSums& xs, uint32_t s_bits,
-                                           uint32_t b_bits, const Q4Consts& qc, float acc) {
+__device__ __forceinline__ float chunk_acc_words(u32x4 w, const uint32_t* xp, const XSums& xs, uint32_t s_bits,
+                                                 uint32_t b_bits, const Q4Consts& qc, float acc);
+
+template <int BITS>
+__device__ __forceinline__ float chunk_acc(const typename RawOf<BITS>::T& w, const uint32_t* xp, const XSums& xs,
+                                           uint32_t s_bits, uint32_t b_bits, const Q4Consts& qc, float acc) {
+  if constexpr (BITS == 5) {
+    // 32 codes in the 160-bit little-endian value of the five words: code i
+    // at bits 5i .. 5i+4; pairs of codes become biased fp16 pairs as for 8 bits
+    const uint32_t wv[5] = {w.a.x, w.a.y, w.a.z, w.a.w, w.e};
+    auto code = [&](int i) __attribute__((always_inline)) -> uint32_t {
+      const int bit = 5 * i, wd = bit >> 5, sh = bit & 31;
+      if (sh + 5 <= 32) return (wv[wd] >> sh) & 31u;
+      return ((wv[wd] >> sh) | (wv[wd + 1] << (32 - sh))) & 31u;
+    };
+    float A = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t p = 0x64006400u | code(2 * j) | (code(2 * j + 1) << 16);
+      A = dot2(p, xp[j], A);
+    }
+    const float dq = A - xs.k;
+    return __builtin_fmaf(half_bits_f(s_bits), dq, __builtin_fmaf(half_bits_f(b_bits), xs.x, acc));
+  } else {
+    return chunk_acc_words<BITS>(w, xp, xs, s_bits, b_bits, qc, acc);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ float chunk_acc_words(u32x4 w, const uint32_t* xp, const XSums& xs, uint32_t s_bits,
+                                                 uint32_t b_bits, const Q4Consts& qc, float acc) {
   const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
   if constexpr (BITS == 4) {
     float A = 0.0f, B = 0.0f;
@@ -205,7 +251,7 @@ struct Rows {
 template <int BITS, int CPL>
 struct RowBuf {
   static constexpr int R = Rows<CPL>::N;
-  u32x4 q[R][CPL];
+  typename RawOf<BITS>::T q[R][CPL];
   uint32_t s[R][CPL], b[R][CPL];
 };
 
@@ -425,6 +471,7 @@ hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_
   if (bits == 4) return fused ? launch_up_cpl<4, true>(cpl, prm, grid, st) : launch_up_cpl<4, false>(cpl, prm, grid, st);
   if (bits == 8) return fused ? launch_up_cpl<8, true>(cpl, prm, grid, st) : launch_up_cpl<8, false>(cpl, prm, grid, st);
   if (bits == 6) return fused ? launch_up_cpl<6, true>(cpl, prm, grid, st) : launch_up_cpl<6, false>(cpl, prm, grid, st);
+  if (bits == 5) return fused ? launch_up_cpl<5, true>(cpl, prm, grid, st) : launch_up_cpl<5, false>(cpl, prm, grid, st);
   return fused ? launch_up_cpl<16, true>(cpl, prm, grid, st) : launch_up_cpl<16, false>(cpl, prm, grid, st);
 }
 
@@ -458,7 +505,7 @@ struct GemvDownParams {
 
 template <int BITS, int DCPL>
 struct DownBuf {
-  u32x4 q[DCPL];
+  typename RawOf<BITS>::T q[DCPL];
   uint32_t s[DCPL], b[DCPL];
 };
 
@@ -680,7 +727,7 @@ hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_sta
 #define X(B, D, K) \
   if (bits == B && dc == D && ks == K) launch_kernel(gemv_down_kernel<B, D, K>, grid, block, 0, st, prm); else
 #define CASES(B) X(B, 1, 1) X(B, 2, 1) X(B, 3, 1) X(B, 4, 1) X(B, 5, 1) X(B, 6, 1) X(B, 2, 2) X(B, 3, 2)
-  CASES(4) CASES(6) CASES(8) CASES(16) return hipErrorInvalidValue;
+  CASES(4) CASES(5) CASES(6) CASES(8) CASES(16) return hipErrorInvalidValue;
 #undef CASES
 #undef X
   return hipGetLastError();

@@ -101,7 +101,7 @@ moe_status device_props(DevProps* out) {
 
 moe_status check_weights(const moe_weights* w, int E, int N, int K) {
   if (!w || !w->q) return MOE_ERR_NULL;
-  if (w->bits != 4 && w->bits != 6 && w->bits != 8 && w->bits != 16) return MOE_ERR_QUANT;
+  if (w->bits != 4 && w->bits != 5 && w->bits != 6 && w->bits != 8 && w->bits != 16) return MOE_ERR_QUANT;
   if (w->bits == 16) {
     if (w->scales || w->biases) return MOE_ERR_QUANT;
   } else {
@@ -302,7 +302,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
                          moe::gemv_down_lds_bytes(kcap, I, bits) <= props.lds_max;
   bool gemv = false;
   if (!(flags & MOE_FLAG_FORCE_MFMA)) gemv = gemv_fits && ((flags & MOE_FLAG_FORCE_GEMV) || P <= kGemvMaxPairs);
-  if (bits == 6 && !gemv) return MOE_ERR_QUANT;  // 6-bit codes: decode path only
+  if ((bits == 5 || bits == 6) && !gemv) return MOE_ERR_QUANT;  // 5- and 6-bit codes: decode path only
   const bool want_sort_taps = taps && (taps->counts || taps->offsets || taps->perm);
   const int k_static = k > 0 ? k : 0;
 
@@ -591,7 +591,7 @@ size_t moe_packed_sb_bytes(int32_t E, int64_t expert_stride_rows, int32_t K) {
 
 moe_status moe_pack_sb(const moe_weights* w, void* out, void* stream) {
   if (!w || !out) return MOE_ERR_NULL;
-  if (w->bits == 16 || w->bits == 6) return MOE_ERR_QUANT;  // packed_sb serves the batched path (4 and 8 bits)
+  if (w->bits != 4 && w->bits != 8) return MOE_ERR_QUANT;  // packed_sb serves the batched path (4 and 8 bits)
   moe_status s = check_weights(w, w->E, w->N, w->K);
   if (s != MOE_OK) return s;
   if (!aligned16(out)) return MOE_ERR_ALIGN;

@@ -45,6 +45,11 @@ CASES = {
     "decode_q6": ("decode_b1", dict(T=3, H=1024, E=16, I=704, bits=6)),
     "decode_q6_h4096": ("decode_b1", dict(T=1, H=4096, E=8, I=2816, bits=6)),
     "decode_q6_long": ("decode_b1", dict(T=2, H=1024, E=8, I=6144, bits=6)),
+    # 5-bit codes (decode path only): one, two and (two waves per slot, a
+    # ragged last round) three chunks per lane
+    "decode_q5": ("decode_b1", dict(T=3, H=1024, E=16, I=704, bits=5)),
+    "decode_q5_h4096": ("decode_b1", dict(T=1, H=4096, E=8, I=2816, bits=5)),
+    "decode_q5_long": ("decode_b1", dict(T=2, H=1024, E=8, I=11008, bits=5)),
 }
 
 
@@ -72,7 +77,7 @@ def _run(dev, flags, fused_tensor=True):
 
 def _paths(inp):
     P = inp.T * inp.kcap
-    if inp.bits == 6:  # the batched path takes 4-, 8- and 16-bit weights only
+    if inp.bits in (5, 6):  # the batched path takes 4-, 8- and 16-bit weights only
         return [("gemv", moe.FLAG_FORCE_GEMV)]
     paths = [("mfma", moe.FLAG_FORCE_MFMA)]
     if P <= 128:
@@ -193,8 +198,9 @@ def test_packed_sb_layout_and_bit_identity(name, built):
         assert np.array_equal(host_bits(y1), y0), flags
 
 
-def test_six_bit_weights_refused_on_the_batched_path(built):
-    inp, _, dev = built("decode_q6")
+@pytest.mark.parametrize("name", ["decode_q5", "decode_q6"])
+def test_five_and_six_bit_weights_refused_on_the_batched_path(name, built):
+    inp, _, dev = built(name)
     with pytest.raises(moe.MoeError) as e:
         dev.forward(flags=moe.FLAG_FORCE_MFMA)
     assert e.value.name == "MOE_ERR_QUANT"
