@@ -37,6 +37,8 @@ MFMA_F16_PEAK_TFLOPS = 2500.0
 WORKLOADS = {
     "decode_b1": dict(recipe="decode_b1", pool=256, T=1,
                       label="decode b1: 1 token/step, H=4096, E=64, top-4, I=11008, 4-bit g64 weights, fp16"),
+    "decode_q5": dict(recipe="decode_b1", pool=256, T=1, bits=5, I=2816,
+                      label="decode b1: 1 token/step, H=4096, E=64, top-4, I=2816, 5-bit g64 weights, fp16"),
     "decode_q6": dict(recipe="decode_b1", pool=256, T=1, bits=6, I=2816,
                       label="decode b1: 1 token/step, H=4096, E=64, top-4, I=2816, 6-bit g64 weights, fp16"),
     "batched_decode": dict(recipe="batched_decode", pool=None, T=64,

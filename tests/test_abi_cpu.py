@@ -87,7 +87,8 @@ def test_zero_tokens_is_a_noop():
     (dict(ws=None), "MOE_ERR_WORKSPACE"),
     (dict(ws_bytes=1024), "MOE_ERR_WORKSPACE"),
     (dict(ws=P + 16), "MOE_ERR_ALIGN"),
-    (dict(gu=W(8, 2 * 128, 256, bits=5)), "MOE_ERR_QUANT"),
+    (dict(gu=W(8, 2 * 128, 256, bits=7)), "MOE_ERR_QUANT"),
+    (dict(gu=W(8, 2 * 128, 256, bits=3)), "MOE_ERR_QUANT"),
     (dict(gu=W(8, 2 * 128, 256, gs=32)), "MOE_ERR_QUANT"),
     (dict(gu=W(8, 2 * 128, 256, s=None)), "MOE_ERR_NULL"),
     (dict(gu=W(8, 2 * 128, 256, q=P + 4)), "MOE_ERR_ALIGN"),

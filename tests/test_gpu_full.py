@@ -60,7 +60,16 @@ def _assert_packed_same(dev, y):
 
 
 def test_decode_b1_full_size():
-    inp, gu_np, dev = _gen("decode_b1", T=6)
+    _decode_one_token_calls(*_gen("decode_b1", T=6), "decode_b1")
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+def test_decode_b1_full_size_5_and_6_bit(bits):
+    # the benchmark's 5- and 6-bit decode shape: H 4096, E 64, top-4, I 2816
+    _decode_one_token_calls(*_gen("decode_b1", T=4, I=2816, bits=bits), "decode_b1 %d-bit" % bits)
+
+
+def _decode_one_token_calls(inp, gu_np, dev, label):
     for t in range(inp.T):
         # one token per call, as the benchmark runs it
         x1 = dev.x[t:t + 1]
@@ -73,7 +82,7 @@ def test_decode_b1_full_size():
         tp = {k: v.cpu().numpy() for k, v in taps.items()}
         import dataclasses
         sub = dataclasses.replace(inp, T=1, x=np.ascontiguousarray(inp.x[t:t + 1]))
-        _check(sub, gu_np, y, tp, np.array([0]), "decode_b1 token %d" % t)
+        _check(sub, gu_np, y, tp, np.array([0]), "%s token %d" % (label, t))
 
 
 def test_decode_b1_full_size_mfma_path():
