@@ -50,6 +50,9 @@ CASES = {
     "decode_q5": ("decode_b1", dict(T=3, H=1024, E=16, I=704, bits=5)),
     "decode_q5_h4096": ("decode_b1", dict(T=1, H=4096, E=8, I=2816, bits=5)),
     "decode_q5_long": ("decode_b1", dict(T=2, H=1024, E=8, I=11008, bits=5)),
+    "decode_q5_bf16": ("decode_b1", dict(T=2, H=512, E=8, I=320, bits=5, dtype="bf16")),
+    # entropy-adaptive k on the decode path (kcap 3, 12 pairs)
+    "entropy_q6": ("entropy", dict(T=4, H=512, E=16, I=192, bits=6, segment=2)),
 }
 
 

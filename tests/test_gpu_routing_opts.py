@@ -84,7 +84,16 @@ LAYER_CASES = {
     "batched_small": ("batched_decode", dict(T=40, H=512, E=8, I=320), 2),
     "prefill_small": ("prefill", dict(T=300, H=512, E=16, I=192), 4),
     "entropy_q4": ("entropy", dict(T=96, H=512, E=16, I=192, bits=4, segment=2), 4),
+    "decode_q5": ("decode_b1", dict(T=3, H=512, E=16, I=320, bits=5), 4),
+    "decode_q6": ("decode_b1", dict(T=2, H=1024, E=16, I=704, bits=6), 4),
 }
+
+
+def _option_paths(inp):
+    """Both paths where the weights allow (5- and 6-bit codes: decode only)."""
+    P = inp.T * inp.kcap
+    paths = [] if inp.bits in (5, 6) else [("mfma", moe.FLAG_FORCE_MFMA)]
+    return paths + ([("gemv", moe.FLAG_FORCE_GEMV)] if P <= 128 else [])
 
 
 @pytest.mark.parametrize("name", list(LAYER_CASES))
@@ -96,8 +105,7 @@ def test_layer_with_options_matches_oracle(name):
     hv = _health(inp.E, seed=7)
     hd = torch.from_numpy(hv).cuda()
     alpha = 0.5
-    P = inp.T * inp.kcap
-    paths = [("mfma", moe.FLAG_FORCE_MFMA)] + ([("gemv", moe.FLAG_FORCE_GEMV)] if P <= 128 else [])
+    paths = _option_paths(inp)
     print("case", name, "T=%d E=%d k=%d groups=%d" % (inp.T, inp.E, inp.k, groups), flush=True)
     for pname, pflag in paths:
         outs = []
@@ -158,6 +166,8 @@ CAP_CASES = {
     "batched_small": ("batched_decode", dict(T=40, H=512, E=8, I=320), [3, 8]),
     "prefill_small": ("prefill", dict(T=300, H=512, E=16, I=192), [20, 64]),
     "entropy_q4": ("entropy", dict(T=96, H=512, E=16, I=192, bits=4, segment=2), [5]),
+    "decode_q5": ("decode_b1", dict(T=4, H=512, E=4, k=2, I=320, bits=5), [1, 3]),
+    "decode_q6": ("decode_b1", dict(T=4, H=512, E=4, k=2, I=320, bits=6), [1, 3]),
 }
 
 
@@ -167,8 +177,7 @@ def test_layer_with_capacity_matches_oracle(name):
     inp = mi.make_inputs(recipe, **kw)
     dev = Dev(inp)
     gu_np = oracle.fuse_gate_up(inp.gate, inp.up)
-    P = inp.T * inp.kcap
-    paths = [("mfma", moe.FLAG_FORCE_MFMA)] + ([("gemv", moe.FLAG_FORCE_GEMV)] if P <= 128 else [])
+    paths = _option_paths(inp)
     for pname, pflag in paths:
         base_t = moe.make_taps(inp.T, inp.E, inp.k, inp.I, "cuda")
         y0 = host_bits(moe.layer_forward(dev.x, dev.wr, inp.k, dev.down, gate_up=dev.gate_up, flags=pflag,
