@@ -115,7 +115,8 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
  * scales and biases as a few contiguous 128-byte lines instead of one line
  * per column.  NULL: the batched path repacks them into the workspace on every
  * call.  The gate and up views of a fused tensor share its packed_sb (the up
- * view's pointer is the gate view's plus inter*8 bytes).
+ * view's pointer is the gate view's plus inter*8 bytes).  Set for weights of
+ * other widths, it is refused with MOE_ERR_QUANT.
  */
 typedef struct {
   const void* q;

@@ -112,7 +112,8 @@ moe_status check_weights(const moe_weights* w, int E, int N, int K) {
   if (w->K % 64 != 0 || w->expert_stride_rows < w->N) return MOE_ERR_SHAPE;
   if (!aligned16(w->q)) return MOE_ERR_ALIGN;
   if (w->bits != 16 && (!aligned16(w->scales) || !aligned16(w->biases))) return MOE_ERR_ALIGN;
-  if (w->packed_sb && (w->bits == 16 || !aligned16(w->packed_sb))) return w->bits == 16 ? MOE_ERR_QUANT : MOE_ERR_ALIGN;
+  if (w->packed_sb && w->bits != 4 && w->bits != 8) return MOE_ERR_QUANT;  // packed_sb: 4- and 8-bit weights only
+  if (w->packed_sb && !aligned16(w->packed_sb)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
