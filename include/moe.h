@@ -94,7 +94,9 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
  *   bits == 6:  q      uint8 [rows, 3K/4], code k at bits 6k .. 6k+5 of the row
  *                      read as a little-endian bit stream (four codes per three
  *                      bytes); codes 0..63
- *               5 and 6 bits: decode path only.  A layer that would take the
+ *               5 and 6 bits: decode path only, within its register layout
+ *                      (5-bit: hidden <= 8192, inter <= 12288; 6-bit: hidden
+ *                      <= 4096, inter <= 6144).  A layer that would take the
  *                      batched path (or MOE_FLAG_FORCE_MFMA) returns
  *                      MOE_ERR_QUANT, as does moe_pack_sb
  *   bits == 8:  q      uint8 [rows, K], codes 0..255

@@ -212,6 +212,15 @@ def test_five_and_six_bit_weights_refused_on_the_batched_path(name, built):
     assert e.value.name == "MOE_ERR_QUANT"
 
 
+@pytest.mark.parametrize("bits,H,I", [(6, 8192, 128), (6, 256, 6208), (5, 256, 12352)])
+def test_five_and_six_bit_rows_beyond_the_decode_layout_are_refused(bits, H, I):
+    inp = mi.make_inputs("decode_b1", T=1, H=H, E=4, k=2, I=I, bits=bits)
+    dev = Dev(inp)
+    with pytest.raises(moe.MoeError) as e:
+        dev.forward(flags=moe.FLAG_FORCE_GEMV)
+    assert e.value.name == "MOE_ERR_QUANT"
+
+
 def test_runs_are_deterministic(built):
     inp, _, dev = built("prefill_small")
     a, _ = _run(dev, 0)
