@@ -484,11 +484,19 @@ hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_
 //
 // Workgroup = kcap waves, wave s handles slot s of token t: it keeps the
 // slot's SwiGLU row h in registers (in unpack order, with per-chunk sums) and
-// streams R rows m = blockIdx.x + j * gridDim.x of that slot's expert (so all
-// workgroups sweep the down weights linearly).  The row values o_s[m] meet in
+// streams R rows m = m0 + j * gridDim.x of that slot's expert, m0 its base row
+// (so all workgroups sweep the down weights linearly).  The row values o_s[m] meet in
 // LDS and wave 0 combines them in slot order: y = sum_s w_s * o_s.
 
 constexpr int DOWN_MAX_ROWS = 64;
+
+// Base row of workgroup b of G.  Workgroup b runs on XCD b % 8, and each XCD
+// has its own L2: when 8 divides G, the workgroups of one XCD take
+// consecutive base rows, so the scale/bias bytes two neighbouring rows share
+// in a 128-byte line are fetched by one XCD, not two (a bijection of [0, G)).
+__device__ __forceinline__ int down_row_base(int b, int G) {
+  return (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
+}
 
 size_t gemv_down_lds_bytes(int kcap, int I, int bits) {
   (void)I;
@@ -603,9 +611,9 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
       qoff[i] = (uint32_t)cc[i] * (uint32_t)C::BYTES;
       goff[i] = (uint32_t)(cc[i] / C::PER_GROUP) * 2u;
     }
-    // rows m(j) = blockIdx.x + j*G, j < nr; loads past the end go through
-    // empty resources (unconditional loads keep the wait counts exact)
-    const int m0 = blockIdx.x;
+    // rows m(j) = m0 + j*G, j < nr; loads past the end go through empty
+    // resources (unconditional loads keep the wait counts exact)
+    const int m0 = down_row_base(blockIdx.x, G);
     const int nr = min(R, (prm.H - m0 + G - 1) / G);
     auto m_of = [&](int j) { return m0 + (j < nr ? j : nr - 1) * G; };
     // SwiGLU-row loads first (see the gate+up kernel), then three weight rows;
@@ -676,7 +684,7 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
   }
   __syncthreads();
   if (wv == 0 && lane < R) {
-    const int m = blockIdx.x + lane * G;  // lanes past this workgroup's rows store nothing
+    const int m = down_row_base(blockIdx.x, G) + lane * G;  // lanes past this workgroup's rows store nothing
     if (m < prm.H) {
       float y = 0.0f;
       for (int q = 0; q < ku; ++q) {
