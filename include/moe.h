@@ -326,8 +326,8 @@ int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
 /*
  * Launch-shape knobs for measurement sweeps (process-wide): key 0 = resident
  * waves per CU targeted by the decode gate+up kernel (1.5 times that for
- * 5-bit codes with hidden <= 6144, whose kernels fit three or more waves per
- * SIMD), key 1 = by the decode
+ * 4- and 5-bit codes with hidden <= 6144, whose kernels fit three or more
+ * waves per SIMD), key 1 = by the decode
  * down kernel, key 2 = row tiles per group in the batched GEMM's tile order,
  * key 3 = the batched GEMM's row tile (32, 64 or 128; other values: chosen
  * from the batch), key 4 = K groups of 64 per pipeline stage (1; other

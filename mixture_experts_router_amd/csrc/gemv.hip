@@ -375,9 +375,10 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   // buffer's loads remain in flight while an older one is reduced.
   const int n = (prm.iters - gw + W - 1) / W;
   auto it_of = [&](int k) { return gw + (k < n ? k : n - 1) * W; };
-  // short rows: two iterations ahead, else one.  5-bit chunks are five words:
-  // one iteration ahead keeps the kernel at three waves per SIMD, not two
-  constexpr bool DEEP = CPL <= 2 && BITS != 5;
+  // short rows of 8-bit or fp16 weights: two iterations ahead, else one.
+  // With one ahead the 4- and 5-bit forms fit three waves per SIMD, not two,
+  // which streams faster than the deeper ring at two
+  constexpr bool DEEP = CPL <= 2 && BITS != 4 && BITS != 5;
 
   // activation loads first: vmcnt retires in issue order, so waiting for
   // them later does not wait for the weight loads issued after them
@@ -464,9 +465,10 @@ hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_
   const int rows = cpl <= 2 ? 4 : 2;
   prm.iters = fused ? N / (rows / 2) : N / rows;
   // about `waves_per_cu` resident waves per CU, shared by the pairs
-  // (1.5x for 5-bit codes at up to three chunks per lane, whose kernels fit
-  // three or more waves per SIMD rather than two)
-  const int upw = bits == 5 && cpl <= 3 ? tuning(TUNE_UP_WAVES_PER_CU) * 3 / 2 : tuning(TUNE_UP_WAVES_PER_CU);
+  // (1.5x for 4- and 5-bit codes at up to three chunks per lane, whose
+  // kernels fit three or more waves per SIMD rather than two)
+  const int upw = (bits == 4 || bits == 5) && cpl <= 3 ? tuning(TUNE_UP_WAVES_PER_CU) * 3 / 2
+                                                       : tuning(TUNE_UP_WAVES_PER_CU);
   const int64_t want = (int64_t)(num_cu > 0 ? num_cu : 256) * upw;
   int64_t per_pair = want / ((int64_t)T * kcap);
   if (per_pair < 4) per_pair = 4;
