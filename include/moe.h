@@ -147,6 +147,17 @@ typedef struct {
  *                                   within an expert; entries past the last pair -1
  *   h          fp16  [T*kcap, inter] SwiGLU output of pair t*kcap+s (unused slots
  *                                   untouched)
+ *   gate_up_preact fp32 [T*kcap, 2*inter] the gate+up projection of pair
+ *                                   t*kcap+s before SwiGLU: g in columns
+ *                                   [0, inter), u in [inter, 2*inter), the
+ *                                   fp32 sums the SwiGLU reads (oMLX gate/up
+ *                                   page, "how correctness is verified": the
+ *                                   fused output equals the separate
+ *                                   projections bit for bit).  Unused slots
+ *                                   untouched; rows of pairs a capacity drops
+ *                                   are unspecified.  Written by the kernels
+ *                                   that form g and u, so it costs HBM
+ *                                   writes: a debug tap
  */
 typedef struct {
   float* logits;
@@ -158,6 +169,7 @@ typedef struct {
   int32_t* offsets;
   int32_t* perm;
   void* h;
+  float* gate_up_preact;
 } moe_taps;
 
 /*

@@ -58,7 +58,8 @@ class CRouteOpts(ctypes.Structure):
 
 class CTaps(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("logits", "topk_idx", "topk_w", "k_used", "entropy", "counts", "offsets", "perm", "h")]
+                ("logits", "topk_idx", "topk_w", "k_used", "entropy", "counts", "offsets", "perm", "h",
+                 "gate_up_preact")]
 
 
 _lib = None
@@ -265,16 +266,19 @@ def topk_from_logits(logits: torch.Tensor, k: int, stream=None, groups: int = 0)
     return dict(idx=idx, w=w, k_used=ku, entropy=ent)
 
 
-TAP_NAMES = ("logits", "topk_idx", "topk_w", "k_used", "entropy", "counts", "offsets", "perm", "h")
+TAP_NAMES = ("logits", "topk_idx", "topk_w", "k_used", "entropy", "counts", "offsets", "perm", "h",
+             "gate_up_preact")
 
 
 def make_taps(T: int, E: int, k: int, inter: int, device, names: Sequence[str] = TAP_NAMES):
-    """Allocate tap buffers (logits, routing, sort results, SwiGLU rows)."""
+    """Allocate tap buffers (logits, routing, sort results, SwiGLU rows, fp32
+    gate+up pre-activations)."""
     kc = _kcap(k)
     P = T * kc
     spec = dict(logits=((T, E), torch.float32), topk_idx=((T, kc), torch.int32), topk_w=((T, kc), torch.float32),
                 k_used=((1,), torch.int32), entropy=((1,), torch.float32), counts=((E,), torch.int32),
-                offsets=((E + 1,), torch.int32), perm=((P,), torch.int32), h=((P, inter), torch.float16))
+                offsets=((E + 1,), torch.int32), perm=((P,), torch.int32), h=((P, inter), torch.float16),
+                gate_up_preact=((P, 2 * inter), torch.float32))
     return {n: torch.zeros(spec[n][0], dtype=spec[n][1], device=device) for n in names}
 
 
@@ -295,8 +299,7 @@ def layer_forward(x: torch.Tensor, router_w: torch.Tensor, k: int, down: Weights
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     ctaps = None
     if taps:
-        ctaps = CTaps(*[(taps[n].data_ptr() if n in taps and taps[n] is not None else None) for n in
-                        ("logits", "topk_idx", "topk_w", "k_used", "entropy", "counts", "offsets", "perm", "h")])
+        ctaps = CTaps(*[(taps[n].data_ptr() if n in taps and taps[n] is not None else None) for n in TAP_NAMES])
     cgu = gate_up.c() if gate_up is not None else None
     cg = gate.c() if gate is not None else None
     cu = up.c() if up is not None else None

@@ -118,6 +118,35 @@ hipError_t launch_gather_rows(const uint16_t* src, const int32_t* pos, int64_t P
   return hipGetLastError();
 }
 
+// The fp32 gate and up rows of the unfused paths, side by side in pair order
+// (the gate_up_preact tap).
+__global__ __launch_bounds__(256) void gather_preact_kernel(const float* __restrict__ g, const float* __restrict__ u,
+                                                            const int32_t* __restrict__ pos, int I,
+                                                            float* __restrict__ pre, int kcap,
+                                                            const int32_t* __restrict__ k_used, int k_static) {
+  const int64_t p = blockIdx.y;
+  int64_t r;
+  if (pos) {
+    r = pos[p];
+  } else {
+    const int ku = k_used ? *k_used : k_static;
+    r = (int)(p % kcap) < ku ? p : -1;
+  }
+  if (r < 0) return;
+  for (int c = (blockIdx.x * 256 + threadIdx.x) * 4; c < 2 * I; c += gridDim.x * 256 * 4) {
+    const float* src = c < I ? g + (size_t)r * I + c : u + (size_t)r * I + (c - I);
+    *(f32x4*)(pre + p * 2 * I + c) = *(const f32x4*)src;
+  }
+}
+
+hipError_t launch_gather_preact(const float* g, const float* u, const int32_t* pos, int64_t P, int I, float* pre,
+                                int kcap, const int32_t* k_used_dev, int k_static, hipStream_t st) {
+  if (I % 4 != 0) return hipErrorInvalidValue;
+  dim3 grid((2 * I / 4 + 255) / 256, (unsigned)P);
+  launch_kernel(gather_preact_kernel, grid, 256, 0, st, g, u, pos, I, pre, kcap, k_used_dev, k_static);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void copy_words_kernel(const uint32_t* __restrict__ s, uint32_t* __restrict__ d,
                                                          int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;

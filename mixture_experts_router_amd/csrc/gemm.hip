@@ -46,6 +46,7 @@ struct GemmParams {
   int kcap, E, K, N;
   WView w0, w1;
   void* out;
+  float* pre;  // fused: fp32 gate and up sums [pairs, 2N] in pair order (NULL: not kept)
   uint32_t a_bytes;  // extent of the A rows (offsets at or past it read nothing)
   int32_t sb_up_delta;  // fused: bytes from a gate column's packed scales to its up column's
   int perm8_out;  // fused: store h blocks in 4-bit unpack order
@@ -691,6 +692,16 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
           const int at = prm.perm8_out ? (col & ~7) + perm8_slot(col & 7) : col;
           ((uint16_t*)prm.out)[orow + at] = f32_to_f16_bits(hv);
         }
+        if (prm.pre) {
+          float* pr = prm.pre + (size_t)prm.perm[row0 + row] * 2 * prm.N;
+#pragma unroll
+          for (int ni = 0; ni < HALFSUB; ++ni) {
+            if (!valid[ni]) continue;
+            const int col = col0 + 32 * ni + col_in;
+            pr[col] = acc[mi][ni][r];
+            pr[prm.N + col] = acc[mi][ni + HALFSUB][r];
+          }
+        }
       } else {
 #pragma unroll
         for (int ni = 0; ni < NSUB; ++ni) {
@@ -767,8 +778,9 @@ static hipError_t launch_bits(GemmMode mode, int bm, const GemmParams& prm, hipS
 
 hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const int32_t* perm, const int32_t* counts,
                        const int32_t* offsets, int kcap, int E, int K, int N, int bits, WView w0, WView w1,
-                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st) {
+                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st, float* pre) {
   GemmParams prm;
+  prm.pre = mode == GEMM_FUSED_SWIGLU ? pre : nullptr;
   prm.a = a;
   prm.perm = perm;
   prm.counts = counts;

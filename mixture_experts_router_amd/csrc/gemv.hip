@@ -236,6 +236,7 @@ struct GemvUpParams {
   WView w0, w1;
   uint16_t* h;
   float* out32;
+  float* pre;  // fused: fp32 gate and up sums [pairs, 2N] (NULL: not kept)
   int iters;  // row-iterations per pair
   int iters_per_wave;
 };
@@ -315,6 +316,11 @@ __device__ __forceinline__ void finish_iter(const RowBuf<BITS, CPL>& buf, const 
     const float u = R == 4 ? dpp_f<DPP_QUAD_2323>(v) : dpp_f<DPP_QUAD_1111>(v);
     const float hv = swiglu(v, u);
     if (store && lane < R / 2) prm.h[(size_t)p * prm.N + (R / 2) * it + lane] = f32_to_f16_bits(hv);
+    if (prm.pre && store && lane < R) {
+      // lane r holds row r: gate rows first, then the matching up rows
+      const int col = lane < R / 2 ? (R / 2) * it + lane : prm.N + (R / 2) * it + (lane - R / 2);
+      prm.pre[(size_t)p * 2 * prm.N + col] = v;
+    }
   } else {
     if (store && lane < R) prm.out32[(size_t)p * prm.N + R * it + lane] = v;
   }
@@ -447,8 +453,9 @@ static hipError_t launch_up_cpl(int cpl, const GemvUpParams& prm, dim3 grid, hip
 
 hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_static, int kcap, int T, int H,
                           int N, int bits, bool fused, WView w0, WView w1, uint16_t* h, float* out32, int num_cu,
-                          hipStream_t st) {
+                          hipStream_t st, float* pre) {
   GemvUpParams prm;
+  prm.pre = fused ? pre : nullptr;
   prm.x = (const uint16_t*)x;
   prm.act = act;
   prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy, route.gs};
@@ -498,12 +505,6 @@ constexpr int DOWN_MAX_ROWS = 64;
 // in a 128-byte line are fetched by one XCD, not two (a bijection of [0, G)).
 __device__ __forceinline__ int down_row_base(int b, int G) {
   return (G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b;
-}
-
-size_t gemv_down_lds_bytes(int kcap, int I, int bits) {
-  (void)I;
-  (void)bits;
-  return (size_t)kcap * DOWN_MAX_ROWS * 4;
 }
 
 struct GemvDownParams {
@@ -702,11 +703,6 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
       ((uint16_t*)prm.y)[(size_t)t * prm.H + m] = f32_to_act_bits(y, prm.act);
     }
   }
-}
-
-hipError_t gemv_down_set_max_lds(int bytes) {
-  (void)bytes;
-  return hipSuccess;
 }
 
 int gemv_down_max_chunks_per_lane() { return 6; }

@@ -88,17 +88,15 @@ struct GemvRoute {
   float* entropy;
   int gs = 1;  // experts per selection group (1: plain top-k)
 };
-// fused=true: h[p, j] = fp16(swiglu(gate_j . x, up_j . x)) for j < I
+// fused=true: h[p, j] = fp16(swiglu(gate_j . x, up_j . x)) for j < I, and
+// with pre set also pre[p, j] = gate_j . x, pre[p, N + j] = up_j . x (fp32)
 // fused=false: out32[p, n] = w0_n . x for n < N
 hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_static, int kcap, int T, int H,
                           int N, int bits, bool fused, WView w0, WView w1, uint16_t* h, float* out32, int num_cu,
-                          hipStream_t st);
-// y[t, m] = act(sum_s w[t,s] * (Wd[e_s, m, :] . h[t*kcap+s, :]))
-size_t gemv_down_lds_bytes(int kcap, int I, int bits);
-// allow the down kernels up to `bytes` of dynamic LDS (once per device)
-hipError_t gemv_down_set_max_lds(int bytes);
+                          hipStream_t st, float* pre = nullptr);
 // largest 16-byte chunks per lane of a down row the decode kernels handle
 int gemv_down_max_chunks_per_lane();
+// y[t, m] = act(sum_s w[t,s] * (Wd[e_s, m, :] . h[t*kcap+s, :]));
 // capacity > 0: a pair beyond the first `capacity` pairs of its expert (pair
 // order) is left out of y (needs route.logits NULL: the selection is read)
 hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_static, int kcap, int T, int H, int I,
@@ -119,9 +117,11 @@ int gemm_max_mtiles(int P, int E, int bm);
 // order if perm8_out); GATHER_F32: out fp32 [rows, N]; ROWS_F16: out fp16
 // a_rows: rows of a (T or P); a and one expert's weight rows must each stay
 // below 4 GB (32-bit buffer offsets), else hipErrorInvalidValue
+// FUSED with pre set: also the fp32 gate and up sums of pair perm[row] at
+// pre[pair, col] and pre[pair, N + col]
 hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const int32_t* perm, const int32_t* counts,
                        const int32_t* offsets, int kcap, int E, int K, int N, int bits, WView w0, WView w1,
-                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st);
+                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st, float* pre = nullptr);
 
 // --------------------------------------------------------- small kernels
 // h[i, j] = fp16(swiglu(g[i, j], u[i, j])) for i < rows
@@ -135,6 +135,10 @@ hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wt
 // or, when pos is NULL, r = p for the pairs whose slot p % kcap < k_used
 hipError_t launch_gather_rows(const uint16_t* src, const int32_t* pos, int64_t P, int I, uint16_t* out, int kcap,
                               const int32_t* k_used_dev, int k_static, bool perm8, hipStream_t st);
+// pre[p, 0:I] = g[r, :], pre[p, I:2I] = u[r, :] (fp32 rows) with r chosen
+// as in launch_gather_rows
+hipError_t launch_gather_preact(const float* g, const float* u, const int32_t* pos, int64_t P, int I, float* pre,
+                                int kcap, const int32_t* k_used_dev, int k_static, hipStream_t st);
 // copy n int32/fp32 words
 hipError_t launch_copy_words(const void* src, void* dst, int64_t n, hipStream_t st);
 // scales/biases of rows [0, N) of E experts -> packed_sb layout (see moe.h)

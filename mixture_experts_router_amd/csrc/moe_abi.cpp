@@ -69,7 +69,6 @@ void plan_step(const char* name, hipStream_t st) {
 struct DevProps {
   bool ok = false;
   bool gfx950 = false;
-  size_t lds_max = 0;
   int num_cu = 0;
 };
 
@@ -85,12 +84,7 @@ moe_status device_props(DevProps* out) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
     p.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    p.lds_max = prop.sharedMemPerBlock;
     p.num_cu = prop.multiProcessorCount;
-    if (p.lds_max > 65536 && moe::gemv_down_set_max_lds((int)p.lds_max) != hipSuccess) {
-      (void)hipGetLastError();  // keep the portable 64 KB limit for the decode path
-      p.lds_max = 65536;
-    }
     p.ok = true;
   }
   *out = p;
@@ -143,7 +137,15 @@ struct Layout {
   size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, a16, hent, sbgu, sbd, g32, u32, total;
 };
 
-Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t flags) {
+// Which regions a call needs: the batched path's GEMM operands, and the
+// per-call repacks of scales and biases when the weights carry no packed_sb.
+// moe_layer_workspace_size reserves all of them (it cannot know the path or
+// the weights); a call lays out only what it uses.
+struct Needs {
+  bool batched = true, sb_gu = true, sb_d = true;
+};
+
+Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t flags, Needs nd = Needs{}) {
   Layout L{};
   const int64_t P = T * kcap;
   size_t at = 0;
@@ -161,12 +163,14 @@ Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t
   L.perm = take((size_t)(P * 4));
   L.pos = take((size_t)(P * 4));
   L.h = take((size_t)(P * I * 2));
-  L.o = take((size_t)(P * H * 2));
-  L.a16 = take((size_t)(T * H * 2));  // batched path: the activations as the GEMM's fp16 operand
-  L.hent = take((size_t)(T * 4));     // adaptive k: per-token entropies
-  // batched path: scales and biases repacked when the weights carry no packed_sb
-  L.sbgu = take((size_t)moe::packed_sb_bytes((int)E, 2 * I, (int)H));
-  L.sbd = take((size_t)moe::packed_sb_bytes((int)E, H, (int)I));
+  L.hent = take((size_t)(T * 4));  // adaptive k: per-token entropies
+  if (nd.batched) {
+    L.o = take((size_t)(P * H * 2));
+    L.a16 = take((size_t)(T * H * 2));  // the activations as the GEMM's fp16 operand
+    // scales and biases repacked when the weights carry no packed_sb
+    if (nd.sb_gu) L.sbgu = take((size_t)moe::packed_sb_bytes((int)E, 2 * I, (int)H));
+    if (nd.sb_d) L.sbd = take((size_t)moe::packed_sb_bytes((int)E, H, (int)I));
+  }
   if (flags & MOE_FLAG_UNFUSED) {
     L.g32 = take((size_t)(P * I * 4));
     L.u32 = take((size_t)(P * I * 4));
@@ -268,8 +272,18 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   }
   const int bits = down->bits;
   const int kcap = kcap_of(k);
-  const Layout L = layout(T, H, E, kcap, I, flags);
+  const int64_t P = (int64_t)T * kcap;
+  const bool gemv_fits = moe::gemv_lanes_chunks(H, bits) <= 4 &&
+                         moe::gemv_lanes_chunks(I, bits) <= moe::gemv_down_max_chunks_per_lane();
+  bool gemv = false;
+  if (!(flags & MOE_FLAG_FORCE_MFMA)) gemv = gemv_fits && ((flags & MOE_FLAG_FORCE_GEMV) || P <= kGemvMaxPairs);
+  Needs nd;
+  nd.batched = !gemv;
+  nd.sb_gu = bits != 16 && !(gate_up && gate_up->packed_sb);
+  nd.sb_d = bits != 16 && !down->packed_sb;
+  const Layout L = layout(T, H, E, kcap, I, flags, nd);
   if (T == 0) return MOE_OK;
+  if ((bits == 5 || bits == 6) && !gemv) return MOE_ERR_QUANT;  // 5- and 6-bit codes: decode path only
   if (!ws) return MOE_ERR_WORKSPACE;
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_ERR_ALIGN;
@@ -279,7 +293,6 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   if ((s = device_props(&props)) != MOE_OK) return s;
 
   uint8_t* W = (uint8_t*)ws;
-  const int64_t P = (int64_t)T * kcap;
   float* logits = (taps && taps->logits) ? taps->logits : (float*)(W + L.logits);
   int32_t* idx = (int32_t*)(W + L.idx);
   float* wts = (float*)(W + L.w);
@@ -298,13 +311,8 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   const int act = (int)dt;
   (void)pos;
 
-  const bool gemv_fits = moe::gemv_lanes_chunks(H, bits) <= 4 &&
-                         moe::gemv_lanes_chunks(I, bits) <= moe::gemv_down_max_chunks_per_lane() &&
-                         moe::gemv_down_lds_bytes(kcap, I, bits) <= props.lds_max;
-  bool gemv = false;
-  if (!(flags & MOE_FLAG_FORCE_MFMA)) gemv = gemv_fits && ((flags & MOE_FLAG_FORCE_GEMV) || P <= kGemvMaxPairs);
-  if ((bits == 5 || bits == 6) && !gemv) return MOE_ERR_QUANT;  // 5- and 6-bit codes: decode path only
   const bool want_sort_taps = taps && (taps->counts || taps->offsets || taps->perm);
+  float* pre_tap = taps ? taps->gate_up_preact : nullptr;
   const int k_static = k > 0 ? k : 0;
 
   plan_begin(st);
@@ -321,7 +329,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     }
     if (!unfused) {
       HIP_TRY(moe::launch_gemv_up(x, act, rt, k_static, kcap, T, H, I, bits, true, wg, wu, h, nullptr, props.num_cu,
-                                  st));
+                                  st, pre_tap));
       plan_step("gemv_gate_up_swiglu", st);
     } else {
       HIP_TRY(moe::launch_gemv_up(x, act, rt, k_static, kcap, T, H, I, bits, false, wg, wg, nullptr, g32,
@@ -332,6 +340,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       plan_step("gemv_up", st);
       HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, false, st));
       plan_step("swiglu", st);
+      if (pre_tap) HIP_TRY(moe::launch_gather_preact(g32, u32, nullptr, P, I, pre_tap, kcap, k_used, k_static, st));
     }
     // the gate+up kernel wrote the selection: the down kernel reads it
     // instead of selecting again
@@ -375,7 +384,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     }
     if (!unfused) {
       HIP_TRY(moe::launch_gemm(moe::GEMM_FUSED_SWIGLU, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wg, wu, h,
-                               perm8, bm, mt, st));
+                               perm8, bm, mt, st, pre_tap));
       plan_step("gemm_gate_up_swiglu", st);
     } else {
       HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wg, wg, g32,
@@ -386,6 +395,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       plan_step("gemm_up", st);
       HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, perm8, st));
       plan_step("swiglu", st);
+      if (pre_tap) HIP_TRY(moe::launch_gather_preact(g32, u32, pos, P, I, pre_tap, kcap, k_used, k_static, st));
     }
     WView wd = view_of(down, 0);
     if (bits != 16 && !wd.sb) {

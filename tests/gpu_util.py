@@ -14,6 +14,7 @@ import torch
 import mixture_experts_router_amd as moe
 import moe_inputs as mi
 import oracle
+from ref64 import half64
 
 MAX_ABS = 2e-2
 REL_L2 = 5e-3
@@ -96,7 +97,6 @@ def reference_outputs(inp: mi.LayerInputs, gate_up_np, tokens, gpu_idx, gpu_w, g
 
 
 def errors(y_bits: np.ndarray, y_ref: np.ndarray, dtype: str):
-    from ref64 import half64
     y = half64(y_bits, dtype)
     d = y - y_ref.astype(np.float64)
     max_abs = float(np.max(np.abs(d))) if d.size else 0.0
@@ -108,7 +108,7 @@ def errors(y_bits: np.ndarray, y_ref: np.ndarray, dtype: str):
 def assert_within_tolerance(y_bits, y_ref, dtype, label=""):
     max_abs, rel, floor = errors(y_bits, y_ref, dtype)
     print("%s max_abs=%.3g rel_l2=%.3g (rounding floor %.3g)" % (label, max_abs, rel, floor), flush=True)
-    assert np.all(np.isfinite(y_bits.astype(np.float64))), "non-finite output"
+    assert np.all(np.isfinite(half64(y_bits, dtype))), "non-finite output"
     assert max_abs <= MAX_ABS, (label, max_abs)
     assert rel <= REL_L2, (label, rel)
     return max_abs, rel

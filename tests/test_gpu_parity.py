@@ -115,6 +115,20 @@ def test_fused_and_unfused_are_bit_identical(name, built):
         hf = t_f["h"].view(np.uint16)[valid]
         assert np.array_equal(hf, t_u["h"].view(np.uint16)[valid]), "%s/%s SwiGLU rows" % (name, pname)
         assert np.array_equal(hf, t_s["h"].view(np.uint16)[valid])
+        # the fp32 gate+up sums themselves, before SwiGLU and its fp16 rounding
+        # (oMLX gate/up page, how correctness is verified: fused == separate)
+        pf = t_f["gate_up_preact"].view(np.uint32)[valid]
+        assert np.array_equal(pf, t_u["gate_up_preact"].view(np.uint32)[valid]), "%s/%s gate_up preact" % (name,
+                                                                                                         pname)
+        assert np.array_equal(pf, t_s["gate_up_preact"].view(np.uint32)[valid])
+        # the tap holds the values the SwiGLU rows were formed from
+        g = t_f["gate_up_preact"][valid][:, :inp.I].astype(np.float64)
+        u = t_f["gate_up_preact"][valid][:, inp.I:].astype(np.float64)
+        with np.errstate(over="ignore"):
+            h_host = (g / (1.0 + np.exp(-g)) * u).astype(np.float16).astype(np.float64)
+        h_gpu = t_f["h"][valid].astype(np.float64)
+        ulp = np.spacing(np.abs(h_host).astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(h_gpu - h_host) <= ulp + 1e-7), "%s/%s preact vs h" % (name, pname)
 
 
 @pytest.mark.parametrize("name", ["tiny", "prefill_small", "batched_small", "entropy_q4", "ragged_shapes",

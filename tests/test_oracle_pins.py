@@ -564,6 +564,44 @@ def test_route_with_options_is_correction_then_grouped_selection():
     assert np.array_equal(idx, i2) and np.array_equal(w, w2)
 
 
+@pytest.mark.parametrize("m,shift,n_moved,k_raw,k_corr", [(12, 40.0, 9, 2, 1), (3, -40.0, 10, 1, 3)])
+def test_entropy_is_taken_on_corrected_logits(m, shift, n_moved, k_raw, k_corr):
+    # Page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析": section 3.3 corrects the
+    # logits by the load index before routing, and section 2.2 picks k from
+    # the entropy of the routing distribution, so the entropy is that of the
+    # corrected logits.  m equal dominant logits 40 above the other E - m give
+    # H = ln m (closed form; the others add about E e^-40).  The correction
+    # alpha * health with alpha = 40 and health 1 (or -1) on n_moved experts
+    # takes them down to (or up to) the others' level, moving H across a band
+    # edge: ln 12 = 2.485 -> ln 3 = 1.099 (k 2 -> 1), ln 3 -> ln 13 = 2.565
+    # (k 1 -> 3).
+    E, H, T = 32, 64, 4
+    x = mi.round_half(np.eye(T, H) * 4.0, "f16")
+    wr64 = np.zeros((E, H))
+    wr64[:m, :T] = 10.0  # logit 40 for the m dominant experts of every token
+    wr = mi.round_half(wr64, "f16")
+    health = np.zeros(E, np.float32)
+    if shift > 0:
+        moved = np.arange(m - n_moved, m)  # the last n_moved dominant experts drop to 0
+        health[moved] = 1.0
+    else:
+        moved = np.arange(m, m + n_moved)  # n_moved others rise to 40
+        health[moved] = -1.0
+    alpha = abs(shift)
+    m_corr = m - n_moved if shift > 0 else m + n_moved
+    _, _, ku_raw, h_raw = oracle.route(x, wr, "f16", -1)
+    assert ku_raw == k_raw and abs(h_raw - math.log(m)) < 1e-5
+    idx, w, ku, hm, logits = oracle.route(x, wr, "f16", -1, want_logits=True, health=health, alpha=alpha)
+    assert abs(hm - math.log(m_corr)) < 1e-5, hm
+    assert ku == k_corr
+    dominant = np.flatnonzero(logits[0] == 40.0)
+    assert dominant.size == m_corr
+    # top-k_corr of equal logits: the lowest indices, equal weights 1/k
+    assert np.array_equal(idx[:, :ku], np.tile(dominant[:ku], (T, 1)))
+    assert np.all(idx[:, ku:] == -1) and np.all(w[:, ku:] == 0)
+    assert np.allclose(w[:, :ku], 1.0 / ku, atol=1e-7, rtol=0)
+
+
 # ------------------------------------------------------------- capacity --
 # Page "Qwen3.5-MoE与Qwen3-MoE架构差异深度解析", section 5.2: a per-expert token
 # capacity (expert_capacity).  Reading: the first C pairs of an expert in pair
