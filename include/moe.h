@@ -68,7 +68,9 @@ typedef enum {
   MOE_ERR_DEVICE = -9,       /* no usable gfx950 device is current */
   MOE_ERR_HIP = -10,         /* a HIP launch or query failed */
   MOE_ERR_INTERNAL = -11,    /* unexpected internal error */
-  MOE_ERR_OPTION = -12       /* a routing option is out of range (moe_route_opts) */
+  MOE_ERR_OPTION = -12,      /* a routing option is out of range (moe_route_opts) */
+  MOE_ERR_SCRATCH = -13      /* moe_layer_forward_noalloc: the call needs more than
+                                MOE_NOALLOC_SCRATCH_BYTES of workspace */
 } moe_status;
 
 typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
@@ -281,6 +283,30 @@ moe_status moe_layer_forward_ex(const void* x, moe_dtype dt, int32_t T, int32_t 
                                 int32_t k, const moe_route_opts* opts, const moe_weights* gate_up,
                                 const moe_weights* gate, const moe_weights* up, const moe_weights* down, void* y,
                                 uint32_t flags, const moe_taps* taps, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_layer_forward_ex without a workspace argument and without allocating:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES that
+ * each GPU the library runs on holds until the process ends; the call makes
+ * no hipMalloc, hipFree or other allocating call.  The caller still passes
+ * inputs, outputs and taps.  A call needing more workspace than the array
+ * (the layout of moe_layer_workspace_size, without the batched path's
+ * regions on the decode path and without the scale repacks when the
+ * weights carry packed_sb) returns MOE_ERR_SCRATCH with nothing enqueued:
+ * decode and batched decode fit; a 4096-token prefill does not.
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's contents (the layer needs none of it cleared): calls that
+ * overlap on one GPU (two streams, two threads) race and must be
+ * serialised by the caller.  Results are bit-identical to
+ * moe_layer_forward_ex with a caller workspace.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w,
+                                     int32_t E, int32_t k, const moe_route_opts* opts, const moe_weights* gate_up,
+                                     const moe_weights* gate, const moe_weights* up, const moe_weights* down,
+                                     void* y, uint32_t flags, const moe_taps* taps, void* stream);
 
 /*
  * Health figures of per-expert activation counts (page "Qwen3.5-MoE与Qwen3-MoE

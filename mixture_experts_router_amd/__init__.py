@@ -29,10 +29,13 @@ FLAG_UNFUSED, FLAG_FORCE_GEMV, FLAG_FORCE_MFMA = 0x1, 0x2, 0x4
 
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE", -4: "MOE_ERR_ALIGN",
           -5: "MOE_ERR_K", -6: "MOE_ERR_QUANT", -7: "MOE_ERR_INCOMPATIBLE", -8: "MOE_ERR_WORKSPACE",
-          -9: "MOE_ERR_DEVICE", -10: "MOE_ERR_HIP", -11: "MOE_ERR_INTERNAL", -12: "MOE_ERR_OPTION"}
+          -9: "MOE_ERR_DEVICE", -10: "MOE_ERR_HIP", -11: "MOE_ERR_INTERNAL", -12: "MOE_ERR_OPTION",
+          -13: "MOE_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_ex", "moe_topk_from_logits",
            "moe_topk_from_logits_ex", "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_ex",
+           "moe_layer_forward_noalloc",
            "moe_expert_load_stats", "moe_fuse_gate_up", "moe_packed_sb_bytes", "moe_pack_sb", "moe_status_string",
            "moe_debug_set_events",
            "moe_debug_last_plan", "moe_debug_set_tuning")
@@ -91,6 +94,10 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(CWeights), ctypes.POINTER(CWeights), ctypes.POINTER(CWeights),
                                        vp, u32, ctypes.POINTER(CTaps), vp, sz, vp]
     L.moe_layer_forward_ex.restype = i32
+    L.moe_layer_forward_noalloc.argtypes = [vp, i32, i32, i32, vp, i32, i32, ropt, ctypes.POINTER(CWeights),
+                                            ctypes.POINTER(CWeights), ctypes.POINTER(CWeights),
+                                            ctypes.POINTER(CWeights), vp, u32, ctypes.POINTER(CTaps), vp]
+    L.moe_layer_forward_noalloc.restype = i32
     L.moe_expert_load_stats.argtypes = [vp, i32, vp, vp, vp]
     L.moe_expert_load_stats.restype = i32
     L.moe_layer_workspace_size.argtypes = [i32, i32, i32, i32, i32, u32]
@@ -314,6 +321,30 @@ def layer_forward(x: torch.Tensor, router_w: torch.Tensor, k: int, down: Weights
         st = lib().moe_layer_forward_ex(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k, ctypes.byref(o),
                                         *wargs)
     _check(st, "moe_layer_forward")
+    return y
+
+
+def layer_forward_noalloc(x: torch.Tensor, router_w: torch.Tensor, k: int, down: Weights,
+                          gate_up: Optional[Weights] = None, gate: Optional[Weights] = None,
+                          up: Optional[Weights] = None, flags: int = 0, taps: Optional[dict] = None,
+                          out: Optional[torch.Tensor] = None, stream=None, health: Optional[torch.Tensor] = None,
+                          alpha: float = 0.0, groups: int = 0, capacity: int = 0) -> torch.Tensor:
+    """layer_forward through moe_layer_forward_noalloc: no workspace argument,
+    the library's per-device scratch array instead (calls on one GPU must not
+    overlap).  With `out` given, nothing is allocated."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    y = torch.empty_like(x) if out is None else out
+    ctaps = None
+    if taps:
+        ctaps = CTaps(*[(taps[n].data_ptr() if n in taps and taps[n] is not None else None) for n in TAP_NAMES])
+    ref = lambda w: ctypes.byref(w.c()) if w is not None else None
+    o = _opts(health, alpha, groups, capacity)
+    st = lib().moe_layer_forward_noalloc(_ptr(x), _dtype_code(x), T, H, _ptr(router_w), E, k,
+                                         ctypes.byref(o) if o is not None else None, ref(gate_up), ref(gate),
+                                         ref(up), ref(down), _ptr(y), flags,
+                                         ctypes.byref(ctaps) if ctaps is not None else None, _stream(stream))
+    _check(st, "moe_layer_forward_noalloc")
     return y
 
 

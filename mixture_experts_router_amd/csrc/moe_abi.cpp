@@ -91,6 +91,34 @@ moe_status device_props(DevProps* out) {
   return p.gfx950 ? MOE_OK : MOE_ERR_DEVICE;
 }
 
+// ---------------------------------------------------- scratch workspace --
+//
+// The workspace of moe_layer_forward_noalloc: a file-scope device array.  In
+// host code `scratch` names a host-side stand-in, not device memory, so the
+// device address is looked up once per device (with that device current)
+// and only that address is handed to kernels.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64];
+
+moe_status scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MOE_ERR_HIP;
+    }
+    if ((reinterpret_cast<uintptr_t>(p) & (kAlign - 1)) != 0) return MOE_ERR_INTERNAL;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
 // ----------------------------------------------------------- validation --
 
 moe_status check_weights(const moe_weights* w, int E, int N, int K) {
@@ -241,10 +269,14 @@ moe_status route_impl(const void* x, moe_dtype dt, int T, int H, const void* wr,
   return select_impl(logits, T, E, k, ro.gs, idx, w, k_used, entropy, scratch, st);
 }
 
+moe_status scratch_ptr(void** out);
+
+// use_scratch: the workspace is this device's file-scope scratch array (ws
+// and ws_bytes ignored); a call that needs more returns MOE_ERR_SCRATCH.
 moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* router_w, int E, int k,
                         const moe_route_opts* opts, const moe_weights* gate_up, const moe_weights* gate,
                         const moe_weights* up, const moe_weights* down, void* y, uint32_t flags,
-                        const moe_taps* taps, void* ws, size_t ws_bytes, hipStream_t st) {
+                        const moe_taps* taps, void* ws, size_t ws_bytes, hipStream_t st, bool use_scratch = false) {
   // ---- validation (host only)
   moe_status s = check_router(x, dt, T, H, router_w, E, k);
   if (s != MOE_OK) return s;
@@ -284,13 +316,18 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   const Layout L = layout(T, H, E, kcap, I, flags, nd);
   if (T == 0) return MOE_OK;
   if ((bits == 5 || bits == 6) && !gemv) return MOE_ERR_QUANT;  // 5- and 6-bit codes: decode path only
-  if (!ws) return MOE_ERR_WORKSPACE;
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_ERR_ALIGN;
+  if (use_scratch) {
+    if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  } else {
+    if (!ws) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return MOE_ERR_ALIGN;
+  }
 
   // ---- device
   DevProps props;
   if ((s = device_props(&props)) != MOE_OK) return s;
+  if (use_scratch && (s = scratch_ptr(&ws)) != MOE_OK) return s;
 
   uint8_t* W = (uint8_t*)ws;
   float* logits = (taps && taps->logits) ? taps->logits : (float*)(W + L.logits);
@@ -460,6 +497,9 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_HIP: return "a HIP call failed";
     case MOE_ERR_INTERNAL: return "internal error";
     case MOE_ERR_OPTION: return "a routing option is out of range";
+    case MOE_ERR_SCRATCH:
+      return "the call needs more workspace than the allocation-free entry point holds "
+             "(MOE_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -569,6 +609,18 @@ moe_status moe_layer_forward_ex(const void* x, moe_dtype dt, int32_t T, int32_t 
   try {
     return forward_impl(x, dt, T, H, router_w, E, k, opts, gate_up, gate, up, down, y, flags, taps, ws, ws_bytes,
                         (hipStream_t)stream);
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
+moe_status moe_layer_forward_noalloc(const void* x, moe_dtype dt, int32_t T, int32_t H, const void* router_w,
+                                     int32_t E, int32_t k, const moe_route_opts* opts, const moe_weights* gate_up,
+                                     const moe_weights* gate, const moe_weights* up, const moe_weights* down,
+                                     void* y, uint32_t flags, const moe_taps* taps, void* stream) {
+  try {
+    return forward_impl(x, dt, T, H, router_w, E, k, opts, gate_up, gate, up, down, y, flags, taps, nullptr, 0,
+                        (hipStream_t)stream, true);
   } catch (...) {
     return MOE_ERR_INTERNAL;
   }

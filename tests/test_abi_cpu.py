@@ -239,3 +239,31 @@ def test_load_stats_validation():
     assert st(L.moe_expert_load_stats(P, 257, P, P, None)) == "MOE_ERR_SHAPE"
     assert st(L.moe_expert_load_stats(None, 8, P, P, None)) == "MOE_ERR_NULL"
     assert st(L.moe_expert_load_stats(P, 8, P + 2, P, None)) == "MOE_ERR_ALIGN"
+
+
+def noalloc(T=4, H=256, E=8, k=2, I=128, x=P, wr=P, y=P, gu=None, down=None, bits=4, flags=0):
+    L = moe.lib()
+    gu = W(E, 2 * I, H, bits) if gu is None else gu
+    down = W(E, H, I, bits) if down is None else down
+    return L.moe_layer_forward_noalloc(x, moe.MOE_F16, T, H, wr, E, k, None, ctypes.byref(gu), None, None,
+                                       ctypes.byref(down), y, flags, None, None)
+
+
+def test_noalloc_validates_on_the_host():
+    # no workspace argument; the same checks as moe_layer_forward, all before any HIP call
+    assert noalloc(T=0) == 0
+    assert moe.STATUS[noalloc(x=None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[noalloc(k=9, E=16)] == "MOE_ERR_K"
+    assert moe.STATUS[noalloc(H=200)] == "MOE_ERR_SHAPE"
+
+
+def test_noalloc_refuses_calls_beyond_its_scratch():
+    # a 4096-token prefill (h, o and the fp16 operand alone are ~214 MB) does
+    # not fit the 64 MiB array: refused before the device is touched
+    st = noalloc(T=4096, H=4096, E=64, k=4, I=1408)
+    assert moe.STATUS[st] == "MOE_ERR_SCRATCH"
+    assert "MOE_NOALLOC_SCRATCH_BYTES" in moe.lib().moe_status_string(st).decode()
+    # a decode-sized call fits: it passes validation and stops at the device
+    # check here (no GPU in this process), never at the size check
+    st = noalloc(T=1, H=4096, E=64, k=4, I=11008)
+    assert moe.STATUS[st] != "MOE_ERR_SCRATCH"
