@@ -109,6 +109,20 @@ def algorithmic(name: str, kernel: str, *, T, H, E, I, bits, idx, k_used, kcap, 
     return float(b), f
 
 
+def layer_algorithmic(*, T, H, E, I, bits, idx, k_used, keep=None):
+    """Algorithmic HBM bytes and flops of one whole layer call: every touched
+    expert's gate_up and down weights (codes plus fp16 scale/bias) read once,
+    the router weights, x and y; flops 2 P (3 I H) + 2 T E H over the P
+    computed (token, slot) pairs."""
+    sel = idx[keep] if keep is not None else idx[:, :k_used]
+    touched = np.unique(sel).size
+    pairs = sel.size
+    b = touched * (2 * I * weight_bytes_per_row(H, bits) + H * weight_bytes_per_row(I, bits)) + E * H * 2 \
+        + 2 * T * H * 2
+    f = 2.0 * pairs * 3 * I * H + 2.0 * T * E * H
+    return float(b), f
+
+
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 counters, if the summary in
     profiles/ was taken on the current kernel source (matching hash)."""
@@ -145,6 +159,9 @@ def main():
                          "(activation counts of a Zipf-1.1 window, mean 1)")
     ap.add_argument("--groups", type=int, default=0, help="group-limited routing: at most one expert per group")
     ap.add_argument("--capacity", type=int, default=0, help="expert capacity: at most this many pairs per expert")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="also time the layer's kernels with a write of this many MiB between steps, which "
+                         "evicts the 256 MB Infinity Cache, so their weight bytes must come from HBM")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -288,6 +305,33 @@ def main():
     torch.cuda.synchronize()
     moe.debug_set_events(None)
 
+    flush = None
+    if args.flush_mib:
+        # ---- timed region 4: the layer's kernels, each step preceded by a
+        # write of flush_mib MiB (a fill kernel outside the events), so no
+        # weight byte of the previous steps is left in the Infinity Cache
+        buf = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
+        nf = min(K, 64)
+        fevents = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(nf)]
+        for evs in fevents:
+            for e in evs:
+                e.record(stream)
+        torch.cuda.synchronize()
+        for i in range(nf):
+            buf.fill_(i & 0xFF)
+            moe.debug_set_events(fevents[i])
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        moe.debug_set_events(None)
+        fk = np.zeros(nk)
+        for evs in fevents:
+            for j in range(nk):
+                fk[j] += evs[2 * j].elapsed_time(evs[2 * j + 1])
+        fk = fk / nf * 1e3
+        flush = {"mib": args.flush_mib, "steps": nf, "per_kernel_us": [round(float(v), 3) for v in fk],
+                 "kernel_sum_us": round(float(fk.sum()), 3)}
+        del buf
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 19  # fp16 elements
         src = torch.empty(n, dtype=torch.float16, device="cuda")
@@ -348,6 +392,32 @@ def main():
     # counters are taken without routing options: with options the traffic is unmeasured
     roof["traffic"] = None if lopt else traffic_from_profiles(kern, args.workload)
 
+    # ---- the whole layer against its roofline: all algorithmic bytes (or
+    # flops) of a step over the measured time per step
+    if wl["pool"]:
+        lb, lf = [], []
+        for s_ in range(min(wl["pool"], K)):
+            b_, f_ = layer_algorithmic(T=1, H=H, E=E, I=I, bits=bits, idx=idx_all[s_:s_ + 1], k_used=ku,
+                                       keep=capacity_keep(idx_all[s_:s_ + 1], ku, args.capacity)
+                                       if args.capacity else None)
+            lb.append(b_)
+            lf.append(f_)
+        lay_b, lay_f = float(np.mean(lb)), float(np.mean(lf))
+    else:
+        lay_b, lay_f = layer_algorithmic(T=T, H=H, E=E, I=I, bits=bits, idx=idx_all, k_used=ku,
+                                         keep=capacity_keep(idx_all, ku, args.capacity) if args.capacity else None)
+    step_s = ms_per_step * 1e-3
+    t_hbm = lay_b / (HBM_PEAK_GBS * 1e9)
+    t_mfma = lay_f / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        roof["layer"] = {"bound": "hbm", "achieved": round(lay_b / step_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(t_hbm / step_s, 4), "algorithmic_bytes": int(lay_b),
+                         "algorithmic_flops": int(lay_f), "roofline_us": round(t_hbm * 1e6, 2)}
+    else:
+        roof["layer"] = {"bound": "mfma", "achieved": round(lay_f / step_s / 1e12, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(t_mfma / step_s, 4), "algorithmic_bytes": int(lay_b),
+                         "algorithmic_flops": int(lay_f), "roofline_us": round(t_mfma * 1e6, 2)}
+
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -371,6 +441,12 @@ def main():
             t_run = run(n)
             cpu = {"value": round(n / t_run, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
                    "sample": "%d single tokens of the decode pool (each: route + 4 experts), %.1fs" % (n, t_run)}
+            oracle.set_threads(1)
+            n1 = max(2, n // max(cores, 1))
+            t1 = run(n1)
+            oracle.set_threads(cores)
+            cpu["value_1core"] = round(n1 / t1, 3)
+            cpu["sample_1core"] = "%d single tokens of the decode pool on 1 thread, %.1fs" % (n1, t1)
         else:
             idx_o, w_o, ku_o, _ = oracle.route(inp.x, inp.wr, inp.dtype, k, **oopt)
             rng = np.random.default_rng(0)
@@ -390,6 +466,18 @@ def main():
             cpu = {"value": round(T / total, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
                    "sample": "routing of all %d tokens (%.1fs) + expert FFN of %d sampled tokens (%.1fs), "
                              "scaled to the batch" % (T, t_route, n, t_tok)}
+            oracle.set_threads(1)
+            n1 = max(2, n // max(cores, 1))
+            t = time.perf_counter()
+            oracle.route(inp.x, inp.wr, inp.dtype, k, **oopt)
+            t_route1 = time.perf_counter() - t
+            t = time.perf_counter()
+            oracle.tokens_forward(inp.x, inp.dtype, toks[:n1], idx_o, w_o, ku_o, gu_np, inp.down)
+            t_tok1 = time.perf_counter() - t
+            oracle.set_threads(cores)
+            cpu["value_1core"] = round(T / (t_route1 + t_tok1 / n1 * T), 3)
+            cpu["sample_1core"] = "1 thread: routing of all %d tokens (%.1fs) + expert FFN of %d sampled tokens " \
+                                  "(%.1fs), scaled to the batch" % (T, t_route1, n1, t_tok1)
 
     out = {
         "metric": METRIC,
@@ -406,12 +494,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl["label"], "tokens_per_step": T, "hidden": H, "experts": E, "top_k": k,
                    "intermediate": I, "weight_bits": bits, "activations": inp.dtype,
+                   "arithmetic": "fp16 operands (dequantised weights, activations, SwiGLU rows), fp32 accumulation",
                    "launch": mode, "eager_tokens_per_s": round(K * T / eager_s, 2),
                    "graph_tokens_per_s": round(K * T / graph_s, 2) if graph_s else None,
                    "kernels_per_step": nk, "plan": plan,
                    "routing_options": {"load_aware_alpha": args.load_aware, "groups": args.groups,
                                        "capacity": args.capacity} if lopt else None,
-                   "per_kernel_us": [round(float(v), 3) for v in per_kernel_us]},
+                   "per_kernel_us": [round(float(v), 3) for v in per_kernel_us],
+                   "cache_flush": flush},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

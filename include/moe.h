@@ -96,11 +96,10 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
  *   bits == 6:  q      uint8 [rows, 3K/4], code k at bits 6k .. 6k+5 of the row
  *                      read as a little-endian bit stream (four codes per three
  *                      bytes); codes 0..63
- *               5 and 6 bits: decode path only, within its register layout
- *                      (5-bit: hidden <= 8192, inter <= 12288; 6-bit: hidden
- *                      <= 4096, inter <= 6144).  A layer that would take the
- *                      batched path (or MOE_FLAG_FORCE_MFMA) returns
- *                      MOE_ERR_QUANT, as does moe_pack_sb
+ *               5 and 6 bits (a reading: the oMLX page names these modes
+ *                      but gives no layout): both paths.  On the batched
+ *                      path 5-bit weights need hidden and inter multiples of
+ *                      128 (MOE_ERR_QUANT otherwise)
  *   bits == 8:  q      uint8 [rows, K], codes 0..255
  *   bits 4-8:   scales fp16 [rows, K/group_size], biases fp16 [rows, K/group_size];
  *               w[n, k] = scales[n, k/gs] * q[n, k] + biases[n, k/gs]
@@ -110,7 +109,7 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
  * group_size must be 64.  K must be a multiple of 64.  q, scales and biases
  * must be 16-byte aligned.
  *
- * packed_sb (optional, bits 4 and 8): the same scales and biases repacked for
+ * packed_sb (optional, bits 4 to 8): the same scales and biases repacked for
  * the batched path by moe_pack_sb, pointing at the tensor's (or view's) first
  * row like q.  Layout: for expert e, group pair p (groups 2p and 2p+1; a
  * missing last group is 0) and row n, 8 bytes {scale[2p], scale[2p+1],
@@ -119,8 +118,8 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
  * scales and biases as a few contiguous 128-byte lines instead of one line
  * per column.  NULL: the batched path repacks them into the workspace on every
  * call.  The gate and up views of a fused tensor share its packed_sb (the up
- * view's pointer is the gate view's plus inter*8 bytes).  Set for weights of
- * other widths, it is refused with MOE_ERR_QUANT.
+ * view's pointer is the gate view's plus inter*8 bytes).  Set for fp16
+ * weights, it is refused with MOE_ERR_QUANT.
  */
 typedef struct {
   const void* q;

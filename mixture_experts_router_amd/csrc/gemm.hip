@@ -95,19 +95,31 @@ int gemm_block_m(int P, int E) {
 int gemm_max_mtiles(int P, int E, int bm) { return (P + bm - 1) / bm + E; }
 
 // Geometry of one pipeline stage (KG quantisation groups of 64 k columns) of
-// a wave's 64 weight rows, stored row-major [64 rows][SEG bytes] in LDS: a
-// load instruction reads SEG contiguous bytes of each of RPI rows (DRAM
-// streams rows in segments of at least 64 bytes far better than in 32).
+// a wave's weight rows in LDS.  Each 32-row subtile is loaded by IPS whole
+// load instructions: instruction i of a subtile moves its 16-byte pieces
+// 64i .. 64i+63 in row-major (row, piece) order, so the subtile sits
+// row-major [32 rows][SEG bytes] at the start of its SUBB-byte region.  For
+// 4-, 8- and 16-bit codes a row is a power-of-two number of pieces and an
+// instruction covers whole rows (DRAM streams rows in segments of at least 64
+// bytes far better than in 32); 5- and 6-bit group rows are 40 and 48 bytes,
+// so rows straddle instructions and the last instruction of a subtile has
+// spare lanes, which re-read the subtile's first piece into the padding.  No
+// instruction spans two subtiles, whose rows may lie in different tensors
+// (gate and up).
 template <int BITS, int KG, int NSUB>
 struct BGeo {
-  static constexpr int ROW = 64 * BITS / 8;  // code bytes of one row per group: 32 / 64 / 128
-  static constexpr int SEG = KG * ROW;       // bytes of one row per stage
-  static constexpr int LPR = SEG / 16;       // 16-byte pieces per row
-  static constexpr int RPI = 64 / LPR;       // rows per 64-lane load instruction
-  static constexpr int ROWS = 32 * NSUB;     // weight rows (output columns) per wave
-  static constexpr int NI = ROWS / RPI;      // load instructions per wave
-  static constexpr int HALF = ROW / 2;       // bytes a lane feeds per group (its half of the group's k)
-  static constexpr int READS = HALF / 16;    // 16-byte LDS reads per lane, subtile and group
+  static constexpr int ROW = 64 * BITS / 8;          // code bytes of one row per group: 32 / 40 / 48 / 64 / 128
+  static constexpr int SEG = KG * ROW;               // bytes of one row per stage
+  static constexpr int LPR = SEG / 16;               // 16-byte pieces per row
+  static constexpr bool WHOLE = 64 % LPR == 0;       // an instruction covers whole rows
+  static constexpr int IPS = (32 * LPR + 63) / 64;   // load instructions per 32-row subtile
+  static constexpr int SUBB = IPS * 1024;            // LDS bytes per subtile (32 * SEG, then padding)
+  static constexpr int ROWS = 32 * NSUB;             // weight rows (output columns) per wave
+  static constexpr int NI = NSUB * IPS;              // load instructions per wave
+  static constexpr int WB = NSUB * SUBB;             // LDS bytes of a wave's weight rows
+  static constexpr int HALF = ROW / 2;               // bytes a lane feeds per group (its half of the group's k)
+  static constexpr int READS = HALF / 16;            // (4, 8, 16 bits) 16-byte LDS reads per lane, subtile, group
+  static_assert(SEG % 16 == 0, "a stage row is whole 16-byte pieces");
 };
 
 // WPC: workgroups per CU the LDS budget allows (1: 156 KB, 2: 78 KB each)
@@ -116,7 +128,7 @@ struct GemmCfg {
   static constexpr int BM = 32 * MS;
   static constexpr int A_SUB = BM * 128;  // A of one group: BM rows x 64 fp16
   static constexpr int A_BYTES = KG * A_SUB;
-  static constexpr int B_BYTES = 4 * BGeo<BITS, KG, NSUB>::ROWS * BGeo<BITS, KG, NSUB>::SEG;
+  static constexpr int B_BYTES = 4 * BGeo<BITS, KG, NSUB>::WB;
   // scales and biases: per column block one 1 KB region (one 64-lane load of
   // its 32*NSUB columns' packed group pair, repeated over the spare lanes)
   static constexpr int SC_BYTES = BITS != 16 ? 4 * 1024 : 0;
@@ -217,6 +229,42 @@ __device__ __forceinline__ f16x8 dequant_b(const u32x4* c, int j, uint32_t s_bit
     }
   }
 }
+
+// The same for 5- and 6-bit codes: w holds the lane's half of a group row,
+// 32 codes as a little-endian bit stream (code c at bits BITS*c); k-step j
+// takes codes 8j .. 8j+7 in natural order.  Each pair of codes becomes the
+// fp16 pair (1024 + q, 1024 + q') with exponent bits 0x6400, then
+// w = fp16(fma(q, s, b)) as for 8-bit codes.
+template <int BITS>
+__device__ __forceinline__ f16x8 dequant_b_odd(const uint32_t* w, int j, uint32_t s_bits, uint32_t b_bits) {
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  auto code = [&](int c) __attribute__((always_inline)) -> uint32_t {
+    const int bit = BITS * c, wd = bit >> 5, sh = bit & 31;
+    if (sh + BITS <= 32) return (w[wd] >> sh) & MASK;
+    return ((w[wd] >> sh) | (w[wd + 1] << (32 - sh))) & MASK;
+  };
+  const f16 s = __builtin_bit_cast(f16, (uint16_t)s_bits), b = __builtin_bit_cast(f16, (uint16_t)b_bits);
+  const f16x2 s2 = {s, s}, b2 = {b, b};
+  const f16x2 m1024 = {(f16)-1024.0f, (f16)-1024.0f};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t p = 0x64006400u | code(8 * j + 2 * i) | (code(8 * j + 2 * i + 1) << 16);
+    const f16x2 q = __builtin_bit_cast(f16x2, p) + m1024;
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
+  }
+  const u32x4 v = {o[0], o[1], o[2], o[3]};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+template <bool C, typename A, typename B>
+struct Pick {
+  typedef A T;
+};
+template <typename A, typename B>
+struct Pick<false, A, B> {
+  typedef B T;
+};
 
 template <int BITS, int MODE, int MS, int KG, int NSUB, int KS, int WPC>
 __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
@@ -368,14 +416,17 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
 #pragma unroll
   for (int qq = 0; qq < NQ; ++qq) {
     const int q = q0 + qq;
-    const int sub = (q * G::RPI) / 32;  // subtile of the whole instruction
+    const int sub = q / G::IPS;  // the instruction's subtile
     const uint8_t* base = qbase[0];
 #pragma unroll
     for (int ni = 1; ni < NSUB; ++ni) base = sub == ni ? qbase[ni] : base;
     rq[qq] = make_rsrc(base, 0xFFFFFFFFu);
-    const int rl = q * G::RPI + lane / G::LPR;
-    const int piece = (lane % G::LPR) ^ piece_swizzle<G::SEG>(rl);
-    b_off[qq] = (uint32_t)(column(rl / 32, rl % 32) * row_bytes) + (uint32_t)piece * 16u;
+    const int item = (q % G::IPS) * 64 + lane;  // (row, piece) of the subtile, row-major
+    const bool live = item < 32 * G::LPR;       // spare lanes re-read the first piece (into the padding)
+    const int r_in = live ? item / G::LPR : 0;
+    const int pl = live ? item % G::LPR : 0;
+    const int piece = G::WHOLE ? pl ^ piece_swizzle<G::SEG>(sub * 32 + r_in) : pl;
+    b_off[qq] = (uint32_t)(column(sub, r_in) * row_bytes) + (uint32_t)piece * 16u;
   }
   const int nst = ng / KG;  // pipeline steps (the launcher makes KG divide ng)
 
@@ -389,7 +440,7 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
 
   // this column block's scale region (both waves of a K split load it, alike)
   const int sc_wave = C::A_BYTES + C::B_BYTES + wn * 1024;
-  const int b_wave = C::A_BYTES + wn * G::ROWS * G::SEG;  // this wave's B codes
+  const int b_wave = C::A_BYTES + wn * G::WB;  // this wave's B codes
   const int last = nst - 1;
   // step k (groups KG k .. KG k + KG - 1; clamped to the last step) into stage S
   auto issue = [&](auto S_, int k) __attribute__((always_inline)) {
@@ -405,7 +456,7 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
       }
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
-      const int lds_off = C::A_BYTES + wn * G::ROWS * G::SEG + (q0 + qq) * 1024;
+      const int lds_off = C::A_BYTES + wn * G::WB + (q0 + qq) * 1024;
       dma16(rq[qq], b_off[qq], (uint32_t)k * G::SEG, st + lds_off);
     }
     if constexpr (BITS != 16) {
@@ -422,7 +473,15 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
   // k-steps) at byte kh*RB of the lane's half of the group.
   constexpr int RB = G::HALF / KS;
   constexpr int RT = RB >= 16 ? RB / 16 : 1;
-  typedef u32x4 Codes[NSUB][RT];
+  constexpr bool ODD = BITS == 5 || BITS == 6;  // 5- and 6-bit codes: 20 or 24 bytes per lane and group
+  static_assert(!ODD || KS == 1, "5- and 6-bit codes: one wave per column block");
+  struct CodesPow2 {
+    u32x4 v[NSUB][RT];
+  };
+  struct CodesOdd {
+    uint32_t w[NSUB][6];
+  };
+  typedef typename Pick<ODD, CodesOdd, CodesPow2>::T Codes;
   // kodd: odd step (one-group stages take the second group of the pair)
   auto read_codes = [&](const uint8_t* st, auto GI_, Codes& bc, uint32_t (&sv)[NSUB], uint32_t (&bv)[NSUB],
                         bool kodd) __attribute__((always_inline)) {
@@ -430,16 +489,31 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
 #pragma unroll
     for (int ni = 0; ni < NSUB; ++ni) {
       const int r = ni * 32 + col_in;
-      if constexpr (RB >= 16) {
+      if constexpr (ODD) {
+        // the lane's half of the group row: 20 bytes (five words) or 24 (three pairs)
+        const int at = b_wave + ni * G::SUBB + col_in * G::SEG + gi * G::ROW + hh * G::HALF;
+        if constexpr (BITS == 5) {
+#pragma unroll
+          for (int w = 0; w < 5; ++w) bc.w[ni][w] = *(const uint32_t*)(st + (at + 4 * w));
+          bc.w[ni][5] = 0u;
+        } else {
+#pragma unroll
+          for (int w = 0; w < 3; ++w) {
+            const u32x2 v = *(const u32x2*)(st + (at + 8 * w));
+            bc.w[ni][2 * w] = v.x;
+            bc.w[ni][2 * w + 1] = v.y;
+          }
+        }
+      } else if constexpr (RB >= 16) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
           const int piece = (gi * (G::ROW / 16) + hh * G::READS + kh * RT + t) ^ piece_swizzle<G::SEG>(r);
-          bc[ni][t] = *(const u32x4*)(st + (b_wave + r * G::SEG + piece * 16));
+          bc.v[ni][t] = *(const u32x4*)(st + (b_wave + r * G::SEG + piece * 16));
         }
       } else {  // 8 bytes inside one piece
         const int piece = (gi * (G::ROW / 16) + hh * G::READS) ^ piece_swizzle<G::SEG>(r);
         const u32x2 v = *(const u32x2*)(st + (b_wave + r * G::SEG + piece * 16 + kh * 8));
-        bc[ni][0] = u32x4{v.x, v.y, 0u, 0u};
+        bc.v[ni][0] = u32x4{v.x, v.y, 0u, 0u};
       }
       if constexpr (BITS != 16) {
         const u32x2 sb = *(const u32x2*)(st + (sc_wave + (ni * 16 + col_in / 2) * 16 + (col_in & 1) * 8));
@@ -470,7 +544,10 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
                  f16x8 (&bf)[NSUB]) __attribute__((always_inline)) {
     constexpr int jj = decltype(JJ_)::value;
 #pragma unroll
-    for (int ni = 0; ni < NSUB; ++ni) bf[ni] = dequant_b<BITS>(bc[ni], jj, sv[ni], bv[ni], qc);
+    for (int ni = 0; ni < NSUB; ++ni) {
+      if constexpr (ODD) bf[ni] = dequant_b_odd<BITS>(bc.w[ni], jj, sv[ni], bv[ni]);
+      else bf[ni] = dequant_b<BITS>(bc.v[ni], jj, sv[ni], bv[ni], qc);
+    }
   };
   auto mma = [&](const f16x8 (&af)[MS], const f16x8 (&bf)[NSUB], bool skip = false) __attribute__((always_inline)) {
 #pragma unroll
@@ -727,33 +804,49 @@ static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
   const int64_t total = (int64_t)prm.n_tiles * prm.m_tiles;
   prm.per_xcd = (int)((total + NUM_XCD - 1) / NUM_XCD);
   dim3 grid((unsigned)(prm.per_xcd * NUM_XCD));
-  // two-group stages: 4-bit rows, or 8-bit rows with the whole LDS
-  if constexpr (BITS == 4 || (BITS == 8 && WPC == 1 && NSUB == 2 && MS < 4 && KS == 1)) {
-    if ((prm.K / 64) % 2 == 0 && tuning(TUNE_GEMM_KG) != 1)
-      return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
+  // 5-bit rows: two-group stages (80 bytes, five whole pieces; the caller
+  // makes K a multiple of 128); 6-bit rows: one group (48 bytes)
+  if constexpr (BITS == 5) {
+    return launch_kernel(gemm_kernel<5, MODE, MS, 2, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
+  } else {
+    // two-group stages: 4-bit rows, or 8-bit rows with the whole LDS
+    if constexpr (BITS == 4 || (BITS == 8 && WPC == 1 && NSUB == 2 && MS < 4 && KS == 1)) {
+      if ((prm.K / 64) % 2 == 0 && tuning(TUNE_GEMM_KG) != 1)
+        return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
+    }
+    return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
   }
-  return launch_kernel(gemm_kernel<BITS, MODE, MS, 1, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
 }
 
 // Row tiles of 64 and 128 run four waves, one per column block, or with the
 // tuning knob eight, two per column block splitting each group's k-steps.
 template <int BITS, int MODE, int MS>
 static hipError_t launch_one(const GemmParams& prm, hipStream_t st) {
-  // fp16 rows: two stages of four subtiles would not fit in LDS
-  if constexpr (MS == 4 && BITS != 16) {
-    if (tuning(TUNE_GEMM_NSUB) == 4) return launch_sub<BITS, MODE, MS, 4, 1, 1>(prm, st);
+  // 5- and 6-bit codes: four waves of two subtiles; 5-bit stages (80-byte row
+  // segments) leave room for one workgroup per CU, 6-bit ones for two at 32-
+  // and 64-row tiles
+  if constexpr (BITS == 5) {
+    return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
+  } else if constexpr (BITS == 6) {
+    if constexpr (MS < 4) return launch_sub<BITS, MODE, MS, 2, 1, 2>(prm, st);
+    else return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
+  } else {
+    // fp16 rows: two stages of four subtiles would not fit in LDS
+    if constexpr (MS == 4 && BITS != 16) {
+      if (tuning(TUNE_GEMM_NSUB) == 4) return launch_sub<BITS, MODE, MS, 4, 1, 1>(prm, st);
+    }
+    if constexpr (MS >= 2) {
+      if (tuning(TUNE_GEMM_KSPLIT) == 2) return launch_sub<BITS, MODE, MS, 2, 2, 1>(prm, st);
+    }
+    if constexpr (MS < 4) {
+      // 8-bit weights at 32-row tiles: one workgroup per CU streaming two-group
+      // (128-byte) row segments measured faster than two with one-group stages
+      const int wpc = tuning(TUNE_GEMM_WPC);
+      if (wpc == 1 || (wpc != 2 && MS == 1 && BITS == 8)) return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
+      return launch_sub<BITS, MODE, MS, 2, 1, 2>(prm, st);
+    }
+    return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
   }
-  if constexpr (MS >= 2) {
-    if (tuning(TUNE_GEMM_KSPLIT) == 2) return launch_sub<BITS, MODE, MS, 2, 2, 1>(prm, st);
-  }
-  if constexpr (MS < 4) {
-    // 8-bit weights at 32-row tiles: one workgroup per CU streaming two-group
-    // (128-byte) row segments measured faster than two with one-group stages
-    const int wpc = tuning(TUNE_GEMM_WPC);
-    if (wpc == 1 || (wpc != 2 && MS == 1 && BITS == 8)) return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
-    return launch_sub<BITS, MODE, MS, 2, 1, 2>(prm, st);
-  }
-  return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
 }
 
 template <int BITS, int MODE>
@@ -810,6 +903,11 @@ hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const i
   if (a_rows * K * 2 > 0x7FFFFFFFll || w0.stride * (int64_t)K * bits / 8 > 0xFFFFFFFFll) return hipErrorInvalidValue;
   prm.m_tiles = max_mtiles;
   if (bits == 4) return launch_bits<4>(mode, bm, prm, st);
+  if (bits == 5) {
+    if ((K / 64) % 2 != 0) return hipErrorInvalidValue;  // two-group stages
+    return launch_bits<5>(mode, bm, prm, st);
+  }
+  if (bits == 6) return launch_bits<6>(mode, bm, prm, st);
   if (bits == 8) return launch_bits<8>(mode, bm, prm, st);
   return launch_bits<16>(mode, bm, prm, st);
 }

@@ -548,9 +548,10 @@ __device__ __forceinline__ void load_down_row(DownBuf<BITS, DCPL>& buf, const Ge
 }
 
 // KS waves share a slot: wave ks owns lane chunks i in [ks*DC, (ks+1)*DC)
-// of every row (DC chunks per lane), halving the registers a long row needs.
+// of every row (DC chunks per lane), dividing the registers a long row needs
+// by KS.
 template <int BITS, int DC, int KS>
-__global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
+__global__ __launch_bounds__(KS == 4 ? 1024 : 512) void gemv_down_kernel(GemvDownParams prm) {
   using C = Chunk<BITS>;
   __shared__ float part[MOE_MAX_K_DEV][KS][DOWN_MAX_ROWS];
   const int t = blockIdx.y;
@@ -705,7 +706,13 @@ __global__ __launch_bounds__(512) void gemv_down_kernel(GemvDownParams prm) {
   }
 }
 
-int gemv_down_max_chunks_per_lane() { return 6; }
+// Rows of up to 6 chunks per lane run with one wave per slot, or (at most 4
+// slots per token) two waves of up to 3 chunks; rows of 7 to 12 chunks per
+// lane need four waves of up to 3 chunks, so at most 4 slots per token.
+bool gemv_down_fits(int I, int bits, int kcap) {
+  const int dcpl = gemv_lanes_chunks(I, bits);
+  return dcpl <= 6 || (dcpl <= 12 && kcap <= 4);
+}
 
 hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_static, int kcap, int T, int H, int I,
                             int bits, WView wd, void* y, int act, int num_cu, hipStream_t st, int capacity) {
@@ -722,8 +729,10 @@ hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_sta
   prm.y = y;
   prm.act = act;
   const int dcpl = gemv_lanes_chunks(I, bits);
-  const int ks = dcpl >= 4 && kcap <= 4 ? 2 : 1;  // waves per slot (block of at most 512 threads)
-  const int dc = (dcpl + ks - 1) / ks;          // chunks per lane per wave
+  if (!gemv_down_fits(I, bits, kcap)) return hipErrorInvalidValue;
+  // waves per slot (blocks of at most 512 threads, 1024 with four waves per slot)
+  const int ks = dcpl > 6 ? 4 : (dcpl >= 4 && kcap <= 4 ? 2 : 1);
+  const int dc = (dcpl + ks - 1) / ks;  // chunks per lane per wave
   // rows per workgroup so that about `waves_per_cu` waves per CU are resident
   const int64_t want = (int64_t)(num_cu > 0 ? num_cu : 256) * tuning(TUNE_DOWN_WAVES_PER_CU);
   int64_t groups = want / ((int64_t)T * kcap * ks);
@@ -737,7 +746,8 @@ hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_sta
   dim3 block(64 * kcap * ks);
 #define X(B, D, K) \
   if (bits == B && dc == D && ks == K) launch_kernel(gemv_down_kernel<B, D, K>, grid, block, 0, st, prm); else
-#define CASES(B) X(B, 1, 1) X(B, 2, 1) X(B, 3, 1) X(B, 4, 1) X(B, 5, 1) X(B, 6, 1) X(B, 2, 2) X(B, 3, 2)
+#define CASES(B) \
+  X(B, 1, 1) X(B, 2, 1) X(B, 3, 1) X(B, 4, 1) X(B, 5, 1) X(B, 6, 1) X(B, 2, 2) X(B, 3, 2) X(B, 2, 4) X(B, 3, 4)
   CASES(4) CASES(5) CASES(6) CASES(8) CASES(16) return hipErrorInvalidValue;
 #undef CASES
 #undef X

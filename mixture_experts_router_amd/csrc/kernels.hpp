@@ -94,8 +94,9 @@ struct GemvRoute {
 hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_static, int kcap, int T, int H,
                           int N, int bits, bool fused, WView w0, WView w1, uint16_t* h, float* out32, int num_cu,
                           hipStream_t st, float* pre = nullptr);
-// largest 16-byte chunks per lane of a down row the decode kernels handle
-int gemv_down_max_chunks_per_lane();
+// whether the decode down kernels take rows of I weights of `bits` bits with
+// kcap slots per token
+bool gemv_down_fits(int I, int bits, int kcap);
 // y[t, m] = act(sum_s w[t,s] * (Wd[e_s, m, :] . h[t*kcap+s, :]));
 // capacity > 0: a pair beyond the first `capacity` pairs of its expert (pair
 // order) is left out of y (needs route.logits NULL: the selection is read)

@@ -134,7 +134,7 @@ moe_status check_weights(const moe_weights* w, int E, int N, int K) {
   if (w->K % 64 != 0 || w->expert_stride_rows < w->N) return MOE_ERR_SHAPE;
   if (!aligned16(w->q)) return MOE_ERR_ALIGN;
   if (w->bits != 16 && (!aligned16(w->scales) || !aligned16(w->biases))) return MOE_ERR_ALIGN;
-  if (w->packed_sb && w->bits != 4 && w->bits != 8) return MOE_ERR_QUANT;  // packed_sb: 4- and 8-bit weights only
+  if (w->packed_sb && w->bits == 16) return MOE_ERR_QUANT;  // packed_sb: quantised weights only
   if (w->packed_sb && !aligned16(w->packed_sb)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
@@ -305,8 +305,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   const int bits = down->bits;
   const int kcap = kcap_of(k);
   const int64_t P = (int64_t)T * kcap;
-  const bool gemv_fits = moe::gemv_lanes_chunks(H, bits) <= 4 &&
-                         moe::gemv_lanes_chunks(I, bits) <= moe::gemv_down_max_chunks_per_lane();
+  const bool gemv_fits = moe::gemv_lanes_chunks(H, bits) <= 4 && moe::gemv_down_fits(I, bits, kcap);
   bool gemv = false;
   if (!(flags & MOE_FLAG_FORCE_MFMA)) gemv = gemv_fits && ((flags & MOE_FLAG_FORCE_GEMV) || P <= kGemvMaxPairs);
   Needs nd;
@@ -315,7 +314,8 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   nd.sb_d = bits != 16 && !down->packed_sb;
   const Layout L = layout(T, H, E, kcap, I, flags, nd);
   if (T == 0) return MOE_OK;
-  if ((bits == 5 || bits == 6) && !gemv) return MOE_ERR_QUANT;  // 5- and 6-bit codes: decode path only
+  // 5-bit rows on the batched path: two-group (80-byte) stages of both GEMMs
+  if (bits == 5 && !gemv && (H % 128 != 0 || I % 128 != 0)) return MOE_ERR_QUANT;
   if (use_scratch) {
     if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
   } else {
@@ -654,7 +654,7 @@ size_t moe_packed_sb_bytes(int32_t E, int64_t expert_stride_rows, int32_t K) {
 
 moe_status moe_pack_sb(const moe_weights* w, void* out, void* stream) {
   if (!w || !out) return MOE_ERR_NULL;
-  if (w->bits != 4 && w->bits != 8) return MOE_ERR_QUANT;  // packed_sb serves the batched path (4 and 8 bits)
+  if (w->bits == 16) return MOE_ERR_QUANT;  // packed_sb holds scales and biases
   moe_status s = check_weights(w, w->E, w->N, w->K);
   if (s != MOE_OK) return s;
   if (!aligned16(out)) return MOE_ERR_ALIGN;

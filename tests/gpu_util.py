@@ -59,6 +59,12 @@ class Dev:
         return y
 
 
+def batched_path_takes(inp: mi.LayerInputs) -> bool:
+    """Whether the batched (MFMA) path takes these weights: every width, with
+    hidden and inter multiples of 128 for 5-bit codes (two-group stages)."""
+    return inp.bits != 5 or (inp.H % 128 == 0 and inp.I % 128 == 0)
+
+
 def boundary_gap(logits_row: np.ndarray, k: int) -> float:
     s = np.sort(logits_row.astype(np.float64))[::-1]
     return float(s[k - 1] - s[k]) if k < s.size else np.inf

@@ -99,9 +99,13 @@ def test_zero_tokens_is_a_noop():
     (dict(down=W(8, 256, 128, bits=16)), "MOE_ERR_QUANT"),
     (dict(gu=W(8, 2 * 128, 256, sb=P + 8)), "MOE_ERR_ALIGN"),
     (dict(down=W(8, 256, 128, sb=P + 4)), "MOE_ERR_ALIGN"),
-    # packed_sb serves the batched path's 4- and 8-bit weights only
-    (dict(gu=W(8, 2 * 128, 256, bits=6, sb=P), down=W(8, 256, 128, bits=6), bits=6), "MOE_ERR_QUANT"),
-    (dict(down=W(8, 256, 128, bits=5, sb=P), bits=5), "MOE_ERR_QUANT"),
+    # packed_sb holds scales and biases: quantised weights only
+    (dict(gu=W(8, 2 * 128, 256, bits=16, sb=P), down=W(8, 256, 128, bits=16), bits=16), "MOE_ERR_QUANT"),
+    # 5-bit codes on the batched path: hidden and inter multiples of 128
+    (dict(I=192, gu=W(8, 2 * 192, 256, bits=5), down=W(8, 256, 192, bits=5), bits=5,
+          flags=moe.FLAG_FORCE_MFMA), "MOE_ERR_QUANT"),
+    (dict(H=320, gu=W(8, 2 * 128, 320, bits=5), down=W(8, 320, 128, bits=5), bits=5,
+          flags=moe.FLAG_FORCE_MFMA), "MOE_ERR_QUANT"),
 ])
 def test_validation_errors(kw, status):
     assert moe.STATUS[fwd(**kw)] == status

@@ -103,8 +103,25 @@ def test_batched_decode_full_size():
 
 
 def test_prefill_full_size():
-    inp, gu_np, dev = _gen("prefill")
+    _prefill_full_size(*_gen("prefill"), "prefill")
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+def test_prefill_full_size_5_and_6_bit(bits):
+    # the prefill shape with 5- and 6-bit codes on the batched path (40- and
+    # 48-byte group rows staged through LDS)
+    _prefill_full_size(*_gen("prefill", bits=bits), "prefill %d-bit" % bits)
+
+
+def test_decode_b1_full_size_6_bit_inter_11008():
+    # the decode shape itself with 6-bit codes: 11 chunks per lane in a down
+    # row, four waves per slot
+    _decode_one_token_calls(*_gen("decode_b1", T=3, bits=6), "decode_b1 6-bit I 11008")
+
+
+def _prefill_full_size(inp, gu_np, dev, label):
     y, taps, plan = _forward(dev)
+    assert "gemm_gate_up_swiglu" in plan, plan
     counts = taps["counts"]
     _say("plan", plan, "hot expert %d tokens, mean %.1f" % (counts.max(), counts.mean()))
     assert counts.max() >= 10 * counts.mean()
@@ -114,7 +131,7 @@ def test_prefill_full_size():
     rng = np.random.default_rng(0)
     tokens = np.unique(np.concatenate([np.arange(4), hot_tokens[:6], hot_tokens[-4:],
                                        rng.choice(inp.T, 14, replace=False), [inp.T - 1]]))
-    _check(inp, gu_np, y, taps, tokens, "prefill")
+    _check(inp, gu_np, y, taps, tokens, label)
     y_u, _, _ = _forward(dev, moe.FLAG_UNFUSED)
     assert np.array_equal(y, y_u)
     _assert_packed_same(dev, y)

@@ -12,8 +12,8 @@ import torch
 import mixture_experts_router_amd as moe
 import moe_inputs as mi
 import oracle
-from gpu_util import (Dev, assert_within_tolerance, check_routing_identical_logits, dev_half, host_bits,
-                      reference_outputs)
+from gpu_util import (Dev, assert_within_tolerance, batched_path_takes, check_routing_identical_logits, dev_half,
+                      host_bits, reference_outputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,16 @@ CASES = {
     "decode_q5_bf16": ("decode_b1", dict(T=2, H=512, E=8, I=320, bits=5, dtype="bf16")),
     # entropy-adaptive k on the decode path (kcap 3, 12 pairs)
     "entropy_q6": ("entropy", dict(T=4, H=512, E=16, I=192, bits=6, segment=2)),
+    # 5- and 6-bit codes on the batched path: 64-row tiles (5-bit two-group
+    # stages, 6-bit one-group stages with an odd group count), 32-row tiles,
+    # 128-row tiles, and bf16 activations
+    "batched_q5": ("prefill", dict(T=300, H=512, E=16, I=256, bits=5)),
+    "batched_q6": ("prefill", dict(T=300, H=512, E=16, I=320, bits=6)),
+    "batched_q5_bm32": ("batched_decode", dict(T=40, H=512, E=8, I=256, bits=5)),
+    "batched_q6_bm32": ("batched_decode", dict(T=40, H=384, E=8, I=192, bits=6)),
+    "prefill_q5_bm128": ("prefill", dict(T=2304, H=256, E=8, I=384, bits=5)),
+    "prefill_q6_bm128": ("prefill", dict(T=2304, H=256, E=8, I=384, bits=6)),
+    "entropy_q5": ("entropy", dict(T=96, H=512, E=16, I=256, bits=5, segment=2)),
 }
 
 
@@ -80,9 +90,7 @@ def _run(dev, flags, fused_tensor=True):
 
 def _paths(inp):
     P = inp.T * inp.kcap
-    if inp.bits in (5, 6):  # the batched path takes 4-, 8- and 16-bit weights only
-        return [("gemv", moe.FLAG_FORCE_GEMV)]
-    paths = [("mfma", moe.FLAG_FORCE_MFMA)]
+    paths = [("mfma", moe.FLAG_FORCE_MFMA)] if batched_path_takes(inp) else []
     if P <= 128:
         paths.append(("gemv", moe.FLAG_FORCE_GEMV))
     return paths
@@ -196,7 +204,8 @@ def _packed_reference(w):
     return out
 
 
-@pytest.mark.parametrize("name", ["prefill_small", "tiny_q8_bf16", "ragged_shapes", "entropy_q4"])
+@pytest.mark.parametrize("name", ["prefill_small", "tiny_q8_bf16", "ragged_shapes", "entropy_q4", "batched_q5",
+                                  "batched_q6"])
 def test_packed_sb_layout_and_bit_identity(name, built):
     inp, gu_np, dev = built(name)
     down = moe.pack_sb(dev.down)
@@ -215,24 +224,42 @@ def test_packed_sb_layout_and_bit_identity(name, built):
         assert np.array_equal(host_bits(y1), y0), flags
 
 
-@pytest.mark.parametrize("name", ["decode_q5", "decode_q6"])
-def test_five_and_six_bit_weights_refused_on_the_batched_path(name, built):
-    inp, _, dev = built(name)
+def test_five_bit_batched_path_needs_multiples_of_128(built):
+    # two-group (80-byte) stages: inter 704 is 11 groups
+    inp, _, dev = built("decode_q5")
     with pytest.raises(moe.MoeError) as e:
         dev.forward(flags=moe.FLAG_FORCE_MFMA)
     assert e.value.name == "MOE_ERR_QUANT"
+    # 5-bit rows longer than the decode kernels take, and 8256 columns: refused
+    inp = mi.make_inputs("decode_b1", T=1, H=8256, E=4, k=2, I=128, bits=5)
     with pytest.raises(moe.MoeError) as e:
-        moe.pack_sb(dev.down)
+        Dev(inp).forward(flags=moe.FLAG_FORCE_GEMV)
     assert e.value.name == "MOE_ERR_QUANT"
 
 
-@pytest.mark.parametrize("bits,H,I", [(6, 8192, 128), (6, 256, 6208), (5, 256, 12352)])
-def test_five_and_six_bit_rows_beyond_the_decode_layout_are_refused(bits, H, I):
-    inp = mi.make_inputs("decode_b1", T=1, H=H, E=4, k=2, I=I, bits=bits)
+@pytest.mark.parametrize("bits,H,I,k,plan", [
+    (6, 8192, 128, 2, "gemm_gate_up_swiglu"),     # hidden beyond the decode layout: the batched path
+    (5, 8320, 256, 2, "gemm_gate_up_swiglu"),
+    (6, 256, 6208, 2, "gemv_down_combine"),       # down rows of 7 chunks per lane: four waves per slot
+    (5, 256, 12352, 4, "gemv_down_combine"),
+    (6, 1024, 11008, 4, "gemv_down_combine"),     # the decode shape's inter with 6-bit codes
+    (8, 512, 11008, 4, "gemv_down_combine"),
+])
+def test_long_rows_take_the_path_that_holds_them(bits, H, I, k, plan):
+    inp = mi.make_inputs("decode_b1", T=1, H=H, E=4 if k == 2 else 8, k=k, I=I, bits=bits)
+    print("case bits=%d H=%d I=%d k=%d" % (bits, H, I, k), flush=True)
     dev = Dev(inp)
-    with pytest.raises(moe.MoeError) as e:
-        dev.forward(flags=moe.FLAG_FORCE_GEMV)
-    assert e.value.name == "MOE_ERR_QUANT"
+    gu_np = oracle.fuse_gate_up(inp.gate, inp.up)
+    taps = moe.make_taps(inp.T, inp.E, inp.k, inp.I, "cuda")
+    y = host_bits(dev.forward(taps=taps))
+    assert plan in moe.last_plan()
+    t = {n: v.cpu().numpy() for n, v in taps.items()}
+    ku = int(t["k_used"][0])
+    check_routing_identical_logits(t["logits"], t["topk_idx"], t["topk_w"], ku)
+    ref, flips = reference_outputs(inp, gu_np, np.arange(inp.T), t["topk_idx"], t["topk_w"], ku)
+    assert_within_tolerance(y, ref, inp.dtype, "bits %d H %d I %d" % (bits, H, I))
+    y_u = host_bits(dev.forward(flags=moe.FLAG_UNFUSED))
+    assert np.array_equal(y, y_u)
 
 
 def test_runs_are_deterministic(built):

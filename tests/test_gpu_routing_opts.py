@@ -15,7 +15,7 @@ import torch
 import mixture_experts_router_amd as moe
 import moe_inputs as mi
 import oracle
-from gpu_util import Dev, assert_within_tolerance, dev_half, host_bits
+from gpu_util import Dev, assert_within_tolerance, batched_path_takes, dev_half, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -86,13 +86,15 @@ LAYER_CASES = {
     "entropy_q4": ("entropy", dict(T=96, H=512, E=16, I=192, bits=4, segment=2), 4),
     "decode_q5": ("decode_b1", dict(T=3, H=512, E=16, I=320, bits=5), 4),
     "decode_q6": ("decode_b1", dict(T=2, H=1024, E=16, I=704, bits=6), 4),
+    "batched_q5": ("prefill", dict(T=200, H=512, E=16, I=256, bits=5), 4),
 }
 
 
 def _option_paths(inp):
-    """Both paths where the weights allow (5- and 6-bit codes: decode only)."""
+    """Both paths where the weights allow (5-bit codes on the batched path:
+    hidden and inter multiples of 128)."""
     P = inp.T * inp.kcap
-    paths = [] if inp.bits in (5, 6) else [("mfma", moe.FLAG_FORCE_MFMA)]
+    paths = [("mfma", moe.FLAG_FORCE_MFMA)] if batched_path_takes(inp) else []
     return paths + ([("gemv", moe.FLAG_FORCE_GEMV)] if P <= 128 else [])
 
 
