@@ -38,6 +38,15 @@
  *     enqueued; an error return means nothing was enqueued.  Validation makes
  *     no HIP call, so it can be exercised without a GPU.
  *   - Layouts are row-major.  Activations and router weights share one dtype.
+ *   - Arithmetic: the expert projections run on fp16 operands (dequantised
+ *     weights, activations, SwiGLU rows) with fp32 accumulation; routing and
+ *     the combine are fp32.  bf16 activations keep bf16's range: token t is
+ *     converted as x * 2^-a_t, a_t >= 0 the smallest exponent with
+ *     max|x_t| * 2^-a_t < 64 (exact while the scaled values stay in fp16's
+ *     normal range; a_t = 0 whenever max|x_t| < 64), its gate and up sums
+ *     are scaled back by 2^a_t, its SwiGLU rows and down outputs are staged
+ *     at 2^-2a_t and y is scaled back by 2^2a_t.  Only values beyond the
+ *     output dtype's range become infinite.
  *   - T == 0 is a no-op returning MOE_OK; buffers whose size is proportional
  *     to T (activations, outputs, routing results) may then be NULL.
  *   - Calls on different streams are independent; the library keeps no
@@ -147,7 +156,8 @@ typedef struct {
  *   perm       int32 [T*kcap]       pair ids t*kcap+s grouped by expert, ascending
  *                                   within an expert; entries past the last pair -1
  *   h          fp16  [T*kcap, inter] SwiGLU output of pair t*kcap+s (unused slots
- *                                   untouched)
+ *                                   untouched), times 2^-2a_t for bf16
+ *                                   activations (see Arithmetic above)
  *   gate_up_preact fp32 [T*kcap, 2*inter] the gate+up projection of pair
  *                                   t*kcap+s before SwiGLU: g in columns
  *                                   [0, inter), u in [inter, 2*inter), the

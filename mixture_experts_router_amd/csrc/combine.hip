@@ -14,7 +14,8 @@ namespace moe {
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o, const int32_t* __restrict__ pos,
                                                       const float* __restrict__ wts,
                                                       const int32_t* __restrict__ k_used, int k_static, int kcap,
-                                                      int H, void* __restrict__ y, int act) {
+                                                      int H, void* __restrict__ y, int act,
+                                                      const int32_t* __restrict__ tokexp) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (c >= H) return;
@@ -36,6 +37,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       acc[2 * i + 1] = acc[2 * i + 1] + hi;
     }
   }
+  if (tokexp) {  // o was staged at 2^-2a_t (exact scaling back)
+    const int e2 = 2 * tokexp[t];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = ldexp_f(acc[i], e2);
+  }
   u32x4 out;
   uint32_t* ow = (uint32_t*)&out;
 #pragma unroll
@@ -45,46 +51,72 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }
 
 hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wts, const int32_t* k_used_dev,
-                          int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st) {
+                          int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st,
+                          const int32_t* tokexp) {
   dim3 grid((H / 8 + 255) / 256, T);
-  launch_kernel(combine_kernel, grid, 256, 0, st, o, pos, wts, k_used_dev, k_static, kcap, H, y, act);
+  launch_kernel(combine_kernel, grid, 256, 0, st, o, pos, wts, k_used_dev, k_static, kcap, H, y, act, tokexp);
   return hipGetLastError();
 }
 
-// h = silu(g) * u; with perm8 set, each 8-element block of h is stored in
-// 4-bit unpack order (the operand order of the batched 4-bit down GEMM).
+// h = 2^-2a silu(g) * u (a: the row's token exponent, 0 without tokexp);
+// with perm8 set, each 8-element block of h is stored in 4-bit unpack order
+// (the operand order of the batched 4-bit down GEMM).
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g, const float* __restrict__ u,
-                                                     uint16_t* __restrict__ h, int64_t n, int perm8) {
+                                                     uint16_t* __restrict__ h, int64_t n, int I, int perm8,
+                                                     const int32_t* __restrict__ tokexp,
+                                                     const int32_t* __restrict__ perm, int kcap) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   const int64_t at = perm8 ? (i & ~(int64_t)7) + perm8_slot((int)(i & 7)) : i;
-  h[at] = f32_to_f16_bits(swiglu(g[i], u[i]));
+  float hv = swiglu(g[i], u[i]);
+  if (tokexp) {
+    const int64_t row = i / I;
+    const int64_t pair = perm ? perm[row] : row;  // perm is -1 past the sorted pairs (rows never read)
+    if (pair >= 0) hv = ldexp_f(hv, -2 * tokexp[pair / kcap]);
+  }
+  h[at] = f32_to_f16_bits(hv);
 }
 
 hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, bool perm8,
-                         hipStream_t st) {
+                         hipStream_t st, const int32_t* tokexp, const int32_t* perm, int kcap) {
   const int64_t n = rows * I;
-  launch_kernel(swiglu_kernel, (unsigned)((n + 255) / 256), 256, 0, st, g, u, h, n, perm8 ? 1 : 0);
+  launch_kernel(swiglu_kernel, (unsigned)((n + 255) / 256), 256, 0, st, g, u, h, n, I, perm8 ? 1 : 0, tokexp, perm,
+                kcap);
   return hipGetLastError();
 }
 
 // Activation operand of the batched GEMM: x (fp16 or bf16) -> fp16, each
-// 8-element block optionally in 4-bit unpack order.  bf16 -> fp16 is exact
-// for values in fp16's normal range.
+// 8-element block optionally in 4-bit unpack order.  One workgroup per token:
+// bf16 rows are converted as x * 2^-a_t (common.hpp; exact) and a_t is
+// written to tokexp[t]; fp16 rows are copied.
 __global__ __launch_bounds__(256) void prep_a_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ a,
-                                                     int64_t n8, int act, int perm8) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  u32x4 v = act8_to_f16(load16(x + 8 * i), act);
-  if (perm8) v = perm8_nibble_order(v);
-  *(u32x4*)(a + 8 * i) = v;
+                                                     int H, int act, int perm8, int32_t* __restrict__ tokexp) {
+  __shared__ uint32_t wmax[4];
+  const int64_t t = blockIdx.x;
+  const uint16_t* xr = x + t * H;
+  uint16_t* ar = a + t * H;
+  int e = 0;
+  if (act == ACT_BF16) {
+    uint32_t m = 0;
+    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) m = max(m, bf16x8_absmax_bits(load16(xr + c)));
+    m = wave_max_u32(m);
+    if (lane_id() == 0) wmax[threadIdx.x / WAVE] = m;
+    __syncthreads();
+    e = bf16_token_exp(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+    if (threadIdx.x == 0) tokexp[t] = e;
+  }
+  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    u32x4 v = act8_to_f16_scaled(load16(xr + c), act, e);
+    if (perm8) v = perm8_nibble_order(v);
+    *(u32x4*)(ar + c) = v;
+  }
 }
 
-hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, bool perm8, hipStream_t st) {
-  const int64_t n8 = T * H / 8;
-  if (n8 <= 0) return hipSuccess;
-  launch_kernel(prep_a_kernel, (unsigned)((n8 + 255) / 256), 256, 0, st, (const uint16_t*)x, a, n8, act,
-                perm8 ? 1 : 0);
+hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, bool perm8, int32_t* tokexp,
+                         hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (act == ACT_BF16 && !tokexp) return hipErrorInvalidValue;
+  launch_kernel(prep_a_kernel, (unsigned)T, 256, 0, st, (const uint16_t*)x, a, H, act, perm8 ? 1 : 0, tokexp);
   return hipGetLastError();
 }
 

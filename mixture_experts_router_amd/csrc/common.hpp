@@ -70,6 +70,55 @@ __device__ __forceinline__ u32x4 act8_to_f16(u32x4 v, int act) {
   return v;
 }
 
+// ------------------------------------------- bf16 activations in range --
+//
+// bf16 activations reach the dot products and matrix cores as fp16 operands.
+// To keep bf16's range, token t is converted as x * 2^-a_t, a_t >= 0 the
+// smallest exponent with max|x_t| * 2^-a_t < 64: exact (powers of two only
+// move the exponent) as long as the scaled values stay in fp16's normal
+// range, and a_t = 0, the plain conversion, for every token whose largest
+// activation is below 64.  The gate and up sums are scaled back by 2^a_t
+// before SwiGLU; h and the down outputs are staged in fp16 at 2^-2a_t and
+// the combine scales y back by 2^2a_t.
+
+// largest |v| bit pattern of 8 bf16 values (for finite values the order of
+// (bits & 0x7FFF) is the order of |v|)
+__device__ __forceinline__ uint32_t bf16x8_absmax_bits(u32x4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, w[i] & 0x7FFFu);
+    m = max(m, (w[i] >> 16) & 0x7FFFu);
+  }
+  return m;
+}
+
+// a_t from the largest |x| bit pattern of the token: 2^(e-127) <= max|x| <
+// 2^(e-126) for biased exponent e, so max|x| * 2^-a < 2^6 needs a >= e - 132
+__device__ __forceinline__ int bf16_token_exp(uint32_t absmax_bits) {
+  const int e = (int)(absmax_bits >> 7);
+  return e > 132 ? e - 132 : 0;
+}
+
+__device__ __forceinline__ float ldexp_f(float v, int e) { return __builtin_amdgcn_ldexpf(v, e); }
+
+// 8 activations (16 bytes) -> 8 fp16 values of x * 2^-a (a = 0 for fp16
+// activations)
+__device__ __forceinline__ u32x4 act8_to_f16_scaled(u32x4 v, int act, int a) {
+  if (act != ACT_BF16) return v;
+  if (a == 0) return act8_to_f16(v, act);
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f16x2 r;
+    r.x = (f16)ldexp_f(bf16_bits_to_f32(w[i] & 0xFFFFu), -a);
+    r.y = (f16)ldexp_f(bf16_bits_to_f32(w[i] >> 16), -a);
+    w[i] = __builtin_bit_cast(uint32_t, r);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // Reorder 8 fp16 values (k0..k7, packed in pairs) to the order in which a
 // packed 4-bit word is unpacked: (k0,k4), (k1,k5), (k2,k6), (k3,k7).
 __device__ __forceinline__ u32x4 perm8_nibble_order(u32x4 v) {
@@ -208,6 +257,17 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<DPP_ROW_MIRROR>(v);
   const float r0 = readlane_f(v, 0), r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
   return ((r0 + r1) + r2) + r3;
+}
+
+// unsigned maximum over the 64 lanes; every lane ends with the same value
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<DPP_QUAD_1032>((int)v));
+  v = max(v, (uint32_t)dpp_i<DPP_QUAD_2301>((int)v));
+  v = max(v, (uint32_t)dpp_i<DPP_ROW_HALF_MIRROR>((int)v));
+  v = max(v, (uint32_t)dpp_i<DPP_ROW_MIRROR>((int)v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -47,6 +47,7 @@ struct GemmParams {
   WView w0, w1;
   void* out;
   float* pre;  // fused: fp32 gate and up sums [pairs, 2N] in pair order (NULL: not kept)
+  const int32_t* tokexp;  // gather modes, bf16 activations: each token's exponent a_t (NULL: 0)
   uint32_t a_bytes;  // extent of the A rows (offsets at or past it read nothing)
   int32_t sb_up_delta;  // fused: bytes from a gate column's packed scales to its up column's
   int perm8_out;  // fused: store h blocks in 4-bit unpack order
@@ -760,11 +761,18 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
       const int row = mi * 32 + 8 * (r / 4) + 4 * hh + (r % 4);
       if (row >= rows) continue;
       const size_t orow = (size_t)(row0 + row) * prm.N;
+      // the operand rows hold x * 2^-a: sums scaled back by 2^a, h staged at 2^-2a
+      int ea = 0;
+      if constexpr (MODE != GEMM_ROWS_F16) {
+        if (prm.tokexp) ea = prm.tokexp[prm.perm[row0 + row] / prm.kcap];
+      }
       if constexpr (MODE == GEMM_FUSED_SWIGLU) {
 #pragma unroll
         for (int ni = 0; ni < HALFSUB; ++ni) {
           if (!valid[ni]) continue;
-          const float hv = swiglu(acc[mi][ni][r], acc[mi][ni + HALFSUB][r]);
+          acc[mi][ni][r] = ldexp_f(acc[mi][ni][r], ea);
+          acc[mi][ni + HALFSUB][r] = ldexp_f(acc[mi][ni + HALFSUB][r], ea);
+          const float hv = ldexp_f(swiglu(acc[mi][ni][r], acc[mi][ni + HALFSUB][r]), -2 * ea);
           const int col = col0 + 32 * ni + col_in;
           const int at = prm.perm8_out ? (col & ~7) + perm8_slot(col & 7) : col;
           ((uint16_t*)prm.out)[orow + at] = f32_to_f16_bits(hv);
@@ -784,7 +792,7 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
         for (int ni = 0; ni < NSUB; ++ni) {
           if (!valid[ni]) continue;
           const int col = col0 + 32 * ni + col_in;
-          if constexpr (MODE == GEMM_GATHER_F32) ((float*)prm.out)[orow + col] = acc[mi][ni][r];
+          if constexpr (MODE == GEMM_GATHER_F32) ((float*)prm.out)[orow + col] = ldexp_f(acc[mi][ni][r], ea);
           else ((uint16_t*)prm.out)[orow + col] = f32_to_f16_bits(acc[mi][ni][r]);
         }
       }
@@ -871,9 +879,11 @@ static hipError_t launch_bits(GemmMode mode, int bm, const GemmParams& prm, hipS
 
 hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const int32_t* perm, const int32_t* counts,
                        const int32_t* offsets, int kcap, int E, int K, int N, int bits, WView w0, WView w1,
-                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st, float* pre) {
+                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st, float* pre,
+                       const int32_t* tokexp) {
   GemmParams prm;
   prm.pre = mode == GEMM_FUSED_SWIGLU ? pre : nullptr;
+  prm.tokexp = mode != GEMM_ROWS_F16 ? tokexp : nullptr;
   prm.a = a;
   prm.perm = perm;
   prm.counts = counts;

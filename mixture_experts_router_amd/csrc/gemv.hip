@@ -237,6 +237,7 @@ struct GemvUpParams {
   uint16_t* h;
   float* out32;
   float* pre;  // fused: fp32 gate and up sums [pairs, 2N] (NULL: not kept)
+  int32_t* tokexp;  // bf16 activations: each token's exponent a_t (written); NULL for fp16
   int iters;  // row-iterations per pair
   int iters_per_wave;
 };
@@ -299,7 +300,7 @@ __device__ __forceinline__ void load_rows(RowBuf<BITS, CPL>& buf, const GemvUpPa
 template <int BITS, int CPL, bool FUSED>
 __device__ __forceinline__ void finish_iter(const RowBuf<BITS, CPL>& buf, const GemvUpParams& prm, int p, int it,
                                             bool store, const uint32_t (*xr)[Chunk<BITS>::PAIRS], const XSums* xs,
-                                            const Q4Consts& qc) {
+                                            const Q4Consts& qc, int a) {
   constexpr int R = Rows<CPL>::N;
   float part[R];
 #pragma unroll
@@ -309,12 +310,13 @@ __device__ __forceinline__ void finish_iter(const RowBuf<BITS, CPL>& buf, const 
     for (int i = 0; i < CPL; ++i) acc = chunk_acc<BITS>(buf.q[r][i], xr[i], xs[i], buf.s[r][i], buf.b[r][i], qc, acc);
     part[r] = acc;
   }
-  const float v = reduce_rows<R>(part);
+  // the sums of the scaled activations x * 2^-a, scaled back (exact)
+  const float v = ldexp_f(reduce_rows<R>(part), a);
   const int lane = lane_id();
   if constexpr (FUSED) {
     // the up value of lane 0 (and 1) sits in lane R/2 (and R/2 + 1)
     const float u = R == 4 ? dpp_f<DPP_QUAD_2323>(v) : dpp_f<DPP_QUAD_1111>(v);
-    const float hv = swiglu(v, u);
+    const float hv = ldexp_f(swiglu(v, u), -2 * a);  // staged at 2^-2a
     if (store && lane < R / 2) prm.h[(size_t)p * prm.N + (R / 2) * it + lane] = f32_to_f16_bits(hv);
     if (prm.pre && store && lane < R) {
       // lane r holds row r: gate rows first, then the matching up rows
@@ -402,6 +404,19 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   load_rows<BITS, CPL, FUSED>(bufA, prm, e, it_of(0), 0 < n, qoff, goff, ng, row_bytes);
   if constexpr (DEEP) load_rows<BITS, CPL, FUSED>(bufB, prm, e, it_of(1), 1 < n, qoff, goff, ng, row_bytes);
 
+  // the token's exponent (bf16 activations; 0 for fp16), the same in every
+  // wave from the same row
+  int a = 0;
+  if (prm.act == ACT_BF16) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+      for (int j = 0; j < C::PIECES; ++j) m = max(m, bf16x8_absmax_bits(xraw[i][j]));
+    a = __builtin_amdgcn_readfirstlane(bf16_token_exp(wave_max_u32(m)));
+    if (prm.tokexp && slot == 0 && blockIdx.x == 0 && threadIdx.x == 0) prm.tokexp[t] = a;
+  }
+
   // activations of this lane's chunks, as fp16 pairs in the unpack order
   uint32_t xr[CPL][C::PAIRS];
   XSums xs[CPL];
@@ -409,7 +424,7 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   for (int i = 0; i < CPL; ++i) {
 #pragma unroll
     for (int j = 0; j < C::PIECES; ++j) {
-      u32x4 v = act8_to_f16(xraw[i][j], prm.act);
+      u32x4 v = act8_to_f16_scaled(xraw[i][j], prm.act, a);
       if constexpr (BITS == 4) v = perm8_nibble_order(v);
       xr[i][4 * j + 0] = v.x;
       xr[i][4 * j + 1] = v.y;
@@ -422,18 +437,18 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   if constexpr (DEEP) {
     for (int k = 0; k < n; k += 3) {
       load_rows<BITS, CPL, FUSED>(bufC, prm, e, it_of(k + 2), k + 2 < n, qoff, goff, ng, row_bytes);
-      finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it_of(k), k < n, xr, xs, qc);
+      finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it_of(k), k < n, xr, xs, qc, a);
       load_rows<BITS, CPL, FUSED>(bufA, prm, e, it_of(k + 3), k + 3 < n, qoff, goff, ng, row_bytes);
-      finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it_of(k + 1), k + 1 < n, xr, xs, qc);
+      finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it_of(k + 1), k + 1 < n, xr, xs, qc, a);
       load_rows<BITS, CPL, FUSED>(bufB, prm, e, it_of(k + 4), k + 4 < n, qoff, goff, ng, row_bytes);
-      finish_iter<BITS, CPL, FUSED>(bufC, prm, p, it_of(k + 2), k + 2 < n, xr, xs, qc);
+      finish_iter<BITS, CPL, FUSED>(bufC, prm, p, it_of(k + 2), k + 2 < n, xr, xs, qc, a);
     }
   } else {
     for (int k = 0; k < n; k += 2) {
       load_rows<BITS, CPL, FUSED>(bufB, prm, e, it_of(k + 1), k + 1 < n, qoff, goff, ng, row_bytes);
-      finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it_of(k), k < n, xr, xs, qc);
+      finish_iter<BITS, CPL, FUSED>(bufA, prm, p, it_of(k), k < n, xr, xs, qc, a);
       load_rows<BITS, CPL, FUSED>(bufA, prm, e, it_of(k + 2), k + 2 < n, qoff, goff, ng, row_bytes);
-      finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it_of(k + 1), k + 1 < n, xr, xs, qc);
+      finish_iter<BITS, CPL, FUSED>(bufB, prm, p, it_of(k + 1), k + 1 < n, xr, xs, qc, a);
     }
   }
 }
@@ -453,9 +468,10 @@ static hipError_t launch_up_cpl(int cpl, const GemvUpParams& prm, dim3 grid, hip
 
 hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_static, int kcap, int T, int H,
                           int N, int bits, bool fused, WView w0, WView w1, uint16_t* h, float* out32, int num_cu,
-                          hipStream_t st, float* pre) {
+                          hipStream_t st, float* pre, int32_t* tokexp) {
   GemvUpParams prm;
   prm.pre = fused ? pre : nullptr;
+  prm.tokexp = tokexp;
   prm.x = (const uint16_t*)x;
   prm.act = act;
   prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy, route.gs};
@@ -508,7 +524,8 @@ __device__ __forceinline__ int down_row_base(int b, int G) {
 }
 
 struct GemvDownParams {
-  const uint16_t* h;  // fp16 [T*kcap, I], pair order
+  const uint16_t* h;  // fp16 [T*kcap, I], pair order, at 2^-2a_t
+  const int32_t* tokexp;  // each token's exponent a_t (NULL: 0)
   RouteSrc rt;
   int k_static, kcap;
   int H, I;
@@ -701,6 +718,7 @@ __global__ __launch_bounds__(KS == 4 ? 1024 : 512) void gemv_down_kernel(GemvDow
         const float c = w * o;
         y = y + c;
       }
+      if (prm.tokexp) y = ldexp_f(y, 2 * prm.tokexp[t]);  // h was staged at 2^-2a_t
       ((uint16_t*)prm.y)[(size_t)t * prm.H + m] = f32_to_act_bits(y, prm.act);
     }
   }
@@ -715,9 +733,11 @@ bool gemv_down_fits(int I, int bits, int kcap) {
 }
 
 hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_static, int kcap, int T, int H, int I,
-                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st, int capacity) {
+                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st, int capacity,
+                            const int32_t* tokexp) {
   if (capacity > 0 && route.logits) return hipErrorInvalidValue;
   GemvDownParams prm;
+  prm.tokexp = tokexp;
   prm.cap = capacity;
   prm.h = h;
   prm.rt = RouteSrc{route.logits, route.E, route.idx, route.wts, route.k_used, route.entropy, route.gs};

@@ -88,20 +88,23 @@ struct GemvRoute {
   float* entropy;
   int gs = 1;  // experts per selection group (1: plain top-k)
 };
-// fused=true: h[p, j] = fp16(swiglu(gate_j . x, up_j . x)) for j < I, and
-// with pre set also pre[p, j] = gate_j . x, pre[p, N + j] = up_j . x (fp32)
+// fused=true: h[p, j] = fp16(2^-2a_t swiglu(gate_j . x, up_j . x)) for j < I,
+// and with pre set also pre[p, j] = gate_j . x, pre[p, N + j] = up_j . x (fp32)
 // fused=false: out32[p, n] = w0_n . x for n < N
+// bf16 activations: a_t as in common.hpp, written to tokexp[t] (if set); 0 for fp16
 hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_static, int kcap, int T, int H,
                           int N, int bits, bool fused, WView w0, WView w1, uint16_t* h, float* out32, int num_cu,
-                          hipStream_t st, float* pre = nullptr);
+                          hipStream_t st, float* pre = nullptr, int32_t* tokexp = nullptr);
 // whether the decode down kernels take rows of I weights of `bits` bits with
 // kcap slots per token
 bool gemv_down_fits(int I, int bits, int kcap);
 // y[t, m] = act(sum_s w[t,s] * (Wd[e_s, m, :] . h[t*kcap+s, :]));
 // capacity > 0: a pair beyond the first `capacity` pairs of its expert (pair
 // order) is left out of y (needs route.logits NULL: the selection is read)
+// tokexp (NULL: all 0): h rows staged at 2^-2a_t, y scaled back by 2^2a_t
 hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_static, int kcap, int T, int H, int I,
-                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st, int capacity = 0);
+                            int bits, WView wd, void* y, int act, int num_cu, hipStream_t st, int capacity = 0,
+                            const int32_t* tokexp = nullptr);
 // whether the router uses one workgroup per (expert, token) logit rather
 // than the 32 x 32 tiled matrix-core kernel
 bool router_use_small(int T, int E);
@@ -119,19 +122,29 @@ int gemm_max_mtiles(int P, int E, int bm);
 // a_rows: rows of a (T or P); a and one expert's weight rows must each stay
 // below 4 GB (32-bit buffer offsets), else hipErrorInvalidValue
 // FUSED with pre set: also the fp32 gate and up sums of pair perm[row] at
-// pre[pair, col] and pre[pair, N + col]
+// pre[pair, col] and pre[pair, N + col].  tokexp (GATHER modes; NULL: all 0):
+// the operand rows hold x * 2^-a_t, so the sums are scaled back by 2^a_t and
+// h is stored at 2^-2a_t
 hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const int32_t* perm, const int32_t* counts,
                        const int32_t* offsets, int kcap, int E, int K, int N, int bits, WView w0, WView w1,
-                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st, float* pre = nullptr);
+                       void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st, float* pre = nullptr,
+                       const int32_t* tokexp = nullptr);
 
 // --------------------------------------------------------- small kernels
-// h[i, j] = fp16(swiglu(g[i, j], u[i, j])) for i < rows
+// h[i, j] = fp16(2^-2a swiglu(g[i, j], u[i, j])) for i < rows, a the
+// exponent of row i's token: tokexp[pair / kcap], pair = perm ? perm[i] : i
+// (tokexp NULL: a = 0)
 hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, bool perm8,
+                         hipStream_t st, const int32_t* tokexp = nullptr, const int32_t* perm = nullptr,
+                         int kcap = 1);
+// the GEMM operand: x * 2^-a_t as fp16; bf16 activations also write a_t to
+// tokexp[t]
+hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, bool perm8, int32_t* tokexp,
                          hipStream_t st);
-hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, bool perm8, hipStream_t st);
-// y[t] = act(sum_{s<k} w[t,s] * o[pos[t*kcap+s]])
+// y[t] = act(2^2a_t sum_{s<k} w[t,s] * o[pos[t*kcap+s]]) (tokexp NULL: a_t = 0)
 hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wts, const int32_t* k_used_dev,
-                          int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st);
+                          int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st,
+                          const int32_t* tokexp = nullptr);
 // out[p, :] = src[r, :] (fp16 rows of width I) with r = pos[p] for pos[p] >= 0,
 // or, when pos is NULL, r = p for the pairs whose slot p % kcap < k_used
 hipError_t launch_gather_rows(const uint16_t* src, const int32_t* pos, int64_t P, int I, uint16_t* out, int kcap,

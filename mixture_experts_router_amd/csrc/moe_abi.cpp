@@ -162,7 +162,7 @@ bool compatible(const moe_weights* a, const moe_weights* b) {
 // ------------------------------------------------------------ workspace --
 
 struct Layout {
-  size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, a16, hent, sbgu, sbd, g32, u32, total;
+  size_t logits, idx, w, scal, counts, offsets, perm, pos, h, o, a16, hent, tokexp, sbgu, sbd, g32, u32, total;
 };
 
 // Which regions a call needs: the batched path's GEMM operands, and the
@@ -192,6 +192,7 @@ Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t
   L.pos = take((size_t)(P * 4));
   L.h = take((size_t)(P * I * 2));
   L.hent = take((size_t)(T * 4));  // adaptive k: per-token entropies
+  L.tokexp = take((size_t)(T * 4));  // bf16 activations: per-token exponents
   if (nd.batched) {
     L.o = take((size_t)(P * H * 2));
     L.a16 = take((size_t)(T * H * 2));  // the activations as the GEMM's fp16 operand
@@ -343,6 +344,8 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   uint16_t* o = (uint16_t*)(W + L.o);
   uint16_t* a16w = (uint16_t*)(W + L.a16);
   float* g32 = (float*)(W + L.g32);
+  // bf16 activations reach the fp16 operands as x * 2^-a_t per token
+  int32_t* tokexp = dt == MOE_BF16 ? (int32_t*)(W + L.tokexp) : nullptr;
   float* u32 = (float*)(W + L.u32);
   const bool unfused = (flags & MOE_FLAG_UNFUSED) != 0;
   const int act = (int)dt;
@@ -366,16 +369,16 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     }
     if (!unfused) {
       HIP_TRY(moe::launch_gemv_up(x, act, rt, k_static, kcap, T, H, I, bits, true, wg, wu, h, nullptr, props.num_cu,
-                                  st, pre_tap));
+                                  st, pre_tap, tokexp));
       plan_step("gemv_gate_up_swiglu", st);
     } else {
       HIP_TRY(moe::launch_gemv_up(x, act, rt, k_static, kcap, T, H, I, bits, false, wg, wg, nullptr, g32,
-                                  props.num_cu, st));
+                                  props.num_cu, st, nullptr, tokexp));
       plan_step("gemv_gate", st);
       HIP_TRY(moe::launch_gemv_up(x, act, rt, k_static, kcap, T, H, I, bits, false, wu, wu, nullptr, u32,
-                                  props.num_cu, st));
+                                  props.num_cu, st, nullptr, tokexp));
       plan_step("gemv_up", st);
-      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, false, st));
+      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, false, st, tokexp, nullptr, kcap));
       plan_step("swiglu", st);
       if (pre_tap) HIP_TRY(moe::launch_gather_preact(g32, u32, nullptr, P, I, pre_tap, kcap, k_used, k_static, st));
     }
@@ -384,7 +387,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     moe::GemvRoute rt_down = rt;
     rt_down.logits = nullptr;
     HIP_TRY(moe::launch_gemv_down(h, rt_down, k_static, kcap, T, H, I, bits, view_of(down, 0), y, act, props.num_cu,
-                                  st, ro.cap));
+                                  st, ro.cap, tokexp));
     plan_step("gemv_down_combine", st);
     if (want_sort_taps) {
       HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st, ro.cap));
@@ -402,7 +405,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     const bool perm8 = bits == 4;
     const uint16_t* a16 = (const uint16_t*)x;
     if (perm8 || dt != MOE_F16) {
-      HIP_TRY(moe::launch_prep_a(x, act, a16w, T, H, perm8, st));
+      HIP_TRY(moe::launch_prep_a(x, act, a16w, T, H, perm8, tokexp, st));
       plan_step("prep_a", st);
       a16 = a16w;
     }
@@ -421,16 +424,16 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     }
     if (!unfused) {
       HIP_TRY(moe::launch_gemm(moe::GEMM_FUSED_SWIGLU, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wg, wu, h,
-                               perm8, bm, mt, st, pre_tap));
+                               perm8, bm, mt, st, pre_tap, tokexp));
       plan_step("gemm_gate_up_swiglu", st);
     } else {
       HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wg, wg, g32,
-                               false, bm, mt, st));
+                               false, bm, mt, st, nullptr, tokexp));
       plan_step("gemm_gate", st);
       HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wu, wu, u32,
-                               false, bm, mt, st));
+                               false, bm, mt, st, nullptr, tokexp));
       plan_step("gemm_up", st);
-      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, perm8, st));
+      HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, perm8, st, tokexp, perm, kcap));
       plan_step("swiglu", st);
       if (pre_tap) HIP_TRY(moe::launch_gather_preact(g32, u32, pos, P, I, pre_tap, kcap, k_used, k_static, st));
     }
@@ -445,7 +448,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     HIP_TRY(moe::launch_gemm(moe::GEMM_ROWS_F16, h, P, perm, counts, offsets, kcap, E, I, H, bits, wd, wd, o, false, bm,
                              mt, st));
     plan_step("gemm_down", st);
-    HIP_TRY(moe::launch_combine(o, pos, wts, k_used, k_static, kcap, T, H, y, act, st));
+    HIP_TRY(moe::launch_combine(o, pos, wts, k_used, k_static, kcap, T, H, y, act, st, tokexp));
     plan_step("combine", st);
   }
 

@@ -12,6 +12,7 @@ import torch
 import mixture_experts_router_amd as moe
 import moe_inputs as mi
 import oracle
+from ref64 import half64
 from gpu_util import (Dev, assert_within_tolerance, batched_path_takes, check_routing_identical_logits, dev_half,
                       host_bits, reference_outputs)
 
@@ -373,3 +374,58 @@ def test_zero_tokens_and_errors_on_gpu():
         moe.layer_forward(dev.x, dev.wr, 9, dev.down, gate_up=dev.gate_up)
     assert e.value.name == "MOE_ERR_K"
 
+
+
+def _token_exponent(x_bits_row: np.ndarray) -> int:
+    """The scale exponent a_t the library takes for a bf16 token: the smallest
+    a >= 0 with max|x| * 2^-a < 64 (include/moe.h, Arithmetic)."""
+    e = int((np.max(x_bits_row & 0x7FFF) >> 7))
+    return max(0, e - 132)
+
+
+@pytest.mark.parametrize("recipe,kw,flag", [
+    ("batched_decode", dict(T=40, H=512, E=8, I=320), moe.FLAG_FORCE_MFMA),   # 8-bit, batched path
+    ("prefill", dict(T=300, H=512, E=16, I=192), moe.FLAG_FORCE_MFMA),        # 4-bit, batched path
+    ("batched_decode", dict(T=6, H=512, E=8, I=320), moe.FLAG_FORCE_GEMV),    # 8-bit, decode path
+    ("prefill", dict(T=4, H=512, E=16, I=192), moe.FLAG_FORCE_GEMV),          # 4-bit, decode path
+])
+def test_bf16_activations_beyond_fp16_range(recipe, kw, flag):
+    # rows of bf16 activations scaled near 1e5 (beyond fp16's 65504) and one
+    # row with a single element of 2e5: the layer keeps bf16's range
+    inp = mi.make_inputs(recipe, dtype="bf16", **kw)
+    x = half64(inp.x, "bf16")
+    big = {1: 1e5, 3: 3e4}
+    for t, c in big.items():
+        x[t] *= c
+    x[2, 7] = 2e5
+    import dataclasses
+    inp = dataclasses.replace(inp, x=mi.round_half(x, "bf16"))
+    a = np.array([_token_exponent(inp.x[t]) for t in range(inp.T)])
+    print("token exponents", a[:6].tolist(), flush=True)
+    assert a[1] > 0 and a[3] > 0 and a[2] > 0 and a[0] == 0
+    dev = Dev(inp)
+    gu_np = oracle.fuse_gate_up(inp.gate, inp.up)
+    taps = moe.make_taps(inp.T, inp.E, inp.k, inp.I, "cuda")
+    yb = host_bits(dev.forward(flags=flag, taps=taps))
+    t = {n: v.cpu().numpy() for n, v in taps.items()}
+    ku = int(t["k_used"][0])
+    check_routing_identical_logits(t["logits"], t["topk_idx"], t["topk_w"], ku)
+    ref, _ = reference_outputs(inp, gu_np, np.arange(inp.T), t["topk_idx"], t["topk_w"], ku)
+    y = half64(yb, "bf16")
+    assert np.all(np.isfinite(y)), "non-finite output"
+    assert np.all(np.isfinite(t["h"].astype(np.float64)))
+    normal = a == 0
+    # tokens at unit scale: the usual bars
+    assert_within_tolerance(yb[normal], ref[normal], "bf16", "bf16 unscaled tokens")
+    # scaled tokens: the same bars on the output in units of its rms
+    for tk in np.where(~normal)[0]:
+        r = ref[tk].astype(np.float64)
+        rms = float(np.sqrt(np.mean(r * r)))
+        d = (y[tk] - r) / rms
+        rel = float(np.linalg.norm(y[tk] - r) / np.linalg.norm(r))
+        print("token %d a=%d rms %.3g: max_abs/rms %.3g rel_l2 %.3g" % (tk, a[tk], rms, np.max(np.abs(d)), rel),
+              flush=True)
+        assert np.max(np.abs(d)) <= 2e-2 and rel <= 5e-3, tk
+    # fused == unfused still holds bit for bit
+    y_u = host_bits(dev.forward(flags=flag | moe.FLAG_UNFUSED))
+    assert np.array_equal(yb, y_u)
