@@ -159,6 +159,8 @@ def main():
                          "(activation counts of a Zipf-1.1 window, mean 1)")
     ap.add_argument("--groups", type=int, default=0, help="group-limited routing: at most one expert per group")
     ap.add_argument("--capacity", type=int, default=0, help="expert capacity: at most this many pairs per expert")
+    ap.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
+                    help="launch-shape knob for measurement sweeps (moe_debug_set_tuning); results do not depend on it")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="also time the layer's kernels with a write of this many MiB between steps, which "
                          "evicts the 256 MB Infinity Cache, so their weight bytes must come from HBM")
@@ -177,6 +179,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     moe.lib()  # fails loudly if the HIP library is missing
+    for kv in args.tune:
+        key, val = kv.split("=")
+        moe.debug_set_tuning(int(key), int(val))
     wl = WORKLOADS[args.workload]
     recipe = wl["recipe"]
     mi.set_threads(min(os.cpu_count() or 1, 16))
@@ -501,6 +506,7 @@ def main():
                    "routing_options": {"load_aware_alpha": args.load_aware, "groups": args.groups,
                                        "capacity": args.capacity} if lopt else None,
                    "per_kernel_us": [round(float(v), 3) for v in per_kernel_us],
+                   "tuning": args.tune or None,
                    "cache_flush": flush},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -48,6 +48,7 @@ struct GemmParams {
   void* out;
   float* pre;  // fused: fp32 gate and up sums [pairs, 2N] in pair order (NULL: not kept)
   const int32_t* tokexp;  // gather modes, bf16 activations: each token's exponent a_t (NULL: 0)
+  const int32_t* any_scaled;  // nonzero when some a_t > 0 (tokexp is read only then)
   uint32_t a_bytes;  // extent of the A rows (offsets at or past it read nothing)
   int32_t sb_up_delta;  // fused: bytes from a gate column's packed scales to its up column's
   int perm8_out;  // fused: store h blocks in 4-bit unpack order
@@ -753,6 +754,9 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
 
   // ---- epilogue.  32x32 accumulator layout: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // whether any token's activations were scaled (bf16 beyond 64): only then
+  // are the exponents read
+  const bool scaled = MODE != GEMM_ROWS_F16 && prm.tokexp && *prm.any_scaled != 0;
 #pragma unroll
   for (int mi = 0; mi < MS; ++mi) {
     if (mi * 32 >= rows) continue;
@@ -764,7 +768,7 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
       // the operand rows hold x * 2^-a: sums scaled back by 2^a, h staged at 2^-2a
       int ea = 0;
       if constexpr (MODE != GEMM_ROWS_F16) {
-        if (prm.tokexp) ea = prm.tokexp[prm.perm[row0 + row] / prm.kcap];
+        if (scaled) ea = prm.tokexp[prm.perm[row0 + row] / prm.kcap];
       }
       if constexpr (MODE == GEMM_FUSED_SWIGLU) {
 #pragma unroll
@@ -880,8 +884,10 @@ static hipError_t launch_bits(GemmMode mode, int bm, const GemmParams& prm, hipS
 hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const int32_t* perm, const int32_t* counts,
                        const int32_t* offsets, int kcap, int E, int K, int N, int bits, WView w0, WView w1,
                        void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st, float* pre,
-                       const int32_t* tokexp) {
+                       const int32_t* tokexp, const int32_t* any_scaled) {
   GemmParams prm;
+  if (tokexp && !any_scaled) return hipErrorInvalidValue;
+  prm.any_scaled = any_scaled;
   prm.pre = mode == GEMM_FUSED_SWIGLU ? pre : nullptr;
   prm.tokexp = mode != GEMM_ROWS_F16 ? tokexp : nullptr;
   prm.a = a;

@@ -496,6 +496,13 @@ hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_
   int64_t per_pair = want / ((int64_t)T * kcap);
   if (per_pair < 4) per_pair = 4;
   if (per_pair > prm.iters) per_pair = prm.iters;
+  // as many waves as give every wave the same number of iterations (at most
+  // the target): with a few waves one iteration longer than the rest, the
+  // last iteration period streams with a fraction of the waves
+  if (tuning(TUNE_UP_BALANCE) != 2) {
+    const int64_t ipw = (prm.iters + per_pair - 1) / per_pair;
+    per_pair = (prm.iters + ipw - 1) / ipw;
+  }
   prm.iters_per_wave = (int)((prm.iters + per_pair - 1) / per_pair);
   dim3 grid((unsigned)((per_pair + 3) / 4), T * kcap);
   if (bits == 4) return fused ? launch_up_cpl<4, true>(cpl, prm, grid, st) : launch_up_cpl<4, false>(cpl, prm, grid, st);

@@ -41,7 +41,8 @@ enum TuneKey {
   TUNE_GEMM_NSUB = 5,  // 4: 128-row GEMM tiles give each wave 128 columns (default 64)
   TUNE_GEMM_KSPLIT = 6,  // 2: 64- and 128-row GEMM tiles run eight waves splitting k (default four)
   TUNE_GEMM_WPC = 7,  // 1 / 2: workgroups per CU at 32- and 64-row GEMM tiles (other values: by bits and tile)
-  TUNE_KEYS = 8
+  TUNE_UP_BALANCE = 8,  // 2: decode gate+up waves per pair from the wave target alone (default: equal iterations)
+  TUNE_KEYS = 9
 };
 int tuning(TuneKey key);
 
@@ -68,10 +69,11 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int gs, int32_t
 
 // ------------------------------------------------------------------ sort
 // k_used_dev may be NULL (then k_static is used); capacity > 0 lists only the
-// first `capacity` pairs of every expert (the rest get pos -1)
+// first `capacity` pairs of every expert (the rest get pos -1); clear_word
+// (if set) is set to 0
 hipError_t launch_sort_pairs(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st,
-                             int capacity = 0);
+                             int capacity = 0, int32_t* clear_word = nullptr);
 
 // ------------------------------------------------- decode (grouped GEMV)
 // chunks of 16 bytes per lane needed for a row of K weights
@@ -124,11 +126,11 @@ int gemm_max_mtiles(int P, int E, int bm);
 // FUSED with pre set: also the fp32 gate and up sums of pair perm[row] at
 // pre[pair, col] and pre[pair, N + col].  tokexp (GATHER modes; NULL: all 0):
 // the operand rows hold x * 2^-a_t, so the sums are scaled back by 2^a_t and
-// h is stored at 2^-2a_t
+// h is stored at 2^-2a_t; read only when *any_scaled is nonzero
 hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const int32_t* perm, const int32_t* counts,
                        const int32_t* offsets, int kcap, int E, int K, int N, int bits, WView w0, WView w1,
                        void* out, bool perm8_out, int bm, int max_mtiles, hipStream_t st, float* pre = nullptr,
-                       const int32_t* tokexp = nullptr);
+                       const int32_t* tokexp = nullptr, const int32_t* any_scaled = nullptr);
 
 // --------------------------------------------------------- small kernels
 // h[i, j] = fp16(2^-2a swiglu(g[i, j], u[i, j])) for i < rows, a the
@@ -138,9 +140,9 @@ hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t ro
                          hipStream_t st, const int32_t* tokexp = nullptr, const int32_t* perm = nullptr,
                          int kcap = 1);
 // the GEMM operand: x * 2^-a_t as fp16; bf16 activations also write a_t to
-// tokexp[t]
+// tokexp[t] and set *any_scaled to 1 when some a_t > 0 (it must be 0 before)
 hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, bool perm8, int32_t* tokexp,
-                         hipStream_t st);
+                         int32_t* any_scaled, hipStream_t st);
 // y[t] = act(2^2a_t sum_{s<k} w[t,s] * o[pos[t*kcap+s]]) (tokexp NULL: a_t = 0)
 hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wts, const int32_t* k_used_dev,
                           int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st,

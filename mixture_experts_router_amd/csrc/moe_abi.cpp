@@ -185,7 +185,7 @@ Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t
   L.logits = take((size_t)(T * E * 4));
   L.idx = take((size_t)(P * 4));
   L.w = take((size_t)(P * 4));
-  L.scal = take(8);
+  L.scal = take(16);  // k_used, entropy, the flag of scaled bf16 tokens
   L.counts = take((size_t)(E * 4));
   L.offsets = take((size_t)((E + 1) * 4));
   L.perm = take((size_t)(P * 4));
@@ -346,6 +346,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   float* g32 = (float*)(W + L.g32);
   // bf16 activations reach the fp16 operands as x * 2^-a_t per token
   int32_t* tokexp = dt == MOE_BF16 ? (int32_t*)(W + L.tokexp) : nullptr;
+  int32_t* any_scaled = (int32_t*)(W + L.scal + 8);
   float* u32 = (float*)(W + L.u32);
   const bool unfused = (flags & MOE_FLAG_UNFUSED) != 0;
   const int act = (int)dt;
@@ -397,7 +398,9 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     if ((s = route_impl(x, dt, T, H, router_w, E, k, ro, idx, wts, k_used, entropy, logits, (float*)(W + L.hent),
                         st)) != MOE_OK)
       return s;
-    HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st, ro.cap));
+    // the sort also clears the flag prep_a raises for scaled bf16 tokens
+    HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st, ro.cap,
+                                   any_scaled));
     plan_step("sort_pairs", st);
     const int bm = moe::gemm_block_m((int)P, E);
     const int mt = moe::gemm_max_mtiles((int)P, E, bm);
@@ -405,7 +408,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     const bool perm8 = bits == 4;
     const uint16_t* a16 = (const uint16_t*)x;
     if (perm8 || dt != MOE_F16) {
-      HIP_TRY(moe::launch_prep_a(x, act, a16w, T, H, perm8, tokexp, st));
+      HIP_TRY(moe::launch_prep_a(x, act, a16w, T, H, perm8, tokexp, any_scaled, st));
       plan_step("prep_a", st);
       a16 = a16w;
     }
@@ -424,14 +427,14 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     }
     if (!unfused) {
       HIP_TRY(moe::launch_gemm(moe::GEMM_FUSED_SWIGLU, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wg, wu, h,
-                               perm8, bm, mt, st, pre_tap, tokexp));
+                               perm8, bm, mt, st, pre_tap, tokexp, any_scaled));
       plan_step("gemm_gate_up_swiglu", st);
     } else {
       HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wg, wg, g32,
-                               false, bm, mt, st, nullptr, tokexp));
+                               false, bm, mt, st, nullptr, tokexp, any_scaled));
       plan_step("gemm_gate", st);
       HIP_TRY(moe::launch_gemm(moe::GEMM_GATHER_F32, a16, T, perm, counts, offsets, kcap, E, H, I, bits, wu, wu, u32,
-                               false, bm, mt, st, nullptr, tokexp));
+                               false, bm, mt, st, nullptr, tokexp, any_scaled));
       plan_step("gemm_up", st);
       HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, perm8, st, tokexp, perm, kcap));
       plan_step("swiglu", st);
@@ -475,7 +478,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
 
 namespace moe {
 namespace {
-int g_tuning[TUNE_KEYS] = {8, 8, 1 << 30, 1, 2, 2, 1, 3};
+int g_tuning[TUNE_KEYS] = {8, 8, 1 << 30, 1, 2, 2, 1, 3, 1};
 }
 int tuning(TuneKey key) { return g_tuning[key]; }
 void set_tuning(int key, int value) {

@@ -27,8 +27,10 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
                                                           const int32_t* __restrict__ k_used_dev, int k_static, int E,
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                                          int32_t* __restrict__ pos, int cap) {
+                                                          int32_t* __restrict__ pos, int cap,
+                                                          int32_t* __restrict__ clear_word) {
   __shared__ int s_lt[16], s_eq[16];
+  if (clear_word && blockIdx.x == 0 && threadIdx.x == 0) *clear_word = 0;
   __shared__ int hist[MOE_MAX_EXPERTS_DEV];
   const int e = blockIdx.x;
   const int lane = lane_id();
@@ -124,18 +126,18 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
 
 hipError_t launch_sort_pairs(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st,
-                             int capacity) {
+                             int capacity, int32_t* clear_word) {
   const int64_t P = (int64_t)T * kcap;
   const int64_t rounds = (P + 16 * 64 - 1) / (16 * 64);  // rounds of 64 pairs per wave
   if (rounds >= 16)
     (void)launch_kernel(sort_pairs_kernel<16>, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
-                        perm, pos, capacity);
+                        perm, pos, capacity, clear_word);
   else if (rounds >= 4)
     (void)launch_kernel(sort_pairs_kernel<4>, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
-                        perm, pos, capacity);
+                        perm, pos, capacity, clear_word);
   else
     (void)launch_kernel(sort_pairs_kernel<2>, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
-                        perm, pos, capacity);
+                        perm, pos, capacity, clear_word);
   return hipGetLastError();
 }
 

@@ -64,6 +64,9 @@ CASES = {
     "prefill_q5_bm128": ("prefill", dict(T=2304, H=256, E=8, I=384, bits=5)),
     "prefill_q6_bm128": ("prefill", dict(T=2304, H=256, E=8, I=384, bits=6)),
     "entropy_q5": ("entropy", dict(T=96, H=512, E=16, I=256, bits=5, segment=2)),
+    # a small batch over long rows (bf16 activations; 8- and 4-bit weights)
+    "batched_long_k": ("batched_decode", dict(T=16, H=2048, E=16, I=1024)),
+    "batched_long_k_q4": ("prefill", dict(T=8, H=2048, E=16, I=1024)),
 }
 
 
@@ -162,7 +165,7 @@ GEMM_SHAPES = [(32, 2, 2, 1, 2), (32, 2, 2, 1, 1), (64, 1, 2, 1, 2), (64, 2, 2, 
 DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2, 6: 1, 7: 3}
 
 
-@pytest.mark.parametrize("name", ["prefill_bm128", "prefill_small", "tiny_q8_bf16", "tiny_fp16w"])
+@pytest.mark.parametrize("name", ["prefill_bm128", "prefill_small", "tiny_q8_bf16", "tiny_fp16w", "batched_long_k"])
 def test_gemm_launch_shapes_are_bit_identical(name, built):
     from ref64 import half64
     inp, _, dev = built(name)
