@@ -67,6 +67,8 @@ def _load():
     lib.gen_decode_half.argtypes = [vp, i64, i32, vp]
     lib.gen_quantize_rows.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
     lib.gen_quant_weights.argtypes = [u64, u32, i32, i32, i32, i32, i32, dbl, vp, vp, vp]
+    lib.gen_quantize_rows_nvfp4.argtypes = [vp, i64, i32, dbl, vp, vp]
+    lib.gen_quant_nvfp4.argtypes = [u64, u32, i32, i32, i32, dbl, dbl, vp, vp]
     lib.gen_zipf_sets.argtypes = [u64, i64, i32, i32, i32, dbl, vp]
     lib.gen_planted_x.argtypes = [u64, i64, i32, i32, i32, i32, vp, i32, vp, dbl, vp]
     _lib = lib
@@ -125,6 +127,9 @@ class Weights:
     the row's little-endian bit stream, b = bits) or [E, N, K] (8-bit);
     ``scales``/``biases`` fp16 bits [E, N, K/group].
     bits 16:  ``q`` fp16 bits [E, N, K]; scales/biases None.
+    fmt "nvfp4" (bits 4, group 16): ``q`` [E, N, K/2] E2M1 codes (sign in
+    bit 3), two per byte, low nibble = even column; ``scales`` E4M3 bytes
+    [E, N, K/16]; no biases; ``tensor_scale`` the fp32 per-tensor scale.
     """
 
     q: np.ndarray
@@ -135,12 +140,16 @@ class Weights:
     K: int
     bits: int
     group_size: int = 64
+    fmt: str = "affine"  # "affine" | "nvfp4"
+    tensor_scale: float = 1.0
 
     @property
     def nbytes(self) -> int:
         n = self.q.nbytes
         if self.scales is not None:
-            n += self.scales.nbytes + self.biases.nbytes
+            n += self.scales.nbytes
+        if self.biases is not None:
+            n += self.biases.nbytes
         return n
 
 
@@ -155,6 +164,33 @@ def quant_weights(seed: int, tid: int, E: int, N: int, K: int, bits: int, sigma:
     b = np.empty((E, N, K // gs), np.uint16)
     _load().gen_quant_weights(seed, tid, E, N, K, bits, gs, sigma, _p(q), _p(s), _p(b))
     return Weights(q, s, b, E, N, K, bits, gs)
+
+
+def nvfp4_weights(seed: int, tid: int, E: int, N: int, K: int, sigma: float = 0.02,
+                  ts: Optional[float] = None) -> Weights:
+    """N(0, sigma) weights [E, N, K] quantised to NVFP4.  The tensor scale
+    defaults to 8 sigma / (6 * 448): an amax of 8 sigma (which such a tensor
+    practically never exceeds) spread over E2M1's largest value and E4M3's."""
+    assert K % 16 == 0
+    ts = float(np.float32(8.0 * sigma / (6.0 * 448.0))) if ts is None else float(np.float32(ts))
+    q = np.empty((E, N, K // 2), np.uint8)
+    s = np.empty((E, N, K // 16), np.uint8)
+    _load().gen_quant_nvfp4(seed, tid, E, N, K, sigma, ts, _p(q), _p(s))
+    return Weights(q, s, None, E, N, K, 4, 16, "nvfp4", ts)
+
+
+def quantize_rows_nvfp4(w: np.ndarray, ts: Optional[float] = None):
+    """NVFP4 codes and block scales of an explicit fp64 matrix [rows, K];
+    ts defaults to amax / (6 * 448) of the matrix.  Returns (q, scales, ts)."""
+    w = np.ascontiguousarray(w, np.float64)
+    rows, K = w.shape
+    if ts is None:
+        ts = float(np.abs(w).max()) / (6.0 * 448.0)
+    ts = float(np.float32(ts))
+    q = np.empty((rows, K // 2), np.uint8)
+    s = np.empty((rows, K // 16), np.uint8)
+    _load().gen_quantize_rows_nvfp4(_p(w), rows, K, ts, _p(q), _p(s))
+    return q, s, ts
 
 
 def quantize_rows(w: np.ndarray, bits: int, gs: int = 64):
@@ -233,6 +269,7 @@ class LayerInputs:
     down: Weights
     sets: Optional[np.ndarray] = None  # planted expert sets (Zipf recipes)
     segment: int = 0
+    fmt: str = "affine"  # weight format: "affine" (bits 4/5/6/8, or 16 unquantised) | "nvfp4"
 
     @property
     def kcap(self) -> int:
@@ -276,20 +313,28 @@ def make_router_inputs(name: str, *, T: Optional[int] = None, H: Optional[int] =
 def make_inputs(name: str, *, T: Optional[int] = None, H: Optional[int] = None, E: Optional[int] = None,
                 I: Optional[int] = None, k: Optional[int] = None, bits: Optional[int] = None,
                 dtype: Optional[str] = None, seed: Optional[int] = None, segment: int = 0,
-                zipf="recipe", token_offset: int = 0) -> LayerInputs:
+                zipf="recipe", token_offset: int = 0, fmt: str = "affine") -> LayerInputs:
     """Build one call's inputs for a recipe, optionally with smaller shapes.
 
     ``segment`` selects the router temperature and token range of the
     ``entropy`` recipe.  ``token_offset`` starts the activation rows further
-    along the stream (a pool of decode tokens).
+    along the stream (a pool of decode tokens).  ``fmt="nvfp4"`` quantises
+    the expert weights to NVFP4 instead (bits is then 4).
     """
     T, H, E, I, k, bits, dtype, seed, _ = _resolve(name, T, H, E, I, k, bits, dtype, seed, zipf)
     x, wr, sets = make_router_inputs(name, T=T, H=H, E=E, k=k, dtype=dtype, seed=seed, segment=segment, zipf=zipf,
                                      token_offset=token_offset)
-    gate = quant_weights(seed, TID_GATE, E, I, H, bits, WEIGHT_SIGMA)
-    up = quant_weights(seed, TID_UP, E, I, H, bits, WEIGHT_SIGMA)
-    down = quant_weights(seed, TID_DOWN, E, H, I, bits, WEIGHT_SIGMA)
-    return LayerInputs(name, T, H, E, I, k, bits, dtype, seed, x, wr, gate, up, down, sets, segment)
+    if fmt == "nvfp4":
+        bits = 4
+        gate = nvfp4_weights(seed, TID_GATE, E, I, H, WEIGHT_SIGMA)
+        up = nvfp4_weights(seed, TID_UP, E, I, H, WEIGHT_SIGMA)
+        down = nvfp4_weights(seed, TID_DOWN, E, H, I, WEIGHT_SIGMA)
+    else:
+        assert fmt == "affine", fmt
+        gate = quant_weights(seed, TID_GATE, E, I, H, bits, WEIGHT_SIGMA)
+        up = quant_weights(seed, TID_UP, E, I, H, bits, WEIGHT_SIGMA)
+        down = quant_weights(seed, TID_DOWN, E, H, I, bits, WEIGHT_SIGMA)
+    return LayerInputs(name, T, H, E, I, k, bits, dtype, seed, x, wr, gate, up, down, sets, segment, fmt)
 
 
 def exact_router_inputs(seed: int, T: int, H: int, E: int, dtype: str = "f16"):

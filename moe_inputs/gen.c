@@ -13,6 +13,9 @@
  *   - Weight groups are quantised with a min-max affine quantiser: scale =
  *     fp16((max-min)/(2^bits-1)), bias = fp16(min), q = clamp(rint((w-bias)/scale)).
  *     4-bit codes are packed two per byte, the even column in the low nibble.
+ *   - NVFP4 blocks of 16 columns: block scale = E4M3(amax / (6 ts)) with the
+ *     tensor scale ts given, codes = nearest E2M1 value of w / (ts * scale);
+ *     E2M1 codes are packed as 4-bit codes.
  *   - Zipf-skewed routing is planted into activations by adding a multiple of
  *     the chosen experts' router rows (see gen_planted_x).
  *
@@ -264,6 +267,96 @@ void gen_quant_weights(uint64_t seed, uint32_t tid, int E, int N, int K, int bit
       if (g == 0) memset(q + r * row_bytes, 0, (size_t)row_bytes);
       quant_group(w, gs, bits, codes, &scales[r * ng + g], &biases[r * ng + g]);
       store_codes(codes, gs, bits, (int64_t)g * gs, q + r * row_bytes);
+    }
+  }
+}
+
+/* ------------------------------------------------------ NVFP4 quantiser -- */
+
+/* value of an FP8 E4M3 byte (OCP "fn": bias 7, subnormals m * 2^-9, 448 max) */
+static double e4m3_value(uint8_t b) {
+  int e = (b >> 3) & 15, m = b & 7;
+  double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (b & 0x80) ? -v : v;
+}
+
+/* nearest E4M3 byte to v >= 0, ties to even mantissa, saturating at 448 */
+static uint8_t e4m3_round(double v) {
+  if (!(v > 0)) return 0;
+  if (v >= 448.0) return 0x7E;
+  int e2;
+  frexp(v, &e2);
+  int E = e2 - 1; /* v in [2^E, 2^(E+1)) */
+  if (E < -6) E = -6; /* below 2^-6: the subnormal step 2^-9 */
+  double m = nearbyint(ldexp(v, 3 - E)); /* default rounding: ties to even */
+  if (m >= 16) {
+    m = 8;
+    E += 1;
+  }
+  int code = m < 8 ? (int)m : ((E + 7) << 3) | ((int)m - 8);
+  return (uint8_t)(code > 0x7E ? 0x7E : code);
+}
+
+/* nearest E2M1 code (sign in bit 3) to r, ties to even mantissa, saturating at 6 */
+static uint8_t e2m1_round(double r) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  double a = fabs(r);
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    double d = fabs(a - mag[c]), db = fabs(a - mag[best]);
+    if (d < db || (d == db && (c & 1) == 0)) best = c;
+  }
+  return (uint8_t)(best == 0 ? 0 : (r < 0 ? 8 | best : best));
+}
+
+/* one block of 16 values: block scale = E4M3(amax / (6 ts)), codes = E2M1(w / (ts * scale)) */
+static void quant_block_nvfp4(const double* w, double ts, uint8_t* codes, uint8_t* s_byte) {
+  double amax = 0;
+  for (int i = 0; i < 16; ++i)
+    if (fabs(w[i]) > amax) amax = fabs(w[i]);
+  uint8_t sb = e4m3_round(amax / (6.0 * ts));
+  double step = ts * e4m3_value(sb);
+  for (int i = 0; i < 16; ++i) codes[i] = step > 0 ? e2m1_round(w[i] / step) : 0;
+  *s_byte = sb;
+}
+
+/* quantise an explicit fp64 matrix [rows, K] to NVFP4 with tensor scale ts */
+void gen_quantize_rows_nvfp4(const double* w, int64_t rows, int K, double ts, uint8_t* q, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    uint8_t codes[16];
+    for (int g = 0; g < K / 16; ++g) {
+      quant_block_nvfp4(w + r * K + (int64_t)g * 16, ts, codes, &scales[r * (K / 16) + g]);
+      store_codes(codes, 16, 4, (int64_t)g * 16, q + r * (K / 2));
+    }
+  }
+}
+
+/*
+ * Draw an expert weight tensor [E, N, K] of N(0, sigma) values (the same
+ * streams and indices as gen_quant_weights) and quantise it to NVFP4 with
+ * tensor scale ts: q [E, N, K/2] (two E2M1 codes per byte, low nibble = even
+ * column), scales [E, N, K/16] E4M3 bytes.
+ */
+void gen_quant_nvfp4(uint64_t seed, uint32_t tid, int E, int N, int K, double sigma, double ts, uint8_t* q,
+                     uint8_t* scales) {
+  uint64_t key = stream_key(seed, tid);
+  int64_t rows = (int64_t)E * N;
+  int nb = K / 16;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t r = 0; r < rows; ++r) {
+    double w[16];
+    uint8_t codes[16];
+    for (int g = 0; g < nb; ++g) {
+      uint64_t base = (uint64_t)(r * K + (int64_t)g * 16);
+      for (int i = 0; i < 16; i += 2) {
+        double c, sn;
+        normal_pair(key, (base + (uint64_t)i) >> 1, &c, &sn);
+        w[i] = sigma * c;
+        w[i + 1] = sigma * sn;
+      }
+      quant_block_nvfp4(w, ts, codes, &scales[r * nb + g]);
+      store_codes(codes, 16, 4, (int64_t)g * 16, q + r * (K / 2));
     }
   }
 }

@@ -23,6 +23,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 DTYPE_CODE = {"f16": 1, "bf16": 2}
+NVFP4 = 0x104  # `bits` code of NVFP4 weights (E2M1 codes, E4M3 block scales, fp32 tensor scale)
 
 
 def build(force: bool = True) -> str:
@@ -46,7 +47,11 @@ def _load():
     lib.oracle_half_to_float.restype = f32
     lib.oracle_float_to_half.argtypes = [f32, i32]
     lib.oracle_float_to_half.restype = ctypes.c_uint16
-    lib.oracle_dequant_row.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    lib.oracle_dequant_row.argtypes = [vp, vp, vp, i32, i32, i32, f32, vp]
+    lib.oracle_e2m1_to_float.argtypes = [i32]
+    lib.oracle_e2m1_to_float.restype = f32
+    lib.oracle_e4m3_to_float.argtypes = [i32]
+    lib.oracle_e4m3_to_float.restype = f32
     lib.oracle_router_logits.argtypes = [vp, i32, i32, i32, vp, i32, vp]
     lib.oracle_select_topk.argtypes = [vp, i32, i32, i32, i32, vp, vp]
     lib.oracle_select_topk_grouped.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
@@ -54,7 +59,7 @@ def _load():
     lib.oracle_load_stats.argtypes = [vp, i32, vp, vp]
     lib.oracle_route_ex.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, f32, i32, vp, vp, vp, vp, vp]
     lib.oracle_layer_forward_ex.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, f32, i32, i32, vp, vp, vp, vp, vp,
-                                            vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+                                            vp, i32, i32, i32, f32, f32, vp, vp, vp, vp, vp, vp]
     lib.oracle_capacity_keep.argtypes = [vp, i32, i32, i32, i32, i32, vp]
     lib.oracle_sort_pairs_capped.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.oracle_token_entropy.argtypes = [vp, i32]
@@ -66,13 +71,13 @@ def _load():
     lib.oracle_route.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.oracle_sort_pairs.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.oracle_fuse_gate_up.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
-    lib.oracle_expert_ffn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp]
-    lib.oracle_expert_ffn_unfused.argtypes = [vp] + [vp] * 9 + [i32, i32, i32, i32, vp, vp]
+    lib.oracle_expert_ffn.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, vp, vp]
+    lib.oracle_expert_ffn_unfused.argtypes = [vp] + [vp] * 9 + [i32, i32, i32, i32, f32, f32, f32, vp, vp]
     lib.oracle_tokens_forward.argtypes = [vp, i32, i32, vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, i32,
-                                          i32, i32, vp, vp]
+                                          i32, i32, f32, f32, vp, vp]
     lib.oracle_round_output.argtypes = [vp, i64, i32, vp]
     lib.oracle_layer_forward.argtypes = [vp, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32,
-                                         vp, vp, vp, vp, vp, vp]
+                                         f32, f32, vp, vp, vp, vp, vp, vp]
     lib.oracle_num_threads.restype = i32
     lib.oracle_set_threads.argtypes = [i32]
     _lib = lib
@@ -115,13 +120,32 @@ def round_output(y_f32: np.ndarray, dtype: str) -> np.ndarray:
     return out
 
 
+def e2m1_to_float(code: int) -> float:
+    return float(_load().oracle_e2m1_to_float(int(code)))
+
+
+def e4m3_to_float(byte: int) -> float:
+    return float(_load().oracle_e4m3_to_float(int(byte)))
+
+
+def code_of(w) -> int:
+    """The oracle's `bits` code of a moe_inputs.Weights (NVFP4 or its width)."""
+    return NVFP4 if getattr(w, "fmt", "affine") == "nvfp4" else w.bits
+
+
+def tensor_scale(w) -> float:
+    return float(getattr(w, "tensor_scale", 1.0)) if w is not None else 1.0
+
+
 # -------------------------------------------------------------- steps ---
 
-def dequant_row(q_row, s_row, b_row, K: int, bits: int, gs: int = 64) -> np.ndarray:
+def dequant_row(q_row, s_row, b_row, K: int, bits: int, gs: int = 64, ts: float = 1.0) -> np.ndarray:
+    """bits 4/5/6/8/16, or NVFP4 (s_row: E4M3 bytes, gs 16, ts the tensor scale)."""
     out = np.empty(K, np.float32)
     qd = np.uint16 if bits == 16 else np.uint8
-    _load().oracle_dequant_row(_p(_c(q_row, qd)), _p(_c(s_row, np.uint16)), _p(_c(b_row, np.uint16)), K, bits, gs,
-                               _p(out))
+    sd = np.uint8 if bits == NVFP4 else np.uint16
+    _load().oracle_dequant_row(_p(_c(q_row, qd)), _p(_c(s_row, sd)), _p(_c(b_row, np.uint16)), K, bits, gs,
+                               float(ts), _p(out))
     return out
 
 
@@ -131,7 +155,8 @@ def dequant(w) -> np.ndarray:
     for e in range(w.E):
         for n in range(w.N):
             out[e, n] = dequant_row(w.q[e, n], None if w.scales is None else w.scales[e, n],
-                                    None if w.biases is None else w.biases[e, n], w.K, w.bits, w.group_size)
+                                    None if w.biases is None else w.biases[e, n], w.K, code_of(w), w.group_size,
+                                    tensor_scale(w))
     return out
 
 
@@ -242,15 +267,16 @@ def capacity_keep(idx: np.ndarray, k_used: int, E: int, capacity: int) -> np.nda
 
 def fuse_gate_up(gate, up):
     """[gate, up] concatenation of two moe_inputs.Weights along the output axis."""
-    from moe_inputs import Weights  # data container only
-    assert gate.bits == up.bits and gate.q.shape == up.q.shape
-    E, I, K, bits, gs = gate.E, gate.N, gate.K, gate.bits, gate.group_size
+    import dataclasses
+    assert code_of(gate) == code_of(up) and gate.q.shape == up.q.shape
+    assert tensor_scale(gate) == tensor_scale(up), "fused NVFP4 gate and up share one tensor scale"
+    E, I, K, bits, gs = gate.E, gate.N, gate.K, code_of(gate), gate.group_size
     oq = np.empty((E, 2 * I) + gate.q.shape[2:], gate.q.dtype)
-    os_ = None if gate.scales is None else np.empty((E, 2 * I, K // gs), np.uint16)
+    os_ = None if gate.scales is None else np.empty((E, 2 * I, K // gs), gate.scales.dtype)
     ob = None if gate.biases is None else np.empty((E, 2 * I, K // gs), np.uint16)
     _load().oracle_fuse_gate_up(_p(gate.q), _p(gate.scales), _p(gate.biases), _p(up.q), _p(up.scales), _p(up.biases),
                                 E, I, K, bits, gs, _p(oq), _p(os_), _p(ob))
-    return Weights(oq, os_, ob, E, 2 * I, K, bits, gs)
+    return dataclasses.replace(gate, q=oq, scales=os_, biases=ob, N=2 * I)
 
 
 def _expert_slice(w, e):
@@ -268,8 +294,8 @@ def expert_ffn(x_f32: np.ndarray, gate_up, down, e: int):
     dq, ds, db = _expert_slice(down, e)
     h = np.empty(I, np.float32)
     o = np.empty(H, np.float32)
-    _load().oracle_expert_ffn(_p(x_f32), _p(gq), _p(gs_), _p(gb), _p(dq), _p(ds), _p(db), H, I, down.bits,
-                              down.group_size, _p(h), _p(o))
+    _load().oracle_expert_ffn(_p(x_f32), _p(gq), _p(gs_), _p(gb), _p(dq), _p(ds), _p(db), H, I, code_of(down),
+                              down.group_size, tensor_scale(gate_up), tensor_scale(down), _p(h), _p(o))
     return h, o
 
 
@@ -281,8 +307,8 @@ def expert_ffn_unfused(x_f32: np.ndarray, gate, up, down, e: int):
     d = _expert_slice(down, e)
     h = np.empty(I, np.float32)
     o = np.empty(H, np.float32)
-    _load().oracle_expert_ffn_unfused(_p(x_f32), *[_p(v) for v in a + b + d], H, I, down.bits, down.group_size,
-                                      _p(h), _p(o))
+    _load().oracle_expert_ffn_unfused(_p(x_f32), *[_p(v) for v in a + b + d], H, I, code_of(down), down.group_size,
+                                      tensor_scale(gate), tensor_scale(up), tensor_scale(down), _p(h), _p(o))
     return h, o
 
 
@@ -300,7 +326,8 @@ def tokens_forward(x: np.ndarray, dtype: str, tokens: Sequence[int], idx: np.nda
     h = np.zeros((toks.size, kcap, I), np.float32) if want_h else None
     _load().oracle_tokens_forward(_p(x), DTYPE_CODE[dtype], H, _p(toks), toks.size, _p(idx), _p(w), kcap, k_used,
                                   _p(gate_up.q), _p(gate_up.scales), _p(gate_up.biases), _p(down.q),
-                                  _p(down.scales), _p(down.biases), I, down.bits, down.group_size, _p(y), _p(h))
+                                  _p(down.scales), _p(down.biases), I, code_of(down), down.group_size,
+                                  tensor_scale(gate_up), tensor_scale(down), _p(y), _p(h))
     return (y, h) if want_h else y
 
 
@@ -322,6 +349,7 @@ def layer_forward(x: np.ndarray, wr: np.ndarray, dtype: str, k: int, gate_up, do
     _load().oracle_layer_forward_ex(_p(x), DTYPE_CODE[dtype], T, H, _p(wr), E, k, _p(h), float(alpha), int(groups),
                                     int(capacity),
                                     _p(gate_up.q), _p(gate_up.scales), _p(gate_up.biases), _p(down.q),
-                                    _p(down.scales), _p(down.biases), down.K, down.bits, down.group_size, _p(y),
-                                    _p(yf), _p(idx), _p(w), _p(ku), _p(hm))
+                                    _p(down.scales), _p(down.biases), down.K, code_of(down), down.group_size,
+                                    tensor_scale(gate_up), tensor_scale(down), _p(y), _p(yf), _p(idx), _p(w),
+                                    _p(ku), _p(hm))
     return dict(y=y, y_f32=yf, idx=idx, w=w, k_used=int(ku[0]), h_mean=float(hm[0]))

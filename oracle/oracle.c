@@ -26,6 +26,12 @@
  *   dequant     affine group quantisation, w = scale * q + bias with one
  *               scale/bias per row and 64-column group (oMLX page, "融合原理":
  *               scales are packed per output row).
+ *   nvfp4       the oMLX page names an nvfp4 weight mode (its list of modes
+ *               under "如何验证正确性") and gives no layout; read as NVIDIA's
+ *               published NVFP4: E2M1 codes two per byte (even column in the
+ *               low nibble), one FP8 E4M3 scale per row and 16 consecutive
+ *               columns, one fp32 scale per tensor, w = (ts * s) * e2m1(q)
+ *               in fp32 (two roundings), no bias.
  *   gate_up     the gate and up projections concatenated along the output
  *               axis, [gate, up] order, then split (oMLX page, steps 3 and 4).
  *   SwiGLU      h = silu(g) * u, silu(g) = g / (1 + e^-g).
@@ -119,6 +125,32 @@ uint16_t oracle_float_to_half(float f, int dtype) {
   return (uint16_t)((sign << 15) | mag);
 }
 
+/* ------------------------------------------- NVFP4 element formats ---- */
+
+enum { ORACLE_NVFP4 = 0x104 }; /* `bits` code of NVFP4 weights: 4-bit codes of the second format */
+
+/* E2M1: sign bit 3, two exponent bits (bias 1), one mantissa bit; exponent
+ * field 0 is subnormal (0 or 0.5).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+float oracle_e2m1_to_float(int code) {
+  int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  float v = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+  return sign ? -v : v;
+}
+
+/* FP8 E4M3 (the OCP "fn" variant): sign bit 7, four exponent bits (bias 7),
+ * three mantissa bits; exponent field 0 is subnormal (m * 2^-9); 0x7F and
+ * 0xFF are NaN and there are no infinities (largest finite 448). */
+float oracle_e4m3_to_float(int byte) {
+  int sign = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+  if ((byte & 0x7F) == 0x7F) return NAN;
+  float v = e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+  return sign ? -v : v;
+}
+
+static int code_bits(int bits) { return bits == ORACLE_NVFP4 ? 4 : bits; }
+/* bytes of one scale: E4M3 bytes for NVFP4, fp16 otherwise */
+static int scale_bytes(int bits) { return bits == ORACLE_NVFP4 ? 1 : 2; }
+
 /* -------------------------------------------------------- dequant (A5) -- */
 
 /*
@@ -128,15 +160,28 @@ uint16_t oracle_float_to_half(float f, int dtype) {
  * unsigned.  w = s*q + b in fp32
  * (two roundings), s and b fp16, one pair per 64-column group.
  * bits 16: the row is fp16 values, copied.
+ * bits ORACLE_NVFP4: E2M1 codes packed as 4-bit codes, s_row the row's E4M3
+ * block scales (one byte per gs = 16 columns), b_row unused, ts the tensor
+ * scale: w = (ts * e4m3(s)) * e2m1(q) in fp32.
  */
-void oracle_dequant_row(const void* q_row, const uint16_t* s_row, const uint16_t* b_row, int K, int bits, int gs,
-                        float* out) {
+void oracle_dequant_row(const void* q_row, const void* s_row, const uint16_t* b_row, int K, int bits, int gs,
+                        float ts, float* out) {
   if (bits == 16) {
     const uint16_t* w = (const uint16_t*)q_row;
     for (int k = 0; k < K; ++k) out[k] = oracle_half_to_float(w[k], ORACLE_F16);
     return;
   }
   const uint8_t* q = (const uint8_t*)q_row;
+  if (bits == ORACLE_NVFP4) {
+    const uint8_t* sb = (const uint8_t*)s_row;
+    for (int k = 0; k < K; ++k) {
+      int code = (q[k / 2] >> (4 * (k & 1))) & 15;
+      float s = ts * oracle_e4m3_to_float(sb[k / gs]);
+      out[k] = s * oracle_e2m1_to_float(code);
+    }
+    return;
+  }
+  const uint16_t* s16 = (const uint16_t*)s_row;
   for (int k = 0; k < K; ++k) {
     int code;
     if (bits == 4) {
@@ -150,14 +195,14 @@ void oracle_dequant_row(const void* q_row, const uint16_t* s_row, const uint16_t
     } else {
       code = q[k];
     }
-    float s = oracle_half_to_float(s_row[k / gs], ORACLE_F16);
+    float s = oracle_half_to_float(s16[k / gs], ORACLE_F16);
     float b = oracle_half_to_float(b_row[k / gs], ORACLE_F16);
     float sq = s * (float)code;
     out[k] = sq + b;
   }
 }
 
-static int64_t row_bytes_of(int K, int bits) { return (int64_t)K * bits / 8; }
+static int64_t row_bytes_of(int K, int bits) { return (int64_t)K * code_bits(bits) / 8; }
 
 /* ---------------------------------------------------------- router (A1) -- */
 
@@ -438,20 +483,26 @@ void oracle_sort_pairs_capped(const int32_t* idx, int T, int kcap, int k_used, i
 
 /*
  * Concatenate gate [E, I, K] and up [E, I, K] along the output axis into
- * gate_up [E, 2I, K], gate rows first; weights, scales and biases alike.
+ * gate_up [E, 2I, K], gate rows first; weights, scales and biases alike
+ * (NVFP4: codes and block scales; the two tensors must share their tensor
+ * scale, which the caller keeps).
  */
-void oracle_fuse_gate_up(const void* gq, const uint16_t* gs_, const uint16_t* gb, const void* uq, const uint16_t* us,
-                         const uint16_t* ub, int E, int I, int K, int bits, int gsz, void* oq, uint16_t* os,
+void oracle_fuse_gate_up(const void* gq, const void* gs_, const uint16_t* gb, const void* uq, const void* us,
+                         const uint16_t* ub, int E, int I, int K, int bits, int gsz, void* oq, void* os,
                          uint16_t* ob) {
   int64_t rb = row_bytes_of(K, bits);
-  int64_t ng = K / gsz;
+  int64_t ng = K / gsz, sb = scale_bytes(bits);
   for (int e = 0; e < E; ++e) {
     uint8_t* dq = (uint8_t*)oq + (int64_t)e * 2 * I * rb;
     memcpy(dq, (const uint8_t*)gq + (int64_t)e * I * rb, (size_t)(I * rb));
     memcpy(dq + I * rb, (const uint8_t*)uq + (int64_t)e * I * rb, (size_t)(I * rb));
     if (bits != 16) {
-      memcpy(os + (int64_t)e * 2 * I * ng, gs_ + (int64_t)e * I * ng, sizeof(uint16_t) * (size_t)(I * ng));
-      memcpy(os + ((int64_t)e * 2 * I + I) * ng, us + (int64_t)e * I * ng, sizeof(uint16_t) * (size_t)(I * ng));
+      uint8_t* ds = (uint8_t*)os;
+      memcpy(ds + (int64_t)e * 2 * I * ng * sb, (const uint8_t*)gs_ + (int64_t)e * I * ng * sb, (size_t)(I * ng * sb));
+      memcpy(ds + ((int64_t)e * 2 * I + I) * ng * sb, (const uint8_t*)us + (int64_t)e * I * ng * sb,
+             (size_t)(I * ng * sb));
+    }
+    if (bits != 16 && bits != ORACLE_NVFP4) {
       memcpy(ob + (int64_t)e * 2 * I * ng, gb + (int64_t)e * I * ng, sizeof(uint16_t) * (size_t)(I * ng));
       memcpy(ob + ((int64_t)e * 2 * I + I) * ng, ub + (int64_t)e * I * ng, sizeof(uint16_t) * (size_t)(I * ng));
     }
@@ -462,13 +513,16 @@ void oracle_fuse_gate_up(const void* gq, const uint16_t* gs_, const uint16_t* gb
 
 typedef struct {
   const void* q;
-  const uint16_t* s;
+  const void* s;
   const uint16_t* b;
   int K, bits, gs;
+  float ts;  /* NVFP4 tensor scale */
 } row_src;
 
 static const void* rq(const row_src* r, int64_t row) { return (const uint8_t*)r->q + row * row_bytes_of(r->K, r->bits); }
-static const uint16_t* rs(const row_src* r, int64_t row) { return r->s ? r->s + row * (r->K / r->gs) : NULL; }
+static const void* rs(const row_src* r, int64_t row) {
+  return r->s ? (const uint8_t*)r->s + row * (r->K / r->gs) * scale_bytes(r->bits) : NULL;
+}
 static const uint16_t* rbias(const row_src* r, int64_t row) { return r->b ? r->b + row * (r->K / r->gs) : NULL; }
 
 /* out[n] = sum_k v[k] * W[row0 + n, k] for n in [0, N), sequential fp32 sums */
@@ -479,7 +533,7 @@ static void matvec(const row_src* W, int64_t row0, int N, const float* v, float*
     float* wrow = (float*)malloc(sizeof(float) * (size_t)K);
 #pragma omp for schedule(static)
     for (int n = 0; n < N; ++n) {
-      oracle_dequant_row(rq(W, row0 + n), rs(W, row0 + n), rbias(W, row0 + n), K, W->bits, W->gs, wrow);
+      oracle_dequant_row(rq(W, row0 + n), rs(W, row0 + n), rbias(W, row0 + n), K, W->bits, W->gs, W->ts, wrow);
       float acc = 0.0f;
       for (int k = 0; k < K; ++k) {
         float p = v[k] * wrow[k];
@@ -496,11 +550,12 @@ static float silu(float g) { return g / (1.0f + expf(-g)); }
 /*
  * One (token, expert): x [H] fp32 values; gate_up rows [2I, H] of this expert
  * (gate first), down rows [H, I].  h_out [I] (may be NULL), o [H].
+ * gu_ts, d_ts: the tensor scales of NVFP4 weights (unused otherwise).
  */
-void oracle_expert_ffn(const float* x, const void* guq, const uint16_t* gus, const uint16_t* gub, const void* dq,
-                       const uint16_t* ds, const uint16_t* db, int H, int I, int bits, int gsz, float* h_out,
-                       float* o) {
-  row_src gu = {guq, gus, gub, H, bits, gsz}, dn = {dq, ds, db, I, bits, gsz};
+void oracle_expert_ffn(const float* x, const void* guq, const void* gus, const uint16_t* gub, const void* dq,
+                       const void* ds, const uint16_t* db, int H, int I, int bits, int gsz, float gu_ts, float d_ts,
+                       float* h_out, float* o) {
+  row_src gu = {guq, gus, gub, H, bits, gsz, gu_ts}, dn = {dq, ds, db, I, bits, gsz, d_ts};
   float* gu_v = (float*)malloc(sizeof(float) * 2 * (size_t)I);
   float* h = (float*)malloc(sizeof(float) * (size_t)I);
   matvec(&gu, 0, 2 * I, x, gu_v);
@@ -514,11 +569,13 @@ void oracle_expert_ffn(const float* x, const void* guq, const uint16_t* gus, con
   free(h);
 }
 
-/* the same with separate gate [I, H] and up [I, H] rows */
-void oracle_expert_ffn_unfused(const float* x, const void* gq, const uint16_t* gs_, const uint16_t* gb, const void* uq,
-                               const uint16_t* us, const uint16_t* ub, const void* dq, const uint16_t* ds,
-                               const uint16_t* db, int H, int I, int bits, int gsz, float* h_out, float* o) {
-  row_src ga = {gq, gs_, gb, H, bits, gsz}, ua = {uq, us, ub, H, bits, gsz}, dn = {dq, ds, db, I, bits, gsz};
+/* the same with separate gate [I, H] and up [I, H] rows (and tensor scales) */
+void oracle_expert_ffn_unfused(const float* x, const void* gq, const void* gs_, const uint16_t* gb, const void* uq,
+                               const void* us, const uint16_t* ub, const void* dq, const void* ds, const uint16_t* db,
+                               int H, int I, int bits, int gsz, float g_ts, float u_ts, float d_ts, float* h_out,
+                               float* o) {
+  row_src ga = {gq, gs_, gb, H, bits, gsz, g_ts}, ua = {uq, us, ub, H, bits, gsz, u_ts},
+          dn = {dq, ds, db, I, bits, gsz, d_ts};
   float* g = (float*)malloc(sizeof(float) * (size_t)I);
   float* u = (float*)malloc(sizeof(float) * (size_t)I);
   float* h = (float*)malloc(sizeof(float) * (size_t)I);
@@ -541,11 +598,11 @@ void oracle_expert_ffn_unfused(const float* x, const void* gq, const uint16_t* g
  * h_out (may be NULL): [n, kcap, I] SwiGLU outputs, rows of unused slots untouched.
  */
 void oracle_tokens_forward(const uint16_t* x, int dtype, int H, const int32_t* tokens, int n, const int32_t* idx,
-                           const float* w, int kcap, int k_used, const void* guq, const uint16_t* gus,
-                           const uint16_t* gub, const void* dq, const uint16_t* ds, const uint16_t* db, int I,
-                           int bits, int gsz, float* y_f32, float* h_out) {
+                           const float* w, int kcap, int k_used, const void* guq, const void* gus,
+                           const uint16_t* gub, const void* dq, const void* ds, const uint16_t* db, int I,
+                           int bits, int gsz, float gu_ts, float d_ts, float* y_f32, float* h_out) {
   int64_t gu_rows = 2 * (int64_t)I, rbh = row_bytes_of(H, bits), rbi = row_bytes_of(I, bits);
-  int64_t ngh = H / gsz, ngi = I / gsz;
+  int64_t ngh = H / gsz, ngi = I / gsz, sb = scale_bytes(bits);
   float* xf = (float*)malloc(sizeof(float) * (size_t)H);
   float* o = (float*)malloc(sizeof(float) * (size_t)H);
   for (int i = 0; i < n; ++i) {
@@ -558,13 +615,13 @@ void oracle_tokens_forward(const uint16_t* x, int dtype, int H, const int32_t* t
       if (e < 0) continue; /* a dropped pair (capacity) contributes nothing */
       float ws = w[(int64_t)t * kcap + s];
       const uint8_t* eq = (const uint8_t*)guq + (int64_t)e * gu_rows * rbh;
-      const uint16_t* es = gus ? gus + (int64_t)e * gu_rows * ngh : NULL;
+      const uint8_t* es = gus ? (const uint8_t*)gus + (int64_t)e * gu_rows * ngh * sb : NULL;
       const uint16_t* eb = gub ? gub + (int64_t)e * gu_rows * ngh : NULL;
       const uint8_t* edq = (const uint8_t*)dq + (int64_t)e * H * rbi;
-      const uint16_t* eds = ds ? ds + (int64_t)e * H * ngi : NULL;
+      const uint8_t* eds = ds ? (const uint8_t*)ds + (int64_t)e * H * ngi * sb : NULL;
       const uint16_t* edb = db ? db + (int64_t)e * H * ngi : NULL;
       float* hrow = h_out ? h_out + ((int64_t)i * kcap + s) * I : NULL;
-      oracle_expert_ffn(xf, eq, es, eb, edq, eds, edb, H, I, bits, gsz, hrow, o);
+      oracle_expert_ffn(xf, eq, es, eb, edq, eds, edb, H, I, bits, gsz, gu_ts, d_ts, hrow, o);
       for (int h = 0; h < H; ++h) {
         float c = ws * o[h];
         y[h] = y[h] + c;
@@ -587,9 +644,9 @@ void oracle_round_output(const float* y_f32, int64_t n, int dtype, uint16_t* y) 
  */
 void oracle_layer_forward_ex(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k,
                              const float* health, float alpha, int groups, int capacity, const void* guq,
-                             const uint16_t* gus, const uint16_t* gub, const void* dq, const uint16_t* ds,
-                             const uint16_t* db, int I, int bits, int gsz, uint16_t* y, float* y_f32, int32_t* idx,
-                             float* w, int32_t* k_used, float* h_mean) {
+                             const void* gus, const uint16_t* gub, const void* dq, const void* ds,
+                             const uint16_t* db, int I, int bits, int gsz, float gu_ts, float d_ts, uint16_t* y,
+                             float* y_f32, int32_t* idx, float* w, int32_t* k_used, float* h_mean) {
   int ku = 0;
   oracle_route_ex(x, dtype, T, H, wr, E, k, health, alpha, groups, idx, w, &ku, h_mean, NULL);
   if (k_used) *k_used = ku;
@@ -603,8 +660,8 @@ void oracle_layer_forward_ex(const uint16_t* x, int dtype, int T, int H, const u
   int32_t* tokens = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
   for (int t = 0; t < T; ++t) tokens[t] = t;
   float* yf = y_f32 ? y_f32 : (float*)malloc(sizeof(float) * (size_t)T * H);
-  oracle_tokens_forward(x, dtype, H, tokens, T, idx_kept, w, kcap, ku, guq, gus, gub, dq, ds, db, I, bits, gsz, yf,
-                        NULL);
+  oracle_tokens_forward(x, dtype, H, tokens, T, idx_kept, w, kcap, ku, guq, gus, gub, dq, ds, db, I, bits, gsz, gu_ts,
+                        d_ts, yf, NULL);
   oracle_round_output(yf, (int64_t)T * H, dtype, y);
   if (!y_f32) free(yf);
   free(tokens);
@@ -613,11 +670,11 @@ void oracle_layer_forward_ex(const uint16_t* x, int dtype, int T, int H, const u
 }
 
 void oracle_layer_forward(const uint16_t* x, int dtype, int T, int H, const uint16_t* wr, int E, int k,
-                          const void* guq, const uint16_t* gus, const uint16_t* gub, const void* dq,
-                          const uint16_t* ds, const uint16_t* db, int I, int bits, int gsz, uint16_t* y,
+                          const void* guq, const void* gus, const uint16_t* gub, const void* dq, const void* ds,
+                          const uint16_t* db, int I, int bits, int gsz, float gu_ts, float d_ts, uint16_t* y,
                           float* y_f32, int32_t* idx, float* w, int32_t* k_used, float* h_mean) {
-  oracle_layer_forward_ex(x, dtype, T, H, wr, E, k, NULL, 0.0f, 0, 0, guq, gus, gub, dq, ds, db, I, bits, gsz, y,
-                          y_f32, idx, w, k_used, h_mean);
+  oracle_layer_forward_ex(x, dtype, T, H, wr, E, k, NULL, 0.0f, 0, 0, guq, gus, gub, dq, ds, db, I, bits, gsz, gu_ts,
+                          d_ts, y, y_f32, idx, w, k_used, h_mean);
 }
 
 int oracle_num_threads(void) {

@@ -32,9 +32,29 @@ def codes(w: mi.Weights) -> np.ndarray:
     return w.q.astype(np.int64)
 
 
+# E2M1 magnitudes of codes 0..7 (NVIDIA's published NVFP4 element format);
+# codes 8..15 are the same values negated (sign bit 3)
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_64(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, np.int64)
+    return np.where(c & 8, -1.0, 1.0) * E2M1_MAGNITUDES[c & 7]
+
+
+def e4m3_64(b: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 bytes decoded by torch's float8_e4m3fn."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(b, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
 def dequant64(w: mi.Weights) -> np.ndarray:
     if w.bits == 16:
         return half64(w.q, "f16")
+    if w.fmt == "nvfp4":
+        s = np.repeat(e4m3_64(w.scales), 16, axis=-1)
+        return float(w.tensor_scale) * s * e2m1_64(codes(w))
     q = codes(w).astype(np.float64)
     s = np.repeat(half64(w.scales, "f16"), w.group_size, axis=-1)
     b = np.repeat(half64(w.biases, "f16"), w.group_size, axis=-1)

@@ -15,7 +15,7 @@ import torch
 import moe_inputs as mi
 import oracle
 from conftest import golden_path
-from ref64 import dense_layer64, dequant64, entropy64, half64, rel_l2, select64, silu64
+from ref64 import dense_layer64, dequant64, e4m3_64, entropy64, half64, rel_l2, select64, silu64
 
 U = 2.0 ** -24  # unit roundoff of fp32
 
@@ -108,6 +108,80 @@ def test_dequant_matches_fp64_statement(bits):
     want = dequant64(w)
     # two fp32 roundings of s*q + b
     assert np.all(np.abs(got - want) <= 2 * U * (np.abs(want) + 1e-3))
+
+
+# --------------------------------------------------------------- NVFP4 --
+
+def test_e4m3_decode_matches_torch_float8_e4m3fn():
+    got = np.array([oracle.e4m3_to_float(b) for b in range(256)], np.float64)
+    want = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2  # 0x7F and 0xFF
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_e2m1_decode_is_the_published_table():
+    # NVFP4 element values, NVIDIA's format definition: codes 0..7 are
+    # 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 is the sign
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    got = [oracle.e2m1_to_float(c) for c in range(16)]
+    assert got == table
+    assert [math.copysign(1, g) for g in got] == [math.copysign(1, v) for v in table]
+
+
+def _read_nvfp4_cases():
+    cases, cur = [], None
+    for line in open(golden_path("nvfp4_blocks.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        tag, *rest = line.split()
+        if tag == "case":
+            cur = dict(name=rest[0], ts=float(rest[1]), s=[int(v, 16) for v in rest[2:6]])
+            cases.append(cur)
+        elif tag == "codes":
+            cur["codes"] = [int(v, 16) for v in rest]
+        elif tag == "expect":
+            cur["expect"] = [float(v) for v in rest]
+    return cases
+
+
+@pytest.mark.parametrize("case", _read_nvfp4_cases(), ids=lambda c: c["name"])
+def test_nvfp4_dequant_golden(case):
+    codes = np.array(case["codes"], np.uint8)
+    q = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)  # even column -> low nibble
+    got = oracle.dequant_row(q, np.array(case["s"], np.uint8), None, 64, oracle.NVFP4, 16, case["ts"])
+    assert np.array_equal(got, np.array(case["expect"], np.float32))
+
+
+def test_nvfp4_requantize_returns_same_codes():
+    w = mi.nvfp4_weights(77, 2, 2, 8, 256)
+    deq = oracle.dequant(w)
+    q2, s2, ts = mi.quantize_rows_nvfp4(deq.reshape(-1, 256).astype(np.float64), ts=w.tensor_scale)
+    assert np.array_equal(q2.reshape(w.q.shape), w.q)
+    assert np.array_equal(s2.reshape(w.scales.shape), w.scales)
+
+
+def test_nvfp4_dequant_matches_fp64_statement():
+    w = mi.nvfp4_weights(5, 3, 2, 16, 192)
+    got = oracle.dequant(w).astype(np.float64)
+    want = dequant64(w)
+    # two fp32 roundings: ts * s, then times the E2M1 value
+    assert np.all(np.abs(got - want) <= 2 * U * np.abs(want))
+    # every block uses its own scale: the largest code of a block is +-6
+    assert np.all(np.abs(want).reshape(2, 16, 12, 16).max(-1) > 0)
+
+
+def test_nvfp4_quantiser_error_within_half_a_step():
+    # the generator's quantiser rounds to the nearest E2M1 value of each
+    # block's grid: the error is at most half the largest gap (2 steps)
+    rng = np.random.default_rng(4)
+    w64 = rng.standard_normal((6, 128)) * 0.02
+    q, s, ts = mi.quantize_rows_nvfp4(w64)
+    back = np.stack([oracle.dequant_row(q[r], s[r], None, 128, oracle.NVFP4, 16, ts) for r in range(6)])
+    step = ts * np.repeat(e4m3_64(s), 16, axis=-1)
+    assert np.all(np.abs(back - w64) <= step * 1.0 + 1e-9)
 
 
 # -------------------------------------------------------------- router --
@@ -303,9 +377,9 @@ def test_sort_pairs_is_stable_counting_sort(T, kcap, ku, E):
 
 # ------------------------------------------------------------------ FFN --
 
-@pytest.mark.parametrize("bits", [4, 8, 16])
+@pytest.mark.parametrize("bits", [4, 8, 16, "nvfp4"])
 def test_fused_gate_up_bit_identical_to_separate(bits):
-    inp = mi.make_inputs("tiny", bits=bits)
+    inp = mi.make_inputs("tiny", fmt="nvfp4") if bits == "nvfp4" else mi.make_inputs("tiny", bits=bits)
     gu = oracle.fuse_gate_up(inp.gate, inp.up)
     assert gu.q.shape[1] == 2 * inp.I
     assert np.array_equal(gu.q[:, :inp.I], inp.gate.q) and np.array_equal(gu.q[:, inp.I:], inp.up.q)
@@ -385,6 +459,8 @@ def test_all_experts_selected_is_the_dense_softmax_mixture():
     dict(name="entropy", T=8, H=256, E=8, I=128, bits=4),
     dict(name="decode_b1", T=3, H=256, E=8, I=192, bits=6),
     dict(name="decode_b1", T=2, H=192, E=8, I=256, bits=5),
+    dict(name="tiny", fmt="nvfp4"),
+    dict(name="prefill", T=24, H=128, E=16, I=192, fmt="nvfp4"),
 ], ids=lambda kw: "-".join("%s%s" % (k, v) for k, v in kw.items()))
 def test_layer_matches_dense_fp64_brute_force(kw):
     kw = dict(kw)
