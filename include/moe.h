@@ -118,6 +118,21 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
  * group_size must be 64.  K must be a multiple of 64.  q, scales and biases
  * must be 16-byte aligned.
  *
+ * format == MOE_FMT_NVFP4 (a reading: the oMLX page names an nvfp4 weight
+ * mode, "如何验证正确性", with no layout; this is NVIDIA's published NVFP4):
+ *   bits 4, group_size 16, biases NULL, both paths.
+ *               q      uint8 [rows, K/2], two E2M1 codes per byte, the even
+ *                      column in the low nibble; code bit 3 is the sign,
+ *                      codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ *               scales uint8 [rows, K/16], one FP8 E4M3 (OCP "fn": bias 7,
+ *                      448 largest, 0x7F/0xFF NaN) block scale per 16 columns
+ *               tensor_scale  fp32, one per tensor (finite, > 0)
+ *               w[n, k] = tensor_scale * e4m3(scales[n, k/16]) * e2m1(q[n, k])
+ *   The kernels form e2m1 * e4m3 exactly in fp16 and apply tensor_scale to
+ *   the fp32 sums.  A fused gate_up tensor has one tensor_scale; separate
+ *   gate and up tensors may differ.
+ * format == MOE_FMT_AFFINE (0): the forms above; tensor_scale is ignored.
+ *
  * packed_sb (optional, bits 4 to 8): the same scales and biases repacked for
  * the batched path by moe_pack_sb, pointing at the tensor's (or view's) first
  * row like q.  Layout: for expert e, group pair p (groups 2p and 2p+1; a
@@ -128,8 +143,12 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
  * per column.  NULL: the batched path repacks them into the workspace on every
  * call.  The gate and up views of a fused tensor share its packed_sb (the up
  * view's pointer is the gate view's plus inter*8 bytes).  Set for fp16
- * weights, it is refused with MOE_ERR_QUANT.
+ * weights, it is refused with MOE_ERR_QUANT.  NVFP4 weights use the same
+ * 8-byte slots for {the four E4M3 block scales of group 2p, those of group
+ * 2p+1} (two little-endian 32-bit words, block 4g+i in byte i).
  */
+typedef enum { MOE_FMT_AFFINE = 0, MOE_FMT_NVFP4 = 1 } moe_weight_format;
+
 typedef struct {
   const void* q;
   const void* scales;
@@ -141,6 +160,8 @@ typedef struct {
   int32_t group_size;
   int64_t expert_stride_rows;
   const void* packed_sb;
+  int32_t format;      /* moe_weight_format */
+  float tensor_scale;  /* NVFP4 only */
 } moe_weights;
 
 /*

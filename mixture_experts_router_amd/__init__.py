@@ -51,7 +51,11 @@ class MoeError(RuntimeError):
 class CWeights(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bits", ctypes.c_int32),
-                ("group_size", ctypes.c_int32), ("expert_stride_rows", ctypes.c_int64), ("packed_sb", ctypes.c_void_p)]
+                ("group_size", ctypes.c_int32), ("expert_stride_rows", ctypes.c_int64), ("packed_sb", ctypes.c_void_p),
+                ("format", ctypes.c_int32), ("tensor_scale", ctypes.c_float)]
+
+
+FMT_AFFINE, FMT_NVFP4 = 0, 1
 
 
 class CRouteOpts(ctypes.Structure):
@@ -161,6 +165,9 @@ class Weights:
     (code k at bits b*k..b*k+b-1 of the row's little-endian bit stream, b =
     bits; decode path only); bits 8: q uint8 [E, N, K];
     bits 16: q float16 [E, N, K].  scales/biases float16 [E, N, K/64] (None for bits 16).
+    ``fmt="nvfp4"`` (bits 4, group_size 16): q uint8 [E, N, K/2] E2M1 codes
+    (even column in the low nibble), scales uint8 [E, N, K/16] E4M3 block
+    scales, biases None, ``tensor_scale`` the fp32 per-tensor scale.
     ``row_offset``/``stride`` describe a view (the gate or up half of a fused
     tensor): rows start ``row_offset`` rows in, experts are ``stride`` rows apart.
     ``packed_sb`` (optional, uint8): the scales and biases repacked by pack_sb
@@ -178,6 +185,8 @@ class Weights:
     stride: Optional[int] = None
     row_offset: int = 0
     packed_sb: Optional[torch.Tensor] = None
+    fmt: str = "affine"  # "affine" | "nvfp4"
+    tensor_scale: float = 1.0
 
     _cstruct: Optional[CWeights] = dataclasses.field(default=None, repr=False, compare=False)
 
@@ -187,11 +196,14 @@ class Weights:
         stride = self.N if self.stride is None else self.stride
         rb = self.K * self.bits // 8
         ng = self.K // self.group_size
+        f4 = self.fmt == "nvfp4"
+        srb = ng if f4 else ng * 2  # scale bytes per row
         q = self.q.data_ptr() + self.row_offset * rb
-        s = None if self.scales is None else self.scales.data_ptr() + self.row_offset * ng * 2
-        b = None if self.biases is None else self.biases.data_ptr() + self.row_offset * ng * 2
+        s = None if self.scales is None else self.scales.data_ptr() + self.row_offset * srb
+        b = None if self.biases is None else self.biases.data_ptr() + self.row_offset * srb
         sb = None if self.packed_sb is None else self.packed_sb.data_ptr() + self.row_offset * 8
-        self._cstruct = CWeights(q, s, b, self.E, self.N, self.K, self.bits, self.group_size, stride, sb)
+        self._cstruct = CWeights(q, s, b, self.E, self.N, self.K, self.bits, self.group_size, stride, sb,
+                                 FMT_NVFP4 if f4 else FMT_AFFINE, float(self.tensor_scale))
         return self._cstruct
 
     def split_gate_up(self):
@@ -366,12 +378,14 @@ def fuse_gate_up(gate: Weights, up: Weights, stream=None) -> Weights:
     q = torch.empty(qshape, dtype=gate.q.dtype, device=dev)
     s = b = None
     if gate.scales is not None:
-        s = torch.empty((E, 2 * I, K // gate.group_size), dtype=torch.float16, device=dev)
-        b = torch.empty_like(s)
+        sdt = torch.uint8 if gate.fmt == "nvfp4" else torch.float16
+        s = torch.empty((E, 2 * I, K // gate.group_size), dtype=sdt, device=dev)
+    if gate.biases is not None:
+        b = torch.empty((E, 2 * I, K // gate.group_size), dtype=torch.float16, device=dev)
     cg, cu = gate.c(), up.c()
     st = lib().moe_fuse_gate_up(ctypes.byref(cg), ctypes.byref(cu), _ptr(q), _ptr(s), _ptr(b), _stream(stream))
     _check(st, "moe_fuse_gate_up")
-    return Weights(q, s, b, E, 2 * I, K, bits, gate.group_size)
+    return Weights(q, s, b, E, 2 * I, K, bits, gate.group_size, fmt=gate.fmt, tensor_scale=gate.tensor_scale)
 
 
 def pack_sb(w: Weights, stream=None) -> Weights:

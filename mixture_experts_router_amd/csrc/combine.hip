@@ -217,14 +217,35 @@ __global__ __launch_bounds__(256) void pack_sb_kernel(const uint16_t* __restrict
   *(u32x2*)(dst + (ep * dst_stride + dst_row0 + n) * 8) = u32x2{s0 | (s1 << 16), b0 | (b1 << 16)};
 }
 
+// NVFP4: slot (e, p, n) holds the four E4M3 block scales of group 2p (one
+// 32-bit word of the row's scale bytes) and those of group 2p+1 (0 if none)
+__global__ __launch_bounds__(256) void pack_sb_f4_kernel(const uint32_t* __restrict__ s, int N, int ng, int NP,
+                                                         int64_t src_stride, uint8_t* dst, int64_t dst_stride,
+                                                         int64_t dst_row0, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int n = (int)(i % N);
+  const int64_t ep = i / N;
+  const int p = (int)(ep % NP);
+  const int64_t e = ep / NP;
+  const int64_t src = (e * src_stride + n) * ng;  // the row's group words
+  const int g0 = 2 * p, g1 = 2 * p + 1;
+  const uint32_t w0 = s[src + g0], w1 = g1 < ng ? s[src + g1] : 0u;
+  *(u32x2*)(dst + (ep * dst_stride + dst_row0 + n) * 8) = u32x2{w0, w1};
+}
+
 hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, int K, int64_t src_stride, uint8_t* dst,
-                          int64_t dst_stride, int64_t dst_row0, hipStream_t st) {
+                          int64_t dst_stride, int64_t dst_row0, hipStream_t st, bool nvfp4) {
   const int ng = K / 64, NP = (ng + 1) / 2;
   const int64_t total = (int64_t)E * NP * N;
   if (total <= 0) return hipSuccess;
   if ((total + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidValue;
-  launch_kernel(pack_sb_kernel, (unsigned)((total + 255) / 256), 256, 0, st, s, b, N, ng, NP, src_stride, dst,
-                dst_stride, dst_row0, total);
+  if (nvfp4)
+    launch_kernel(pack_sb_f4_kernel, (unsigned)((total + 255) / 256), 256, 0, st, (const uint32_t*)s, N, ng, NP,
+                  src_stride, dst, dst_stride, dst_row0, total);
+  else
+    launch_kernel(pack_sb_kernel, (unsigned)((total + 255) / 256), 256, 0, st, s, b, N, ng, NP, src_stride, dst,
+                  dst_stride, dst_row0, total);
   return hipGetLastError();
 }
 

@@ -203,6 +203,25 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
+// --------------------------------------------------------------- NVFP4 ---
+//
+// The E2M1 codes of a 32-bit word (eight codes, column 2i in the low nibble
+// of byte i) as four fp16 pairs (columns 2i, 2i+1), exact: the gfx950
+// conversion with a scale of 1 (the instruction takes only the exponent of
+// its scale operand, so block scales are applied separately).
+__device__ __forceinline__ void e2m1_word_to_pairs(uint32_t w, uint32_t (&p)[4]) {
+  p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+  p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+  p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+  p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+}
+
+// FP8 E4M3 byte B of v (OCP "fn" format on gfx950), exact in fp32
+template <int B>
+__device__ __forceinline__ float e4m3_byte(uint32_t v) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)v, B);
+}
+
 // -------------------------------------------------------------- SwiGLU ---
 
 // The one SwiGLU used by every path (fused epilogues and the standalone

@@ -28,7 +28,10 @@
 // group, then the next group's loads are issued and the stage is consumed:
 // B codes read once per group, dequantised per MFMA k-step in registers
 // (w = fma(q, s, b) in fp16, one rounding), v_mfma_f32_32x32x16_f16 with fp32
-// accumulation.
+// accumulation.  NVFP4 weights stage like 4-bit codes; each code pair becomes
+// an exact fp16 E2M1 pair (one conversion instruction) times its block's
+// E4M3 scale (exact in fp16: at most six significant bits), and the tensor
+// scale multiplies the fp32 sums in the epilogue.
 //
 // Each output element's reduction runs over the same k order whichever
 // instantiation, tile or column position computes it, so the fused and
@@ -110,7 +113,7 @@ int gemm_max_mtiles(int P, int E, int bm) { return (P + bm - 1) / bm + E; }
 // (gate and up).
 template <int BITS, int KG, int NSUB>
 struct BGeo {
-  static constexpr int ROW = 64 * BITS / 8;          // code bytes of one row per group: 32 / 40 / 48 / 64 / 128
+  static constexpr int ROW = 64 * code_bits(BITS) / 8;  // code bytes of one row per group: 32 / 40 / 48 / 64 / 128
   static constexpr int SEG = KG * ROW;               // bytes of one row per stage
   static constexpr int LPR = SEG / 16;               // 16-byte pieces per row
   static constexpr bool WHOLE = 64 % LPR == 0;       // an instruction covers whole rows
@@ -259,6 +262,25 @@ __device__ __forceinline__ f16x8 dequant_b_odd(const uint32_t* w, int j, uint32_
   return __builtin_bit_cast(f16x8, v);
 }
 
+// NVFP4: k-step J of the lane's share of a group, 8 codes in column order
+// in one word of c; sv holds the E4M3 scales of the lane's two 16-column
+// blocks (low byte first), k-steps 2i and 2i+1 using block i.
+// w = fp16(e2m1) * fp16(e4m3), exact.
+template <int J>
+__device__ __forceinline__ f16x8 dequant_b_f4(const u32x4* c, uint32_t sv) {
+  const uint32_t w = J == 0 ? c[0].x : J == 1 ? c[0].y : J == 2 ? c[0].z : c[0].w;
+  const f16 s = (f16)e4m3_byte<J / 2>(sv);
+  const f16x2 s2 = {s, s};
+  uint32_t p[4];
+  e2m1_word_to_pairs(w, p);
+  u32x4 o;
+  o.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p[0]) * s2);
+  o.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p[1]) * s2);
+  o.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p[2]) * s2);
+  o.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, p[3]) * s2);
+  return __builtin_bit_cast(f16x8, o);
+}
+
 template <bool C, typename A, typename B>
 struct Pick {
   typedef A T;
@@ -384,7 +406,7 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
     const int c = col0 + 32 * (MODE == GEMM_FUSED_SWIGLU ? ni % HALFSUB : ni) + rin;
     return valid[ni] ? c : 0;
   };
-  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  const int64_t row_bytes = (int64_t)K * code_bits(BITS) / 8;
   const uint8_t* qbase[NSUB];
 #pragma unroll
   for (int ni = 0; ni < NSUB; ++ni) {
@@ -517,7 +539,14 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
         const u32x2 v = *(const u32x2*)(st + (b_wave + r * G::SEG + piece * 16 + kh * 8));
         bc.v[ni][0] = u32x4{v.x, v.y, 0u, 0u};
       }
-      if constexpr (BITS != 16) {
+      if constexpr (BITS == NVF4) {
+        // the slot's two words are the block scales of the pair's groups;
+        // this lane's k-steps cover blocks 2hh + kh*JW/2 onward
+        const u32x2 sb = *(const u32x2*)(st + (sc_wave + (ni * 16 + col_in / 2) * 16 + (col_in & 1) * 8));
+        const bool hi = KG == 2 ? gi == 1 : kodd;
+        sv[ni] = ((hi ? sb.y : sb.x) >> (16 * hh + 8 * (kh * JW / 2))) & 0xFFFFu;
+        bv[ni] = 0u;
+      } else if constexpr (BITS != 16) {
         const u32x2 sb = *(const u32x2*)(st + (sc_wave + (ni * 16 + col_in / 2) * 16 + (col_in & 1) * 8));
         const bool hi = KG == 2 ? gi == 1 : kodd;
         sv[ni] = hi ? sb.x >> 16 : sb.x & 0xFFFFu;
@@ -548,6 +577,7 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
 #pragma unroll
     for (int ni = 0; ni < NSUB; ++ni) {
       if constexpr (ODD) bf[ni] = dequant_b_odd<BITS>(bc.w[ni], jj, sv[ni], bv[ni]);
+      else if constexpr (BITS == NVF4) bf[ni] = dequant_b_f4<jj>(bc.v[ni], sv[ni]);
       else bf[ni] = dequant_b<BITS>(bc.v[ni], jj, sv[ni], bv[ni], qc);
     }
   };
@@ -757,6 +787,17 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
   // whether any token's activations were scaled (bf16 beyond 64): only then
   // are the exponents read
   const bool scaled = MODE != GEMM_ROWS_F16 && prm.tokexp && *prm.any_scaled != 0;
+  // NVFP4: the tensor scales multiply the sums (fused: gate and up halves)
+  if constexpr (BITS == NVF4) {
+#pragma unroll
+    for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NSUB; ++ni) {
+        const float ts = (MODE == GEMM_FUSED_SWIGLU && ni >= HALFSUB) ? prm.w1.ts : prm.w0.ts;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= ts;
+      }
+  }
 #pragma unroll
   for (int mi = 0; mi < MS; ++mi) {
     if (mi * 32 >= rows) continue;
@@ -822,7 +863,7 @@ static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
     return launch_kernel(gemm_kernel<5, MODE, MS, 2, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
   } else {
     // two-group stages: 4-bit rows, or 8-bit rows with the whole LDS
-    if constexpr (BITS == 4 || (BITS == 8 && WPC == 1 && NSUB == 2 && MS < 4 && KS == 1)) {
+    if constexpr (BITS == 4 || BITS == NVF4 || (BITS == 8 && WPC == 1 && NSUB == 2 && MS < 4 && KS == 1)) {
       if ((prm.K / 64) % 2 == 0 && tuning(TUNE_GEMM_KG) != 1)
         return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
     }
@@ -916,9 +957,11 @@ hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const i
   prm.perm8_out = perm8_out ? 1 : 0;
   // per-lane buffer offsets are 32-bit: the operand rows and one expert's weight rows
   // (A below 2 GB, so an offset of 2^31 is past its end)
-  if (a_rows * K * 2 > 0x7FFFFFFFll || w0.stride * (int64_t)K * bits / 8 > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  if (a_rows * K * 2 > 0x7FFFFFFFll || w0.stride * (int64_t)K * code_bits(bits) / 8 > 0xFFFFFFFFll)
+    return hipErrorInvalidValue;
   prm.m_tiles = max_mtiles;
   if (bits == 4) return launch_bits<4>(mode, bm, prm, st);
+  if (bits == NVF4) return launch_bits<NVF4>(mode, bm, prm, st);
   if (bits == 5) {
     if ((K / 64) % 2 != 0) return hipErrorInvalidValue;  // two-group stages
     return launch_bits<5>(mode, bm, prm, st);

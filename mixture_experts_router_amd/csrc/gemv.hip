@@ -18,7 +18,10 @@
 // where A and B are v_dot2_f32_f16 sums (fp32 accumulation) over the two
 // kinds of pairs and Xa, Xb the matching activation sums, computed once per
 // wave.  8-bit codes use v_perm_b32 to build 1024 + q pairs the same way.
-// About 1.4 VALU operations per 4-bit weight.
+// About 1.4 VALU operations per 4-bit weight.  NVFP4 codes have no bias: a
+// chunk's two 16-column blocks give two dot sums of exact fp16 E2M1 values
+// (one conversion instruction per code pair), weighted by the blocks' E4M3
+// scales; the tensor scale multiplies the row's sum.
 //
 // Lane l of a wave owns the 16-byte chunks c = l + 64*i of every row, so one
 // load instruction covers 1 KB of contiguous weights.  The chunk loops have no
@@ -59,7 +62,7 @@ __device__ __forceinline__ void for_slot(int s, F f) {
 // bytes of 5-bit codes (32 weights: five whole words)
 template <int BITS>
 struct Chunk {
-  static constexpr int VALS = BITS == 4 || BITS == 5 ? 32 : (BITS == 6 || BITS == 8 ? 16 : 8);  // weights per chunk
+  static constexpr int VALS = BITS == 4 || BITS == 5 || BITS == NVF4 ? 32 : (BITS == 6 || BITS == 8 ? 16 : 8);
   static constexpr int BYTES = BITS == 6 ? 12 : (BITS == 5 ? 20 : 16);                          // bytes per chunk
   static constexpr int PAIRS = VALS / 2;       // fp16 pairs of activations
   static constexpr int PER_GROUP = 64 / VALS;  // chunks per 64-column group
@@ -67,7 +70,7 @@ struct Chunk {
 };
 
 int gemv_lanes_chunks(int K, int bits) {
-  int vals = bits == 4 || bits == 5 ? 32 : (bits == 6 || bits == 8 ? 16 : 8);
+  int vals = bits == 4 || bits == 5 || bits == NVF4 ? 32 : (bits == 6 || bits == 8 ? 16 : 8);
   return (K / vals + 63) / 64;
 }
 
@@ -218,11 +221,39 @@ __device__ __forceinline__ float chunk_acc_words(u32x4 w, const uint32_t* xp, co
     }
     const float dq = A - xs.k;
     return __builtin_fmaf(half_bits_f(s_bits), dq, __builtin_fmaf(half_bits_f(b_bits), xs.x, acc));
+  } else if constexpr (BITS == NVF4) {
+    // 32 E2M1 codes in column order: words 0-1 are block 0, words 2-3 block
+    // 1; s_bits holds the two blocks' E4M3 scales (block 0 in the low byte)
+    float A0 = 0.0f, A1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t p[4];
+      e2m1_word_to_pairs(wv[j], p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (j < 2) A0 = dot2(p[i], xp[4 * j + i], A0);
+        else A1 = dot2(p[i], xp[4 * j + i], A1);
+      }
+    }
+    return __builtin_fmaf(e4m3_byte<1>(s_bits), A1, __builtin_fmaf(e4m3_byte<0>(s_bits), A0, acc));
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc = dot2(wv[j], xp[j], acc);
     return acc;
   }
+}
+
+// Byte offset of chunk c's scales in a row's scale bytes: the group's fp16
+// scale, or (NVF4) the two E4M3 block scales of the chunk's 32 columns
+template <int BITS>
+__device__ __forceinline__ uint32_t chunk_scale_off(int c) {
+  if constexpr (BITS == NVF4) return (uint32_t)c * 2u;
+  else return (uint32_t)(c / Chunk<BITS>::PER_GROUP) * 2u;
+}
+// scale bytes of one row of K weights
+template <int BITS>
+__device__ __forceinline__ int64_t scale_row_bytes(int K) {
+  return BITS == NVF4 ? K / 16 : (K / 64) * 2;
 }
 
 // ------------------------------------------------------------- gate + up --
@@ -274,7 +305,8 @@ __device__ __forceinline__ void load_rows(RowBuf<BITS, CPL>& buf, const GemvUpPa
                                           const uint32_t* qoff, const uint32_t* goff, int ng, int64_t row_bytes) {
   constexpr int R = Rows<CPL>::N;
   const uint32_t nq = live ? (uint32_t)row_bytes : 0u;
-  const uint32_t ns = live ? (uint32_t)ng * 2u : 0u;
+  const int64_t srb = scale_row_bytes<BITS>(prm.H);
+  const uint32_t ns = live ? (uint32_t)srb : 0u;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const WView& wv = (FUSED && r >= R / 2) ? prm.w1 : prm.w0;
@@ -283,12 +315,16 @@ __device__ __forceinline__ void load_rows(RowBuf<BITS, CPL>& buf, const GemvUpPa
 #pragma unroll
     for (int i = 0; i < CPL; ++i) buf.q[r][i] = load_chunk_nt<BITS>(rq, qoff[i]);
     if constexpr (BITS != 16) {
-      const rsrc_t rs = make_rsrc(wv.s + row * ng, ns);
-      const rsrc_t rb = make_rsrc(wv.b + row * ng, ns);
+      const rsrc_t rs = make_rsrc((const uint8_t*)wv.s + row * srb, ns);
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        buf.s[r][i] = buf_load_u16_nt(rs, goff[i]);
-        buf.b[r][i] = buf_load_u16_nt(rb, goff[i]);
+      for (int i = 0; i < CPL; ++i) buf.s[r][i] = buf_load_u16_nt(rs, goff[i]);
+      if constexpr (BITS != NVF4) {
+        const rsrc_t rb = make_rsrc((const uint8_t*)wv.b + row * srb, ns);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) buf.b[r][i] = buf_load_u16_nt(rb, goff[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) buf.b[r][i] = 0u;
       }
     }
   }
@@ -311,8 +347,10 @@ __device__ __forceinline__ void finish_iter(const RowBuf<BITS, CPL>& buf, const 
     part[r] = acc;
   }
   // the sums of the scaled activations x * 2^-a, scaled back (exact)
-  const float v = ldexp_f(reduce_rows<R>(part), a);
+  float v = ldexp_f(reduce_rows<R>(part), a);
   const int lane = lane_id();
+  // NVFP4: lane r holds row r, whose tensor's scale multiplies its sum
+  if constexpr (BITS == NVF4) v *= (FUSED && lane >= R / 2) ? prm.w1.ts : prm.w0.ts;
   if constexpr (FUSED) {
     // the up value of lane 0 (and 1) sits in lane R/2 (and R/2 + 1)
     const float u = R == 4 ? dpp_f<DPP_QUAD_2323>(v) : dpp_f<DPP_QUAD_1111>(v);
@@ -360,7 +398,7 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   const int H = prm.H;
   const int nch = H / C::VALS;
   const int ng = H / 64;
-  const int64_t row_bytes = (int64_t)H * BITS / 8;
+  const int64_t row_bytes = (int64_t)H * code_bits(BITS) / 8;
   const Q4Consts qc = q4_consts();
 
   // lane chunks c = lane + 64 i; a lane past the end of the row re-reads the
@@ -374,7 +412,7 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
     valid[i] = c < nch;
     cc[i] = valid[i] ? c : nch - 1;
     qoff[i] = (uint32_t)cc[i] * (uint32_t)C::BYTES;
-    goff[i] = (uint32_t)(cc[i] / C::PER_GROUP) * 2u;
+    goff[i] = chunk_scale_off<BITS>(cc[i]);
   }
 
   // The wave's iterations are it(k) = gw + k*W, k < n.  Loads are issued
@@ -386,7 +424,7 @@ __global__ __launch_bounds__(256) void gemv_up_kernel(GemvUpParams prm) {
   // short rows of 8-bit or fp16 weights: two iterations ahead, else one.
   // With one ahead the 4- and 5-bit forms fit three waves per SIMD, not two,
   // which streams faster than the deeper ring at two
-  constexpr bool DEEP = CPL <= 2 && BITS != 4 && BITS != 5;
+  constexpr bool DEEP = CPL <= 2 && BITS != 4 && BITS != 5 && BITS != NVF4;
 
   // activation loads first: vmcnt retires in issue order, so waiting for
   // them later does not wait for the weight loads issued after them
@@ -490,8 +528,8 @@ hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_
   // about `waves_per_cu` resident waves per CU, shared by the pairs
   // (1.5x for 4- and 5-bit codes at up to three chunks per lane, whose
   // kernels fit three or more waves per SIMD rather than two)
-  const int upw = (bits == 4 || bits == 5) && cpl <= 3 ? tuning(TUNE_UP_WAVES_PER_CU) * 3 / 2
-                                                       : tuning(TUNE_UP_WAVES_PER_CU);
+  const int upw = (bits == 4 || bits == 5 || bits == NVF4) && cpl <= 3 ? tuning(TUNE_UP_WAVES_PER_CU) * 3 / 2
+                                                                        : tuning(TUNE_UP_WAVES_PER_CU);
   const int64_t want = (int64_t)(num_cu > 0 ? num_cu : 256) * upw;
   int64_t per_pair = want / ((int64_t)T * kcap);
   if (per_pair < 4) per_pair = 4;
@@ -509,6 +547,8 @@ hipError_t launch_gemv_up(const void* x, int act, const GemvRoute& route, int k_
   if (bits == 8) return fused ? launch_up_cpl<8, true>(cpl, prm, grid, st) : launch_up_cpl<8, false>(cpl, prm, grid, st);
   if (bits == 6) return fused ? launch_up_cpl<6, true>(cpl, prm, grid, st) : launch_up_cpl<6, false>(cpl, prm, grid, st);
   if (bits == 5) return fused ? launch_up_cpl<5, true>(cpl, prm, grid, st) : launch_up_cpl<5, false>(cpl, prm, grid, st);
+  if (bits == NVF4)
+    return fused ? launch_up_cpl<NVF4, true>(cpl, prm, grid, st) : launch_up_cpl<NVF4, false>(cpl, prm, grid, st);
   return fused ? launch_up_cpl<16, true>(cpl, prm, grid, st) : launch_up_cpl<16, false>(cpl, prm, grid, st);
 }
 
@@ -560,13 +600,18 @@ __device__ __forceinline__ void load_down_row(DownBuf<BITS, DCPL>& buf, const Ge
 #pragma unroll
   for (int i = 0; i < DCPL; ++i) buf.q[i] = load_chunk_nt<BITS>(rq, qoff[i]);
   if constexpr (BITS != 16) {
-    const uint32_t ns = live ? (uint32_t)ng * 2u : 0u;
-    const rsrc_t rs = make_rsrc(prm.wd.s + row * ng, ns);
-    const rsrc_t rb = make_rsrc(prm.wd.b + row * ng, ns);
+    const int64_t srb = scale_row_bytes<BITS>(prm.I);
+    const uint32_t ns = live ? (uint32_t)srb : 0u;
+    const rsrc_t rs = make_rsrc((const uint8_t*)prm.wd.s + row * srb, ns);
 #pragma unroll
-    for (int i = 0; i < DCPL; ++i) {
-      buf.s[i] = buf_load_u16_nt(rs, goff[i]);
-      buf.b[i] = buf_load_u16_nt(rb, goff[i]);
+    for (int i = 0; i < DCPL; ++i) buf.s[i] = buf_load_u16_nt(rs, goff[i]);
+    if constexpr (BITS != NVF4) {
+      const rsrc_t rb = make_rsrc((const uint8_t*)prm.wd.b + row * srb, ns);
+#pragma unroll
+      for (int i = 0; i < DCPL; ++i) buf.b[i] = buf_load_u16_nt(rb, goff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DCPL; ++i) buf.b[i] = 0u;
     }
   }
 }
@@ -588,7 +633,7 @@ __global__ __launch_bounds__(KS == 4 ? 1024 : 512) void gemv_down_kernel(GemvDow
   const int ng = I / 64;
   const int G = gridDim.x;
   const int R = prm.rows;
-  const int64_t row_bytes = (int64_t)I * BITS / 8;
+  const int64_t row_bytes = (int64_t)I * code_bits(BITS) / 8;
   const Q4Consts qc = q4_consts();
 
   // the token's experts and routing weights, uniform across the wave
@@ -637,7 +682,7 @@ __global__ __launch_bounds__(KS == 4 ? 1024 : 512) void gemv_down_kernel(GemvDow
       valid[i] = c < nch;
       cc[i] = valid[i] ? c : nch - 1;
       qoff[i] = (uint32_t)cc[i] * (uint32_t)C::BYTES;
-      goff[i] = (uint32_t)(cc[i] / C::PER_GROUP) * 2u;
+      goff[i] = chunk_scale_off<BITS>(cc[i]);
     }
     // rows m(j) = m0 + j*G, j < nr; loads past the end go through empty
     // resources (unconditional loads keep the wait counts exact)
@@ -722,6 +767,7 @@ __global__ __launch_bounds__(KS == 4 ? 1024 : 512) void gemv_down_kernel(GemvDow
         float o = part[q][0][lane];
 #pragma unroll
         for (int k2 = 1; k2 < KS; ++k2) o = o + part[q][k2][lane];
+        if constexpr (BITS == NVF4) o = o * prm.wd.ts;
         const float c = w * o;
         y = y + c;
       }
@@ -775,7 +821,7 @@ hipError_t launch_gemv_down(const uint16_t* h, const GemvRoute& route, int k_sta
   if (bits == B && dc == D && ks == K) launch_kernel(gemv_down_kernel<B, D, K>, grid, block, 0, st, prm); else
 #define CASES(B) \
   X(B, 1, 1) X(B, 2, 1) X(B, 3, 1) X(B, 4, 1) X(B, 5, 1) X(B, 6, 1) X(B, 2, 2) X(B, 3, 2) X(B, 2, 4) X(B, 3, 4)
-  CASES(4) CASES(5) CASES(6) CASES(8) CASES(16) return hipErrorInvalidValue;
+  CASES(4) CASES(5) CASES(6) CASES(8) CASES(16) CASES(NVF4) return hipErrorInvalidValue;
 #undef CASES
 #undef X
   return hipGetLastError();

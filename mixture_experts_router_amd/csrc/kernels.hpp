@@ -11,6 +11,12 @@
 
 namespace moe {
 
+// Width code of NVFP4 weights inside the library (4-bit E2M1 codes with E4M3
+// block scales per 16 columns); code_bits gives the bits per code of a width
+// code.
+constexpr int NVF4 = 0x104;
+__host__ __device__ constexpr int code_bits(int bits) { return bits == NVF4 ? 4 : bits; }
+
 // Debug timing hook (moe_debug_set_events): the start/stop event pair for the
 // next kernel launch on this thread, if one is pending.
 bool next_launch_events(hipEvent_t* start, hipEvent_t* stop);
@@ -47,13 +53,15 @@ enum TuneKey {
 int tuning(TuneKey key);
 
 // One expert weight view: row n of expert e starts at q + (e*stride + n)*row_bytes.
+// `bits` arguments below are widths 4/5/6/8/16 or NVF4 (common.hpp).
 struct WView {
   const uint8_t* q;
-  const uint16_t* s;  // fp16 scales [rows, K/64] (NULL for bits 16)
-  const uint16_t* b;  // fp16 biases
+  const uint16_t* s;  // fp16 scales [rows, K/64] (NULL for bits 16); NVF4: E4M3 bytes [rows, K/16]
+  const uint16_t* b;  // fp16 biases (NULL for NVF4)
   int64_t stride;     // rows between experts
   const uint8_t* sb;  // scales and biases in the packed_sb layout (batched path)
   int64_t sb_stride;  // rows between experts in sb
+  float ts = 1.0f;    // NVF4: the tensor scale, applied to the fp32 sums
 };
 
 // ---------------------------------------------------------------- router
@@ -157,9 +165,10 @@ hipError_t launch_gather_preact(const float* g, const float* u, const int32_t* p
                                 int kcap, const int32_t* k_used_dev, int k_static, hipStream_t st);
 // copy n int32/fp32 words
 hipError_t launch_copy_words(const void* src, void* dst, int64_t n, hipStream_t st);
-// scales/biases of rows [0, N) of E experts -> packed_sb layout (see moe.h)
+// scales/biases of rows [0, N) of E experts -> packed_sb layout (see moe.h);
+// nvfp4: s holds E4M3 block-scale bytes [rows, K/16] and b is unused
 hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, int K, int64_t src_stride, uint8_t* dst,
-                          int64_t dst_stride, int64_t dst_row0, hipStream_t st);
+                          int64_t dst_stride, int64_t dst_row0, hipStream_t st, bool nvfp4 = false);
 inline int64_t packed_sb_bytes(int E, int64_t stride, int K) { return (int64_t)E * ((K / 64 + 1) / 2) * stride * 8; }
 
 }  // namespace moe

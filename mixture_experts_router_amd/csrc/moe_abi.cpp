@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <exception>
@@ -121,19 +122,32 @@ moe_status scratch_ptr(void** out) {
 
 // ----------------------------------------------------------- validation --
 
+// the library's width code of a tensor: 4/5/6/8/16, or NVF4
+int wcode(const moe_weights* w) { return w->format == MOE_FMT_NVFP4 ? moe::NVF4 : w->bits; }
+
 moe_status check_weights(const moe_weights* w, int E, int N, int K) {
   if (!w || !w->q) return MOE_ERR_NULL;
-  if (w->bits != 4 && w->bits != 5 && w->bits != 6 && w->bits != 8 && w->bits != 16) return MOE_ERR_QUANT;
-  if (w->bits == 16) {
-    if (w->scales || w->biases) return MOE_ERR_QUANT;
+  if (w->format == MOE_FMT_NVFP4) {
+    // E2M1 codes, E4M3 scales per 16 columns, a finite positive tensor scale, no biases
+    if (w->bits != 4 || w->group_size != 16 || w->biases) return MOE_ERR_QUANT;
+    if (!w->scales) return MOE_ERR_NULL;
+    if (!(w->tensor_scale > 0.0f) || !std::isfinite(w->tensor_scale)) return MOE_ERR_QUANT;
+  } else if (w->format != MOE_FMT_AFFINE) {
+    return MOE_ERR_QUANT;
   } else {
-    if (!w->scales || !w->biases) return MOE_ERR_NULL;
-    if (w->group_size != 64) return MOE_ERR_QUANT;
+    if (w->bits != 4 && w->bits != 5 && w->bits != 6 && w->bits != 8 && w->bits != 16) return MOE_ERR_QUANT;
+    if (w->bits == 16) {
+      if (w->scales || w->biases) return MOE_ERR_QUANT;
+    } else {
+      if (!w->scales || !w->biases) return MOE_ERR_NULL;
+      if (w->group_size != 64) return MOE_ERR_QUANT;
+    }
   }
   if (w->E != E || w->N != N || w->K != K) return MOE_ERR_SHAPE;
   if (w->K % 64 != 0 || w->expert_stride_rows < w->N) return MOE_ERR_SHAPE;
   if (!aligned16(w->q)) return MOE_ERR_ALIGN;
-  if (w->bits != 16 && (!aligned16(w->scales) || !aligned16(w->biases))) return MOE_ERR_ALIGN;
+  if (w->bits != 16 && !aligned16(w->scales)) return MOE_ERR_ALIGN;
+  if (w->biases && !aligned16(w->biases)) return MOE_ERR_ALIGN;
   if (w->packed_sb && w->bits == 16) return MOE_ERR_QUANT;  // packed_sb: quantised weights only
   if (w->packed_sb && !aligned16(w->packed_sb)) return MOE_ERR_ALIGN;
   return MOE_OK;
@@ -154,7 +168,10 @@ moe_status check_router(const void* x, moe_dtype dt, int T, int H, const void* w
   return MOE_OK;
 }
 
-bool compatible(const moe_weights* a, const moe_weights* b) {
+// same_scale: NVFP4 tensors must also share the tensor scale (one fused tensor)
+bool compatible(const moe_weights* a, const moe_weights* b, bool same_scale) {
+  if (a->format != b->format) return false;
+  if (same_scale && a->format == MOE_FMT_NVFP4 && a->tensor_scale != b->tensor_scale) return false;
   return a->bits == b->bits && a->group_size == b->group_size && a->E == b->E && a->N == b->N && a->K == b->K &&
          (a->scales == nullptr) == (b->scales == nullptr) && (a->biases == nullptr) == (b->biases == nullptr);
 }
@@ -210,14 +227,16 @@ Layout layout(int64_t T, int64_t H, int64_t E, int64_t kcap, int64_t I, uint32_t
 
 WView view_of(const moe_weights* w, int64_t row_offset) {
   WView v;
+  const bool f4 = w->format == MOE_FMT_NVFP4;
   const int64_t rb = (int64_t)w->K * w->bits / 8;
-  const int64_t ng = w->K / 64;
+  const int64_t srb = f4 ? w->K / 16 : (w->K / 64) * 2;  // scale bytes per row
   v.q = (const uint8_t*)w->q + row_offset * rb;
-  v.s = w->scales ? (const uint16_t*)w->scales + row_offset * ng : nullptr;
-  v.b = w->biases ? (const uint16_t*)w->biases + row_offset * ng : nullptr;
+  v.s = w->scales ? (const uint16_t*)((const uint8_t*)w->scales + row_offset * srb) : nullptr;
+  v.b = w->biases ? (const uint16_t*)((const uint8_t*)w->biases + row_offset * srb) : nullptr;
   v.stride = w->expert_stride_rows;
   v.sb = (const uint8_t*)w->packed_sb;
   v.sb_stride = w->expert_stride_rows;
+  v.ts = f4 ? w->tensor_scale : 1.0f;
   return v;
 }
 
@@ -291,19 +310,19 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   WView wg, wu;
   if (gate_up) {
     if ((s = check_weights(gate_up, E, 2 * I, H)) != MOE_OK) return s;
-    if (gate_up->bits != down->bits) return MOE_ERR_QUANT;
+    if (wcode(gate_up) != wcode(down)) return MOE_ERR_QUANT;
     wg = view_of(gate_up, 0);
     wu = view_of(gate_up, I);
   } else {
     if (!gate || !up) return MOE_ERR_NULL;
-    if (!compatible(gate, up)) return MOE_ERR_INCOMPATIBLE;
+    if (!compatible(gate, up, false)) return MOE_ERR_INCOMPATIBLE;
     if ((s = check_weights(gate, E, I, H)) != MOE_OK) return s;
     if ((s = check_weights(up, E, I, H)) != MOE_OK) return s;
-    if (gate->bits != down->bits) return MOE_ERR_QUANT;
+    if (wcode(gate) != wcode(down)) return MOE_ERR_QUANT;
     wg = view_of(gate, 0);
     wu = view_of(up, 0);
   }
-  const int bits = down->bits;
+  const int bits = wcode(down);  // NVFP4 weights: moe::NVF4
   const int kcap = kcap_of(k);
   const int64_t P = (int64_t)T * kcap;
   const bool gemv_fits = moe::gemv_lanes_chunks(H, bits) <= 4 && moe::gemv_down_fits(I, bits, kcap);
@@ -404,7 +423,8 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     plan_step("sort_pairs", st);
     const int bm = moe::gemm_block_m((int)P, E);
     const int mt = moe::gemm_max_mtiles((int)P, E, bm);
-    // the GEMM operand: fp16 activations, 8-element blocks in 4-bit unpack order
+    // the GEMM operand: fp16 activations, 8-element blocks in 4-bit unpack
+    // order for affine 4-bit codes (NVFP4 codes unpack in column order)
     const bool perm8 = bits == 4;
     const uint16_t* a16 = (const uint16_t*)x;
     if (perm8 || dt != MOE_F16) {
@@ -416,8 +436,8 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     // rows (the GEMM reads both halves with one descriptor)
     if (bits != 16 && !(gate_up && gate_up->packed_sb)) {
       uint8_t* sb = W + L.sbgu;
-      HIP_TRY(moe::launch_pack_sb(wg.s, wg.b, E, I, H, wg.stride, sb, 2 * I, 0, st));
-      HIP_TRY(moe::launch_pack_sb(wu.s, wu.b, E, I, H, wu.stride, sb, 2 * I, I, st));
+      HIP_TRY(moe::launch_pack_sb(wg.s, wg.b, E, I, H, wg.stride, sb, 2 * I, 0, st, bits == moe::NVF4));
+      HIP_TRY(moe::launch_pack_sb(wu.s, wu.b, E, I, H, wu.stride, sb, 2 * I, I, st, bits == moe::NVF4));
       plan_step("pack_sb_gate_up", st);
       wg.sb = sb;
       wu.sb = sb + (size_t)I * 8;
@@ -443,7 +463,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     WView wd = view_of(down, 0);
     if (bits != 16 && !wd.sb) {
       uint8_t* sb = W + L.sbd;
-      HIP_TRY(moe::launch_pack_sb(wd.s, wd.b, E, H, I, wd.stride, sb, H, 0, st));
+      HIP_TRY(moe::launch_pack_sb(wd.s, wd.b, E, H, I, wd.stride, sb, H, 0, st, bits == moe::NVF4));
       plan_step("pack_sb_down", st);
       wd.sb = sb;
       wd.sb_stride = H;
@@ -669,7 +689,8 @@ moe_status moe_pack_sb(const moe_weights* w, void* out, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   plan_begin(st);
   HIP_TRY(moe::launch_pack_sb((const uint16_t*)w->scales, (const uint16_t*)w->biases, w->E, w->N, w->K,
-                              w->expert_stride_rows, (uint8_t*)out, w->expert_stride_rows, 0, st));
+                              w->expert_stride_rows, (uint8_t*)out, w->expert_stride_rows, 0, st,
+                              w->format == MOE_FMT_NVFP4));
   plan_step("pack_sb", st);
   return MOE_OK;
 }
@@ -678,20 +699,23 @@ moe_status moe_fuse_gate_up(const moe_weights* gate, const moe_weights* up, void
                             void* stream) {
   try {
     if (!gate || !up || !gate->q || !up->q || !q_out) return MOE_ERR_NULL;
-    if (!compatible(gate, up)) return MOE_ERR_INCOMPATIBLE;
+    if (!compatible(gate, up, true)) return MOE_ERR_INCOMPATIBLE;
     moe_status s = check_weights(gate, gate->E, gate->N, gate->K);
     if (s != MOE_OK) return s;
     if ((s = check_weights(up, gate->E, gate->N, gate->K)) != MOE_OK) return s;
+    const bool f4 = gate->format == MOE_FMT_NVFP4;
     const bool quant = gate->bits != 16;
-    if (quant && (!s_out || !b_out)) return MOE_ERR_NULL;
-    if (!quant && (s_out || b_out)) return MOE_ERR_QUANT;
-    if (!aligned16(q_out) || (quant && (!aligned16(s_out) || !aligned16(b_out)))) return MOE_ERR_ALIGN;
+    const bool has_b = quant && !f4;  // NVFP4 weights have no biases
+    if (quant && !s_out) return MOE_ERR_NULL;
+    if (has_b && !b_out) return MOE_ERR_NULL;
+    if ((!quant && s_out) || (!has_b && b_out)) return MOE_ERR_QUANT;
+    if (!aligned16(q_out) || (quant && !aligned16(s_out)) || (has_b && !aligned16(b_out))) return MOE_ERR_ALIGN;
     DevProps props;
     if ((s = device_props(&props)) != MOE_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     plan_begin(st);
     const size_t E = (size_t)gate->E, I = (size_t)gate->N;
-    const size_t rb = (size_t)gate->K * gate->bits / 8, sb = (size_t)(gate->K / 64) * 2;
+    const size_t rb = (size_t)gate->K * gate->bits / 8, sb = f4 ? (size_t)gate->K / 16 : (size_t)(gate->K / 64) * 2;
     struct Part {
       void* dst;
       const void* src;
@@ -703,7 +727,7 @@ moe_status moe_fuse_gate_up(const moe_weights* gate, const moe_weights* up, void
                      {(uint8_t*)s_out + I * sb, up->scales, sb, (size_t)up->expert_stride_rows},
                      {b_out, gate->biases, sb, (size_t)gate->expert_stride_rows},
                      {(uint8_t*)b_out + I * sb, up->biases, sb, (size_t)up->expert_stride_rows}};
-    const int nparts = quant ? 6 : 2;
+    const int nparts = has_b ? 6 : (quant ? 4 : 2);
     for (int i = 0; i < nparts; ++i) {
       const Part& p = parts[i];
       // E blocks of I rows; destination experts are 2*I rows apart

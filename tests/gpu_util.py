@@ -35,6 +35,9 @@ def dev_weights(w: mi.Weights) -> moe.Weights:
         q = torch.from_numpy(np.ascontiguousarray(w.q).view(np.int16)).view(torch.float16).cuda()
         return moe.Weights(q, None, None, w.E, w.N, w.K, 16)
     q = torch.from_numpy(np.ascontiguousarray(w.q)).cuda()
+    if w.fmt == "nvfp4":
+        s = torch.from_numpy(np.ascontiguousarray(w.scales)).cuda()
+        return moe.Weights(q, s, None, w.E, w.N, w.K, 4, 16, fmt="nvfp4", tensor_scale=w.tensor_scale)
     s = torch.from_numpy(np.ascontiguousarray(w.scales).view(np.int16)).view(torch.float16).cuda()
     b = torch.from_numpy(np.ascontiguousarray(w.biases).view(np.int16)).view(torch.float16).cuda()
     return moe.Weights(q, s, b, w.E, w.N, w.K, w.bits)

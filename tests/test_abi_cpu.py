@@ -154,6 +154,48 @@ def test_fuse_gate_up_validation():
     assert moe.STATUS[L.moe_fuse_gate_up(ctypes.byref(g), ctypes.byref(u), P + 8, P, P, None)] == "MOE_ERR_ALIGN"
 
 
+def F4(E, N, K, q=P, s=P, b=None, gs=16, ts=0.01, bits=4, fmt=moe.FMT_NVFP4, stride=None):
+    return moe.CWeights(q, s, b, E, N, K, bits, gs, N if stride is None else stride, None, fmt, ts)
+
+
+def test_nvfp4_weights_validation():
+    ok_gu, ok_d = F4(8, 256, 256), F4(8, 256, 128)
+    assert fwd(T=0, gu=ok_gu, down=ok_d) == 0
+    for bad, status in [
+        (F4(8, 256, 256, bits=8), "MOE_ERR_QUANT"),     # E2M1 codes are 4 bits
+        (F4(8, 256, 256, gs=64), "MOE_ERR_QUANT"),      # one block scale per 16 columns
+        (F4(8, 256, 256, b=P), "MOE_ERR_QUANT"),        # no biases
+        (F4(8, 256, 256, ts=0.0), "MOE_ERR_QUANT"),
+        (F4(8, 256, 256, ts=-1.0), "MOE_ERR_QUANT"),
+        (F4(8, 256, 256, ts=float("nan")), "MOE_ERR_QUANT"),
+        (F4(8, 256, 256, ts=float("inf")), "MOE_ERR_QUANT"),
+        (F4(8, 256, 256, s=None), "MOE_ERR_NULL"),
+        (F4(8, 256, 256, s=P + 4), "MOE_ERR_ALIGN"),
+        (F4(8, 256, 256, fmt=2), "MOE_ERR_QUANT"),
+        (F4(8, 256, 200), "MOE_ERR_SHAPE"),
+    ]:
+        assert moe.STATUS[fwd(T=4, gu=bad, down=ok_d)] == status, (bad.bits, bad.group_size, bad.tensor_scale)
+    # gate_up and down in one format
+    assert moe.STATUS[fwd(gu=ok_gu, down=W(8, 256, 128))] == "MOE_ERR_QUANT"
+    assert moe.STATUS[fwd(gu=W(8, 256, 256), down=ok_d)] == "MOE_ERR_QUANT"
+    # separate gate and up: one format; their tensor scales may differ
+    assert moe.STATUS[fwd(gu=None, gate=F4(8, 128, 256), up=W(8, 128, 256), down=ok_d)] == "MOE_ERR_INCOMPATIBLE"
+    assert fwd(T=0, gu=None, gate=F4(8, 128, 256, ts=0.5), up=F4(8, 128, 256, ts=0.25), down=ok_d) == 0
+
+
+def test_nvfp4_fuse_and_pack_validation():
+    L = moe.lib()
+    g = F4(8, 128, 256)
+    # a fused tensor holds one tensor scale
+    u = F4(8, 128, 256, ts=0.02)
+    assert moe.STATUS[L.moe_fuse_gate_up(ctypes.byref(g), ctypes.byref(u), P, P, None, None)] == \
+        "MOE_ERR_INCOMPATIBLE"
+    u = F4(8, 128, 256)
+    assert moe.STATUS[L.moe_fuse_gate_up(ctypes.byref(g), ctypes.byref(u), P, P, P, None)] == "MOE_ERR_QUANT"
+    assert moe.STATUS[L.moe_fuse_gate_up(ctypes.byref(g), ctypes.byref(u), P, None, None, None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[L.moe_pack_sb(ctypes.byref(F4(8, 256, 256, gs=64)), P, None)] == "MOE_ERR_QUANT"
+
+
 def test_route_validation():
     L = moe.lib()
     ws = 1 << 20

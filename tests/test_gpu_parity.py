@@ -67,6 +67,18 @@ CASES = {
     # a small batch over long rows (bf16 activations; 8- and 4-bit weights)
     "batched_long_k": ("batched_decode", dict(T=16, H=2048, E=16, I=1024)),
     "batched_long_k_q4": ("prefill", dict(T=8, H=2048, E=16, I=1024)),
+    # NVFP4 weights (E2M1 codes, E4M3 block scales, tensor scale): decode
+    # (one and two chunks per lane, long down rows), the batched tiles of 32,
+    # 64 and 128 rows with an odd group count on the down GEMM, bf16
+    # activations, and entropy-adaptive k
+    "decode_f4": ("decode_b1", dict(T=3, H=1024, E=16, I=704, fmt="nvfp4")),
+    "decode_f4_h4096": ("decode_b1", dict(T=1, H=4096, E=8, I=2816, fmt="nvfp4")),
+    "decode_f4_long": ("decode_b1", dict(T=2, H=1024, E=8, I=11008, fmt="nvfp4")),
+    "batched_f4": ("prefill", dict(T=300, H=512, E=16, I=192, fmt="nvfp4")),
+    "batched_f4_bm32": ("batched_decode", dict(T=40, H=512, E=8, I=320, fmt="nvfp4")),
+    "prefill_f4_bm128": ("prefill", dict(T=2304, H=256, E=8, I=384, fmt="nvfp4")),
+    "entropy_f4": ("entropy", dict(T=96, H=512, E=16, I=192, fmt="nvfp4", segment=2)),
+    "batched_long_k_f4": ("batched_decode", dict(T=16, H=2048, E=16, I=1024, fmt="nvfp4")),
 }
 
 
@@ -103,8 +115,8 @@ def _paths(inp):
 @pytest.mark.parametrize("name", list(CASES))
 def test_layer_matches_oracle(name, built):
     inp, gu_np, dev = built(name)
-    print("case", name, "T=%d H=%d E=%d I=%d k=%d bits=%d %s" % (inp.T, inp.H, inp.E, inp.I, inp.k, inp.bits,
-                                                                 inp.dtype), flush=True)
+    print("case", name, "T=%d H=%d E=%d I=%d k=%d bits=%d %s %s" % (inp.T, inp.H, inp.E, inp.I, inp.k, inp.bits,
+                                                                    inp.fmt, inp.dtype), flush=True)
     for pname, pflag in _paths(inp):
         y, taps = _run(dev, pflag)
         ku = int(taps["k_used"][0])
@@ -165,7 +177,8 @@ GEMM_SHAPES = [(32, 2, 2, 1, 2), (32, 2, 2, 1, 1), (64, 1, 2, 1, 2), (64, 2, 2, 
 DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2, 6: 1, 7: 3}
 
 
-@pytest.mark.parametrize("name", ["prefill_bm128", "prefill_small", "tiny_q8_bf16", "tiny_fp16w", "batched_long_k"])
+@pytest.mark.parametrize("name", ["prefill_bm128", "prefill_small", "tiny_q8_bf16", "tiny_fp16w", "batched_long_k",
+                                  "prefill_f4_bm128"])
 def test_gemm_launch_shapes_are_bit_identical(name, built):
     from ref64 import half64
     inp, _, dev = built(name)
@@ -196,6 +209,17 @@ def test_gemm_launch_shapes_are_bit_identical(name, built):
 
 def _packed_reference(w):
     """packed_sb layout written out with numpy from the host copies."""
+    if w.fmt == "nvfp4":
+        # the four block-scale bytes of groups 2p and 2p+1 (0 if none), as words
+        E, N, nb = w.scales.shape
+        ng = nb // 4
+        words = np.ascontiguousarray(w.scales).view(np.uint32)  # [E, N, ng]
+        if ng % 2:
+            words = np.concatenate([words, np.zeros((E, N, 1), np.uint32)], axis=2)
+        out = np.zeros((E, (ng + 1) // 2, N, 2), np.uint32)
+        out[..., 0] = words[:, :, 0::2].transpose(0, 2, 1)
+        out[..., 1] = words[:, :, 1::2].transpose(0, 2, 1)
+        return out.view(np.uint16)
     E, N, ng = w.scales.shape
     NP = (ng + 1) // 2
     pad = lambda a: np.concatenate([a, np.zeros((E, N, 1), np.uint16)], axis=2) if ng % 2 else a
@@ -209,13 +233,15 @@ def _packed_reference(w):
 
 
 @pytest.mark.parametrize("name", ["prefill_small", "tiny_q8_bf16", "ragged_shapes", "entropy_q4", "batched_q5",
-                                  "batched_q6"])
+                                  "batched_q6", "batched_f4", "entropy_f4"])
 def test_packed_sb_layout_and_bit_identity(name, built):
     inp, gu_np, dev = built(name)
     down = moe.pack_sb(dev.down)
     gate_up = moe.pack_sb(dev.gate_up)
     torch.cuda.synchronize()
     E, N, ng = inp.down.scales.shape
+    if inp.fmt == "nvfp4":
+        ng //= 4  # four block scales per group
     got = down.packed_sb.cpu().numpy().view(np.uint16).reshape(E, (ng + 1) // 2, N, 4)
     assert np.array_equal(got, _packed_reference(inp.down))
     got = gate_up.packed_sb.cpu().numpy().view(np.uint16).reshape(E, -1, 2 * inp.I, 4)
@@ -284,10 +310,14 @@ def test_token_permutation_equivariance(built):
 
 
 def test_fuse_gate_up_matches_oracle_concatenation(built):
-    for name in ("tiny", "tiny_q8_bf16", "tiny_fp16w"):
+    for name in ("tiny", "tiny_q8_bf16", "tiny_fp16w", "decode_f4"):
         inp, gu_np, dev = built(name)
         if inp.bits == 16:
             assert np.array_equal(host_bits(dev.gate_up.q), gu_np.q)
+        elif inp.fmt == "nvfp4":
+            assert np.array_equal(dev.gate_up.q.cpu().numpy(), gu_np.q)
+            assert np.array_equal(dev.gate_up.scales.cpu().numpy(), gu_np.scales)
+            assert dev.gate_up.biases is None and dev.gate_up.tensor_scale == gu_np.tensor_scale
         else:
             assert np.array_equal(dev.gate_up.q.cpu().numpy(), gu_np.q)
             assert np.array_equal(host_bits(dev.gate_up.scales), gu_np.scales)
@@ -391,6 +421,8 @@ def _token_exponent(x_bits_row: np.ndarray) -> int:
     ("prefill", dict(T=300, H=512, E=16, I=192), moe.FLAG_FORCE_MFMA),        # 4-bit, batched path
     ("batched_decode", dict(T=6, H=512, E=8, I=320), moe.FLAG_FORCE_GEMV),    # 8-bit, decode path
     ("prefill", dict(T=4, H=512, E=16, I=192), moe.FLAG_FORCE_GEMV),          # 4-bit, decode path
+    ("prefill", dict(T=300, H=512, E=16, I=192, fmt="nvfp4"), moe.FLAG_FORCE_MFMA),  # NVFP4, batched path
+    ("prefill", dict(T=4, H=512, E=16, I=192, fmt="nvfp4"), moe.FLAG_FORCE_GEMV),    # NVFP4, decode path
 ])
 def test_bf16_activations_beyond_fp16_range(recipe, kw, flag):
     # rows of bf16 activations scaled near 1e5 (beyond fp16's 65504) and one
