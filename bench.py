@@ -45,6 +45,10 @@ WORKLOADS = {
                            label="batched decode: 64 tokens, H=4096, E=32, top-2, I=2816, 8-bit g64, bf16, Zipf 1.1"),
     "prefill": dict(recipe="prefill", pool=None, T=4096,
                     label="prefill: 4096 tokens, H=4096, E=64, top-4, I=1408, 4-bit g64, bf16, Zipf 1.2"),
+    "decode_f4": dict(recipe="decode_b1", pool=256, T=1, fmt="nvfp4",
+                      label="decode b1: 1 token/step, H=4096, E=64, top-4, I=11008, NVFP4 weights, fp16"),
+    "prefill_f4": dict(recipe="prefill", pool=None, T=4096, fmt="nvfp4",
+                       label="prefill: 4096 tokens, H=4096, E=64, top-4, I=1408, NVFP4 weights, bf16, Zipf 1.2"),
     "entropy_q4": dict(recipe="entropy", pool=None, T=512, bits=4,
                        label="entropy-adaptive: 512 tokens (segment k=3), H=4096, E=32, I=2816, 4-bit g64, fp16"),
     "entropy_fp16": dict(recipe="entropy", pool=None, T=512, bits=16,
@@ -56,7 +60,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def weight_bytes_per_row(K: int, bits: int) -> int:
+def weight_bytes_per_row(K: int, bits) -> int:
+    """Bytes of one weight row: codes plus scales (and biases); bits "nvfp4":
+    K/2 code bytes and K/16 E4M3 block scales."""
+    if bits == "nvfp4":
+        return K // 2 + K // 16
     return K * bits // 8 + (0 if bits == 16 else 2 * 2 * (K // 64))
 
 
@@ -188,7 +196,7 @@ def main():
 
     t0 = time.time()
     kw = {}
-    for key in ("bits", "I"):
+    for key in ("bits", "I", "fmt"):
         if key in wl:
             kw[key] = wl[key]
     if recipe == "entropy":
@@ -196,7 +204,8 @@ def main():
     T_pool = wl["pool"] or wl["T"]
     inp = mi.make_inputs(recipe, T=T_pool, **kw)
     log("generated %s inputs in %.1fs" % (args.workload, time.time() - t0))
-    H, E, I, k, bits = inp.H, inp.E, inp.I, inp.k, inp.bits
+    H, E, I, k = inp.H, inp.E, inp.I, inp.k
+    bits = "nvfp4" if inp.fmt == "nvfp4" else inp.bits  # the byte counts' weight format
     dt = torch.float16 if inp.dtype == "f16" else torch.bfloat16
 
     def dev_bits(a, dtype):
@@ -205,6 +214,9 @@ def main():
     def dev_w(w):
         if w.bits == 16:
             return moe.Weights(dev_bits(w.q, torch.float16), None, None, w.E, w.N, w.K, 16)
+        if w.fmt == "nvfp4":
+            return moe.Weights(torch.from_numpy(w.q).cuda(), torch.from_numpy(w.scales).cuda(), None, w.E, w.N,
+                               w.K, 4, 16, fmt="nvfp4", tensor_scale=w.tensor_scale)
         return moe.Weights(torch.from_numpy(w.q).cuda(), dev_bits(w.scales, torch.float16),
                            dev_bits(w.biases, torch.float16), w.E, w.N, w.K, w.bits)
 

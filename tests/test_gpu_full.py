@@ -119,6 +119,16 @@ def test_decode_b1_full_size_6_bit_inter_11008():
     _decode_one_token_calls(*_gen("decode_b1", T=3, bits=6), "decode_b1 6-bit I 11008")
 
 
+def test_decode_b1_full_size_nvfp4():
+    # the decode shape with NVFP4 weights: H 4096 (two chunks per lane),
+    # I 11008 (six chunks per down row, two waves per slot)
+    _decode_one_token_calls(*_gen("decode_b1", T=3, fmt="nvfp4"), "decode_b1 NVFP4")
+
+
+def test_prefill_full_size_nvfp4():
+    _prefill_full_size(*_gen("prefill", fmt="nvfp4"), "prefill NVFP4")
+
+
 def _prefill_full_size(inp, gu_np, dev, label):
     y, taps, plan = _forward(dev)
     assert "gemm_gate_up_swiglu" in plan, plan
