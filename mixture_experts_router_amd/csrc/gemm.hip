@@ -196,9 +196,9 @@ __device__ __forceinline__ void for_stages(F&& f) {
 // Dequantised B operand of MFMA k-step j (8 weights of this lane's column)
 // of one group, from the lane's code bytes c (4-bit: c[0]; 8-bit: c[0..1];
 // fp16: c[0..3]).  Every weight is w = fp16(fma(q, s, b)) (one rounding):
-// codes become 1024 + q (or 1024 + 16q for the high nibble of a 4-bit byte)
-// with v_and_or_b32 / v_perm_b32, an exact packed fp16 operation recovers q,
-// and a packed fma applies the group's scale and bias.
+// 4-bit codes become exact fp16 pairs through the fp8 conversion below;
+// 8-bit codes become 1024 + q with v_perm_b32 and an exact packed fp16
+// subtraction recovers q; a packed fma applies the group's scale and bias.
 template <int BITS>
 __device__ __forceinline__ f16x8 dequant_b(const u32x4* c, int j, uint32_t s_bits, uint32_t b_bits,
                                            const Q4Consts& qc) {
@@ -213,15 +213,20 @@ __device__ __forceinline__ f16x8 dequant_b(const u32x4* c, int j, uint32_t s_bit
       return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
     };
     if constexpr (BITS == 4) {
-      const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f}, m64 = {(f16)-64.0f, (f16)-64.0f};
-      auto hi = [&](uint32_t p) {  // 1024 + 16q  ->  q (exact)  ->  s q + b
-        const f16x2 q = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, p), sixteenth, m64);
-        return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
-      };
+      // bytes reordered to (b0, b2, b1, b3), so the low nibbles are codes
+      // (0, 4, 2, 6) and the high nibbles (1, 5, 3, 7), one per byte.  A byte
+      // holding q in 0..15 is the FP8 E4M3 pattern of q * 2^-9 (subnormal
+      // below 8, exponent field 1 from 8 on), so the scaled conversion with
+      // 2^9 gives the fp16 pair of codes exactly, one instruction per pair
       const uint32_t w = j == 0 ? c[0].x : j == 1 ? c[0].y : j == 2 ? c[0].z : c[0].w;
-      uint32_t p04, p15, p26, p37;
-      q4_word_unpack(w, qc, p04, p15, p26, p37);
-      const u32x4 o = {lo(p04), hi(p15), lo(p26), hi(p37)};
+      const uint32_t v = __builtin_amdgcn_perm(w, w, 0x03010200u);
+      const uint32_t lo4 = v & 0x0F0F0F0Fu, hi4 = (v >> 4) & 0x0F0F0F0Fu;
+      auto fq = [&](f16x2 q) { return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2)); };
+      const u32x4 o = {fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo4, 512.0f, false)),   // (k0, k4)
+                       fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi4, 512.0f, false)),   // (k1, k5)
+                       fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo4, 512.0f, true)),    // (k2, k6)
+                       fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi4, 512.0f, true))};   // (k3, k7)
+      (void)qc;
       return __builtin_bit_cast(f16x8, o);
     } else {
       const u32x4 q = c[j / 2];
