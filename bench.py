@@ -274,31 +274,46 @@ def main():
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t0
 
-    # ---- timed region 2: hipGraph replay of G consecutive layer calls
+    # ---- timed region 2: hipGraph replays of consecutive layer calls,
+    # exactly K steps in chunks: first a 2-step graph, then 64-step graphs and
+    # a remainder.  A replay's kernels start only once its whole graph is
+    # submitted (about 70 us for 20 steps), so the short first chunk lets the
+    # GPU start while the longer ones are submitted behind it.
     graph_s = None
-    G = min(64, K)
-    reps = max(1, K // G)
+    sizes = [min(2, K)]
+    while sum(sizes) < K:
+        sizes.append(min(64, K - sum(sizes)))
     try:
         if args.no_graph:
             raise RuntimeError("skipped (--no-graph)")
-        g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            for i in range(G):
+            for i in range(min(K, 66)):
                 step(i)
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for i in range(G):
-                step(i)
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
+        # chunk j covers steps s_j .. s_j + n_j - 1 of the token pool; chunks
+        # of the same size and pool offset share one graph
+        graphs, plan_g, s0 = {}, [], 0
+        for n in sizes:
+            key = (n, s0 % 256)
+            if key not in graphs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(n):
+                        step(s0 + i)
+                graphs[key] = g
+            plan_g.append(graphs[key])
+            s0 += n
+        for g in graphs.values():
             g.replay()
         torch.cuda.synchronize()
-        graph_s = (time.perf_counter() - t0) * K / (reps * G)
+        t0 = time.perf_counter()
+        for g in plan_g:
+            g.replay()
+        torch.cuda.synchronize()
+        graph_s = time.perf_counter() - t0
     except Exception as ex:  # graph capture unavailable: report stream launches only
         log("graph capture failed:", ex)
 
