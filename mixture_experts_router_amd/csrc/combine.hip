@@ -59,7 +59,7 @@ hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wt
 }
 
 // h = 2^-2a silu(g) * u (a: the row's token exponent, 0 without tokexp);
-// with perm8 set, each 8-element block of h is stored in 4-bit unpack order
+// with perm8 set, each 8-element block of h is stored in the 4-bit GEMM order (q4g_order)
 // (the operand order of the batched 4-bit down GEMM).
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g, const float* __restrict__ u,
                                                      uint16_t* __restrict__ h, int64_t n, int I, int perm8,
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g
                                                      const int32_t* __restrict__ perm, int kcap) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const int64_t at = perm8 ? (i & ~(int64_t)7) + perm8_slot((int)(i & 7)) : i;
+  const int64_t at = perm8 ? (i & ~(int64_t)7) + q4g_slot((int)(i & 7)) : i;
   float hv = swiglu(g[i], u[i]);
   if (tokexp) {
     const int64_t row = i / I;
@@ -86,7 +86,7 @@ hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t ro
 }
 
 // Activation operand of the batched GEMM: x (fp16 or bf16) -> fp16, each
-// 8-element block optionally in 4-bit unpack order.  One workgroup per token:
+// 8-element block optionally in the 4-bit GEMM order (q4g_order).  One workgroup per token:
 // bf16 rows are converted as x * 2^-a_t (common.hpp; exact) and a_t is
 // written to tokexp[t]; fp16 rows are copied.
 __global__ __launch_bounds__(256) void prep_a_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ a,
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void prep_a_kernel(const uint16_t* __restrict_
   }
   for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
     u32x4 v = act8_to_f16_scaled(load16(xr + c), act, e);
-    if (perm8) v = perm8_nibble_order(v);
+    if (perm8) v = q4g_order(v);
     *(u32x4*)(ar + c) = v;
   }
 }
@@ -126,7 +126,7 @@ hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, 
 }
 
 // Rows of h in pair order (taps); perm8 restores the natural element order
-// of rows stored in 4-bit unpack order.
+// of rows stored in the 4-bit GEMM order.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ src,
                                                           const int32_t* __restrict__ pos, int I,
                                                           uint16_t* __restrict__ out, int kcap,
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
   if (r < 0) return;
   for (int c = (blockIdx.x * 256 + threadIdx.x) * 8; c < I; c += gridDim.x * 256 * 8) {
     u32x4 v = load16(src + (size_t)r * I + c);
-    if (perm8) v = perm8_natural_order(v);
+    if (perm8) v = q4g_natural(v);
     *(u32x4*)(out + p * I + c) = v;
   }
 }

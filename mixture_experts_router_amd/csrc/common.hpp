@@ -131,18 +131,31 @@ __device__ __forceinline__ u32x4 perm8_nibble_order(u32x4 v) {
   return r;
 }
 
-// Inverse of perm8_nibble_order: (k0,k4) (k1,k5) (k2,k6) (k3,k7) -> k0..k7.
-__device__ __forceinline__ u32x4 perm8_natural_order(u32x4 v) {
+// The batched path's operand order for 4-bit weights: each 8-element block
+// as (k0,k2) (k4,k6) (k1,k3) (k5,k7), the order in which the GEMM turns a
+// word of eight codes into fp16 pairs (the low nibbles of its bytes, then
+// the high nibbles).  From natural pairs (k0,k1) (k2,k3) (k4,k5) (k6,k7):
+__device__ __forceinline__ u32x4 q4g_order(u32x4 v) {
   u32x4 r;
-  r.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (k0, k1)
-  r.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (k2, k3)
-  r.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (k4, k5)
-  r.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (k6, k7)
+  r.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (k0, k2)
+  r.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (k4, k6)
+  r.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (k1, k3)
+  r.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (k5, k7)
   return r;
 }
 
-// Position of element i (0..7) of an 8-element block in unpack order.
-__device__ __forceinline__ int perm8_slot(int i) { return (i & 3) * 2 + (i >> 2); }
+// Inverse of q4g_order: (k0,k2) (k4,k6) (k1,k3) (k5,k7) -> k0..k7.
+__device__ __forceinline__ u32x4 q4g_natural(u32x4 v) {
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // (k0, k1)
+  r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // (k2, k3)
+  r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // (k4, k5)
+  r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // (k6, k7)
+  return r;
+}
+
+// Position of element i (0..7) of an 8-element block in q4g order.
+__device__ __forceinline__ int q4g_slot(int i) { return (i & 1) * 4 + (i >> 1); }
 
 // ----------------------------------------------------- unpacking codes ---
 //

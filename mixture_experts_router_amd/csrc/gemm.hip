@@ -13,7 +13,7 @@
 //   GEMM_ROWS_F16      A = h rows in sorted order, B = down, fp16 output
 //
 // The A operand is fp16 in HBM, each 8-element block in the order in which
-// the weights unpack (4-bit: 0,4,1,5,2,6,3,7; otherwise natural): the
+// the weights unpack (4-bit: 0,2,4,6,1,3,5,7; otherwise natural): the
 // activations are converted once by prep_a_kernel and the fused epilogue
 // writes h that way.  Tile: BM = 32*MS rows x 256 columns (fused: 128
 // gate/up column pairs), 4 waves side by side along N, each 32*MS x 64; K
@@ -54,7 +54,7 @@ struct GemmParams {
   const int32_t* any_scaled;  // nonzero when some a_t > 0 (tokexp is read only then)
   uint32_t a_bytes;  // extent of the A rows (offsets at or past it read nothing)
   int32_t sb_up_delta;  // fused: bytes from a gate column's packed scales to its up column's
-  int perm8_out;  // fused: store h blocks in 4-bit unpack order
+  int perm8_out;  // fused: store h blocks in the 4-bit order (q4g_order)
   // tile order (see tile_of): n_tiles column tiles x m_tiles row tiles, in
   // groups of group_m row tiles; per_xcd consecutive tiles per XCD
   int n_tiles, m_tiles, group_m, per_xcd;
@@ -213,19 +213,19 @@ __device__ __forceinline__ f16x8 dequant_b(const u32x4* c, int j, uint32_t s_bit
       return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2));
     };
     if constexpr (BITS == 4) {
-      // bytes reordered to (b0, b2, b1, b3), so the low nibbles are codes
-      // (0, 4, 2, 6) and the high nibbles (1, 5, 3, 7), one per byte.  A byte
-      // holding q in 0..15 is the FP8 E4M3 pattern of q * 2^-9 (subnormal
-      // below 8, exponent field 1 from 8 on), so the scaled conversion with
-      // 2^9 gives the fp16 pair of codes exactly, one instruction per pair
+      // the low nibbles of the word's bytes are codes (0, 2, 4, 6), the high
+      // nibbles (1, 3, 5, 7), one per byte after two masks.  A byte holding
+      // q in 0..15 is the FP8 E4M3 pattern of q * 2^-9 (subnormal below 8,
+      // exponent field 1 from 8 on), so the scaled conversion with 2^9 gives
+      // a pair of codes exactly, one instruction per pair; the operand rows
+      // are in the matching order (q4g_order)
       const uint32_t w = j == 0 ? c[0].x : j == 1 ? c[0].y : j == 2 ? c[0].z : c[0].w;
-      const uint32_t v = __builtin_amdgcn_perm(w, w, 0x03010200u);
-      const uint32_t lo4 = v & 0x0F0F0F0Fu, hi4 = (v >> 4) & 0x0F0F0F0Fu;
+      const uint32_t lo4 = w & 0x0F0F0F0Fu, hi4 = (w >> 4) & 0x0F0F0F0Fu;
       auto fq = [&](f16x2 q) { return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, b2)); };
-      const u32x4 o = {fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo4, 512.0f, false)),   // (k0, k4)
-                       fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi4, 512.0f, false)),   // (k1, k5)
-                       fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo4, 512.0f, true)),    // (k2, k6)
-                       fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi4, 512.0f, true))};   // (k3, k7)
+      const u32x4 o = {fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo4, 512.0f, false)),   // (k0, k2)
+                       fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo4, 512.0f, true)),    // (k4, k6)
+                       fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi4, 512.0f, false)),   // (k1, k3)
+                       fq(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi4, 512.0f, true))};   // (k5, k7)
       (void)qc;
       return __builtin_bit_cast(f16x8, o);
     } else {
@@ -824,7 +824,7 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
           acc[mi][ni + HALFSUB][r] = ldexp_f(acc[mi][ni + HALFSUB][r], ea);
           const float hv = ldexp_f(swiglu(acc[mi][ni][r], acc[mi][ni + HALFSUB][r]), -2 * ea);
           const int col = col0 + 32 * ni + col_in;
-          const int at = prm.perm8_out ? (col & ~7) + perm8_slot(col & 7) : col;
+          const int at = prm.perm8_out ? (col & ~7) + q4g_slot(col & 7) : col;
           ((uint16_t*)prm.out)[orow + at] = f32_to_f16_bits(hv);
         }
         if (prm.pre) {
