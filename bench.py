@@ -51,6 +51,12 @@ WORKLOADS = {
                        label="prefill: 4096 tokens, H=4096, E=64, top-4, I=1408, NVFP4 weights, bf16, Zipf 1.2"),
     "entropy_q4": dict(recipe="entropy", pool=None, T=512, bits=4,
                        label="entropy-adaptive: 512 tokens (segment k=3), H=4096, E=32, I=2816, 4-bit g64, fp16"),
+    "entropy_all_q4": dict(recipe="entropy", pool=None, T=512, bits=4, segments=4,
+                           label="entropy-adaptive: 4 segments x 512 tokens (k 1/2/3/3), H=4096, E=32, I=2816, "
+                                 "4-bit g64, fp16"),
+    "entropy_all_fp16": dict(recipe="entropy", pool=None, T=512, bits=16, segments=4,
+                             label="entropy-adaptive: 4 segments x 512 tokens (k 1/2/3/3), H=4096, E=32, I=2816, "
+                                   "fp16 weights"),
     "entropy_fp16": dict(recipe="entropy", pool=None, T=512, bits=16,
                          label="entropy-adaptive: 512 tokens (segment k=3), H=4096, E=32, I=2816, fp16 weights"),
 }
@@ -222,6 +228,15 @@ def main():
 
     x_pool = dev_bits(inp.x, dt)
     wr = dev_bits(inp.wr, dt)
+    # entropy segments: one layer call per segment (its own tokens and router
+    # temperature, the same experts), a step being all of them
+    nseg = wl.get("segments", 1)
+    if nseg > 1:
+        seg_np = [mi.make_router_inputs(recipe, segment=sg)[:2] for sg in range(nseg)]
+        seg_dev = [(dev_bits(a, dt), dev_bits(b, dt)) for a, b in seg_np]
+    else:
+        seg_np = [(inp.x, inp.wr)]
+        seg_dev = [(x_pool, wr)]
     gate, up = dev_w(inp.gate), dev_w(inp.up)
     gate_up = moe.fuse_gate_up(gate, up)  # the caller then frees the separate tensors
     del gate, up
@@ -252,14 +267,29 @@ def main():
         ropt["groups"] = args.groups
     lopt = dict(ropt, capacity=args.capacity) if args.capacity else ropt
 
-    def step(i):
-        moe.layer_forward(x_of(i), wr, k, down, gate_up=gate_up, out=y, workspace=ws, **lopt)
+    def step(i, evs=None):
+        """One step; evs: the step's event pairs, handed to each call in turn
+        (every library call starts again at the first pair it is given)."""
+        if nseg > 1:
+            for c_, (xs_, wrs_) in enumerate(seg_dev):
+                if evs is not None:
+                    moe.debug_set_events(evs[2 * nk * c_:2 * nk * (c_ + 1)])
+                moe.layer_forward(xs_, wrs_, k, down, gate_up=gate_up, out=y, workspace=ws, **lopt)
+        else:
+            if evs is not None:
+                moe.debug_set_events(evs)
+            moe.layer_forward(x_of(i), wr, k, down, gate_up=gate_up, out=y, workspace=ws, **lopt)
 
-    # discover the kernel plan
-    step(0)
-    torch.cuda.synchronize()
-    plan = moe.last_plan()
+    # discover the kernel plan (every segment's call launches the same kernels)
+    plans = []
+    for xs_, wrs_ in seg_dev[:nseg]:
+        moe.layer_forward(xs_ if nseg > 1 else x_of(0), wrs_, k, down, gate_up=gate_up, out=y, workspace=ws, **lopt)
+        torch.cuda.synchronize()
+        plans.append(moe.last_plan())
+    assert all(p_ == plans[0] for p_ in plans), plans
+    plan = plans[0]
     nk = len(plan)
+    nl = nk * nseg  # launches per step
 
     for i in range(args.warmup):
         step(i)
@@ -322,7 +352,7 @@ def main():
     # take the kernel's own start and end timestamps on the launch stream.
     # Each chunk of steps is queued behind a spin kernel, so the GPU runs the
     # chunk back to back as in the untimed loop.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(K)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nl)] for _ in range(K)]
     for evs in events:  # create the underlying HIP events
         for e in evs:
             e.record(stream)
@@ -332,8 +362,7 @@ def main():
     for c0 in range(0, K, CH):
         torch.cuda._sleep(20_000_000)
         for i in range(c0, min(K, c0 + CH)):
-            moe.debug_set_events(events[i])
-            step(args.warmup + i)
+            step(args.warmup + i, events[i])
     torch.cuda.synchronize()
     moe.debug_set_events(None)
 
@@ -344,21 +373,20 @@ def main():
         # weight byte of the previous steps is left in the Infinity Cache
         buf = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
         nf = min(K, 64)
-        fevents = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(nf)]
+        fevents = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nl)] for _ in range(nf)]
         for evs in fevents:
             for e in evs:
                 e.record(stream)
         torch.cuda.synchronize()
         for i in range(nf):
             buf.fill_(i & 0xFF)
-            moe.debug_set_events(fevents[i])
-            step(args.warmup + i)
+            step(args.warmup + i, fevents[i])
         torch.cuda.synchronize()
         moe.debug_set_events(None)
         fk = np.zeros(nk)
         for evs in fevents:
-            for j in range(nk):
-                fk[j] += evs[2 * j].elapsed_time(evs[2 * j + 1])
+            for j in range(nl):
+                fk[j % nk] += evs[2 * j].elapsed_time(evs[2 * j + 1])
         fk = fk / nf * 1e3
         flush = {"mib": args.flush_mib, "steps": nf, "per_kernel_us": [round(float(v), 3) for v in fk],
                  "kernel_sum_us": round(float(fk.sum()), 3)}
@@ -377,12 +405,16 @@ def main():
     mode = "graph" if graph_s is not None and graph_s <= eager_s else "eager"
     elapsed = best_s
     ms_per_step = elapsed * 1e3 / K
-    value = K * T / elapsed
-    per_kernel = np.zeros(nk)
+    value = K * T * nseg / elapsed
+    per_kernel = np.zeros(nk)  # summed over the step's calls
+    per_call = np.zeros(nseg)
     for evs in events:
-        for j in range(nk):
-            per_kernel[j] += evs[2 * j].elapsed_time(evs[2 * j + 1])
+        for j in range(nl):
+            d_ = evs[2 * j].elapsed_time(evs[2 * j + 1])
+            per_kernel[j % nk] += d_
+            per_call[j // nk] += d_
     per_kernel_us = per_kernel / K * 1e3
+    per_call_us = per_call / K * 1e3
     gpu_step_us = float(sum(per_kernel_us))
     log("plan:", ", ".join("%s %.2fus" % (n, t) for n, t in zip(plan, per_kernel_us)))
     log("per step: eager %.2f us, graph %s us, sum of kernel durations %.2f us" % (
@@ -392,10 +424,12 @@ def main():
     j = int(np.argmax(per_kernel_us))
     kern = plan[j]
     # routing of a representative step (decode: over the pool; averaged bytes)
-    r = moe.route(x_pool, wr, k, **ropt)
-    torch.cuda.synchronize()
-    idx_all = r["idx"].cpu().numpy()
-    ku = int(r["k_used"].item())
+    routes = []
+    for xs_, wrs_ in seg_dev:
+        r = moe.route(xs_, wrs_, k, **ropt)
+        torch.cuda.synchronize()
+        routes.append((r["idx"].cpu().numpy(), int(r["k_used"].item())))
+    idx_all, ku = routes[0]
     if wl["pool"]:
         bs, fs = [], []
         for s in range(min(wl["pool"], K)):
@@ -406,8 +440,12 @@ def main():
             fs.append(f_)
         alg_b, alg_f = float(np.mean(bs)), float(np.mean(fs))
     else:
-        alg_b, alg_f = algorithmic(args.workload, kern, T=T, H=H, E=E, I=I, bits=bits, idx=idx_all, k_used=ku,
-                                   kcap=kcap, keep=capacity_keep(idx_all, ku, args.capacity) if args.capacity else None)
+        alg_b, alg_f = 0.0, 0.0
+        for idx_s, ku_s in routes:  # summed over the step's calls
+            b_, f_ = algorithmic(args.workload, kern, T=T, H=H, E=E, I=I, bits=bits, idx=idx_s, k_used=ku_s,
+                                 kcap=kcap, keep=capacity_keep(idx_s, ku_s, args.capacity) if args.capacity else None)
+            alg_b += b_
+            alg_f += f_
     dur_s = per_kernel_us[j] * 1e-6
     gbs = alg_b / dur_s / 1e9
     tflops = alg_f / dur_s / 1e12
@@ -422,7 +460,9 @@ def main():
     roof["algorithmic_bytes"] = int(alg_b)
     roof["algorithmic_flops"] = int(alg_f)
     # counters are taken without routing options: with options the traffic is unmeasured
-    roof["traffic"] = None if lopt else traffic_from_profiles(kern, args.workload)
+    # (per dispatch; a step of several calls launches the kernel once per call)
+    tr_ = None if lopt else traffic_from_profiles(kern, args.workload)
+    roof["traffic"] = tr_ * nseg if tr_ is not None else None
 
     # ---- the whole layer against its roofline: all algorithmic bytes (or
     # flops) of a step over the measured time per step
@@ -436,8 +476,12 @@ def main():
             lf.append(f_)
         lay_b, lay_f = float(np.mean(lb)), float(np.mean(lf))
     else:
-        lay_b, lay_f = layer_algorithmic(T=T, H=H, E=E, I=I, bits=bits, idx=idx_all, k_used=ku,
-                                         keep=capacity_keep(idx_all, ku, args.capacity) if args.capacity else None)
+        lay_b, lay_f = 0.0, 0.0
+        for idx_s, ku_s in routes:
+            b_, f_ = layer_algorithmic(T=T, H=H, E=E, I=I, bits=bits, idx=idx_s, k_used=ku_s,
+                                       keep=capacity_keep(idx_s, ku_s, args.capacity) if args.capacity else None)
+            lay_b += b_
+            lay_f += f_
     step_s = ms_per_step * 1e-3
     t_hbm = lay_b / (HBM_PEAK_GBS * 1e9)
     t_mfma = lay_f / (MFMA_F16_PEAK_TFLOPS * 1e12)
@@ -480,36 +524,46 @@ def main():
             cpu["value_1core"] = round(n1 / t1, 3)
             cpu["sample_1core"] = "%d single tokens of the decode pool on 1 thread, %.1fs" % (n1, t1)
         else:
-            idx_o, w_o, ku_o, _ = oracle.route(inp.x, inp.wr, inp.dtype, k, **oopt)
+            # per call (segment): routing of all T tokens plus T token FFNs at
+            # the cost of a random sample of them; the step is the sum
             rng = np.random.default_rng(0)
+
+            def sample(n_tok):
+                t_route_, t_tok_, total_ = 0.0, 0.0, 0.0
+                for xn, wrn in seg_np:
+                    t = time.perf_counter()
+                    idx_o, w_o, ku_o, _ = oracle.route(xn, wrn, inp.dtype, k, **oopt)
+                    tr = time.perf_counter() - t
+                    toks = np.sort(rng.choice(T, n_tok, replace=False))
+                    t = time.perf_counter()
+                    oracle.tokens_forward(xn, inp.dtype, toks, idx_o, w_o, ku_o, gu_np, inp.down)
+                    tt = time.perf_counter() - t
+                    t_route_ += tr
+                    t_tok_ += tt
+                    total_ += tr + tt / n_tok * T
+                return t_route_, t_tok_, total_
+
+            x0, wr0 = seg_np[-1]  # the last call: the largest k of the entropy segments
+            idx_o, w_o, ku_o, _ = oracle.route(x0, wr0, inp.dtype, k, **oopt)
             t = time.perf_counter()
-            oracle.tokens_forward(inp.x, inp.dtype, [0], idx_o, w_o, ku_o, gu_np, inp.down)
+            oracle.tokens_forward(x0, inp.dtype, [0], idx_o, w_o, ku_o, gu_np, inp.down)
             per_tok = time.perf_counter() - t
-            n = int(max(2, min(T, args.cpu_seconds / max(per_tok, 1e-6))))
-            toks = np.sort(rng.choice(T, n, replace=False))
-            t = time.perf_counter()
-            oracle.route(inp.x, inp.wr, inp.dtype, k, **oopt)
-            t_route = time.perf_counter() - t
-            t = time.perf_counter()
-            oracle.tokens_forward(inp.x, inp.dtype, toks, idx_o, w_o, ku_o, gu_np, inp.down)
-            t_tok = time.perf_counter() - t
-            # whole-batch rate: routing of all T tokens plus T token FFNs at the sampled per-token cost
-            total = t_route + t_tok / n * T
-            cpu = {"value": round(T / total, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-                   "sample": "routing of all %d tokens (%.1fs) + expert FFN of %d sampled tokens (%.1fs), "
-                             "scaled to the batch" % (T, t_route, n, t_tok)}
+            n = int(max(2, min(T, args.cpu_seconds / nseg / max(per_tok, 1e-6))))
+            t_route, t_tok, total = sample(n)
+            what = "routing of all %d tokens (%.1fs) + expert FFN of %d sampled tokens (%.1fs)" % (T, t_route, n,
+                                                                                                  t_tok)
+            if nseg > 1:
+                what = "per segment (%d segments): %d tokens routed, %d sampled; totals: routing %.1fs, FFN %.1fs" % (
+                    nseg, T, n, t_route, t_tok)
+            cpu = {"value": round(T * nseg / total, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                   "sample": what + ", scaled to the batch"}
             oracle.set_threads(1)
             n1 = max(2, n // max(cores, 1))
-            t = time.perf_counter()
-            oracle.route(inp.x, inp.wr, inp.dtype, k, **oopt)
-            t_route1 = time.perf_counter() - t
-            t = time.perf_counter()
-            oracle.tokens_forward(inp.x, inp.dtype, toks[:n1], idx_o, w_o, ku_o, gu_np, inp.down)
-            t_tok1 = time.perf_counter() - t
+            t_route1, t_tok1, total1 = sample(n1)
             oracle.set_threads(cores)
-            cpu["value_1core"] = round(T / (t_route1 + t_tok1 / n1 * T), 3)
-            cpu["sample_1core"] = "1 thread: routing of all %d tokens (%.1fs) + expert FFN of %d sampled tokens " \
-                                  "(%.1fs), scaled to the batch" % (T, t_route1, n1, t_tok1)
+            cpu["value_1core"] = round(T * nseg / total1, 3)
+            cpu["sample_1core"] = "1 thread: routing %.1fs + expert FFN of %d sampled tokens per call (%.1fs), " \
+                                  "scaled to the batch" % (t_route1, n1, t_tok1)
 
     out = {
         "metric": METRIC,
@@ -524,15 +578,18 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": wl["label"], "tokens_per_step": T, "hidden": H, "experts": E, "top_k": k,
+        "config": {"workload": wl["label"], "tokens_per_step": T * nseg, "hidden": H, "experts": E, "top_k": k,
                    "intermediate": I, "weight_bits": bits, "activations": inp.dtype,
                    "arithmetic": "fp16 operands (dequantised weights, activations, SwiGLU rows), fp32 accumulation",
-                   "launch": mode, "eager_tokens_per_s": round(K * T / eager_s, 2),
-                   "graph_tokens_per_s": round(K * T / graph_s, 2) if graph_s else None,
+                   "launch": mode, "eager_tokens_per_s": round(K * T * nseg / eager_s, 2),
+                   "graph_tokens_per_s": round(K * T * nseg / graph_s, 2) if graph_s else None,
                    "kernels_per_step": nk, "plan": plan,
                    "routing_options": {"load_aware_alpha": args.load_aware, "groups": args.groups,
                                        "capacity": args.capacity} if lopt else None,
                    "per_kernel_us": [round(float(v), 3) for v in per_kernel_us],
+                   "segments": [{"segment": sg, "tokens": T, "k_used": routes[sg][1],
+                                 "kernel_sum_us": round(float(per_call_us[sg]), 3)} for sg in range(nseg)]
+                   if nseg > 1 else None,
                    "tuning": args.tune or None,
                    "cache_flush": flush},
         "roofline": roof,
