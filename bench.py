@@ -494,6 +494,28 @@ def main():
                          "unit": "TFLOP/s", "frac": round(t_mfma / step_s, 4), "algorithmic_bytes": int(lay_b),
                          "algorithmic_flops": int(lay_f), "roofline_us": round(t_mfma * 1e6, 2)}
 
+    # ---- the practical read ceiling: the library's streaming-read reference
+    # (16-byte non-temporal loads, a contiguous segment per workgroup) over
+    # as many bytes as a step's algorithmic bytes, timed with events over 10
+    # launches
+    nbytes = int(min(max(lay_b, 1 << 24), (1 << 32) - (1 << 20))) // 16 * 16
+    sbuf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(moe.STREAM_READ_WAVES, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        moe.debug_stream_read(sbuf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        moe.debug_stream_read(sbuf, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s_us = e0.elapsed_time(e1) * 1e3 / 10
+    s_gbs = nbytes / (s_us * 1e-6) / 1e9
+    roof["stream_read"] = {"bytes": nbytes, "us": round(s_us, 2), "achieved": round(s_gbs, 1), "unit": "GB/s",
+                           "frac": round(s_gbs / HBM_PEAK_GBS, 4)}
+    roof["layer"]["bytes_rate_vs_stream_read"] = round(lay_b / step_s / 1e9 / s_gbs, 4)
+    del sbuf, sink
+
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu_baseline:

@@ -404,10 +404,27 @@ int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
  * the 64- and 128-row tiles (2, splitting each group's k-steps; other values:
  * 1), key 7 = workgroups per CU at the 32- and 64-row tiles (1: the whole LDS
  * for one, deeper pipeline and two-group 8-bit stages; 2: two; other values:
- * one for 8-bit weights at 32-row tiles, else two).
+ * one for 8-bit weights at 32-row tiles, else two), key 8 = waves per
+ * (token, slot) pair of the decode gate+up kernel (2: from the resident-wave
+ * target alone; other values: as many as give every wave the same number of
+ * row iterations, at most that target).
  * Values <= 0 are ignored.  Results do not depend on them.
  */
 void moe_debug_set_tuning(int32_t key, int32_t value);
+
+/*
+ * Measurement reference: a plain streaming read of `bytes` bytes at `src`
+ * (device memory, 16-byte aligned, bytes a multiple of 16 and below 4 GiB)
+ * (16-byte non-temporal buffer loads as in the decode kernels, four per
+ * lane in flight, each of 2048 workgroups of four waves streaming its own
+ * contiguous segment).  It bounds what a weight-streaming kernel can reach
+ * on this device.  Each wave writes the XOR of the 32-bit words it read to
+ * sink[wave] (device memory, MOE_STREAM_READ_WAVES words; every word of src
+ * is read exactly once, so the XOR of the sink equals the XOR of src).
+ * Errors: MOE_ERR_NULL, MOE_ERR_ALIGN, MOE_ERR_SHAPE (bytes), MOE_ERR_DEVICE.
+ */
+#define MOE_STREAM_READ_WAVES 8192
+moe_status moe_debug_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

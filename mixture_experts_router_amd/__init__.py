@@ -38,7 +38,7 @@ EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_ex", "moe_topk_fr
            "moe_layer_forward_noalloc",
            "moe_expert_load_stats", "moe_fuse_gate_up", "moe_packed_sb_bytes", "moe_pack_sb", "moe_status_string",
            "moe_debug_set_events",
-           "moe_debug_last_plan", "moe_debug_set_tuning")
+           "moe_debug_last_plan", "moe_debug_set_tuning", "moe_debug_stream_read")
 
 
 class MoeError(RuntimeError):
@@ -124,6 +124,8 @@ def lib() -> ctypes.CDLL:
     L.moe_debug_last_plan.restype = i32
     L.moe_debug_set_tuning.argtypes = [i32, i32]
     L.moe_debug_set_tuning.restype = None
+    L.moe_debug_stream_read.argtypes = [vp, sz, vp, vp]
+    L.moe_debug_stream_read.restype = i32
     _lib = L
     return L
 
@@ -415,8 +417,22 @@ def debug_set_tuning(key: int, value: int) -> None:
     """Launch-shape knob (0: decode gate+up waves/CU, 1: decode down waves/CU, 2: GEMM row tiles per group,
     3: GEMM row tile 32/64/128 (else automatic), 4: GEMM K groups per stage (1 or 2), 5: GEMM N subtiles
     per wave (2 or 4), 6: GEMM waves per column block (1 or 2), 7: GEMM workgroups per CU at 32/64-row
-    tiles (1 or 2))."""
+    tiles (1 or 2), 8: decode gate+up waves per pair (2: from the wave target alone, else equal iterations
+    per wave))."""
     lib().moe_debug_set_tuning(int(key), int(value))
+
+
+STREAM_READ_WAVES = 8192
+
+
+def debug_stream_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The streaming-read reference over all of `src` (see moe_debug_stream_read);
+    returns the int32 sink [STREAM_READ_WAVES] of per-wave XORs."""
+    if sink is None:
+        sink = torch.empty(STREAM_READ_WAVES, dtype=torch.int32, device=src.device)
+    nbytes = src.numel() * src.element_size()
+    _check(lib().moe_debug_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "moe_debug_stream_read")
+    return sink
 
 
 def source_hash() -> str:

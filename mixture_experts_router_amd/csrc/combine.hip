@@ -249,4 +249,40 @@ hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, in
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- stream read ---
+//
+// The practical read ceiling for weight-streaming kernels: 16-byte
+// non-temporal buffer loads, four per lane in flight, each of 2048
+// workgroups streaming its own contiguous segment of the range (measured
+// 6.7-7.0 TB/s at 0.3-1 GB, against 5.5-6.1 TB/s when all workgroups sweep
+// the range together grid-stride).  Loads past the end go through the
+// descriptor's range check and read nothing.
+constexpr int STREAM_BLOCKS = 2048;
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* __restrict__ src, uint32_t bytes,
+                                                          uint32_t* __restrict__ sink) {
+  const rsrc_t r = make_rsrc(src, bytes);
+  // ceil(bytes / blocks) rounded up to whole 4 KB pieces: the segments cover the range
+  const uint64_t seg = (((uint64_t)bytes + STREAM_BLOCKS - 1) / STREAM_BLOCKS + 4095u) & ~(uint64_t)4095u;
+  const uint64_t b0 = (uint64_t)blockIdx.x * seg, b1 = b0 + seg;
+  uint32_t acc = 0;
+  for (uint64_t o0 = b0 + threadIdx.x * 16u; o0 < b1; o0 += 4u * 4096u) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t o = o0 + (uint64_t)u * 4096u;  // 256 lanes x 16 B = one 4 KB piece per load
+      v[u] = (o < b1 && o < bytes) ? buf_load16_nt(r, (uint32_t)o) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) acc ^= __shfl_xor(acc, d, WAVE);
+  if (lane_id() == 0) sink[blockIdx.x * 4 + wave_id()] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, uint32_t bytes, uint32_t* sink, hipStream_t st) {
+  launch_kernel(stream_read_kernel, STREAM_BLOCKS, 256, 0, st, (const uint8_t*)src, bytes, sink);
+  return hipGetLastError();
+}
+
 }  // namespace moe

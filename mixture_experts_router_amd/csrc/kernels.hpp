@@ -165,6 +165,10 @@ hipError_t launch_gather_preact(const float* g, const float* u, const int32_t* p
                                 int kcap, const int32_t* k_used_dev, int k_static, hipStream_t st);
 // copy n int32/fp32 words
 hipError_t launch_copy_words(const void* src, void* dst, int64_t n, hipStream_t st);
+// streaming read of `bytes` (multiple of 16, < 4 GiB) at src, a contiguous
+// segment per workgroup; sink[w] = XOR of the words wave w read (2048
+// workgroups of 256 threads: 8192 waves)
+hipError_t launch_stream_read(const void* src, uint32_t bytes, uint32_t* sink, hipStream_t st);
 // scales/biases of rows [0, N) of E experts -> packed_sb layout (see moe.h);
 // nvfp4: s holds E4M3 block-scale bytes [rows, K/16] and b is unused
 hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, int K, int64_t src_stride, uint8_t* dst,

@@ -755,6 +755,24 @@ void moe_debug_set_events(void* const* events, int32_t n) {
 
 void moe_debug_set_tuning(int32_t key, int32_t value) { moe::set_tuning(key, value); }
 
+moe_status moe_debug_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  try {
+    if (!src || !sink) return MOE_ERR_NULL;
+    if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return MOE_ERR_ALIGN;
+    if (bytes == 0 || bytes % 16 != 0 || bytes >= (size_t(1) << 32)) return MOE_ERR_SHAPE;
+    DevProps props;
+    moe_status s = device_props(&props);
+    if (s != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    plan_begin(st);
+    HIP_TRY(moe::launch_stream_read(src, (uint32_t)bytes, sink, st));
+    plan_step("stream_read", st);
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
+}
+
 int32_t moe_debug_last_plan(char* buf, size_t buf_bytes) {
   const std::string& p = g_prof.plan;
   if (buf && buf_bytes > 0) {

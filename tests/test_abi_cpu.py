@@ -196,6 +196,17 @@ def test_nvfp4_fuse_and_pack_validation():
     assert moe.STATUS[L.moe_pack_sb(ctypes.byref(F4(8, 256, 256, gs=64)), P, None)] == "MOE_ERR_QUANT"
 
 
+def test_stream_read_validation():
+    L = moe.lib()
+    sink = P + 1024
+    assert moe.STATUS[L.moe_debug_stream_read(None, 1024, sink, None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[L.moe_debug_stream_read(P, 1024, None, None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[L.moe_debug_stream_read(P + 8, 1024, sink, None)] == "MOE_ERR_ALIGN"
+    assert moe.STATUS[L.moe_debug_stream_read(P, 1024, sink + 2, None)] == "MOE_ERR_ALIGN"
+    for bad in (0, 15, 1000, 1 << 32):
+        assert moe.STATUS[L.moe_debug_stream_read(P, bad, sink, None)] == "MOE_ERR_SHAPE", bad
+
+
 def test_route_validation():
     L = moe.lib()
     ws = 1 << 20

@@ -22,6 +22,8 @@ GRAPH_CASES = {
     "batched_mfma": ("batched_decode", dict(T=96, H=512, E=8, I=320), 32, {}),
     "entropy_two_pass": ("entropy", dict(T=192, H=512, E=16, I=192, bits=4, segment=2), 64, {}),
     "prefill_opts": ("prefill", dict(T=600, H=512, E=16, I=192), 200, dict(groups=4, capacity=96, alpha=0.5)),
+    "decode_f4": ("decode_b1", dict(T=6, H=1024, E=16, I=704, fmt="nvfp4"), 1, {}),
+    "batched_f4": ("prefill", dict(T=300, H=512, E=16, I=192, fmt="nvfp4"), 96, {}),
 }
 
 

@@ -416,6 +416,18 @@ def _token_exponent(x_bits_row: np.ndarray) -> int:
     return max(0, e - 132)
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096, 8 << 20, (37 << 20) + 48])
+def test_stream_read_reads_every_word_once(nbytes):
+    # the measurement reference's sink XORs fold to the XOR of the buffer
+    g = torch.Generator().manual_seed(nbytes % 1000003)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
+    sink = moe.debug_stream_read(src.cuda())
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(src.numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
+
+
 @pytest.mark.parametrize("recipe,kw,flag", [
     ("batched_decode", dict(T=40, H=512, E=8, I=320), moe.FLAG_FORCE_MFMA),   # 8-bit, batched path
     ("prefill", dict(T=300, H=512, E=16, I=192), moe.FLAG_FORCE_MFMA),        # 4-bit, batched path

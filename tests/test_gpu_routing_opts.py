@@ -87,6 +87,8 @@ LAYER_CASES = {
     "decode_q5": ("decode_b1", dict(T=3, H=512, E=16, I=320, bits=5), 4),
     "decode_q6": ("decode_b1", dict(T=2, H=1024, E=16, I=704, bits=6), 4),
     "batched_q5": ("prefill", dict(T=200, H=512, E=16, I=256, bits=5), 4),
+    "decode_f4": ("decode_b1", dict(T=3, H=512, E=16, I=320, fmt="nvfp4"), 4),
+    "batched_f4": ("prefill", dict(T=200, H=512, E=16, I=256, fmt="nvfp4"), 4),
 }
 
 
@@ -170,6 +172,8 @@ CAP_CASES = {
     "entropy_q4": ("entropy", dict(T=96, H=512, E=16, I=192, bits=4, segment=2), [5]),
     "decode_q5": ("decode_b1", dict(T=4, H=512, E=4, k=2, I=320, bits=5), [1, 3]),
     "decode_q6": ("decode_b1", dict(T=4, H=512, E=4, k=2, I=320, bits=6), [1, 3]),
+    "decode_f4": ("decode_b1", dict(T=4, H=512, E=4, k=2, I=320, fmt="nvfp4"), [1, 3]),
+    "prefill_f4": ("prefill", dict(T=300, H=512, E=16, I=192, fmt="nvfp4"), [20, 64]),
 }
 
 
