@@ -175,6 +175,8 @@ def main():
     ap.add_argument("--capacity", type=int, default=0, help="expert capacity: at most this many pairs per expert")
     ap.add_argument("--tune", action="append", default=[], metavar="KEY=VALUE",
                     help="launch-shape knob for measurement sweeps (moe_debug_set_tuning); results do not depend on it")
+    ap.add_argument("--no-packed-q", action="store_true",
+                    help="batched workloads: keep the row-major codes only (no packed_q repack)")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="also time the layer's kernels with a write of this many MiB between steps, which "
                          "evicts the 256 MB Infinity Cache, so their weight bytes must come from HBM")
@@ -241,10 +243,14 @@ def main():
     gate_up = moe.fuse_gate_up(gate, up)  # the caller then frees the separate tensors
     del gate, up
     down = dev_w(inp.down)
-    if bits != 16 and wl["T"] > 1:
-        # one-time repack of scales and biases for the batched path (like the
-        # gate/up fusion, done when the weights are loaded)
-        gate_up, down = moe.pack_sb(gate_up), moe.pack_sb(down)
+    if wl["T"] > 1:
+        # one-time repacks for the batched path (like the gate/up fusion, done
+        # when the weights are loaded): scales and biases, and the codes in
+        # 32-row blocks (a second copy of the codes)
+        if bits != 16:
+            gate_up, down = moe.pack_sb(gate_up), moe.pack_sb(down)
+        if not args.no_packed_q:
+            gate_up, down = moe.pack_q(gate_up), moe.pack_q(down)
     torch.cuda.synchronize()
 
     T = wl["T"]
@@ -613,7 +619,8 @@ def main():
                                  "kernel_sum_us": round(float(per_call_us[sg]), 3)} for sg in range(nseg)]
                    if nseg > 1 else None,
                    "tuning": args.tune or None,
-                   "cache_flush": flush},
+                   "cache_flush": flush,
+                   "packed_q": bool(wl["T"] > 1 and not args.no_packed_q)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

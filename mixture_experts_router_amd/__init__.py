@@ -36,7 +36,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("moe_route_workspace_size", "moe_route", "moe_route_ex", "moe_topk_from_logits",
            "moe_topk_from_logits_ex", "moe_layer_workspace_size", "moe_layer_forward", "moe_layer_forward_ex",
            "moe_layer_forward_noalloc",
-           "moe_expert_load_stats", "moe_fuse_gate_up", "moe_packed_sb_bytes", "moe_pack_sb", "moe_status_string",
+           "moe_expert_load_stats", "moe_fuse_gate_up", "moe_packed_sb_bytes", "moe_pack_sb", "moe_packed_q_bytes", "moe_pack_q", "moe_status_string",
            "moe_debug_set_events",
            "moe_debug_last_plan", "moe_debug_set_tuning", "moe_debug_stream_read")
 
@@ -52,7 +52,7 @@ class CWeights(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("E", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("expert_stride_rows", ctypes.c_int64), ("packed_sb", ctypes.c_void_p),
-                ("format", ctypes.c_int32), ("tensor_scale", ctypes.c_float)]
+                ("format", ctypes.c_int32), ("tensor_scale", ctypes.c_float), ("packed_q", ctypes.c_void_p)]
 
 
 FMT_AFFINE, FMT_NVFP4 = 0, 1
@@ -115,6 +115,9 @@ def lib() -> ctypes.CDLL:
     L.moe_packed_sb_bytes.argtypes = [i32, ctypes.c_int64, i32]
     L.moe_packed_sb_bytes.restype = sz
     L.moe_pack_sb.argtypes = [ctypes.POINTER(CWeights), vp, vp]
+    L.moe_packed_q_bytes.argtypes = [i32, ctypes.c_int64, i32, i32]
+    L.moe_packed_q_bytes.restype = sz
+    L.moe_pack_q.argtypes = [ctypes.POINTER(CWeights), vp, vp]
     L.moe_pack_sb.restype = i32
     L.moe_status_string.argtypes = [i32]
     L.moe_status_string.restype = ctypes.c_char_p
@@ -173,7 +176,9 @@ class Weights:
     ``row_offset``/``stride`` describe a view (the gate or up half of a fused
     tensor): rows start ``row_offset`` rows in, experts are ``stride`` rows apart.
     ``packed_sb`` (optional, uint8): the scales and biases repacked by pack_sb
-    for the batched path (the whole tensor's; views share it).
+    for the batched path (the whole tensor's; views share it).  ``packed_q``
+    (optional, uint8): the codes repacked by pack_q for the batched path (the
+    whole tensor's; views share it).
     """
 
     q: torch.Tensor
@@ -189,6 +194,7 @@ class Weights:
     packed_sb: Optional[torch.Tensor] = None
     fmt: str = "affine"  # "affine" | "nvfp4"
     tensor_scale: float = 1.0
+    packed_q: Optional[torch.Tensor] = None
 
     _cstruct: Optional[CWeights] = dataclasses.field(default=None, repr=False, compare=False)
 
@@ -204,8 +210,12 @@ class Weights:
         s = None if self.scales is None else self.scales.data_ptr() + self.row_offset * srb
         b = None if self.biases is None else self.biases.data_ptr() + self.row_offset * srb
         sb = None if self.packed_sb is None else self.packed_sb.data_ptr() + self.row_offset * 8
+        pq = None
+        if self.packed_q is not None:
+            np_ = (self.K + 127) // 128
+            pq = self.packed_q.data_ptr() + self.row_offset // 32 * np_ * 32 * 16 * self.bits
         self._cstruct = CWeights(q, s, b, self.E, self.N, self.K, self.bits, self.group_size, stride, sb,
-                                 FMT_NVFP4 if f4 else FMT_AFFINE, float(self.tensor_scale))
+                                 FMT_NVFP4 if f4 else FMT_AFFINE, float(self.tensor_scale), pq)
         return self._cstruct
 
     def split_gate_up(self):
@@ -400,6 +410,20 @@ def pack_sb(w: Weights, stream=None) -> Weights:
     out = torch.empty(nbytes, dtype=torch.uint8, device=w.q.device)
     _check(lib().moe_pack_sb(ctypes.byref(w.c()), _ptr(out), _stream(stream)), "moe_pack_sb")
     return dataclasses.replace(w, packed_sb=out, _cstruct=None)
+
+
+def pack_q(w: Weights, stream=None) -> Weights:
+    """The same weights with packed_q filled (the codes in the batched path's
+    block layout; a one-time repack, a second copy of the codes)."""
+    if w.row_offset != 0:
+        raise ValueError("pack_q: needs a whole tensor")
+    stride = w.N if w.stride is None else w.stride
+    nbytes = int(lib().moe_packed_q_bytes(w.E, stride, w.K, w.bits))
+    if nbytes == 0:
+        raise ValueError("pack_q: rows per expert and N must be multiples of 32")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w.q.device)
+    _check(lib().moe_pack_q(ctypes.byref(w.c()), _ptr(out), _stream(stream)), "moe_pack_q")
+    return dataclasses.replace(w, packed_q=out, _cstruct=None)
 
 
 def debug_set_events(events: Optional[Sequence]) -> None:

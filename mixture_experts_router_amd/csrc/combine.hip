@@ -249,6 +249,54 @@ hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, in
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------- packed_q ---
+//
+// One thread per 16-byte piece of the packed_q layout (moe.h): piece c of
+// row r of 32-row block j, group pair p, expert e.  Source rows are read as
+// 32-bit words (5-bit rows are only 8-byte aligned); words past the row's
+// code bytes (a missing last group) and rows at or past N are zero.
+__global__ __launch_bounds__(256) void pack_q_kernel(const uint8_t* __restrict__ q, int N, int rb, int pb, int np,
+                                                     int nb_src, int nb_dst, int64_t src_stride,
+                                                     uint8_t* __restrict__ dst, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int ppr = pb / 16;
+  int64_t rest = i;
+  const int c = (int)(rest % ppr);
+  rest /= ppr;
+  const int r = (int)(rest % 32);
+  rest /= 32;
+  const int p = (int)(rest % np);
+  rest /= np;
+  const int j = (int)(rest % nb_src);
+  const int64_t e = rest / nb_src;
+  const int n = 32 * j + r;
+  const int64_t col = (int64_t)p * pb + (int64_t)c * 16;  // byte within the row's codes
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (n < N) {
+    const uint32_t* src = (const uint32_t*)(q + (e * src_stride + n) * rb);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (col + 4 * u < rb) w[u] = src[(col >> 2) + u];
+  }
+  *(u32x4*)(dst + (((e * nb_dst + j) * np + p) * 32 + r) * pb + c * 16) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+hipError_t launch_pack_q(const uint8_t* q, int E, int N, int K, int bits, int64_t src_stride, uint8_t* dst,
+                         int64_t dst_stride, hipStream_t st) {
+  const int rb = K * code_bits(bits) / 8;
+  const int pb = (int)packed_q_pair_bytes(bits);
+  const int np = (K + 127) / 128;
+  const int nb_src = (N + 31) / 32;
+  const int nb_dst = (int)((dst_stride + 31) / 32);
+  const int64_t total = (int64_t)E * nb_src * np * 32 * (pb / 16);
+  if (total <= 0) return hipSuccess;
+  if ((total + 255) / 256 > 0x7FFFFFFF || rb % 4 != 0) return hipErrorInvalidValue;
+  launch_kernel(pack_q_kernel, (unsigned)((total + 255) / 256), 256, 0, st, q, N, rb, pb, np, nb_src, nb_dst,
+                src_stride, dst, total);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------- stream read ---
 //
 // The practical read ceiling for weight-streaming kernels: 16-byte

@@ -412,17 +412,21 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
     return valid[ni] ? c : 0;
   };
   const int64_t row_bytes = (int64_t)K * code_bits(BITS) / 8;
+  // packed_q: each 32-row block's group pairs contiguous (PB bytes per row and
+  // pair), so a step streams 32*PB contiguous bytes per block
+  const bool tiled = prm.w0.pq != nullptr;
+  constexpr int PB = 16 * code_bits(BITS);
+  const int np = (ng + 1) / 2;
   const uint8_t* qbase[NSUB];
 #pragma unroll
   for (int ni = 0; ni < NSUB; ++ni) {
     const WView& v = *view[ni];
-    qbase[ni] = v.q + (int64_t)e * v.stride * row_bytes;  // the expert's first row
+    qbase[ni] = tiled ? v.pq + (int64_t)e * v.pq_expert : v.q + (int64_t)e * v.stride * row_bytes;  // the expert's start
   }
   // ---- scales and biases (packed_sb layout: 8 bytes per column and group
   // pair, columns contiguous): one load per step, lane l takes the 16 bytes
   // of columns 2(c%16), 2(c%16)+1 of subtile c/16, c = l % (16 NSUB); the up
   // columns of the fused tensor lie sb_up_delta bytes after the gate columns
-  const int np = (ng + 1) / 2;
   const int64_t sb_expert = (int64_t)np * prm.w0.sb_stride * 8;
   const rsrc_t rsb = make_rsrc(prm.w0.sb + (BITS != 16 ? e * sb_expert : 0), (uint32_t)sb_expert);
   uint32_t sb_off;
@@ -455,7 +459,9 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
     const int r_in = live ? item / G::LPR : 0;
     const int pl = live ? item % G::LPR : 0;
     const int piece = G::WHOLE ? pl ^ piece_swizzle<G::SEG>(sub * 32 + r_in) : pl;
-    b_off[qq] = (uint32_t)(column(sub, r_in) * row_bytes) + (uint32_t)piece * 16u;
+    const int c = column(sub, r_in);
+    b_off[qq] = (tiled ? (uint32_t)((((int64_t)(c >> 5) * np) * 32 + (c & 31)) * PB) : (uint32_t)(c * row_bytes)) +
+                (uint32_t)piece * 16u;
   }
   const int nst = ng / KG;  // pipeline steps (the launcher makes KG divide ng)
 
@@ -483,10 +489,15 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
         const int lds_off = gi * C::A_SUB + 8 * (qa0 + q) * 128;
         dma16(ra, a_off[q], (uint32_t)(k * KG + gi) * 128u, st + lds_off);
       }
+    // the step's bytes of each row: stage k of the row-major rows, or (packed
+    // layout) pair k (two groups per stage) or half k%2 of pair k/2
+    const uint32_t b_soff = !tiled ? (uint32_t)k * G::SEG
+                            : KG == 2 ? (uint32_t)k * 32u * PB
+                                      : (uint32_t)(k >> 1) * 32u * PB + (uint32_t)(k & 1) * G::ROW;
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
       const int lds_off = C::A_BYTES + wn * G::WB + (q0 + qq) * 1024;
-      dma16(rq[qq], b_off[qq], (uint32_t)k * G::SEG, st + lds_off);
+      dma16(rq[qq], b_off[qq], b_soff, st + lds_off);
     }
     if constexpr (BITS != 16) {
       const uint32_t pair = KG == 2 ? (uint32_t)k : (uint32_t)k >> 1;  // group pair of the step
@@ -949,6 +960,9 @@ hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const i
   prm.out = out;
   prm.a_bytes = (uint32_t)(a_rows * K * 2);
   prm.sb_up_delta = 0;
+  // both operand views in one layout; one expert's packed codes within 32-bit offsets
+  if ((w0.pq == nullptr) != (w1.pq == nullptr)) return hipErrorInvalidValue;
+  if (w0.pq && (w0.pq_expert > 0xFFFFFFFFll || w1.pq_expert > 0xFFFFFFFFll)) return hipErrorInvalidValue;
   if (bits != 16) {
     if (!w0.sb || !w1.sb) return hipErrorInvalidValue;
     const int64_t delta = w1.sb - w0.sb;

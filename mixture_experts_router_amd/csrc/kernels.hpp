@@ -62,6 +62,8 @@ struct WView {
   const uint8_t* sb;  // scales and biases in the packed_sb layout (batched path)
   int64_t sb_stride;  // rows between experts in sb
   float ts = 1.0f;    // NVF4: the tensor scale, applied to the fp32 sums
+  const uint8_t* pq = nullptr;  // codes in the packed_q layout (batched path), or NULL
+  int64_t pq_expert = 0;        // bytes between experts in pq
 };
 
 // ---------------------------------------------------------------- router
@@ -174,5 +176,14 @@ hipError_t launch_stream_read(const void* src, uint32_t bytes, uint32_t* sink, h
 hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, int K, int64_t src_stride, uint8_t* dst,
                           int64_t dst_stride, int64_t dst_row0, hipStream_t st, bool nvfp4 = false);
 inline int64_t packed_sb_bytes(int E, int64_t stride, int K) { return (int64_t)E * ((K / 64 + 1) / 2) * stride * 8; }
+// packed_q: bytes of one row's group pair, and of one expert
+inline int64_t packed_q_pair_bytes(int bits) { return 16 * (int64_t)code_bits(bits); }
+inline int64_t packed_q_expert_bytes(int64_t stride, int K, int bits) {
+  return (stride + 31) / 32 * ((K + 127) / 128) * 32 * packed_q_pair_bytes(bits);
+}
+// codes of rows [0, N) of E experts (row-major, src_stride rows apart) ->
+// packed_q layout with dst_stride rows per expert (N, strides multiples of 32)
+hipError_t launch_pack_q(const uint8_t* q, int E, int N, int K, int bits, int64_t src_stride, uint8_t* dst,
+                         int64_t dst_stride, hipStream_t st);
 
 }  // namespace moe

@@ -150,6 +150,10 @@ moe_status check_weights(const moe_weights* w, int E, int N, int K) {
   if (w->biases && !aligned16(w->biases)) return MOE_ERR_ALIGN;
   if (w->packed_sb && w->bits == 16) return MOE_ERR_QUANT;  // packed_sb: quantised weights only
   if (w->packed_sb && !aligned16(w->packed_sb)) return MOE_ERR_ALIGN;
+  if (w->packed_q) {
+    if (!aligned16(w->packed_q)) return MOE_ERR_ALIGN;
+    if (w->N % 32 != 0 || w->expert_stride_rows % 32 != 0) return MOE_ERR_SHAPE;  // whole 32-row blocks
+  }
   return MOE_OK;
 }
 
@@ -237,6 +241,12 @@ WView view_of(const moe_weights* w, int64_t row_offset) {
   v.sb = (const uint8_t*)w->packed_sb;
   v.sb_stride = w->expert_stride_rows;
   v.ts = f4 ? w->tensor_scale : 1.0f;
+  if (w->packed_q) {
+    const int code = f4 ? moe::NVF4 : w->bits;
+    const int64_t np = (w->K + 127) / 128;
+    v.pq = (const uint8_t*)w->packed_q + row_offset / 32 * np * 32 * moe::packed_q_pair_bytes(code);
+    v.pq_expert = moe::packed_q_expert_bytes(w->expert_stride_rows, w->K, code);
+  }
   return v;
 }
 
@@ -316,6 +326,8 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
   } else {
     if (!gate || !up) return MOE_ERR_NULL;
     if (!compatible(gate, up, false)) return MOE_ERR_INCOMPATIBLE;
+    // the fused GEMM reads gate and up columns in one layout
+    if ((gate->packed_q == nullptr) != (up->packed_q == nullptr)) return MOE_ERR_INCOMPATIBLE;
     if ((s = check_weights(gate, E, I, H)) != MOE_OK) return s;
     if ((s = check_weights(up, E, I, H)) != MOE_OK) return s;
     if (wcode(gate) != wcode(down)) return MOE_ERR_QUANT;
@@ -693,6 +705,32 @@ moe_status moe_pack_sb(const moe_weights* w, void* out, void* stream) {
                               w->format == MOE_FMT_NVFP4));
   plan_step("pack_sb", st);
   return MOE_OK;
+}
+
+size_t moe_packed_q_bytes(int32_t E, int64_t expert_stride_rows, int32_t K, int32_t bits) {
+  if (E < 1 || expert_stride_rows < 32 || expert_stride_rows % 32 != 0 || K < 64 || K % 64 != 0) return 0;
+  if (bits != 4 && bits != 5 && bits != 6 && bits != 8 && bits != 16) return 0;
+  return (size_t)E * (size_t)moe::packed_q_expert_bytes(expert_stride_rows, K, bits);
+}
+
+moe_status moe_pack_q(const moe_weights* w, void* out, void* stream) {
+  try {
+    if (!w || !out) return MOE_ERR_NULL;
+    moe_status s = check_weights(w, w->E, w->N, w->K);
+    if (s != MOE_OK) return s;
+    if (w->N % 32 != 0 || w->expert_stride_rows % 32 != 0) return MOE_ERR_SHAPE;
+    if (!aligned16(out)) return MOE_ERR_ALIGN;
+    DevProps props;
+    if ((s = device_props(&props)) != MOE_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    plan_begin(st);
+    HIP_TRY(moe::launch_pack_q((const uint8_t*)w->q, w->E, w->N, w->K, wcode(w), w->expert_stride_rows,
+                               (uint8_t*)out, w->expert_stride_rows, st));
+    plan_step("pack_q", st);
+    return MOE_OK;
+  } catch (...) {
+    return MOE_ERR_INTERNAL;
+  }
 }
 
 moe_status moe_fuse_gate_up(const moe_weights* gate, const moe_weights* up, void* q_out, void* s_out, void* b_out,

@@ -196,6 +196,31 @@ def test_nvfp4_fuse_and_pack_validation():
     assert moe.STATUS[L.moe_pack_sb(ctypes.byref(F4(8, 256, 256, gs=64)), P, None)] == "MOE_ERR_QUANT"
 
 
+def test_packed_q_size_and_validation():
+    L = moe.lib()
+    # E * (rows/32) * ceil(K/128) * 32 * 16 * bits
+    assert L.moe_packed_q_bytes(8, 256, 256, 4) == 8 * 8 * 2 * 32 * 64
+    assert L.moe_packed_q_bytes(8, 256, 192, 5) == 8 * 8 * 2 * 32 * 80
+    assert L.moe_packed_q_bytes(2, 64, 64, 6) == 2 * 2 * 1 * 32 * 96
+    assert L.moe_packed_q_bytes(64, 2816, 4096, 4) == 64 * 88 * 32 * 32 * 64
+    assert L.moe_packed_q_bytes(4, 96, 4096, 16) == 4 * 3 * 32 * 32 * 256
+    for bad in [(0, 256, 256, 4), (8, 100, 256, 4), (8, 256, 200, 4), (8, 256, 256, 7)]:
+        assert L.moe_packed_q_bytes(*bad) == 0, bad
+    w = W(8, 256, 256)
+    assert moe.STATUS[L.moe_pack_q(ctypes.byref(w), None, None)] == "MOE_ERR_NULL"
+    assert moe.STATUS[L.moe_pack_q(ctypes.byref(w), P + 8, None)] == "MOE_ERR_ALIGN"
+    assert moe.STATUS[L.moe_pack_q(ctypes.byref(W(8, 256, 256, stride=272)), P, None)] == "MOE_ERR_SHAPE"
+    # the layer: packed codes 16-byte aligned, whole 32-row blocks, gate and up alike
+    def wq(E, N, K, pq, stride=None):
+        c = W(E, N, K, stride=stride)
+        c.packed_q = pq
+        return c
+    assert moe.STATUS[fwd(gu=wq(8, 256, 256, P + 8))] == "MOE_ERR_ALIGN"
+    assert moe.STATUS[fwd(gu=wq(8, 256, 256, P, stride=272))] == "MOE_ERR_SHAPE"
+    assert moe.STATUS[fwd(gu=None, gate=wq(8, 128, 256, P), up=W(8, 128, 256))] == "MOE_ERR_INCOMPATIBLE"
+    assert fwd(T=0, gu=None, gate=wq(8, 128, 256, P), up=wq(8, 128, 256, P)) == 0
+
+
 def test_stream_read_validation():
     L = moe.lib()
     sink = P + 1024

@@ -183,6 +183,11 @@ def test_gemm_launch_shapes_are_bit_identical(name, built):
     from ref64 import half64
     inp, _, dev = built(name)
     first = {}
+    # the same weights with packed codes (and scales): every shape gives the same bits
+    gu_p = moe.pack_q(dev.gate_up)
+    dn_p = moe.pack_q(dev.down)
+    if inp.bits != 16:
+        gu_p, dn_p = moe.pack_sb(gu_p), moe.pack_sb(dn_p)
     try:
         for bm, kg, nsub, ks, wpc in GEMM_SHAPES:
             print("case", name, "bm", bm, "kg", kg, "nsub", nsub, "ksplit", ks, "wpc", wpc, flush=True)
@@ -193,6 +198,9 @@ def test_gemm_launch_shapes_are_bit_identical(name, built):
             moe.debug_set_tuning(6, ks)
             moe.debug_set_tuning(2, 2)  # short row groups: exercises the grouped tile order
             y, _ = _run(dev, moe.FLAG_FORCE_MFMA)
+            yp = host_bits(moe.layer_forward(dev.x, dev.wr, inp.k, dn_p, gate_up=gu_p, flags=moe.FLAG_FORCE_MFMA))
+            torch.cuda.synchronize()
+            assert np.array_equal(yp, y), "packed codes, bm %d kg %d nsub %d ksplit %d" % (bm, kg, nsub, ks)
             split = ks if bm > 32 else 1  # 32-row tiles always run one wave per column block
             if split in first:
                 assert np.array_equal(y, first[split]), "%s bm %d kg %d nsub %d ksplit %d" % (name, bm, kg, nsub, ks)
@@ -252,6 +260,38 @@ def test_packed_sb_layout_and_bit_identity(name, built):
         y1 = moe.layer_forward(dev.x, dev.wr, inp.k, down, gate_up=gate_up, flags=flags)
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(y1), y0), flags
+
+
+def _packed_q_reference(w):
+    """packed_q layout written out with numpy from the host copies: [E, NB, NP, 32, PB] bytes."""
+    q = np.ascontiguousarray(w.q).view(np.uint8).reshape(w.E, w.N, -1)
+    pb = 16 * w.bits
+    npairs = (w.K + 127) // 128
+    padded = np.zeros((w.E, w.N, npairs * pb), np.uint8)
+    padded[:, :, :q.shape[2]] = q
+    return padded.reshape(w.E, w.N // 32, 32, npairs, pb).transpose(0, 1, 3, 2, 4)
+
+
+@pytest.mark.parametrize("name", ["prefill_small", "tiny_q8_bf16", "tiny_fp16w", "batched_q5", "batched_q6",
+                                  "batched_f4", "entropy_q4", "batched_small"])
+def test_packed_q_layout_and_bit_identity(name, built):
+    inp, gu_np, dev = built(name)
+    down = moe.pack_q(dev.down)
+    gate_up = moe.pack_q(dev.gate_up)
+    torch.cuda.synchronize()
+    got = down.packed_q.cpu().numpy().reshape(_packed_q_reference(inp.down).shape)
+    assert np.array_equal(got, _packed_q_reference(inp.down))
+    got = gate_up.packed_q.cpu().numpy().reshape(_packed_q_reference(gu_np).shape)
+    assert np.array_equal(got, _packed_q_reference(gu_np))
+    # separate gate and up tensors, each with its own packed codes
+    gate, up = moe.pack_q(dev.gate), moe.pack_q(dev.up)
+    for flags in (moe.FLAG_FORCE_MFMA, moe.FLAG_FORCE_MFMA | moe.FLAG_UNFUSED):
+        y0 = host_bits(dev.forward(flags=flags))
+        y1 = host_bits(moe.layer_forward(dev.x, dev.wr, inp.k, down, gate_up=gate_up, flags=flags))
+        y2 = host_bits(moe.layer_forward(dev.x, dev.wr, inp.k, down, gate=gate, up=up, flags=flags))
+        torch.cuda.synchronize()
+        assert np.array_equal(y1, y0), flags
+        assert np.array_equal(y2, y0), flags
 
 
 def test_five_bit_batched_path_needs_multiples_of_128(built):
