@@ -150,18 +150,20 @@ typedef enum { MOE_F16 = 1, MOE_BF16 = 2 } moe_dtype;
 /*
  * packed_q (optional, any format): the same codes (or fp16 weights) repacked
  * for the batched path by moe_pack_q, pointing at the tensor's (or view's)
- * first 32-row block like q.  Layout: for expert e, 32-row block j (rows
- * 32j .. 32j+31; NB = ceil(expert_stride_rows / 32) blocks per expert),
- * group pair p (columns 128p .. 128p+127; NP = ceil(K/128), a missing last
- * group zero) and row r of the block, the row's PB bytes of the pair
- * (PB = 16 * bits per code: 64, 80, 96, 128, 256; NVFP4 64) at byte
- * (((e*NB + j)*NP + p)*32 + r)*PB.  A pipeline step of the batched GEMM
- * then streams each 32-row block's next 32*PB bytes contiguously instead of
- * PB bytes of 32 rows K*bits/8 bytes apart (a DRAM-friendlier pattern:
- * 6.3 TB/s against 4.5 TB/s for the same loads in a probe).  It is a second
- * copy of the codes; q stays required (the decode path reads q).  The up
- * view of a fused tensor starts (inter/32)*NP*32*PB bytes after the gate
- * view.  Needs N and expert_stride_rows multiples of 32.
+ * first 32-row block like q.  A unit is U groups of 64 columns: U = 2 for
+ * 4-, 5- and 8-bit codes and NVFP4, U = 1 for 6-bit codes and fp16 weights.
+ * Layout: for expert e, 32-row block j (rows 32j .. 32j+31; NB =
+ * ceil(expert_stride_rows / 32) blocks per expert), unit p (NU =
+ * ceil(K / (64 U)) units, a missing last group zero) and row r of the
+ * block, the row's PB bytes of the unit (PB = 8 * U * bits per code: 64,
+ * 80, 48, 128, 128; NVFP4 64) at byte (((e*NB + j)*NU + p)*32 + r)*PB.  A
+ * pipeline step of the batched GEMM then streams each 32-row block's next
+ * 32*PB bytes contiguously instead of PB bytes of 32 rows K*bits/8 bytes
+ * apart (a DRAM-friendlier pattern: 6.3 TB/s against 4.5 TB/s for the same
+ * loads in a probe).  It is a second copy of the codes; q stays required
+ * (the decode path reads q).  The up view of a fused tensor starts
+ * (inter/32)*NU*32*PB bytes after the gate view.  Needs N and
+ * expert_stride_rows multiples of 32.
  */
 typedef enum { MOE_FMT_AFFINE = 0, MOE_FMT_NVFP4 = 1 } moe_weight_format;
 
@@ -396,8 +398,8 @@ moe_status moe_pack_sb(const moe_weights* w, void* out, void* stream);
 /*
  * Bytes of packed_q for a tensor of E experts, expert_stride_rows rows per
  * expert (a multiple of 32), K input columns and the given width code
- * (bits 4, 5, 6, 8 or 16; NVFP4: 4): E * ceil(rows/32) * ceil(K/128) * 32 *
- * 16 * bits.  0 for arguments out of range.
+ * (bits 4, 5, 6, 8 or 16; NVFP4: 4): E * (rows/32) * NU * 32 * PB (see
+ * moe_weights).  0 for arguments out of range.
  */
 size_t moe_packed_q_bytes(int32_t E, int64_t expert_stride_rows, int32_t K, int32_t bits);
 /*

@@ -212,8 +212,9 @@ class Weights:
         sb = None if self.packed_sb is None else self.packed_sb.data_ptr() + self.row_offset * 8
         pq = None
         if self.packed_q is not None:
-            np_ = (self.K + 127) // 128
-            pq = self.packed_q.data_ptr() + self.row_offset // 32 * np_ * 32 * 16 * self.bits
+            ug = 1 if self.bits in (6, 16) else 2  # groups per unit
+            nu = (self.K + 64 * ug - 1) // (64 * ug)
+            pq = self.packed_q.data_ptr() + self.row_offset // 32 * nu * 32 * 8 * self.bits * ug
         self._cstruct = CWeights(q, s, b, self.E, self.N, self.K, self.bits, self.group_size, stride, sb,
                                  FMT_NVFP4 if f4 else FMT_AFFINE, float(self.tensor_scale), pq)
         return self._cstruct

@@ -252,7 +252,7 @@ hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, in
 // ---------------------------------------------------------- packed_q ---
 //
 // One thread per 16-byte piece of the packed_q layout (moe.h): piece c of
-// row r of 32-row block j, group pair p, expert e.  Source rows are read as
+// row r of 32-row block j, unit p (one or two groups), expert e.  Source rows are read as
 // 32-bit words (5-bit rows are only 8-byte aligned); words past the row's
 // code bytes (a missing last group) and rows at or past N are zero.
 __global__ __launch_bounds__(256) void pack_q_kernel(const uint8_t* __restrict__ q, int N, int rb, int pb, int np,
@@ -285,8 +285,8 @@ __global__ __launch_bounds__(256) void pack_q_kernel(const uint8_t* __restrict__
 hipError_t launch_pack_q(const uint8_t* q, int E, int N, int K, int bits, int64_t src_stride, uint8_t* dst,
                          int64_t dst_stride, hipStream_t st) {
   const int rb = K * code_bits(bits) / 8;
-  const int pb = (int)packed_q_pair_bytes(bits);
-  const int np = (K + 127) / 128;
+  const int pb = (int)packed_q_unit_bytes(bits);
+  const int np = (int)packed_q_units(K, bits);
   const int nb_src = (N + 31) / 32;
   const int nb_dst = (int)((dst_stride + 31) / 32);
   const int64_t total = (int64_t)E * nb_src * np * 32 * (pb / 16);

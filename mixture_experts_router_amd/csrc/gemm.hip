@@ -412,10 +412,13 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
     return valid[ni] ? c : 0;
   };
   const int64_t row_bytes = (int64_t)K * code_bits(BITS) / 8;
-  // packed_q: each 32-row block's group pairs contiguous (PB bytes per row and
-  // pair), so a step streams 32*PB contiguous bytes per block
+  // packed_q: each 32-row block's units (UG groups, PB bytes per row)
+  // contiguous, so a step streams 32*PB contiguous bytes per block
   const bool tiled = prm.w0.pq != nullptr;
-  constexpr int PB = 16 * code_bits(BITS);
+  constexpr int UG = BITS == 6 || BITS == 16 ? 1 : 2;
+  constexpr int PB = UG * G::ROW;
+  static_assert(UG == 2 || KG == 1, "one-group units are read one group per step");
+  const int nu = (ng + UG - 1) / UG;
   const int np = (ng + 1) / 2;
   const uint8_t* qbase[NSUB];
 #pragma unroll
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
     const int pl = live ? item % G::LPR : 0;
     const int piece = G::WHOLE ? pl ^ piece_swizzle<G::SEG>(sub * 32 + r_in) : pl;
     const int c = column(sub, r_in);
-    b_off[qq] = (tiled ? (uint32_t)((((int64_t)(c >> 5) * np) * 32 + (c & 31)) * PB) : (uint32_t)(c * row_bytes)) +
+    b_off[qq] = (tiled ? (uint32_t)((((int64_t)(c >> 5) * nu) * 32 + (c & 31)) * PB) : (uint32_t)(c * row_bytes)) +
                 (uint32_t)piece * 16u;
   }
   const int nst = ng / KG;  // pipeline steps (the launcher makes KG divide ng)
@@ -490,10 +493,10 @@ __global__ __launch_bounds__(256 * KS, WPC) void gemm_kernel(GemmParams prm) {
         dma16(ra, a_off[q], (uint32_t)(k * KG + gi) * 128u, st + lds_off);
       }
     // the step's bytes of each row: stage k of the row-major rows, or (packed
-    // layout) pair k (two groups per stage) or half k%2 of pair k/2
+    // layout) unit k (a unit per stage) or half k%2 of two-group unit k/2
     const uint32_t b_soff = !tiled ? (uint32_t)k * G::SEG
-                            : KG == 2 ? (uint32_t)k * 32u * PB
-                                      : (uint32_t)(k >> 1) * 32u * PB + (uint32_t)(k & 1) * G::ROW;
+                            : KG == UG ? (uint32_t)k * 32u * PB
+                                       : (uint32_t)(k >> 1) * 32u * PB + (uint32_t)(k & 1) * G::ROW;
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
       const int lds_off = C::A_BYTES + wn * G::WB + (q0 + qq) * 1024;

@@ -176,10 +176,17 @@ hipError_t launch_stream_read(const void* src, uint32_t bytes, uint32_t* sink, h
 hipError_t launch_pack_sb(const uint16_t* s, const uint16_t* b, int E, int N, int K, int64_t src_stride, uint8_t* dst,
                           int64_t dst_stride, int64_t dst_row0, hipStream_t st, bool nvfp4 = false);
 inline int64_t packed_sb_bytes(int E, int64_t stride, int K) { return (int64_t)E * ((K / 64 + 1) / 2) * stride * 8; }
-// packed_q: bytes of one row's group pair, and of one expert
-inline int64_t packed_q_pair_bytes(int bits) { return 16 * (int64_t)code_bits(bits); }
+// packed_q: a unit is the groups one pipeline step of the batched GEMM reads
+// (two for 4-, 5- and 8-bit codes and NVFP4, one for 6-bit codes and fp16);
+// bytes of one row's unit, units per row, and bytes of one expert
+inline int packed_q_unit_groups(int bits) { return bits == 6 || bits == 16 ? 1 : 2; }
+inline int64_t packed_q_unit_bytes(int bits) { return 8 * (int64_t)code_bits(bits) * packed_q_unit_groups(bits); }
+inline int64_t packed_q_units(int K, int bits) {
+  const int u = 64 * packed_q_unit_groups(bits);
+  return (K + u - 1) / u;
+}
 inline int64_t packed_q_expert_bytes(int64_t stride, int K, int bits) {
-  return (stride + 31) / 32 * ((K + 127) / 128) * 32 * packed_q_pair_bytes(bits);
+  return (stride + 31) / 32 * packed_q_units(K, bits) * 32 * packed_q_unit_bytes(bits);
 }
 // codes of rows [0, N) of E experts (row-major, src_stride rows apart) ->
 // packed_q layout with dst_stride rows per expert (N, strides multiples of 32)

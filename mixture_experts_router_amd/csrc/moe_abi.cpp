@@ -243,8 +243,8 @@ WView view_of(const moe_weights* w, int64_t row_offset) {
   v.ts = f4 ? w->tensor_scale : 1.0f;
   if (w->packed_q) {
     const int code = f4 ? moe::NVF4 : w->bits;
-    const int64_t np = (w->K + 127) / 128;
-    v.pq = (const uint8_t*)w->packed_q + row_offset / 32 * np * 32 * moe::packed_q_pair_bytes(code);
+    v.pq = (const uint8_t*)w->packed_q +
+           row_offset / 32 * moe::packed_q_units(w->K, code) * 32 * moe::packed_q_unit_bytes(code);
     v.pq_expert = moe::packed_q_expert_bytes(w->expert_stride_rows, w->K, code);
   }
   return v;

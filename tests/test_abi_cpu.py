@@ -198,12 +198,14 @@ def test_nvfp4_fuse_and_pack_validation():
 
 def test_packed_q_size_and_validation():
     L = moe.lib()
-    # E * (rows/32) * ceil(K/128) * 32 * 16 * bits
+    # E * (rows/32) * units * 32 * unit bytes; two-group units for 4/5/8 bits, one group for 6 and 16
     assert L.moe_packed_q_bytes(8, 256, 256, 4) == 8 * 8 * 2 * 32 * 64
     assert L.moe_packed_q_bytes(8, 256, 192, 5) == 8 * 8 * 2 * 32 * 80
-    assert L.moe_packed_q_bytes(2, 64, 64, 6) == 2 * 2 * 1 * 32 * 96
+    assert L.moe_packed_q_bytes(8, 256, 192, 8) == 8 * 8 * 2 * 32 * 128
+    assert L.moe_packed_q_bytes(2, 64, 64, 6) == 2 * 2 * 1 * 32 * 48
+    assert L.moe_packed_q_bytes(2, 64, 192, 6) == 2 * 2 * 3 * 32 * 48
     assert L.moe_packed_q_bytes(64, 2816, 4096, 4) == 64 * 88 * 32 * 32 * 64
-    assert L.moe_packed_q_bytes(4, 96, 4096, 16) == 4 * 3 * 32 * 32 * 256
+    assert L.moe_packed_q_bytes(4, 96, 4096, 16) == 4 * 3 * 64 * 32 * 128
     for bad in [(0, 256, 256, 4), (8, 100, 256, 4), (8, 256, 200, 4), (8, 256, 256, 7)]:
         assert L.moe_packed_q_bytes(*bad) == 0, bad
     w = W(8, 256, 256)

@@ -263,17 +263,18 @@ def test_packed_sb_layout_and_bit_identity(name, built):
 
 
 def _packed_q_reference(w):
-    """packed_q layout written out with numpy from the host copies: [E, NB, NP, 32, PB] bytes."""
+    """packed_q layout written out with numpy from the host copies: [E, NB, NU, 32, PB] bytes."""
     q = np.ascontiguousarray(w.q).view(np.uint8).reshape(w.E, w.N, -1)
-    pb = 16 * w.bits
-    npairs = (w.K + 127) // 128
-    padded = np.zeros((w.E, w.N, npairs * pb), np.uint8)
+    ug = 1 if w.bits in (6, 16) else 2  # groups per unit
+    pb = 8 * w.bits * ug
+    nu = (w.K + 64 * ug - 1) // (64 * ug)
+    padded = np.zeros((w.E, w.N, nu * pb), np.uint8)
     padded[:, :, :q.shape[2]] = q
-    return padded.reshape(w.E, w.N // 32, 32, npairs, pb).transpose(0, 1, 3, 2, 4)
+    return padded.reshape(w.E, w.N // 32, 32, nu, pb).transpose(0, 1, 3, 2, 4)
 
 
 @pytest.mark.parametrize("name", ["prefill_small", "tiny_q8_bf16", "tiny_fp16w", "batched_q5", "batched_q6",
-                                  "batched_f4", "entropy_q4", "batched_small"])
+                                  "batched_f4", "entropy_q4", "batched_small", "entropy_fp16w", "prefill_q6_bm128"])
 def test_packed_q_layout_and_bit_identity(name, built):
     inp, gu_np, dev = built(name)
     down = moe.pack_q(dev.down)
