@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_amd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["router.hip", "sort.hip", "gemv.hip", "gemm.hip", "combine.hip", "moe_abi.cpp"]
+SOURCES = ["router.hip", "sort.hip", "gemv.hip", "gemm.hip", "gemm_w4.hip", "gemm_w56.hip", "gemm_w8.hip",
+           "gemm_w16.hip", "gemm_wf4.hip", "combine.hip", "moe_abi.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

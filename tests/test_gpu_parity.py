@@ -171,7 +171,7 @@ def test_sort_matches_oracle_exactly(name, built):
 # workgroups per CU): every launch shape of one k split accumulates each
 # output over K in the same order, so the shapes of a split give identical
 # bits; the two splits are compared with each other within the layer tolerance
-GEMM_SHAPES = [(32, 2, 2, 1, 2), (32, 2, 2, 1, 1), (64, 1, 2, 1, 2), (64, 2, 2, 1, 1), (64, 2, 2, 2, 2),
+GEMM_SHAPES = [(32, 2, 2, 1, 2), (32, 2, 2, 1, 1), (32, 2, 2, 2, 1), (32, 1, 2, 2, 1), (64, 1, 2, 1, 2), (64, 2, 2, 1, 1), (64, 2, 2, 2, 2),
                (64, 1, 2, 2, 2), (128, 1, 2, 1, 2), (128, 2, 2, 1, 2), (128, 2, 4, 1, 2), (128, 1, 2, 2, 2),
                (128, 2, 2, 2, 2)]
 DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2, 6: 1, 7: 3}
@@ -201,7 +201,7 @@ def test_gemm_launch_shapes_are_bit_identical(name, built):
             yp = host_bits(moe.layer_forward(dev.x, dev.wr, inp.k, dn_p, gate_up=gu_p, flags=moe.FLAG_FORCE_MFMA))
             torch.cuda.synchronize()
             assert np.array_equal(yp, y), "packed codes, bm %d kg %d nsub %d ksplit %d" % (bm, kg, nsub, ks)
-            split = ks if bm > 32 else 1  # 32-row tiles always run one wave per column block
+            split = ks
             if split in first:
                 assert np.array_equal(y, first[split]), "%s bm %d kg %d nsub %d ksplit %d" % (name, bm, kg, nsub, ks)
             else:
