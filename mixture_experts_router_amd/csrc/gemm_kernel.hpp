@@ -897,9 +897,11 @@ static hipError_t launch_one(const GemmParams& prm, hipStream_t st) {
     if (tuning(TUNE_GEMM_KSPLIT) == 2) return launch_sub<BITS, MODE, MS, 2, 2, 1>(prm, st);
     if constexpr (MS < 4) {
       // 8-bit weights at 32-row tiles: one workgroup per CU streaming two-group
-      // (128-byte) row segments measured faster than two with one-group stages
+      // (128-byte) row segments measured faster than two with one-group stages;
+      // so did the fp16 down projection (three stages instead of two)
       const int wpc = tuning(TUNE_GEMM_WPC);
-      if (wpc == 1 || (wpc != 2 && MS == 1 && BITS == 8)) return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
+      if (wpc == 1 || (wpc != 2 && ((MS == 1 && BITS == 8) || (BITS == 16 && MODE == GEMM_ROWS_F16))))
+        return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
       return launch_sub<BITS, MODE, MS, 2, 1, 2>(prm, st);
     }
     return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
