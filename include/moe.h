@@ -436,9 +436,12 @@ int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
  * from the batch), key 4 = K groups of 64 per pipeline stage (1; other
  * values: 2 where the stage fits in LDS), key 5 = 32-column subtiles per wave
  * at the 128-row tile (4; other values: 2), key 6 = waves per column block
- * (2, splitting each group's k-steps; other values: 1), key 7 = workgroups per CU at the 32- and 64-row tiles (1: the whole LDS
- * for one, deeper pipeline and two-group 8-bit stages; 2: two; other values:
- * one for 8-bit weights at 32-row tiles, else two), key 8 = waves per
+ * (2, splitting each group's k-steps; other values: 1), key 7 = workgroups
+ * per CU at the 32- and 64-row tiles (1: the whole LDS for one, deeper
+ * pipeline and two-group 8-bit stages; 2: two; 3: three, for 4-bit and NVFP4
+ * weights at 64-row tiles; other values: one for 8-bit weights at 32-row
+ * tiles and for fp16 down projections, three for 4-bit and NVFP4 down
+ * projections at 64-row tiles, else two), key 8 = waves per
  * (token, slot) pair of the decode gate+up kernel (2: from the resident-wave
  * target alone; other values: as many as give every wave the same number of
  * row iterations, at most that target).

@@ -111,7 +111,7 @@ struct BGeo {
   static_assert(SEG % 16 == 0, "a stage row is whole 16-byte pieces");
 };
 
-// WPC: workgroups per CU the LDS budget allows (1: 156 KB, 2: 78 KB each)
+// WPC: workgroups per CU the LDS budget allows (1: 156 KB, 2: 78 KB, 3: 52 KB each)
 template <int BITS, int MS, int KG, int NSUB, int KS, int WPC>
 struct GemmCfg {
   static constexpr int BM = 32 * MS;
@@ -122,7 +122,7 @@ struct GemmCfg {
   // its 32*NSUB columns' packed group pair, repeated over the spare lanes)
   static constexpr int SC_BYTES = BITS != 16 ? 4 * 1024 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
-  static constexpr int BUDGET = WPC == 1 ? 156 * 1024 : 78 * 1024;
+  static constexpr int BUDGET = WPC == 1 ? 156 * 1024 : WPC == 2 ? 78 * 1024 : 52 * 1024;
   static constexpr int NS_FIT = BUDGET / STAGE;
   static constexpr int NS = NS_FIT < 2 ? 2 : (NS_FIT > 6 ? 6 : NS_FIT);
   // vector memory instructions per wave per stage: A, B, scales and biases
@@ -869,7 +869,7 @@ static hipError_t launch_sub(GemmParams prm, hipStream_t st) {
     return launch_kernel(gemm_kernel<5, MODE, MS, 2, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
   } else {
     // two-group stages: 4-bit rows, or 8-bit rows with the whole LDS
-    if constexpr (BITS == 4 || BITS == NVF4 || (BITS == 8 && WPC == 1 && NSUB == 2 && MS < 4)) {
+    if constexpr ((BITS == 4 || BITS == NVF4 || (BITS == 8 && WPC == 1 && NSUB == 2 && MS < 4)) && WPC < 3) {
       if ((prm.K / 64) % 2 == 0 && tuning(TUNE_GEMM_KG) != 1)
         return launch_kernel(gemm_kernel<BITS, MODE, MS, 2, NSUB, KS, WPC>, grid, 256 * KS, 0, st, prm);
     }
@@ -900,6 +900,12 @@ static hipError_t launch_one(const GemmParams& prm, hipStream_t st) {
       // (128-byte) row segments measured faster than two with one-group stages;
       // so did the fp16 down projection (three stages instead of two)
       const int wpc = tuning(TUNE_GEMM_WPC);
+      // 4-bit and NVFP4 down projections at 64-row tiles: three workgroups per
+      // CU (one-group stages, 40 KB of LDS each) measured 3-10% faster than two
+      if constexpr (MS == 2 && (BITS == 4 || BITS == NVF4)) {
+        if (wpc == 3 || (wpc != 1 && wpc != 2 && MODE == GEMM_ROWS_F16))
+          return launch_sub<BITS, MODE, MS, 2, 1, 3>(prm, st);
+      }
       if (wpc == 1 || (wpc != 2 && ((MS == 1 && BITS == 8) || (BITS == 16 && MODE == GEMM_ROWS_F16))))
         return launch_sub<BITS, MODE, MS, 2, 1, 1>(prm, st);
       return launch_sub<BITS, MODE, MS, 2, 1, 2>(prm, st);

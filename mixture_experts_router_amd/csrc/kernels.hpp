@@ -46,7 +46,7 @@ enum TuneKey {
   TUNE_GEMM_KG = 4,  // 1: 4-bit GEMM stages one quantisation group per step (default: two when K allows)
   TUNE_GEMM_NSUB = 5,  // 4: 128-row GEMM tiles give each wave 128 columns (default 64)
   TUNE_GEMM_KSPLIT = 6,  // 2: GEMM tiles run eight waves, two per column block splitting k (default four)
-  TUNE_GEMM_WPC = 7,  // 1 / 2: workgroups per CU at 32- and 64-row GEMM tiles (other values: by bits and tile)
+  TUNE_GEMM_WPC = 7,  // 1 / 2 / 3: workgroups per CU at 32- and 64-row GEMM tiles (3: 4-bit and NVFP4 at 64 rows; other values: by bits, tile and mode)
   TUNE_UP_BALANCE = 8,  // 2: decode gate+up waves per pair from the wave target alone (default: equal iterations)
   TUNE_KEYS = 9
 };

@@ -171,10 +171,10 @@ def test_sort_matches_oracle_exactly(name, built):
 # workgroups per CU): every launch shape of one k split accumulates each
 # output over K in the same order, so the shapes of a split give identical
 # bits; the two splits are compared with each other within the layer tolerance
-GEMM_SHAPES = [(32, 2, 2, 1, 2), (32, 2, 2, 1, 1), (32, 2, 2, 2, 1), (32, 1, 2, 2, 1), (64, 1, 2, 1, 2), (64, 2, 2, 1, 1), (64, 2, 2, 2, 2),
+GEMM_SHAPES = [(32, 2, 2, 1, 2), (32, 2, 2, 1, 1), (32, 2, 2, 2, 1), (32, 1, 2, 2, 1), (64, 1, 2, 1, 2), (64, 1, 2, 1, 3), (64, 2, 2, 1, 1), (64, 2, 2, 2, 2),
                (64, 1, 2, 2, 2), (128, 1, 2, 1, 2), (128, 2, 2, 1, 2), (128, 2, 4, 1, 2), (128, 1, 2, 2, 2),
                (128, 2, 2, 2, 2)]
-DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2, 6: 1, 7: 3}
+DEFAULT_TUNING = {2: 1 << 30, 3: 1, 4: 2, 5: 2, 6: 1, 7: 8}
 
 
 @pytest.mark.parametrize("name", ["prefill_bm128", "prefill_small", "tiny_q8_bf16", "tiny_fp16w", "batched_long_k",
