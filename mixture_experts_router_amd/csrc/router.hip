@@ -28,65 +28,87 @@ __device__ __forceinline__ void unpack8(u32x4 r, int act, float* v) {
 
 // --------------------------------------------------------- small batches --
 //
-// One workgroup per (expert, token); its four waves take consecutive quarters
-// of H, each lane sums its 8-element slices in order, the wave sums its lanes,
-// and the four wave partials are added in wave order.  Spreads a decode
-// step's router over E workgroups (E x 8 KB of router rows at H = 4096).
-template <int ACT>
+// One workgroup per token and EB consecutive experts; its four waves take
+// consecutive quarters of H, each lane sums its 8-element slices in order (a
+// slice of x is loaded once and used for all EB experts), the wave sums its
+// lanes, and the four wave partials are added in wave order, so every EB
+// gives the same bits.  EB = 1 spreads a decode step's router over E
+// workgroups (E x 8 KB of router rows at H = 4096); larger EB read each token
+// row EB times less often, where many tokens would otherwise make E x T
+// workgroups that each fetch a whole token row for one logit.
+template <int ACT, int EB>
 __global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t* __restrict__ x,
                                                                   const uint16_t* __restrict__ wr,
                                                                   float* __restrict__ logits, int H, int E,
                                                                   int act, const float* __restrict__ health,
                                                                   float alpha) {
-  __shared__ float part[4];
-  const int e = blockIdx.x, t = blockIdx.y;
+  __shared__ float part[EB][4];
+  const int e0 = blockIdx.x * EB, t = blockIdx.y;
   const int lane = lane_id(), wave = wave_id();
   const int q = H / 4;
   const uint16_t* xr = x + (size_t)t * H + wave * q;
-  const uint16_t* wrow = wr + (size_t)e * H + wave * q;
+  const uint16_t* wrow[EB];
+#pragma unroll
+  for (int j = 0; j < EB; ++j) wrow[j] = wr + (size_t)min(e0 + j, E - 1) * H + wave * q;  // past E: re-read
   // up to four slices per lane per round, all loaded before the sums (which
   // run slice by slice in order, as one slice at a time would)
-  float acc = 0.0f;
-  auto slice = [&](u32x4 xr8, u32x4 wr8) __attribute__((always_inline)) {
-    float xv[8], wv[8];
+  float acc[EB];
+#pragma unroll
+  for (int j = 0; j < EB; ++j) acc[j] = 0.0f;
+  // one slice of x (converted once) against the same slice of every expert row
+  auto slice = [&](u32x4 xr8, const u32x4* wr8) __attribute__((always_inline)) {
+    float xv[8];
     unpack8(xr8, ACT, xv);
-    unpack8(wr8, ACT, wv);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf(xv[i], wv[i], acc);
+    for (int j = 0; j < EB; ++j) {
+      float wv[8];
+      unpack8(wr8[j], ACT, wv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[j] = fmaf(xv[i], wv[i], acc[j]);
+    }
   };
+  constexpr int R = EB <= 2 ? 4 : 2;  // slices per round (registers: (1 + EB) * R loads)
   int h = lane * 8;
-  for (; h + 3 * 512 < q; h += 4 * 512) {
-    u32x4 xa[4], wa[4];
+  for (; h + (R - 1) * 512 < q; h += R * 512) {
+    u32x4 xa[R], wa[R][EB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < R; ++u) {
       xa[u] = load16(xr + h + 512 * u);
-      wa[u] = load16(wrow + h + 512 * u);
+#pragma unroll
+      for (int j = 0; j < EB; ++j) wa[u][j] = load16(wrow[j] + h + 512 * u);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) slice(xa[u], wa[u]);
+    for (int u = 0; u < R; ++u) slice(xa[u], wa[u]);
   }
   if (h < q) {
-    // the remaining one to three slices of this lane, loaded together
-    u32x4 xa[3], wa[3];
+    // the remaining one to R-1 slices of this lane, loaded together
+    u32x4 xa[R - 1], wa[R - 1][EB];
 #pragma unroll
-    for (int u = 0; u < 3; ++u)
+    for (int u = 0; u < R - 1; ++u)
       if (h + 512 * u < q) {
         xa[u] = load16(xr + h + 512 * u);
-        wa[u] = load16(wrow + h + 512 * u);
+#pragma unroll
+        for (int j = 0; j < EB; ++j) wa[u][j] = load16(wrow[j] + h + 512 * u);
       }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < 3; ++u)
+    for (int u = 0; u < R - 1; ++u)
       if (h + 512 * u < q) slice(xa[u], wa[u]);
   }
-  const float s = wave_sum(acc);
-  if (lane == 0) part[wave] = s;
+#pragma unroll
+  for (int j = 0; j < EB; ++j) {
+    const float s = wave_sum(acc[j]);
+    if (lane == 0) part[j][wave] = s;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float l = ((part[0] + part[1]) + part[2]) + part[3];
-    if (health) l = l - alpha * health[e];
-    logits[(size_t)t * E + e] = l;
+  if (threadIdx.x < EB) {
+    const int j = threadIdx.x, e = e0 + j;
+    if (e < E) {
+      float l = ((part[j][0] + part[j][1]) + part[j][2]) + part[j][3];
+      if (health) l = l - alpha * health[e];
+      logits[(size_t)t * E + e] = l;
+    }
   }
 }
 
@@ -333,12 +355,25 @@ hipError_t launch_router_logits(const void* x, const void* wr, float* logits, in
     return launch_kernel(router_logits_mfma_kernel<ACT_F16, 4>, grid, 256, 0, st, xs, ws, logits, T, H, E, health,
                          alpha);
   }
-  if (act == ACT_BF16)
-    launch_kernel(router_logits_small_kernel<ACT_BF16>, dim3(E, T), 256, 0, st, (const uint16_t*)x,
-                  (const uint16_t*)wr, logits, H, E, act, health, alpha);
-  else
-    launch_kernel(router_logits_small_kernel<ACT_F16>, dim3(E, T), 256, 0, st, (const uint16_t*)x,
-                  (const uint16_t*)wr, logits, H, E, act, health, alpha);
+  // experts per workgroup: one while the logits alone give at most 1024
+  // workgroups, then enough to keep about a thousand
+  const int64_t n = (int64_t)T * E;
+  const int eb = n <= 1024 ? 1 : n <= 2048 ? 2 : n <= 4096 ? 4 : 8;
+  auto go = [&](auto kern, int b) {
+    launch_kernel(kern, dim3((E + b - 1) / b, T), 256, 0, st, (const uint16_t*)x, (const uint16_t*)wr, logits, H, E,
+                  act, health, alpha);
+  };
+  if (act == ACT_BF16) {
+    if (eb == 1) go(router_logits_small_kernel<ACT_BF16, 1>, 1);
+    else if (eb == 2) go(router_logits_small_kernel<ACT_BF16, 2>, 2);
+    else if (eb == 4) go(router_logits_small_kernel<ACT_BF16, 4>, 4);
+    else go(router_logits_small_kernel<ACT_BF16, 8>, 8);
+  } else {
+    if (eb == 1) go(router_logits_small_kernel<ACT_F16, 1>, 1);
+    else if (eb == 2) go(router_logits_small_kernel<ACT_F16, 2>, 2);
+    else if (eb == 4) go(router_logits_small_kernel<ACT_F16, 4>, 4);
+    else go(router_logits_small_kernel<ACT_F16, 8>, 8);
+  }
   return hipGetLastError();
 }
 
