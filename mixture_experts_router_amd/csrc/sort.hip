@@ -56,7 +56,10 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
       v[u] = valid ? raw : 0x7FFFFFFF;
     }
   };
+  // the segment's first group stays in registers for the second pass (the
+  // launcher sizes CH so that one group usually covers the segment)
   int lt = 0, eq = 0;
+  int v0[CH];
   for (int64_t c0 = beg; c0 < end; c0 += 64 * CH) {
     int v[CH];
     load_group(c0, v);
@@ -64,6 +67,7 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
     for (int u = 0; u < CH; ++u) {
       lt += __popcll(__ballot(v[u] < e));
       eq += __popcll(__ballot(v[u] == e));
+      if (c0 == beg) v0[u] = v[u];
     }
   }
   if (lane == 0) {
@@ -91,7 +95,12 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
   int r = before;  // rank within expert e of the segment's first pair of e
   for (int64_t c0 = beg; c0 < end; c0 += 64 * CH) {
     int v[CH];
-    load_group(c0, v);
+    if (c0 == beg) {
+#pragma unroll
+      for (int u = 0; u < CH; ++u) v[u] = v0[u];
+    } else {
+      load_group(c0, v);
+    }
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int64_t p = c0 + 64 * u + lane;
