@@ -209,6 +209,79 @@ __global__ __launch_bounds__(256) void topk_static_kernel(const float* __restric
   }
 }
 
+// E <= 64: one wave selects for four tokens, sixteen lanes each (lane i of
+// row r holds experts i, i+16, i+32, i+48 of token 4*wave + r).  A row
+// reduction over sixteen lanes needs four DPP steps and no lane reads, so a
+// token costs about a quarter of the instructions of wave_topk.  The order of
+// the candidates is total, so the same experts are chosen, and the weights
+// are formed with the same operations in slot order: the same bits as
+// topk_static_kernel.
+__global__ __launch_bounds__(256) void topk_static_rows_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                               int gs, int32_t* __restrict__ idx,
+                                                               float* __restrict__ w, int32_t* __restrict__ k_used,
+                                                               float* __restrict__ entropy) {
+  const int lane = lane_id(), r = lane / 16, i16 = lane % 16;
+  const int t = (blockIdx.x * 4 + wave_id()) * 4 + r;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (k_used) *k_used = k;
+    if (entropy) *entropy = 0.0f;
+  }
+  // every lane stays active for the row reductions; tokens past T have no
+  // live candidate and store nothing
+  const bool tv = t < T;
+  const float* row = logits + (size_t)(tv ? t : 0) * E;
+  float v[4];
+  bool live[4];
+  int grp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = i16 + 16 * j;
+    live[j] = tv && e < E;
+    v[j] = live[j] ? row[e] : 0.0f;
+    grp[j] = e / gs;
+  }
+  float sv[MOE_MAX_K_DEV];
+  int si[MOE_MAX_K_DEV];
+#pragma unroll
+  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
+    if (s < k) {
+      Cand c = {0.0f, -1};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Cand d = {v[j], live[j] ? i16 + 16 * j : -1};
+        c = better(c, d);
+      }
+      c = better(c, dpp_cand<DPP_QUAD_1032>(c));
+      c = better(c, dpp_cand<DPP_QUAD_2301>(c));
+      c = better(c, dpp_cand<DPP_ROW_HALF_MIRROR>(c));
+      c = better(c, dpp_cand<DPP_ROW_MIRROR>(c));
+      sv[s] = c.v;
+      si[s] = c.i;
+      const int cg = c.i / gs;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (grp[j] == cg) live[j] = false;
+    }
+  }
+  if (i16 == 0 && tv) {
+    float ex[MOE_MAX_K_DEV];
+    float z = 0.0f;
+#pragma unroll
+    for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
+      if (s < k) {
+        ex[s] = expf(sv[s] - sv[0]);
+        z += ex[s];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < MOE_MAX_K_DEV; ++s)
+      if (s < k) {
+        idx[(size_t)t * k + s] = si[s];
+        w[(size_t)t * k + s] = ex[s] / z;
+      }
+  }
+}
+
 // Shannon entropy (nats) of softmax(row): H = ln Z - sum_e p_e (l_e - l_max)
 __device__ __forceinline__ float wave_entropy(const float* __restrict__ row, int E) {
   const int lane = lane_id();
@@ -387,7 +460,10 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int gs, int32_t
                          k_used, entropy);
   }
   if (k > 0) {
-    launch_kernel(topk_static_kernel, (T + 3) / 4, 256, 0, st, logits, T, E, k, gs, idx, w, k_used, entropy);
+    if (E <= 64)
+      launch_kernel(topk_static_rows_kernel, (T + 15) / 16, 256, 0, st, logits, T, E, k, gs, idx, w, k_used, entropy);
+    else
+      launch_kernel(topk_static_kernel, (T + 3) / 4, 256, 0, st, logits, T, E, k, gs, idx, w, k_used, entropy);
   } else {
     launch_kernel(topk_entropy_kernel, 1, 1024, 0, st, logits, T, E, gs, idx, w, k_used, entropy);
   }
