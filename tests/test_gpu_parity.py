@@ -373,12 +373,13 @@ def test_fuse_gate_up_matches_oracle_concatenation(built):
                                    (400, 40, 2)])
 def test_router_exact_inputs_with_planted_ties(dtype, T, E, k):
     # H = 1024 takes the sixteen-wave MFMA router above 128 tokens and 16384
-    # logits; H = 320 (not a multiple of 256) the four-wave one; H = 8192 runs
+    # logits (H = 2048: one whole round of eight k-steps per wave); H = 320
+    # (not a multiple of 256) the four-wave one; H = 8192 runs
     # the small-batch router's four-slice rounds (partial sums stay exact:
     # multiples of 2^-14 below 2^9).  The small-batch router takes 1, 2, 4 or 8
     # experts per workgroup as T*E grows (E = 20, 45 and 40: a partial last
     # block)
-    for H in (1024, 320) + ((8192,) if T <= 128 else ()):
+    for H in (1024, 320) + ((8192,) if T <= 128 else (2048,)):
         _router_exact_case(dtype, T, E, k, H)
 
 
