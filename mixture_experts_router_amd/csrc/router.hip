@@ -216,20 +216,12 @@ __global__ __launch_bounds__(256) void topk_static_kernel(const float* __restric
 // the candidates is total, so the same experts are chosen, and the weights
 // are formed with the same operations in slot order: the same bits as
 // topk_static_kernel.
-__global__ __launch_bounds__(256) void topk_static_rows_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                               int gs, int32_t* __restrict__ idx,
-                                                               float* __restrict__ w, int32_t* __restrict__ k_used,
-                                                               float* __restrict__ entropy) {
-  const int lane = lane_id(), r = lane / 16, i16 = lane % 16;
-  const int t = (blockIdx.x * 4 + wave_id()) * 4 + r;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (k_used) *k_used = k;
-    if (entropy) *entropy = 0.0f;
-  }
-  // every lane stays active for the row reductions; tokens past T have no
-  // live candidate and store nothing
-  const bool tv = t < T;
-  const float* row = logits + (size_t)(tv ? t : 0) * E;
+// The k best of one token's E <= 64 logits over the sixteen lanes of a row
+// (lane i holds experts i, i+16, i+32, i+48); every lane of the row receives
+// the selected logits and indices in slot order.  No live candidate (a token
+// past T) gives index -1.
+__device__ __forceinline__ void row16_topk(const float* __restrict__ row, bool tv, int E, int k, int gs, int i16,
+                                           float* sv, int* si) {
   float v[4];
   bool live[4];
   int grp[4];
@@ -240,8 +232,6 @@ __global__ __launch_bounds__(256) void topk_static_rows_kernel(const float* __re
     v[j] = live[j] ? row[e] : 0.0f;
     grp[j] = e / gs;
   }
-  float sv[MOE_MAX_K_DEV];
-  int si[MOE_MAX_K_DEV];
 #pragma unroll
   for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
     if (s < k) {
@@ -263,23 +253,46 @@ __global__ __launch_bounds__(256) void topk_static_rows_kernel(const float* __re
         if (grp[j] == cg) live[j] = false;
     }
   }
-  if (i16 == 0 && tv) {
-    float ex[MOE_MAX_K_DEV];
-    float z = 0.0f;
+}
+
+// slots [0, kc) of token t: the k selected experts with exp(l_s - l_1) / z
+// (z summed in slot order, as route_token), then index -1 and weight 0
+__device__ __forceinline__ void row16_store(int32_t* __restrict__ idx, float* __restrict__ w, int64_t t, int k, int kc,
+                                            const float* sv, const int* si) {
+  float ex[MOE_MAX_K_DEV];
+  float z = 0.0f;
 #pragma unroll
-    for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
-      if (s < k) {
-        ex[s] = expf(sv[s] - sv[0]);
-        z += ex[s];
-      }
+  for (int s = 0; s < MOE_MAX_K_DEV; ++s) {
+    if (s < k) {
+      ex[s] = expf(sv[s] - sv[0]);
+      z += ex[s];
     }
-#pragma unroll
-    for (int s = 0; s < MOE_MAX_K_DEV; ++s)
-      if (s < k) {
-        idx[(size_t)t * k + s] = si[s];
-        w[(size_t)t * k + s] = ex[s] / z;
-      }
   }
+#pragma unroll
+  for (int s = 0; s < MOE_MAX_K_DEV; ++s)
+    if (s < kc) {
+      idx[t * kc + s] = s < k ? si[s] : -1;
+      w[t * kc + s] = s < k ? ex[s] / z : 0.0f;
+    }
+}
+
+__global__ __launch_bounds__(256) void topk_static_rows_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                               int gs, int32_t* __restrict__ idx,
+                                                               float* __restrict__ w, int32_t* __restrict__ k_used,
+                                                               float* __restrict__ entropy) {
+  const int lane = lane_id(), r = lane / 16, i16 = lane % 16;
+  const int t = (blockIdx.x * 4 + wave_id()) * 4 + r;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (k_used) *k_used = k;
+    if (entropy) *entropy = 0.0f;
+  }
+  // every lane stays active for the row reductions; tokens past T have no
+  // live candidate and store nothing
+  const bool tv = t < T;
+  float sv[MOE_MAX_K_DEV];
+  int si[MOE_MAX_K_DEV];
+  row16_topk(logits + (size_t)(tv ? t : 0) * E, tv, E, k, gs, i16, sv, si);
+  if (i16 == 0 && tv) row16_store(idx, w, t, k, k, sv, si);
 }
 
 // Shannon entropy (nats) of softmax(row): H = ln Z - sum_e p_e (l_e - l_max)
@@ -401,12 +414,13 @@ __global__ __launch_bounds__(256) void entropy_select_kernel(const float* __rest
 
 // ------------------------------------------------------------- launchers --
 
-// The one-workgroup-per-logit kernel up to 16384 logits (measured at H =
-// 4096: 9.4 us against 19.6 us for the tiled kernel at 256 tokens x 32
-// experts, 12.2 against 18.8 at 512 x 32; above that the tiled kernel wins).
-// The tiled kernel's loads take 32 B of each of 32 rows per instruction, so
-// its sixteen waves' working set outgrows the vector L1 and it settles near
-// 19 us whatever the size up to 1024 x 64.
+// The small-batch kernel up to 16384 logits (measured at H = 4096 with one
+// logit per workgroup: 9.4 us against 19.6 us for the tiled kernel at 256
+// tokens x 32 experts, 12.2 against 18.8 at 512 x 32, and 10.3 us at 512 x 32
+// with eight experts per workgroup; above that the tiled kernel wins).  The
+// tiled kernel's loads take 32 B of each of 32 rows per instruction, so its
+// sixteen waves' working set outgrows the vector L1 and it settles near 19 us
+// whatever the size up to 1024 x 64.
 bool router_use_small(int T, int E) { return T <= 128 || (int64_t)T * E <= 16384; }
 
 hipError_t launch_router_logits(const void* x, const void* wr, float* logits, int T, int H, int E, int act,
