@@ -178,8 +178,11 @@ def main():
     ap.add_argument("--no-packed-q", action="store_true",
                     help="batched workloads: keep the row-major codes only (no packed_q repack)")
     ap.add_argument("--flush-mib", type=int, default=0,
-                    help="also time the layer's kernels with a write of this many MiB between steps, which "
-                         "evicts the 256 MB Infinity Cache, so their weight bytes must come from HBM")
+                    help="also time the layer's kernels with a read of this many MiB of another buffer between "
+                         "steps, which evicts the 256 MB Infinity Cache, so their weight bytes must come from HBM")
+    ap.add_argument("--flush-write", action="store_true",
+                    help="with --flush-mib: write the buffer instead of reading it (its dirty lines are then "
+                         "written back while the next step's kernels read)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -375,9 +378,9 @@ def main():
     flush = None
     if args.flush_mib:
         # ---- timed region 4: the layer's kernels, each step preceded by a
-        # write of flush_mib MiB (a fill kernel outside the events), so no
-        # weight byte of the previous steps is left in the Infinity Cache
-        buf = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
+        # read (a sum) or a write (a fill) of flush_mib MiB outside the events,
+        # so no weight byte of the previous steps is left in the Infinity Cache
+        buf = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
         nf = min(K, 64)
         fevents = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nl)] for _ in range(nf)]
         for evs in fevents:
@@ -385,7 +388,10 @@ def main():
                 e.record(stream)
         torch.cuda.synchronize()
         for i in range(nf):
-            buf.fill_(i & 0xFF)
+            if args.flush_write:
+                buf.fill_(float(i))
+            else:
+                buf.sum()
             step(args.warmup + i, fevents[i])
         torch.cuda.synchronize()
         moe.debug_set_events(None)
@@ -394,7 +400,8 @@ def main():
             for j in range(nl):
                 fk[j % nk] += evs[2 * j].elapsed_time(evs[2 * j + 1])
         fk = fk / nf * 1e3
-        flush = {"mib": args.flush_mib, "steps": nf, "per_kernel_us": [round(float(v), 3) for v in fk],
+        flush = {"mib": args.flush_mib, "mode": "write" if args.flush_write else "read", "steps": nf,
+                 "per_kernel_us": [round(float(v), 3) for v in fk],
                  "kernel_sum_us": round(float(fk.sum()), 3)}
         del buf
 
