@@ -85,46 +85,6 @@ hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t ro
   return hipGetLastError();
 }
 
-// Activation operand of the batched GEMM: x (fp16 or bf16) -> fp16, each
-// 8-element block optionally in the 4-bit GEMM order (q4g_order).  One workgroup per token:
-// bf16 rows are converted as x * 2^-a_t (common.hpp; exact) and a_t is
-// written to tokexp[t]; fp16 rows are copied.
-__global__ __launch_bounds__(256) void prep_a_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ a,
-                                                     int H, int act, int perm8, int32_t* __restrict__ tokexp,
-                                                     int32_t* __restrict__ any_scaled) {
-  __shared__ uint32_t wmax[4];
-  const int64_t t = blockIdx.x;
-  const uint16_t* xr = x + t * H;
-  uint16_t* ar = a + t * H;
-  int e = 0;
-  if (act == ACT_BF16) {
-    uint32_t m = 0;
-    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) m = max(m, bf16x8_absmax_bits(load16(xr + c)));
-    m = wave_max_u32(m);
-    if (lane_id() == 0) wmax[threadIdx.x / WAVE] = m;
-    __syncthreads();
-    e = bf16_token_exp(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
-    if (threadIdx.x == 0) {
-      tokexp[t] = e;
-      if (e != 0) *any_scaled = 1;  // every writer stores the same value
-    }
-  }
-  for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
-    u32x4 v = act8_to_f16_scaled(load16(xr + c), act, e);
-    if (perm8) v = q4g_order(v);
-    *(u32x4*)(ar + c) = v;
-  }
-}
-
-hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, bool perm8, int32_t* tokexp,
-                         int32_t* any_scaled, hipStream_t st) {
-  if (T <= 0) return hipSuccess;
-  if (act == ACT_BF16 && (!tokexp || !any_scaled)) return hipErrorInvalidValue;
-  launch_kernel(prep_a_kernel, (unsigned)T, 256, 0, st, (const uint16_t*)x, a, H, act, perm8 ? 1 : 0, tokexp,
-                any_scaled);
-  return hipGetLastError();
-}
-
 // Rows of h in pair order (taps); perm8 restores the natural element order
 // of rows stored in the 4-bit GEMM order.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ src,

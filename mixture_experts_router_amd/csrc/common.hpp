@@ -396,4 +396,38 @@ __device__ __forceinline__ u32x4 load_stream16(const void* p) {
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
 
+// The GEMM operand row of token t: the activations as fp16, each 8-element
+// block optionally in the 4-bit GEMM order (q4g_order).  bf16 rows are
+// converted as x * 2^-a_t (exact) and a_t is written to tokexp[t], raising
+// *any_scaled when a_t > 0; fp16 rows are copied.  One 256-thread group of a
+// workgroup per token; every thread of the workgroup calls it (the bf16 form
+// has a workgroup barrier), `live` false for a group past the last token.
+// wmax: four words of LDS for this group.
+__device__ __forceinline__ void prep_a_row(const uint16_t* __restrict__ x, uint16_t* __restrict__ a, int64_t t,
+                                           bool live, int H, int act, int perm8, int32_t* __restrict__ tokexp,
+                                           int32_t* __restrict__ any_scaled, int tid, uint32_t* wmax) {
+  const uint16_t* xr = x + t * H;
+  uint16_t* ar = a + t * H;
+  int e = 0;
+  if (act == ACT_BF16) {
+    uint32_t m = 0;
+    if (live)
+      for (int c = tid * 8; c < H; c += 256 * 8) m = max(m, bf16x8_absmax_bits(load16(xr + c)));
+    m = wave_max_u32(m);
+    if (lane_id() == 0) wmax[tid / WAVE] = m;
+    __syncthreads();
+    e = bf16_token_exp(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+    if (live && tid == 0) {
+      tokexp[t] = e;
+      if (e != 0) *any_scaled = 1;  // every writer stores the same value
+    }
+  }
+  if (!live) return;
+  for (int c = tid * 8; c < H; c += 256 * 8) {
+    u32x4 v = act8_to_f16_scaled(load16(xr + c), act, e);
+    if (perm8) v = q4g_order(v);
+    *(u32x4*)(ar + c) = v;
+  }
+}
+
 }  // namespace moe

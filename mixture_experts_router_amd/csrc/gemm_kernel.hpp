@@ -14,7 +14,7 @@
 //
 // The A operand is fp16 in HBM, each 8-element block in the order in which
 // the weights unpack (4-bit: 0,2,4,6,1,3,5,7; otherwise natural): the
-// activations are converted once by prep_a_kernel and the fused epilogue
+// activations are converted once by sort_prep_kernel and the fused epilogue
 // writes h that way.  Tile: BM = 32*MS rows x 256 columns (fused: 128
 // gate/up column pairs), 4 waves side by side along N, each 32*MS x 64; K
 // advances one 64-column quantisation group per step.

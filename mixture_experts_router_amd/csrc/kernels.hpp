@@ -74,16 +74,24 @@ hipError_t launch_router_logits(const void* x, const void* wr, float* logits, in
 hipError_t launch_load_stats(const int32_t* counts, int E, int32_t* least_used, float* stddev, hipStream_t st);
 // k > 0: static top-k; k <= 0: entropy-adaptive, kcap = 3 (scratch: T
 // floats, or NULL for the single-workgroup pass); gs experts per group
+// clear_word (optional): a device word set to 0 before the selection's
+// consumers run (the batched path's flag of scaled bf16 tokens)
 hipError_t launch_topk(const float* logits, int T, int E, int k, int gs, int32_t* idx, float* w, int32_t* k_used,
-                       float* entropy, float* scratch, hipStream_t st);
+                       float* entropy, float* scratch, hipStream_t st, int32_t* clear_word = nullptr);
 
 // ------------------------------------------------------------------ sort
 // k_used_dev may be NULL (then k_static is used); capacity > 0 lists only the
-// first `capacity` pairs of every expert (the rest get pos -1); clear_word
-// (if set) is set to 0
+// first `capacity` pairs of every expert (the rest get pos -1)
 hipError_t launch_sort_pairs(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st,
-                             int capacity = 0, int32_t* clear_word = nullptr);
+                             int capacity = 0);
+// the same sort, and in the same launch the batched GEMM's operand: x as fp16
+// (x * 2^-a_t for bf16, which also writes a_t to tokexp[t] and sets
+// *any_scaled to 1 when some a_t > 0; it must be 0 before)
+hipError_t launch_sort_prep(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
+                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st,
+                            int capacity, const void* x, int act, uint16_t* a, int H, bool perm8, int32_t* tokexp,
+                            int32_t* any_scaled);
 
 // ------------------------------------------------- decode (grouped GEMV)
 // chunks of 16 bytes per lane needed for a row of K weights
@@ -127,7 +135,7 @@ enum GemmMode { GEMM_FUSED_SWIGLU = 0, GEMM_GATHER_F32 = 1, GEMM_ROWS_F16 = 2 };
 int gemm_block_m(int P, int E);
 // upper bound on M tiles for P pairs over E experts
 int gemm_max_mtiles(int P, int E, int bm);
-// a: fp16 rows, 8-element blocks in the weights' unpack order (prep_a / the
+// a: fp16 rows, 8-element blocks in the weights' unpack order (sort_prep / the
 // fused epilogue); GATHER modes read a[perm[row]/kcap], ROWS mode a[row];
 // K = reduction dim.  FUSED: out = h fp16 [rows, N=I] (blocks in 4-bit unpack
 // order if perm8_out); GATHER_F32: out fp32 [rows, N]; ROWS_F16: out fp16
@@ -149,10 +157,6 @@ hipError_t launch_gemm(GemmMode mode, const uint16_t* a, int64_t a_rows, const i
 hipError_t launch_swiglu(const float* g, const float* u, uint16_t* h, int64_t rows, int I, bool perm8,
                          hipStream_t st, const int32_t* tokexp = nullptr, const int32_t* perm = nullptr,
                          int kcap = 1);
-// the GEMM operand: x * 2^-a_t as fp16; bf16 activations also write a_t to
-// tokexp[t] and set *any_scaled to 1 when some a_t > 0 (it must be 0 before)
-hipError_t launch_prep_a(const void* x, int act, uint16_t* a, int64_t T, int H, bool perm8, int32_t* tokexp,
-                         int32_t* any_scaled, hipStream_t st);
 // y[t] = act(2^2a_t sum_{s<k} w[t,s] * o[pos[t*kcap+s]]) (tokexp NULL: a_t = 0)
 hipError_t launch_combine(const uint16_t* o, const int32_t* pos, const float* wts, const int32_t* k_used_dev,
                           int k_static, int kcap, int T, int H, void* y, int act, hipStream_t st,

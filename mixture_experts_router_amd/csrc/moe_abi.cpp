@@ -283,9 +283,10 @@ moe_status check_opts(const moe_route_opts* o, int E, int k, RouteOpt* out) {
 
 // the selection launches: static top-k, or the adaptive pass (two launches
 // with scratch for the per-token entropies, one without)
+// (clear_word: see launch_topk)
 moe_status select_impl(const float* logits, int T, int E, int k, int gs, int32_t* idx, float* w, int32_t* k_used,
-                       float* entropy, float* scratch, hipStream_t st) {
-  HIP_TRY(moe::launch_topk(logits, T, E, k, gs, idx, w, k_used, entropy, scratch, st));
+                       float* entropy, float* scratch, hipStream_t st, int32_t* clear_word = nullptr) {
+  HIP_TRY(moe::launch_topk(logits, T, E, k, gs, idx, w, k_used, entropy, scratch, st, clear_word));
   if (k <= 0 && scratch) plan_step("entropy_tokens", st);
   plan_step(k > 0 ? "topk" : "topk_entropy", st);
   return MOE_OK;
@@ -293,10 +294,10 @@ moe_status select_impl(const float* logits, int T, int E, int k, int gs, int32_t
 
 moe_status route_impl(const void* x, moe_dtype dt, int T, int H, const void* wr, int E, int k, const RouteOpt& ro,
                       int32_t* idx, float* w, int32_t* k_used, float* entropy, float* logits, float* scratch,
-                      hipStream_t st) {
+                      hipStream_t st, int32_t* clear_word = nullptr) {
   HIP_TRY(moe::launch_router_logits(x, wr, logits, T, H, E, (int)dt, ro.health, ro.alpha, st));
   plan_step("router_logits", st);
-  return select_impl(logits, T, E, k, ro.gs, idx, w, k_used, entropy, scratch, st);
+  return select_impl(logits, T, E, k, ro.gs, idx, w, k_used, entropy, scratch, st, clear_word);
 }
 
 moe_status scratch_ptr(void** out);
@@ -426,23 +427,26 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       plan_step("sort_pairs", st);
     }
   } else {
+    // the selection also clears the flag that the operand conversion raises
+    // for scaled bf16 tokens
     if ((s = route_impl(x, dt, T, H, router_w, E, k, ro, idx, wts, k_used, entropy, logits, (float*)(W + L.hent),
-                        st)) != MOE_OK)
+                        st, any_scaled)) != MOE_OK)
       return s;
-    // the sort also clears the flag prep_a raises for scaled bf16 tokens
-    HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st, ro.cap,
-                                   any_scaled));
-    plan_step("sort_pairs", st);
     const int bm = moe::gemm_block_m((int)P, E);
     const int mt = moe::gemm_max_mtiles((int)P, E, bm);
     // the GEMM operand: fp16 activations, 8-element blocks in 4-bit unpack
-    // order for affine 4-bit codes (NVFP4 codes unpack in column order)
+    // order for affine 4-bit codes (NVFP4 codes unpack in column order),
+    // converted in the sort's launch
     const bool perm8 = bits == 4;
     const uint16_t* a16 = (const uint16_t*)x;
     if (perm8 || dt != MOE_F16) {
-      HIP_TRY(moe::launch_prep_a(x, act, a16w, T, H, perm8, tokexp, any_scaled, st));
-      plan_step("prep_a", st);
+      HIP_TRY(moe::launch_sort_prep(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st, ro.cap, x, act,
+                                    a16w, H, perm8, tokexp, any_scaled));
+      plan_step("sort_pairs_prep_a", st);
       a16 = a16w;
+    } else {
+      HIP_TRY(moe::launch_sort_pairs(idx, T, kcap, k_used, k_static, E, counts, offsets, perm, pos, st, ro.cap));
+      plan_step("sort_pairs", st);
     }
     // the gate and up scales in one packed_sb, up rows inter rows after gate
     // rows (the GEMM reads both halves with one descriptor)

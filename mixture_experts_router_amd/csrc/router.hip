@@ -189,11 +189,13 @@ __global__ __launch_bounds__(64 * NW) void router_logits_mfma_kernel(const uint1
 
 __global__ __launch_bounds__(256) void topk_static_kernel(const float* __restrict__ logits, int T, int E, int k, int gs,
                                                           int32_t* __restrict__ idx, float* __restrict__ w,
-                                                          int32_t* __restrict__ k_used, float* __restrict__ entropy) {
+                                                          int32_t* __restrict__ k_used, float* __restrict__ entropy,
+                                                          int32_t* __restrict__ clear_word) {
   const int t = blockIdx.x * 4 + wave_id();
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (k_used) *k_used = k;
     if (entropy) *entropy = 0.0f;
+    if (clear_word) *clear_word = 0;
   }
   if (t >= T) return;
   int si[MOE_MAX_K_DEV];
@@ -279,12 +281,14 @@ __device__ __forceinline__ void row16_store(int32_t* __restrict__ idx, float* __
 __global__ __launch_bounds__(256) void topk_static_rows_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                                int gs, int32_t* __restrict__ idx,
                                                                float* __restrict__ w, int32_t* __restrict__ k_used,
-                                                               float* __restrict__ entropy) {
+                                                               float* __restrict__ entropy,
+                                                               int32_t* __restrict__ clear_word) {
   const int lane = lane_id(), r = lane / 16, i16 = lane % 16;
   const int t = (blockIdx.x * 4 + wave_id()) * 4 + r;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (k_used) *k_used = k;
     if (entropy) *entropy = 0.0f;
+    if (clear_word) *clear_word = 0;
   }
   // every lane stays active for the row reductions; tokens past T have no
   // live candidate and store nothing
@@ -328,10 +332,12 @@ __device__ __forceinline__ float wave_entropy(const float* __restrict__ row, int
 __global__ __launch_bounds__(1024) void topk_entropy_kernel(const float* __restrict__ logits, int T, int E, int gs,
                                                             int32_t* __restrict__ idx, float* __restrict__ w,
                                                             int32_t* __restrict__ k_used,
-                                                            float* __restrict__ entropy) {
+                                                            float* __restrict__ entropy,
+                                                            int32_t* __restrict__ clear_word) {
   __shared__ float part[16];
   __shared__ int k_sh;
   const int wave = wave_id();
+  if (clear_word && threadIdx.x == 0) *clear_word = 0;
   float hs = 0.0f;
   for (int t = wave; t < T; t += 16) hs += wave_entropy(logits + (size_t)t * E, E);
   if (lane_id() == 0) part[wave] = hs;
@@ -368,7 +374,8 @@ __global__ __launch_bounds__(1024) void topk_entropy_kernel(const float* __restr
 // in order; the lanes are combined by the DPP butterfly), so all of them
 // reach the same batch entropy and k, and selects its own tokens.
 __global__ __launch_bounds__(256) void entropy_tokens_kernel(const float* __restrict__ logits, int T, int E,
-                                                             float* __restrict__ hent) {
+                                                             float* __restrict__ hent, int32_t* __restrict__ clear_word) {
+  if (clear_word && blockIdx.x == 0 && threadIdx.x == 0) *clear_word = 0;
   const int t = blockIdx.x * 4 + wave_id();
   if (t >= T) return;
   const float h = wave_entropy(logits + (size_t)t * E, E);
@@ -465,21 +472,23 @@ hipError_t launch_router_logits(const void* x, const void* wr, float* logits, in
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int gs, int32_t* idx, float* w, int32_t* k_used,
-                       float* entropy, float* scratch, hipStream_t st) {
+                       float* entropy, float* scratch, hipStream_t st, int32_t* clear_word) {
   if (k <= 0 && scratch) {
     const unsigned g = (unsigned)((T + 3) / 4);
-    hipError_t e = launch_kernel(entropy_tokens_kernel, g, 256, 0, st, logits, T, E, scratch);
+    hipError_t e = launch_kernel(entropy_tokens_kernel, g, 256, 0, st, logits, T, E, scratch, clear_word);
     if (e != hipSuccess) return e;
     return launch_kernel(entropy_select_kernel, g, 256, 0, st, logits, T, E, gs, (const float*)scratch, idx, w,
                          k_used, entropy);
   }
   if (k > 0) {
     if (E <= 64)
-      launch_kernel(topk_static_rows_kernel, (T + 15) / 16, 256, 0, st, logits, T, E, k, gs, idx, w, k_used, entropy);
+      launch_kernel(topk_static_rows_kernel, (T + 15) / 16, 256, 0, st, logits, T, E, k, gs, idx, w, k_used, entropy,
+                    clear_word);
     else
-      launch_kernel(topk_static_kernel, (T + 3) / 4, 256, 0, st, logits, T, E, k, gs, idx, w, k_used, entropy);
+      launch_kernel(topk_static_kernel, (T + 3) / 4, 256, 0, st, logits, T, E, k, gs, idx, w, k_used, entropy,
+                    clear_word);
   } else {
-    launch_kernel(topk_entropy_kernel, 1, 1024, 0, st, logits, T, E, gs, idx, w, k_used, entropy);
+    launch_kernel(topk_entropy_kernel, 1, 1024, 0, st, logits, T, E, gs, idx, w, k_used, entropy, clear_word);
   }
   return hipGetLastError();
 }

@@ -22,17 +22,14 @@
 
 namespace moe {
 
+// expert e's part of the sort: one 1024-thread workgroup
 template <int CH>
-__global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restrict__ idx, int T, int kcap,
-                                                          const int32_t* __restrict__ k_used_dev, int k_static, int E,
-                                                          int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                                          int32_t* __restrict__ pos, int cap,
-                                                          int32_t* __restrict__ clear_word) {
+__device__ __forceinline__ void sort_expert(int e, const int32_t* __restrict__ idx, int T, int kcap,
+                                            const int32_t* __restrict__ k_used_dev, int k_static, int E,
+                                            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                            int32_t* __restrict__ perm, int32_t* __restrict__ pos, int cap) {
   __shared__ int s_lt[16], s_eq[16];
-  if (clear_word && blockIdx.x == 0 && threadIdx.x == 0) *clear_word = 0;
   __shared__ int hist[MOE_MAX_EXPERTS_DEV];
-  const int e = blockIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
   const int ku = k_used_dev ? *k_used_dev : k_static;
@@ -133,20 +130,73 @@ __global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restr
   }
 }
 
+template <int CH>
+__global__ __launch_bounds__(1024) void sort_pairs_kernel(const int32_t* __restrict__ idx, int T, int kcap,
+                                                          const int32_t* __restrict__ k_used_dev, int k_static, int E,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                          int32_t* __restrict__ pos, int cap) {
+  sort_expert<CH>(blockIdx.x, idx, T, kcap, k_used_dev, k_static, E, counts, offsets, perm, pos, cap);
+}
+
+// The sort and the batched GEMM's activation operand in one launch (they are
+// independent): workgroups 0 .. E-1 sort, the others convert four tokens each
+// (prep_a_row, one 256-thread group per token).
+template <int CH>
+__global__ __launch_bounds__(1024) void sort_prep_kernel(const int32_t* __restrict__ idx, int T, int kcap,
+                                                         const int32_t* __restrict__ k_used_dev, int k_static, int E,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                                                         int32_t* __restrict__ pos, int cap,
+                                                         const uint16_t* __restrict__ x, uint16_t* __restrict__ a,
+                                                         int H, int act, int perm8, int32_t* __restrict__ tokexp,
+                                                         int32_t* __restrict__ any_scaled) {
+  if ((int)blockIdx.x < E) {
+    sort_expert<CH>(blockIdx.x, idx, T, kcap, k_used_dev, k_static, E, counts, offsets, perm, pos, cap);
+    return;
+  }
+  __shared__ uint32_t wmax[4][4];
+  const int g = threadIdx.x / 256;
+  const int64_t t = (int64_t)(blockIdx.x - E) * 4 + g;
+  prep_a_row(x, a, t < T ? t : 0, t < T, H, act, perm8, tokexp, any_scaled, threadIdx.x % 256, wmax[g]);
+}
+
 hipError_t launch_sort_pairs(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
                              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st,
-                             int capacity, int32_t* clear_word) {
+                             int capacity) {
   const int64_t P = (int64_t)T * kcap;
   const int64_t rounds = (P + 16 * 64 - 1) / (16 * 64);  // rounds of 64 pairs per wave
   if (rounds >= 16)
     (void)launch_kernel(sort_pairs_kernel<16>, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
-                        perm, pos, capacity, clear_word);
+                        perm, pos, capacity);
   else if (rounds >= 4)
     (void)launch_kernel(sort_pairs_kernel<4>, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
-                        perm, pos, capacity, clear_word);
+                        perm, pos, capacity);
   else
     (void)launch_kernel(sort_pairs_kernel<2>, E, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
-                        perm, pos, capacity, clear_word);
+                        perm, pos, capacity);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_prep(const int32_t* idx, int T, int kcap, const int32_t* k_used_dev, int k_static, int E,
+                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t st,
+                            int capacity, const void* x, int act, uint16_t* a, int H, bool perm8, int32_t* tokexp,
+                            int32_t* any_scaled) {
+  if (act == ACT_BF16 && (!tokexp || !any_scaled)) return hipErrorInvalidValue;
+  const int64_t P = (int64_t)T * kcap;
+  const int64_t rounds = (P + 16 * 64 - 1) / (16 * 64);
+  const unsigned grid = (unsigned)(E + (T + 3) / 4);
+  const uint16_t* xs = (const uint16_t*)x;
+  const int p8 = perm8 ? 1 : 0;
+  if (rounds >= 16)
+    (void)launch_kernel(sort_prep_kernel<16>, grid, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts,
+                        offsets, perm, pos, capacity, xs, a, H, act, p8, tokexp, any_scaled);
+  else if (rounds >= 4)
+    (void)launch_kernel(sort_prep_kernel<4>, grid, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
+                        perm, pos, capacity, xs, a, H, act, p8, tokexp, any_scaled);
+  else
+    (void)launch_kernel(sort_prep_kernel<2>, grid, 1024, 0, st, idx, T, kcap, k_used_dev, k_static, E, counts, offsets,
+                        perm, pos, capacity, xs, a, H, act, p8, tokexp, any_scaled);
   return hipGetLastError();
 }
 

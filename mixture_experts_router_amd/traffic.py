@@ -34,6 +34,7 @@ KERNEL_PLAN = [
     (re.compile(r"gemm_kernel<\d+, 0,"), "gemm_gate_up_swiglu"),
     (re.compile(r"gemm_kernel<\d+, 2,"), "gemm_down"),
     (re.compile(r"sort_pairs_kernel"), "sort_pairs"),
+    (re.compile(r"sort_prep_kernel"), "sort_pairs_prep_a"),
     (re.compile(r"combine_kernel"), "combine"),
 ]
 COPY_KERNEL = re.compile(r"neg")  # torch.neg over fp16: one read and one write per element
