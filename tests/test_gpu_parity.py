@@ -34,6 +34,10 @@ CASES = {
     "dense_k_eq_e": ("tiny", dict(k=8, T=6)),
     "k8_e256": ("tiny", dict(E=256, k=8, T=12, H=128, I=64)),
     "ragged_shapes": ("tiny", dict(T=37, H=192, E=12, k=3, I=320)),
+    # bf16 batches that end inside a sort-and-convert workgroup (four tokens
+    # each): 8-bit and 4-bit weights
+    "batched_bf16_ragged": ("batched_decode", dict(T=37, H=512, E=8, I=320)),
+    "prefill_bf16_ragged": ("prefill", dict(T=301, H=512, E=16, I=192)),
     # more than 16384 logits with H not a multiple of 256: the four-wave MFMA router
     "ragged_mfma_router": ("tiny", dict(T=200, H=192, E=96, k=3, I=128)),
     # decode shapes with long down rows (two waves per slot), one per
