@@ -168,7 +168,8 @@ class Weights:
 
     bits 4: q uint8 [E, N, K/2]; bits 5 / 6: q uint8 [E, N, 5K/8] / [E, N, 3K/4]
     (code k at bits b*k..b*k+b-1 of the row's little-endian bit stream, b =
-    bits; decode path only); bits 8: q uint8 [E, N, K];
+    bits; the batched path takes 5-bit rows when hidden and inter are multiples
+    of 128); bits 8: q uint8 [E, N, K];
     bits 16: q float16 [E, N, K].  scales/biases float16 [E, N, K/64] (None for bits 16).
     ``fmt="nvfp4"`` (bits 4, group_size 16): q uint8 [E, N, K/2] E2M1 codes
     (even column in the low nibble), scales uint8 [E, N, K/16] E4M3 block
@@ -442,7 +443,7 @@ def debug_set_tuning(key: int, value: int) -> None:
     """Launch-shape knob (0: decode gate+up waves/CU, 1: decode down waves/CU, 2: GEMM row tiles per group,
     3: GEMM row tile 32/64/128 (else automatic), 4: GEMM K groups per stage (1 or 2), 5: GEMM N subtiles
     per wave (2 or 4), 6: GEMM waves per column block (1 or 2), 7: GEMM workgroups per CU at 32/64-row
-    tiles (1 or 2), 8: decode gate+up waves per pair (2: from the wave target alone, else equal iterations
+    tiles (1 or 2; 3 for 4-bit and NVFP4 weights at 64-row tiles), 8: decode gate+up waves per pair (2: from the wave target alone, else equal iterations
     per wave))."""
     lib().moe_debug_set_tuning(int(key), int(value))
 

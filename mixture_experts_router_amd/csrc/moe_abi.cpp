@@ -413,7 +413,10 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       plan_step("gemv_up", st);
       HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, false, st, tokexp, nullptr, kcap));
       plan_step("swiglu", st);
-      if (pre_tap) HIP_TRY(moe::launch_gather_preact(g32, u32, nullptr, P, I, pre_tap, kcap, k_used, k_static, st));
+      if (pre_tap) {
+        HIP_TRY(moe::launch_gather_preact(g32, u32, nullptr, P, I, pre_tap, kcap, k_used, k_static, st));
+        plan_step("gather_preact", st);
+      }
     }
     // the gate+up kernel wrote the selection: the down kernel reads it
     // instead of selecting again
@@ -453,8 +456,9 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
     if (bits != 16 && !(gate_up && gate_up->packed_sb)) {
       uint8_t* sb = W + L.sbgu;
       HIP_TRY(moe::launch_pack_sb(wg.s, wg.b, E, I, H, wg.stride, sb, 2 * I, 0, st, bits == moe::NVF4));
+      plan_step("pack_sb_gate", st);
       HIP_TRY(moe::launch_pack_sb(wu.s, wu.b, E, I, H, wu.stride, sb, 2 * I, I, st, bits == moe::NVF4));
-      plan_step("pack_sb_gate_up", st);
+      plan_step("pack_sb_up", st);
       wg.sb = sb;
       wu.sb = sb + (size_t)I * 8;
       wg.sb_stride = wu.sb_stride = 2 * I;
@@ -474,7 +478,10 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
       plan_step("gemm_up", st);
       HIP_TRY(moe::launch_swiglu(g32, u32, h, P, I, perm8, st, tokexp, perm, kcap));
       plan_step("swiglu", st);
-      if (pre_tap) HIP_TRY(moe::launch_gather_preact(g32, u32, pos, P, I, pre_tap, kcap, k_used, k_static, st));
+      if (pre_tap) {
+        HIP_TRY(moe::launch_gather_preact(g32, u32, pos, P, I, pre_tap, kcap, k_used, k_static, st));
+        plan_step("gather_preact", st);
+      }
     }
     WView wd = view_of(down, 0);
     if (bits != 16 && !wd.sb) {

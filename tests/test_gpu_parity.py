@@ -38,6 +38,8 @@ CASES = {
     # each): 8-bit and 4-bit weights
     "batched_bf16_ragged": ("batched_decode", dict(T=37, H=512, E=8, I=320)),
     "prefill_bf16_ragged": ("prefill", dict(T=301, H=512, E=16, I=192)),
+    # 256 experts over 4800 pairs: four experts per sort workgroup
+    "batched_e256": ("prefill", dict(T=600, H=256, E=256, k=8, I=128)),
     # more than 16384 logits with H not a multiple of 256: the four-wave MFMA router
     "ragged_mfma_router": ("tiny", dict(T=200, H=192, E=96, k=3, I=128)),
     # decode shapes with long down rows (two waves per slot), one per
@@ -160,7 +162,7 @@ def test_fused_and_unfused_are_bit_identical(name, built):
 
 
 @pytest.mark.parametrize("name", ["tiny", "prefill_small", "batched_small", "entropy_q4", "ragged_shapes",
-                                  "prefill_bm128"])
+                                  "prefill_bm128", "k8_e256", "ragged_mfma_router", "batched_e256"])
 def test_sort_matches_oracle_exactly(name, built):
     inp, _, dev = built(name)
     _, taps = _run(dev, moe.FLAG_FORCE_MFMA)

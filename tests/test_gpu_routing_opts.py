@@ -174,6 +174,9 @@ CAP_CASES = {
     "decode_q6": ("decode_b1", dict(T=4, H=512, E=4, k=2, I=320, bits=6), [1, 3]),
     "decode_f4": ("decode_b1", dict(T=4, H=512, E=4, k=2, I=320, fmt="nvfp4"), [1, 3]),
     "prefill_f4": ("prefill", dict(T=300, H=512, E=16, I=192, fmt="nvfp4"), [20, 64]),
+    # more than 64 experts: the sort's workgroups take two and four experts each
+    "batched_e96": ("prefill", dict(T=300, H=256, E=96, k=4, I=128), [4, 12]),
+    "batched_e256": ("prefill", dict(T=400, H=256, E=256, k=8, I=128), [3, 10]),
 }
 
 
