@@ -444,7 +444,9 @@ int32_t moe_debug_last_plan(char* buf, size_t buf_bytes);
  * projections at 64-row tiles, else two), key 8 = waves per
  * (token, slot) pair of the decode gate+up kernel (2: from the resident-wave
  * target alone; other values: as many as give every wave the same number of
- * row iterations, at most that target).
+ * row iterations, at most that target), key 9 = tokens per workgroup of the
+ * small-batch router where it takes eight experts per workgroup (1 or 4;
+ * other values: 2).
  * Values <= 0 are ignored.  Key 6 changes the order of the fp32 sums
  * (results within the layer tolerance of the default); the other keys do not
  * change results.

@@ -444,7 +444,7 @@ def debug_set_tuning(key: int, value: int) -> None:
     3: GEMM row tile 32/64/128 (else automatic), 4: GEMM K groups per stage (1 or 2), 5: GEMM N subtiles
     per wave (2 or 4), 6: GEMM waves per column block (1 or 2), 7: GEMM workgroups per CU at 32/64-row
     tiles (1 or 2; 3 for 4-bit and NVFP4 weights at 64-row tiles), 8: decode gate+up waves per pair (2: from the wave target alone, else equal iterations
-    per wave))."""
+    per wave), 9: tokens per small-batch router workgroup at eight experts each (1, 2 or 4; default 2))."""
     lib().moe_debug_set_tuning(int(key), int(value))
 
 

@@ -48,7 +48,8 @@ enum TuneKey {
   TUNE_GEMM_KSPLIT = 6,  // 2: GEMM tiles run eight waves, two per column block splitting k (default four)
   TUNE_GEMM_WPC = 7,  // 1 / 2 / 3: workgroups per CU at 32- and 64-row GEMM tiles (3: 4-bit and NVFP4 at 64 rows; other values: by bits, tile and mode)
   TUNE_UP_BALANCE = 8,  // 2: decode gate+up waves per pair from the wave target alone (default: equal iterations)
-  TUNE_KEYS = 9
+  TUNE_ROUTER_TOKENS = 9,  // 1 / 4: tokens per small-batch router workgroup at eight experts each (default 2)
+  TUNE_KEYS = 10
 };
 int tuning(TuneKey key);
 

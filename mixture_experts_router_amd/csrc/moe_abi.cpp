@@ -521,7 +521,7 @@ moe_status forward_impl(const void* x, moe_dtype dt, int T, int H, const void* r
 
 namespace moe {
 namespace {
-int g_tuning[TUNE_KEYS] = {8, 8, 1 << 30, 1, 2, 2, 1, 8, 1};
+int g_tuning[TUNE_KEYS] = {8, 8, 1 << 30, 1, 2, 2, 1, 8, 1, 2};
 }
 int tuning(TuneKey key) { return g_tuning[key]; }
 void set_tuning(int key, int value) {

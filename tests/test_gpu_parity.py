@@ -404,6 +404,32 @@ def _router_exact_case(dtype, T, E, k, H):
     assert np.max(np.abs(r["w"].cpu().numpy() - w_o)) <= 1e-6
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("T,E,H", [(512, 32, 4096), (130, 64, 1024), (401, 40, 2048), (97, 100, 512)])
+def test_router_tokens_per_workgroup_bit_identical(dtype, T, E, H):
+    # the small-batch router at eight experts per workgroup, with one, two or
+    # four tokens per workgroup: each logit is summed in the same order, so the
+    # bits agree (T not a multiple of 4 and E not of 8: partial last blocks),
+    # with and without the load-aware correction
+    rng = np.random.default_rng(T * E)
+    xs = (rng.standard_normal((T, H))).astype(np.float32)
+    ws = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    xd, wd = torch.from_numpy(xs).to(tdt).cuda(), torch.from_numpy(ws).to(tdt).cuda()
+    hv = torch.from_numpy(rng.random(E).astype(np.float32)).cuda()
+    try:
+        for health in (None, hv):
+            got = {}
+            for tb in (1, 2, 4):
+                moe.debug_set_tuning(9, tb)
+                r = moe.route(xd, wd, 4, want_logits=True, health=health, alpha=0.5 if health is not None else 0.0)
+                torch.cuda.synchronize()
+                got[tb] = r["logits"].cpu().numpy().view(np.uint32)
+            assert np.array_equal(got[1], got[2]) and np.array_equal(got[1], got[4])
+    finally:
+        moe.debug_set_tuning(9, 2)
+
+
 @pytest.mark.parametrize("E,k", [(8, 1), (64, 4), (256, 8), (32, -1)])
 def test_topk_from_identical_logits(E, k):
     rng = np.random.default_rng(E)
