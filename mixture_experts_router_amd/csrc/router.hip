@@ -134,9 +134,10 @@ __global__ __launch_bounds__(256) void router_logits_small_kernel(const uint16_t
 // (lane l supplies row l%32 and 8 consecutive k), and the partial tiles are
 // added in wave order through LDS.  Products of two fp16 (bf16) values are
 // exact in fp32; only the summation order differs from a sequential sum.
-// Sixteen waves (H % 256 == 0) keep a wave's share of H to a few k-steps
-// whose loads all go out at once: the tile count is small (16 tiles for 512
-// tokens and 32 experts), so the kernel is bound by load latency.
+// Sixteen waves (H % 256 == 0, fewer tiles than CUs) keep a wave's share of
+// H to a few k-steps whose loads all go out at once: the tile count is small
+// (16 tiles for 512 tokens and 32 experts), so the kernel is bound by load
+// latency.  Four waves take the rest.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 template <int ACT, int NW>
@@ -450,7 +451,11 @@ hipError_t launch_router_logits(const void* x, const void* wr, float* logits, in
     dim3 grid((T + 31) / 32, (E + 31) / 32);
     const uint16_t* xs = (const uint16_t*)x;
     const uint16_t* ws = (const uint16_t*)wr;
-    if (H % (16 * 16) == 0) {
+    // sixteen waves per tile while the tiles are few (each wave's loads then
+    // all go out in one or two rounds); four once there is a tile per CU,
+    // where the sixteen waves' rows overflow the vector L1 (4096 tokens x 64
+    // experts: 23.1-23.4 against 25.2-25.6 us)
+    if (H % (16 * 16) == 0 && (int64_t)grid.x * grid.y < 256) {
       if (act == ACT_BF16)
         return launch_kernel(router_logits_mfma_kernel<ACT_BF16, 16>, grid, 1024, 0, st, xs, ws, logits, T, H, E, health,
                              alpha);

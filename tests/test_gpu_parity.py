@@ -376,11 +376,12 @@ def test_fuse_gate_up_matches_oracle_concatenation(built):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("T,E,k", [(1, 64, 4), (7, 8, 2), (300, 64, 4), (64, 256, 8), (33, 32, -1),
                                    (300, 32, -1), (200, 8, 2), (129, 256, 8), (300, 20, 2), (90, 45, 3),
-                                   (400, 40, 2)])
+                                   (400, 40, 2), (4096, 64, 4)])
 def test_router_exact_inputs_with_planted_ties(dtype, T, E, k):
     # H = 1024 takes the sixteen-wave MFMA router above 128 tokens and 16384
     # logits (H = 2048: one whole round of eight k-steps per wave); H = 320
-    # (not a multiple of 256) the four-wave one; H = 8192 runs
+    # (not a multiple of 256) the four-wave one, as do 256 tiles or more
+    # (4096 tokens x 64 experts); H = 8192 runs
     # the small-batch router's four-slice rounds (partial sums stay exact:
     # multiples of 2^-14 below 2^9).  The small-batch router takes 1, 2, 4 or 8
     # experts per workgroup as T*E grows (E = 20, 45 and 40: a partial last
